@@ -1,0 +1,328 @@
+"""Pins for the CPU oracle: page values, closed forms, invariants and finite
+differences. None of these compares the oracle with itself."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import gpt_oracle as O
+from transformer_lm_gpt_amd import workloads as W
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _cfg(**kw):
+    base = W.CONFIGS["tiny"]
+    return base.with_(**kw)
+
+
+# --------------------------------------------------------------------------- parameter counts
+
+EXPECTED_COUNTS = {"tiny": 4000, "char_small": 809856, "char_6l": 10770816,
+                   "bpe_12l_512": 63847424, "gpt2_124m": 124475904}
+
+
+@pytest.mark.parametrize("name", W.ORDER)
+def test_param_count_closed_form(name):
+    c = W.CONFIGS[name]
+    V, d, T, L = c.padded_vocab, c.n_embd, c.block_size, c.n_layer
+    closed = V * d + T * d + L * (12 * d * d + 13 * d) + 2 * d
+    assert O.n_params(c) == closed == EXPECTED_COUNTS[name]
+
+
+def test_param_count_page_values():
+    g = _gold("page_values.json")
+    mg = g["microgpt_param_count"]
+    c = _cfg(vocab_size=27, padded_vocab=27, n_embd=16, n_head=4, n_layer=1, block_size=16)
+    assert O.n_params(c, "microgpt") == mg["value"]
+    e = g["bpe_wte_params"]
+    wte = dict(O.param_shapes(_cfg(padded_vocab=50257, n_embd=512, n_layer=12, block_size=512)))["wte"]
+    assert abs(np.prod(wte) - e["value_approx"]) <= e["rel_tol"] * e["value_approx"]
+    a = g["attention_params_per_layer"]
+    sh = dict(O.param_shapes(_cfg(n_embd=512, n_layer=1)))
+    attn = np.prod(sh["h0.attn.w"]) + np.prod(sh["h0.proj.w"])
+    assert abs(attn - a["value_approx"]) <= a["rel_tol"] * a["value_approx"]
+    s = g["gpt2_small_params_millions"]
+    c = W.CONFIGS["gpt2_124m"].with_(padded_vocab=50257)
+    assert abs(O.n_params(c) / 1e6 - s["value_approx"]) <= s["rel_tol"] * s["value_approx"]
+
+
+def test_generator_table_matches_oracle_layout():
+    for name in W.ORDER:
+        c = W.CONFIGS[name]
+        assert W.tensor_table(c) == O.param_shapes(c)
+
+
+# --------------------------------------------------------------------------- closed forms
+
+def test_layernorm_closed_form():
+    g = _gold("closed_forms.json")["layernorm_pm1"]
+    y, _ = O.layernorm_fwd(np.array([g["x"]], float), np.ones(4), np.zeros(4))
+    np.testing.assert_allclose(y[0], g["y"], rtol=0, atol=1e-15)
+
+
+def test_gelu_table_values():
+    g = _gold("closed_forms.json")["gelu_values"]
+    np.testing.assert_allclose(O.gelu(np.array(g["u"])), g["gelu"], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(O.gelu_grad(np.array(g["u_grad"])), g["gelu_grad"], rtol=1e-14)
+
+
+def test_gelu_grad_matches_difference_quotient():
+    u = np.linspace(-6, 6, 97)
+    h = 1e-6
+    fd = (O.gelu(u + h) - O.gelu(u - h)) / (2 * h)
+    np.testing.assert_allclose(O.gelu_grad(u), fd, atol=1e-8)
+
+
+def test_gelu_is_exact_not_tanh():
+    u = np.linspace(-5, 5, 20001)
+    tanh = 0.5 * u * (1 + np.tanh(math.sqrt(2 / math.pi) * (u + 0.044715 * u ** 3)))
+    diff = np.abs(O.gelu(u) - tanh)
+    assert 4.0e-4 < diff.max() < 5.0e-4
+
+
+def test_attention_worked_example():
+    g = _gold("closed_forms.json")["attention_two_keys"]
+    q, k, v = (np.array(g[n], float)[None] for n in ("q", "k", "v"))
+    o, p = O.attention_fwd(q, k, v)
+    np.testing.assert_allclose(o[0], g["out"], atol=1e-12)
+
+
+def test_attention_T1_and_zero_query():
+    rng = np.random.default_rng(0)
+    v = rng.normal(size=(3, 1, 8))
+    o, _ = O.attention_fwd(rng.normal(size=(3, 1, 8)), rng.normal(size=(3, 1, 8)), v)
+    assert np.array_equal(o, v)
+    T = 7
+    v = rng.normal(size=(2, T, 8))
+    o, p = O.attention_fwd(np.zeros((2, T, 8)), rng.normal(size=(2, T, 8)), v)
+    expect = np.cumsum(v, axis=1) / np.arange(1, T + 1)[None, :, None]
+    np.testing.assert_allclose(o, expect, atol=1e-13)
+
+
+def test_attention_brute_force_loops():
+    rng = np.random.default_rng(1)
+    H, T, hd = 2, 4, 3
+    q, k, v = (rng.normal(size=(H, T, hd)) for _ in range(3))
+    o, p = O.attention_fwd(q, k, v)
+    for h in range(H):
+        for i in range(T):
+            w = [math.exp(sum(q[h, i, c] * k[h, j, c] for c in range(hd)) / math.sqrt(hd)) for j in range(i + 1)]
+            z = sum(w)
+            for c in range(hd):
+                assert abs(o[h, i, c] - sum(w[j] * v[h, j, c] for j in range(i + 1)) / z) < 1e-12
+    assert np.all(p[:, np.triu_indices(T, 1)[0], np.triu_indices(T, 1)[1]] == 0)
+    np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-14)
+
+
+def test_adam_constant_gradient_closed_form():
+    g = _gold("closed_forms.json")["adam_constant_gradient"]
+    P = {"w": np.array([[g["p0"]]])}
+    m = {"w": np.zeros((1, 1))}
+    v = {"w": np.zeros((1, 1))}
+    for t in range(1, 4):
+        O.adamw_update(P, {"w": np.array([[g["g"]]])}, m, v, t, g["lr"], g["beta1"], g["beta2"],
+                       g["eps"], g["wd"], 1.0, {"w": True})
+        assert abs(P["w"][0, 0] - g["p"][t - 1]) < 1e-12
+
+
+def test_adam_step1_and_decay_mask():
+    rng = np.random.default_rng(2)
+    p0 = {"w": rng.normal(size=(3, 4)), "b": rng.normal(size=(4,))}
+    gr = {"w": rng.normal(size=(3, 4)), "b": np.zeros(4)}
+    P = {k: v.copy() for k, v in p0.items()}
+    m = {k: np.zeros_like(v) for k, v in P.items()}
+    vv = {k: np.zeros_like(v) for k, v in P.items()}
+    lr, wd, eps = 0.01, 0.1, 1e-8
+    mask = {k: O.decays(k, v.shape) for k, v in P.items()}
+    O.adamw_update(P, gr, m, vv, 1, lr, 0.9, 0.95, eps, wd, 1.0, mask)
+    np.testing.assert_allclose(P["w"], p0["w"] * (1 - lr * wd) - lr * gr["w"] / (np.abs(gr["w"]) + eps), rtol=1e-13)
+    assert np.array_equal(P["b"], p0["b"])          # no decay on 1-D tensors, zero grad
+
+
+def test_clip_closed_form():
+    rng = np.random.default_rng(3)
+    g = {"a": rng.normal(size=(10, 10)), "b": rng.normal(size=(7,))}
+    n = O.grad_norm(g)
+    assert abs(n - math.sqrt(sum((x ** 2).sum() for x in g.values()))) < 1e-12
+    c = O.clip_coef(n, 1.0)
+    clipped = math.sqrt(sum(((x * c) ** 2).sum() for x in g.values()))
+    assert abs(clipped - n / (n + 1e-6)) < 1e-12
+    assert O.clip_coef(n, 1e9) == 1.0
+    assert O.clip_coef(n, 0.0) == 1.0
+
+
+# --------------------------------------------------------------------------- model-level pins
+
+def _setup(name, perturb=False, B=None, T=None, **kw):
+    c = W.CONFIGS[name].with_(**kw) if kw else W.CONFIGS[name]
+    drng, wrng = W.rngs()
+    params = W.init_params(c, wrng, perturb=perturb)
+    tok, tgt = W.make_batch(c, drng, B, T)
+    return c, params, tok, tgt
+
+
+@pytest.mark.parametrize("name,B", [("tiny", None), ("char_small", None), ("char_6l", 2), ("bpe_12l_512", 1)])
+def test_initial_loss_near_log_vocab(name, B):
+    c, params, tok, tgt = _setup(name, B=B)
+    z = O.logits(params, tok, c)
+    rl, _ = O.microbatch(params, tok, tgt, c)
+    L0 = rl.mean()
+    expect = math.log(c.padded_vocab) + 0.5 * z.var(axis=-1).mean()
+    assert abs(L0 - expect) < 0.05, (L0, expect)
+
+
+def test_initial_loss_page_value_bpe():
+    g = _gold("page_values.json")["initial_loss_bpe"]
+    c, params, tok, tgt = _setup("bpe_12l_512", B=1, T=128)
+    rl, _ = O.microbatch(params, tok, tgt, c)
+    assert abs(rl.mean() - g["value_approx"]) < g["abs_tol"]
+
+
+def test_zero_wte_gives_log_vocab_and_uniform_dlogits():
+    c, params, tok, tgt = _setup("tiny", perturb=True)
+    params["wte"][:] = 0.0
+    z = O.logits(params, tok, c)
+    assert np.all(z == 0.0)
+    rl, _ = O.microbatch(params, tok, tgt, c)
+    assert np.allclose(rl, math.log(c.padded_vocab), rtol=0, atol=1e-14)
+    ell, sm = O.xent_rows(z[0], tgt[0])
+    dz = sm.copy()
+    dz[np.arange(len(tgt[0])), tgt[0]] -= 1
+    expect = np.full_like(dz, 1.0 / c.padded_vocab)
+    expect[np.arange(len(tgt[0])), tgt[0]] -= 1
+    np.testing.assert_allclose(dz, expect, atol=1e-15)
+
+
+def test_dlogits_rows_sum_to_zero():
+    c, params, tok, tgt = _setup("char_small", perturb=True, B=2)
+    z = O.logits(params, tok, c)
+    ell, sm = O.xent_rows(z[0], tgt[0])
+    dz = sm.copy()
+    dz[np.arange(len(tgt[0])), tgt[0]] -= 1
+    assert np.abs(dz.sum(-1)).max() < 1e-14
+    np.testing.assert_allclose(sm.sum(-1), 1.0, atol=1e-14)
+
+
+def test_causality_bitwise():
+    c, params, tok, tgt = _setup("char_small", perturb=True, B=2)
+    z0 = O.logits(params, tok, c)
+    t = 20
+    tok2 = tok.copy()
+    tok2[:, t + 1:] = (tok2[:, t + 1:] + 17) % c.vocab_size
+    z1 = O.logits(params, tok2, c)
+    assert np.array_equal(z0[:, :t + 1], z1[:, :t + 1])
+    assert not np.array_equal(z0[:, t + 1:], z1[:, t + 1:])
+
+
+def test_layernorm_invariants():
+    rng = np.random.default_rng(4)
+    x = rng.normal(size=(5, 32)) * 3 + 1
+    y, cache = O.layernorm_fwd(x, np.ones(32), np.zeros(32))
+    np.testing.assert_allclose(y.mean(-1), 0, atol=1e-14)
+    np.testing.assert_allclose((y ** 2).mean(-1), 1 / (1 + 1e-5 / x.var(-1)), rtol=1e-12)
+    dy = rng.normal(size=(5, 32))
+    dx, dg, db = O.layernorm_bwd(dy, cache, np.ones(32))
+    np.testing.assert_allclose(dx.sum(-1), 0, atol=1e-13)
+    # orthogonal to xhat up to the eps term: sum(dx xhat) = rstd sum(dy xhat) eps / (var + eps)
+    xhat, rstd = cache
+    var = x.var(-1, keepdims=True)
+    expect = (rstd * (dy * xhat).sum(-1, keepdims=True) * 1e-5 / (var + 1e-5))[:, 0]
+    np.testing.assert_allclose((dx * xhat).sum(-1), expect, rtol=1e-6, atol=1e-15)
+    np.testing.assert_allclose(dg, (dy * xhat).sum(0), rtol=1e-14)
+    np.testing.assert_allclose(db, dy.sum(0), rtol=1e-14)
+
+
+def _fd_check(c, params, tok, tgt, n_random=20, seed=5):
+    P = {k: v.astype(np.float64) for k, v in params.items()}
+    B, T = tok.shape
+    _, G = O.microbatch(P, tok, tgt, c, grad_scale=1.0 / (B * T))
+
+    def loss(Pp):
+        return O.microbatch(Pp, tok, tgt, c)[0].mean()
+
+    rng = np.random.default_rng(seed)
+    h = 1e-5
+    checked = 0
+    for name, arr in P.items():
+        flat = arr.reshape(-1)
+        if arr.ndim == 1:
+            idx = np.arange(flat.size)                     # every bias / gain / shift
+        else:
+            idx = rng.choice(flat.size, size=min(n_random, flat.size), replace=False)
+            if name == "wte":                              # rows that are inputs and targets
+                idx = np.unique(np.concatenate([idx, tok[0, :3] * arr.shape[1], tgt[0, :3] * arr.shape[1] + 1]))
+        g = G[name].reshape(-1)
+        scale = np.abs(g).max() + 1e-12
+        for i in idx:
+            old = flat[i]
+            flat[i] = old + h
+            lp = loss(P)
+            flat[i] = old - h
+            lm = loss(P)
+            flat[i] = old
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - g[i]) <= 1e-6 * scale + 1e-10, (name, int(i), fd, g[i])
+            checked += 1
+    return checked
+
+
+def test_finite_difference_tiny():
+    c, params, tok, tgt = _setup("tiny", perturb=True)
+    assert _fd_check(c, params, tok, tgt) > 200
+
+
+@pytest.mark.slow
+def test_finite_difference_shrunk_char():
+    c = W.CONFIGS["char_small"].with_(n_layer=2, n_embd=32, n_head=4, block_size=8, batch=2)
+    drng, wrng = W.rngs()
+    params = W.init_params(c, wrng, perturb=True)
+    tok, tgt = W.make_batch(c, drng)
+    assert _fd_check(c, params, tok, tgt, n_random=8) > 500
+
+
+def test_grad_accumulation_equals_big_batch():
+    c, params, tok, tgt = _setup("char_small", perturb=True, B=4, T=16)
+    _, g_big = O.accumulate_grads(params, [(tok, tgt)], c)
+    _, g_acc = O.accumulate_grads(params, [(tok[:2], tgt[:2]), (tok[2:], tgt[2:])], c)
+    for k in g_big:
+        np.testing.assert_allclose(g_acc[k], g_big[k], rtol=1e-12, atol=1e-17)
+
+
+# --------------------------------------------------------------------------- generators
+
+def test_generators_deterministic():
+    for name in ["tiny", "char_small", "char_6l", "gpt2_124m"]:
+        c = W.CONFIGS[name]
+        a = W.make_batch(c, W.rngs()[0], B=2, T=16)
+        b = W.make_batch(c, W.rngs()[0], B=2, T=16)
+        assert a[0].tobytes() == b[0].tobytes() and a[1].tobytes() == b[1].tobytes()
+        assert np.array_equal(a[0][:, 1:], a[1][:, :-1])        # targets are the next tokens
+        assert a[0].min() >= 0 and a[0].max() < c.vocab_size
+    p1 = W.init_params(W.CONFIGS["char_small"], W.rngs()[1])
+    p2 = W.init_params(W.CONFIGS["char_small"], W.rngs()[1])
+    assert all(p1[k].tobytes() == p2[k].tobytes() for k in p1)
+
+
+def test_zipf_head_mass():
+    assert abs(W.zipf_cdf(65, 1.1)[0] - 0.250) < 0.001
+    assert abs(W.zipf_cdf(50257, 1.07)[0] - 0.122) < 0.001
+    c = W.CONFIGS["gpt2_124m"]
+    tok, _ = W.make_batch(c, W.rngs()[0])
+    assert abs((tok == 0).mean() - 0.122) < 0.01
+
+
+def test_init_std_and_residual_scale():
+    c = W.CONFIGS["gpt2_124m"].with_(padded_vocab=64, block_size=64)
+    p = W.init_params(c, W.rngs()[1])
+    assert abs(p["h0.fc.w"].std() - 0.02) < 5e-4
+    assert abs(p["h0.fcproj.w"].std() - 0.02 / math.sqrt(24)) < 2e-4
+    assert abs(p["h0.proj.w"].std() - 0.02 / math.sqrt(24)) < 3e-4
+    assert np.all(p["h0.ln1.g"] == 1) and np.all(p["h0.attn.b"] == 0)
