@@ -1,0 +1,188 @@
+/*
+ * gpt.h - C ABI of the MI355X (gfx950) GPT training-step library, libgpt.so.
+ *
+ * One training step of a GPT-2-style causal language model: token plus learned
+ * position embedding, pre-LayerNorm decoder blocks (causal multi-head
+ * attention, 4x GELU MLP, residual adds), final LayerNorm, lm_head tied to the
+ * token embedding, softmax cross-entropy over the (padded) vocabulary, the full
+ * backward pass with gradient accumulation, and an AdamW update with decoupled
+ * weight decay and global-norm gradient clipping.
+ *
+ * Passages that define the operations (the nanoGPT pages):
+ *   - "Building microGPT from scratch" (blog.hotdry.top), model-core section:
+ *     embeddings, QKV projection, scaled dot-product, softmax, weighted V,
+ *     output projection, the 4x MLP, residual plus norm; training-loop
+ *     section: causal next-token loss averaged over positions, backward,
+ *     Adam with (beta1, beta2, eps), gradient clipping at 1.0.
+ *   - nanoGPT run log (wmrh.cn), section 2.1: AdamW with weight decay 0.1 and
+ *     betas 0.9/0.95; section 3.1: gradient accumulation adds micro-batch
+ *     gradients before one update (effective batch = batch x steps).
+ *   - nanoGPT README translation (oa0.com): the GPT-2 124M model at block 1024.
+ *
+ * Conventions
+ *   - All device pointers are plain HIP device addresses. The library never
+ *     allocates device memory: the caller allocates the buffers whose sizes
+ *     gpt_get_sizes() reports and hands them over with gpt_bind(), together
+ *     with the HIP stream every call is enqueued on. Calls are asynchronous
+ *     on that stream unless stated otherwise.
+ *   - Every function returns GPT_OK (0) or a negative GPT_E_* code; the
+ *     message is available from gpt_last_error(). No exception crosses the ABI.
+ *     An error is sticky: later calls on the handle return it until
+ *     gpt_sync() reports and clears it.
+ *   - One handle must not be used from several host threads at once.
+ *   - Layout: parameters, gradients and both Adam moments are flat fp32 arrays
+ *     with identical offsets (gpt_tensor_info_at). Every linear weight is
+ *     stored [out, in] row-major and acts as y = x W^T + b. All 2-D tensors
+ *     (the decayed ones) come first, then all 1-D tensors; every tensor starts
+ *     at a multiple of 64 elements and the gaps are zero.
+ */
+#ifndef GPT_MI355X_H
+#define GPT_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define GPT_OK              0
+#define GPT_E_INVAL        -1  /* bad argument, config or shape                      */
+#define GPT_E_SEQ_TOO_LONG -2  /* T > block_size or B > batch                        */
+#define GPT_E_STATE        -3  /* call out of order (backward with no forward, ...)  */
+#define GPT_E_UNSUPPORTED  -4  /* valid request this build does not implement        */
+#define GPT_E_HIP          -5  /* HIP runtime or launch error                        */
+#define GPT_E_NONFINITE    -6  /* non-finite loss or gradient norm: update skipped   */
+
+#define GPT_PREC_FP32 0        /* every GEMM operand fp32                            */
+#define GPT_PREC_BF16 1        /* GEMM/attention operands bf16, everything else fp32 */
+
+typedef struct gpt_model gpt_model;
+
+typedef struct gpt_config {
+  int32_t vocab_size;    /* ids in tokens/targets are < vocab_size                  */
+  int32_t padded_vocab;  /* rows of wte and softmax width, >= vocab_size            */
+  int32_t n_layer;
+  int32_t n_head;
+  int32_t n_embd;        /* multiple of n_head; head_dim = n_embd / n_head <= 64    */
+  int32_t block_size;    /* maximum T (rows of wpe)                                 */
+  int32_t batch;         /* maximum micro-batch B per gpt_forward_loss call         */
+  int32_t grad_accum;    /* A: backward scales the micro-batch mean loss by 1/A     */
+  int32_t precision;     /* GPT_PREC_FP32 or GPT_PREC_BF16                          */
+  float   dropout;       /* must be 0                                               */
+  uint32_t flags;        /* reserved, must be 0                                     */
+} gpt_config;
+
+typedef struct gpt_sizes {
+  size_t n_params;         /* trainable scalars (no alignment gaps)                 */
+  size_t n_flat;           /* elements of the flat param/grad/m/v arrays            */
+  size_t param_bytes;      /* fp32 master weights                                    */
+  size_t grad_bytes;       /* fp32 gradients                                         */
+  size_t m_bytes, v_bytes; /* fp32 Adam moments                                      */
+  size_t shadow_bytes;     /* bf16 copy of the weights (0 in fp32 mode)              */
+  size_t activation_bytes; /* saved forward activations                              */
+  size_t workspace_bytes;  /* backward scratch, reductions, device state             */
+} gpt_sizes;
+
+typedef struct gpt_tensor_info {
+  char    name[48];        /* e.g. "wte", "h3.fc.w", "lnf.b"                         */
+  size_t  offset;          /* element offset in the flat arrays                      */
+  int32_t ndim;            /* 1 or 2                                                 */
+  int64_t shape[2];        /* [rows, cols] for 2-D, [n, 1] for 1-D                   */
+  int32_t decay;           /* 1 if weight decay applies                              */
+} gpt_tensor_info;
+
+typedef struct gpt_buffers {
+  void* params;       /* fp32 [n_flat]                        read/write            */
+  void* grads;        /* fp32 [n_flat]                        written by backward   */
+  void* m;            /* fp32 [n_flat]                        Adam first moment     */
+  void* v;            /* fp32 [n_flat]                        Adam second moment    */
+  void* shadow;       /* bf16 [n_flat] (NULL in fp32 mode)    weights as GEMM input */
+  void* activations;  /* activation_bytes, 256-byte aligned                          */
+  void* workspace;    /* workspace_bytes, 256-byte aligned                           */
+} gpt_buffers;
+
+/* Validates the configuration and plans every layout. Touches no GPU.
+ * On failure *out is NULL and gpt_last_error(NULL) holds the reason. */
+int gpt_create(const gpt_config* cfg, gpt_model** out);
+void gpt_destroy(gpt_model* h);
+
+/* Thread-local message for the last failed call (h may be NULL for gpt_create). */
+const char* gpt_last_error(const gpt_model* h);
+
+int gpt_get_sizes(const gpt_model* h, gpt_sizes* out);
+int gpt_num_tensors(const gpt_model* h);
+int gpt_tensor_info_at(const gpt_model* h, int i, gpt_tensor_info* out);
+
+/* Binds caller-owned device buffers (see gpt_buffers) and the HIP stream
+ * (hipStream_t, NULL = default stream). Buffers must stay alive and unmoved
+ * until gpt_destroy or the next gpt_bind. */
+int gpt_bind(gpt_model* h, const gpt_buffers* bufs, void* hip_stream);
+
+/* Call after writing weights into `params`: refreshes the bf16 shadow, zeroes
+ * gradients, both moments and the step counter. */
+int gpt_init_state(gpt_model* h);
+
+/* Forward of one micro-batch and the loss.
+ * d_tokens, d_targets: int32 [B, T] row-major on the device, ids in
+ * [0, vocab_size); 1 <= B <= batch, 1 <= T <= block_size. The tokens are
+ * copied, so the caller may reuse them after the call returns.
+ * d_loss (nullable): receives the fp32 mean over the B*T positions of
+ * -log softmax(logits)[target]. The loss gradient is formed in the same pass
+ * and kept for gpt_backward. */
+int gpt_forward_loss(gpt_model* h, const int32_t* d_tokens, const int32_t* d_targets,
+                     int32_t B, int32_t T, float* d_loss);
+
+/* Forward only, up to the logits, copied as fp32 [B, T, padded_vocab] into
+ * d_logits. Does not disturb a pending backward's saved state only if no
+ * forward_loss is pending; it invalidates it otherwise. */
+int gpt_forward_logits(gpt_model* h, const int32_t* d_tokens, int32_t B, int32_t T,
+                       float* d_logits);
+
+/* Backward of the last gpt_forward_loss. Adds d(loss / grad_accum) into the
+ * gradients; the first backward after gpt_init_state, gpt_zero_grad or
+ * gpt_adamw_step overwrites them instead. */
+int gpt_backward(gpt_model* h);
+
+/* Makes the next backward overwrite the gradients (no kernel runs). */
+int gpt_zero_grad(gpt_model* h);
+
+/* Global L2 norm n of all gradients; coef = min(1, clip / (n + 1e-6)) if
+ * clip > 0 else 1; t += 1; for every element: g' = coef g,
+ * m = beta1 m + (1 - beta1) g', v = beta2 v + (1 - beta2) g'^2,
+ * p = p (1 - lr wd) [decayed tensors only] - lr (m / (1 - beta1^t)) /
+ * (sqrt(v / (1 - beta2^t)) + eps); then refreshes the bf16 shadow.
+ * d_grad_norm (nullable) receives n (before clipping). If n is not finite the
+ * update is skipped on the device, t is not advanced, and the next gpt_sync
+ * returns GPT_E_NONFINITE. */
+int gpt_adamw_step(gpt_model* h, float lr, float beta1, float beta2, float eps,
+                   float weight_decay, float clip, float* d_grad_norm);
+
+/* Waits for the stream, then reports a pending sticky error, a device-side
+ * non-finite flag (GPT_E_NONFINITE) or GPT_OK, and clears them. */
+int gpt_sync(gpt_model* h);
+
+/* Synchronous: the device step counter t. */
+int gpt_get_step(gpt_model* h, int64_t* t);
+
+/* Synchronous copy of a saved activation into caller memory on the device.
+ * what: "x" (fp32 [M, d] residual input of block `layer`, layer == n_layer
+ * is the input of the final LayerNorm), "qkv" ([M, 3d], operand type),
+ * "attn" ([M, d], operand type), "lse" (fp32 [B, H, T]), "h" (GELU output,
+ * [M, 4d], operand type). bytes must equal the size of the request. */
+int gpt_debug_copy(gpt_model* h, const char* what, int32_t layer, void* d_dst, size_t bytes);
+
+/* Kernel timing hook used by benchmarks: while enabled, every launch of the
+ * named kernel family ("lm_head_fwd", "gemm", "attn_fwd", "attn_bwd",
+ * "xent", "adamw") is bracketed by HIP events on the bound stream.
+ * gpt_timer_read synchronizes and returns the summed milliseconds and the
+ * number of launches since enable. */
+int gpt_timer_enable(gpt_model* h, const char* family);
+int gpt_timer_disable(gpt_model* h);
+int gpt_timer_read(gpt_model* h, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPT_MI355X_H */

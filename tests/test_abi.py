@@ -1,0 +1,119 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, plans the layout the oracle's table describes, and rejects bad input."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import gpt_oracle as O
+from transformer_lm_gpt_amd import binding as Bd
+from transformer_lm_gpt_amd import workloads as W
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "gpt.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gpt_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = Bd.load_library()
+    declared = header_functions()
+    assert len(declared) >= 19
+    assert sorted(Bd.EXPORTS) == declared
+    for name in declared:
+        assert getattr(lib, name) is not None
+
+
+def test_library_is_gfx950_only():
+    # the shared object carries a gfx950 code object and no other GPU target
+    blob = open(Bd.LIB_PATH, "rb").read()
+    assert b"gfx950" in blob
+    for other in (b"gfx942", b"gfx90a", b"gfx1100", b"sm_80"):
+        assert other not in blob
+
+
+@pytest.mark.parametrize("name", W.ORDER)
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+def test_layout_matches_oracle(name, prec):
+    cfg = W.CONFIGS[name]
+    lay = Bd.Layout(cfg, prec)
+    try:
+        assert lay.sizes.n_params == O.n_params(cfg)
+        table = {n: (shape, dec) for n, _, shape, dec in lay.tensors}
+        oracle = {n: (s, O.decays(n, s)) for n, s in O.param_shapes(cfg)}
+        assert table == oracle
+        # offsets: 64-aligned, disjoint, decayed tensors first
+        spans = sorted((off, off + int(np.prod(shape)), dec) for _, off, shape, dec in lay.tensors)
+        for (a0, a1, _), (b0, _, _) in zip(spans, spans[1:]):
+            assert a1 <= b0
+        assert all(off % 64 == 0 for _, off, _, _ in lay.tensors)
+        decs = [dec for _, _, dec in spans]
+        assert decs == sorted(decs, reverse=True)
+        assert spans[-1][1] <= lay.sizes.n_flat and lay.sizes.n_flat % 256 == 0
+        assert lay.sizes.shadow_bytes == (lay.sizes.n_flat * 2 if prec == "bf16" else 0)
+        # round trip through the flat layout
+        p = W.init_params(cfg, np.random.default_rng(0)) if cfg.padded_vocab < 1000 else None
+        if p is not None:
+            back = lay.unflatten(lay.flatten(p))
+            assert all(np.array_equal(back[k], p[k]) for k in p)
+    finally:
+        lay.close()
+
+
+def _raw(**kw):
+    c = W.CONFIGS["tiny"]
+    r = Bd.make_config(c, "fp32")
+    for k, v in kw.items():
+        setattr(r, k, v)
+    return r
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_embd=18), -1),                 # not a multiple of n_head
+    (dict(n_head=0), -1),
+    (dict(padded_vocab=10), -1),           # below vocab_size
+    (dict(precision=7), -1),
+    (dict(flags=1), -1),
+    (dict(dropout=0.1), -4),
+    (dict(n_embd=512, n_head=4), -4),      # head_dim 128
+    (dict(batch=4096, block_size=16), -4),  # M above the single-workgroup sort
+])
+def test_create_rejects(kw, code):
+    lib = Bd.load_library()
+    h = C.c_void_p()
+    rc = lib.gpt_create(C.byref(_raw(**kw)), C.byref(h))
+    assert rc == code
+    assert not h.value
+    assert len(lib.gpt_last_error(None)) > 0
+
+
+def test_calls_before_bind_are_state_errors():
+    lib = Bd.load_library()
+    lay = Bd.Layout(W.CONFIGS["tiny"], "fp32")
+    try:
+        assert lib.gpt_backward(lay.h) == -3
+        assert lib.gpt_forward_loss(lay.h, None, None, 1, 1, None) == -3
+        assert b"bind" in lib.gpt_last_error(lay.h)
+    finally:
+        lay.close()
+
+
+def test_bind_rejects_misaligned_and_null():
+    lib = Bd.load_library()
+    lay = Bd.Layout(W.CONFIGS["tiny"], "bf16")
+    try:
+        b = Bd.gpt_buffers(256, 512, 768, 1024, None, 1280, 1536)      # shadow missing in bf16 mode
+        assert lib.gpt_bind(lay.h, C.byref(b), None) == -1
+    finally:
+        lay.close()
+    lay = Bd.Layout(W.CONFIGS["tiny"], "fp32")
+    try:
+        b = Bd.gpt_buffers(256 + 4, 512, 768, 1024, None, 1280, 1536)  # misaligned params
+        assert lib.gpt_bind(lay.h, C.byref(b), None) == -1
+    finally:
+        lay.close()

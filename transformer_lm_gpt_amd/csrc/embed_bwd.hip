@@ -1,0 +1,130 @@
+// Embedding backward, deterministic.
+//
+// x0[b, t] = wte[tok[b, t]] + wpe[t], so
+//   dwpe[t]  = sum_b dx0[b, t]
+//   dwte[id] += sum over positions m with tok[m] == id of dx0[m]
+// (the second adds to the lm_head contribution of the tied embedding).
+// Repeated ids are frequent (Zipf-distributed tokens put about an eighth of all
+// positions on one id), so the scatter is done without float atomics: the
+// (id, position) pairs are sorted in LDS by one workgroup, the sorted list is
+// cut into fixed chunks whose same-id runs are summed in order, and every
+// distinct id then adds its run sums in order. The summation order depends only
+// on the token ids, never on scheduling.
+#include "common.h"
+#include "kernels.h"
+
+namespace gpt {
+
+constexpr int PIECE = 32;          // sorted positions per chunk
+constexpr int SORT_MAX = 32768;    // keys sorted in one workgroup's LDS
+
+static int ceil_log2(int x) {
+  int s = 0;
+  while ((1 << s) < x) s++;
+  return s;
+}
+
+int embed_bwd_sort_size(int M) { return 1 << ceil_log2(M < 2 ? 2 : M); }
+
+__global__ void wpe_grad_kernel(const float* __restrict__ dx0, float* __restrict__ dwpe, float beta, int B, int T,
+                                int d) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;   // over T*d
+  if (i >= T * d) return;
+  float s = 0.f;
+  for (int b = 0; b < B; b++) s += dx0[(int64_t)b * T * d + i];
+  dwpe[i] = (beta != 0.f ? beta * dwpe[i] : 0.f) + s;
+}
+
+// Bitonic sort of n (a power of two) keys (id << shift) | position in LDS.
+__global__ __launch_bounds__(1024) void sort_keys_kernel(const int32_t* __restrict__ tok, int M, int shift, int n,
+                                                         uint32_t* __restrict__ out) {
+  extern __shared__ uint32_t sk[];
+  for (int i = threadIdx.x; i < n; i += 1024)
+    sk[i] = i < M ? (((uint32_t)tok[i]) << shift) | (uint32_t)i : 0xFFFFFFFFu;
+  __syncthreads();
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n; i += 1024) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const uint32_t a = sk[i], b = sk[ixj];
+          const bool up = (i & k) == 0;
+          if ((a > b) == up) {
+            sk[i] = b;
+            sk[ixj] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < M; i += 1024) out[i] = sk[i];
+}
+
+// One workgroup per chunk of PIECE sorted positions: walks them in order and
+// writes the sum of every same-id run to piece_sums[first position of the run].
+__global__ __launch_bounds__(256) void piece_sum_kernel(const uint32_t* __restrict__ keys, const float* __restrict__ dx0,
+                                                        float* __restrict__ piece_sums, int M, int shift, int d) {
+  const int i0 = blockIdx.x * PIECE;
+  const int i1 = min(M, i0 + PIECE);
+  const uint32_t mask = (1u << shift) - 1u;
+  for (int c = threadIdx.x; c < d; c += 256) {
+    int start = i0;
+    uint32_t cur = keys[i0] >> shift;
+    float s = 0.f;
+    for (int i = i0; i < i1; i++) {
+      const uint32_t k = keys[i];
+      const uint32_t id = k >> shift;
+      if (id != cur) {
+        piece_sums[(int64_t)start * d + c] = s;
+        s = 0.f;
+        start = i;
+        cur = id;
+      }
+      s += dx0[(int64_t)(k & mask) * d + c];
+    }
+    piece_sums[(int64_t)start * d + c] = s;
+  }
+}
+
+// One workgroup per sorted position; those that start an id's run add the run's
+// chunk sums, in order, into dwte[id].
+__global__ __launch_bounds__(256) void segment_add_kernel(const uint32_t* __restrict__ keys,
+                                                          const float* __restrict__ piece_sums,
+                                                          float* __restrict__ dwte, int M, int shift, int d,
+                                                          int Vp) {
+  const int i = blockIdx.x;
+  const uint32_t id = keys[i] >> shift;
+  if (i > 0 && (keys[i - 1] >> shift) == id) return;
+  if (id >= (uint32_t)Vp) return;   // ids outside the table are dropped, never written
+  // pieces of this run start at i and at every chunk boundary inside the run
+  for (int c = threadIdx.x; c < d; c += 256) {
+    float s = piece_sums[(int64_t)i * d + c];
+    for (int j = (i / PIECE + 1) * PIECE; j < M && (keys[j] >> shift) == id; j += PIECE)
+      s += piece_sums[(int64_t)j * d + c];
+    dwte[(int64_t)id * d + c] += s;
+  }
+}
+
+hipError_t launch_embed_bwd(const float* dx0, const int32_t* tok, float* dwte, float* dwpe, float beta_wpe, int B,
+                            int T, int d, int Vp, EmbedBwdScratch scr, hipStream_t s) {
+  const int M = B * T;
+  const int shift = ceil_log2(M < 2 ? 2 : M);
+  const int n = 1 << shift;
+  if (n > SORT_MAX || ((uint64_t)Vp << shift) > 0xFFFFFFFFull) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(wpe_grad_kernel, dim3((T * d + 255) / 256), dim3(256), 0, s, dx0, dwpe, beta_wpe, B, T, d);
+  const size_t lds = (size_t)n * sizeof(uint32_t);
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)sort_keys_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(sort_keys_kernel, dim3(1), dim3(1024), lds, s, tok, M, shift, n, scr.keys);
+  hipLaunchKernelGGL(piece_sum_kernel, dim3((M + PIECE - 1) / PIECE), dim3(256), 0, s, (const uint32_t*)scr.keys,
+                     dx0, scr.piece_sums, M, shift, d);
+  hipLaunchKernelGGL(segment_add_kernel, dim3(M), dim3(256), 0, s, (const uint32_t*)scr.keys,
+                     (const float*)scr.piece_sums, dwte, M, shift, d, Vp);
+  return hipGetLastError();
+}
+
+}  // namespace gpt

@@ -1,0 +1,115 @@
+// Host-side launchers of the gfx950 kernels. Each returns hipSuccess or the
+// launch error; shapes are validated by the runtime before the call.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gpt {
+
+enum Epilogue {
+  EPI_STORE = 0,       // C(T)   = acc
+  EPI_BIAS = 1,        // C(T)   = acc + bias[n]
+  EPI_BIAS_RESID = 2,  // C(f32) = resid[m, n] + acc + bias[n]
+  EPI_BIAS_GELU = 3,   // aux(f32) = u = acc + bias[n];  C(T) = gelu(u)
+  EPI_F32 = 4,         // C(f32) = acc
+  EPI_GELU_BWD = 5,    // C(T)   = acc * gelu'(aux[m, n])
+  EPI_ACC = 6,         // C(f32) = beta * C + acc   (beta is 0 or 1; C is not read when 0)
+};
+
+// C[m, n] = sum_k A(m, k) B(n, k) followed by the epilogue, where
+//   A(m, k) = a_kc ? A[m * lda + k] : A[k * lda + m]
+//   B(n, k) = b_kc ? B[n * ldb + k] : B[k * ldb + n]
+// T is the operand type (float or bf16), selected by `bf16_operands`.
+struct GemmDesc {
+  const void* A; int64_t lda; bool a_kc;
+  const void* B; int64_t ldb; bool b_kc;
+  void* C; int64_t ldc;
+  int M, N, K;
+  int epi;
+  const float* bias;
+  const float* resid; int64_t ldr;
+  float* aux; int64_t ldaux;
+  float beta;
+};
+
+hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s);
+
+// x0[m, :] = wte[tok[m], :] + wpe[m % T, :]   (fp32)
+// Ids outside [0, Vp) produce NaN rows instead of out-of-bounds reads.
+hipError_t launch_embed_fwd(const float* wte, const float* wpe, const int32_t* tok, float* x0,
+                            int M, int T, int d, int Vp, hipStream_t s);
+
+// y = LN(x) with gain g, shift b; writes y as operand type, mean and rstd (fp32 [M]).
+hipError_t launch_layernorm_fwd(const float* x, const float* g, const float* b, void* y, bool bf16_out,
+                                float* mean, float* rstd, int M, int d, hipStream_t s);
+
+// dx = dres + LN backward of dy; writes dx (fp32) and optionally its operand-type copy
+// dx_op; per-block partial column sums of dy * xhat and dy into part_g / part_b
+// ([nblk, d] each, nblk = ceil(M / LN_BWD_ROWS)).
+constexpr int LN_BWD_ROWS = 64;
+hipError_t launch_layernorm_bwd(const float* dy, const float* x, const float* mean, const float* rstd,
+                                const float* g, const float* dres, float* dx, void* dx_op, bool bf16_out,
+                                float* part_g, float* part_b, int M, int d, hipStream_t s);
+
+// Column sums of an [M, N] matrix (fp32 or bf16) into per-block partials [nblk, N].
+constexpr int COLSUM_ROWS = 64;
+hipError_t launch_colsum_partial(const void* X, bool bf16_in, int64_t ldx, int M, int N, float* part,
+                                 hipStream_t s);
+// dst[n] = beta * dst[n] + sum_j part[j, n] (j in order).
+hipError_t launch_colsum_final(const float* part, int nblk, int N, float* dst, float beta, hipStream_t s);
+
+// Row-wise softmax cross-entropy over Vp columns of z (operand type, row stride ldz).
+// Writes row_loss[m] = lse - z[m, y[m]] and overwrites z with
+// (softmax - onehot(y)) * grad_scale.
+hipError_t launch_xent(void* z, bool bf16_z, int64_t ldz, const int32_t* y, float* row_loss,
+                       int M, int Vp, float grad_scale, hipStream_t s);
+// out = sum(row_loss) / M (single block, fixed order).
+hipError_t launch_mean(const float* row_loss, int M, float* out, hipStream_t s);
+
+// Causal attention forward. qkv: [B*T, 3*d] (q | k | v, head h at columns h*hd);
+// o: [B*T, d]; lse: fp32 [B*H, T].
+hipError_t launch_attn_fwd(const void* qkv, void* o, float* lse, bool bf16_ops, int B, int T, int H,
+                           int hd, hipStream_t s);
+// Attention backward: D = rowsum(dO * O), then dK/dV and dQ into dqkv [B*T, 3*d].
+hipError_t launch_attn_bwd(const void* qkv, const void* o, const void* dout, const float* lse,
+                           float* Dbuf, void* dqkv, bool bf16_ops, int B, int T, int H, int hd,
+                           hipStream_t s);
+
+// Embedding backward: dwpe[t] = beta * dwpe[t] + sum_b dx0[b, t]; dwte[tok] += rows of dx0,
+// summed deterministically (stable sort by id, fixed-order segment sums).
+struct EmbedBwdScratch {
+  uint32_t* keys;       // [sort_n]
+  float* piece_sums;    // [M, d]
+};
+int embed_bwd_sort_size(int M);   // power of two >= M
+hipError_t launch_embed_bwd(const float* dx0, const int32_t* tok, float* dwte, float* dwpe, float beta_wpe,
+                            int B, int T, int d, int Vp, EmbedBwdScratch scr, hipStream_t s);
+
+// Sum of squares of n floats into per-block partials [NORM_BLOCKS].
+constexpr int NORM_BLOCKS = 1024;
+hipError_t launch_sumsq_partial(const float* g, size_t n, float* part, hipStream_t s);
+
+// Device state used by the optimizer (lives in the workspace).
+struct OptState {
+  int64_t t;            // completed steps
+  float norm;           // last gradient norm (pre-clip)
+  float coef;           // clip coefficient applied
+  float bc1, bc2;       // 1 - beta^t for the pending step
+  int32_t skip;         // 1 if the pending step is skipped (non-finite norm)
+  int32_t nonfinite;    // sticky flag read by the host at sync
+};
+// Reduces the partials to the norm, decides skip/coef, advances t, sets bias corrections.
+hipError_t launch_opt_prepare(const float* part, OptState* st, float clip, float beta1, float beta2,
+                              float* norm_out, hipStream_t s);
+// AdamW over n elements; elements [0, n_decay) decay. Writes the bf16 shadow if non-null.
+hipError_t launch_adamw(float* p, const float* g, float* m, float* v, void* shadow_bf16, size_t n,
+                        size_t n_decay, const OptState* st, float lr, float beta1, float beta2, float eps,
+                        float wd, hipStream_t s);
+// bf16 copy of n fp32 values.
+hipError_t launch_cast_bf16(const float* src, void* dst, size_t n, hipStream_t s);
+// Zero n 32-bit words with a fill kernel (safe inside captured graphs).
+hipError_t launch_zero(void* p, size_t n_words, hipStream_t s);
+// dst[m * N + n] = float(src[m * ld + n]) for an [M, N] block of operand type.
+hipError_t launch_rows_to_f32(const void* src, bool bf16_src, int64_t ld, int M, int N, float* dst, hipStream_t s);
+
+}  // namespace gpt

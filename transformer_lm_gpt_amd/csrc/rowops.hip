@@ -1,0 +1,294 @@
+// Row-wise, HBM-bound kernels of the step: embedding gather, LayerNorm forward
+// and backward, deterministic column sums (bias and LayerNorm parameter
+// gradients), the fused softmax cross-entropy forward+backward and the loss mean.
+#include "common.h"
+#include "kernels.h"
+
+namespace gpt {
+
+// ----------------------------------------------------------------------------- embedding
+// Token embedding plus learned position embedding ("Building microGPT from
+// scratch", model-core section: token/pos embedding, no rotary).
+__global__ void embed_fwd_kernel(const float* __restrict__ wte, const float* __restrict__ wpe,
+                                 const int32_t* __restrict__ tok, float* __restrict__ x0, int M, int T, int d,
+                                 int Vp) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t total = (int64_t)M * d;
+  if (i >= total) return;
+  int m = (int)(i / d), c = (int)(i % d);
+  const int id = tok[m];
+  // an id outside the table poisons the row instead of reading out of bounds
+  x0[i] = (id >= 0 && id < Vp) ? wte[(int64_t)id * d + c] + wpe[(int64_t)(m % T) * d + c] : __builtin_nanf("");
+}
+
+hipError_t launch_embed_fwd(const float* wte, const float* wpe, const int32_t* tok, float* x0, int M, int T,
+                            int d, int Vp, hipStream_t s) {
+  int64_t total = (int64_t)M * d;
+  hipLaunchKernelGGL(embed_fwd_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, wte, wpe, tok,
+                     x0, M, T, d, Vp);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- LayerNorm
+// One wavefront per row: mean, biased variance, rstd = 1/sqrt(var + 1e-5).
+template <typename T>
+__global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x, const float* __restrict__ g,
+                                                     const float* __restrict__ b, T* __restrict__ y,
+                                                     float* __restrict__ mean, float* __restrict__ rstd, int M,
+                                                     int d) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const float* xr = x + (int64_t)row * d;
+  float s = 0.f;
+  for (int c = lane; c < d; c += 64) s += xr[c];
+  const float mu = wave_sum(s) / d;
+  float v = 0.f;
+  for (int c = lane; c < d; c += 64) {
+    float t = xr[c] - mu;
+    v += t * t;
+  }
+  const float rs = 1.0f / sqrtf(wave_sum(v) / d + 1e-5f);
+  T* yr = y + (int64_t)row * d;
+  for (int c = lane; c < d; c += 64) yr[c] = from_f32<T>((xr[c] - mu) * rs * g[c] + b[c]);
+  if (lane == 0) {
+    mean[row] = mu;
+    rstd[row] = rs;
+  }
+}
+
+hipError_t launch_layernorm_fwd(const float* x, const float* g, const float* b, void* y, bool bf16_out,
+                                float* mean, float* rstd, int M, int d, hipStream_t s) {
+  dim3 grid((M + 3) / 4);
+  if (bf16_out)
+    hipLaunchKernelGGL(ln_fwd_kernel<bf16>, grid, dim3(256), 0, s, x, g, b, (bf16*)y, mean, rstd, M, d);
+  else
+    hipLaunchKernelGGL(ln_fwd_kernel<float>, grid, dim3(256), 0, s, x, g, b, (float*)y, mean, rstd, M, d);
+  return hipGetLastError();
+}
+
+// Backward: with xhat = (x - mu) rstd and gh = dy * g,
+//   dx = rstd (gh - mean(gh) - xhat mean(gh xhat)) + dres.
+// Each workgroup owns LN_BWD_ROWS rows; each wave accumulates its own column
+// partials of dy*xhat and dy in LDS, and the four waves are summed in order.
+constexpr int LN_MAX_D = 1024;
+template <typename T>
+__global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ dy, const float* __restrict__ x,
+                                                     const float* __restrict__ mean,
+                                                     const float* __restrict__ rstd, const float* __restrict__ g,
+                                                     const float* dres, float* dx, T* dx_op,
+                                                     float* __restrict__ part_g, float* __restrict__ part_b,
+                                                     int M, int d) {
+  __shared__ float sg[4][LN_MAX_D];
+  __shared__ float sb[4][LN_MAX_D];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int c = lane; c < d; c += 64) {
+    sg[w][c] = 0.f;
+    sb[w][c] = 0.f;
+  }
+  const int row_begin = blockIdx.x * LN_BWD_ROWS;
+  const int row_end = min(M, row_begin + LN_BWD_ROWS);
+  for (int row = row_begin + w; row < row_end; row += 4) {
+    const int64_t o = (int64_t)row * d;
+    const float mu = mean[row], rs = rstd[row];
+    float sa = 0.f, sbb = 0.f;
+    for (int c = lane; c < d; c += 64) {
+      float xh = (x[o + c] - mu) * rs;
+      float dyv = dy[o + c];
+      float gh = dyv * g[c];
+      sa += gh;
+      sbb += gh * xh;
+      sg[w][c] += dyv * xh;
+      sb[w][c] += dyv;
+    }
+    const float a = wave_sum(sa) / d;
+    const float bb = wave_sum(sbb) / d;
+    for (int c = lane; c < d; c += 64) {
+      float xh = (x[o + c] - mu) * rs;
+      float gh = dy[o + c] * g[c];
+      float v = rs * (gh - a - xh * bb);
+      if (dres) v += dres[o + c];
+      dx[o + c] = v;
+      if (dx_op) dx_op[o + c] = from_f32<T>(v);
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < d; c += 256) {
+    part_g[(int64_t)blockIdx.x * d + c] = ((sg[0][c] + sg[1][c]) + sg[2][c]) + sg[3][c];
+    part_b[(int64_t)blockIdx.x * d + c] = ((sb[0][c] + sb[1][c]) + sb[2][c]) + sb[3][c];
+  }
+}
+
+hipError_t launch_layernorm_bwd(const float* dy, const float* x, const float* mean, const float* rstd,
+                                const float* g, const float* dres, float* dx, void* dx_op, bool bf16_out,
+                                float* part_g, float* part_b, int M, int d, hipStream_t s) {
+  if (d > LN_MAX_D) return hipErrorInvalidValue;
+  dim3 grid((M + LN_BWD_ROWS - 1) / LN_BWD_ROWS);
+  if (bf16_out)
+    hipLaunchKernelGGL(ln_bwd_kernel<bf16>, grid, dim3(256), 0, s, dy, x, mean, rstd, g, dres, dx, (bf16*)dx_op,
+                       part_g, part_b, M, d);
+  else
+    hipLaunchKernelGGL(ln_bwd_kernel<float>, grid, dim3(256), 0, s, dy, x, mean, rstd, g, dres, dx,
+                       (float*)dx_op, part_g, part_b, M, d);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- column sums
+template <typename T>
+__global__ void colsum_partial_kernel(const T* __restrict__ X, int64_t ldx, int M, int N, float* __restrict__ part) {
+  const int col = blockIdx.x * 256 + threadIdx.x;
+  if (col >= N) return;
+  const int r0 = blockIdx.y * COLSUM_ROWS;
+  const int r1 = min(M, r0 + COLSUM_ROWS);
+  float s = 0.f;
+  for (int r = r0; r < r1; r++) s += to_f32(X[(int64_t)r * ldx + col]);
+  part[(int64_t)blockIdx.y * N + col] = s;
+}
+
+hipError_t launch_colsum_partial(const void* X, bool bf16_in, int64_t ldx, int M, int N, float* part,
+                                 hipStream_t s) {
+  dim3 grid((N + 255) / 256, (M + COLSUM_ROWS - 1) / COLSUM_ROWS);
+  if (bf16_in)
+    hipLaunchKernelGGL(colsum_partial_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)X, ldx, M, N, part);
+  else
+    hipLaunchKernelGGL(colsum_partial_kernel<float>, grid, dim3(256), 0, s, (const float*)X, ldx, M, N, part);
+  return hipGetLastError();
+}
+
+__global__ void colsum_final_kernel(const float* __restrict__ part, int nblk, int N, float* dst, float beta) {
+  const int col = blockIdx.x * 256 + threadIdx.x;
+  if (col >= N) return;
+  float s = 0.f;
+  for (int j = 0; j < nblk; j++) s += part[(int64_t)j * N + col];
+  dst[col] = (beta != 0.f ? beta * dst[col] : 0.f) + s;
+}
+
+hipError_t launch_colsum_final(const float* part, int nblk, int N, float* dst, float beta, hipStream_t s) {
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((N + 255) / 256), dim3(256), 0, s, part, nblk, N, dst, beta);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- cross-entropy
+// Per row m of logits z: lse = log sum_j exp(z_j) over all Vp columns,
+// loss_m = lse - z[y_m]; the row is then overwritten by its gradient
+// (softmax - onehot(y)) * grad_scale ("Building microGPT from scratch",
+// training-loop section: -log probs[target], averaged over positions).
+template <typename T>
+__global__ __launch_bounds__(256) void xent_kernel(T* z, int64_t ldz, const int32_t* __restrict__ y,
+                                                   float* __restrict__ row_loss, int Vp, float grad_scale) {
+  __shared__ float red_m[4], red_s[4];
+  __shared__ float s_lse, s_zt;
+  const int row = blockIdx.x;
+  T* zr = z + (int64_t)row * ldz;
+  const int tgt = y[row];
+  float m = -INFINITY, s = 0.f;
+  for (int c = threadIdx.x; c < Vp; c += 256) {
+    float v = to_f32(zr[c]);
+    if (v > m) {
+      s = s * __expf(m - v) + 1.f;
+      m = v;
+    } else {
+      s += __expf(v - m);
+    }
+  }
+  // wave combine of (m, s)
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float m2 = __shfl_xor(m, o, WAVE), s2 = __shfl_xor(s, o, WAVE);
+    float mm = fmaxf(m, m2);
+    s = (m == -INFINITY ? 0.f : s * __expf(m - mm)) + (m2 == -INFINITY ? 0.f : s2 * __expf(m2 - mm));
+    m = mm;
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red_m[w] = m;
+    red_s[w] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float mm = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+    float ss = 0.f;
+    for (int i = 0; i < 4; i++) ss += red_m[i] == -INFINITY ? 0.f : red_s[i] * __expf(red_m[i] - mm);
+    float lse = mm + logf(ss);
+    s_lse = lse;
+    const bool ok = tgt >= 0 && tgt < Vp;   // an id outside the table yields a NaN loss
+    float zt = ok ? to_f32(zr[tgt]) : __builtin_nanf("");
+    s_zt = zt;
+    row_loss[row] = lse - zt;
+  }
+  __syncthreads();
+  const float lse = s_lse;
+  for (int c = threadIdx.x; c < Vp; c += 256) {
+    float p = __expf(to_f32(zr[c]) - lse);
+    zr[c] = from_f32<T>((p - (c == tgt ? 1.f : 0.f)) * grad_scale);
+  }
+}
+
+hipError_t launch_xent(void* z, bool bf16_z, int64_t ldz, const int32_t* y, float* row_loss, int M, int Vp,
+                       float grad_scale, hipStream_t s) {
+  if (bf16_z)
+    hipLaunchKernelGGL(xent_kernel<bf16>, dim3(M), dim3(256), 0, s, (bf16*)z, ldz, y, row_loss, Vp, grad_scale);
+  else
+    hipLaunchKernelGGL(xent_kernel<float>, dim3(M), dim3(256), 0, s, (float*)z, ldz, y, row_loss, Vp,
+                       grad_scale);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void mean_kernel(const float* __restrict__ x, int M, float* out) {
+  __shared__ float red[4];
+  float s = 0.f;
+  for (int i = threadIdx.x; i < M; i += 256) s += x[i];
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) *out = (((red[0] + red[1]) + red[2]) + red[3]) / (float)M;
+}
+
+hipError_t launch_mean(const float* row_loss, int M, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(256), 0, s, row_loss, M, out);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- small utilities
+__global__ void cast_bf16_kernel(const float* __restrict__ src, bf16* __restrict__ dst, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = (bf16)src[i];
+}
+hipError_t launch_cast_bf16(const float* src, void* dst, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 65536);
+  hipLaunchKernelGGL(cast_bf16_kernel, dim3(blocks), dim3(256), 0, s, src, (bf16*)dst, n);
+  return hipGetLastError();
+}
+
+__global__ void zero_kernel(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+hipError_t launch_zero(void* p, size_t n_words, hipStream_t s) {
+  if (n_words == 0) return hipSuccess;
+  unsigned blocks = (unsigned)std::min<size_t>((n_words + 255) / 256, 65536);
+  hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, s, (uint32_t*)p, n_words);
+  return hipGetLastError();
+}
+
+template <typename T>
+__global__ void rows_to_f32_kernel(const T* __restrict__ src, int64_t ld, int M, int N, float* __restrict__ dst) {
+  const int64_t total = (int64_t)M * N;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = i / N, n = i % N;
+    dst[i] = to_f32(src[m * ld + n]);
+  }
+}
+hipError_t launch_rows_to_f32(const void* src, bool bf16_src, int64_t ld, int M, int N, float* dst, hipStream_t s) {
+  const int64_t total = (int64_t)M * N;
+  if (total == 0) return hipSuccess;
+  unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 65536);
+  if (bf16_src)
+    hipLaunchKernelGGL(rows_to_f32_kernel<bf16>, dim3(blocks), dim3(256), 0, s, (const bf16*)src, ld, M, N, dst);
+  else
+    hipLaunchKernelGGL(rows_to_f32_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)src, ld, M, N, dst);
+  return hipGetLastError();
+}
+
+}  // namespace gpt

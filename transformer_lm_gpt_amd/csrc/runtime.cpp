@@ -1,0 +1,723 @@
+// C ABI of the GPT training step (see include/gpt.h): configuration checks,
+// the flat parameter layout, the activation and workspace plans, and the
+// launch sequences of forward, backward and AdamW on the bound HIP stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/gpt.h"
+#include "kernels.h"
+
+using namespace gpt;
+
+namespace {
+
+thread_local std::string g_create_error;
+
+constexpr size_t ALIGN_ELEMS = 64;     // tensor offsets in the flat arrays
+constexpr size_t ALIGN_BYTES = 256;    // arena slices
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Tensor {
+  std::string name;
+  size_t offset;
+  int ndim;
+  int64_t rows, cols;
+  int decay;
+  size_t numel() const { return (size_t)rows * (size_t)cols; }
+};
+
+struct Slice {
+  size_t off = 0, bytes = 0;
+};
+
+struct Planner {
+  size_t total = 0;
+  Slice take(size_t bytes) {
+    Slice s;
+    s.off = total;
+    s.bytes = bytes;
+    total = round_up(total + bytes, ALIGN_BYTES);
+    return s;
+  }
+};
+
+struct LayerAct {
+  Slice x, xmid, ln1, ln1_mean, ln1_rstd, qkv, att, lse, ln2, ln2_mean, ln2_rstd, u, h;
+};
+
+struct Timer {
+  bool on = false;
+  std::string family;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> events;
+  size_t used = 0;
+};
+
+}  // namespace
+
+struct gpt_model {
+  gpt_config cfg;
+  bool bf16;
+  int d, H, hd, L, V, Vp, Tmax, Bmax, A;
+  int64_t ldz;
+  size_t op_size;  // bytes per operand element
+  std::vector<Tensor> tensors;
+  size_t n_params = 0, n_flat = 0, n_decay = 0;
+  // activations
+  std::vector<LayerAct> layers;
+  Slice x_final, lnf, lnf_mean, lnf_rstd, logits, row_loss, tokens, targets;
+  size_t act_bytes = 0;
+  // workspace
+  Slice dres, dres_op, dln, du, dO, dqkv, attnD, part_g, part_b, colsum_part, emb_keys, emb_piece, norm_part, opt;
+  size_t ws_bytes = 0;
+  // binding
+  gpt_buffers buf{};
+  bool bound = false;
+  hipStream_t stream = nullptr;
+  // state
+  bool grads_fresh = true;
+  bool fwd_pending = false;
+  int cur_B = 0, cur_T = 0;
+  int sticky = GPT_OK;
+  std::string err;
+  Timer timer;
+};
+
+// ----------------------------------------------------------------------------- helpers
+namespace {
+
+int fail(gpt_model* h, int code, const std::string& msg) {
+  if (h) {
+    if (h->sticky == GPT_OK) h->sticky = code;
+    h->err = msg;
+  }
+  g_create_error = msg;
+  return code;
+}
+
+int hip_check(gpt_model* h, hipError_t e, const char* what) {
+  if (e == hipSuccess) return GPT_OK;
+  return fail(h, GPT_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+const Tensor* find(const gpt_model* h, const std::string& name) {
+  for (const auto& t : h->tensors)
+    if (t.name == name) return &t;
+  return nullptr;
+}
+
+float* P(gpt_model* h, const std::string& name) { return (float*)h->buf.params + find(h, name)->offset; }
+float* G(gpt_model* h, const std::string& name) { return (float*)h->buf.grads + find(h, name)->offset; }
+// Weight as a GEMM operand: the bf16 shadow in bf16 mode, the fp32 master otherwise.
+const void* Wop(gpt_model* h, const std::string& name) {
+  const Tensor* t = find(h, name);
+  if (h->bf16) return (const uint16_t*)h->buf.shadow + t->offset;
+  return (const float*)h->buf.params + t->offset;
+}
+
+template <typename X = void>
+X* act(gpt_model* h, const Slice& s) { return (X*)((char*)h->buf.activations + s.off); }
+template <typename X = void>
+X* ws(gpt_model* h, const Slice& s) { return (X*)((char*)h->buf.workspace + s.off); }
+
+// Launch wrapper: brackets the call with events when the timer is on for `family`.
+template <typename F>
+int run(gpt_model* h, const char* family, const char* what, F&& f) {
+  Timer& tm = h->timer;
+  const bool timed = tm.on && (tm.family == family || (tm.family == "gemm" && std::strncmp(family, "gemm", 4) == 0) ||
+                               (tm.family == "gemm" && std::strcmp(family, "lm_head_fwd") == 0));
+  if (timed) {
+    if (tm.used == tm.events.size()) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess)
+        return fail(h, GPT_E_HIP, "hipEventCreate failed");
+      tm.events.push_back({a, b});
+    }
+    hipEventRecord(tm.events[tm.used].first, h->stream);
+  }
+  hipError_t e = f();
+  if (timed) {
+    hipEventRecord(tm.events[tm.used].second, h->stream);
+    tm.used++;
+  }
+  return hip_check(h, e, what);
+}
+
+#define RUN(fam, what, call)                                     \
+  do {                                                           \
+    int rc__ = run(h, fam, what, [&]() { return (call); });      \
+    if (rc__ != GPT_OK) return rc__;                             \
+  } while (0)
+
+GemmDesc gemm_desc(const void* A, int64_t lda, bool a_kc, const void* B, int64_t ldb, bool b_kc, void* C,
+                   int64_t ldc, int M, int N, int K, int epi) {
+  GemmDesc d;
+  std::memset(&d, 0, sizeof(d));
+  d.A = A; d.lda = lda; d.a_kc = a_kc;
+  d.B = B; d.ldb = ldb; d.b_kc = b_kc;
+  d.C = C; d.ldc = ldc; d.M = M; d.N = N; d.K = K; d.epi = epi;
+  return d;
+}
+
+int check_usable(gpt_model* h) {
+  if (!h) return GPT_E_INVAL;
+  if (h->sticky != GPT_OK) return h->sticky;
+  if (!h->bound) return fail(h, GPT_E_STATE, "buffers are not bound (call gpt_bind)");
+  return GPT_OK;
+}
+
+void plan(gpt_model* h) {
+  const int d = h->d, L = h->L, Vp = h->Vp;
+  // ---- parameters: 2-D tensors first (decayed), then 1-D tensors
+  size_t off = 0;
+  auto add = [&](const std::string& name, int64_t rows, int64_t cols, int ndim, int decay) {
+    Tensor t{name, off, ndim, rows, cols, decay};
+    h->tensors.push_back(t);
+    h->n_params += t.numel();
+    off = round_up(off + t.numel(), ALIGN_ELEMS);
+  };
+  add("wte", Vp, d, 2, 1);
+  add("wpe", h->Tmax, d, 2, 1);
+  for (int l = 0; l < L; l++) {
+    const std::string p = "h" + std::to_string(l) + ".";
+    add(p + "attn.w", 3 * d, d, 2, 1);
+    add(p + "proj.w", d, d, 2, 1);
+    add(p + "fc.w", 4 * d, d, 2, 1);
+    add(p + "fcproj.w", d, 4 * d, 2, 1);
+  }
+  h->n_decay = off;
+  for (int l = 0; l < L; l++) {
+    const std::string p = "h" + std::to_string(l) + ".";
+    add(p + "ln1.g", d, 1, 1, 0);
+    add(p + "ln1.b", d, 1, 1, 0);
+    add(p + "attn.b", 3 * d, 1, 1, 0);
+    add(p + "proj.b", d, 1, 1, 0);
+    add(p + "ln2.g", d, 1, 1, 0);
+    add(p + "ln2.b", d, 1, 1, 0);
+    add(p + "fc.b", 4 * d, 1, 1, 0);
+    add(p + "fcproj.b", d, 1, 1, 0);
+  }
+  add("lnf.g", d, 1, 1, 0);
+  add("lnf.b", d, 1, 1, 0);
+  h->n_flat = round_up(off, 256);
+
+  // ---- activations for the largest micro-batch
+  const size_t M = (size_t)h->Bmax * h->Tmax;
+  const size_t ob = h->op_size, fb = 4;
+  const size_t bht = (size_t)h->Bmax * h->H * h->Tmax;
+  Planner a;
+  h->layers.resize(L);
+  for (int l = 0; l < L; l++) {
+    LayerAct& la = h->layers[l];
+    la.x = a.take(M * d * fb);
+    la.xmid = a.take(M * d * fb);
+    la.ln1 = a.take(M * d * ob);
+    la.ln1_mean = a.take(M * fb);
+    la.ln1_rstd = a.take(M * fb);
+    la.qkv = a.take(M * 3 * d * ob);
+    la.att = a.take(M * d * ob);
+    la.lse = a.take(bht * fb);
+    la.ln2 = a.take(M * d * ob);
+    la.ln2_mean = a.take(M * fb);
+    la.ln2_rstd = a.take(M * fb);
+    la.u = a.take(M * 4 * d * fb);
+    la.h = a.take(M * 4 * d * ob);
+  }
+  h->x_final = a.take(M * d * fb);
+  h->lnf = a.take(M * d * ob);
+  h->lnf_mean = a.take(M * fb);
+  h->lnf_rstd = a.take(M * fb);
+  h->ldz = (int64_t)round_up((size_t)Vp, 64);
+  h->logits = a.take(M * (size_t)h->ldz * ob);
+  h->row_loss = a.take(M * fb);
+  h->tokens = a.take(M * 4);
+  h->targets = a.take(M * 4);
+  h->act_bytes = a.total;
+
+  // ---- workspace
+  Planner w;
+  h->dres = w.take(M * d * fb);
+  h->dres_op = w.take(h->bf16 ? M * d * ob : 0);
+  h->dln = w.take(M * d * fb);
+  h->du = w.take(M * 4 * d * ob);
+  h->dO = w.take(M * d * ob);
+  h->dqkv = w.take(M * 3 * d * ob);
+  h->attnD = w.take(bht * fb);
+  const size_t ln_blk = (M + LN_BWD_ROWS - 1) / LN_BWD_ROWS;
+  h->part_g = w.take(ln_blk * d * fb);
+  h->part_b = w.take(ln_blk * d * fb);
+  const size_t cs_blk = (M + COLSUM_ROWS - 1) / COLSUM_ROWS;
+  h->colsum_part = w.take(cs_blk * 4 * d * fb);
+  h->emb_keys = w.take((size_t)embed_bwd_sort_size((int)M) * 4);
+  h->emb_piece = w.take(M * d * fb);
+  h->norm_part = w.take(NORM_BLOCKS * fb);
+  h->opt = w.take(sizeof(OptState));
+  h->ws_bytes = w.total;
+}
+
+int colsum(gpt_model* h, const void* X, bool bf16_in, int64_t ldx, int M, int N, float* dst, float beta) {
+  float* part = ws<float>(h, h->colsum_part);
+  const int nblk = (M + COLSUM_ROWS - 1) / COLSUM_ROWS;
+  RUN("colsum", "colsum_partial", launch_colsum_partial(X, bf16_in, ldx, M, N, part, h->stream));
+  RUN("colsum", "colsum_final", launch_colsum_final(part, nblk, N, dst, beta, h->stream));
+  return GPT_OK;
+}
+
+int ln_bwd(gpt_model* h, const float* dy, const float* x, const float* mean, const float* rstd,
+           const std::string& gname, const std::string& bname, const float* dres, int M, float beta) {
+  float* pg = ws<float>(h, h->part_g);
+  float* pb = ws<float>(h, h->part_b);
+  void* dx_op = h->bf16 ? ws(h, h->dres_op) : nullptr;
+  RUN("layernorm", "layernorm_bwd",
+      launch_layernorm_bwd(dy, x, mean, rstd, P(h, gname), dres, ws<float>(h, h->dres), dx_op, h->bf16, pg, pb, M,
+                           h->d, h->stream));
+  const int nblk = (M + LN_BWD_ROWS - 1) / LN_BWD_ROWS;
+  RUN("colsum", "ln_dgamma", launch_colsum_final(pg, nblk, h->d, G(h, gname), beta, h->stream));
+  RUN("colsum", "ln_dbeta", launch_colsum_final(pb, nblk, h->d, G(h, bname), beta, h->stream));
+  return GPT_OK;
+}
+
+// Forward up to the logits for B x T tokens already copied into the arena.
+int forward_to_logits(gpt_model* h, int B, int T) {
+  const int d = h->d, M = B * T;
+  const bool bf = h->bf16;
+  hipStream_t s = h->stream;
+  const int32_t* tok = act<int32_t>(h, h->tokens);
+  RUN("embed", "embed_fwd", launch_embed_fwd(P(h, "wte"), P(h, "wpe"), tok, act<float>(h, h->layers[0].x), M, T, d, h->Vp, s));
+  for (int l = 0; l < h->L; l++) {
+    const LayerAct& la = h->layers[l];
+    const std::string p = "h" + std::to_string(l) + ".";
+    float* x = act<float>(h, la.x);
+    float* xmid = act<float>(h, la.xmid);
+    float* xnext = (l + 1 < h->L) ? act<float>(h, h->layers[l + 1].x) : act<float>(h, h->x_final);
+    RUN("layernorm", "ln1_fwd",
+        launch_layernorm_fwd(x, P(h, p + "ln1.g"), P(h, p + "ln1.b"), act(h, la.ln1), bf, act<float>(h, la.ln1_mean),
+                             act<float>(h, la.ln1_rstd), M, d, s));
+    {
+      GemmDesc g = gemm_desc(act(h, la.ln1), d, true, Wop(h, p + "attn.w"), d, true, act(h, la.qkv), 3 * d, M,
+                             3 * d, d, EPI_BIAS);
+      g.bias = P(h, p + "attn.b");
+      RUN("gemm_fwd", "qkv_fwd", launch_gemm(g, bf, s));
+    }
+    RUN("attn_fwd", "attn_fwd", launch_attn_fwd(act(h, la.qkv), act(h, la.att), act<float>(h, la.lse), bf, B, T, h->H, h->hd, s));
+    {
+      GemmDesc g = gemm_desc(act(h, la.att), d, true, Wop(h, p + "proj.w"), d, true, xmid, d, M, d, d,
+                             EPI_BIAS_RESID);
+      g.bias = P(h, p + "proj.b");
+      g.resid = x;
+      g.ldr = d;
+      RUN("gemm_fwd", "proj_fwd", launch_gemm(g, bf, s));
+    }
+    RUN("layernorm", "ln2_fwd",
+        launch_layernorm_fwd(xmid, P(h, p + "ln2.g"), P(h, p + "ln2.b"), act(h, la.ln2), bf,
+                             act<float>(h, la.ln2_mean), act<float>(h, la.ln2_rstd), M, d, s));
+    {
+      GemmDesc g = gemm_desc(act(h, la.ln2), d, true, Wop(h, p + "fc.w"), d, true, act(h, la.h), 4 * d, M, 4 * d,
+                             d, EPI_BIAS_GELU);
+      g.bias = P(h, p + "fc.b");
+      g.aux = act<float>(h, la.u);
+      g.ldaux = 4 * d;
+      RUN("gemm_fwd", "fc_fwd", launch_gemm(g, bf, s));
+    }
+    {
+      GemmDesc g = gemm_desc(act(h, la.h), 4 * d, true, Wop(h, p + "fcproj.w"), 4 * d, true, xnext, d, M, d,
+                             4 * d, EPI_BIAS_RESID);
+      g.bias = P(h, p + "fcproj.b");
+      g.resid = xmid;
+      g.ldr = d;
+      RUN("gemm_fwd", "fcproj_fwd", launch_gemm(g, bf, s));
+    }
+  }
+  RUN("layernorm", "lnf_fwd",
+      launch_layernorm_fwd(act<float>(h, h->x_final), P(h, "lnf.g"), P(h, "lnf.b"), act(h, h->lnf), bf,
+                           act<float>(h, h->lnf_mean), act<float>(h, h->lnf_rstd), M, d, s));
+  {
+    GemmDesc g = gemm_desc(act(h, h->lnf), d, true, Wop(h, "wte"), d, true, act(h, h->logits), h->ldz, M, h->Vp, d,
+                           EPI_STORE);
+    RUN("lm_head_fwd", "lm_head_fwd", launch_gemm(g, bf, s));
+  }
+  return GPT_OK;
+}
+
+int copy_ids(gpt_model* h, const int32_t* src, const Slice& dst, int M) {
+  return hip_check(h, hipMemcpyAsync(act(h, dst), src, (size_t)M * 4, hipMemcpyDeviceToDevice, h->stream),
+                   "copy token ids");
+}
+
+int check_shape(gpt_model* h, int B, int T) {
+  if (B < 1 || T < 1) return fail(h, GPT_E_INVAL, "B and T must be >= 1");
+  if (B > h->Bmax || T > h->Tmax)
+    return fail(h, GPT_E_SEQ_TOO_LONG, "B " + std::to_string(B) + " x T " + std::to_string(T) +
+                                           " exceeds batch " + std::to_string(h->Bmax) + " x block_size " +
+                                           std::to_string(h->Tmax));
+  return GPT_OK;
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------- ABI
+extern "C" {
+
+const char* gpt_last_error(const gpt_model* h) {
+  if (h) return h->err.c_str();
+  return g_create_error.c_str();
+}
+
+int gpt_create(const gpt_config* cfg, gpt_model** out) {
+  if (!out) return fail(nullptr, GPT_E_INVAL, "out is NULL");
+  *out = nullptr;
+  if (!cfg) return fail(nullptr, GPT_E_INVAL, "cfg is NULL");
+  const gpt_config& c = *cfg;
+  if (c.vocab_size < 1 || c.padded_vocab < c.vocab_size) return fail(nullptr, GPT_E_INVAL, "need 1 <= vocab_size <= padded_vocab");
+  if (c.n_layer < 1 || c.n_head < 1 || c.n_embd < 1 || c.block_size < 1 || c.batch < 1 || c.grad_accum < 1)
+    return fail(nullptr, GPT_E_INVAL, "n_layer, n_head, n_embd, block_size, batch and grad_accum must be >= 1");
+  if (c.n_embd % c.n_head != 0) return fail(nullptr, GPT_E_INVAL, "n_embd must be a multiple of n_head");
+  if (c.n_embd / c.n_head > 64) return fail(nullptr, GPT_E_UNSUPPORTED, "head_dim above 64 is not implemented");
+  if (c.n_embd > 1024) return fail(nullptr, GPT_E_UNSUPPORTED, "n_embd above 1024 is not implemented");
+  if (c.n_embd % 4 != 0) return fail(nullptr, GPT_E_UNSUPPORTED, "n_embd must be a multiple of 4");
+  if (c.precision != GPT_PREC_FP32 && c.precision != GPT_PREC_BF16) return fail(nullptr, GPT_E_INVAL, "unknown precision");
+  if (c.dropout != 0.0f) return fail(nullptr, GPT_E_UNSUPPORTED, "dropout must be 0");
+  if (c.flags != 0) return fail(nullptr, GPT_E_INVAL, "flags must be 0");
+  const int64_t M = (int64_t)c.batch * c.block_size;
+  if (M > 32768) return fail(nullptr, GPT_E_UNSUPPORTED, "batch * block_size above 32768 is not implemented");
+  {
+    int sh = 0;
+    while ((1ll << sh) < (M < 2 ? 2 : M)) sh++;
+    if (((uint64_t)c.padded_vocab << sh) > 0xFFFFFFFFull)
+      return fail(nullptr, GPT_E_UNSUPPORTED, "padded_vocab * batch * block_size too large for the embedding sort");
+  }
+  gpt_model* h = new gpt_model();
+  h->cfg = c;
+  h->bf16 = c.precision == GPT_PREC_BF16;
+  h->d = c.n_embd;
+  h->H = c.n_head;
+  h->hd = c.n_embd / c.n_head;
+  h->L = c.n_layer;
+  h->V = c.vocab_size;
+  h->Vp = c.padded_vocab;
+  h->Tmax = c.block_size;
+  h->Bmax = c.batch;
+  h->A = c.grad_accum;
+  h->op_size = h->bf16 ? 2 : 4;
+  plan(h);
+  *out = h;
+  return GPT_OK;
+}
+
+void gpt_destroy(gpt_model* h) {
+  if (!h) return;
+  for (auto& e : h->timer.events) {
+    hipEventDestroy(e.first);
+    hipEventDestroy(e.second);
+  }
+  delete h;
+}
+
+int gpt_get_sizes(const gpt_model* h, gpt_sizes* out) {
+  if (!h || !out) return GPT_E_INVAL;
+  out->n_params = h->n_params;
+  out->n_flat = h->n_flat;
+  out->param_bytes = out->grad_bytes = out->m_bytes = out->v_bytes = h->n_flat * 4;
+  out->shadow_bytes = h->bf16 ? h->n_flat * 2 : 0;
+  out->activation_bytes = h->act_bytes;
+  out->workspace_bytes = h->ws_bytes;
+  return GPT_OK;
+}
+
+int gpt_num_tensors(const gpt_model* h) { return h ? (int)h->tensors.size() : GPT_E_INVAL; }
+
+int gpt_tensor_info_at(const gpt_model* h, int i, gpt_tensor_info* out) {
+  if (!h || !out || i < 0 || i >= (int)h->tensors.size()) return GPT_E_INVAL;
+  const Tensor& t = h->tensors[i];
+  std::memset(out, 0, sizeof(*out));
+  std::snprintf(out->name, sizeof(out->name), "%s", t.name.c_str());
+  out->offset = t.offset;
+  out->ndim = t.ndim;
+  out->shape[0] = t.rows;
+  out->shape[1] = t.cols;
+  out->decay = t.decay;
+  return GPT_OK;
+}
+
+int gpt_bind(gpt_model* h, const gpt_buffers* bufs, void* hip_stream) {
+  if (!h || !bufs) return fail(h, GPT_E_INVAL, "NULL handle or buffers");
+  if (!bufs->params || !bufs->grads || !bufs->m || !bufs->v || !bufs->activations || !bufs->workspace ||
+      (h->bf16 && !bufs->shadow))
+    return fail(h, GPT_E_INVAL, "a required buffer is NULL");
+  const void* ptrs[] = {bufs->params, bufs->grads, bufs->m, bufs->v, bufs->activations, bufs->workspace};
+  for (const void* p : ptrs)
+    if ((uintptr_t)p % ALIGN_BYTES != 0) return fail(h, GPT_E_INVAL, "buffers must be 256-byte aligned");
+  if (h->bf16 && (uintptr_t)bufs->shadow % ALIGN_BYTES != 0) return fail(h, GPT_E_INVAL, "shadow must be 256-byte aligned");
+  h->buf = *bufs;
+  h->stream = (hipStream_t)hip_stream;
+  h->bound = true;
+  h->fwd_pending = false;
+  h->grads_fresh = true;
+  return GPT_OK;
+}
+
+int gpt_init_state(gpt_model* h) {
+  int rc = check_usable(h);
+  if (rc) return rc;
+  hipStream_t s = h->stream;
+  RUN("init", "zero grads", launch_zero(h->buf.grads, h->n_flat, s));
+  RUN("init", "zero m", launch_zero(h->buf.m, h->n_flat, s));
+  RUN("init", "zero v", launch_zero(h->buf.v, h->n_flat, s));
+  RUN("init", "zero optimizer state", launch_zero(ws(h, h->opt), sizeof(OptState) / 4, s));
+  if (h->bf16) RUN("init", "bf16 shadow", launch_cast_bf16((const float*)h->buf.params, h->buf.shadow, h->n_flat, s));
+  h->grads_fresh = true;
+  h->fwd_pending = false;
+  return GPT_OK;
+}
+
+int gpt_forward_loss(gpt_model* h, const int32_t* d_tokens, const int32_t* d_targets, int32_t B, int32_t T,
+                     float* d_loss) {
+  int rc = check_usable(h);
+  if (rc) return rc;
+  if (!d_tokens || !d_targets) return fail(h, GPT_E_INVAL, "NULL token or target pointer");
+  if ((rc = check_shape(h, B, T))) return rc;
+  const int M = B * T;
+  if ((rc = copy_ids(h, d_tokens, h->tokens, M))) return rc;
+  if ((rc = copy_ids(h, d_targets, h->targets, M))) return rc;
+  h->fwd_pending = false;
+  if ((rc = forward_to_logits(h, B, T))) return rc;
+  const float scale = (float)(1.0 / ((double)M * (double)h->A));
+  RUN("xent", "xent", launch_xent(act(h, h->logits), h->bf16, h->ldz, act<int32_t>(h, h->targets),
+                                   act<float>(h, h->row_loss), M, h->Vp, scale, h->stream));
+  if (d_loss) RUN("xent", "loss_mean", launch_mean(act<float>(h, h->row_loss), M, d_loss, h->stream));
+  h->fwd_pending = true;
+  h->cur_B = B;
+  h->cur_T = T;
+  return GPT_OK;
+}
+
+int gpt_forward_logits(gpt_model* h, const int32_t* d_tokens, int32_t B, int32_t T, float* d_logits) {
+  int rc = check_usable(h);
+  if (rc) return rc;
+  if (!d_tokens || !d_logits) return fail(h, GPT_E_INVAL, "NULL pointer");
+  if ((rc = check_shape(h, B, T))) return rc;
+  const int M = B * T;
+  h->fwd_pending = false;
+  if ((rc = copy_ids(h, d_tokens, h->tokens, M))) return rc;
+  if ((rc = forward_to_logits(h, B, T))) return rc;
+  RUN("copy", "logits_to_f32",
+      launch_rows_to_f32(act(h, h->logits), h->bf16, h->ldz, M, h->Vp, d_logits, h->stream));
+  return GPT_OK;
+}
+
+int gpt_backward(gpt_model* h) {
+  int rc = check_usable(h);
+  if (rc) return rc;
+  if (!h->fwd_pending) return fail(h, GPT_E_STATE, "gpt_backward needs a preceding gpt_forward_loss");
+  const int B = h->cur_B, T = h->cur_T, M = B * T, d = h->d;
+  const bool bf = h->bf16;
+  hipStream_t s = h->stream;
+  const float beta = h->grads_fresh ? 0.f : 1.f;
+  float* dres = ws<float>(h, h->dres);
+  const void* dres_opnd = bf ? ws(h, h->dres_op) : (const void*)dres;   // GEMM operand view of dres
+  float* dln = ws<float>(h, h->dln);
+  void* du = ws(h, h->du);
+  void* dO = ws(h, h->dO);
+  void* dqkv = ws(h, h->dqkv);
+
+  // lm_head (tied): dwte = dlogits^T lnf; dlnf = dlogits wte
+  {
+    GemmDesc g = gemm_desc(act(h, h->logits), h->ldz, false, act(h, h->lnf), d, false, G(h, "wte"), d, h->Vp, d, M,
+                           EPI_ACC);
+    g.beta = beta;
+    RUN("gemm_wgrad", "lm_head_wgrad", launch_gemm(g, bf, s));
+    GemmDesc g2 = gemm_desc(act(h, h->logits), h->ldz, true, Wop(h, "wte"), d, false, dln, d, M, d, h->Vp, EPI_F32);
+    RUN("gemm_dgrad", "lm_head_dgrad", launch_gemm(g2, bf, s));
+  }
+  if ((rc = ln_bwd(h, dln, act<float>(h, h->x_final), act<float>(h, h->lnf_mean), act<float>(h, h->lnf_rstd),
+                   "lnf.g", "lnf.b", nullptr, M, beta)))
+    return rc;
+
+  for (int l = h->L - 1; l >= 0; l--) {
+    const LayerAct& la = h->layers[l];
+    const std::string p = "h" + std::to_string(l) + ".";
+    // ---- MLP: x_{l+1} = xmid + gelu(LN2(xmid) Wfc^T + bfc) Wp^T + bp ; dres holds d x_{l+1}
+    {
+      GemmDesc g = gemm_desc(dres_opnd, d, true, Wop(h, p + "fcproj.w"), 4 * d, false, du, 4 * d, M, 4 * d, d,
+                             EPI_GELU_BWD);
+      g.aux = act<float>(h, la.u);
+      g.ldaux = 4 * d;
+      RUN("gemm_dgrad", "fcproj_dgrad", launch_gemm(g, bf, s));
+      GemmDesc gw = gemm_desc(dres_opnd, d, false, act(h, la.h), 4 * d, false, G(h, p + "fcproj.w"), 4 * d, d, 4 * d,
+                              M, EPI_ACC);
+      gw.beta = beta;
+      RUN("gemm_wgrad", "fcproj_wgrad", launch_gemm(gw, bf, s));
+      if ((rc = colsum(h, dres, false, d, M, d, G(h, p + "fcproj.b"), beta))) return rc;
+      GemmDesc g2 = gemm_desc(du, 4 * d, true, Wop(h, p + "fc.w"), d, false, dln, d, M, d, 4 * d, EPI_F32);
+      RUN("gemm_dgrad", "fc_dgrad", launch_gemm(g2, bf, s));
+      GemmDesc gw2 = gemm_desc(du, 4 * d, false, act(h, la.ln2), d, false, G(h, p + "fc.w"), d, 4 * d, d, M, EPI_ACC);
+      gw2.beta = beta;
+      RUN("gemm_wgrad", "fc_wgrad", launch_gemm(gw2, bf, s));
+      if ((rc = colsum(h, du, bf, 4 * d, M, 4 * d, G(h, p + "fc.b"), beta))) return rc;
+      if ((rc = ln_bwd(h, dln, act<float>(h, la.xmid), act<float>(h, la.ln2_mean), act<float>(h, la.ln2_rstd),
+                       p + "ln2.g", p + "ln2.b", dres, M, beta)))
+        return rc;
+    }
+    // ---- attention: xmid = x + attn(LN1(x)) Wo^T + bo ; dres now holds d xmid
+    {
+      GemmDesc g = gemm_desc(dres_opnd, d, true, Wop(h, p + "proj.w"), d, false, dO, d, M, d, d, EPI_STORE);
+      RUN("gemm_dgrad", "proj_dgrad", launch_gemm(g, bf, s));
+      GemmDesc gw = gemm_desc(dres_opnd, d, false, act(h, la.att), d, false, G(h, p + "proj.w"), d, d, d, M, EPI_ACC);
+      gw.beta = beta;
+      RUN("gemm_wgrad", "proj_wgrad", launch_gemm(gw, bf, s));
+      if ((rc = colsum(h, dres, false, d, M, d, G(h, p + "proj.b"), beta))) return rc;
+      RUN("attn_bwd", "attn_bwd",
+          launch_attn_bwd(act(h, la.qkv), act(h, la.att), dO, act<float>(h, la.lse), ws<float>(h, h->attnD), dqkv, bf,
+                          B, T, h->H, h->hd, s));
+      GemmDesc g2 = gemm_desc(dqkv, 3 * d, true, Wop(h, p + "attn.w"), d, false, dln, d, M, d, 3 * d, EPI_F32);
+      RUN("gemm_dgrad", "qkv_dgrad", launch_gemm(g2, bf, s));
+      GemmDesc gw2 = gemm_desc(dqkv, 3 * d, false, act(h, la.ln1), d, false, G(h, p + "attn.w"), d, 3 * d, d, M,
+                               EPI_ACC);
+      gw2.beta = beta;
+      RUN("gemm_wgrad", "qkv_wgrad", launch_gemm(gw2, bf, s));
+      if ((rc = colsum(h, dqkv, bf, 3 * d, M, 3 * d, G(h, p + "attn.b"), beta))) return rc;
+      if ((rc = ln_bwd(h, dln, act<float>(h, la.x), act<float>(h, la.ln1_mean), act<float>(h, la.ln1_rstd),
+                       p + "ln1.g", p + "ln1.b", dres, M, beta)))
+        return rc;
+    }
+  }
+  // ---- embeddings: dres holds d x0
+  if (h->grads_fresh && T < h->Tmax) {
+    float* wpe_tail = G(h, "wpe") + (size_t)T * d;
+    RUN("embed", "zero wpe tail", launch_zero(wpe_tail, (size_t)(h->Tmax - T) * d, s));
+  }
+  EmbedBwdScratch scr{ws<uint32_t>(h, h->emb_keys), ws<float>(h, h->emb_piece)};
+  RUN("embed", "embed_bwd",
+      launch_embed_bwd(dres, act<int32_t>(h, h->tokens), G(h, "wte"), G(h, "wpe"), beta, B, T, d, h->Vp, scr, s));
+  h->grads_fresh = false;
+  h->fwd_pending = false;
+  return GPT_OK;
+}
+
+int gpt_zero_grad(gpt_model* h) {
+  if (!h) return GPT_E_INVAL;
+  h->grads_fresh = true;
+  return GPT_OK;
+}
+
+int gpt_adamw_step(gpt_model* h, float lr, float beta1, float beta2, float eps, float weight_decay, float clip,
+                   float* d_grad_norm) {
+  int rc = check_usable(h);
+  if (rc) return rc;
+  if (!(beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f && eps >= 0.f && std::isfinite(lr) &&
+        std::isfinite(weight_decay) && std::isfinite(clip)))
+    return fail(h, GPT_E_INVAL, "invalid AdamW hyper-parameters");
+  if (h->grads_fresh) return fail(h, GPT_E_STATE, "gpt_adamw_step needs at least one gpt_backward since the last step");
+  hipStream_t s = h->stream;
+  float* part = ws<float>(h, h->norm_part);
+  OptState* st = ws<OptState>(h, h->opt);
+  RUN("adamw", "grad_sumsq", launch_sumsq_partial((const float*)h->buf.grads, h->n_flat, part, s));
+  RUN("adamw", "opt_prepare", launch_opt_prepare(part, st, clip, beta1, beta2, d_grad_norm, s));
+  RUN("adamw", "adamw",
+      launch_adamw((float*)h->buf.params, (const float*)h->buf.grads, (float*)h->buf.m, (float*)h->buf.v,
+                   h->bf16 ? h->buf.shadow : nullptr, h->n_flat, h->n_decay, st, lr, beta1, beta2, eps, weight_decay,
+                   s));
+  h->grads_fresh = true;
+  return GPT_OK;
+}
+
+int gpt_sync(gpt_model* h) {
+  if (!h) return GPT_E_INVAL;
+  hipError_t e = hipStreamSynchronize(h->stream);
+  int rc = h->sticky;
+  h->sticky = GPT_OK;
+  if (e != hipSuccess) return fail(h, GPT_E_HIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
+  if (rc != GPT_OK) return rc;
+  if (h->bound) {
+    OptState st;
+    e = hipMemcpy(&st, ws(h, h->opt), sizeof(st), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(h, GPT_E_HIP, std::string("read optimizer state: ") + hipGetErrorString(e));
+    if (st.nonfinite) {
+      int32_t zero = 0;
+      e = hipMemcpy((char*)ws(h, h->opt) + offsetof(OptState, nonfinite), &zero, 4, hipMemcpyHostToDevice);
+      h->err = "non-finite gradient norm: the AdamW update was skipped";
+      return GPT_E_NONFINITE;
+    }
+  }
+  return GPT_OK;
+}
+
+int gpt_get_step(gpt_model* h, int64_t* t) {
+  int rc = check_usable(h);
+  if (rc) return rc;
+  if (!t) return fail(h, GPT_E_INVAL, "NULL output");
+  OptState st;
+  hipError_t e = hipStreamSynchronize(h->stream);
+  if (e == hipSuccess) e = hipMemcpy(&st, ws(h, h->opt), sizeof(st), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_check(h, e, "read optimizer state");
+  *t = st.t;
+  return GPT_OK;
+}
+
+int gpt_debug_copy(gpt_model* h, const char* what, int32_t layer, void* d_dst, size_t bytes) {
+  int rc = check_usable(h);
+  if (rc) return rc;
+  if (!what || !d_dst) return fail(h, GPT_E_INVAL, "NULL argument");
+  const size_t M = (size_t)h->cur_B * h->cur_T;
+  const std::string w(what);
+  const void* src = nullptr;
+  size_t n = 0;
+  const size_t d = h->d;
+  if (w == "x") {
+    if (layer < 0 || layer > h->L) return fail(h, GPT_E_INVAL, "layer out of range");
+    src = layer == h->L ? act(h, h->x_final) : act(h, h->layers[layer].x);
+    n = M * d * 4;
+  } else if (w == "qkv" || w == "attn" || w == "h" || w == "lse" || w == "u") {
+    if (layer < 0 || layer >= h->L) return fail(h, GPT_E_INVAL, "layer out of range");
+    const LayerAct& la = h->layers[layer];
+    if (w == "qkv") { src = act(h, la.qkv); n = M * 3 * d * h->op_size; }
+    if (w == "attn") { src = act(h, la.att); n = M * d * h->op_size; }
+    if (w == "h") { src = act(h, la.h); n = M * 4 * d * h->op_size; }
+    if (w == "u") { src = act(h, la.u); n = M * 4 * d * 4; }
+    if (w == "lse") { src = act(h, la.lse); n = (size_t)h->cur_B * h->H * h->cur_T * 4; }
+  } else {
+    return fail(h, GPT_E_INVAL, "unknown activation '" + w + "'");
+  }
+  if (M == 0) return fail(h, GPT_E_STATE, "no forward has run");
+  if (bytes != n) return fail(h, GPT_E_INVAL, "size mismatch: expected " + std::to_string(n) + " bytes");
+  hipError_t e = hipMemcpyAsync(d_dst, src, n, hipMemcpyDeviceToDevice, h->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
+  return hip_check(h, e, "debug copy");
+}
+
+int gpt_timer_enable(gpt_model* h, const char* family) {
+  if (!h || !family) return GPT_E_INVAL;
+  h->timer.on = true;
+  h->timer.family = family;
+  h->timer.used = 0;
+  return GPT_OK;
+}
+
+int gpt_timer_disable(gpt_model* h) {
+  if (!h) return GPT_E_INVAL;
+  h->timer.on = false;
+  return GPT_OK;
+}
+
+int gpt_timer_read(gpt_model* h, double* total_ms, int64_t* launches) {
+  if (!h || !total_ms || !launches) return GPT_E_INVAL;
+  hipError_t e = hipStreamSynchronize(h->stream);
+  if (e != hipSuccess) return hip_check(h, e, "timer sync");
+  double tot = 0.0;
+  for (size_t i = 0; i < h->timer.used; i++) {
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, h->timer.events[i].first, h->timer.events[i].second);
+    if (e != hipSuccess) return hip_check(h, e, "hipEventElapsedTime");
+    tot += ms;
+  }
+  *total_ms = tot;
+  *launches = (int64_t)h->timer.used;
+  return GPT_OK;
+}
+
+}  // extern "C"
