@@ -1,0 +1,184 @@
+"""Training-step throughput of the gfx950 GPT path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_124m]
+
+One step = A x (forward_loss + backward) on micro-batches of B x T synthetic
+token ids, then one AdamW update (global-norm clip, decoupled weight decay).
+The default workload is GPT-2 124M (12 layers, 12 heads, n_embd 768, vocab
+50257 padded to 50304), B 12, T 1024, A 5, bf16 GEMM/attention operands with
+fp32 master weights: the configuration of the nanoGPT pages' GPT-2
+reproduction with gradient accumulation. Inputs are generated on the host
+and copied to the device before timing; the timed region holds only the
+library's kernels. Prints one JSON line.
+
+MFU uses the conventional count of 6N + 12 L d T FLOPs per token (N = parameters
+without the position embedding) against 2.5 PFLOP/s dense bf16.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5e15        # dense bf16 MFMA, FLOP/s
+PEAK_FP32 = 157.3e12      # dense fp32 MFMA
+PEAK_HBM = 8.0e12         # bytes/s
+
+
+def flops_per_token(cfg) -> float:
+    d, L, T, V = cfg.n_embd, cfg.n_layer, cfg.block_size, cfg.padded_vocab
+    n_params = V * d + T * d + L * (12 * d * d + 13 * d) + 2 * d
+    N = n_params - T * d
+    return 6.0 * N + 12.0 * L * d * T
+
+
+def cpu_baseline(cfg, params, batches, n_seq: int):
+    """The oracle, as it stands, on n_seq sequences of the same workload (float64)."""
+    from oracle import gpt_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    tok, tgt = batches[0]
+    tok, tgt = tok[:n_seq], tgt[:n_seq]
+    t0 = time.perf_counter()
+    O.microbatch(params, tok, tgt, cfg, grad_scale=1.0 / tok.size)
+    dt = time.perf_counter() - t0
+    return {"value": round(tok.size / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_seq} sequence(s) x {tok.shape[1]} tokens, forward + backward in float64 "
+                      f"({dt:.1f} s); AdamW excluded"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gpt2_124m")
+    ap.add_argument("--precision", default="bf16", choices=["bf16", "fp32"])
+    ap.add_argument("--kernel", default="lm_head_fwd",
+                    help="kernel family whose launches are timed for the roofline line")
+    ap.add_argument("--cpu-seqs", type=int, default=1, help="sequences in the oracle's timed sample (0: skip)")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the data-parallel all-reduce "
+              f"is not part of this build", file=sys.stderr)
+        return 2
+
+    import torch
+    from transformer_lm_gpt_amd import workloads as W
+    from transformer_lm_gpt_amd.binding import GPT
+
+    cfg = W.CONFIGS[a.workload]
+    B, T, A = cfg.batch, cfg.block_size, cfg.grad_accum
+    torch.cuda.set_device(0)
+    drng, wrng = W.rngs()
+    params = W.init_params(cfg, wrng)
+    n_steps = a.warmup + a.steps
+    host_batches = [W.make_step_batches(cfg, drng) for _ in range(min(n_steps, 4))]
+    dev_batches = [[(torch.from_numpy(t).cuda(), torch.from_numpy(y).cuda()) for t, y in s] for s in host_batches]
+
+    gpu = GPT(cfg, a.precision, device="cuda:0")
+    gpu.load_params(params)
+    loss = torch.zeros(A, dtype=torch.float32, device="cuda:0")
+    norm = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+
+    def step(i):
+        for j, (t, y) in enumerate(dev_batches[i % len(dev_batches)]):
+            gpu.forward_loss(t, y, loss_out=loss[j:j + 1])
+            gpu.backward()
+        gpu.adamw_step(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.grad_clip, norm_out=norm)
+
+    for i in range(a.warmup):
+        step(i)
+    gpu.sync()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    gpu.timer_enable(a.kernel)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(a.steps):
+        step(a.warmup + i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms, kern_n = gpu.timer_read()
+    gpu.timer_disable()
+    gpu.sync()
+    step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(a.steps)]
+    total_ms = ev[0].elapsed_time(ev[-1])
+    final_loss = float(loss.mean().item())
+    if not math.isfinite(final_loss):
+        raise RuntimeError(f"non-finite loss {final_loss}")
+
+    tokens_per_step = B * T * A
+    ms = total_ms / a.steps
+    tps = tokens_per_step / (ms / 1e3)
+    ftok = flops_per_token(cfg)
+    peak = PEAK_BF16 if a.precision == "bf16" else PEAK_FP32
+    mfu = tps * ftok / peak
+    causal_ftok = ftok - 6.0 * cfg.n_layer * cfg.n_embd * T
+
+    # roofline of the timed kernel family
+    roof = None
+    if kern_n:
+        avg_ms = kern_ms / kern_n
+        if a.kernel == "lm_head_fwd":
+            work = 2.0 * B * T * cfg.padded_vocab * cfg.n_embd          # FLOPs per launch
+            roof = {"kernel": "lm_head_fwd (gemm_kernel<bf16, k-contig, k-contig, store>)", "bound": "mfma",
+                    "achieved": round(work / (avg_ms / 1e3) / 1e12, 2), "peak": peak / 1e12, "unit": "TFLOP/s",
+                    "frac": round(work / (avg_ms / 1e3) / peak, 4), "traffic": None,
+                    "avg_launch_ms": round(avg_ms, 4), "launches": kern_n,
+                    "work_per_launch": f"2*M*Vp*d = {work:.4g} FLOP, M = {B * T}"}
+        else:
+            roof = {"kernel": a.kernel, "avg_launch_ms": round(avg_ms, 4), "launches": kern_n}
+
+    cpu = None
+    if a.cpu_seqs > 0:
+        cpu = cpu_baseline(cfg, params, host_batches[0], a.cpu_seqs)
+
+    out = {
+        "metric": "training tokens/sec and MFU, GPT-2 124M fwd+bwd+AdamW, T=1024, 1 MI355X",
+        "value": round(tps, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": a.precision,
+        "data": "synthetic (seeded Zipf(1.07) ids over 50257, random-init weights N(0,0.02))",
+        "config": {"workload": f"{cfg.name}: L{cfg.n_layer} H{cfg.n_head} d{cfg.n_embd} V{cfg.vocab_size}"
+                               f"(pad {cfg.padded_vocab}) B{B} T{T} accum{A}",
+                   "global_batch": B * A, "seq_len": T, "tokens_per_step": tokens_per_step},
+        "mfu": round(mfu, 4),
+        "mfu_causal_exact": round(tps * causal_ftok / peak, 4),
+        "achieved_tflops": round(tps * ftok / 1e12, 1),
+        "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 3) for q in (10, 50, 90)],
+        "wall_s": round(wall, 3),
+        "final_loss": round(final_loss, 5),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    gpu.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -172,17 +172,29 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv
 }
 
 // ----------------------------------------------------------------------------- backward
+// D[b*H + h, t] = sum_c dO[b, t, h, c] O[b, t, h, c]; one thread per (b, t, h), heads
+// fastest so that a wavefront reads whole rows; 16-byte loads when hd allows.
 template <typename T>
 __global__ void attn_bwd_D_kernel(const T* __restrict__ o, const T* __restrict__ dout, float* __restrict__ D,
                                   int B, int Tn, int H, int hd) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;   // over B*H*T
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;   // over B*T*H, h fastest
   if (i >= B * H * Tn) return;
-  const int t = i % Tn, bh = i / Tn, b = bh / H, h = bh % H;
-  const int d = H * hd;
-  const int64_t off = ((int64_t)b * Tn + t) * d + h * hd;
+  const int h = i % H, bt = i / H, t = bt % Tn, b = bt / Tn;
+  const int64_t off = (int64_t)bt * H * hd + h * hd;
+  constexpr int VW = 16 / sizeof(T);
   float s = 0.f;
-  for (int c = 0; c < hd; c++) s += to_f32(dout[off + c]) * to_f32(o[off + c]);
-  D[i] = s;
+  if (hd % VW == 0) {
+    typedef T vec __attribute__((ext_vector_type(VW)));
+    for (int c = 0; c < hd; c += VW) {
+      const vec a = *(const vec*)(dout + off + c);
+      const vec bv = *(const vec*)(o + off + c);
+#pragma unroll
+      for (int e = 0; e < VW; e++) s += to_f32(a[e]) * to_f32(bv[e]);
+    }
+  } else {
+    for (int c = 0; c < hd; c++) s += to_f32(dout[off + c]) * to_f32(o[off + c]);
+  }
+  D[((int64_t)b * H + h) * Tn + t] = s;
 }
 
 template <typename T, int HDP>

@@ -175,7 +175,43 @@ struct GemmArgs {
   float* aux; int64_t ldaux;
   float beta;
   int a_vec, b_vec;
+  int kchunk;          // contraction length per split (gridDim.z splits)
+  float* part;         // split partials [gridDim.z, M, N] (EPI_ACC with gridDim.z > 1)
 };
+
+template <int EPI>
+__device__ inline float epi_bias(const GemmArgs& p, int col) {
+  if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU) return p.bias[col];
+  return 0.f;
+}
+
+// One output element: the fused epilogue of every GEMM of the step.
+template <typename T, int EPI>
+__device__ inline void epi_store(const GemmArgs& p, int row, int col, float v, float bias) {
+  const int64_t ci = (int64_t)row * p.ldc + col;
+  if constexpr (EPI == EPI_STORE) {
+    ((T*)p.C)[ci] = from_f32<T>(v);
+  } else if constexpr (EPI == EPI_BIAS) {
+    ((T*)p.C)[ci] = from_f32<T>(v + bias);
+  } else if constexpr (EPI == EPI_BIAS_RESID) {
+    ((float*)p.C)[ci] = p.resid[(int64_t)row * p.ldr + col] + (v + bias);
+  } else if constexpr (EPI == EPI_BIAS_GELU) {
+    const float u = v + bias;
+    p.aux[(int64_t)row * p.ldaux + col] = u;
+    ((T*)p.C)[ci] = from_f32<T>(gelu_f(u));
+  } else if constexpr (EPI == EPI_F32) {
+    ((float*)p.C)[ci] = v;
+  } else if constexpr (EPI == EPI_GELU_BWD) {
+    ((T*)p.C)[ci] = from_f32<T>(v * gelu_grad_f(p.aux[(int64_t)row * p.ldaux + col]));
+  } else {  // EPI_ACC
+    if (gridDim.z > 1) {
+      p.part[((int64_t)blockIdx.z * p.M + row) * p.N + col] = v;
+    } else {
+      float* c = (float*)p.C + ci;
+      *c = (p.beta != 0.f ? p.beta * *c : 0.f) + v;
+    }
+  }
+}
 
 template <typename T, bool AK, bool BK_, int EPI>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
@@ -200,9 +236,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
 
   Loader<T, AK> la;
   Loader<T, BK_> lb;
-  const int nk = (p.K + BK - 1) / BK;
-  la.load(A, p.lda, m0, p.M, 0, p.K, p.a_vec);
-  lb.load(B, p.ldb, n0, p.N, 0, p.K, p.b_vec);
+  const int kb = blockIdx.z * p.kchunk;
+  const int ke = min(p.K, kb + p.kchunk);
+  const int nk = (ke - kb + BK - 1) / BK;
+  la.load(A, p.lda, m0, p.M, kb, ke, p.a_vec);
+  lb.load(B, p.ldb, n0, p.N, kb, ke, p.b_vec);
   la.store(smem);
   lb.store(smem + 2 * TILE);
   __syncthreads();
@@ -210,8 +248,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
   for (int kt = 0; kt < nk; kt++) {
     const int cur = kt & 1;
     if (kt + 1 < nk) {
-      la.load(A, p.lda, m0, p.M, (kt + 1) * BK, p.K, p.a_vec);
-      lb.load(B, p.ldb, n0, p.N, (kt + 1) * BK, p.K, p.b_vec);
+      la.load(A, p.lda, m0, p.M, kb + (kt + 1) * BK, ke, p.a_vec);
+      lb.load(B, p.ldb, n0, p.N, kb + (kt + 1) * BK, ke, p.b_vec);
     }
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; kk++) {
@@ -239,34 +277,230 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
     for (int j = 0; j < 4; j++) {
       const int col = n0 + wn * 64 + j * 16 + (lane & 15);
       if (col >= p.N) continue;
-      float bias = 0.f;
-      if (EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU) bias = p.bias[col];
+      const float bias = epi_bias<EPI>(p, col);
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         const int row = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
-        if (row >= p.M) continue;
-        float v = acc[i][j][e];
-        const int64_t ci = (int64_t)row * p.ldc + col;
-        if constexpr (EPI == EPI_STORE) {
-          ((T*)p.C)[ci] = from_f32<T>(v);
-        } else if constexpr (EPI == EPI_BIAS) {
-          ((T*)p.C)[ci] = from_f32<T>(v + bias);
-        } else if constexpr (EPI == EPI_BIAS_RESID) {
-          ((float*)p.C)[ci] = p.resid[(int64_t)row * p.ldr + col] + (v + bias);
-        } else if constexpr (EPI == EPI_BIAS_GELU) {
-          float u = v + bias;
-          p.aux[(int64_t)row * p.ldaux + col] = u;
-          ((T*)p.C)[ci] = from_f32<T>(gelu_f(u));
-        } else if constexpr (EPI == EPI_F32) {
-          ((float*)p.C)[ci] = v;
-        } else if constexpr (EPI == EPI_GELU_BWD) {
-          ((T*)p.C)[ci] = from_f32<T>(v * gelu_grad_f(p.aux[(int64_t)row * p.ldaux + col]));
-        } else {  // EPI_ACC
-          float* c = (float*)p.C + ci;
-          *c = (p.beta != 0.f ? p.beta * *c : 0.f) + v;
-        }
+        if (row < p.M) epi_store<T, EPI>(p, row, col, acc[i][j][e], bias);
       }
     }
+  }
+}
+
+// ----------------------------------------------------------------------------- pipelined bf16 (global -> LDS)
+// BM_ x BN_ tile, BK = 32, STAGES LDS buffers filled straight from global memory
+// (global_load_lds, 16 bytes per lane, a wavefront's 64 lanes land on 1 KB of
+// consecutive LDS), so loads for STAGES-1 future k-slices are in flight while a
+// slice is multiplied. Requires K (and the split length) to be a multiple of 32;
+// rows past the edge are clamped to a valid address and masked at the store.
+//
+// k-contiguous operand, per stage [ROWS][4 units of 8 k]; unit u of row r sits at
+// r*4 + (u ^ ((r >> 1) & 3)). Measured on gfx950, this XOR keeps the MFMA fragment
+// reads (16 consecutive rows of one unit column) at the full ds_read_b128 rate,
+// where the unswizzled layout or an XOR with (r >> 2) loses about a fifth.
+// m-contiguous operand, per stage [32 k][ROWS/8 units of 8 m]; unit mu of row k
+// sits at k*(ROWS/8) + (mu ^ swz(k)). It is read with ds_read_tr16_b64: in each
+// 16-lane group, lane q reads 4 m at (k0 + q/4, m0 + 4*(q%4)) and receives 4 k of
+// column m0 + q, which is one half of an MFMA fragment.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ inline int mc_swz(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
+
+template <int ROWS, int NW>
+__device__ inline void dma_kc(const bf16* __restrict__ src, int64_t ld, int row0, int nrows, int k0, char* lds,
+                              int wave, int lane) {
+  constexpr int CHUNKS = ROWS * 32 * 2 / 1024;   // 1 KB per wavefront instruction
+#pragma unroll
+  for (int i = 0; i < CHUNKS / NW; i++) {
+    const int ch = wave + NW * i;
+    const int r = ch * 16 + (lane >> 2);
+    const int u = (lane & 3) ^ ((r >> 1) & 3);
+    const int gr = min(row0 + r, nrows - 1);
+    const bf16* g = src + (int64_t)gr * ld + k0 + 8 * u;
+    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(lds + ch * 1024), 16, 0, 0);
+  }
+}
+
+template <int ROWS, int NW>
+__device__ inline void dma_mc(const bf16* __restrict__ src, int64_t ld, int row0, int nrows, int k0, char* lds,
+                              int wave, int lane) {
+  constexpr int UPR = ROWS / 8;                  // 16-byte units per k-row
+  constexpr int RPC = 64 / UPR;                  // k-rows per 1 KB chunk
+  constexpr int CHUNKS = 32 / RPC;
+#pragma unroll
+  for (int i = 0; i < CHUNKS / NW; i++) {
+    const int ch = wave + NW * i;
+    const int k = ch * RPC + lane / UPR;
+    const int mu = (lane % UPR) ^ mc_swz(k);
+    const int gm = min(row0 + 8 * mu, nrows - 8);
+    const bf16* g = src + (int64_t)(k0 + k) * ld + gm;
+    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(lds + ch * 1024), 16, 0, 0);
+  }
+}
+
+// MFMA fragment (8 consecutive k = 8*(lane>>4) .. +7 of one row) from a stage buffer.
+template <int ROWS>
+__device__ inline bf16x8 frag_kc(const char* lds, int r) {
+  const int u = ((threadIdx.x & 63) >> 4) ^ ((r >> 1) & 3);
+  return *(const bf16x8*)(lds + (r * 4 + u) * 16);
+}
+template <int ROWS>
+__device__ inline bf16x8 frag_mc(const char* lds, int mbase) {
+  constexpr int UPR = ROWS / 8;
+  const int lane = threadIdx.x & 63;
+  const int q = lane & 15, g = lane >> 4;
+  const int mu = (mbase >> 3) + ((q & 3) >> 1);
+  s16x4 h[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; hh++) {
+    const int k = 8 * g + 4 * hh + (q >> 2);
+    const char* a = lds + (k * UPR + (mu ^ mc_swz(k))) * 16 + (q & 1) * 8;
+    h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a));
+  }
+  bf16x8 f;
+  __builtin_memcpy(&f, h, 16);
+  return f;
+}
+
+template <int BM_, int BN_, int WM_, int WN_, int STAGES, bool AK, bool BK_, int EPI>
+__global__ __launch_bounds__(64 * WM_ * WN_) void gemm_dma_kernel(GemmArgs p) {
+  constexpr int NW = WM_ * WN_;
+  constexpr int TM = BM_ / WM_, TN = BN_ / WN_;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr int AB = BM_ * 32 * 2, BB = BN_ * 32 * 2, SB = AB + BB;
+  constexpr int LPS = (AB + BB) / 1024 / NW;     // load instructions per stage per wave
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * SB];
+
+  const int tiles_m = (p.M + BM_ - 1) / BM_, tiles_n = (p.N + BN_ - 1) / BN_;
+  const int total = tiles_m * tiles_n;
+  int bid = blockIdx.x;
+  if (total % 8 == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+  constexpr int GM = 8;
+  const int group = GM * tiles_n;
+  const int first_m = (bid / group) * GM;
+  const int gsz = min(tiles_m - first_m, GM);
+  const int tm = first_m + (bid % group) % gsz;
+  const int tn = (bid % group) / gsz;
+  const int m0 = tm * BM_, n0 = tn * BN_;
+
+  const bf16* A = (const bf16*)p.A;
+  const bf16* B = (const bf16*)p.B;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN_, wn = wave % WN_;
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; i++)
+#pragma unroll
+    for (int j = 0; j < FN; j++) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int kb = blockIdx.z * p.kchunk;
+  const int ke = min(p.K, kb + p.kchunk);
+  const int nk = (ke - kb) / 32;
+
+  auto issue = [&](int t) {
+    char* st = smem + (t % STAGES) * SB;
+    const int k0 = kb + t * 32;
+    if constexpr (AK) dma_kc<BM_, NW>(A, p.lda, m0, p.M, k0, st, wave, lane);
+    else dma_mc<BM_, NW>(A, p.lda, m0, p.M, k0, st, wave, lane);
+    if constexpr (BK_) dma_kc<BN_, NW>(B, p.ldb, n0, p.N, k0, st + AB, wave, lane);
+    else dma_mc<BN_, NW>(B, p.ldb, n0, p.N, k0, st + AB, wave, lane);
+  };
+
+#pragma unroll
+  for (int t = 0; t < STAGES - 1; t++)
+    if (t < nk) issue(t);
+
+  for (int t = 0; t < nk; t++) {
+    // stage t complete: later stages (up to STAGES-2 of them) may still be in flight
+    // A plain s_barrier: __syncthreads() would also wait for every global->LDS
+    // load still in flight, which would serialise the pipeline. LDS reads of the
+    // previous slice are complete (their MFMAs consumed them) before the barrier.
+    if (t + STAGES - 2 < nk) {
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((STAGES - 2) * LPS) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    if (t + STAGES - 1 < nk) issue(t + STAGES - 1);
+    const char* As = smem + (t % STAGES) * SB;
+    const char* Bs = As + AB;
+    bf16x8 af[FM], bfr[FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++) {
+      const int r = wm * TM + i * 16;
+      if constexpr (AK) af[i] = frag_kc<BM_>(As, r + (lane & 15));
+      else af[i] = frag_mc<BM_>(As, r);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; j++) {
+      const int r = wn * TN + j * 16;
+      if constexpr (BK_) bfr[j] = frag_kc<BN_>(Bs, r + (lane & 15));
+      else bfr[j] = frag_mc<BN_>(Bs, r);
+    }
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+      for (int j = 0; j < FN; j++) acc[i][j] = Mfma<bf16>::mma(af[i], bfr[j], acc[i][j]);
+  }
+
+#pragma unroll
+  for (int i = 0; i < FM; i++) {
+#pragma unroll
+    for (int j = 0; j < FN; j++) {
+      const int col = n0 + wn * TN + j * 16 + (lane & 15);
+      if (col >= p.N) continue;
+      const float bias = epi_bias<EPI>(p, col);
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int row = m0 + wm * TM + i * 16 + (lane >> 4) * 4 + e;
+        if (row < p.M) epi_store<bf16, EPI>(p, row, col, acc[i][j][e], bias);
+      }
+    }
+  }
+}
+
+template <int BM_, int BN_, int WM_, int WN_, int STAGES, bool AK, bool BK_>
+static hipError_t dma_epi(const GemmArgs& a, int epi, int splits, hipStream_t s) {
+  const int total = ((a.M + BM_ - 1) / BM_) * ((a.N + BN_ - 1) / BN_);
+  dim3 grid(total, 1, splits);
+  switch (epi) {
+#define GPT_DMA_CASE(E)                                                                                          \
+  case E:                                                                                                        \
+    hipLaunchKernelGGL((gemm_dma_kernel<BM_, BN_, WM_, WN_, STAGES, AK, BK_, E>), grid, dim3(64 * WM_ * WN_), 0, \
+                       s, a);                                                                                    \
+    break;
+    GPT_DMA_CASE(EPI_STORE)
+    GPT_DMA_CASE(EPI_BIAS)
+    GPT_DMA_CASE(EPI_BIAS_RESID)
+    GPT_DMA_CASE(EPI_BIAS_GELU)
+    GPT_DMA_CASE(EPI_F32)
+    GPT_DMA_CASE(EPI_GELU_BWD)
+    GPT_DMA_CASE(EPI_ACC)
+#undef GPT_DMA_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int BM_, int BN_, int WM_, int WN_, int STAGES>
+static hipError_t dma_layout(const GemmDesc& d, const GemmArgs& a, int splits, hipStream_t s) {
+  if (d.a_kc && d.b_kc) return dma_epi<BM_, BN_, WM_, WN_, STAGES, true, true>(a, d.epi, splits, s);
+  if (d.a_kc && !d.b_kc) return dma_epi<BM_, BN_, WM_, WN_, STAGES, true, false>(a, d.epi, splits, s);
+  if (!d.a_kc && !d.b_kc) return dma_epi<BM_, BN_, WM_, WN_, STAGES, false, false>(a, d.epi, splits, s);
+  return hipErrorInvalidValue;
+}
+
+// C[m, n] = beta * C[m, n] + sum_z part[z, m, n], z in order.
+__global__ void splitk_reduce_kernel(const float* __restrict__ part, int S, int M, int N, float* C, int64_t ldc,
+                                     float beta) {
+  const int64_t total = (int64_t)M * N;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    float s = 0.f;
+    for (int z = 0; z < S; z++) s += part[(int64_t)z * total + i];
+    const int64_t m = i / N, n = i % N;
+    float* c = C + m * ldc + n;
+    *c = (beta != 0.f ? beta * *c : 0.f) + s;
   }
 }
 
@@ -303,11 +537,48 @@ hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
   a.M = d.M; a.N = d.N; a.K = d.K; a.bias = d.bias; a.resid = d.resid; a.ldr = d.ldr;
   a.aux = d.aux; a.ldaux = d.ldaux; a.beta = d.beta;
   const int vw = bf16_operands ? 8 : 4;               // elements per 16-byte vector
-  a.a_vec = (d.lda % vw == 0) && ((uintptr_t)d.A % 16 == 0);
-  a.b_vec = (d.ldb % vw == 0) && ((uintptr_t)d.B % 16 == 0);
-  dim3 grid((d.N + BN - 1) / BN, (d.M + BM - 1) / BM);
-  if (bf16_operands) return dispatch_layout<bf16>(d, a, grid, s);
-  return dispatch_layout<float>(d, a, grid, s);
+  auto vec_ok = [&](const void* ptr, int64_t ld) { return (ld % vw == 0) && ((uintptr_t)ptr % 16 == 0); };
+  a.a_vec = vec_ok(d.A, d.lda);
+  a.b_vec = vec_ok(d.B, d.ldb);
+  // The pipelined 256x256 kernel loads 16-byte vectors straight into LDS with no
+  // edge handling along k: it needs bf16, K a multiple of 32, aligned operands and,
+  // for m-contiguous operands, a row count that is a multiple of 8.
+  const bool pipelined = bf16_operands && d.M >= 256 && d.N >= 256 && d.K % 32 == 0 && a.a_vec && a.b_vec &&
+                         (d.a_kc || d.M % 8 == 0) && (d.b_kc || d.N % 8 == 0);
+  const int TBM = pipelined ? 256 : BM, TBN = pipelined ? 256 : BN;
+  const int tiles = ((d.M + TBM - 1) / TBM) * ((d.N + TBN - 1) / TBN);
+  const int BKt = bf16_operands ? GemmCfg<bf16>::BK : GemmCfg<float>::BK;
+  a.kchunk = d.K > 0 ? d.K : 1;
+  a.part = nullptr;
+  // Split the contraction when the output has too few tiles to fill the chip
+  // (weight gradients: small outputs, K = B*T); partials are reduced in order.
+  int S = 1;
+  if (d.epi == EPI_ACC && d.split_ws) {
+    const int want = (512 + tiles - 1) / tiles;
+    const int by_k = d.K / (4 * BKt);
+    const int64_t mn = (int64_t)d.M * d.N;
+    const int by_ws = (int)std::min<int64_t>(64, (int64_t)(d.split_ws_floats / (size_t)mn));
+    S = std::max(1, std::min(want, std::min(by_k, by_ws)));
+    if (S > 1) {
+      const int kc = ((d.K + S - 1) / S + BKt - 1) / BKt * BKt;   // a multiple of 64 (bf16) or 16
+      S = (d.K + kc - 1) / kc;
+      a.kchunk = kc;
+      a.part = d.split_ws;
+    }
+  }
+  hipError_t e;
+  if (pipelined) {
+    e = dma_layout<256, 256, 2, 4, 4>(d, a, S, s);
+  } else {
+    dim3 grid((d.N + BN - 1) / BN, (d.M + BM - 1) / BM, S);
+    e = bf16_operands ? dispatch_layout<bf16>(d, a, grid, s) : dispatch_layout<float>(d, a, grid, s);
+  }
+  if (e != hipSuccess || S == 1) return e;
+  const int64_t total = (int64_t)d.M * d.N;
+  const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 8192);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, (const float*)d.split_ws, S, d.M, d.N,
+                     (float*)d.C, d.ldc, d.beta);
+  return hipGetLastError();
 }
 
 }  // namespace gpt

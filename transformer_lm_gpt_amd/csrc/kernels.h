@@ -30,6 +30,7 @@ struct GemmDesc {
   const float* resid; int64_t ldr;
   float* aux; int64_t ldaux;
   float beta;
+  float* split_ws; size_t split_ws_floats;   // optional split-K workspace (EPI_ACC only)
 };
 
 hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s);
@@ -44,12 +45,13 @@ hipError_t launch_layernorm_fwd(const float* x, const float* g, const float* b, 
                                 float* mean, float* rstd, int M, int d, hipStream_t s);
 
 // dx = dres + LN backward of dy; writes dx (fp32) and optionally its operand-type copy
-// dx_op; per-block partial column sums of dy * xhat and dy into part_g / part_b
-// ([nblk, d] each, nblk = ceil(M / LN_BWD_ROWS)).
-constexpr int LN_BWD_ROWS = 64;
+// dx_op; per-block partial column sums of dy * xhat, dy and dres (dres may be NULL,
+// then part_r is unused) into part_g / part_b / part_r ([nblk, d] each,
+// nblk = ceil(M / LN_BWD_ROWS)). dx may alias dres. d must be a multiple of 4.
+constexpr int LN_BWD_ROWS = 16;
 hipError_t launch_layernorm_bwd(const float* dy, const float* x, const float* mean, const float* rstd,
                                 const float* g, const float* dres, float* dx, void* dx_op, bool bf16_out,
-                                float* part_g, float* part_b, int M, int d, hipStream_t s);
+                                float* part_g, float* part_b, float* part_r, int M, int d, hipStream_t s);
 
 // Column sums of an [M, N] matrix (fp32 or bf16) into per-block partials [nblk, N].
 constexpr int COLSUM_ROWS = 64;

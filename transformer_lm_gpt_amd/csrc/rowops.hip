@@ -69,68 +69,125 @@ hipError_t launch_layernorm_fwd(const float* x, const float* g, const float* b, 
 
 // Backward: with xhat = (x - mu) rstd and gh = dy * g,
 //   dx = rstd (gh - mean(gh) - xhat mean(gh xhat)) + dres.
-// Each workgroup owns LN_BWD_ROWS rows; each wave accumulates its own column
-// partials of dy*xhat and dy in LDS, and the four waves are summed in order.
+// One wavefront per row, LN_BWD_ROWS rows per workgroup. Each lane owns
+// NCH float4 column groups and keeps its column partials of dy*xhat, dy and
+// dres in registers; the four waves are combined in LDS in a fixed order and
+// written as one partial row per workgroup (reduced later by colsum_final).
+// The dres column sum is the bias gradient of the projection whose output
+// feeds this residual, so it comes for free here.
 constexpr int LN_MAX_D = 1024;
-template <typename T>
+template <typename T, int NCH>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ dy, const float* __restrict__ x,
                                                      const float* __restrict__ mean,
                                                      const float* __restrict__ rstd, const float* __restrict__ g,
                                                      const float* dres, float* dx, T* dx_op,
                                                      float* __restrict__ part_g, float* __restrict__ part_b,
-                                                     int M, int d) {
-  __shared__ float sg[4][LN_MAX_D];
-  __shared__ float sb[4][LN_MAX_D];
+                                                     float* __restrict__ part_r, int M, int d) {
+  __shared__ f32x4 red[4][LN_MAX_D / 4];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int c = lane; c < d; c += 64) {
-    sg[w][c] = 0.f;
-    sb[w][c] = 0.f;
+  const int d4 = d >> 2;
+  f32x4 gg[NCH], pg[NCH], pb[NCH], pr[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; j++) {
+    const int c4 = j * 64 + lane;
+    gg[j] = c4 < d4 ? ((const f32x4*)g)[c4] : (f32x4){0.f, 0.f, 0.f, 0.f};
+    pg[j] = pb[j] = pr[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
-  const int row_begin = blockIdx.x * LN_BWD_ROWS;
-  const int row_end = min(M, row_begin + LN_BWD_ROWS);
-  for (int row = row_begin + w; row < row_end; row += 4) {
-    const int64_t o = (int64_t)row * d;
+  const int row0 = blockIdx.x * LN_BWD_ROWS;
+  for (int r = w; r < LN_BWD_ROWS; r += 4) {
+    const int row = row0 + r;
+    if (row >= M) break;
+    const int64_t o4 = (int64_t)row * d4;
     const float mu = mean[row], rs = rstd[row];
+    f32x4 xh[NCH], dyv[NCH];
     float sa = 0.f, sbb = 0.f;
-    for (int c = lane; c < d; c += 64) {
-      float xh = (x[o + c] - mu) * rs;
-      float dyv = dy[o + c];
-      float gh = dyv * g[c];
-      sa += gh;
-      sbb += gh * xh;
-      sg[w][c] += dyv * xh;
-      sb[w][c] += dyv;
+#pragma unroll
+    for (int j = 0; j < NCH; j++) {
+      const int c4 = j * 64 + lane;
+      if (c4 < d4) {
+        const f32x4 xv = ((const f32x4*)x)[o4 + c4];
+        dyv[j] = ((const f32x4*)dy)[o4 + c4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          xh[j][e] = (xv[e] - mu) * rs;
+          const float gh = dyv[j][e] * gg[j][e];
+          sa += gh;
+          sbb += gh * xh[j][e];
+          pg[j][e] += dyv[j][e] * xh[j][e];
+          pb[j][e] += dyv[j][e];
+        }
+      }
     }
     const float a = wave_sum(sa) / d;
     const float bb = wave_sum(sbb) / d;
-    for (int c = lane; c < d; c += 64) {
-      float xh = (x[o + c] - mu) * rs;
-      float gh = dy[o + c] * g[c];
-      float v = rs * (gh - a - xh * bb);
-      if (dres) v += dres[o + c];
-      dx[o + c] = v;
-      if (dx_op) dx_op[o + c] = from_f32<T>(v);
+#pragma unroll
+    for (int j = 0; j < NCH; j++) {
+      const int c4 = j * 64 + lane;
+      if (c4 < d4) {
+        f32x4 rv = dres ? ((const f32x4*)dres)[o4 + c4] : (f32x4){0.f, 0.f, 0.f, 0.f};
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          v[e] = rs * (dyv[j][e] * gg[j][e] - a - xh[j][e] * bb) + rv[e];
+          pr[j][e] += rv[e];
+        }
+        ((f32x4*)dx)[o4 + c4] = v;
+        if (dx_op) {
+          if constexpr (sizeof(T) == 2) {
+            bf16x4 vb;
+#pragma unroll
+            for (int e = 0; e < 4; e++) vb[e] = (bf16)v[e];
+            ((bf16x4*)dx_op)[o4 + c4] = vb;
+          } else {
+            ((f32x4*)dx_op)[o4 + c4] = v;
+          }
+        }
+      }
     }
   }
-  __syncthreads();
-  for (int c = threadIdx.x; c < d; c += 256) {
-    part_g[(int64_t)blockIdx.x * d + c] = ((sg[0][c] + sg[1][c]) + sg[2][c]) + sg[3][c];
-    part_b[(int64_t)blockIdx.x * d + c] = ((sb[0][c] + sb[1][c]) + sb[2][c]) + sb[3][c];
+  // fixed-order combine of the four waves, one quantity at a time
+  float* const outs[3] = {part_g, part_b, part_r};
+#pragma unroll
+  for (int q = 0; q < 3; q++) {
+    if (q == 2 && !part_r) break;
+#pragma unroll
+    for (int j = 0; j < NCH; j++) {
+      const int c4 = j * 64 + lane;
+      if (c4 < d4) red[w][c4] = q == 0 ? pg[j] : (q == 1 ? pb[j] : pr[j]);
+    }
+    __syncthreads();
+    for (int c4 = threadIdx.x; c4 < d4; c4 += 256) {
+      f32x4 t = red[0][c4];
+#pragma unroll
+      for (int ww = 1; ww < 4; ww++) t += red[ww][c4];
+      ((f32x4*)outs[q])[(int64_t)blockIdx.x * d4 + c4] = t;
+    }
+    __syncthreads();
   }
+}
+
+template <typename T>
+static hipError_t ln_bwd_t(const float* dy, const float* x, const float* mean, const float* rstd, const float* g,
+                           const float* dres, float* dx, void* dx_op, float* pg, float* pb, float* pr, int M, int d,
+                           hipStream_t s) {
+  dim3 grid((M + LN_BWD_ROWS - 1) / LN_BWD_ROWS);
+  const int nch = (d / 4 + 63) / 64;
+  switch (nch) {
+#define LNB(N) \
+  case N: hipLaunchKernelGGL((ln_bwd_kernel<T, N>), grid, dim3(256), 0, s, dy, x, mean, rstd, g, dres, dx, (T*)dx_op, pg, pb, pr, M, d); break;
+    LNB(1) LNB(2) LNB(3) LNB(4)
+#undef LNB
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_layernorm_bwd(const float* dy, const float* x, const float* mean, const float* rstd,
                                 const float* g, const float* dres, float* dx, void* dx_op, bool bf16_out,
-                                float* part_g, float* part_b, int M, int d, hipStream_t s) {
-  if (d > LN_MAX_D) return hipErrorInvalidValue;
-  dim3 grid((M + LN_BWD_ROWS - 1) / LN_BWD_ROWS);
-  if (bf16_out)
-    hipLaunchKernelGGL(ln_bwd_kernel<bf16>, grid, dim3(256), 0, s, dy, x, mean, rstd, g, dres, dx, (bf16*)dx_op,
-                       part_g, part_b, M, d);
-  else
-    hipLaunchKernelGGL(ln_bwd_kernel<float>, grid, dim3(256), 0, s, dy, x, mean, rstd, g, dres, dx,
-                       (float*)dx_op, part_g, part_b, M, d);
-  return hipGetLastError();
+                                float* part_g, float* part_b, float* part_r, int M, int d, hipStream_t s) {
+  if (d > LN_MAX_D || d % 4 != 0) return hipErrorInvalidValue;
+  if (bf16_out) return ln_bwd_t<bf16>(dy, x, mean, rstd, g, dres, dx, dx_op, part_g, part_b, part_r, M, d, s);
+  return ln_bwd_t<float>(dy, x, mean, rstd, g, dres, dx, dx_op, part_g, part_b, part_r, M, d, s);
 }
 
 // ----------------------------------------------------------------------------- column sums
@@ -155,16 +212,28 @@ hipError_t launch_colsum_partial(const void* X, bool bf16_in, int64_t ldx, int M
   return hipGetLastError();
 }
 
-__global__ void colsum_final_kernel(const float* __restrict__ part, int nblk, int N, float* dst, float beta) {
-  const int col = blockIdx.x * 256 + threadIdx.x;
-  if (col >= N) return;
+// 32 columns per workgroup, 8 row groups: each thread sums every eighth partial
+// in order, then the 8 group sums are added in a fixed order.
+__global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part, int nblk, int N,
+                                                           float* dst, float beta) {
+  __shared__ float red[8][32];
+  const int cl = threadIdx.x & 31, grp = threadIdx.x >> 5;
+  const int col = blockIdx.x * 32 + cl;
   float s = 0.f;
-  for (int j = 0; j < nblk; j++) s += part[(int64_t)j * N + col];
-  dst[col] = (beta != 0.f ? beta * dst[col] : 0.f) + s;
+  if (col < N)
+    for (int j = grp; j < nblk; j += 8) s += part[(int64_t)j * N + col];
+  red[grp][cl] = s;
+  __syncthreads();
+  if (grp == 0 && col < N) {
+    float t = red[0][cl];
+#pragma unroll
+    for (int q = 1; q < 8; q++) t += red[q][cl];
+    dst[col] = (beta != 0.f ? beta * dst[col] : 0.f) + t;
+  }
 }
 
 hipError_t launch_colsum_final(const float* part, int nblk, int N, float* dst, float beta, hipStream_t s) {
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((N + 255) / 256), dim3(256), 0, s, part, nblk, N, dst, beta);
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((N + 31) / 32), dim3(256), 0, s, part, nblk, N, dst, beta);
   return hipGetLastError();
 }
 

@@ -73,7 +73,9 @@ struct gpt_model {
   Slice x_final, lnf, lnf_mean, lnf_rstd, logits, row_loss, tokens, targets;
   size_t act_bytes = 0;
   // workspace
-  Slice dres, dres_op, dln, du, dO, dqkv, attnD, part_g, part_b, colsum_part, emb_keys, emb_piece, norm_part, opt;
+  Slice dres, dres_op, dln, du, dO, dqkv, attnD, part_g, part_b, part_r, colsum_part, emb_keys, emb_piece, norm_part,
+      opt, split;
+  size_t split_floats = 0;
   size_t ws_bytes = 0;
   // binding
   gpt_buffers buf{};
@@ -158,6 +160,8 @@ GemmDesc gemm_desc(const void* A, int64_t lda, bool a_kc, const void* B, int64_t
                    int64_t ldc, int M, int N, int K, int epi) {
   GemmDesc d;
   std::memset(&d, 0, sizeof(d));
+  d.split_ws = nullptr;
+  d.split_ws_floats = 0;
   d.A = A; d.lda = lda; d.a_kc = a_kc;
   d.B = B; d.ldb = ldb; d.b_kc = b_kc;
   d.C = C; d.ldc = ldc; d.M = M; d.N = N; d.K = K; d.epi = epi;
@@ -256,6 +260,9 @@ void plan(gpt_model* h) {
   h->emb_keys = w.take((size_t)embed_bwd_sort_size((int)M) * 4);
   h->emb_piece = w.take(M * d * fb);
   h->norm_part = w.take(NORM_BLOCKS * fb);
+  h->split_floats = 16 * (size_t)d * d + 4096;
+  h->split = w.take(h->split_floats * fb);
+  h->part_r = w.take(ln_blk * d * fb);
   h->opt = w.take(sizeof(OptState));
   h->ws_bytes = w.total;
 }
@@ -268,17 +275,23 @@ int colsum(gpt_model* h, const void* X, bool bf16_in, int64_t ldx, int M, int N,
   return GPT_OK;
 }
 
+// LayerNorm backward into dres (in place when dres is given); also reduces the
+// gain and shift gradients and, when `resid_bias` names a tensor, the column sum
+// of the incoming residual gradient (the bias gradient of that projection).
 int ln_bwd(gpt_model* h, const float* dy, const float* x, const float* mean, const float* rstd,
-           const std::string& gname, const std::string& bname, const float* dres, int M, float beta) {
+           const std::string& gname, const std::string& bname, const float* dres, const char* resid_bias, int M,
+           float beta) {
   float* pg = ws<float>(h, h->part_g);
   float* pb = ws<float>(h, h->part_b);
+  float* pr = resid_bias ? ws<float>(h, h->part_r) : nullptr;
   void* dx_op = h->bf16 ? ws(h, h->dres_op) : nullptr;
   RUN("layernorm", "layernorm_bwd",
-      launch_layernorm_bwd(dy, x, mean, rstd, P(h, gname), dres, ws<float>(h, h->dres), dx_op, h->bf16, pg, pb, M,
-                           h->d, h->stream));
+      launch_layernorm_bwd(dy, x, mean, rstd, P(h, gname), dres, ws<float>(h, h->dres), dx_op, h->bf16, pg, pb, pr,
+                           M, h->d, h->stream));
   const int nblk = (M + LN_BWD_ROWS - 1) / LN_BWD_ROWS;
   RUN("colsum", "ln_dgamma", launch_colsum_final(pg, nblk, h->d, G(h, gname), beta, h->stream));
   RUN("colsum", "ln_dbeta", launch_colsum_final(pb, nblk, h->d, G(h, bname), beta, h->stream));
+  if (resid_bias) RUN("colsum", "resid_bias", launch_colsum_final(pr, nblk, h->d, G(h, resid_bias), beta, h->stream));
   return GPT_OK;
 }
 
@@ -530,12 +543,14 @@ int gpt_backward(gpt_model* h) {
     GemmDesc g = gemm_desc(act(h, h->logits), h->ldz, false, act(h, h->lnf), d, false, G(h, "wte"), d, h->Vp, d, M,
                            EPI_ACC);
     g.beta = beta;
+    g.split_ws = ws<float>(h, h->split);
+    g.split_ws_floats = h->split_floats;
     RUN("gemm_wgrad", "lm_head_wgrad", launch_gemm(g, bf, s));
     GemmDesc g2 = gemm_desc(act(h, h->logits), h->ldz, true, Wop(h, "wte"), d, false, dln, d, M, d, h->Vp, EPI_F32);
     RUN("gemm_dgrad", "lm_head_dgrad", launch_gemm(g2, bf, s));
   }
   if ((rc = ln_bwd(h, dln, act<float>(h, h->x_final), act<float>(h, h->lnf_mean), act<float>(h, h->lnf_rstd),
-                   "lnf.g", "lnf.b", nullptr, M, beta)))
+                   "lnf.g", "lnf.b", nullptr, nullptr, M, beta)))
     return rc;
 
   for (int l = h->L - 1; l >= 0; l--) {
@@ -551,16 +566,20 @@ int gpt_backward(gpt_model* h) {
       GemmDesc gw = gemm_desc(dres_opnd, d, false, act(h, la.h), 4 * d, false, G(h, p + "fcproj.w"), 4 * d, d, 4 * d,
                               M, EPI_ACC);
       gw.beta = beta;
+      gw.split_ws = ws<float>(h, h->split);
+      gw.split_ws_floats = h->split_floats;
       RUN("gemm_wgrad", "fcproj_wgrad", launch_gemm(gw, bf, s));
-      if ((rc = colsum(h, dres, false, d, M, d, G(h, p + "fcproj.b"), beta))) return rc;
       GemmDesc g2 = gemm_desc(du, 4 * d, true, Wop(h, p + "fc.w"), d, false, dln, d, M, d, 4 * d, EPI_F32);
       RUN("gemm_dgrad", "fc_dgrad", launch_gemm(g2, bf, s));
       GemmDesc gw2 = gemm_desc(du, 4 * d, false, act(h, la.ln2), d, false, G(h, p + "fc.w"), d, 4 * d, d, M, EPI_ACC);
       gw2.beta = beta;
+      gw2.split_ws = ws<float>(h, h->split);
+      gw2.split_ws_floats = h->split_floats;
       RUN("gemm_wgrad", "fc_wgrad", launch_gemm(gw2, bf, s));
       if ((rc = colsum(h, du, bf, 4 * d, M, 4 * d, G(h, p + "fc.b"), beta))) return rc;
+      const std::string fcproj_b = p + "fcproj.b";
       if ((rc = ln_bwd(h, dln, act<float>(h, la.xmid), act<float>(h, la.ln2_mean), act<float>(h, la.ln2_rstd),
-                       p + "ln2.g", p + "ln2.b", dres, M, beta)))
+                       p + "ln2.g", p + "ln2.b", dres, fcproj_b.c_str(), M, beta)))
         return rc;
     }
     // ---- attention: xmid = x + attn(LN1(x)) Wo^T + bo ; dres now holds d xmid
@@ -569,8 +588,9 @@ int gpt_backward(gpt_model* h) {
       RUN("gemm_dgrad", "proj_dgrad", launch_gemm(g, bf, s));
       GemmDesc gw = gemm_desc(dres_opnd, d, false, act(h, la.att), d, false, G(h, p + "proj.w"), d, d, d, M, EPI_ACC);
       gw.beta = beta;
+      gw.split_ws = ws<float>(h, h->split);
+      gw.split_ws_floats = h->split_floats;
       RUN("gemm_wgrad", "proj_wgrad", launch_gemm(gw, bf, s));
-      if ((rc = colsum(h, dres, false, d, M, d, G(h, p + "proj.b"), beta))) return rc;
       RUN("attn_bwd", "attn_bwd",
           launch_attn_bwd(act(h, la.qkv), act(h, la.att), dO, act<float>(h, la.lse), ws<float>(h, h->attnD), dqkv, bf,
                           B, T, h->H, h->hd, s));
@@ -579,10 +599,13 @@ int gpt_backward(gpt_model* h) {
       GemmDesc gw2 = gemm_desc(dqkv, 3 * d, false, act(h, la.ln1), d, false, G(h, p + "attn.w"), d, 3 * d, d, M,
                                EPI_ACC);
       gw2.beta = beta;
+      gw2.split_ws = ws<float>(h, h->split);
+      gw2.split_ws_floats = h->split_floats;
       RUN("gemm_wgrad", "qkv_wgrad", launch_gemm(gw2, bf, s));
       if ((rc = colsum(h, dqkv, bf, 3 * d, M, 3 * d, G(h, p + "attn.b"), beta))) return rc;
+      const std::string proj_b = p + "proj.b";
       if ((rc = ln_bwd(h, dln, act<float>(h, la.x), act<float>(h, la.ln1_mean), act<float>(h, la.ln1_rstd),
-                       p + "ln1.g", p + "ln1.b", dres, M, beta)))
+                       p + "ln1.g", p + "ln1.b", dres, proj_b.c_str(), M, beta)))
         return rc;
     }
   }
