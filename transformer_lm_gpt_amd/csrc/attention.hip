@@ -23,6 +23,8 @@
 
 namespace gpt {
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
 // LDS tile of ROWS rows by a contraction dimension, stored [kdim/KG][ROWS+PADR][KG]
 // so that one MFMA fragment is one contiguous read.
 template <typename T, int ROWS, int PADR>
@@ -399,6 +401,365 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const T* __restrict__ 
   }
 }
 
+// ----------------------------------------------------------------------------- bf16, register-resident P
+// Transposed formulation for bf16 with head_dim HDP in {32, 64}. A wavefront owns
+// 16 columns (queries, or keys in the dK/dV kernel); a 64-row tile of the other
+// side streams through LDS. Scores are produced as S^T = K Q^T, so the MFMA
+// output layout puts four keys of one query in each lane. Two such 16-key
+// blocks are exactly the B operand of the next MFMA (Vt P^T, K^T dS^T, ...) when
+// the A operand reads its keys in the same order, which the 16-lane transposing
+// LDS read gives. So P and dS never leave registers, the row statistics need two
+// cross-lane steps, and the output rescale needs none.
+//
+// LDS tiles are [64 rows][HDP] bf16 with 16-byte units XOR-swizzled by row.
+template <int HDP>
+struct ATile {
+  static constexpr int UR = HDP / 8;                  // 16-byte units per row
+  __device__ static inline int swz(int r) { return UR == 8 ? ((r >> 1) & 7) : ((r >> 1) & 3); }
+  __device__ static inline int unit(int r, int u) { return r * UR + (u ^ swz(r)); }
+  // 8 consecutive columns u*8.. of row r (an A or B fragment along the row)
+  __device__ static inline bf16x8 row_frag(const bf16* t, int r, int u) {
+    return *(const bf16x8*)(t + unit(r, u) * 8);
+  }
+  // 16-lane transposed read: lane j of each group gets rows k0..k0+3 of column c0 + j
+  __device__ static inline s16x4 tr(const bf16* t, int k0, int c0) {
+    const int q = threadIdx.x & 15;
+    const int r = k0 + (q >> 2), c = c0 + 4 * (q & 3);
+    const bf16* a = t + unit(r, c >> 3) * 8 + (c & 4);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a));
+  }
+};
+
+__device__ inline bf16x8 cat4(s16x4 lo, s16x4 hi) {
+  s16x4 h[2] = {lo, hi};
+  bf16x8 f;
+  __builtin_memcpy(&f, h, 16);
+  return f;
+}
+__device__ inline bf16x8 pack_p(const f32x4& lo, const f32x4& hi) {
+  bf16x8 f;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    f[i] = (bf16)lo[i];
+    f[4 + i] = (bf16)hi[i];
+  }
+  return f;
+}
+
+// Loads a 64-row tile (rows row0.., columns col0..col0+HDP of a row-major [*, ld]
+// source) into registers, zero past nrows: each thread holds HDP/32 units.
+template <int HDP>
+struct TileRegs {
+  static constexpr int NU = 64 * HDP / 8 / 256;
+  bf16x8 v[NU];
+  __device__ inline void load(const bf16* src, int64_t ld, int row0, int nrows, int col0) {
+#pragma unroll
+    for (int j = 0; j < NU; j++) {
+      const int idx = threadIdx.x + 256 * j;
+      const int r = idx / (HDP / 8), u = idx % (HDP / 8);
+      if (row0 + r < nrows) v[j] = *(const bf16x8*)(src + (int64_t)(row0 + r) * ld + col0 + u * 8);
+      else v[j] = (bf16x8){};
+    }
+  }
+  __device__ inline void store(bf16* t) const {
+#pragma unroll
+    for (int j = 0; j < NU; j++) {
+      const int idx = threadIdx.x + 256 * j;
+      const int r = idx / (HDP / 8), u = idx % (HDP / 8);
+      *(bf16x8*)(t + ATile<HDP>::unit(r, u) * 8) = v[j];
+    }
+  }
+};
+
+template <int HDP>
+__global__ __launch_bounds__(256) void attn_fwd_v2(const bf16* __restrict__ qkv, bf16* __restrict__ o,
+                                                   float* __restrict__ lse, int Tn, int H, float scale) {
+  typedef ATile<HDP> AT;
+  constexpr int KK = HDP / 32, CB = HDP / 16;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[64 * HDP];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[64 * HDP];
+  const int nqb = (Tn + 63) / 64;
+  const int qb = nqb - 1 - blockIdx.x;               // longest rows first
+  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4;
+  const int d = H * HDP;
+  const int64_t ld = 3 * (int64_t)d;
+  const bf16* base = qkv + (int64_t)b * Tn * ld;
+  const int q = qb * 64 + w * 16 + (lane & 15);      // this lane's query
+  bf16x8 qf[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; kk++)
+    qf[kk] = q < Tn ? *(const bf16x8*)(base + (int64_t)q * ld + h * HDP + kk * 32 + g * 8) : (bf16x8){};
+  f32x4 ot[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; cb++) ot[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+
+  TileRegs<HDP> kr, vr;
+  kr.load(base, ld, 0, Tn, d + h * HDP);
+  vr.load(base, ld, 0, Tn, 2 * d + h * HDP);
+  for (int kt = 0; kt <= qb; kt++) {
+    __syncthreads();
+    kr.store(Ks);
+    vr.store(Vs);
+    __syncthreads();
+    if (kt < qb) {
+      kr.load(base, ld, (kt + 1) * 64, Tn, d + h * HDP);
+      vr.load(base, ld, (kt + 1) * 64, Tn, 2 * d + h * HDP);
+    }
+    const int k0 = kt * 64;
+    f32x4 st[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; nb++) {
+      st[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; kk++)
+        st[nb] = Mfma<bf16>::mma(AT::row_frag(Ks, nb * 16 + (lane & 15), kk * 4 + g), qf[kk], st[nb]);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int nb = 0; nb < 4; nb++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int key = k0 + nb * 16 + 4 * g + i;
+        const float v = (key <= q && key < Tn) ? st[nb][i] * scale : -INFINITY;
+        st[nb][i] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+    const float mnew = fmaxf(m, mx);                 // finite: key 0 is always visible
+    const float alpha = __expf(m - mnew);
+    float rs = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < 4; nb++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const float p = __expf(st[nb][i] - mnew);
+        st[nb][i] = p;
+        rs += p;
+      }
+    rs += __shfl_xor(rs, 16, WAVE);
+    rs += __shfl_xor(rs, 32, WAVE);
+    l = l * alpha + rs;
+    m = mnew;
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++) ot[cb] *= alpha;
+#pragma unroll
+    for (int kp = 0; kp < 2; kp++) {
+      const bf16x8 pf = pack_p(st[2 * kp], st[2 * kp + 1]);
+#pragma unroll
+      for (int cb = 0; cb < CB; cb++) {
+        const bf16x8 vf = cat4(AT::tr(Vs, 32 * kp + 4 * g, cb * 16), AT::tr(Vs, 32 * kp + 16 + 4 * g, cb * 16));
+        ot[cb] = Mfma<bf16>::mma(vf, pf, ot[cb]);
+      }
+    }
+  }
+  if (q < Tn) {
+    const float inv = 1.f / l;
+    bf16* orow = o + ((int64_t)b * Tn + q) * d + h * HDP;
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++) {
+      bf16x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; i++) v[i] = (bf16)(ot[cb][i] * inv);
+      *(bf16x4*)(orow + cb * 16 + 4 * g) = v;
+    }
+    if (g == 0) lse[(int64_t)bh * Tn + q] = m + logf(l);
+  }
+}
+
+// dQ for a 64-query block; also writes D = rowsum(dO * O) for these queries,
+// which the dK/dV kernel (launched after) reads.
+template <int HDP>
+__global__ __launch_bounds__(256) void attn_bwd_dq_v2(const bf16* __restrict__ qkv, const bf16* __restrict__ o,
+                                                      const bf16* __restrict__ dout, const float* __restrict__ lse,
+                                                      float* __restrict__ Dv, bf16* __restrict__ dqkv, int Tn, int H,
+                                                      float scale) {
+  typedef ATile<HDP> AT;
+  constexpr int KK = HDP / 32, CB = HDP / 16;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[64 * HDP];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[64 * HDP];
+  const int nqb = (Tn + 63) / 64;
+  const int qb = nqb - 1 - blockIdx.x;
+  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4;
+  const int d = H * HDP;
+  const int64_t ld = 3 * (int64_t)d;
+  const bf16* base = qkv + (int64_t)b * Tn * ld;
+  const int q = qb * 64 + w * 16 + (lane & 15);
+  bf16x8 qf[KK], dof[KK];
+  float Dq = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < KK; kk++) {
+    const int c = kk * 32 + g * 8;
+    if (q < Tn) {
+      qf[kk] = *(const bf16x8*)(base + (int64_t)q * ld + h * HDP + c);
+      dof[kk] = *(const bf16x8*)(dout + ((int64_t)b * Tn + q) * d + h * HDP + c);
+      const bf16x8 ov = *(const bf16x8*)(o + ((int64_t)b * Tn + q) * d + h * HDP + c);
+#pragma unroll
+      for (int e = 0; e < 8; e++) Dq += (float)dof[kk][e] * (float)ov[e];
+    } else {
+      qf[kk] = (bf16x8){};
+      dof[kk] = (bf16x8){};
+    }
+  }
+  Dq += __shfl_xor(Dq, 16, WAVE);
+  Dq += __shfl_xor(Dq, 32, WAVE);
+  const float lq = q < Tn ? lse[(int64_t)bh * Tn + q] : 0.f;
+  if (q < Tn && g == 0) Dv[(int64_t)bh * Tn + q] = Dq;
+
+  f32x4 dqt[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; cb++) dqt[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  TileRegs<HDP> kr, vr;
+  kr.load(base, ld, 0, Tn, d + h * HDP);
+  vr.load(base, ld, 0, Tn, 2 * d + h * HDP);
+  for (int kt = 0; kt <= qb; kt++) {
+    __syncthreads();
+    kr.store(Ks);
+    vr.store(Vs);
+    __syncthreads();
+    if (kt < qb) {
+      kr.load(base, ld, (kt + 1) * 64, Tn, d + h * HDP);
+      vr.load(base, ld, (kt + 1) * 64, Tn, 2 * d + h * HDP);
+    }
+    const int k0 = kt * 64;
+    f32x4 ds[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; nb++) {
+      f32x4 st = (f32x4){0.f, 0.f, 0.f, 0.f}, dpt = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; kk++) {
+        st = Mfma<bf16>::mma(AT::row_frag(Ks, nb * 16 + (lane & 15), kk * 4 + g), qf[kk], st);
+        dpt = Mfma<bf16>::mma(AT::row_frag(Vs, nb * 16 + (lane & 15), kk * 4 + g), dof[kk], dpt);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int key = k0 + nb * 16 + 4 * g + i;
+        const float p = (key <= q && q < Tn) ? __expf(st[i] * scale - lq) : 0.f;
+        ds[nb][i] = p * (dpt[i] - Dq);
+      }
+    }
+#pragma unroll
+    for (int kp = 0; kp < 2; kp++) {
+      const bf16x8 df = pack_p(ds[2 * kp], ds[2 * kp + 1]);
+#pragma unroll
+      for (int cb = 0; cb < CB; cb++) {
+        const bf16x8 kf = cat4(AT::tr(Ks, 32 * kp + 4 * g, cb * 16), AT::tr(Ks, 32 * kp + 16 + 4 * g, cb * 16));
+        dqt[cb] = Mfma<bf16>::mma(kf, df, dqt[cb]);
+      }
+    }
+  }
+  if (q < Tn) {
+    bf16* row = dqkv + ((int64_t)b * Tn + q) * ld + h * HDP;
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++) {
+      bf16x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; i++) v[i] = (bf16)(dqt[cb][i] * scale);
+      *(bf16x4*)(row + cb * 16 + 4 * g) = v;
+    }
+  }
+}
+
+// dK and dV for a 64-key block over the query tiles at or after it.
+template <int HDP>
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_v2(const bf16* __restrict__ qkv, const bf16* __restrict__ dout,
+                                                        const float* __restrict__ lse, const float* __restrict__ Dv,
+                                                        bf16* __restrict__ dqkv, int Tn, int H, float scale) {
+  typedef ATile<HDP> AT;
+  constexpr int KK = HDP / 32, CB = HDP / 16;
+  __shared__ __attribute__((aligned(16))) bf16 Qs[64 * HDP];
+  __shared__ __attribute__((aligned(16))) bf16 dOs[64 * HDP];
+  __shared__ float ls[64], Ds[64];
+  const int nb_t = (Tn + 63) / 64;
+  const int kb = blockIdx.x;                          // key blocks near 0 see the most queries
+  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4;
+  const int d = H * HDP;
+  const int64_t ld = 3 * (int64_t)d;
+  const bf16* base = qkv + (int64_t)b * Tn * ld;
+  const bf16* dob = dout + (int64_t)b * Tn * d;
+  const int key = kb * 64 + w * 16 + (lane & 15);    // this lane's key (B-operand column)
+  bf16x8 kf[KK], vf[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; kk++) {
+    const int c = kk * 32 + g * 8;
+    kf[kk] = key < Tn ? *(const bf16x8*)(base + (int64_t)key * ld + d + h * HDP + c) : (bf16x8){};
+    vf[kk] = key < Tn ? *(const bf16x8*)(base + (int64_t)key * ld + 2 * d + h * HDP + c) : (bf16x8){};
+  }
+  f32x4 dkt[CB], dvt[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; cb++) {
+    dkt[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    dvt[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+  TileRegs<HDP> qr, dr;
+  qr.load(base, ld, kb * 64, Tn, h * HDP);
+  dr.load(dob, d, kb * 64, Tn, h * HDP);
+  for (int qt = kb; qt < nb_t; qt++) {
+    const int q0 = qt * 64;
+    __syncthreads();
+    qr.store(Qs);
+    dr.store(dOs);
+    if (threadIdx.x < 64) {
+      const int gq = q0 + threadIdx.x;
+      ls[threadIdx.x] = gq < Tn ? lse[(int64_t)bh * Tn + gq] : 0.f;
+      Ds[threadIdx.x] = gq < Tn ? Dv[(int64_t)bh * Tn + gq] : 0.f;
+    }
+    __syncthreads();
+    if (qt + 1 < nb_t) {
+      qr.load(base, ld, q0 + 64, Tn, h * HDP);
+      dr.load(dob, d, q0 + 64, Tn, h * HDP);
+    }
+    f32x4 p[4], ds[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; nb++) {
+      f32x4 s = (f32x4){0.f, 0.f, 0.f, 0.f}, dp = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; kk++) {
+        s = Mfma<bf16>::mma(AT::row_frag(Qs, nb * 16 + (lane & 15), kk * 4 + g), kf[kk], s);
+        dp = Mfma<bf16>::mma(AT::row_frag(dOs, nb * 16 + (lane & 15), kk * 4 + g), vf[kk], dp);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int ql = nb * 16 + 4 * g + i;
+        const int qq = q0 + ql;
+        const float pv = (key <= qq && qq < Tn) ? __expf(s[i] * scale - ls[ql]) : 0.f;
+        p[nb][i] = pv;
+        ds[nb][i] = pv * (dp[i] - Ds[ql]);
+      }
+    }
+#pragma unroll
+    for (int qp = 0; qp < 2; qp++) {
+      const bf16x8 pf = pack_p(p[2 * qp], p[2 * qp + 1]);
+      const bf16x8 df = pack_p(ds[2 * qp], ds[2 * qp + 1]);
+#pragma unroll
+      for (int cb = 0; cb < CB; cb++) {
+        const bf16x8 dof = cat4(AT::tr(dOs, 32 * qp + 4 * g, cb * 16), AT::tr(dOs, 32 * qp + 16 + 4 * g, cb * 16));
+        dvt[cb] = Mfma<bf16>::mma(dof, pf, dvt[cb]);
+        const bf16x8 qf = cat4(AT::tr(Qs, 32 * qp + 4 * g, cb * 16), AT::tr(Qs, 32 * qp + 16 + 4 * g, cb * 16));
+        dkt[cb] = Mfma<bf16>::mma(qf, df, dkt[cb]);
+      }
+    }
+  }
+  if (key < Tn) {
+    bf16* row = dqkv + ((int64_t)b * Tn + key) * ld + h * HDP;
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++) {
+      bf16x4 vk, vv;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        vk[i] = (bf16)(dkt[cb][i] * scale);
+        vv[i] = (bf16)dvt[cb][i];
+      }
+      *(bf16x4*)(row + d + cb * 16 + 4 * g) = vk;
+      *(bf16x4*)(row + 2 * d + cb * 16 + 4 * g) = vv;
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------- launchers
 template <typename T, int HDP>
 static hipError_t fwd_t(const void* qkv, void* o, float* lse, int B, int Tn, int H, int hd, hipStream_t s) {
@@ -411,6 +772,15 @@ static hipError_t fwd_t(const void* qkv, void* o, float* lse, int B, int Tn, int
 hipError_t launch_attn_fwd(const void* qkv, void* o, float* lse, bool bf16_ops, int B, int T, int H, int hd,
                            hipStream_t s) {
   if (hd <= 0 || hd > 64) return hipErrorInvalidValue;
+  if (bf16_ops && (hd == 32 || hd == 64)) {
+    dim3 grid((T + 63) / 64, B * H);
+    const float scale = 1.0f / sqrtf((float)hd);
+    if (hd == 64)
+      hipLaunchKernelGGL(attn_fwd_v2<64>, grid, dim3(256), 0, s, (const bf16*)qkv, (bf16*)o, lse, T, H, scale);
+    else
+      hipLaunchKernelGGL(attn_fwd_v2<32>, grid, dim3(256), 0, s, (const bf16*)qkv, (bf16*)o, lse, T, H, scale);
+    return hipGetLastError();
+  }
   if (bf16_ops) return hd <= 32 ? fwd_t<bf16, 32>(qkv, o, lse, B, T, H, hd, s) : fwd_t<bf16, 64>(qkv, o, lse, B, T, H, hd, s);
   return hd <= 32 ? fwd_t<float, 32>(qkv, o, lse, B, T, H, hd, s) : fwd_t<float, 64>(qkv, o, lse, B, T, H, hd, s);
 }
@@ -433,6 +803,22 @@ static hipError_t bwd_t(const void* qkv, const void* o, const void* dout, const 
 hipError_t launch_attn_bwd(const void* qkv, const void* o, const void* dout, const float* lse, float* D,
                            void* dqkv, bool bf16_ops, int B, int T, int H, int hd, hipStream_t s) {
   if (hd <= 0 || hd > 64) return hipErrorInvalidValue;
+  if (bf16_ops && (hd == 32 || hd == 64)) {
+    dim3 grid((T + 63) / 64, B * H);
+    const float scale = 1.0f / sqrtf((float)hd);
+    if (hd == 64) {
+      hipLaunchKernelGGL(attn_bwd_dq_v2<64>, grid, dim3(256), 0, s, (const bf16*)qkv, (const bf16*)o,
+                         (const bf16*)dout, lse, D, (bf16*)dqkv, T, H, scale);
+      hipLaunchKernelGGL(attn_bwd_dkdv_v2<64>, grid, dim3(256), 0, s, (const bf16*)qkv, (const bf16*)dout, lse,
+                         (const float*)D, (bf16*)dqkv, T, H, scale);
+    } else {
+      hipLaunchKernelGGL(attn_bwd_dq_v2<32>, grid, dim3(256), 0, s, (const bf16*)qkv, (const bf16*)o,
+                         (const bf16*)dout, lse, D, (bf16*)dqkv, T, H, scale);
+      hipLaunchKernelGGL(attn_bwd_dkdv_v2<32>, grid, dim3(256), 0, s, (const bf16*)qkv, (const bf16*)dout, lse,
+                         (const float*)D, (bf16*)dqkv, T, H, scale);
+    }
+    return hipGetLastError();
+  }
   if (bf16_ops)
     return hd <= 32 ? bwd_t<bf16, 32>(qkv, o, dout, lse, D, dqkv, B, T, H, hd, s)
                     : bwd_t<bf16, 64>(qkv, o, dout, lse, D, dqkv, B, T, H, hd, s);
