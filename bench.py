@@ -68,7 +68,7 @@ def main(argv=None):
     ap.add_argument("--precision", default="bf16", choices=["bf16", "fp32"])
     ap.add_argument("--kernel", default="lm_head_fwd",
                     help="kernel family whose launches are timed for the roofline line")
-    ap.add_argument("--cpu-seqs", type=int, default=1, help="sequences in the oracle's timed sample (0: skip)")
+    ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the oracle's timed sample (0: skip)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the data-parallel all-reduce "

@@ -175,6 +175,7 @@ struct GemmArgs {
   float* aux; int64_t ldaux;
   float beta;
   int a_vec, b_vec;
+  int c_vec;           // C / aux / resid rows allow 16-column vector access
   int kchunk;          // contraction length per split (gridDim.z splits)
   float* part;         // split partials [gridDim.z, M, N] (EPI_ACC with gridDim.z > 1)
 };
@@ -209,6 +210,90 @@ __device__ inline void epi_store(const GemmArgs& p, int row, int col, float v, f
     } else {
       float* c = (float*)p.C + ci;
       *c = (p.beta != 0.f ? p.beta * *c : 0.f) + v;
+    }
+  }
+}
+
+// Sixteen consecutive output columns col0.. of one row: vector loads and stores
+// when the run is inside the matrix and aligned, element-wise otherwise.
+template <int EPI>
+__device__ inline void epi_store16(const GemmArgs& p, int row, int col0, const float (&v)[16], bool vec) {
+  if (!vec) {
+#pragma unroll
+    for (int c = 0; c < 16; c++)
+      if (col0 + c < p.N) epi_store<bf16, EPI>(p, row, col0 + c, v[c], epi_bias<EPI>(p, col0 + c));
+    return;
+  }
+  const int64_t ci = (int64_t)row * p.ldc + col0;
+  float x[16];
+#pragma unroll
+  for (int c = 0; c < 16; c++) x[c] = v[c];
+  if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU) {
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const f32x4 b = *(const f32x4*)(p.bias + col0 + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; e++) x[4 * q + e] += b[e];
+    }
+  }
+  if constexpr (EPI == EPI_STORE || EPI == EPI_BIAS) {
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; e++) o[e] = (bf16)x[8 * q + e];
+      *(bf16x8*)((bf16*)p.C + ci + 8 * q) = o;
+    }
+  } else if constexpr (EPI == EPI_BIAS_RESID) {
+    const float* r = p.resid + (int64_t)row * p.ldr + col0;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const f32x4 rv = *(const f32x4*)(r + 4 * q);
+      f32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; e++) o[e] = rv[e] + x[4 * q + e];
+      *(f32x4*)((float*)p.C + ci + 4 * q) = o;
+    }
+  } else if constexpr (EPI == EPI_BIAS_GELU) {
+    float* u = p.aux + (int64_t)row * p.ldaux + col0;
+#pragma unroll
+    for (int q = 0; q < 4; q++) *(f32x4*)(u + 4 * q) = (f32x4){x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; e++) o[e] = (bf16)gelu_f(x[8 * q + e]);
+      *(bf16x8*)((bf16*)p.C + ci + 8 * q) = o;
+    }
+  } else if constexpr (EPI == EPI_F32) {
+#pragma unroll
+    for (int q = 0; q < 4; q++) *(f32x4*)((float*)p.C + ci + 4 * q) = (f32x4){x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
+  } else if constexpr (EPI == EPI_GELU_BWD) {
+    const float* u = p.aux + (int64_t)row * p.ldaux + col0;
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      const f32x4 u0 = *(const f32x4*)(u + 8 * q), u1 = *(const f32x4*)(u + 8 * q + 4);
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        o[e] = (bf16)(x[8 * q + e] * gelu_grad_f(u0[e]));
+        o[4 + e] = (bf16)(x[8 * q + 4 + e] * gelu_grad_f(u1[e]));
+      }
+      *(bf16x8*)((bf16*)p.C + ci + 8 * q) = o;
+    }
+  } else {  // EPI_ACC
+    if (gridDim.z > 1) {
+      float* d = p.part + ((int64_t)blockIdx.z * p.M + row) * p.N + col0;
+#pragma unroll
+      for (int q = 0; q < 4; q++) *(f32x4*)(d + 4 * q) = (f32x4){x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
+    } else {
+      float* c = (float*)p.C + ci;
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        f32x4 o = (f32x4){x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
+        if (p.beta != 0.f) o += *(const f32x4*)(c + 4 * q);
+        *(f32x4*)(c + 4 * q) = o;
+      }
     }
   }
 }
@@ -363,27 +448,29 @@ __device__ inline bf16x8 frag_mc(const char* lds, int mbase) {
   return f;
 }
 
+// Grouped tile order: runs of 8 tile-rows, column by column, so that tiles in
+// flight together share A and B panels in L2.
+__device__ inline void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int GM = 8;
+  const int group = GM * tiles_n;
+  const int first_m = (t / group) * GM;
+  const int gsz = min(tiles_m - first_m, GM);
+  tm = first_m + (t % group) % gsz;
+  tn = (t % group) / gsz;
+}
+
+// One output tile over k-slices [s0, s1) of 32. With park == nullptr the fused
+// epilogue is applied; otherwise the raw fp32 sums go to park (BM_ x BN_, row-major).
+// Ends with a barrier, so the LDS may be reused by the caller.
 template <int BM_, int BN_, int WM_, int WN_, int STAGES, bool AK, bool BK_, int EPI>
-__global__ __launch_bounds__(64 * WM_ * WN_) void gemm_dma_kernel(GemmArgs p) {
+__device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, int tn, int s0, int s1,
+                                         float* park) {
   constexpr int NW = WM_ * WN_;
   constexpr int TM = BM_ / WM_, TN = BN_ / WN_;
   constexpr int FM = TM / 16, FN = TN / 16;
   constexpr int AB = BM_ * 32 * 2, BB = BN_ * 32 * 2, SB = AB + BB;
   constexpr int LPS = (AB + BB) / 1024 / NW;     // load instructions per stage per wave
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * SB];
-
-  const int tiles_m = (p.M + BM_ - 1) / BM_, tiles_n = (p.N + BN_ - 1) / BN_;
-  const int total = tiles_m * tiles_n;
-  int bid = blockIdx.x;
-  if (total % 8 == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
-  constexpr int GM = 8;
-  const int group = GM * tiles_n;
-  const int first_m = (bid / group) * GM;
-  const int gsz = min(tiles_m - first_m, GM);
-  const int tm = first_m + (bid % group) % gsz;
-  const int tn = (bid % group) / gsz;
   const int m0 = tm * BM_, n0 = tn * BN_;
-
   const bf16* A = (const bf16*)p.A;
   const bf16* B = (const bf16*)p.B;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -395,13 +482,10 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void gemm_dma_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < FN; j++) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  const int kb = blockIdx.z * p.kchunk;
-  const int ke = min(p.K, kb + p.kchunk);
-  const int nk = (ke - kb) / 32;
-
+  const int nk = s1 - s0;
   auto issue = [&](int t) {
     char* st = smem + (t % STAGES) * SB;
-    const int k0 = kb + t * 32;
+    const int k0 = (s0 + t) * 32;
     if constexpr (AK) dma_kc<BM_, NW>(A, p.lda, m0, p.M, k0, st, wave, lane);
     else dma_mc<BM_, NW>(A, p.lda, m0, p.M, k0, st, wave, lane);
     if constexpr (BK_) dma_kc<BN_, NW>(B, p.ldb, n0, p.N, k0, st + AB, wave, lane);
@@ -413,7 +497,6 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void gemm_dma_kernel(GemmArgs p) {
     if (t < nk) issue(t);
 
   for (int t = 0; t < nk; t++) {
-    // stage t complete: later stages (up to STAGES-2 of them) may still be in flight
     // A plain s_barrier: __syncthreads() would also wait for every global->LDS
     // load still in flight, which would serialise the pipeline. LDS reads of the
     // previous slice are complete (their MFMAs consumed them) before the barrier.
@@ -444,21 +527,120 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void gemm_dma_kernel(GemmArgs p) {
       for (int j = 0; j < FN; j++) acc[i][j] = Mfma<bf16>::mma(af[i], bfr[j], acc[i][j]);
   }
 
+  // Epilogue through LDS: each wave parks one 16-row block of its TM x TN
+  // quadrant, then every lane handles 16 contiguous columns of one row, so bias,
+  // residual and GELU inputs are read and outputs written as vectors.
+  __syncthreads();   // every wave is done with the stage buffers
+  constexpr int ELD = TN + 4;
+  float* scr = (float*)smem + wave * 16 * ELD;
+  const int er = lane >> 2, ec = (lane & 3) * 16;
+  const int col0 = n0 + wn * TN + ec;
+  const bool vec = (col0 + 16 <= p.N) && p.c_vec;
 #pragma unroll
   for (int i = 0; i < FM; i++) {
 #pragma unroll
-    for (int j = 0; j < FN; j++) {
-      const int col = n0 + wn * TN + j * 16 + (lane & 15);
-      if (col >= p.N) continue;
-      const float bias = epi_bias<EPI>(p, col);
+    for (int j = 0; j < FN; j++)
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const int row = m0 + wm * TM + i * 16 + (lane >> 4) * 4 + e;
-        if (row < p.M) epi_store<bf16, EPI>(p, row, col, acc[i][j][e], bias);
-      }
+      for (int e = 0; e < 4; e++) scr[(4 * (lane >> 4) + e) * ELD + j * 16 + (lane & 15)] = acc[i][j][e];
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const f32x4 t = *(const f32x4*)(scr + er * ELD + ec + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; e++) v[4 * q + e] = t[e];
+    }
+    const int rt = wm * TM + i * 16 + er;        // row within the tile
+    if (park) {
+      float* d = park + (int64_t)rt * BN_ + wn * TN + ec;
+#pragma unroll
+      for (int q = 0; q < 4; q++) *(f32x4*)(d + 4 * q) = (f32x4){v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+    } else {
+      const int row = m0 + rt;
+      if (row < p.M && col0 < p.N) epi_store16<EPI>(p, row, col0, v, vec);
     }
   }
+  __syncthreads();
 }
+
+template <int BM_, int BN_, int WM_, int WN_, int STAGES, bool AK, bool BK_, int EPI>
+__global__ __launch_bounds__(64 * WM_ * WN_) void gemm_dma_kernel(GemmArgs p) {
+  constexpr int SB = (BM_ + BN_) * 32 * 2;
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * SB];
+  const int tiles_m = (p.M + BM_ - 1) / BM_, tiles_n = (p.N + BN_ - 1) / BN_;
+  const int total = tiles_m * tiles_n;
+  // the hardware deals workgroups round-robin to the 8 XCDs; give each XCD a
+  // contiguous run of tiles
+  int bid = blockIdx.x;
+  if (total % 8 == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+  int tm, tn;
+  tile_coords(bid, tiles_m, tiles_n, tm, tn);
+  const int s0 = blockIdx.z * (p.kchunk / 32);
+  const int s1 = min(p.K, (int)(blockIdx.z + 1) * p.kchunk) / 32;
+  dma_tile<BM_, BN_, WM_, WN_, STAGES, AK, BK_, EPI>(p, smem, tm, tn, s0, s1, nullptr);
+}
+
+// Stream-K: gridDim.x workgroups share the tiles x (K/32) slice-units evenly, each a
+// contiguous range; a tile cut between workgroups is parked as fp32 partial sums
+// (slot = tile * maxseg + segment) and finished by sk_fixup_kernel in a fixed order.
+__device__ inline int sk_owner(long long x, int W, long long U) { return (int)(((x + 1) * W - 1) / U); }
+
+template <int BM_, int BN_, int WM_, int WN_, int STAGES, bool AK, bool BK_, int EPI>
+__global__ __launch_bounds__(64 * WM_ * WN_) void gemm_sk_kernel(GemmArgs p, float* ws, int maxseg) {
+  constexpr int SB = (BM_ + BN_) * 32 * 2;
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * SB];
+  const int tiles_m = (p.M + BM_ - 1) / BM_, tiles_n = (p.N + BN_ - 1) / BN_;
+  const int KI = p.K / 32;
+  const int W = gridDim.x, w = blockIdx.x;
+  const long long U = (long long)tiles_m * tiles_n * KI;
+  const long long beg = (long long)w * U / W, end = (long long)(w + 1) * U / W;
+  for (long long x = beg; x < end;) {
+    const int t = (int)(x / KI);
+    const int s0 = (int)(x - (long long)t * KI);
+    const int s1 = (int)min((long long)KI, end - (long long)t * KI);
+    const int first = sk_owner((long long)t * KI, W, U);
+    const int last = sk_owner((long long)t * KI + KI - 1, W, U);
+    float* park = nullptr;
+    if (first != last) park = ws + ((int64_t)t * maxseg + (w - first)) * (BM_ * BN_);
+    int tm, tn;
+    tile_coords(t, tiles_m, tiles_n, tm, tn);
+    dma_tile<BM_, BN_, WM_, WN_, STAGES, AK, BK_, EPI>(p, smem, tm, tn, s0, s1, park);
+    x = (long long)t * KI + s1;
+  }
+}
+
+// One workgroup per 16 rows of a split tile (blockIdx.y picks the rows), one
+// thread per 16-column run: sums the tile's parked partials in segment order and
+// applies the epilogue.
+template <int BM_, int BN_, int EPI>
+__global__ __launch_bounds__(256) void sk_fixup_kernel(GemmArgs p, const float* __restrict__ ws, int maxseg, int W) {
+  static_assert(BN_ == 256, "one thread per 16 columns of a 256-wide tile row");
+  const int tiles_m = (p.M + BM_ - 1) / BM_, tiles_n = (p.N + BN_ - 1) / BN_;
+  const int KI = p.K / 32;
+  const long long U = (long long)tiles_m * tiles_n * KI;
+  const int t = blockIdx.x;
+  const int first = sk_owner((long long)t * KI, W, U);
+  const int nseg = sk_owner((long long)t * KI + KI - 1, W, U) - first + 1;
+  if (nseg == 1) return;
+  int tm, tn;
+  tile_coords(t, tiles_m, tiles_n, tm, tn);
+  const int r = blockIdx.y * 16 + (threadIdx.x >> 4), c0 = (threadIdx.x & 15) * 16;
+  const int row = tm * BM_ + r, col0 = tn * BN_ + c0;
+  if (row >= p.M || col0 >= p.N) return;
+  const float* src = ws + (int64_t)t * maxseg * (BM_ * BN_) + r * BN_ + c0;
+  float v[16];
+#pragma unroll
+  for (int e = 0; e < 16; e++) v[e] = 0.f;
+  for (int sg = 0; sg < nseg; sg++) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; q4++) {
+      const f32x4 x = *(const f32x4*)(src + (int64_t)sg * (BM_ * BN_) + 4 * q4);
+#pragma unroll
+      for (int e = 0; e < 4; e++) v[4 * q4 + e] += x[e];
+    }
+  }
+  epi_store16<EPI>(p, row, col0, v, p.c_vec && col0 + 16 <= p.N);
+}
+
 
 template <int BM_, int BN_, int WM_, int WN_, int STAGES, bool AK, bool BK_>
 static hipError_t dma_epi(const GemmArgs& a, int epi, int splits, hipStream_t s) {
@@ -481,6 +663,38 @@ static hipError_t dma_epi(const GemmArgs& a, int epi, int splits, hipStream_t s)
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int BM_, int BN_, int WM_, int WN_, int STAGES, bool AK, bool BK_>
+static hipError_t sk_epi(const GemmArgs& a, int epi, int W, float* ws, int maxseg, hipStream_t s) {
+  const int tiles = ((a.M + BM_ - 1) / BM_) * ((a.N + BN_ - 1) / BN_);
+  switch (epi) {
+#define GPT_SK_CASE(E)                                                                                             \
+  case E:                                                                                                          \
+    hipLaunchKernelGGL((gemm_sk_kernel<BM_, BN_, WM_, WN_, STAGES, AK, BK_, E>), dim3(W), dim3(64 * WM_ * WN_), 0, \
+                       s, a, ws, maxseg);                                                                          \
+    hipLaunchKernelGGL((sk_fixup_kernel<BM_, BN_, E>), dim3(tiles, BM_ / 16), dim3(256), 0, s, a,                 \
+                       (const float*)ws, maxseg, W);                                                               \
+    break;
+    GPT_SK_CASE(EPI_STORE)
+    GPT_SK_CASE(EPI_BIAS)
+    GPT_SK_CASE(EPI_BIAS_RESID)
+    GPT_SK_CASE(EPI_BIAS_GELU)
+    GPT_SK_CASE(EPI_F32)
+    GPT_SK_CASE(EPI_GELU_BWD)
+    GPT_SK_CASE(EPI_ACC)
+#undef GPT_SK_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int BM_, int BN_, int WM_, int WN_, int STAGES>
+static hipError_t sk_layout(const GemmDesc& d, const GemmArgs& a, int W, float* ws, int maxseg, hipStream_t s) {
+  if (d.a_kc && d.b_kc) return sk_epi<BM_, BN_, WM_, WN_, STAGES, true, true>(a, d.epi, W, ws, maxseg, s);
+  if (d.a_kc && !d.b_kc) return sk_epi<BM_, BN_, WM_, WN_, STAGES, true, false>(a, d.epi, W, ws, maxseg, s);
+  if (!d.a_kc && !d.b_kc) return sk_epi<BM_, BN_, WM_, WN_, STAGES, false, false>(a, d.epi, W, ws, maxseg, s);
+  return hipErrorInvalidValue;
 }
 
 template <int BM_, int BN_, int WM_, int WN_, int STAGES>
@@ -530,6 +744,18 @@ static hipError_t dispatch_layout(const GemmDesc& d, const GemmArgs& a, dim3 gri
   return hipErrorInvalidValue;  // m-contiguous A with k-contiguous B is not used by the step
 }
 
+static int num_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      n = cus;
+    else
+      n = 256;
+  }
+  return n;
+}
+
 hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
   if (d.M <= 0 || d.N <= 0) return hipSuccess;
   GemmArgs a;
@@ -540,6 +766,15 @@ hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
   auto vec_ok = [&](const void* ptr, int64_t ld) { return (ld % vw == 0) && ((uintptr_t)ptr % 16 == 0); };
   a.a_vec = vec_ok(d.A, d.lda);
   a.b_vec = vec_ok(d.B, d.ldb);
+  {
+    // vector epilogue: 16-byte aligned rows for every matrix the epilogue touches
+    bool cv = ((uintptr_t)d.C % 16 == 0) && (d.ldc % 8 == 0);
+    if (d.resid) cv = cv && ((uintptr_t)d.resid % 16 == 0) && (d.ldr % 4 == 0);
+    if (d.aux) cv = cv && ((uintptr_t)d.aux % 16 == 0) && (d.ldaux % 4 == 0);
+    if (d.bias) cv = cv && ((uintptr_t)d.bias % 16 == 0);
+    if (d.epi == EPI_ACC && d.split_ws) cv = cv && (d.N % 4 == 0) && ((uintptr_t)d.split_ws % 16 == 0);
+    a.c_vec = cv;
+  }
   // The pipelined 256x256 kernel loads 16-byte vectors straight into LDS with no
   // edge handling along k: it needs bf16, K a multiple of 32, aligned operands and,
   // for m-contiguous operands, a row count that is a multiple of 8.
@@ -567,6 +802,23 @@ hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
     }
   }
   hipError_t e;
+  // Stream-K over the whole chip for long contractions with too few output tiles
+  // (weight gradients, K = B*T; the lm_head input gradient, K = vocab): every CU
+  // gets the same number of k-slices. Measured on gfx950 it loses to one tile per
+  // workgroup when K <= 3072, where parking partial tiles costs more than it saves.
+  if (pipelined && tiles < 2 * num_cus() && d.K >= 8192 && d.split_ws) {
+    const long long KI = d.K / 32;
+    const long long U = (long long)tiles * KI;
+    const int W = (int)std::min<long long>(num_cus(), U);
+    const long long per = U / W;
+    const int maxseg = per > 0 ? (int)((KI + per - 1) / per + 1) : 1;
+    const size_t need = (size_t)tiles * maxseg * 256 * 256;
+    if (per >= 4 && need <= d.split_ws_floats) {
+      a.kchunk = d.K;
+      a.part = nullptr;
+      return sk_layout<256, 256, 2, 4, 4>(d, a, W, d.split_ws, maxseg, s);
+    }
+  }
   if (pipelined) {
     e = dma_layout<256, 256, 2, 4, 4>(d, a, S, s);
   } else {

@@ -57,8 +57,14 @@ hipError_t launch_layernorm_bwd(const float* dy, const float* x, const float* me
 constexpr int COLSUM_ROWS = 64;
 hipError_t launch_colsum_partial(const void* X, bool bf16_in, int64_t ldx, int M, int N, float* part,
                                  hipStream_t s);
-// dst[n] = beta * dst[n] + sum_j part[j, n] (j in order).
+// dst[n] = beta * dst[n] + sum_j part[j, n] (fixed order).
 hipError_t launch_colsum_final(const float* part, int nblk, int N, float* dst, float beta, hipStream_t s);
+// Up to three such reductions over equally shaped partials in one launch.
+struct ColsumJobs {
+  const float* part[3];
+  float* dst[3];
+};
+hipError_t launch_colsum_final_multi(const ColsumJobs& jobs, int njobs, int nblk, int N, float beta, hipStream_t s);
 
 // Row-wise softmax cross-entropy over Vp columns of z (operand type, row stride ldz).
 // Writes row_loss[m] = lse - z[m, y[m]] and overwrites z with

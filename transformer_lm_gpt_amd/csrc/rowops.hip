@@ -212,29 +212,38 @@ hipError_t launch_colsum_partial(const void* X, bool bf16_in, int64_t ldx, int M
   return hipGetLastError();
 }
 
-// 32 columns per workgroup, 8 row groups: each thread sums every eighth partial
-// in order, then the 8 group sums are added in a fixed order.
-__global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part, int nblk, int N,
-                                                           float* dst, float beta) {
-  __shared__ float red[8][32];
-  const int cl = threadIdx.x & 31, grp = threadIdx.x >> 5;
-  const int col = blockIdx.x * 32 + cl;
+// 16 columns per workgroup, 16 row groups: each thread sums every 16th partial in
+// order, then the 16 group sums are added in a fixed order. blockIdx.y selects
+// one of up to three independent (partials, destination) jobs.
+__global__ __launch_bounds__(256) void colsum_final_kernel(ColsumJobs jobs, int nblk, int N, float beta) {
+  __shared__ float red[16][17];
+  const float* __restrict__ part = jobs.part[blockIdx.y];
+  float* dst = jobs.dst[blockIdx.y];
+  const int cl = threadIdx.x & 15, grp = threadIdx.x >> 4;
+  const int col = blockIdx.x * 16 + cl;
   float s = 0.f;
   if (col < N)
-    for (int j = grp; j < nblk; j += 8) s += part[(int64_t)j * N + col];
+    for (int j = grp; j < nblk; j += 16) s += part[(int64_t)j * N + col];
   red[grp][cl] = s;
   __syncthreads();
   if (grp == 0 && col < N) {
     float t = red[0][cl];
 #pragma unroll
-    for (int q = 1; q < 8; q++) t += red[q][cl];
+    for (int q = 1; q < 16; q++) t += red[q][cl];
     dst[col] = (beta != 0.f ? beta * dst[col] : 0.f) + t;
   }
 }
 
-hipError_t launch_colsum_final(const float* part, int nblk, int N, float* dst, float beta, hipStream_t s) {
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((N + 31) / 32), dim3(256), 0, s, part, nblk, N, dst, beta);
+hipError_t launch_colsum_final_multi(const ColsumJobs& jobs, int njobs, int nblk, int N, float beta, hipStream_t s) {
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((N + 15) / 16, njobs), dim3(256), 0, s, jobs, nblk, N, beta);
   return hipGetLastError();
+}
+
+hipError_t launch_colsum_final(const float* part, int nblk, int N, float* dst, float beta, hipStream_t s) {
+  ColsumJobs j{};
+  j.part[0] = part;
+  j.dst[0] = dst;
+  return launch_colsum_final_multi(j, 1, nblk, N, beta, s);
 }
 
 // ----------------------------------------------------------------------------- cross-entropy
@@ -293,8 +302,82 @@ __global__ __launch_bounds__(256) void xent_kernel(T* z, int64_t ldz, const int3
   }
 }
 
+// bf16 logits rows up to XENT_LDS_MAX columns: the row is read once from HBM into
+// LDS with 16-byte loads while the running max and sum are formed, then the
+// gradient row is written back from LDS with 16-byte stores. 1024 threads per row.
+constexpr int XENT_LDS_MAX = 57344;     // 112 KB of bf16
+__global__ __launch_bounds__(1024) void xent_lds_kernel(bf16* z, int64_t ldz, const int32_t* __restrict__ y,
+                                                        float* __restrict__ row_loss, int Vp, float grad_scale) {
+  extern __shared__ __attribute__((aligned(16))) bf16 zs[];
+  __shared__ float red_m[16], red_s[16];
+  __shared__ float s_lse;
+  const int row = blockIdx.x;
+  bf16* zr = z + (int64_t)row * ldz;
+  const int tgt = y[row];
+  const int nv = Vp / 8;                     // Vp is a multiple of 8 here
+  float m = -INFINITY, s = 0.f;
+  for (int i = threadIdx.x; i < nv; i += 1024) {
+    const bf16x8 v = *(const bf16x8*)(zr + 8 * i);
+    *(bf16x8*)(zs + 8 * i) = v;
+    float vm = (float)v[0];
+#pragma unroll
+    for (int e = 1; e < 8; e++) vm = fmaxf(vm, (float)v[e]);
+    const float mn = fmaxf(m, vm);
+    float add = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) add += __expf((float)v[e] - mn);
+    s = (m == -INFINITY ? 0.f : s * __expf(m - mn)) + add;
+    m = mn;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, WAVE), s2 = __shfl_xor(s, o, WAVE);
+    const float mm = fmaxf(m, m2);
+    s = (m == -INFINITY ? 0.f : s * __expf(m - mm)) + (m2 == -INFINITY ? 0.f : s2 * __expf(m2 - mm));
+    m = mm;
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red_m[w] = m;
+    red_s[w] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float mm = red_m[0];
+    for (int i = 1; i < 16; i++) mm = fmaxf(mm, red_m[i]);
+    float ss = 0.f;
+    for (int i = 0; i < 16; i++) ss += red_m[i] == -INFINITY ? 0.f : red_s[i] * __expf(red_m[i] - mm);
+    const float lse = mm + logf(ss);
+    s_lse = lse;
+    const bool ok = tgt >= 0 && tgt < Vp;   // an id outside the table yields a NaN loss
+    row_loss[row] = lse - (ok ? (float)zs[tgt] : __builtin_nanf(""));
+  }
+  __syncthreads();
+  const float lse = s_lse;
+  for (int i = threadIdx.x; i < nv; i += 1024) {
+    const bf16x8 v = *(const bf16x8*)(zs + 8 * i);
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      const int c = 8 * i + e;
+      o[e] = (bf16)((__expf((float)v[e] - lse) - (c == tgt ? 1.f : 0.f)) * grad_scale);
+    }
+    *(bf16x8*)(zr + 8 * i) = o;
+  }
+}
+
 hipError_t launch_xent(void* z, bool bf16_z, int64_t ldz, const int32_t* y, float* row_loss, int M, int Vp,
                        float grad_scale, hipStream_t s) {
+  if (bf16_z && Vp % 8 == 0 && ldz % 8 == 0 && Vp <= XENT_LDS_MAX && (uintptr_t)z % 16 == 0) {
+    const size_t lds = (size_t)Vp * 2;
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute((const void*)xent_lds_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(xent_lds_kernel, dim3(M), dim3(1024), lds, s, (bf16*)z, ldz, y, row_loss, Vp, grad_scale);
+    return hipGetLastError();
+  }
   if (bf16_z)
     hipLaunchKernelGGL(xent_kernel<bf16>, dim3(M), dim3(256), 0, s, (bf16*)z, ldz, y, row_loss, Vp, grad_scale);
   else

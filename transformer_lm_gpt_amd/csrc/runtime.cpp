@@ -150,6 +150,13 @@ int run(gpt_model* h, const char* family, const char* what, F&& f) {
   return hip_check(h, e, what);
 }
 
+// GEMM launch with the shared split / stream-K workspace attached.
+hipError_t gemm(gpt_model* h, GemmDesc g, bool bf) {
+  g.split_ws = (float*)((char*)h->buf.workspace + h->split.off);
+  g.split_ws_floats = h->split_floats;
+  return launch_gemm(g, bf, h->stream);
+}
+
 #define RUN(fam, what, call)                                     \
   do {                                                           \
     int rc__ = run(h, fam, what, [&]() { return (call); });      \
@@ -260,7 +267,10 @@ void plan(gpt_model* h) {
   h->emb_keys = w.take((size_t)embed_bwd_sort_size((int)M) * 4);
   h->emb_piece = w.take(M * d * fb);
   h->norm_part = w.take(NORM_BLOCKS * fb);
+  // split-K partials, or stream-K partial tiles of 256 x 256 (at most about
+  // CUs + 2 * tiles of them for the < 512-tile GEMMs that use stream-K)
   h->split_floats = 16 * (size_t)d * d + 4096;
+  if (M >= 256 && d >= 256) h->split_floats = std::max(h->split_floats, (size_t)1664 * 256 * 256);
   h->split = w.take(h->split_floats * fb);
   h->part_r = w.take(ln_blk * d * fb);
   h->opt = w.take(sizeof(OptState));
@@ -289,9 +299,16 @@ int ln_bwd(gpt_model* h, const float* dy, const float* x, const float* mean, con
       launch_layernorm_bwd(dy, x, mean, rstd, P(h, gname), dres, ws<float>(h, h->dres), dx_op, h->bf16, pg, pb, pr,
                            M, h->d, h->stream));
   const int nblk = (M + LN_BWD_ROWS - 1) / LN_BWD_ROWS;
-  RUN("colsum", "ln_dgamma", launch_colsum_final(pg, nblk, h->d, G(h, gname), beta, h->stream));
-  RUN("colsum", "ln_dbeta", launch_colsum_final(pb, nblk, h->d, G(h, bname), beta, h->stream));
-  if (resid_bias) RUN("colsum", "resid_bias", launch_colsum_final(pr, nblk, h->d, G(h, resid_bias), beta, h->stream));
+  ColsumJobs jobs{};
+  jobs.part[0] = pg;
+  jobs.dst[0] = G(h, gname);
+  jobs.part[1] = pb;
+  jobs.dst[1] = G(h, bname);
+  if (resid_bias) {
+    jobs.part[2] = pr;
+    jobs.dst[2] = G(h, resid_bias);
+  }
+  RUN("colsum", "ln_param_grads", launch_colsum_final_multi(jobs, resid_bias ? 3 : 2, nblk, h->d, beta, h->stream));
   return GPT_OK;
 }
 
@@ -315,7 +332,7 @@ int forward_to_logits(gpt_model* h, int B, int T) {
       GemmDesc g = gemm_desc(act(h, la.ln1), d, true, Wop(h, p + "attn.w"), d, true, act(h, la.qkv), 3 * d, M,
                              3 * d, d, EPI_BIAS);
       g.bias = P(h, p + "attn.b");
-      RUN("gemm_fwd", "qkv_fwd", launch_gemm(g, bf, s));
+      RUN("gemm_fwd", "qkv_fwd", gemm(h, g, bf));
     }
     RUN("attn_fwd", "attn_fwd", launch_attn_fwd(act(h, la.qkv), act(h, la.att), act<float>(h, la.lse), bf, B, T, h->H, h->hd, s));
     {
@@ -324,7 +341,7 @@ int forward_to_logits(gpt_model* h, int B, int T) {
       g.bias = P(h, p + "proj.b");
       g.resid = x;
       g.ldr = d;
-      RUN("gemm_fwd", "proj_fwd", launch_gemm(g, bf, s));
+      RUN("gemm_fwd", "proj_fwd", gemm(h, g, bf));
     }
     RUN("layernorm", "ln2_fwd",
         launch_layernorm_fwd(xmid, P(h, p + "ln2.g"), P(h, p + "ln2.b"), act(h, la.ln2), bf,
@@ -335,7 +352,7 @@ int forward_to_logits(gpt_model* h, int B, int T) {
       g.bias = P(h, p + "fc.b");
       g.aux = act<float>(h, la.u);
       g.ldaux = 4 * d;
-      RUN("gemm_fwd", "fc_fwd", launch_gemm(g, bf, s));
+      RUN("gemm_fwd", "fc_fwd", gemm(h, g, bf));
     }
     {
       GemmDesc g = gemm_desc(act(h, la.h), 4 * d, true, Wop(h, p + "fcproj.w"), 4 * d, true, xnext, d, M, d,
@@ -343,7 +360,7 @@ int forward_to_logits(gpt_model* h, int B, int T) {
       g.bias = P(h, p + "fcproj.b");
       g.resid = xmid;
       g.ldr = d;
-      RUN("gemm_fwd", "fcproj_fwd", launch_gemm(g, bf, s));
+      RUN("gemm_fwd", "fcproj_fwd", gemm(h, g, bf));
     }
   }
   RUN("layernorm", "lnf_fwd",
@@ -352,7 +369,7 @@ int forward_to_logits(gpt_model* h, int B, int T) {
   {
     GemmDesc g = gemm_desc(act(h, h->lnf), d, true, Wop(h, "wte"), d, true, act(h, h->logits), h->ldz, M, h->Vp, d,
                            EPI_STORE);
-    RUN("lm_head_fwd", "lm_head_fwd", launch_gemm(g, bf, s));
+    RUN("lm_head_fwd", "lm_head_fwd", gemm(h, g, bf));
   }
   return GPT_OK;
 }
@@ -543,11 +560,9 @@ int gpt_backward(gpt_model* h) {
     GemmDesc g = gemm_desc(act(h, h->logits), h->ldz, false, act(h, h->lnf), d, false, G(h, "wte"), d, h->Vp, d, M,
                            EPI_ACC);
     g.beta = beta;
-    g.split_ws = ws<float>(h, h->split);
-    g.split_ws_floats = h->split_floats;
-    RUN("gemm_wgrad", "lm_head_wgrad", launch_gemm(g, bf, s));
+    RUN("gemm_wgrad", "lm_head_wgrad", gemm(h, g, bf));
     GemmDesc g2 = gemm_desc(act(h, h->logits), h->ldz, true, Wop(h, "wte"), d, false, dln, d, M, d, h->Vp, EPI_F32);
-    RUN("gemm_dgrad", "lm_head_dgrad", launch_gemm(g2, bf, s));
+    RUN("gemm_dgrad", "lm_head_dgrad", gemm(h, g2, bf));
   }
   if ((rc = ln_bwd(h, dln, act<float>(h, h->x_final), act<float>(h, h->lnf_mean), act<float>(h, h->lnf_rstd),
                    "lnf.g", "lnf.b", nullptr, nullptr, M, beta)))
@@ -562,20 +577,16 @@ int gpt_backward(gpt_model* h) {
                              EPI_GELU_BWD);
       g.aux = act<float>(h, la.u);
       g.ldaux = 4 * d;
-      RUN("gemm_dgrad", "fcproj_dgrad", launch_gemm(g, bf, s));
+      RUN("gemm_dgrad", "fcproj_dgrad", gemm(h, g, bf));
       GemmDesc gw = gemm_desc(dres_opnd, d, false, act(h, la.h), 4 * d, false, G(h, p + "fcproj.w"), 4 * d, d, 4 * d,
                               M, EPI_ACC);
       gw.beta = beta;
-      gw.split_ws = ws<float>(h, h->split);
-      gw.split_ws_floats = h->split_floats;
-      RUN("gemm_wgrad", "fcproj_wgrad", launch_gemm(gw, bf, s));
+      RUN("gemm_wgrad", "fcproj_wgrad", gemm(h, gw, bf));
       GemmDesc g2 = gemm_desc(du, 4 * d, true, Wop(h, p + "fc.w"), d, false, dln, d, M, d, 4 * d, EPI_F32);
-      RUN("gemm_dgrad", "fc_dgrad", launch_gemm(g2, bf, s));
+      RUN("gemm_dgrad", "fc_dgrad", gemm(h, g2, bf));
       GemmDesc gw2 = gemm_desc(du, 4 * d, false, act(h, la.ln2), d, false, G(h, p + "fc.w"), d, 4 * d, d, M, EPI_ACC);
       gw2.beta = beta;
-      gw2.split_ws = ws<float>(h, h->split);
-      gw2.split_ws_floats = h->split_floats;
-      RUN("gemm_wgrad", "fc_wgrad", launch_gemm(gw2, bf, s));
+      RUN("gemm_wgrad", "fc_wgrad", gemm(h, gw2, bf));
       if ((rc = colsum(h, du, bf, 4 * d, M, 4 * d, G(h, p + "fc.b"), beta))) return rc;
       const std::string fcproj_b = p + "fcproj.b";
       if ((rc = ln_bwd(h, dln, act<float>(h, la.xmid), act<float>(h, la.ln2_mean), act<float>(h, la.ln2_rstd),
@@ -585,23 +596,19 @@ int gpt_backward(gpt_model* h) {
     // ---- attention: xmid = x + attn(LN1(x)) Wo^T + bo ; dres now holds d xmid
     {
       GemmDesc g = gemm_desc(dres_opnd, d, true, Wop(h, p + "proj.w"), d, false, dO, d, M, d, d, EPI_STORE);
-      RUN("gemm_dgrad", "proj_dgrad", launch_gemm(g, bf, s));
+      RUN("gemm_dgrad", "proj_dgrad", gemm(h, g, bf));
       GemmDesc gw = gemm_desc(dres_opnd, d, false, act(h, la.att), d, false, G(h, p + "proj.w"), d, d, d, M, EPI_ACC);
       gw.beta = beta;
-      gw.split_ws = ws<float>(h, h->split);
-      gw.split_ws_floats = h->split_floats;
-      RUN("gemm_wgrad", "proj_wgrad", launch_gemm(gw, bf, s));
+      RUN("gemm_wgrad", "proj_wgrad", gemm(h, gw, bf));
       RUN("attn_bwd", "attn_bwd",
           launch_attn_bwd(act(h, la.qkv), act(h, la.att), dO, act<float>(h, la.lse), ws<float>(h, h->attnD), dqkv, bf,
                           B, T, h->H, h->hd, s));
       GemmDesc g2 = gemm_desc(dqkv, 3 * d, true, Wop(h, p + "attn.w"), d, false, dln, d, M, d, 3 * d, EPI_F32);
-      RUN("gemm_dgrad", "qkv_dgrad", launch_gemm(g2, bf, s));
+      RUN("gemm_dgrad", "qkv_dgrad", gemm(h, g2, bf));
       GemmDesc gw2 = gemm_desc(dqkv, 3 * d, false, act(h, la.ln1), d, false, G(h, p + "attn.w"), d, 3 * d, d, M,
                                EPI_ACC);
       gw2.beta = beta;
-      gw2.split_ws = ws<float>(h, h->split);
-      gw2.split_ws_floats = h->split_floats;
-      RUN("gemm_wgrad", "qkv_wgrad", launch_gemm(gw2, bf, s));
+      RUN("gemm_wgrad", "qkv_wgrad", gemm(h, gw2, bf));
       if ((rc = colsum(h, dqkv, bf, 3 * d, M, 3 * d, G(h, p + "attn.b"), beta))) return rc;
       const std::string proj_b = p + "proj.b";
       if ((rc = ln_bwd(h, dln, act<float>(h, la.x), act<float>(h, la.ln1_mean), act<float>(h, la.ln1_rstd),
