@@ -138,7 +138,7 @@ def main(argv=None):
         avg_ms = kern_ms / kern_n
         if a.kernel == "lm_head_fwd":
             work = 2.0 * B * T * cfg.padded_vocab * cfg.n_embd          # FLOPs per launch
-            roof = {"kernel": "lm_head_fwd (gemm_kernel<bf16, k-contig, k-contig, store>)", "bound": "mfma",
+            roof = {"kernel": "lm_head forward GEMM (gemm_dma_kernel 256x256, bf16, store epilogue)", "bound": "mfma",
                     "achieved": round(work / (avg_ms / 1e3) / 1e12, 2), "peak": peak / 1e12, "unit": "TFLOP/s",
                     "frac": round(work / (avg_ms / 1e3) / peak, 4), "traffic": None,
                     "avg_launch_ms": round(avg_ms, 4), "launches": kern_n,
