@@ -80,7 +80,7 @@ typedef struct gpt_sizes {
   size_t param_bytes;      /* fp32 master weights                                    */
   size_t grad_bytes;       /* fp32 gradients                                         */
   size_t m_bytes, v_bytes; /* fp32 Adam moments                                      */
-  size_t shadow_bytes;     /* bf16 copy of the weights (0 in fp32 mode)              */
+  size_t shadow_bytes;     /* bf16 copies of the weights (0 in fp32 mode)            */
   size_t activation_bytes; /* saved forward activations                              */
   size_t workspace_bytes;  /* backward scratch, reductions, device state             */
 } gpt_sizes;
@@ -98,7 +98,9 @@ typedef struct gpt_buffers {
   void* grads;        /* fp32 [n_flat]                        written by backward   */
   void* m;            /* fp32 [n_flat]                        Adam first moment     */
   void* v;            /* fp32 [n_flat]                        Adam second moment    */
-  void* shadow;       /* bf16 [n_flat] (NULL in fp32 mode)    weights as GEMM input */
+  void* shadow;       /* bf16 [2 * n_flat] (NULL in fp32 mode): the weights as GEMM
+                         input, then at offset n_flat each 2-D weight transposed
+                         ([in, out] at the tensor's own offset)                    */
   void* activations;  /* activation_bytes, 256-byte aligned                          */
   void* workspace;    /* workspace_bytes, 256-byte aligned                           */
 } gpt_buffers;
@@ -152,7 +154,7 @@ int gpt_zero_grad(gpt_model* h);
  * clip > 0 else 1; t += 1; for every element: g' = coef g,
  * m = beta1 m + (1 - beta1) g', v = beta2 v + (1 - beta2) g'^2,
  * p = p (1 - lr wd) [decayed tensors only] - lr (m / (1 - beta1^t)) /
- * (sqrt(v / (1 - beta2^t)) + eps); then refreshes the bf16 shadow.
+ * (sqrt(v / (1 - beta2^t)) + eps); then refreshes both bf16 shadows.
  * d_grad_norm (nullable) receives n (before clipping). If n is not finite the
  * update is skipped on the device, t is not advanced, and the next gpt_sync
  * returns GPT_E_NONFINITE. */

@@ -55,7 +55,7 @@ def test_layout_matches_oracle(name, prec):
         decs = [dec for _, _, dec in spans]
         assert decs == sorted(decs, reverse=True)
         assert spans[-1][1] <= lay.sizes.n_flat and lay.sizes.n_flat % 256 == 0
-        assert lay.sizes.shadow_bytes == (lay.sizes.n_flat * 2 if prec == "bf16" else 0)
+        assert lay.sizes.shadow_bytes == (lay.sizes.n_flat * 4 if prec == "bf16" else 0)   # weights + transposed weights
         # round trip through the flat layout
         p = W.init_params(cfg, np.random.default_rng(0)) if cfg.padded_vocab < 1000 else None
         if p is not None:

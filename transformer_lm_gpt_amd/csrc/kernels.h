@@ -113,6 +113,13 @@ hipError_t launch_opt_prepare(const float* part, OptState* st, float clip, float
 hipError_t launch_adamw(float* p, const float* g, float* m, float* v, void* shadow_bf16, size_t n,
                         size_t n_decay, const OptState* st, float lr, float beta1, float beta2, float eps,
                         float wd, hipStream_t s);
+// Transposed bf16 copies of 2-D tensors: for every entry {offset, rows, cols} of the
+// device table, dst[offset + c * rows + r] = src[offset + r * cols + c].
+struct TransposeEntry {
+  int64_t offset, rows, cols, first_tile;   // first_tile: prefix sum of 64x64 tiles
+};
+hipError_t launch_transpose_bf16(const void* src, void* dst, const TransposeEntry* d_table, int n_entries,
+                                 int64_t total_tiles, hipStream_t s);
 // bf16 copy of n fp32 values.
 hipError_t launch_cast_bf16(const float* src, void* dst, size_t n, hipStream_t s);
 // Zero n 32-bit words with a fill kernel (safe inside captured graphs).

@@ -402,6 +402,43 @@ hipError_t launch_mean(const float* row_loss, int M, float* out, hipStream_t s) 
 }
 
 // ----------------------------------------------------------------------------- small utilities
+// 64 x 64 tiles of every 2-D weight, transposed through LDS with coalesced reads
+// and writes; the tensor of a tile is found by binary search over first_tile.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16* __restrict__ src, bf16* __restrict__ dst,
+                                                             const TransposeEntry* __restrict__ table, int n) {
+  __shared__ bf16 t[64][65];
+  const int64_t tile = blockIdx.x;
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (table[mid].first_tile <= tile) lo = mid;
+    else hi = mid - 1;
+  }
+  const TransposeEntry e = table[lo];
+  const int64_t local = tile - e.first_tile;
+  const int64_t tiles_c = (e.cols + 63) / 64;
+  const int64_t r0 = (local / tiles_c) * 64, c0 = (local % tiles_c) * 64;
+  const bf16* s0 = src + e.offset;
+  bf16* d0 = dst + e.offset;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int rr = i >> 6, cc = i & 63;
+    if (r0 + rr < e.rows && c0 + cc < e.cols) t[rr][cc] = s0[(r0 + rr) * e.cols + c0 + cc];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int cc = i >> 6, rr = i & 63;
+    if (r0 + rr < e.rows && c0 + cc < e.cols) d0[(c0 + cc) * e.rows + r0 + rr] = t[rr][cc];
+  }
+}
+
+hipError_t launch_transpose_bf16(const void* src, void* dst, const TransposeEntry* d_table, int n_entries,
+                                 int64_t total_tiles, hipStream_t s) {
+  if (total_tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)total_tiles), dim3(256), 0, s, (const bf16*)src,
+                     (bf16*)dst, d_table, n_entries);
+  return hipGetLastError();
+}
+
 __global__ void cast_bf16_kernel(const float* __restrict__ src, bf16* __restrict__ dst, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
     dst[i] = (bf16)src[i];

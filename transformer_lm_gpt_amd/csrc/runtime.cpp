@@ -74,8 +74,10 @@ struct gpt_model {
   size_t act_bytes = 0;
   // workspace
   Slice dres, dres_op, dln, du, dO, dqkv, attnD, part_g, part_b, part_r, colsum_part, emb_keys, emb_piece, norm_part,
-      opt, split;
+      opt, split, ttable;
   size_t split_floats = 0;
+  std::vector<TransposeEntry> tentries;   // 2-D weights whose transposed shadow the dgrads read
+  int64_t ttiles = 0;
   size_t ws_bytes = 0;
   // binding
   gpt_buffers buf{};
@@ -122,6 +124,11 @@ const void* Wop(gpt_model* h, const std::string& name) {
   return (const float*)h->buf.params + t->offset;
 }
 
+// Transposed weight ([in, out]) for the input-gradient GEMMs; bf16 mode only.
+const void* WopT(gpt_model* h, const std::string& name) {
+  return (const uint16_t*)h->buf.shadow + h->n_flat + find(h, name)->offset;
+}
+
 template <typename X = void>
 X* act(gpt_model* h, const Slice& s) { return (X*)((char*)h->buf.activations + s.off); }
 template <typename X = void>
@@ -155,6 +162,12 @@ hipError_t gemm(gpt_model* h, GemmDesc g, bool bf) {
   g.split_ws = (float*)((char*)h->buf.workspace + h->split.off);
   g.split_ws_floats = h->split_floats;
   return launch_gemm(g, bf, h->stream);
+}
+
+hipError_t transpose_shadow(gpt_model* h) {
+  return launch_transpose_bf16(h->buf.shadow, (uint16_t*)h->buf.shadow + h->n_flat,
+                               (const TransposeEntry*)((char*)h->buf.workspace + h->ttable.off), (int)h->tentries.size(),
+                               h->ttiles, h->stream);
 }
 
 #define RUN(fam, what, call)                                     \
@@ -273,6 +286,13 @@ void plan(gpt_model* h) {
   if (M >= 256 && d >= 256) h->split_floats = std::max(h->split_floats, (size_t)1664 * 256 * 256);
   h->split = w.take(h->split_floats * fb);
   h->part_r = w.take(ln_blk * d * fb);
+  for (const Tensor& t : h->tensors) {
+    if (t.ndim != 2 || t.name == "wpe") continue;
+    TransposeEntry e{(int64_t)t.offset, t.rows, t.cols, h->ttiles};
+    h->tentries.push_back(e);
+    h->ttiles += ((t.rows + 63) / 64) * ((t.cols + 63) / 64);
+  }
+  h->ttable = w.take(h->tentries.size() * sizeof(TransposeEntry));
   h->opt = w.take(sizeof(OptState));
   h->ws_bytes = w.total;
 }
@@ -453,7 +473,7 @@ int gpt_get_sizes(const gpt_model* h, gpt_sizes* out) {
   out->n_params = h->n_params;
   out->n_flat = h->n_flat;
   out->param_bytes = out->grad_bytes = out->m_bytes = out->v_bytes = h->n_flat * 4;
-  out->shadow_bytes = h->bf16 ? h->n_flat * 2 : 0;
+  out->shadow_bytes = h->bf16 ? h->n_flat * 2 * 2 : 0;
   out->activation_bytes = h->act_bytes;
   out->workspace_bytes = h->ws_bytes;
   return GPT_OK;
@@ -499,7 +519,14 @@ int gpt_init_state(gpt_model* h) {
   RUN("init", "zero m", launch_zero(h->buf.m, h->n_flat, s));
   RUN("init", "zero v", launch_zero(h->buf.v, h->n_flat, s));
   RUN("init", "zero optimizer state", launch_zero(ws(h, h->opt), sizeof(OptState) / 4, s));
-  if (h->bf16) RUN("init", "bf16 shadow", launch_cast_bf16((const float*)h->buf.params, h->buf.shadow, h->n_flat, s));
+  if (h->bf16) {
+    RUN("init", "bf16 shadow", launch_cast_bf16((const float*)h->buf.params, h->buf.shadow, h->n_flat, s));
+    hipError_t e = hipMemcpyAsync(ws(h, h->ttable), h->tentries.data(), h->tentries.size() * sizeof(TransposeEntry),
+                                  hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_check(h, e, "upload transpose table");
+    RUN("init", "transposed shadow", transpose_shadow(h));
+  }
   h->grads_fresh = true;
   h->fwd_pending = false;
   return GPT_OK;
@@ -561,7 +588,8 @@ int gpt_backward(gpt_model* h) {
                            EPI_ACC);
     g.beta = beta;
     RUN("gemm_wgrad", "lm_head_wgrad", gemm(h, g, bf));
-    GemmDesc g2 = gemm_desc(act(h, h->logits), h->ldz, true, Wop(h, "wte"), d, false, dln, d, M, d, h->Vp, EPI_F32);
+    GemmDesc g2 = bf ? gemm_desc(act(h, h->logits), h->ldz, true, WopT(h, "wte"), h->Vp, true, dln, d, M, d, h->Vp, EPI_F32)
+                     : gemm_desc(act(h, h->logits), h->ldz, true, Wop(h, "wte"), d, false, dln, d, M, d, h->Vp, EPI_F32);
     RUN("gemm_dgrad", "lm_head_dgrad", gemm(h, g2, bf));
   }
   if ((rc = ln_bwd(h, dln, act<float>(h, h->x_final), act<float>(h, h->lnf_mean), act<float>(h, h->lnf_rstd),
@@ -573,8 +601,9 @@ int gpt_backward(gpt_model* h) {
     const std::string p = "h" + std::to_string(l) + ".";
     // ---- MLP: x_{l+1} = xmid + gelu(LN2(xmid) Wfc^T + bfc) Wp^T + bp ; dres holds d x_{l+1}
     {
-      GemmDesc g = gemm_desc(dres_opnd, d, true, Wop(h, p + "fcproj.w"), 4 * d, false, du, 4 * d, M, 4 * d, d,
-                             EPI_GELU_BWD);
+      GemmDesc g = bf ? gemm_desc(dres_opnd, d, true, WopT(h, p + "fcproj.w"), d, true, du, 4 * d, M, 4 * d, d, EPI_GELU_BWD)
+                      : gemm_desc(dres_opnd, d, true, Wop(h, p + "fcproj.w"), 4 * d, false, du, 4 * d, M, 4 * d, d,
+                                  EPI_GELU_BWD);
       g.aux = act<float>(h, la.u);
       g.ldaux = 4 * d;
       RUN("gemm_dgrad", "fcproj_dgrad", gemm(h, g, bf));
@@ -582,7 +611,8 @@ int gpt_backward(gpt_model* h) {
                               M, EPI_ACC);
       gw.beta = beta;
       RUN("gemm_wgrad", "fcproj_wgrad", gemm(h, gw, bf));
-      GemmDesc g2 = gemm_desc(du, 4 * d, true, Wop(h, p + "fc.w"), d, false, dln, d, M, d, 4 * d, EPI_F32);
+      GemmDesc g2 = bf ? gemm_desc(du, 4 * d, true, WopT(h, p + "fc.w"), 4 * d, true, dln, d, M, d, 4 * d, EPI_F32)
+                       : gemm_desc(du, 4 * d, true, Wop(h, p + "fc.w"), d, false, dln, d, M, d, 4 * d, EPI_F32);
       RUN("gemm_dgrad", "fc_dgrad", gemm(h, g2, bf));
       GemmDesc gw2 = gemm_desc(du, 4 * d, false, act(h, la.ln2), d, false, G(h, p + "fc.w"), d, 4 * d, d, M, EPI_ACC);
       gw2.beta = beta;
@@ -595,7 +625,8 @@ int gpt_backward(gpt_model* h) {
     }
     // ---- attention: xmid = x + attn(LN1(x)) Wo^T + bo ; dres now holds d xmid
     {
-      GemmDesc g = gemm_desc(dres_opnd, d, true, Wop(h, p + "proj.w"), d, false, dO, d, M, d, d, EPI_STORE);
+      GemmDesc g = bf ? gemm_desc(dres_opnd, d, true, WopT(h, p + "proj.w"), d, true, dO, d, M, d, d, EPI_STORE)
+                      : gemm_desc(dres_opnd, d, true, Wop(h, p + "proj.w"), d, false, dO, d, M, d, d, EPI_STORE);
       RUN("gemm_dgrad", "proj_dgrad", gemm(h, g, bf));
       GemmDesc gw = gemm_desc(dres_opnd, d, false, act(h, la.att), d, false, G(h, p + "proj.w"), d, d, d, M, EPI_ACC);
       gw.beta = beta;
@@ -603,7 +634,8 @@ int gpt_backward(gpt_model* h) {
       RUN("attn_bwd", "attn_bwd",
           launch_attn_bwd(act(h, la.qkv), act(h, la.att), dO, act<float>(h, la.lse), ws<float>(h, h->attnD), dqkv, bf,
                           B, T, h->H, h->hd, s));
-      GemmDesc g2 = gemm_desc(dqkv, 3 * d, true, Wop(h, p + "attn.w"), d, false, dln, d, M, d, 3 * d, EPI_F32);
+      GemmDesc g2 = bf ? gemm_desc(dqkv, 3 * d, true, WopT(h, p + "attn.w"), 3 * d, true, dln, d, M, d, 3 * d, EPI_F32)
+                       : gemm_desc(dqkv, 3 * d, true, Wop(h, p + "attn.w"), d, false, dln, d, M, d, 3 * d, EPI_F32);
       RUN("gemm_dgrad", "qkv_dgrad", gemm(h, g2, bf));
       GemmDesc gw2 = gemm_desc(dqkv, 3 * d, false, act(h, la.ln1), d, false, G(h, p + "attn.w"), d, 3 * d, d, M,
                                EPI_ACC);
@@ -652,6 +684,7 @@ int gpt_adamw_step(gpt_model* h, float lr, float beta1, float beta2, float eps, 
       launch_adamw((float*)h->buf.params, (const float*)h->buf.grads, (float*)h->buf.m, (float*)h->buf.v,
                    h->bf16 ? h->buf.shadow : nullptr, h->n_flat, h->n_decay, st, lr, beta1, beta2, eps, weight_decay,
                    s));
+  if (h->bf16) RUN("adamw", "transposed shadow", transpose_shadow(h));
   h->grads_fresh = true;
   return GPT_OK;
 }
