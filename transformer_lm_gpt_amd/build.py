@@ -25,6 +25,9 @@ LIB = os.path.join(PKG, "libgpt.so")
 SOURCES = ["gemm.hip", "attention.hip", "rowops.hip", "embed_bwd.hip", "optim.hip", "runtime.cpp"]
 ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# per-source device flags: attention keeps its MFMA accumulators in ordinary VGPRs,
+# so the softmax arithmetic on them needs no copies out of the accumulation registers
+SOURCE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
 
 
@@ -39,7 +42,7 @@ def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
-        cmd[1:1] = [f"--offload-arch={ARCH}", *DEVICE_FLAGS]
+        cmd[1:1] = [f"--offload-arch={ARCH}", *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, [])]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -446,19 +446,25 @@ __device__ inline bf16x8 pack_p(const f32x4& lo, const f32x4& hi) {
   return f;
 }
 
-// Loads a 64-row tile (rows row0.., columns col0..col0+HDP of a row-major [*, ld]
-// source) into registers, zero past nrows: each thread holds HDP/32 units.
+// Buffer resource over `bytes` bytes from `base`: loads at or past the end read as
+// zero, so rows past the sequence need no branch.
+__device__ inline __amdgpu_buffer_rsrc_t range_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// A 64-row tile (rows row0.., columns col0..col0+HDP of a row-major [rows, ld]
+// bf16 source) staged through registers: each thread holds HDP/32 16-byte units.
 template <int HDP>
 struct TileRegs {
   static constexpr int NU = 64 * HDP / 8 / 256;
   bf16x8 v[NU];
-  __device__ inline void load(const bf16* src, int64_t ld, int row0, int nrows, int col0) {
+  __device__ inline void load(__amdgpu_buffer_rsrc_t src, int ld, int row0, int col0) {
 #pragma unroll
     for (int j = 0; j < NU; j++) {
       const int idx = threadIdx.x + 256 * j;
       const int r = idx / (HDP / 8), u = idx % (HDP / 8);
-      if (row0 + r < nrows) v[j] = *(const bf16x8*)(src + (int64_t)(row0 + r) * ld + col0 + u * 8);
-      else v[j] = (bf16x8){};
+      const int off = ((row0 + r) * ld + col0 + u * 8) * 2;
+      v[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(src, off, 0, 0));
     }
   }
   __device__ inline void store(bf16* t) const {
@@ -471,6 +477,27 @@ struct TileRegs {
   }
 };
 
+constexpr float LOG2E_F = 1.4426950408889634f;
+constexpr float LN2_F = 0.6931471805599453f;
+
+// Reductions over the four lanes l, l^16, l^32, l^48 that hold one column's four
+// 4-row groups of an MFMA output block. Every lane gets the same bits.
+__device__ inline float group_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float group_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// The exponentials run in base 2 with the 1/sqrt(hd) scale folded in: with
+// c = log2(e)/sqrt(hd), exp(S*scale - x) = exp2(S*c - x*log2(e)), one FMA and one
+// v_exp per score. Only the diagonal tile of a causal block needs the mask.
 template <int HDP>
 __global__ __launch_bounds__(256) void attn_fwd_v2(const bf16* __restrict__ qkv, bf16* __restrict__ o,
                                                    float* __restrict__ lse, int Tn, int H, float scale) {
@@ -479,13 +506,17 @@ __global__ __launch_bounds__(256) void attn_fwd_v2(const bf16* __restrict__ qkv,
   __shared__ __attribute__((aligned(16))) bf16 Ks[64 * HDP];
   __shared__ __attribute__((aligned(16))) bf16 Vs[64 * HDP];
   const int nqb = (Tn + 63) / 64;
-  const int qb = nqb - 1 - blockIdx.x;               // longest rows first
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  // (batch*head) varies fastest, so every block of a query-block index is issued
+  // before any shorter one (longest first keeps the tail short) and one head's
+  // blocks share an XCD's L2 (workgroups go round-robin over the 8 XCDs)
+  const int qb = nqb - 1 - blockIdx.y;
+  const int bh = blockIdx.x, b = bh / H, h = bh % H;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4;
   const int d = H * HDP;
   const int64_t ld = 3 * (int64_t)d;
   const bf16* base = qkv + (int64_t)b * Tn * ld;
   const int q = qb * 64 + w * 16 + (lane & 15);      // this lane's query
+  const float c = scale * LOG2E_F;
   bf16x8 qf[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; kk++)
@@ -493,21 +524,22 @@ __global__ __launch_bounds__(256) void attn_fwd_v2(const bf16* __restrict__ qkv,
   f32x4 ot[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; cb++) ot[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY;   // running max of S*c over the keys seen (same in the four lanes of a query)
+  float l = 0.f;         // this lane's part of the running sum of exp2(S*c - m)
 
+  const auto src = range_rsrc(base, (int64_t)Tn * ld * 2);
   TileRegs<HDP> kr, vr;
-  kr.load(base, ld, 0, Tn, d + h * HDP);
-  vr.load(base, ld, 0, Tn, 2 * d + h * HDP);
+  kr.load(src, (int)ld, 0, d + h * HDP);
+  vr.load(src, (int)ld, 0, 2 * d + h * HDP);
   for (int kt = 0; kt <= qb; kt++) {
     __syncthreads();
     kr.store(Ks);
     vr.store(Vs);
     __syncthreads();
     if (kt < qb) {
-      kr.load(base, ld, (kt + 1) * 64, Tn, d + h * HDP);
-      vr.load(base, ld, (kt + 1) * 64, Tn, 2 * d + h * HDP);
+      kr.load(src, (int)ld, (kt + 1) * 64, d + h * HDP);
+      vr.load(src, (int)ld, (kt + 1) * 64, 2 * d + h * HDP);
     }
-    const int k0 = kt * 64;
     f32x4 st[4];
 #pragma unroll
     for (int nb = 0; nb < 4; nb++) {
@@ -516,35 +548,37 @@ __global__ __launch_bounds__(256) void attn_fwd_v2(const bf16* __restrict__ qkv,
       for (int kk = 0; kk < KK; kk++)
         st[nb] = Mfma<bf16>::mma(AT::row_frag(Ks, nb * 16 + (lane & 15), kk * 4 + g), qf[kk], st[nb]);
     }
-    float mx = -INFINITY;
+    if (kt == qb) {                                   // keys after the query, or past Tn
+      const int lim = q - kt * 64;
+#pragma unroll
+      for (int nb = 0; nb < 4; nb++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int kl = nb * 16 + 4 * g + i;
+          if (kl > lim || kt * 64 + kl >= Tn) st[nb][i] = -INFINITY;
+        }
+    }
+    float mx = st[0][0];
+#pragma unroll
+    for (int nb = 0; nb < 4; nb++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) mx = fmaxf(mx, st[nb][i]);
+    const float mnew = fmaxf(m, group_max(mx) * c);   // finite: key 0 is always visible
+    if (__any(mnew > m)) {
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      l *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < CB; cb++) ot[cb] *= alpha;
+      m = mnew;
+    }
 #pragma unroll
     for (int nb = 0; nb < 4; nb++)
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        const int key = k0 + nb * 16 + 4 * g + i;
-        const float v = (key <= q && key < Tn) ? st[nb][i] * scale : -INFINITY;
-        st[nb][i] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-    const float mnew = fmaxf(m, mx);                 // finite: key 0 is always visible
-    const float alpha = __expf(m - mnew);
-    float rs = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < 4; nb++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const float p = __expf(st[nb][i] - mnew);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[nb][i], c, -m));
         st[nb][i] = p;
-        rs += p;
+        l += p;
       }
-    rs += __shfl_xor(rs, 16, WAVE);
-    rs += __shfl_xor(rs, 32, WAVE);
-    l = l * alpha + rs;
-    m = mnew;
-#pragma unroll
-    for (int cb = 0; cb < CB; cb++) ot[cb] *= alpha;
 #pragma unroll
     for (int kp = 0; kp < 2; kp++) {
       const bf16x8 pf = pack_p(st[2 * kp], st[2 * kp + 1]);
@@ -555,6 +589,7 @@ __global__ __launch_bounds__(256) void attn_fwd_v2(const bf16* __restrict__ qkv,
       }
     }
   }
+  l = group_sum(l);
   if (q < Tn) {
     const float inv = 1.f / l;
     bf16* orow = o + ((int64_t)b * Tn + q) * d + h * HDP;
@@ -565,7 +600,7 @@ __global__ __launch_bounds__(256) void attn_fwd_v2(const bf16* __restrict__ qkv,
       for (int i = 0; i < 4; i++) v[i] = (bf16)(ot[cb][i] * inv);
       *(bf16x4*)(orow + cb * 16 + 4 * g) = v;
     }
-    if (g == 0) lse[(int64_t)bh * Tn + q] = m + logf(l);
+    if (g == 0) lse[(int64_t)bh * Tn + q] = (m + log2f(l)) * LN2_F;
   }
 }
 
@@ -581,22 +616,23 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_v2(const bf16* __restrict__ q
   __shared__ __attribute__((aligned(16))) bf16 Ks[64 * HDP];
   __shared__ __attribute__((aligned(16))) bf16 Vs[64 * HDP];
   const int nqb = (Tn + 63) / 64;
-  const int qb = nqb - 1 - blockIdx.x;
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int qb = nqb - 1 - blockIdx.y;                // longest first, as in the forward
+  const int bh = blockIdx.x, b = bh / H, h = bh % H;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4;
   const int d = H * HDP;
   const int64_t ld = 3 * (int64_t)d;
   const bf16* base = qkv + (int64_t)b * Tn * ld;
   const int q = qb * 64 + w * 16 + (lane & 15);
+  const float c = scale * LOG2E_F;
   bf16x8 qf[KK], dof[KK];
   float Dq = 0.f;
 #pragma unroll
   for (int kk = 0; kk < KK; kk++) {
-    const int c = kk * 32 + g * 8;
+    const int col = kk * 32 + g * 8;
     if (q < Tn) {
-      qf[kk] = *(const bf16x8*)(base + (int64_t)q * ld + h * HDP + c);
-      dof[kk] = *(const bf16x8*)(dout + ((int64_t)b * Tn + q) * d + h * HDP + c);
-      const bf16x8 ov = *(const bf16x8*)(o + ((int64_t)b * Tn + q) * d + h * HDP + c);
+      qf[kk] = *(const bf16x8*)(base + (int64_t)q * ld + h * HDP + col);
+      dof[kk] = *(const bf16x8*)(dout + ((int64_t)b * Tn + q) * d + h * HDP + col);
+      const bf16x8 ov = *(const bf16x8*)(o + ((int64_t)b * Tn + q) * d + h * HDP + col);
 #pragma unroll
       for (int e = 0; e < 8; e++) Dq += (float)dof[kk][e] * (float)ov[e];
     } else {
@@ -604,42 +640,53 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_v2(const bf16* __restrict__ q
       dof[kk] = (bf16x8){};
     }
   }
-  Dq += __shfl_xor(Dq, 16, WAVE);
-  Dq += __shfl_xor(Dq, 32, WAVE);
-  const float lq = q < Tn ? lse[(int64_t)bh * Tn + q] : 0.f;
+  Dq = group_sum(Dq);
+  // lse in base-2 units; +inf past Tn makes every P of such a query exactly 0
+  const float lq = q < Tn ? lse[(int64_t)bh * Tn + q] * LOG2E_F : INFINITY;
   if (q < Tn && g == 0) Dv[(int64_t)bh * Tn + q] = Dq;
 
   f32x4 dqt[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; cb++) dqt[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const auto src = range_rsrc(base, (int64_t)Tn * ld * 2);
   TileRegs<HDP> kr, vr;
-  kr.load(base, ld, 0, Tn, d + h * HDP);
-  vr.load(base, ld, 0, Tn, 2 * d + h * HDP);
+  kr.load(src, (int)ld, 0, d + h * HDP);
+  vr.load(src, (int)ld, 0, 2 * d + h * HDP);
   for (int kt = 0; kt <= qb; kt++) {
     __syncthreads();
     kr.store(Ks);
     vr.store(Vs);
     __syncthreads();
     if (kt < qb) {
-      kr.load(base, ld, (kt + 1) * 64, Tn, d + h * HDP);
-      vr.load(base, ld, (kt + 1) * 64, Tn, 2 * d + h * HDP);
+      kr.load(src, (int)ld, (kt + 1) * 64, d + h * HDP);
+      vr.load(src, (int)ld, (kt + 1) * 64, 2 * d + h * HDP);
     }
-    const int k0 = kt * 64;
-    f32x4 ds[4];
+    f32x4 st[4], ds[4];
 #pragma unroll
     for (int nb = 0; nb < 4; nb++) {
-      f32x4 st = (f32x4){0.f, 0.f, 0.f, 0.f}, dpt = (f32x4){0.f, 0.f, 0.f, 0.f};
+      f32x4 dpt = (f32x4){0.f, 0.f, 0.f, 0.f};
+      st[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KK; kk++) {
-        st = Mfma<bf16>::mma(AT::row_frag(Ks, nb * 16 + (lane & 15), kk * 4 + g), qf[kk], st);
+        st[nb] = Mfma<bf16>::mma(AT::row_frag(Ks, nb * 16 + (lane & 15), kk * 4 + g), qf[kk], st[nb]);
         dpt = Mfma<bf16>::mma(AT::row_frag(Vs, nb * 16 + (lane & 15), kk * 4 + g), dof[kk], dpt);
       }
+      ds[nb] = dpt - Dq;
+    }
+    if (kt == qb) {                                   // diagonal tile: local keys <= q - k0 are visible
+      const int lim = q - kt * 64;
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int key = k0 + nb * 16 + 4 * g + i;
-        const float p = (key <= q && q < Tn) ? __expf(st[i] * scale - lq) : 0.f;
-        ds[nb][i] = p * (dpt[i] - Dq);
-      }
+      for (int nb = 0; nb < 4; nb++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const float p = nb * 16 + 4 * g + i <= lim ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[nb][i], c, -lq)) : 0.f;
+          ds[nb][i] *= p;
+        }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < 4; nb++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) ds[nb][i] *= __builtin_amdgcn_exp2f(__builtin_fmaf(st[nb][i], c, -lq));
     }
 #pragma unroll
     for (int kp = 0; kp < 2; kp++) {
@@ -672,22 +719,24 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_v2(const bf16* __restrict__
   constexpr int KK = HDP / 32, CB = HDP / 16;
   __shared__ __attribute__((aligned(16))) bf16 Qs[64 * HDP];
   __shared__ __attribute__((aligned(16))) bf16 dOs[64 * HDP];
-  __shared__ float ls[64], Ds[64];
+  __shared__ __attribute__((aligned(16))) float ls[64];
+  __shared__ __attribute__((aligned(16))) float Ds[64];
   const int nb_t = (Tn + 63) / 64;
-  const int kb = blockIdx.x;                          // key blocks near 0 see the most queries
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int kb = blockIdx.y;                          // key blocks near 0 see the most queries: first
+  const int bh = blockIdx.x, b = bh / H, h = bh % H;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4;
   const int d = H * HDP;
   const int64_t ld = 3 * (int64_t)d;
   const bf16* base = qkv + (int64_t)b * Tn * ld;
   const bf16* dob = dout + (int64_t)b * Tn * d;
   const int key = kb * 64 + w * 16 + (lane & 15);    // this lane's key (B-operand column)
+  const float c = scale * LOG2E_F;
   bf16x8 kf[KK], vf[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; kk++) {
-    const int c = kk * 32 + g * 8;
-    kf[kk] = key < Tn ? *(const bf16x8*)(base + (int64_t)key * ld + d + h * HDP + c) : (bf16x8){};
-    vf[kk] = key < Tn ? *(const bf16x8*)(base + (int64_t)key * ld + 2 * d + h * HDP + c) : (bf16x8){};
+    const int col = kk * 32 + g * 8;
+    kf[kk] = key < Tn ? *(const bf16x8*)(base + (int64_t)key * ld + d + h * HDP + col) : (bf16x8){};
+    vf[kk] = key < Tn ? *(const bf16x8*)(base + (int64_t)key * ld + 2 * d + h * HDP + col) : (bf16x8){};
   }
   f32x4 dkt[CB], dvt[CB];
 #pragma unroll
@@ -695,42 +744,63 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_v2(const bf16* __restrict__
     dkt[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
     dvt[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
+  // lse (base-2 units, +inf past Tn so those queries get P = 0) and D of the next
+  // query tile, held by the first wavefront until the tile is stored to LDS
+  const auto lsrc = range_rsrc(lse + (int64_t)bh * Tn, (int64_t)Tn * 4);
+  const auto dsrc = range_rsrc(Dv + (int64_t)bh * Tn, (int64_t)Tn * 4);
+  auto stats = [&](int gq, float& lv, float& dv) {
+    lv = gq < Tn ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lsrc, gq * 4, 0, 0)) * LOG2E_F : INFINITY;
+    dv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(dsrc, gq * 4, 0, 0));
+  };
+  float lnext = 0.f, dnext = 0.f;
+  if (threadIdx.x < 64) stats(kb * 64 + threadIdx.x, lnext, dnext);
+  const auto qsrc = range_rsrc(base, (int64_t)Tn * ld * 2);
+  const auto dosrc = range_rsrc(dob, (int64_t)Tn * d * 2);
   TileRegs<HDP> qr, dr;
-  qr.load(base, ld, kb * 64, Tn, h * HDP);
-  dr.load(dob, d, kb * 64, Tn, h * HDP);
+  qr.load(qsrc, (int)ld, kb * 64, h * HDP);
+  dr.load(dosrc, d, kb * 64, h * HDP);
   for (int qt = kb; qt < nb_t; qt++) {
     const int q0 = qt * 64;
     __syncthreads();
     qr.store(Qs);
     dr.store(dOs);
     if (threadIdx.x < 64) {
-      const int gq = q0 + threadIdx.x;
-      ls[threadIdx.x] = gq < Tn ? lse[(int64_t)bh * Tn + gq] : 0.f;
-      Ds[threadIdx.x] = gq < Tn ? Dv[(int64_t)bh * Tn + gq] : 0.f;
+      ls[threadIdx.x] = lnext;
+      Ds[threadIdx.x] = dnext;
     }
     __syncthreads();
     if (qt + 1 < nb_t) {
-      qr.load(base, ld, q0 + 64, Tn, h * HDP);
-      dr.load(dob, d, q0 + 64, Tn, h * HDP);
+      qr.load(qsrc, (int)ld, q0 + 64, h * HDP);
+      dr.load(dosrc, d, q0 + 64, h * HDP);
+      if (threadIdx.x < 64) stats(q0 + 64 + threadIdx.x, lnext, dnext);
     }
     f32x4 p[4], ds[4];
 #pragma unroll
     for (int nb = 0; nb < 4; nb++) {
-      f32x4 s = (f32x4){0.f, 0.f, 0.f, 0.f}, dp = (f32x4){0.f, 0.f, 0.f, 0.f};
+      f32x4 dp = (f32x4){0.f, 0.f, 0.f, 0.f};
+      p[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KK; kk++) {
-        s = Mfma<bf16>::mma(AT::row_frag(Qs, nb * 16 + (lane & 15), kk * 4 + g), kf[kk], s);
+        p[nb] = Mfma<bf16>::mma(AT::row_frag(Qs, nb * 16 + (lane & 15), kk * 4 + g), kf[kk], p[nb]);
         dp = Mfma<bf16>::mma(AT::row_frag(dOs, nb * 16 + (lane & 15), kk * 4 + g), vf[kk], dp);
       }
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int ql = nb * 16 + 4 * g + i;
-        const int qq = q0 + ql;
-        const float pv = (key <= qq && qq < Tn) ? __expf(s[i] * scale - ls[ql]) : 0.f;
-        p[nb][i] = pv;
-        ds[nb][i] = pv * (dp[i] - Ds[ql]);
-      }
+      p[nb] = __builtin_elementwise_fma(p[nb], (f32x4){c, c, c, c}, -*(const f32x4*)(ls + nb * 16 + 4 * g));
+      ds[nb] = dp - *(const f32x4*)(Ds + nb * 16 + 4 * g);
     }
+    if (qt == kb) {                                   // diagonal tile: local queries >= key - q0 see the key
+      const int lim = key - q0;
+#pragma unroll
+      for (int nb = 0; nb < 4; nb++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) p[nb][i] = nb * 16 + 4 * g + i >= lim ? __builtin_amdgcn_exp2f(p[nb][i]) : 0.f;
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < 4; nb++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) p[nb][i] = __builtin_amdgcn_exp2f(p[nb][i]);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; nb++) ds[nb] *= p[nb];
 #pragma unroll
     for (int qp = 0; qp < 2; qp++) {
       const bf16x8 pf = pack_p(p[2 * qp], p[2 * qp + 1]);
@@ -773,7 +843,8 @@ hipError_t launch_attn_fwd(const void* qkv, void* o, float* lse, bool bf16_ops, 
                            hipStream_t s) {
   if (hd <= 0 || hd > 64) return hipErrorInvalidValue;
   if (bf16_ops && (hd == 32 || hd == 64)) {
-    dim3 grid((T + 63) / 64, B * H);
+    if ((int64_t)T * 3 * H * hd * 2 > INT32_MAX) return hipErrorInvalidValue;   // 32-bit buffer offsets per sequence
+    dim3 grid(B * H, (T + 63) / 64);
     const float scale = 1.0f / sqrtf((float)hd);
     if (hd == 64)
       hipLaunchKernelGGL(attn_fwd_v2<64>, grid, dim3(256), 0, s, (const bf16*)qkv, (bf16*)o, lse, T, H, scale);
@@ -804,7 +875,8 @@ hipError_t launch_attn_bwd(const void* qkv, const void* o, const void* dout, con
                            void* dqkv, bool bf16_ops, int B, int T, int H, int hd, hipStream_t s) {
   if (hd <= 0 || hd > 64) return hipErrorInvalidValue;
   if (bf16_ops && (hd == 32 || hd == 64)) {
-    dim3 grid((T + 63) / 64, B * H);
+    if ((int64_t)T * 3 * H * hd * 2 > INT32_MAX) return hipErrorInvalidValue;   // 32-bit buffer offsets per sequence
+    dim3 grid(B * H, (T + 63) / 64);
     const float scale = 1.0f / sqrtf((float)hd);
     if (hd == 64) {
       hipLaunchKernelGGL(attn_bwd_dq_v2<64>, grid, dim3(256), 0, s, (const bf16*)qkv, (const bf16*)o,
