@@ -57,14 +57,20 @@ hipError_t launch_layernorm_bwd(const float* dy, const float* x, const float* me
 constexpr int COLSUM_ROWS = 64;
 hipError_t launch_colsum_partial(const void* X, bool bf16_in, int64_t ldx, int M, int N, float* part,
                                  hipStream_t s);
-// dst[n] = beta * dst[n] + sum_j part[j, n] (fixed order).
-hipError_t launch_colsum_final(const float* part, int nblk, int N, float* dst, float beta, hipStream_t s);
-// Up to three such reductions over equally shaped partials in one launch.
-struct ColsumJobs {
-  const float* part[3];
-  float* dst[3];
+// Deferred column-sum reductions: job j adds the sum of its partial rows,
+// part[r, n] for r < nblk (fixed order), into dst: dst[n] = beta * dst[n] + sum.
+// All jobs of one backward run in a single launch of total_blk workgroups (16
+// columns each); first_blk numbers them, ascending.
+struct RedJob {
+  int64_t part;       // float offset of the [nblk, n] partials in the partial area
+  int64_t dst;        // float offset of the destination in the gradient array
+  int32_t n;          // columns
+  int32_t rows_kind;  // 0: LayerNorm partials (nblk_ln rows), 1: column-sum partials (nblk_cs rows)
+  int32_t first_blk;
+  int32_t pad;
 };
-hipError_t launch_colsum_final_multi(const ColsumJobs& jobs, int njobs, int nblk, int N, float beta, hipStream_t s);
+hipError_t launch_reduce_jobs(const RedJob* jobs, int njobs, int total_blk, const float* part, float* grads,
+                              int nblk_ln, int nblk_cs, float beta, hipStream_t s);
 
 // Row-wise softmax cross-entropy over Vp columns of z (operand type, row stride ldz).
 // Writes row_loss[m] = lse - z[m, y[m]] and overwrites z with

@@ -212,38 +212,49 @@ hipError_t launch_colsum_partial(const void* X, bool bf16_in, int64_t ldx, int M
   return hipGetLastError();
 }
 
-// 16 columns per workgroup, 16 row groups: each thread sums every 16th partial in
-// order, then the 16 group sums are added in a fixed order. blockIdx.y selects
-// one of up to three independent (partials, destination) jobs.
-__global__ __launch_bounds__(256) void colsum_final_kernel(ColsumJobs jobs, int nblk, int N, float beta) {
+// 16 columns per workgroup, 16 row groups: each thread sums every 16th partial row
+// in order, then the 16 group sums are added in a fixed order. A workgroup finds
+// its job by binary search over first_blk.
+__global__ __launch_bounds__(256) void reduce_jobs_kernel(const RedJob* __restrict__ jobs, int njobs,
+                                                          const float* __restrict__ part, float* __restrict__ grads,
+                                                          int nblk_ln, int nblk_cs, float beta) {
   __shared__ float red[16][17];
-  const float* __restrict__ part = jobs.part[blockIdx.y];
-  float* dst = jobs.dst[blockIdx.y];
+  __shared__ int job;
+  if (threadIdx.x == 0) {
+    int lo = 0, hi = njobs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (jobs[mid].first_blk <= (int)blockIdx.x) lo = mid;
+      else hi = mid - 1;
+    }
+    job = lo;
+  }
+  __syncthreads();
+  const RedJob J = jobs[job];
+  const int nblk = J.rows_kind == 0 ? nblk_ln : nblk_cs;
+  const float* pp = part + J.part;
   const int cl = threadIdx.x & 15, grp = threadIdx.x >> 4;
-  const int col = blockIdx.x * 16 + cl;
+  const int col = ((int)blockIdx.x - J.first_blk) * 16 + cl;
   float s = 0.f;
-  if (col < N)
-    for (int j = grp; j < nblk; j += 16) s += part[(int64_t)j * N + col];
+  if (col < J.n)
+    for (int r = grp; r < nblk; r += 16) s += pp[(int64_t)r * J.n + col];
   red[grp][cl] = s;
   __syncthreads();
-  if (grp == 0 && col < N) {
+  if (grp == 0 && col < J.n) {
     float t = red[0][cl];
 #pragma unroll
     for (int q = 1; q < 16; q++) t += red[q][cl];
+    float* dst = grads + J.dst;
     dst[col] = (beta != 0.f ? beta * dst[col] : 0.f) + t;
   }
 }
 
-hipError_t launch_colsum_final_multi(const ColsumJobs& jobs, int njobs, int nblk, int N, float beta, hipStream_t s) {
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((N + 15) / 16, njobs), dim3(256), 0, s, jobs, nblk, N, beta);
+hipError_t launch_reduce_jobs(const RedJob* jobs, int njobs, int total_blk, const float* part, float* grads,
+                              int nblk_ln, int nblk_cs, float beta, hipStream_t s) {
+  if (njobs <= 0 || total_blk <= 0) return hipSuccess;
+  hipLaunchKernelGGL(reduce_jobs_kernel, dim3(total_blk), dim3(256), 0, s, jobs, njobs, part, grads, nblk_ln,
+                     nblk_cs, beta);
   return hipGetLastError();
-}
-
-hipError_t launch_colsum_final(const float* part, int nblk, int N, float* dst, float beta, hipStream_t s) {
-  ColsumJobs j{};
-  j.part[0] = part;
-  j.dst[0] = dst;
-  return launch_colsum_final_multi(j, 1, nblk, N, beta, s);
 }
 
 // ----------------------------------------------------------------------------- cross-entropy

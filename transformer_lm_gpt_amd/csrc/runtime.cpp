@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <string>
 #include <vector>
 
@@ -73,11 +74,16 @@ struct gpt_model {
   Slice x_final, lnf, lnf_mean, lnf_rstd, logits, row_loss, tokens, targets;
   size_t act_bytes = 0;
   // workspace
-  Slice dres, dres_op, dln, du, dO, dqkv, attnD, part_g, part_b, part_r, colsum_part, emb_keys, emb_piece, norm_part,
-      opt, split, ttable;
+  Slice dres, dres_op, dln, du, dO, dqkv, attnD, red, emb_keys, emb_piece, norm_part, opt, split, ttable, rtable;
   size_t split_floats = 0;
   std::vector<TransposeEntry> tentries;   // 2-D weights whose transposed shadow the dgrads read
   int64_t ttiles = 0;
+  // bias and LayerNorm-parameter gradients: partial column sums written during the
+  // backward, reduced by one launch at its end
+  std::vector<RedJob> rjobs;
+  std::map<std::string, int64_t> rpart;   // destination tensor -> float offset of its partials in `red`
+  int rblocks = 0;
+  bool tables_ready = false;              // device copies of the two tables are in this workspace
   size_t ws_bytes = 0;
   // binding
   gpt_buffers buf{};
@@ -273,10 +279,26 @@ void plan(gpt_model* h) {
   h->dqkv = w.take(M * 3 * d * ob);
   h->attnD = w.take(bht * fb);
   const size_t ln_blk = (M + LN_BWD_ROWS - 1) / LN_BWD_ROWS;
-  h->part_g = w.take(ln_blk * d * fb);
-  h->part_b = w.take(ln_blk * d * fb);
   const size_t cs_blk = (M + COLSUM_ROWS - 1) / COLSUM_ROWS;
-  h->colsum_part = w.take(cs_blk * 4 * d * fb);
+  size_t red_floats = 0;
+  auto red_job = [&](const std::string& dst, int kind) {
+    const Tensor* t = find(h, dst);
+    RedJob j{(int64_t)red_floats, (int64_t)t->offset, (int32_t)t->numel(), kind, h->rblocks, 0};
+    h->rjobs.push_back(j);
+    h->rpart[dst] = j.part;
+    red_floats += (kind == 0 ? ln_blk : cs_blk) * t->numel();
+    h->rblocks += (int)((t->numel() + 15) / 16);
+  };
+  red_job("lnf.g", 0);
+  red_job("lnf.b", 0);
+  for (int l = 0; l < h->L; l++) {
+    const std::string p = "h" + std::to_string(l) + ".";
+    for (const char* n : {"ln1.g", "ln1.b", "proj.b", "ln2.g", "ln2.b", "fcproj.b"}) red_job(p + n, 0);
+    red_job(p + "fc.b", 1);
+    red_job(p + "attn.b", 1);
+  }
+  h->red = w.take(red_floats * fb);
+  h->rtable = w.take(h->rjobs.size() * sizeof(RedJob));
   h->emb_keys = w.take((size_t)embed_bwd_sort_size((int)M) * 4);
   h->emb_piece = w.take(M * d * fb);
   h->norm_part = w.take(NORM_BLOCKS * fb);
@@ -285,7 +307,6 @@ void plan(gpt_model* h) {
   h->split_floats = 16 * (size_t)d * d + 4096;
   if (M >= 256 && d >= 256) h->split_floats = std::max(h->split_floats, (size_t)1664 * 256 * 256);
   h->split = w.take(h->split_floats * fb);
-  h->part_r = w.take(ln_blk * d * fb);
   for (const Tensor& t : h->tensors) {
     if (t.ndim != 2 || t.name == "wpe") continue;
     TransposeEntry e{(int64_t)t.offset, t.rows, t.cols, h->ttiles};
@@ -297,38 +318,40 @@ void plan(gpt_model* h) {
   h->ws_bytes = w.total;
 }
 
-int colsum(gpt_model* h, const void* X, bool bf16_in, int64_t ldx, int M, int N, float* dst, float beta) {
-  float* part = ws<float>(h, h->colsum_part);
-  const int nblk = (M + COLSUM_ROWS - 1) / COLSUM_ROWS;
-  RUN("colsum", "colsum_partial", launch_colsum_partial(X, bf16_in, ldx, M, N, part, h->stream));
-  RUN("colsum", "colsum_final", launch_colsum_final(part, nblk, N, dst, beta, h->stream));
+float* red_part(gpt_model* h, const std::string& dst) {
+  return (float*)((char*)h->buf.workspace + h->red.off) + h->rpart.at(dst);
+}
+
+// Partial column sums of X into the partials of bias `dst` (reduced at the end of the backward).
+int colsum(gpt_model* h, const void* X, bool bf16_in, int64_t ldx, int M, int N, const std::string& dst) {
+  RUN("colsum", "colsum_partial", launch_colsum_partial(X, bf16_in, ldx, M, N, red_part(h, dst), h->stream));
   return GPT_OK;
 }
 
-// LayerNorm backward into dres (in place when dres is given); also reduces the
-// gain and shift gradients and, when `resid_bias` names a tensor, the column sum
-// of the incoming residual gradient (the bias gradient of that projection).
+// LayerNorm backward into dres (in place when dres is given); writes the partial
+// column sums of the gain and shift gradients and, when `resid_bias` names a
+// tensor, of the incoming residual gradient (the bias gradient of that projection).
 int ln_bwd(gpt_model* h, const float* dy, const float* x, const float* mean, const float* rstd,
-           const std::string& gname, const std::string& bname, const float* dres, const char* resid_bias, int M,
-           float beta) {
-  float* pg = ws<float>(h, h->part_g);
-  float* pb = ws<float>(h, h->part_b);
-  float* pr = resid_bias ? ws<float>(h, h->part_r) : nullptr;
+           const std::string& gname, const std::string& bname, const float* dres, const char* resid_bias, int M) {
+  float* pr = resid_bias ? red_part(h, resid_bias) : nullptr;
   void* dx_op = h->bf16 ? ws(h, h->dres_op) : nullptr;
   RUN("layernorm", "layernorm_bwd",
-      launch_layernorm_bwd(dy, x, mean, rstd, P(h, gname), dres, ws<float>(h, h->dres), dx_op, h->bf16, pg, pb, pr,
-                           M, h->d, h->stream));
-  const int nblk = (M + LN_BWD_ROWS - 1) / LN_BWD_ROWS;
-  ColsumJobs jobs{};
-  jobs.part[0] = pg;
-  jobs.dst[0] = G(h, gname);
-  jobs.part[1] = pb;
-  jobs.dst[1] = G(h, bname);
-  if (resid_bias) {
-    jobs.part[2] = pr;
-    jobs.dst[2] = G(h, resid_bias);
-  }
-  RUN("colsum", "ln_param_grads", launch_colsum_final_multi(jobs, resid_bias ? 3 : 2, nblk, h->d, beta, h->stream));
+      launch_layernorm_bwd(dy, x, mean, rstd, P(h, gname), dres, ws<float>(h, h->dres), dx_op, h->bf16,
+                           red_part(h, gname), red_part(h, bname), pr, M, h->d, h->stream));
+  return GPT_OK;
+}
+
+// Copies the transpose and reduction tables into the bound workspace (once per bind).
+int upload_tables(gpt_model* h) {
+  if (h->tables_ready) return GPT_OK;
+  hipError_t e = hipMemcpyAsync(ws(h, h->rtable), h->rjobs.data(), h->rjobs.size() * sizeof(RedJob),
+                                hipMemcpyHostToDevice, h->stream);
+  if (e == hipSuccess && h->bf16)
+    e = hipMemcpyAsync(ws(h, h->ttable), h->tentries.data(), h->tentries.size() * sizeof(TransposeEntry),
+                       hipMemcpyHostToDevice, h->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
+  if (e != hipSuccess) return hip_check(h, e, "upload tables");
+  h->tables_ready = true;
   return GPT_OK;
 }
 
@@ -506,6 +529,7 @@ int gpt_bind(gpt_model* h, const gpt_buffers* bufs, void* hip_stream) {
   h->buf = *bufs;
   h->stream = (hipStream_t)hip_stream;
   h->bound = true;
+  h->tables_ready = false;
   h->fwd_pending = false;
   h->grads_fresh = true;
   return GPT_OK;
@@ -521,10 +545,7 @@ int gpt_init_state(gpt_model* h) {
   RUN("init", "zero optimizer state", launch_zero(ws(h, h->opt), sizeof(OptState) / 4, s));
   if (h->bf16) {
     RUN("init", "bf16 shadow", launch_cast_bf16((const float*)h->buf.params, h->buf.shadow, h->n_flat, s));
-    hipError_t e = hipMemcpyAsync(ws(h, h->ttable), h->tentries.data(), h->tentries.size() * sizeof(TransposeEntry),
-                                  hipMemcpyHostToDevice, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
-    if (e != hipSuccess) return hip_check(h, e, "upload transpose table");
+    if ((rc = upload_tables(h))) return rc;
     RUN("init", "transposed shadow", transpose_shadow(h));
   }
   h->grads_fresh = true;
@@ -571,6 +592,7 @@ int gpt_backward(gpt_model* h) {
   int rc = check_usable(h);
   if (rc) return rc;
   if (!h->fwd_pending) return fail(h, GPT_E_STATE, "gpt_backward needs a preceding gpt_forward_loss");
+  if ((rc = upload_tables(h))) return rc;
   const int B = h->cur_B, T = h->cur_T, M = B * T, d = h->d;
   const bool bf = h->bf16;
   hipStream_t s = h->stream;
@@ -593,7 +615,7 @@ int gpt_backward(gpt_model* h) {
     RUN("gemm_dgrad", "lm_head_dgrad", gemm(h, g2, bf));
   }
   if ((rc = ln_bwd(h, dln, act<float>(h, h->x_final), act<float>(h, h->lnf_mean), act<float>(h, h->lnf_rstd),
-                   "lnf.g", "lnf.b", nullptr, nullptr, M, beta)))
+                   "lnf.g", "lnf.b", nullptr, nullptr, M)))
     return rc;
 
   for (int l = h->L - 1; l >= 0; l--) {
@@ -617,10 +639,10 @@ int gpt_backward(gpt_model* h) {
       GemmDesc gw2 = gemm_desc(du, 4 * d, false, act(h, la.ln2), d, false, G(h, p + "fc.w"), d, 4 * d, d, M, EPI_ACC);
       gw2.beta = beta;
       RUN("gemm_wgrad", "fc_wgrad", gemm(h, gw2, bf));
-      if ((rc = colsum(h, du, bf, 4 * d, M, 4 * d, G(h, p + "fc.b"), beta))) return rc;
+      if ((rc = colsum(h, du, bf, 4 * d, M, 4 * d, p + "fc.b"))) return rc;
       const std::string fcproj_b = p + "fcproj.b";
       if ((rc = ln_bwd(h, dln, act<float>(h, la.xmid), act<float>(h, la.ln2_mean), act<float>(h, la.ln2_rstd),
-                       p + "ln2.g", p + "ln2.b", dres, fcproj_b.c_str(), M, beta)))
+                       p + "ln2.g", p + "ln2.b", dres, fcproj_b.c_str(), M)))
         return rc;
     }
     // ---- attention: xmid = x + attn(LN1(x)) Wo^T + bo ; dres now holds d xmid
@@ -641,13 +663,17 @@ int gpt_backward(gpt_model* h) {
                                EPI_ACC);
       gw2.beta = beta;
       RUN("gemm_wgrad", "qkv_wgrad", gemm(h, gw2, bf));
-      if ((rc = colsum(h, dqkv, bf, 3 * d, M, 3 * d, G(h, p + "attn.b"), beta))) return rc;
+      if ((rc = colsum(h, dqkv, bf, 3 * d, M, 3 * d, p + "attn.b"))) return rc;
       const std::string proj_b = p + "proj.b";
       if ((rc = ln_bwd(h, dln, act<float>(h, la.x), act<float>(h, la.ln1_mean), act<float>(h, la.ln1_rstd),
-                       p + "ln1.g", p + "ln1.b", dres, proj_b.c_str(), M, beta)))
+                       p + "ln1.g", p + "ln1.b", dres, proj_b.c_str(), M)))
         return rc;
     }
   }
+  RUN("colsum", "bias_and_ln_grads",
+      launch_reduce_jobs(ws<RedJob>(h, h->rtable), (int)h->rjobs.size(), h->rblocks, ws<float>(h, h->red),
+                         (float*)h->buf.grads, (M + LN_BWD_ROWS - 1) / LN_BWD_ROWS, (M + COLSUM_ROWS - 1) / COLSUM_ROWS,
+                         beta, s));
   // ---- embeddings: dres holds d x0
   if (h->grads_fresh && T < h->Tmax) {
     float* wpe_tail = G(h, "wpe") + (size_t)T * d;
