@@ -171,8 +171,9 @@ int gpt_get_step(gpt_model* h, int64_t* t);
 /* Synchronous copy of a saved activation into caller memory on the device.
  * what: "x" (fp32 [M, d] residual input of block `layer`, layer == n_layer
  * is the input of the final LayerNorm), "qkv" ([M, 3d], operand type),
- * "attn" ([M, d], operand type), "lse" (fp32 [B, H, T]), "h" (GELU output,
- * [M, 4d], operand type). bytes must equal the size of the request. */
+ * "attn" ([M, d], operand type), "lse" (fp32 [B, H, T]), "u" (GELU input,
+ * [M, 4d], operand type), "h" (GELU output, [M, 4d], operand type). bytes
+ * must equal the size of the request. */
 int gpt_debug_copy(gpt_model* h, const char* what, int32_t layer, void* d_dst, size_t bytes);
 
 /* Kernel timing hook used by benchmarks: while enabled, every launch of the

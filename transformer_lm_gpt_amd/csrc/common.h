@@ -71,11 +71,31 @@ __device__ inline float row16_max(float v) {
 }
 
 // Exact GELU u * Phi(u) and its derivative Phi(u) + u phi(u), with the device erf.
-__device__ inline float gelu_f(float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f)); }
+// Standard normal CDF Phi(u) = (1 + erf(u / sqrt 2)) / 2 and density phi(u) from one
+// exponential, with erf from Abramowitz and Stegun, Handbook of Mathematical
+// Functions, formula 7.1.26: for z >= 0, 1 - erf(z) = t (a1 + t (a2 + t (a3 + t (a4 +
+// t a5)))) exp(-z^2), t = 1 / (1 + p z), absolute error at most 1.5e-7. The
+// coefficients below are the published ones halved, so the polynomial gives
+// (1 - erf(z)) / 2 directly; exp(-z^2) with z = |u|/sqrt 2 is exp(-u^2/2).
+__device__ inline void normal_cdf_pdf(float u, float& cdf, float& pdf) {
+  const float z = fabsf(u) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * z);
+  const float e = __builtin_amdgcn_exp2f(-0.72134752044448170f * u * u);   // exp(-u^2 / 2)
+  const float q = t * (0.127414796f + t * (-0.142248368f + t * (0.7107068705f + t * (-0.7265760135f + t * 0.5307027145f))));
+  const float tail = q * e;                                               // (1 - erf(z)) / 2
+  cdf = u >= 0.f ? 1.0f - tail : tail;
+  pdf = 0.39894228040143268f * e;
+}
+// GELU(u) = u Phi(u) and its derivative Phi(u) + u phi(u).
+__device__ inline float gelu_f(float u) {
+  float c, d;
+  normal_cdf_pdf(u, c, d);
+  return u * c;
+}
 __device__ inline float gelu_grad_f(float u) {
-  float cdf = 0.5f * (1.0f + erff(u * 0.70710678118654752f));
-  float pdf = 0.39894228040143268f * __expf(-0.5f * u * u);
-  return cdf + u * pdf;
+  float c, d;
+  normal_cdf_pdf(u, c, d);
+  return c + u * d;
 }
 
 }  // namespace gpt

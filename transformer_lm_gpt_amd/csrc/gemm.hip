@@ -172,7 +172,7 @@ struct GemmArgs {
   int M, N, K;
   const float* bias;
   const float* resid; int64_t ldr;
-  float* aux; int64_t ldaux;
+  void* aux; int64_t ldaux;   // operand type
   float beta;
   int a_vec, b_vec;
   int c_vec;           // C / aux / resid rows allow 16-column vector access
@@ -198,12 +198,12 @@ __device__ inline void epi_store(const GemmArgs& p, int row, int col, float v, f
     ((float*)p.C)[ci] = p.resid[(int64_t)row * p.ldr + col] + (v + bias);
   } else if constexpr (EPI == EPI_BIAS_GELU) {
     const float u = v + bias;
-    p.aux[(int64_t)row * p.ldaux + col] = u;
+    ((T*)p.aux)[(int64_t)row * p.ldaux + col] = from_f32<T>(u);
     ((T*)p.C)[ci] = from_f32<T>(gelu_f(u));
   } else if constexpr (EPI == EPI_F32) {
     ((float*)p.C)[ci] = v;
   } else if constexpr (EPI == EPI_GELU_BWD) {
-    ((T*)p.C)[ci] = from_f32<T>(v * gelu_grad_f(p.aux[(int64_t)row * p.ldaux + col]));
+    ((T*)p.C)[ci] = from_f32<T>(v * gelu_grad_f(to_f32(((const T*)p.aux)[(int64_t)row * p.ldaux + col])));
   } else {  // EPI_ACC
     if (gridDim.z > 1) {
       p.part[((int64_t)blockIdx.z * p.M + row) * p.N + col] = v;
@@ -255,30 +255,29 @@ __device__ inline void epi_store16(const GemmArgs& p, int row, int col0, const f
       *(f32x4*)((float*)p.C + ci + 4 * q) = o;
     }
   } else if constexpr (EPI == EPI_BIAS_GELU) {
-    float* u = p.aux + (int64_t)row * p.ldaux + col0;
-#pragma unroll
-    for (int q = 0; q < 4; q++) *(f32x4*)(u + 4 * q) = (f32x4){x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
+    bf16* u = (bf16*)p.aux + (int64_t)row * p.ldaux + col0;
 #pragma unroll
     for (int q = 0; q < 2; q++) {
-      bf16x8 o;
+      bf16x8 uo, o;
 #pragma unroll
-      for (int e = 0; e < 8; e++) o[e] = (bf16)gelu_f(x[8 * q + e]);
+      for (int e = 0; e < 8; e++) {
+        uo[e] = (bf16)x[8 * q + e];
+        o[e] = (bf16)gelu_f(x[8 * q + e]);
+      }
+      *(bf16x8*)(u + 8 * q) = uo;
       *(bf16x8*)((bf16*)p.C + ci + 8 * q) = o;
     }
   } else if constexpr (EPI == EPI_F32) {
 #pragma unroll
     for (int q = 0; q < 4; q++) *(f32x4*)((float*)p.C + ci + 4 * q) = (f32x4){x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
   } else if constexpr (EPI == EPI_GELU_BWD) {
-    const float* u = p.aux + (int64_t)row * p.ldaux + col0;
+    const bf16* u = (const bf16*)p.aux + (int64_t)row * p.ldaux + col0;
 #pragma unroll
     for (int q = 0; q < 2; q++) {
-      const f32x4 u0 = *(const f32x4*)(u + 8 * q), u1 = *(const f32x4*)(u + 8 * q + 4);
+      const bf16x8 uv = *(const bf16x8*)(u + 8 * q);
       bf16x8 o;
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        o[e] = (bf16)(x[8 * q + e] * gelu_grad_f(u0[e]));
-        o[4 + e] = (bf16)(x[8 * q + 4 + e] * gelu_grad_f(u1[e]));
-      }
+      for (int e = 0; e < 8; e++) o[e] = (bf16)(x[8 * q + e] * gelu_grad_f((float)uv[e]));
       *(bf16x8*)((bf16*)p.C + ci + 8 * q) = o;
     }
   } else {  // EPI_ACC
@@ -396,6 +395,7 @@ template <int ROWS, int NW>
 __device__ inline void dma_kc(const bf16* __restrict__ src, int64_t ld, int row0, int nrows, int k0, char* lds,
                               int wave, int lane) {
   constexpr int CHUNKS = ROWS * 32 * 2 / 1024;   // 1 KB per wavefront instruction
+  static_assert(ROWS % 16 == 0 && CHUNKS % NW == 0, "k-contiguous tile shape");
 #pragma unroll
   for (int i = 0; i < CHUNKS / NW; i++) {
     const int ch = wave + NW * i;
@@ -413,6 +413,7 @@ __device__ inline void dma_mc(const bf16* __restrict__ src, int64_t ld, int row0
   constexpr int UPR = ROWS / 8;                  // 16-byte units per k-row
   constexpr int RPC = 64 / UPR;                  // k-rows per 1 KB chunk
   constexpr int CHUNKS = 32 / RPC;
+  static_assert(64 % UPR == 0 && 32 % RPC == 0 && CHUNKS % NW == 0, "m-contiguous tile shape");
 #pragma unroll
   for (int i = 0; i < CHUNKS / NW; i++) {
     const int ch = wave + NW * i;
@@ -528,35 +529,40 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, 
   }
 
   // Epilogue through LDS: each wave parks one 16-row block of its TM x TN
-  // quadrant, then every lane handles 16 contiguous columns of one row, so bias,
+  // quadrant, then a lane handles 16 contiguous columns of one row (TN/16 such
+  // groups per row, so 64 lanes cover the block in one or more passes), so bias,
   // residual and GELU inputs are read and outputs written as vectors.
   __syncthreads();   // every wave is done with the stage buffers
   constexpr int ELD = TN + 4;
+  constexpr int CG = TN / 16, ITEMS = 16 * CG, PASSES = (ITEMS + 63) / 64;
   float* scr = (float*)smem + wave * 16 * ELD;
-  const int er = lane >> 2, ec = (lane & 3) * 16;
-  const int col0 = n0 + wn * TN + ec;
-  const bool vec = (col0 + 16 <= p.N) && p.c_vec;
 #pragma unroll
   for (int i = 0; i < FM; i++) {
 #pragma unroll
     for (int j = 0; j < FN; j++)
 #pragma unroll
       for (int e = 0; e < 4; e++) scr[(4 * (lane >> 4) + e) * ELD + j * 16 + (lane & 15)] = acc[i][j][e];
-    float v[16];
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
-      const f32x4 t = *(const f32x4*)(scr + er * ELD + ec + 4 * q);
+    for (int ps = 0; ps < PASSES; ps++) {
+      const int it = lane + 64 * ps;
+      if (ITEMS % 64 != 0 && it >= ITEMS) break;
+      const int er = it / CG, ec = (it % CG) * 16;
+      float v[16];
 #pragma unroll
-      for (int e = 0; e < 4; e++) v[4 * q + e] = t[e];
-    }
-    const int rt = wm * TM + i * 16 + er;        // row within the tile
-    if (park) {
-      float* d = park + (int64_t)rt * BN_ + wn * TN + ec;
+      for (int q = 0; q < 4; q++) {
+        const f32x4 t = *(const f32x4*)(scr + er * ELD + ec + 4 * q);
 #pragma unroll
-      for (int q = 0; q < 4; q++) *(f32x4*)(d + 4 * q) = (f32x4){v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
-    } else {
-      const int row = m0 + rt;
-      if (row < p.M && col0 < p.N) epi_store16<EPI>(p, row, col0, v, vec);
+        for (int e = 0; e < 4; e++) v[4 * q + e] = t[e];
+      }
+      const int rt = wm * TM + i * 16 + er;      // row within the tile
+      if (park) {
+        float* d = park + (int64_t)rt * BN_ + wn * TN + ec;
+#pragma unroll
+        for (int q = 0; q < 4; q++) *(f32x4*)(d + 4 * q) = (f32x4){v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+      } else {
+        const int row = m0 + rt, col0 = n0 + wn * TN + ec;
+        if (row < p.M && col0 < p.N) epi_store16<EPI>(p, row, col0, v, (col0 + 16 <= p.N) && p.c_vec);
+      }
     }
   }
   __syncthreads();
@@ -770,7 +776,7 @@ hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
     // vector epilogue: 16-byte aligned rows for every matrix the epilogue touches
     bool cv = ((uintptr_t)d.C % 16 == 0) && (d.ldc % 8 == 0);
     if (d.resid) cv = cv && ((uintptr_t)d.resid % 16 == 0) && (d.ldr % 4 == 0);
-    if (d.aux) cv = cv && ((uintptr_t)d.aux % 16 == 0) && (d.ldaux % 4 == 0);
+    if (d.aux) cv = cv && ((uintptr_t)d.aux % 16 == 0) && (d.ldaux % 8 == 0);
     if (d.bias) cv = cv && ((uintptr_t)d.bias % 16 == 0);
     if (d.epi == EPI_ACC && d.split_ws) cv = cv && (d.N % 4 == 0) && ((uintptr_t)d.split_ws % 16 == 0);
     a.c_vec = cv;
@@ -806,6 +812,11 @@ hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
   // (weight gradients, K = B*T; the lm_head input gradient, K = vocab): every CU
   // gets the same number of k-slices. Measured on gfx950 it loses to one tile per
   // workgroup when K <= 3072, where parking partial tiles costs more than it saves.
+  // Both operands k-contiguous (every GEMM of the step except the weight
+  // gradients): 192 x 192 tiles on four wavefronts, three stages. For 12288-row
+  // outputs with 768, 2304 or 3072 columns these come in whole multiples of 256
+  // tiles, where 256 x 256 tiles leave part of the last wave of CUs idle.
+  if (pipelined && d.a_kc && d.b_kc && S == 1) return dma_epi<192, 192, 2, 2, 3, true, true>(a, d.epi, 1, s);
   if (pipelined && tiles < 2 * num_cus() && d.K >= 8192 && d.split_ws) {
     const long long KI = d.K / 32;
     const long long U = (long long)tiles * KI;

@@ -10,9 +10,9 @@ enum Epilogue {
   EPI_STORE = 0,       // C(T)   = acc
   EPI_BIAS = 1,        // C(T)   = acc + bias[n]
   EPI_BIAS_RESID = 2,  // C(f32) = resid[m, n] + acc + bias[n]
-  EPI_BIAS_GELU = 3,   // aux(f32) = u = acc + bias[n];  C(T) = gelu(u)
+  EPI_BIAS_GELU = 3,   // aux(T) = u = acc + bias[n];  C(T) = gelu(u)
   EPI_F32 = 4,         // C(f32) = acc
-  EPI_GELU_BWD = 5,    // C(T)   = acc * gelu'(aux[m, n])
+  EPI_GELU_BWD = 5,    // C(T)   = acc * gelu'(aux[m, n])   (aux in operand type T)
   EPI_ACC = 6,         // C(f32) = beta * C + acc   (beta is 0 or 1; C is not read when 0)
 };
 
@@ -28,7 +28,7 @@ struct GemmDesc {
   int epi;
   const float* bias;
   const float* resid; int64_t ldr;
-  float* aux; int64_t ldaux;
+  void* aux; int64_t ldaux;
   float beta;
   float* split_ws; size_t split_ws_floats;   // optional split-K workspace (EPI_ACC only)
 };

@@ -255,7 +255,7 @@ void plan(gpt_model* h) {
     la.ln2 = a.take(M * d * ob);
     la.ln2_mean = a.take(M * fb);
     la.ln2_rstd = a.take(M * fb);
-    la.u = a.take(M * 4 * d * fb);
+    la.u = a.take(M * 4 * d * ob);
     la.h = a.take(M * 4 * d * ob);
   }
   h->x_final = a.take(M * d * fb);
@@ -393,7 +393,7 @@ int forward_to_logits(gpt_model* h, int B, int T) {
       GemmDesc g = gemm_desc(act(h, la.ln2), d, true, Wop(h, p + "fc.w"), d, true, act(h, la.h), 4 * d, M, 4 * d,
                              d, EPI_BIAS_GELU);
       g.bias = P(h, p + "fc.b");
-      g.aux = act<float>(h, la.u);
+      g.aux = act(h, la.u);
       g.ldaux = 4 * d;
       RUN("gemm_fwd", "fc_fwd", gemm(h, g, bf));
     }
@@ -626,7 +626,7 @@ int gpt_backward(gpt_model* h) {
       GemmDesc g = bf ? gemm_desc(dres_opnd, d, true, WopT(h, p + "fcproj.w"), d, true, du, 4 * d, M, 4 * d, d, EPI_GELU_BWD)
                       : gemm_desc(dres_opnd, d, true, Wop(h, p + "fcproj.w"), 4 * d, false, du, 4 * d, M, 4 * d, d,
                                   EPI_GELU_BWD);
-      g.aux = act<float>(h, la.u);
+      g.aux = act(h, la.u);
       g.ldaux = 4 * d;
       RUN("gemm_dgrad", "fcproj_dgrad", gemm(h, g, bf));
       GemmDesc gw = gemm_desc(dres_opnd, d, false, act(h, la.h), 4 * d, false, G(h, p + "fcproj.w"), 4 * d, d, 4 * d,
@@ -767,7 +767,7 @@ int gpt_debug_copy(gpt_model* h, const char* what, int32_t layer, void* d_dst, s
     if (w == "qkv") { src = act(h, la.qkv); n = M * 3 * d * h->op_size; }
     if (w == "attn") { src = act(h, la.att); n = M * d * h->op_size; }
     if (w == "h") { src = act(h, la.h); n = M * 4 * d * h->op_size; }
-    if (w == "u") { src = act(h, la.u); n = M * 4 * d * 4; }
+    if (w == "u") { src = act(h, la.u); n = M * 4 * d * h->op_size; }
     if (w == "lse") { src = act(h, la.lse); n = (size_t)h->cur_B * h->H * h->cur_T * 4; }
   } else {
     return fail(h, GPT_E_INVAL, "unknown activation '" + w + "'");
