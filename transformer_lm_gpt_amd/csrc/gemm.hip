@@ -178,6 +178,7 @@ struct GemmArgs {
   int c_vec;           // C / aux / resid rows allow 16-column vector access
   int kchunk;          // contraction length per split (gridDim.z splits)
   float* part;         // split partials [gridDim.z, M, N] (EPI_ACC with gridDim.z > 1)
+  float* colsum;       // EPI_GELU_BWD: per-tile-row column sums [tiles_m, N], or NULL
 };
 
 template <int EPI>
@@ -216,12 +217,19 @@ __device__ inline void epi_store(const GemmArgs& p, int row, int col, float v, f
 
 // Sixteen consecutive output columns col0.. of one row: vector loads and stores
 // when the run is inside the matrix and aligned, element-wise otherwise.
+// With EPI_GELU_BWD the final fp32 values are also added into sum16 (the bias
+// gradient's column sums); other epilogues leave it alone.
 template <int EPI>
-__device__ inline void epi_store16(const GemmArgs& p, int row, int col0, const float (&v)[16], bool vec) {
+__device__ inline void epi_store16(const GemmArgs& p, int row, int col0, const float (&v)[16], bool vec,
+                                   float (&sum16)[16]) {
   if (!vec) {
 #pragma unroll
     for (int c = 0; c < 16; c++)
-      if (col0 + c < p.N) epi_store<bf16, EPI>(p, row, col0 + c, v[c], epi_bias<EPI>(p, col0 + c));
+      if (col0 + c < p.N) {
+        epi_store<bf16, EPI>(p, row, col0 + c, v[c], epi_bias<EPI>(p, col0 + c));
+        if constexpr (EPI == EPI_GELU_BWD)
+          sum16[c] += v[c] * gelu_grad_f((float)((const bf16*)p.aux)[(int64_t)row * p.ldaux + col0 + c]);
+      }
     return;
   }
   const int64_t ci = (int64_t)row * p.ldc + col0;
@@ -277,7 +285,11 @@ __device__ inline void epi_store16(const GemmArgs& p, int row, int col0, const f
       const bf16x8 uv = *(const bf16x8*)(u + 8 * q);
       bf16x8 o;
 #pragma unroll
-      for (int e = 0; e < 8; e++) o[e] = (bf16)(x[8 * q + e] * gelu_grad_f((float)uv[e]));
+      for (int e = 0; e < 8; e++) {
+        const float y = x[8 * q + e] * gelu_grad_f((float)uv[e]);
+        o[e] = (bf16)y;
+        sum16[8 * q + e] += y;
+      }
       *(bf16x8*)((bf16*)p.C + ci + 8 * q) = o;
     }
   } else {  // EPI_ACC
@@ -536,6 +548,14 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, 
   constexpr int ELD = TN + 4;
   constexpr int CG = TN / 16, ITEMS = 16 * CG, PASSES = (ITEMS + 63) / 64;
   float* scr = (float*)smem + wave * 16 * ELD;
+  // fused bias gradient (GELU backward): this lane's column sums of its items
+  constexpr bool CS = EPI == EPI_GELU_BWD;
+  const bool colsum = CS && p.colsum && !park;
+  float cs[PASSES][16];
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ps++)
+#pragma unroll
+    for (int e = 0; e < 16; e++) cs[ps][e] = 0.f;
 #pragma unroll
   for (int i = 0; i < FM; i++) {
 #pragma unroll
@@ -561,7 +581,36 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, 
         for (int q = 0; q < 4; q++) *(f32x4*)(d + 4 * q) = (f32x4){v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
       } else {
         const int row = m0 + rt, col0 = n0 + wn * TN + ec;
-        if (row < p.M && col0 < p.N) epi_store16<EPI>(p, row, col0, v, (col0 + 16 <= p.N) && p.c_vec);
+        if (row < p.M && col0 < p.N)
+          epi_store16<EPI>(p, row, col0, v, (col0 + 16 <= p.N) && p.c_vec, cs[ps]);
+      }
+    }
+  }
+  if constexpr (CS) {
+    if (colsum) {
+      // rows of each wave's items through its own scratch, then the WM waves that
+      // share a column range in a fixed order, into one partial row per tile row
+      float* red = (float*)smem + NW * 16 * ELD;   // [WM_][BN_]
+#pragma unroll
+      for (int ps = 0; ps < PASSES; ps++) {
+        const int it = lane + 64 * ps;
+        if (ITEMS % 64 != 0 && it >= ITEMS) break;
+        const int er = it / CG, ec = (it % CG) * 16;
+#pragma unroll
+        for (int e = 0; e < 16; e++) scr[er * ELD + ec + e] = cs[ps][e];
+      }
+      for (int c = lane; c < TN; c += 64) {
+        float t = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r++) t += scr[r * ELD + c];
+        red[wm * BN_ + wn * TN + c] = t;
+      }
+      __syncthreads();
+      for (int c = threadIdx.x; c < BN_; c += 64 * NW) {
+        float t = red[c];
+#pragma unroll
+        for (int q = 1; q < WM_; q++) t += red[q * BN_ + c];
+        if (n0 + c < p.N) p.colsum[(int64_t)tm * p.N + n0 + c] = t;
       }
     }
   }
@@ -571,6 +620,7 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, 
 template <int BM_, int BN_, int WM_, int WN_, int STAGES, bool AK, bool BK_, int EPI>
 __global__ __launch_bounds__(64 * WM_ * WN_) void gemm_dma_kernel(GemmArgs p) {
   constexpr int SB = (BM_ + BN_) * 32 * 2;
+  static_assert(STAGES * SB >= (WM_ * WN_ * 16 * (BN_ / WN_ + 4) + WM_ * BN_) * 4, "epilogue scratch fits the stages");
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * SB];
   const int tiles_m = (p.M + BM_ - 1) / BM_, tiles_n = (p.N + BN_ - 1) / BN_;
   const int total = tiles_m * tiles_n;
@@ -644,7 +694,8 @@ __global__ __launch_bounds__(256) void sk_fixup_kernel(GemmArgs p, const float* 
       for (int e = 0; e < 4; e++) v[4 * q4 + e] += x[e];
     }
   }
-  epi_store16<EPI>(p, row, col0, v, p.c_vec && col0 + 16 <= p.N);
+  float unused[16];
+  epi_store16<EPI>(p, row, col0, v, p.c_vec && col0 + 16 <= p.N, unused);
 }
 
 
@@ -762,9 +813,32 @@ static int num_cus() {
   return n;
 }
 
+// The pipelined kernels load 16-byte vectors straight into LDS with no edge
+// handling along k: they need bf16, K a multiple of 32, aligned operands and, for
+// m-contiguous operands, a row count that is a multiple of 8.
+static bool pipelined_ok(const GemmDesc& d, bool bf16_operands) {
+  auto vec_ok = [&](const void* ptr, int64_t ld) { return (ld % 8 == 0) && ((uintptr_t)ptr % 16 == 0); };
+  return bf16_operands && d.M >= 256 && d.N >= 256 && d.K % 32 == 0 && vec_ok(d.A, d.lda) && vec_ok(d.B, d.ldb) &&
+         (d.a_kc || d.M % 8 == 0) && (d.b_kc || d.N % 8 == 0);
+}
+// Both operands k-contiguous (every GEMM of the step except the weight
+// gradients): 192 x 192 tiles on four wavefronts, three stages. For 12288-row
+// outputs with 768, 2304 or 3072 columns these come in whole multiples of 256
+// tiles, where 256 x 256 tiles leave part of the last wave of CUs idle.
+static bool use_k192(const GemmDesc& d, bool bf16_operands) {
+  return pipelined_ok(d, bf16_operands) && d.a_kc && d.b_kc && d.epi != EPI_ACC;
+}
+
+int gemm_colsum_rows(const GemmDesc& d, bool bf16_operands) {
+  if (d.epi != EPI_GELU_BWD || !use_k192(d, bf16_operands)) return 0;
+  return (d.M + 191) / 192;
+}
+
 hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
   if (d.M <= 0 || d.N <= 0) return hipSuccess;
+  if (d.colsum && gemm_colsum_rows(d, bf16_operands) == 0) return hipErrorInvalidValue;
   GemmArgs a;
+  a.colsum = d.colsum;
   a.A = d.A; a.lda = d.lda; a.B = d.B; a.ldb = d.ldb; a.C = d.C; a.ldc = d.ldc;
   a.M = d.M; a.N = d.N; a.K = d.K; a.bias = d.bias; a.resid = d.resid; a.ldr = d.ldr;
   a.aux = d.aux; a.ldaux = d.ldaux; a.beta = d.beta;
@@ -781,11 +855,7 @@ hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
     if (d.epi == EPI_ACC && d.split_ws) cv = cv && (d.N % 4 == 0) && ((uintptr_t)d.split_ws % 16 == 0);
     a.c_vec = cv;
   }
-  // The pipelined 256x256 kernel loads 16-byte vectors straight into LDS with no
-  // edge handling along k: it needs bf16, K a multiple of 32, aligned operands and,
-  // for m-contiguous operands, a row count that is a multiple of 8.
-  const bool pipelined = bf16_operands && d.M >= 256 && d.N >= 256 && d.K % 32 == 0 && a.a_vec && a.b_vec &&
-                         (d.a_kc || d.M % 8 == 0) && (d.b_kc || d.N % 8 == 0);
+  const bool pipelined = pipelined_ok(d, bf16_operands);
   const int TBM = pipelined ? 256 : BM, TBN = pipelined ? 256 : BN;
   const int tiles = ((d.M + TBM - 1) / TBM) * ((d.N + TBN - 1) / TBN);
   const int BKt = bf16_operands ? GemmCfg<bf16>::BK : GemmCfg<float>::BK;
@@ -812,11 +882,8 @@ hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
   // (weight gradients, K = B*T; the lm_head input gradient, K = vocab): every CU
   // gets the same number of k-slices. Measured on gfx950 it loses to one tile per
   // workgroup when K <= 3072, where parking partial tiles costs more than it saves.
-  // Both operands k-contiguous (every GEMM of the step except the weight
-  // gradients): 192 x 192 tiles on four wavefronts, three stages. For 12288-row
-  // outputs with 768, 2304 or 3072 columns these come in whole multiples of 256
-  // tiles, where 256 x 256 tiles leave part of the last wave of CUs idle.
-  if (pipelined && d.a_kc && d.b_kc && S == 1) return dma_epi<192, 192, 2, 2, 3, true, true>(a, d.epi, 1, s);
+  if (use_k192(d, bf16_operands)) return dma_epi<192, 192, 2, 2, 3, true, true>(a, d.epi, 1, s);
+  a.colsum = nullptr;
   if (pipelined && tiles < 2 * num_cus() && d.K >= 8192 && d.split_ws) {
     const long long KI = d.K / 32;
     const long long U = (long long)tiles * KI;

@@ -31,9 +31,15 @@ struct GemmDesc {
   void* aux; int64_t ldaux;
   float beta;
   float* split_ws; size_t split_ws_floats;   // optional split-K workspace (EPI_ACC only)
+  // optional, EPI_GELU_BWD only: per-tile-row column sums of C (fp32, before
+  // rounding) into colsum[r * N + n], r < gemm_colsum_rows(...)
+  float* colsum;
 };
 
 hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s);
+// Partial rows the fused column sum of `d` writes, or 0 when the kernel chosen for
+// `d` cannot fuse it (then colsum must be NULL and the caller sums C itself).
+int gemm_colsum_rows(const GemmDesc& d, bool bf16_operands);
 
 // x0[m, :] = wte[tok[m], :] + wpe[m % T, :]   (fp32)
 // Ids outside [0, Vp) produce NaN rows instead of out-of-bounds reads.
@@ -65,12 +71,16 @@ struct RedJob {
   int64_t part;       // float offset of the [nblk, n] partials in the partial area
   int64_t dst;        // float offset of the destination in the gradient array
   int32_t n;          // columns
-  int32_t rows_kind;  // 0: LayerNorm partials (nblk_ln rows), 1: column-sum partials (nblk_cs rows)
+  int32_t rows_kind;  // index into RedRows: which producer wrote the partials
   int32_t first_blk;
   int32_t pad;
 };
+constexpr int RED_KINDS = 3;
+struct RedRows {
+  int32_t nblk[RED_KINDS];   // partial rows written by each kind of producer in this backward
+};
 hipError_t launch_reduce_jobs(const RedJob* jobs, int njobs, int total_blk, const float* part, float* grads,
-                              int nblk_ln, int nblk_cs, float beta, hipStream_t s);
+                              RedRows rows, float beta, hipStream_t s);
 
 // Row-wise softmax cross-entropy over Vp columns of z (operand type, row stride ldz).
 // Writes row_loss[m] = lse - z[m, y[m]] and overwrites z with

@@ -57,14 +57,80 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
   }
 }
 
+// The same with the row held in registers: each lane owns NCH float4 column groups
+// (d a multiple of 4, at most 256 * NCH), so x is read once, as 16-byte vectors.
+template <typename T, int NCH>
+__global__ __launch_bounds__(256) void ln_fwd_vec_kernel(const float* __restrict__ x, const float* __restrict__ g,
+                                                         const float* __restrict__ b, T* __restrict__ y,
+                                                         float* __restrict__ mean, float* __restrict__ rstd, int M,
+                                                         int d) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int d4 = d >> 2;
+  const f32x4* xr = (const f32x4*)(x + (int64_t)row * d);
+  f32x4 xv[NCH];
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < NCH; j++) {
+    const int c4 = j * 64 + lane;
+    xv[j] = c4 < d4 ? xr[c4] : (f32x4){0.f, 0.f, 0.f, 0.f};
+    s += (xv[j][0] + xv[j][1]) + (xv[j][2] + xv[j][3]);
+  }
+  const float mu = wave_sum(s) / d;
+  float v = 0.f;
+#pragma unroll
+  for (int j = 0; j < NCH; j++)
+    if (j * 64 + lane < d4)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const float t = xv[j][e] - mu;
+        v += t * t;
+      }
+  const float rs = 1.0f / sqrtf(wave_sum(v) / d + 1e-5f);
+#pragma unroll
+  for (int j = 0; j < NCH; j++) {
+    const int c4 = j * 64 + lane;
+    if (c4 >= d4) continue;
+    const f32x4 gv = ((const f32x4*)g)[c4], bv = ((const f32x4*)b)[c4];
+    f32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; e++) o[e] = (xv[j][e] - mu) * rs * gv[e] + bv[e];
+    if constexpr (sizeof(T) == 2) {
+      bf16x4 ob;
+#pragma unroll
+      for (int e = 0; e < 4; e++) ob[e] = (bf16)o[e];
+      ((bf16x4*)(y + (int64_t)row * d))[c4] = ob;
+    } else {
+      ((f32x4*)(y + (int64_t)row * d))[c4] = o;
+    }
+  }
+  if (lane == 0) {
+    mean[row] = mu;
+    rstd[row] = rs;
+  }
+}
+
+template <typename T>
+static hipError_t ln_fwd_t(const float* x, const float* g, const float* b, T* y, float* mean, float* rstd, int M,
+                           int d, hipStream_t s) {
+  dim3 grid((M + 3) / 4);
+  const bool vec = d % 4 == 0 && ((uintptr_t)x | (uintptr_t)g | (uintptr_t)b) % 16 == 0 &&
+                   (uintptr_t)y % (4 * sizeof(T)) == 0;
+  switch (vec ? (d / 4 + 63) / 64 : 0) {
+#define LNF(N) \
+  case N: hipLaunchKernelGGL((ln_fwd_vec_kernel<T, N>), grid, dim3(256), 0, s, x, g, b, y, mean, rstd, M, d); break;
+    LNF(1) LNF(2) LNF(3) LNF(4)
+#undef LNF
+    default: hipLaunchKernelGGL(ln_fwd_kernel<T>, grid, dim3(256), 0, s, x, g, b, y, mean, rstd, M, d);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_layernorm_fwd(const float* x, const float* g, const float* b, void* y, bool bf16_out,
                                 float* mean, float* rstd, int M, int d, hipStream_t s) {
-  dim3 grid((M + 3) / 4);
-  if (bf16_out)
-    hipLaunchKernelGGL(ln_fwd_kernel<bf16>, grid, dim3(256), 0, s, x, g, b, (bf16*)y, mean, rstd, M, d);
-  else
-    hipLaunchKernelGGL(ln_fwd_kernel<float>, grid, dim3(256), 0, s, x, g, b, (float*)y, mean, rstd, M, d);
-  return hipGetLastError();
+  if (bf16_out) return ln_fwd_t<bf16>(x, g, b, (bf16*)y, mean, rstd, M, d, s);
+  return ln_fwd_t<float>(x, g, b, (float*)y, mean, rstd, M, d, s);
 }
 
 // Backward: with xhat = (x - mu) rstd and gh = dy * g,
@@ -217,7 +283,7 @@ hipError_t launch_colsum_partial(const void* X, bool bf16_in, int64_t ldx, int M
 // its job by binary search over first_blk.
 __global__ __launch_bounds__(256) void reduce_jobs_kernel(const RedJob* __restrict__ jobs, int njobs,
                                                           const float* __restrict__ part, float* __restrict__ grads,
-                                                          int nblk_ln, int nblk_cs, float beta) {
+                                                          RedRows rows, float beta) {
   __shared__ float red[16][17];
   __shared__ int job;
   if (threadIdx.x == 0) {
@@ -231,7 +297,7 @@ __global__ __launch_bounds__(256) void reduce_jobs_kernel(const RedJob* __restri
   }
   __syncthreads();
   const RedJob J = jobs[job];
-  const int nblk = J.rows_kind == 0 ? nblk_ln : nblk_cs;
+  const int nblk = rows.nblk[J.rows_kind];
   const float* pp = part + J.part;
   const int cl = threadIdx.x & 15, grp = threadIdx.x >> 4;
   const int col = ((int)blockIdx.x - J.first_blk) * 16 + cl;
@@ -250,10 +316,9 @@ __global__ __launch_bounds__(256) void reduce_jobs_kernel(const RedJob* __restri
 }
 
 hipError_t launch_reduce_jobs(const RedJob* jobs, int njobs, int total_blk, const float* part, float* grads,
-                              int nblk_ln, int nblk_cs, float beta, hipStream_t s) {
+                              RedRows rows, float beta, hipStream_t s) {
   if (njobs <= 0 || total_blk <= 0) return hipSuccess;
-  hipLaunchKernelGGL(reduce_jobs_kernel, dim3(total_blk), dim3(256), 0, s, jobs, njobs, part, grads, nblk_ln,
-                     nblk_cs, beta);
+  hipLaunchKernelGGL(reduce_jobs_kernel, dim3(total_blk), dim3(256), 0, s, jobs, njobs, part, grads, rows, beta);
   return hipGetLastError();
 }
 

@@ -61,6 +61,8 @@ struct Timer {
 
 }  // namespace
 
+enum { RED_LN = 0, RED_QKV = 1, RED_FC = 2 };   // rows_kind of the deferred reductions
+
 struct gpt_model {
   gpt_config cfg;
   bool bf16;
@@ -286,16 +288,18 @@ void plan(gpt_model* h) {
     RedJob j{(int64_t)red_floats, (int64_t)t->offset, (int32_t)t->numel(), kind, h->rblocks, 0};
     h->rjobs.push_back(j);
     h->rpart[dst] = j.part;
-    red_floats += (kind == 0 ? ln_blk : cs_blk) * t->numel();
+    red_floats += (kind == RED_LN ? ln_blk : cs_blk) * t->numel();
     h->rblocks += (int)((t->numel() + 15) / 16);
   };
-  red_job("lnf.g", 0);
-  red_job("lnf.b", 0);
+  // kinds: RED_LN LayerNorm backward partials, RED_QKV and RED_FC the qkv and fc
+  // bias column sums (from the GEMM epilogue or a column-sum pass)
+  red_job("lnf.g", RED_LN);
+  red_job("lnf.b", RED_LN);
   for (int l = 0; l < h->L; l++) {
     const std::string p = "h" + std::to_string(l) + ".";
-    for (const char* n : {"ln1.g", "ln1.b", "proj.b", "ln2.g", "ln2.b", "fcproj.b"}) red_job(p + n, 0);
-    red_job(p + "fc.b", 1);
-    red_job(p + "attn.b", 1);
+    for (const char* n : {"ln1.g", "ln1.b", "proj.b", "ln2.g", "ln2.b", "fcproj.b"}) red_job(p + n, RED_LN);
+    red_job(p + "fc.b", RED_FC);
+    red_job(p + "attn.b", RED_QKV);
   }
   h->red = w.take(red_floats * fb);
   h->rtable = w.take(h->rjobs.size() * sizeof(RedJob));
@@ -594,6 +598,10 @@ int gpt_backward(gpt_model* h) {
   if (!h->fwd_pending) return fail(h, GPT_E_STATE, "gpt_backward needs a preceding gpt_forward_loss");
   if ((rc = upload_tables(h))) return rc;
   const int B = h->cur_B, T = h->cur_T, M = B * T, d = h->d;
+  RedRows rows;                                   // partial rows per producer kind, set as they run
+  rows.nblk[RED_LN] = (M + LN_BWD_ROWS - 1) / LN_BWD_ROWS;
+  rows.nblk[RED_QKV] = (M + COLSUM_ROWS - 1) / COLSUM_ROWS;
+  rows.nblk[RED_FC] = (M + COLSUM_ROWS - 1) / COLSUM_ROWS;
   const bool bf = h->bf16;
   hipStream_t s = h->stream;
   const float beta = h->grads_fresh ? 0.f : 1.f;
@@ -628,6 +636,9 @@ int gpt_backward(gpt_model* h) {
                                   EPI_GELU_BWD);
       g.aux = act(h, la.u);
       g.ldaux = 4 * d;
+      const int fc_rows = gemm_colsum_rows(g, bf);   // fc.b gradient fused into this GEMM when possible
+      if (fc_rows) g.colsum = red_part(h, p + "fc.b");
+      rows.nblk[RED_FC] = fc_rows ? fc_rows : (M + COLSUM_ROWS - 1) / COLSUM_ROWS;
       RUN("gemm_dgrad", "fcproj_dgrad", gemm(h, g, bf));
       GemmDesc gw = gemm_desc(dres_opnd, d, false, act(h, la.h), 4 * d, false, G(h, p + "fcproj.w"), 4 * d, d, 4 * d,
                               M, EPI_ACC);
@@ -639,7 +650,7 @@ int gpt_backward(gpt_model* h) {
       GemmDesc gw2 = gemm_desc(du, 4 * d, false, act(h, la.ln2), d, false, G(h, p + "fc.w"), d, 4 * d, d, M, EPI_ACC);
       gw2.beta = beta;
       RUN("gemm_wgrad", "fc_wgrad", gemm(h, gw2, bf));
-      if ((rc = colsum(h, du, bf, 4 * d, M, 4 * d, p + "fc.b"))) return rc;
+      if (!fc_rows && (rc = colsum(h, du, bf, 4 * d, M, 4 * d, p + "fc.b"))) return rc;
       const std::string fcproj_b = p + "fcproj.b";
       if ((rc = ln_bwd(h, dln, act<float>(h, la.xmid), act<float>(h, la.ln2_mean), act<float>(h, la.ln2_rstd),
                        p + "ln2.g", p + "ln2.b", dres, fcproj_b.c_str(), M)))
@@ -672,8 +683,7 @@ int gpt_backward(gpt_model* h) {
   }
   RUN("colsum", "bias_and_ln_grads",
       launch_reduce_jobs(ws<RedJob>(h, h->rtable), (int)h->rjobs.size(), h->rblocks, ws<float>(h, h->red),
-                         (float*)h->buf.grads, (M + LN_BWD_ROWS - 1) / LN_BWD_ROWS, (M + COLSUM_ROWS - 1) / COLSUM_ROWS,
-                         beta, s));
+                         (float*)h->buf.grads, rows, beta, s));
   // ---- embeddings: dres holds d x0
   if (h->grads_fresh && T < h->Tmax) {
     float* wpe_tail = G(h, "wpe") + (size_t)T * d;
