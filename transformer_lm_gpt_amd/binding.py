@@ -14,7 +14,8 @@ from typing import Dict, List, Optional, Tuple
 import numpy as np
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libgpt.so")
+# GPT_MI355X_LIB names another build of the library (to compare two builds side by side)
+LIB_PATH = os.environ.get("GPT_MI355X_LIB") or os.path.join(PKG, "libgpt.so")
 
 GPT_OK = 0
 ERRORS = {-1: "GPT_E_INVAL", -2: "GPT_E_SEQ_TOO_LONG", -3: "GPT_E_STATE", -4: "GPT_E_UNSUPPORTED",

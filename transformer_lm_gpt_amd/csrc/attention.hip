@@ -495,6 +495,38 @@ __device__ inline float group_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Inclusive prefix sum along each 16-lane row with DPP row shifts (a lane whose
+// source is outside its row adds 0): lane 15 of every row ends with the row total.
+__device__ inline float row16_total(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, false));   // row_shr:1
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, false));   // row_shr:2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, false));   // row_shr:4
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, false));   // row_shr:8
+  return v;
+}
+
+// Column sums of a wave's CB x 4 accumulator values (hd column cb*16 + 4g + i, one
+// query or key per lane & 15) over its 16 rows and then over the four waves in a
+// fixed order, into dst[c] for c < HDP (bias gradient partials).
+template <int HDP>
+__device__ inline void block_colsum(const f32x4 (&acc)[HDP / 16], float mul, float* red, float* dst) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4;
+#pragma unroll
+  for (int cb = 0; cb < HDP / 16; cb++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const float t = row16_total(acc[cb][i] * mul);
+      if ((lane & 15) == 15) red[w * HDP + cb * 16 + 4 * g + i] = t;
+    }
+  __syncthreads();
+  if (threadIdx.x < HDP) {
+    float t = red[threadIdx.x];
+#pragma unroll
+    for (int q = 1; q < 4; q++) t += red[q * HDP + threadIdx.x];
+    dst[threadIdx.x] = t;
+  }
+}
+
 // The exponentials run in base 2 with the 1/sqrt(hd) scale folded in: with
 // c = log2(e)/sqrt(hd), exp(S*scale - x) = exp2(S*c - x*log2(e)), one FMA and one
 // v_exp per score. Only the diagonal tile of a causal block needs the mask.
@@ -607,10 +639,10 @@ __global__ __launch_bounds__(256) void attn_fwd_v2(const bf16* __restrict__ qkv,
 // dQ for a 64-query block; also writes D = rowsum(dO * O) for these queries,
 // which the dK/dV kernel (launched after) reads.
 template <int HDP>
-__global__ __launch_bounds__(256) void attn_bwd_dq_v2(const bf16* __restrict__ qkv, const bf16* __restrict__ o,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_bwd_dq_v2(const bf16* __restrict__ qkv, const bf16* __restrict__ o,
                                                       const bf16* __restrict__ dout, const float* __restrict__ lse,
                                                       float* __restrict__ Dv, bf16* __restrict__ dqkv, int Tn, int H,
-                                                      float scale) {
+                                                      float scale, float* __restrict__ bias_part) {
   typedef ATile<HDP> AT;
   constexpr int KK = HDP / 32, CB = HDP / 16;
   __shared__ __attribute__((aligned(16))) bf16 Ks[64 * HDP];
@@ -708,13 +740,19 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_v2(const bf16* __restrict__ q
       *(bf16x4*)(row + cb * 16 + 4 * g) = v;
     }
   }
+  // queries past Tn have P = 0, so their dq is 0 and adds nothing here
+  if (bias_part) {
+    __syncthreads();                                  // the K/V tiles are free: reuse them for the reduction
+    block_colsum<HDP>(dqt, scale, (float*)Ks, bias_part + ((int64_t)b * nqb + qb) * ld + h * HDP);
+  }
 }
 
 // dK and dV for a 64-key block over the query tiles at or after it.
 template <int HDP>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_v2(const bf16* __restrict__ qkv, const bf16* __restrict__ dout,
                                                         const float* __restrict__ lse, const float* __restrict__ Dv,
-                                                        bf16* __restrict__ dqkv, int Tn, int H, float scale) {
+                                                        bf16* __restrict__ dqkv, int Tn, int H, float scale,
+                                                        float* __restrict__ bias_part) {
   typedef ATile<HDP> AT;
   constexpr int KK = HDP / 32, CB = HDP / 16;
   __shared__ __attribute__((aligned(16))) bf16 Qs[64 * HDP];
@@ -828,6 +866,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_v2(const bf16* __restrict__
       *(bf16x4*)(row + 2 * d + cb * 16 + 4 * g) = vv;
     }
   }
+  // keys past Tn see no query with P != 0, so their dk and dv are 0
+  if (bias_part) {
+    float* dst = bias_part + ((int64_t)b * nb_t + kb) * ld + h * HDP;
+    __syncthreads();
+    block_colsum<HDP>(dkt, scale, (float*)Qs, dst + d);
+    __syncthreads();
+    block_colsum<HDP>(dvt, 1.f, (float*)Qs, dst + 2 * d);
+  }
 }
 
 // ----------------------------------------------------------------------------- launchers
@@ -871,23 +917,28 @@ static hipError_t bwd_t(const void* qkv, const void* o, const void* dout, const 
   return hipGetLastError();
 }
 
+int attn_bwd_colsum_rows(bool bf16_ops, int B, int T, int hd) {
+  return bf16_ops && (hd == 32 || hd == 64) ? B * ((T + 63) / 64) : 0;
+}
+
 hipError_t launch_attn_bwd(const void* qkv, const void* o, const void* dout, const float* lse, float* D,
-                           void* dqkv, bool bf16_ops, int B, int T, int H, int hd, hipStream_t s) {
+                           void* dqkv, bool bf16_ops, int B, int T, int H, int hd, float* bias_part, hipStream_t s) {
   if (hd <= 0 || hd > 64) return hipErrorInvalidValue;
+  if (bias_part && attn_bwd_colsum_rows(bf16_ops, B, T, hd) == 0) return hipErrorInvalidValue;
   if (bf16_ops && (hd == 32 || hd == 64)) {
     if ((int64_t)T * 3 * H * hd * 2 > INT32_MAX) return hipErrorInvalidValue;   // 32-bit buffer offsets per sequence
     dim3 grid(B * H, (T + 63) / 64);
     const float scale = 1.0f / sqrtf((float)hd);
     if (hd == 64) {
       hipLaunchKernelGGL(attn_bwd_dq_v2<64>, grid, dim3(256), 0, s, (const bf16*)qkv, (const bf16*)o,
-                         (const bf16*)dout, lse, D, (bf16*)dqkv, T, H, scale);
+                         (const bf16*)dout, lse, D, (bf16*)dqkv, T, H, scale, bias_part);
       hipLaunchKernelGGL(attn_bwd_dkdv_v2<64>, grid, dim3(256), 0, s, (const bf16*)qkv, (const bf16*)dout, lse,
-                         (const float*)D, (bf16*)dqkv, T, H, scale);
+                         (const float*)D, (bf16*)dqkv, T, H, scale, bias_part);
     } else {
       hipLaunchKernelGGL(attn_bwd_dq_v2<32>, grid, dim3(256), 0, s, (const bf16*)qkv, (const bf16*)o,
-                         (const bf16*)dout, lse, D, (bf16*)dqkv, T, H, scale);
+                         (const bf16*)dout, lse, D, (bf16*)dqkv, T, H, scale, bias_part);
       hipLaunchKernelGGL(attn_bwd_dkdv_v2<32>, grid, dim3(256), 0, s, (const bf16*)qkv, (const bf16*)dout, lse,
-                         (const float*)D, (bf16*)dqkv, T, H, scale);
+                         (const float*)D, (bf16*)dqkv, T, H, scale, bias_part);
     }
     return hipGetLastError();
   }

@@ -95,9 +95,13 @@ hipError_t launch_mean(const float* row_loss, int M, float* out, hipStream_t s);
 hipError_t launch_attn_fwd(const void* qkv, void* o, float* lse, bool bf16_ops, int B, int T, int H,
                            int hd, hipStream_t s);
 // Attention backward: D = rowsum(dO * O), then dK/dV and dQ into dqkv [B*T, 3*d].
+// bias_part (optional): the qkv bias gradient's partial column sums of dqkv (fp32,
+// before rounding), one row per (sequence, 64-row block): [attn_bwd_colsum_rows(), 3 H hd].
+// Must be NULL when attn_bwd_colsum_rows() is 0 for the same arguments.
 hipError_t launch_attn_bwd(const void* qkv, const void* o, const void* dout, const float* lse,
                            float* Dbuf, void* dqkv, bool bf16_ops, int B, int T, int H, int hd,
-                           hipStream_t s);
+                           float* bias_part, hipStream_t s);
+int attn_bwd_colsum_rows(bool bf16_ops, int B, int T, int hd);
 
 // Embedding backward: dwpe[t] = beta * dwpe[t] + sum_b dx0[b, t]; dwte[tok] += rows of dx0,
 // summed deterministically (stable sort by id, fixed-order segment sums).

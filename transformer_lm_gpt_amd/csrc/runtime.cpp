@@ -288,7 +288,10 @@ void plan(gpt_model* h) {
     RedJob j{(int64_t)red_floats, (int64_t)t->offset, (int32_t)t->numel(), kind, h->rblocks, 0};
     h->rjobs.push_back(j);
     h->rpart[dst] = j.part;
-    red_floats += (kind == RED_LN ? ln_blk : cs_blk) * t->numel();
+    const size_t rows = kind == RED_LN ? ln_blk
+                        : kind == RED_QKV ? std::max(cs_blk, (size_t)h->Bmax * ((h->Tmax + 63) / 64))
+                                          : cs_blk;
+    red_floats += rows * t->numel();
     h->rblocks += (int)((t->numel() + 15) / 16);
   };
   // kinds: RED_LN LayerNorm backward partials, RED_QKV and RED_FC the qkv and fc
@@ -664,9 +667,11 @@ int gpt_backward(gpt_model* h) {
       GemmDesc gw = gemm_desc(dres_opnd, d, false, act(h, la.att), d, false, G(h, p + "proj.w"), d, d, d, M, EPI_ACC);
       gw.beta = beta;
       RUN("gemm_wgrad", "proj_wgrad", gemm(h, gw, bf));
+      const int qkv_rows = attn_bwd_colsum_rows(bf, B, T, h->hd);   // attn.b gradient fused into the kernels
+      rows.nblk[RED_QKV] = qkv_rows ? qkv_rows : (M + COLSUM_ROWS - 1) / COLSUM_ROWS;
       RUN("attn_bwd", "attn_bwd",
           launch_attn_bwd(act(h, la.qkv), act(h, la.att), dO, act<float>(h, la.lse), ws<float>(h, h->attnD), dqkv, bf,
-                          B, T, h->H, h->hd, s));
+                          B, T, h->H, h->hd, qkv_rows ? red_part(h, p + "attn.b") : nullptr, s));
       GemmDesc g2 = bf ? gemm_desc(dqkv, 3 * d, true, WopT(h, p + "attn.w"), 3 * d, true, dln, d, M, d, 3 * d, EPI_F32)
                        : gemm_desc(dqkv, 3 * d, true, Wop(h, p + "attn.w"), d, false, dln, d, M, d, 3 * d, EPI_F32);
       RUN("gemm_dgrad", "qkv_dgrad", gemm(h, g2, bf));
@@ -674,7 +679,7 @@ int gpt_backward(gpt_model* h) {
                                EPI_ACC);
       gw2.beta = beta;
       RUN("gemm_wgrad", "qkv_wgrad", gemm(h, gw2, bf));
-      if ((rc = colsum(h, dqkv, bf, 3 * d, M, 3 * d, p + "attn.b"))) return rc;
+      if (!qkv_rows && (rc = colsum(h, dqkv, bf, 3 * d, M, 3 * d, p + "attn.b"))) return rc;
       const std::string proj_b = p + "proj.b";
       if ((rc = ln_bwd(h, dln, act<float>(h, la.x), act<float>(h, la.ln1_mean), act<float>(h, la.ln1_rstd),
                        p + "ln1.g", p + "ln1.b", dres, proj_b.c_str(), M)))
