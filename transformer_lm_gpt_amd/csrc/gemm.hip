@@ -813,6 +813,122 @@ static int num_cus() {
   return n;
 }
 
+// ----------------------------------------------------------------------------- grouped weight gradients
+__device__ inline int find_problem(const WgradProblem* __restrict__ pr, int np, int t) {
+  int lo = 0, hi = np - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pr[mid].first_tile <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ inline GemmArgs problem_args(const WgradProblem& pr, int K, float beta) {
+  GemmArgs p;
+  p.A = pr.A; p.lda = pr.lda; p.B = pr.B; p.ldb = pr.ldb; p.C = pr.C; p.ldc = pr.ldc;
+  p.M = pr.M; p.N = pr.N; p.K = K;
+  p.bias = nullptr; p.resid = nullptr; p.ldr = 0; p.aux = nullptr; p.ldaux = 0;
+  p.beta = beta; p.a_vec = 1; p.b_vec = 1; p.c_vec = pr.c_vec; p.kchunk = K; p.part = nullptr; p.colsum = nullptr;
+  return p;
+}
+
+// Stream-K partial tiles: workgroup w parks at most two (the tile its range starts
+// in, slot 0, and the one it ends in, slot 1).
+__device__ inline int group_slot(int w, int r, int W, long long U, int KI) {
+  const long long beg = (long long)w * U / W;
+  return 2 * w + (r == (int)(beg / KI) ? 0 : 1);
+}
+
+template <int BM_, int BN_, int WM_, int WN_, int STAGES>
+__global__ __launch_bounds__(64 * WM_ * WN_) void gemm_group_kernel(const WgradProblem* __restrict__ probs, int nprob,
+                                                                    int total, int dp_tiles, int K, float beta,
+                                                                    float* __restrict__ ws) {
+  constexpr int SB = (BM_ + BN_) * 32 * 2;
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * SB];
+  const int W = gridDim.x, w = blockIdx.x, KI = K / 32;
+  auto run = [&](int t, int s0, int s1, float* park) {
+    const WgradProblem pr = probs[find_problem(probs, nprob, t)];
+    const GemmArgs p = problem_args(pr, K, beta);
+    int tm, tn;
+    tile_coords(t - pr.first_tile, pr.tiles_m, pr.tiles_n, tm, tn);
+    dma_tile<BM_, BN_, WM_, WN_, STAGES, false, false, EPI_ACC>(p, smem, tm, tn, s0, s1, park);
+  };
+  for (int t = w; t < dp_tiles; t += W) run(t, 0, KI, nullptr);   // whole tiles, round-robin
+  const int rem = total - dp_tiles;
+  if (rem == 0) return;
+  const long long U = (long long)rem * KI;
+  const long long beg = (long long)w * U / W, end = (long long)(w + 1) * U / W;
+  for (long long x = beg; x < end;) {
+    const int r = (int)(x / KI);
+    const int s0 = (int)(x - (long long)r * KI);
+    const int s1 = (int)min((long long)KI, end - (long long)r * KI);
+    const bool split = sk_owner((long long)r * KI, W, U) != sk_owner((long long)r * KI + KI - 1, W, U);
+    run(dp_tiles + r, s0, s1, split ? ws + (int64_t)group_slot(w, r, W, U, KI) * (BM_ * BN_) : nullptr);
+    x = (long long)r * KI + s1;
+  }
+}
+
+// One workgroup per 16 rows of a split leftover tile: its parked partials summed in
+// owner order, then C = beta * C + sum.
+template <int BM_, int BN_>
+__global__ __launch_bounds__(256) void group_fixup_kernel(const WgradProblem* __restrict__ probs, int nprob,
+                                                          int total, int dp_tiles, int K, float beta,
+                                                          const float* __restrict__ ws, int W) {
+  static_assert(BN_ == 256, "one thread per 16 columns of a 256-wide tile row");
+  const int KI = K / 32, rem = total - dp_tiles;
+  const long long U = (long long)rem * KI;
+  const int r = blockIdx.x;
+  const int first = sk_owner((long long)r * KI, W, U), last = sk_owner((long long)r * KI + KI - 1, W, U);
+  if (first == last) return;
+  const int t = dp_tiles + r;
+  const WgradProblem pr = probs[find_problem(probs, nprob, t)];
+  const GemmArgs p = problem_args(pr, K, beta);
+  int tm, tn;
+  tile_coords(t - pr.first_tile, pr.tiles_m, pr.tiles_n, tm, tn);
+  const int rr = blockIdx.y * 16 + (threadIdx.x >> 4), c0 = (threadIdx.x & 15) * 16;
+  const int row = tm * BM_ + rr, col0 = tn * BN_ + c0;
+  if (row >= p.M || col0 >= p.N) return;
+  float v[16];
+#pragma unroll
+  for (int e = 0; e < 16; e++) v[e] = 0.f;
+  for (int o = first; o <= last; o++) {
+    if ((long long)o * U / W == (long long)(o + 1) * U / W) continue;   // a workgroup with no units
+    const float* src = ws + (int64_t)group_slot(o, r, W, U, KI) * (BM_ * BN_) + rr * BN_ + c0;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; q4++) {
+      const f32x4 x = *(const f32x4*)(src + 4 * q4);
+#pragma unroll
+      for (int e = 0; e < 4; e++) v[4 * q4 + e] += x[e];
+    }
+  }
+  float unused[16];
+  epi_store16<EPI_ACC>(p, row, col0, v, p.c_vec && col0 + 16 <= p.N, unused);
+}
+
+static int num_cus();
+
+bool wgrad_group_ok(int M, int N, int64_t lda, int64_t ldb, int64_t ldc) {
+  return M >= 8 && N >= 8 && M % 8 == 0 && N % 8 == 0 && lda % 8 == 0 && ldb % 8 == 0 && ldc >= N;
+}
+int wgrad_group_tiles(int M, int N) { return ((M + 255) / 256) * ((N + 255) / 256); }
+// two parked 256 x 256 partial tiles per workgroup, for up to 256 workgroups
+size_t wgrad_group_ws_floats() { return (size_t)2 * 256 * 256 * 256; }
+
+hipError_t launch_wgrad_group(const WgradProblem* probs, int nprob, int total_tiles, int K, float beta, float* ws,
+                              size_t ws_floats, hipStream_t s) {
+  if (nprob <= 0 || total_tiles <= 0 || K <= 0) return hipSuccess;
+  const int W = (int)std::min<size_t>(num_cus(), ws_floats / (2 * 256 * 256));   // one workgroup per CU
+  if (K % 32 != 0 || W < 1) return hipErrorInvalidValue;
+  const int dp = total_tiles / W * W, rem = total_tiles - dp;
+  hipLaunchKernelGGL((gemm_group_kernel<256, 256, 2, 4, 4>), dim3(W), dim3(512), 0, s, probs, nprob, total_tiles, dp,
+                     K, beta, ws);
+  if (rem > 0)
+    hipLaunchKernelGGL((group_fixup_kernel<256, 256>), dim3(rem, 16), dim3(256), 0, s, probs, nprob, total_tiles, dp,
+                       K, beta, (const float*)ws, W);
+  return hipGetLastError();
+}
+
 // The pipelined kernels load 16-byte vectors straight into LDS with no edge
 // handling along k: they need bf16, K a multiple of 32, aligned operands and, for
 // m-contiguous operands, a row count that is a multiple of 8.

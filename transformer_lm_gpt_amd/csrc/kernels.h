@@ -41,6 +41,31 @@ hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s);
 // `d` cannot fuse it (then colsum must be NULL and the caller sums C itself).
 int gemm_colsum_rows(const GemmDesc& d, bool bf16_operands);
 
+// Grouped weight gradients, all sharing the contraction length K (the tokens):
+// for each problem, C[m, n] = beta * C[m, n] + sum_k A[k * lda + m] * B[k * ldb + n]
+// (bf16 operands, both m-contiguous; fp32 C). One launch covers every problem:
+// whole 256 x 256 tiles are dealt round-robin to one workgroup per CU, and the
+// tiles left over after the last full round are shared stream-K style, their
+// partial sums reduced in a fixed order by a second kernel.
+struct WgradProblem {
+  const void* A; int64_t lda;
+  const void* B; int64_t ldb;
+  float* C; int64_t ldc;
+  int32_t M, N;
+  int32_t tiles_m, tiles_n;
+  int32_t first_tile;   // tiles of the problems before this one
+  int32_t c_vec;        // C rows allow 16-column vector access
+};
+// Whether a problem of this shape can join the grouped launch (pointers 16-byte aligned).
+bool wgrad_group_ok(int M, int N, int64_t lda, int64_t ldb, int64_t ldc);
+// Tiles of a problem in the grouped launch.
+int wgrad_group_tiles(int M, int N);
+// Partial-sum workspace (floats) for the full grouped launch (fewer workgroups run
+// with less).
+size_t wgrad_group_ws_floats();
+hipError_t launch_wgrad_group(const WgradProblem* probs, int nprob, int total_tiles, int K, float beta, float* ws,
+                              size_t ws_floats, hipStream_t s);
+
 // x0[m, :] = wte[tok[m], :] + wpe[m % T, :]   (fp32)
 // Ids outside [0, Vp) produce NaN rows instead of out-of-bounds reads.
 hipError_t launch_embed_fwd(const float* wte, const float* wpe, const int32_t* tok, float* x0,

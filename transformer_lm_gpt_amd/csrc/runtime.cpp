@@ -76,7 +76,15 @@ struct gpt_model {
   Slice x_final, lnf, lnf_mean, lnf_rstd, logits, row_loss, tokens, targets;
   size_t act_bytes = 0;
   // workspace
-  Slice dres, dres_op, dln, du, dO, dqkv, attnD, red, emb_keys, emb_piece, norm_part, opt, split, ttable, rtable;
+  Slice dres, dln, du, dO, dqkv, attnD, red, emb_keys, emb_piece, norm_part, opt, split, ttable, rtable;
+  // bf16: operand copies of the residual-stream gradients, d x_l (l = 0..L) and
+  // d xmid_l, and per-layer du and dqkv, kept for the weight gradients that run
+  // together at the end of the backward
+  Slice rx, rm, wtable;
+  size_t layer_stride_du = 0, layer_stride_dqkv = 0, resid_stride = 0;   // bytes
+  std::vector<WgradProblem> wprobs;   // host copy of the grouped weight-gradient table
+  int wtiles = 0;
+  bool wgroup = false;                // every weight gradient can join the grouped launch
   size_t split_floats = 0;
   std::vector<TransposeEntry> tentries;   // 2-D weights whose transposed shadow the dgrads read
   int64_t ttiles = 0;
@@ -274,11 +282,17 @@ void plan(gpt_model* h) {
   // ---- workspace
   Planner w;
   h->dres = w.take(M * d * fb);
-  h->dres_op = w.take(h->bf16 ? M * d * ob : 0);
+
   h->dln = w.take(M * d * fb);
-  h->du = w.take(M * 4 * d * ob);
+  const size_t per_layer = h->bf16 ? (size_t)L : 1;
+  h->layer_stride_du = h->bf16 ? M * 4 * d * ob : 0;
+  h->layer_stride_dqkv = h->bf16 ? M * 3 * d * ob : 0;
+  h->resid_stride = M * d * ob;
+  h->du = w.take(per_layer * M * 4 * d * ob);
+  h->rx = w.take(h->bf16 ? (L + 1) * M * d * ob : 0);
+  h->rm = w.take(h->bf16 ? L * M * d * ob : 0);
   h->dO = w.take(M * d * ob);
-  h->dqkv = w.take(M * 3 * d * ob);
+  h->dqkv = w.take(per_layer * M * 3 * d * ob);
   h->attnD = w.take(bht * fb);
   const size_t ln_blk = (M + LN_BWD_ROWS - 1) / LN_BWD_ROWS;
   const size_t cs_blk = (M + COLSUM_ROWS - 1) / COLSUM_ROWS;
@@ -313,6 +327,7 @@ void plan(gpt_model* h) {
   // CUs + 2 * tiles of them for the < 512-tile GEMMs that use stream-K)
   h->split_floats = 16 * (size_t)d * d + 4096;
   if (M >= 256 && d >= 256) h->split_floats = std::max(h->split_floats, (size_t)1664 * 256 * 256);
+  if (h->bf16) h->split_floats = std::max(h->split_floats, wgrad_group_ws_floats());
   h->split = w.take(h->split_floats * fb);
   for (const Tensor& t : h->tensors) {
     if (t.ndim != 2 || t.name == "wpe") continue;
@@ -322,6 +337,17 @@ void plan(gpt_model* h) {
   }
   h->ttable = w.take(h->tentries.size() * sizeof(TransposeEntry));
   h->opt = w.take(sizeof(OptState));
+  // the weight gradients as one grouped launch: wte (tied lm_head), then per layer
+  // fcproj.w, fc.w, proj.w, attn.w; operands are [tokens, features] (m-contiguous)
+  if (h->bf16) {
+    const int64_t Vp = h->Vp, D = d;
+    bool ok = wgrad_group_ok(h->Vp, d, h->ldz, D, D) && h->split_floats >= wgrad_group_ws_floats();
+    ok = ok && wgrad_group_ok(d, 4 * d, D, 4 * D, 4 * D) && wgrad_group_ok(4 * d, d, 4 * D, D, D);
+    ok = ok && wgrad_group_ok(d, d, D, D, D) && wgrad_group_ok(3 * d, d, 3 * D, D, D);
+    h->wgroup = ok;
+    (void)Vp;
+    h->wtable = w.take((4 * (size_t)L + 1) * sizeof(WgradProblem));
+  }
   h->ws_bytes = w.total;
 }
 
@@ -339,13 +365,45 @@ int colsum(gpt_model* h, const void* X, bool bf16_in, int64_t ldx, int M, int N,
 // column sums of the gain and shift gradients and, when `resid_bias` names a
 // tensor, of the incoming residual gradient (the bias gradient of that projection).
 int ln_bwd(gpt_model* h, const float* dy, const float* x, const float* mean, const float* rstd,
-           const std::string& gname, const std::string& bname, const float* dres, const char* resid_bias, int M) {
+           const std::string& gname, const std::string& bname, const float* dres, const char* resid_bias, void* dx_op,
+           int M) {
   float* pr = resid_bias ? red_part(h, resid_bias) : nullptr;
-  void* dx_op = h->bf16 ? ws(h, h->dres_op) : nullptr;
   RUN("layernorm", "layernorm_bwd",
       launch_layernorm_bwd(dy, x, mean, rstd, P(h, gname), dres, ws<float>(h, h->dres), dx_op, h->bf16,
                            red_part(h, gname), red_part(h, bname), pr, M, h->d, h->stream));
   return GPT_OK;
+}
+
+// bf16 operand slots of the backward (see gpt_model)
+void* rx_slot(gpt_model* h, int l) { return (char*)ws(h, h->rx) + (size_t)l * h->resid_stride; }
+void* rm_slot(gpt_model* h, int l) { return (char*)ws(h, h->rm) + (size_t)l * h->resid_stride; }
+void* du_slot(gpt_model* h, int l) { return (char*)ws(h, h->du) + (size_t)l * h->layer_stride_du; }
+void* dqkv_slot(gpt_model* h, int l) { return (char*)ws(h, h->dqkv) + (size_t)l * h->layer_stride_dqkv; }
+
+// The grouped weight-gradient problems with this binding's addresses.
+void build_wgrad_table(gpt_model* h) {
+  h->wprobs.clear();
+  h->wtiles = 0;
+  const int d = h->d;
+  auto add = [&](const void* A, int64_t lda, const void* B, int64_t ldb, const std::string& w, int Mo, int No) {
+    WgradProblem q;
+    q.A = A; q.lda = lda; q.B = B; q.ldb = ldb; q.C = G(h, w); q.ldc = No;
+    q.M = Mo; q.N = No;
+    q.tiles_m = (Mo + 255) / 256; q.tiles_n = (No + 255) / 256;
+    q.first_tile = h->wtiles;
+    q.c_vec = (No % 8 == 0) ? 1 : 0;
+    h->wtiles += wgrad_group_tiles(Mo, No);
+    h->wprobs.push_back(q);
+  };
+  add(act(h, h->logits), h->ldz, act(h, h->lnf), d, "wte", h->Vp, d);
+  for (int l = h->L - 1; l >= 0; l--) {
+    const LayerAct& la = h->layers[l];
+    const std::string p = "h" + std::to_string(l) + ".";
+    add(rx_slot(h, l + 1), d, act(h, la.h), 4 * d, p + "fcproj.w", d, 4 * d);
+    add(du_slot(h, l), 4 * d, act(h, la.ln2), d, p + "fc.w", 4 * d, d);
+    add(rm_slot(h, l), d, act(h, la.att), d, p + "proj.w", d, d);
+    add(dqkv_slot(h, l), 3 * d, act(h, la.ln1), d, p + "attn.w", 3 * d, d);
+  }
 }
 
 // Copies the transpose and reduction tables into the bound workspace (once per bind).
@@ -356,6 +414,11 @@ int upload_tables(gpt_model* h) {
   if (e == hipSuccess && h->bf16)
     e = hipMemcpyAsync(ws(h, h->ttable), h->tentries.data(), h->tentries.size() * sizeof(TransposeEntry),
                        hipMemcpyHostToDevice, h->stream);
+  if (e == hipSuccess && h->bf16) {
+    build_wgrad_table(h);
+    e = hipMemcpyAsync(ws(h, h->wtable), h->wprobs.data(), h->wprobs.size() * sizeof(WgradProblem),
+                       hipMemcpyHostToDevice, h->stream);
+  }
   if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
   if (e != hipSuccess) return hip_check(h, e, "upload tables");
   h->tables_ready = true;
@@ -600,7 +663,7 @@ int gpt_backward(gpt_model* h) {
   if (rc) return rc;
   if (!h->fwd_pending) return fail(h, GPT_E_STATE, "gpt_backward needs a preceding gpt_forward_loss");
   if ((rc = upload_tables(h))) return rc;
-  const int B = h->cur_B, T = h->cur_T, M = B * T, d = h->d;
+  const int B = h->cur_B, T = h->cur_T, M = B * T, d = h->d, L = h->L;
   RedRows rows;                                   // partial rows per producer kind, set as they run
   rows.nblk[RED_LN] = (M + LN_BWD_ROWS - 1) / LN_BWD_ROWS;
   rows.nblk[RED_QKV] = (M + COLSUM_ROWS - 1) / COLSUM_ROWS;
@@ -609,33 +672,41 @@ int gpt_backward(gpt_model* h) {
   hipStream_t s = h->stream;
   const float beta = h->grads_fresh ? 0.f : 1.f;
   float* dres = ws<float>(h, h->dres);
-  const void* dres_opnd = bf ? ws(h, h->dres_op) : (const void*)dres;   // GEMM operand view of dres
   float* dln = ws<float>(h, h->dln);
-  void* du = ws(h, h->du);
   void* dO = ws(h, h->dO);
-  void* dqkv = ws(h, h->dqkv);
+  // In bf16 mode the weight gradients wait for the end of the backward (their
+  // operands stay in per-layer slots); in fp32 mode each runs as soon as its
+  // operands exist, before the residual gradient is overwritten.
+  auto wgrad_now = [&](const void* A, int64_t lda, const void* Bm, int64_t ldb, const std::string& w, int Mo,
+                       int No, const char* what) {
+    GemmDesc g = gemm_desc(A, lda, false, Bm, ldb, false, G(h, w), No, Mo, No, M, EPI_ACC);
+    g.beta = beta;
+    RUN("gemm_wgrad", what, gemm(h, g, bf));
+    return GPT_OK;
+  };
 
   // lm_head (tied): dwte = dlogits^T lnf; dlnf = dlogits wte
   {
-    GemmDesc g = gemm_desc(act(h, h->logits), h->ldz, false, act(h, h->lnf), d, false, G(h, "wte"), d, h->Vp, d, M,
-                           EPI_ACC);
-    g.beta = beta;
-    RUN("gemm_wgrad", "lm_head_wgrad", gemm(h, g, bf));
+    if (!bf && (rc = wgrad_now(act(h, h->logits), h->ldz, act(h, h->lnf), d, "wte", h->Vp, d, "lm_head_wgrad")))
+      return rc;
     GemmDesc g2 = bf ? gemm_desc(act(h, h->logits), h->ldz, true, WopT(h, "wte"), h->Vp, true, dln, d, M, d, h->Vp, EPI_F32)
                      : gemm_desc(act(h, h->logits), h->ldz, true, Wop(h, "wte"), d, false, dln, d, M, d, h->Vp, EPI_F32);
     RUN("gemm_dgrad", "lm_head_dgrad", gemm(h, g2, bf));
   }
   if ((rc = ln_bwd(h, dln, act<float>(h, h->x_final), act<float>(h, h->lnf_mean), act<float>(h, h->lnf_rstd),
-                   "lnf.g", "lnf.b", nullptr, nullptr, M)))
+                   "lnf.g", "lnf.b", nullptr, nullptr, bf ? rx_slot(h, L) : nullptr, M)))
     return rc;
 
-  for (int l = h->L - 1; l >= 0; l--) {
+  for (int l = L - 1; l >= 0; l--) {
     const LayerAct& la = h->layers[l];
     const std::string p = "h" + std::to_string(l) + ".";
+    void* du = bf ? du_slot(h, l) : ws(h, h->du);
+    void* dqkv = bf ? dqkv_slot(h, l) : ws(h, h->dqkv);
     // ---- MLP: x_{l+1} = xmid + gelu(LN2(xmid) Wfc^T + bfc) Wp^T + bp ; dres holds d x_{l+1}
     {
-      GemmDesc g = bf ? gemm_desc(dres_opnd, d, true, WopT(h, p + "fcproj.w"), d, true, du, 4 * d, M, 4 * d, d, EPI_GELU_BWD)
-                      : gemm_desc(dres_opnd, d, true, Wop(h, p + "fcproj.w"), 4 * d, false, du, 4 * d, M, 4 * d, d,
+      const void* dx = bf ? rx_slot(h, l + 1) : (const void*)dres;   // GEMM operand view of d x_{l+1}
+      GemmDesc g = bf ? gemm_desc(dx, d, true, WopT(h, p + "fcproj.w"), d, true, du, 4 * d, M, 4 * d, d, EPI_GELU_BWD)
+                      : gemm_desc(dx, d, true, Wop(h, p + "fcproj.w"), 4 * d, false, du, 4 * d, M, 4 * d, d,
                                   EPI_GELU_BWD);
       g.aux = act(h, la.u);
       g.ldaux = 4 * d;
@@ -643,30 +714,24 @@ int gpt_backward(gpt_model* h) {
       if (fc_rows) g.colsum = red_part(h, p + "fc.b");
       rows.nblk[RED_FC] = fc_rows ? fc_rows : (M + COLSUM_ROWS - 1) / COLSUM_ROWS;
       RUN("gemm_dgrad", "fcproj_dgrad", gemm(h, g, bf));
-      GemmDesc gw = gemm_desc(dres_opnd, d, false, act(h, la.h), 4 * d, false, G(h, p + "fcproj.w"), 4 * d, d, 4 * d,
-                              M, EPI_ACC);
-      gw.beta = beta;
-      RUN("gemm_wgrad", "fcproj_wgrad", gemm(h, gw, bf));
+      if (!bf && (rc = wgrad_now(dx, d, act(h, la.h), 4 * d, p + "fcproj.w", d, 4 * d, "fcproj_wgrad"))) return rc;
       GemmDesc g2 = bf ? gemm_desc(du, 4 * d, true, WopT(h, p + "fc.w"), 4 * d, true, dln, d, M, d, 4 * d, EPI_F32)
                        : gemm_desc(du, 4 * d, true, Wop(h, p + "fc.w"), d, false, dln, d, M, d, 4 * d, EPI_F32);
       RUN("gemm_dgrad", "fc_dgrad", gemm(h, g2, bf));
-      GemmDesc gw2 = gemm_desc(du, 4 * d, false, act(h, la.ln2), d, false, G(h, p + "fc.w"), d, 4 * d, d, M, EPI_ACC);
-      gw2.beta = beta;
-      RUN("gemm_wgrad", "fc_wgrad", gemm(h, gw2, bf));
+      if (!bf && (rc = wgrad_now(du, 4 * d, act(h, la.ln2), d, p + "fc.w", 4 * d, d, "fc_wgrad"))) return rc;
       if (!fc_rows && (rc = colsum(h, du, bf, 4 * d, M, 4 * d, p + "fc.b"))) return rc;
       const std::string fcproj_b = p + "fcproj.b";
       if ((rc = ln_bwd(h, dln, act<float>(h, la.xmid), act<float>(h, la.ln2_mean), act<float>(h, la.ln2_rstd),
-                       p + "ln2.g", p + "ln2.b", dres, fcproj_b.c_str(), M)))
+                       p + "ln2.g", p + "ln2.b", dres, fcproj_b.c_str(), bf ? rm_slot(h, l) : nullptr, M)))
         return rc;
     }
     // ---- attention: xmid = x + attn(LN1(x)) Wo^T + bo ; dres now holds d xmid
     {
-      GemmDesc g = bf ? gemm_desc(dres_opnd, d, true, WopT(h, p + "proj.w"), d, true, dO, d, M, d, d, EPI_STORE)
-                      : gemm_desc(dres_opnd, d, true, Wop(h, p + "proj.w"), d, false, dO, d, M, d, d, EPI_STORE);
+      const void* dx = bf ? rm_slot(h, l) : (const void*)dres;       // GEMM operand view of d xmid
+      GemmDesc g = bf ? gemm_desc(dx, d, true, WopT(h, p + "proj.w"), d, true, dO, d, M, d, d, EPI_STORE)
+                      : gemm_desc(dx, d, true, Wop(h, p + "proj.w"), d, false, dO, d, M, d, d, EPI_STORE);
       RUN("gemm_dgrad", "proj_dgrad", gemm(h, g, bf));
-      GemmDesc gw = gemm_desc(dres_opnd, d, false, act(h, la.att), d, false, G(h, p + "proj.w"), d, d, d, M, EPI_ACC);
-      gw.beta = beta;
-      RUN("gemm_wgrad", "proj_wgrad", gemm(h, gw, bf));
+      if (!bf && (rc = wgrad_now(dx, d, act(h, la.att), d, p + "proj.w", d, d, "proj_wgrad"))) return rc;
       const int qkv_rows = attn_bwd_colsum_rows(bf, B, T, h->hd);   // attn.b gradient fused into the kernels
       rows.nblk[RED_QKV] = qkv_rows ? qkv_rows : (M + COLSUM_ROWS - 1) / COLSUM_ROWS;
       RUN("attn_bwd", "attn_bwd",
@@ -675,21 +740,34 @@ int gpt_backward(gpt_model* h) {
       GemmDesc g2 = bf ? gemm_desc(dqkv, 3 * d, true, WopT(h, p + "attn.w"), 3 * d, true, dln, d, M, d, 3 * d, EPI_F32)
                        : gemm_desc(dqkv, 3 * d, true, Wop(h, p + "attn.w"), d, false, dln, d, M, d, 3 * d, EPI_F32);
       RUN("gemm_dgrad", "qkv_dgrad", gemm(h, g2, bf));
-      GemmDesc gw2 = gemm_desc(dqkv, 3 * d, false, act(h, la.ln1), d, false, G(h, p + "attn.w"), d, 3 * d, d, M,
-                               EPI_ACC);
-      gw2.beta = beta;
-      RUN("gemm_wgrad", "qkv_wgrad", gemm(h, gw2, bf));
+      if (!bf && (rc = wgrad_now(dqkv, 3 * d, act(h, la.ln1), d, p + "attn.w", 3 * d, d, "qkv_wgrad"))) return rc;
       if (!qkv_rows && (rc = colsum(h, dqkv, bf, 3 * d, M, 3 * d, p + "attn.b"))) return rc;
       const std::string proj_b = p + "proj.b";
+      // d x_0 feeds only the embedding backward, which reads the fp32 copy
       if ((rc = ln_bwd(h, dln, act<float>(h, la.x), act<float>(h, la.ln1_mean), act<float>(h, la.ln1_rstd),
-                       p + "ln1.g", p + "ln1.b", dres, proj_b.c_str(), M)))
+                       p + "ln1.g", p + "ln1.b", dres, proj_b.c_str(), bf && l > 0 ? rx_slot(h, l) : nullptr, M)))
         return rc;
+    }
+  }
+  if (bf) {
+    // every weight gradient of the micro-batch: one grouped launch when the shapes
+    // allow it (K = B*T a multiple of 32), else one GEMM each
+    if (h->wgroup && M % 32 == 0) {
+      RUN("gemm_wgrad", "grouped_wgrad",
+          launch_wgrad_group(ws<WgradProblem>(h, h->wtable), (int)h->wprobs.size(), h->wtiles, M, beta,
+                             (float*)((char*)h->buf.workspace + h->split.off), h->split_floats, s));
+    } else {
+      for (const WgradProblem& q : h->wprobs) {
+        GemmDesc g = gemm_desc(q.A, q.lda, false, q.B, q.ldb, false, q.C, q.ldc, q.M, q.N, M, EPI_ACC);
+        g.beta = beta;
+        RUN("gemm_wgrad", "wgrad", gemm(h, g, bf));
+      }
     }
   }
   RUN("colsum", "bias_and_ln_grads",
       launch_reduce_jobs(ws<RedJob>(h, h->rtable), (int)h->rjobs.size(), h->rblocks, ws<float>(h, h->red),
                          (float*)h->buf.grads, rows, beta, s));
-  // ---- embeddings: dres holds d x0
+  // ---- embeddings: dres holds d x0 (after the lm_head weight gradient: both write wte's gradient)
   if (h->grads_fresh && T < h->Tmax) {
     float* wpe_tail = G(h, "wpe") + (size_t)T * d;
     RUN("embed", "zero wpe tail", launch_zero(wpe_tail, (size_t)(h->Tmax - T) * d, s));
