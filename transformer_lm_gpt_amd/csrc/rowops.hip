@@ -378,80 +378,90 @@ __global__ __launch_bounds__(256) void xent_kernel(T* z, int64_t ldz, const int3
   }
 }
 
-// bf16 logits rows up to XENT_LDS_MAX columns: the row is read once from HBM into
-// LDS with 16-byte loads while the running max and sum are formed, then the
-// gradient row is written back from LDS with 16-byte stores. 1024 threads per row.
-constexpr int XENT_LDS_MAX = 57344;     // 112 KB of bf16
-__global__ __launch_bounds__(1024) void xent_lds_kernel(bf16* z, int64_t ldz, const int32_t* __restrict__ y,
+// bf16 rows of up to 8192 NV columns held in registers: each of 1024 threads keeps
+// NV 16-byte vectors of the row, forms the max and the sum of exp relative to its
+// own max, the (max, sum) pairs are merged over the row, and the gradient is
+// written from the registers: one read and one write of the row, and registers
+// small enough for two rows in flight per CU.
+template <int NV>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void xent_reg_kernel(bf16* z, int64_t ldz, const int32_t* __restrict__ y,
                                                         float* __restrict__ row_loss, int Vp, float grad_scale) {
-  extern __shared__ __attribute__((aligned(16))) bf16 zs[];
+  constexpr float L2E = 1.4426950408889634f;
   __shared__ float red_m[16], red_s[16];
-  __shared__ float s_lse;
-  const int row = blockIdx.x;
+  __shared__ float s_m, s_s;
+  const int row = blockIdx.x, tid = threadIdx.x, w = tid >> 6;
   bf16* zr = z + (int64_t)row * ldz;
   const int tgt = y[row];
-  const int nv = Vp / 8;                     // Vp is a multiple of 8 here
-  float m = -INFINITY, s = 0.f;
-  for (int i = threadIdx.x; i < nv; i += 1024) {
-    const bf16x8 v = *(const bf16x8*)(zr + 8 * i);
-    *(bf16x8*)(zs + 8 * i) = v;
-    float vm = (float)v[0];
+  const int nv = Vp / 8;
+  bf16x8 v[NV];
+  float m = -INFINITY;
 #pragma unroll
-    for (int e = 1; e < 8; e++) vm = fmaxf(vm, (float)v[e]);
-    const float mn = fmaxf(m, vm);
-    float add = 0.f;
+  for (int j = 0; j < NV; j++) {
+    const int i = tid + 1024 * j;
+    if (i < nv) {
+      v[j] = *(const bf16x8*)(zr + 8 * i);
 #pragma unroll
-    for (int e = 0; e < 8; e++) add += __expf((float)v[e] - mn);
-    s = (m == -INFINITY ? 0.f : s * __expf(m - mn)) + add;
-    m = mn;
+      for (int e = 0; e < 8; e++) m = fmaxf(m, (float)v[j][e]);
+    }
   }
+  float s = 0.f;
+  const float ml = m * L2E;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float m2 = __shfl_xor(m, o, WAVE), s2 = __shfl_xor(s, o, WAVE);
+  for (int j = 0; j < NV; j++)
+    if (tid + 1024 * j < nv)
+#pragma unroll
+      for (int e = 0; e < 8; e++) s += __builtin_amdgcn_exp2f(__builtin_fmaf((float)v[j][e], L2E, -ml));
+  // merge (max, sum) pairs: s is relative to m
+  auto merge = [](float& m, float& s, float m2, float s2) {
     const float mm = fmaxf(m, m2);
-    s = (m == -INFINITY ? 0.f : s * __expf(m - mm)) + (m2 == -INFINITY ? 0.f : s2 * __expf(m2 - mm));
+    s = (m == -INFINITY ? 0.f : s * __builtin_amdgcn_exp2f((m - mm) * L2E)) +
+        (m2 == -INFINITY ? 0.f : s2 * __builtin_amdgcn_exp2f((m2 - mm) * L2E));
     m = mm;
-  }
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
+  };
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) merge(m, s, __shfl_xor(m, o, WAVE), __shfl_xor(s, o, WAVE));
+  if ((tid & 63) == 0) {
     red_m[w] = m;
     red_s[w] = s;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float mm = red_m[0];
-    for (int i = 1; i < 16; i++) mm = fmaxf(mm, red_m[i]);
-    float ss = 0.f;
-    for (int i = 0; i < 16; i++) ss += red_m[i] == -INFINITY ? 0.f : red_s[i] * __expf(red_m[i] - mm);
-    const float lse = mm + logf(ss);
-    s_lse = lse;
+  if (tid == 0) {
+    float mm = red_m[0], ss = red_s[0];
+    for (int i = 1; i < 16; i++) merge(mm, ss, red_m[i], red_s[i]);
+    s_m = mm;
+    s_s = ss;
     const bool ok = tgt >= 0 && tgt < Vp;   // an id outside the table yields a NaN loss
-    row_loss[row] = lse - (ok ? (float)zs[tgt] : __builtin_nanf(""));
+    row_loss[row] = mm + logf(ss) - (ok ? (float)zr[tgt] : __builtin_nanf(""));
   }
   __syncthreads();
-  const float lse = s_lse;
-  for (int i = threadIdx.x; i < nv; i += 1024) {
-    const bf16x8 v = *(const bf16x8*)(zs + 8 * i);
-    bf16x8 o;
+  const float mrow = s_m * L2E, inv = grad_scale / s_s;
 #pragma unroll
-    for (int e = 0; e < 8; e++) {
-      const int c = 8 * i + e;
-      o[e] = (bf16)((__expf((float)v[e] - lse) - (c == tgt ? 1.f : 0.f)) * grad_scale);
+  for (int j = 0; j < NV; j++) {
+    const int i = tid + 1024 * j;
+    if (i < nv) {
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        float g = __builtin_amdgcn_exp2f(__builtin_fmaf((float)v[j][e], L2E, -mrow)) * inv;
+        if (8 * i + e == tgt) g -= grad_scale;
+        o[e] = (bf16)g;
+      }
+      *(bf16x8*)(zr + 8 * i) = o;
     }
-    *(bf16x8*)(zr + 8 * i) = o;
   }
 }
 
 hipError_t launch_xent(void* z, bool bf16_z, int64_t ldz, const int32_t* y, float* row_loss, int M, int Vp,
                        float grad_scale, hipStream_t s) {
-  if (bf16_z && Vp % 8 == 0 && ldz % 8 == 0 && Vp <= XENT_LDS_MAX && (uintptr_t)z % 16 == 0) {
-    const size_t lds = (size_t)Vp * 2;
-    if (lds > 65536) {
-      hipError_t e = hipFuncSetAttribute((const void*)xent_lds_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)lds);
-      if (e != hipSuccess) return e;
+  if (bf16_z && Vp % 8 == 0 && ldz % 8 == 0 && (uintptr_t)z % 16 == 0 && Vp <= 8 * 8192) {
+    const int nv = (Vp / 8 + 1023) / 1024;
+    switch (nv) {
+#define XR(N) \
+  case N: hipLaunchKernelGGL((xent_reg_kernel<N>), dim3(M), dim3(1024), 0, s, (bf16*)z, ldz, y, row_loss, Vp, grad_scale); break;
+      XR(1) XR(2) XR(3) XR(4) XR(5) XR(6) XR(7) XR(8)
+#undef XR
+      default: return hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL(xent_lds_kernel, dim3(M), dim3(1024), lds, s, (bf16*)z, ldz, y, row_loss, Vp, grad_scale);
     return hipGetLastError();
   }
   if (bf16_z)
