@@ -59,6 +59,24 @@ def cpu_baseline(cfg, params, batches, n_seq: int):
                       f"({dt:.1f} s); AdamW excluded"}
 
 
+def traffic_of(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    (profiles/traffic.json), or None when its source has changed since the counters
+    were taken (the summary records a hash of the kernel's source file)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec:
+        return None
+    with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+            return None
+    return rec["bytes_per_launch"]
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -66,9 +84,12 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gpt2_124m")
     ap.add_argument("--precision", default="bf16", choices=["bf16", "fp32"])
-    ap.add_argument("--kernel", default="lm_head_fwd",
-                    help="kernel family whose launches are timed for the roofline line")
+    ap.add_argument("--kernel", default="gemm_wgrad",
+                    help="kernel family whose launches are timed for the roofline line "
+                         "(gemm_wgrad: the grouped weight-gradient GEMM, the step's largest kernel; lm_head_fwd)")
     ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the oracle's timed sample (0: skip)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run 3 plain device copies of this many bytes (calibrates the HBM byte counters)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the data-parallel all-reduce "
@@ -78,6 +99,15 @@ def main(argv=None):
     import torch
     from transformer_lm_gpt_amd import workloads as W
     from transformer_lm_gpt_amd.binding import GPT
+
+    if a.copy_bytes > 0:
+        src = torch.ones(a.copy_bytes // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": a.copy_bytes, "copies": 3}), flush=True)
+        return 0
 
     cfg = W.CONFIGS[a.workload]
     B, T, A = cfg.batch, cfg.block_size, cfg.grad_accum
@@ -136,13 +166,23 @@ def main(argv=None):
     roof = None
     if kern_n:
         avg_ms = kern_ms / kern_n
+        d, L, Vp = cfg.n_embd, cfg.n_layer, cfg.padded_vocab
         if a.kernel == "lm_head_fwd":
-            work = 2.0 * B * T * cfg.padded_vocab * cfg.n_embd          # FLOPs per launch
-            roof = {"kernel": "lm_head forward GEMM (gemm_dma_kernel 256x256, bf16, store epilogue)", "bound": "mfma",
+            work = 2.0 * B * T * Vp * d                                  # FLOPs per launch
+            roof = {"kernel": "lm_head forward GEMM (gemm_dma_kernel 192x192, bf16, store epilogue)", "bound": "mfma",
                     "achieved": round(work / (avg_ms / 1e3) / 1e12, 2), "peak": peak / 1e12, "unit": "TFLOP/s",
                     "frac": round(work / (avg_ms / 1e3) / peak, 4), "traffic": None,
                     "avg_launch_ms": round(avg_ms, 4), "launches": kern_n,
                     "work_per_launch": f"2*M*Vp*d = {work:.4g} FLOP, M = {B * T}"}
+        elif a.kernel == "gemm_wgrad" and a.precision == "bf16":
+            # one launch per micro-batch: every weight gradient, K = B*T tokens each
+            work = 2.0 * B * T * (Vp * d + L * 12 * d * d)               # FLOPs per launch
+            roof = {"kernel": "grouped weight-gradient GEMM (gemm_group_kernel 256x256 + group_fixup_kernel, "
+                              "bf16 operands, fp32 accumulate)", "bound": "mfma",
+                    "achieved": round(work / (avg_ms / 1e3) / 1e12, 2), "peak": peak / 1e12, "unit": "TFLOP/s",
+                    "frac": round(work / (avg_ms / 1e3) / peak, 4), "traffic": traffic_of("gemm_group_kernel"),
+                    "avg_launch_ms": round(avg_ms, 4), "launches": kern_n,
+                    "work_per_launch": f"2*M*(Vp*d + 12*L*d^2) = {work:.4g} FLOP, M = {B * T}"}
         else:
             roof = {"kernel": a.kernel, "avg_launch_ms": round(avg_ms, 4), "launches": kern_n}
 

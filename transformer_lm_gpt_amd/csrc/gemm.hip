@@ -854,7 +854,11 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void gemm_group_kernel(const WgradP
     tile_coords(t - pr.first_tile, pr.tiles_m, pr.tiles_n, tm, tn);
     dma_tile<BM_, BN_, WM_, WN_, STAGES, false, false, EPI_ACC>(p, smem, tm, tn, s0, s1, park);
   };
-  for (int t = w; t < dp_tiles; t += W) run(t, 0, KI, nullptr);   // whole tiles, round-robin
+  // whole tiles, one round of W at a time; workgroups are dealt round-robin to the 8
+  // XCDs, so give each XCD a contiguous run of the round's tiles (they share A or B
+  // panels in that XCD's L2)
+  const int lw = W % 8 == 0 ? (w & 7) * (W >> 3) + (w >> 3) : w;
+  for (int t = lw; t < dp_tiles; t += W) run(t, 0, KI, nullptr);
   const int rem = total - dp_tiles;
   if (rem == 0) return;
   const long long U = (long long)rem * KI;
