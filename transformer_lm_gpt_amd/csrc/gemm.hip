@@ -437,6 +437,30 @@ __device__ inline void dma_mc(const bf16* __restrict__ src, int64_t ld, int row0
   }
 }
 
+// 64-wide k-slices of a k-contiguous operand: a row is 128 bytes = 8 units, unit u of
+// row r at r*8 + (u ^ ((r >> 1) & 7)); a 1 KB wavefront instruction covers 8 rows, one
+// whole 128-byte line per row (half the requests per byte of the 32-wide slices).
+template <int ROWS, int NW>
+__device__ inline void dma_kc64(const bf16* __restrict__ src, int64_t ld, int row0, int nrows, int k0, char* lds,
+                                int wave, int lane) {
+  constexpr int CHUNKS = ROWS * 64 * 2 / 1024;
+  static_assert(ROWS % 16 == 0 && CHUNKS % NW == 0, "k-contiguous tile shape");
+#pragma unroll
+  for (int i = 0; i < CHUNKS / NW; i++) {
+    const int ch = wave + NW * i;
+    const int r = ch * 8 + (lane >> 3);
+    const int u = (lane & 7) ^ ((r >> 1) & 7);
+    const int gr = min(row0 + r, nrows - 1);
+    const bf16* g = src + (int64_t)gr * ld + k0 + 8 * u;
+    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(lds + ch * 1024), 16, 0, 0);
+  }
+}
+// fragment of the h-th 32-wide half of a 64-wide slice
+__device__ inline bf16x8 frag_kc64(const char* lds, int r, int h) {
+  const int u = (4 * h + ((threadIdx.x & 63) >> 4)) ^ ((r >> 1) & 7);
+  return *(const bf16x8*)(lds + (r * 8 + u) * 16);
+}
+
 // MFMA fragment (8 consecutive k = 8*(lane>>4) .. +7 of one row) from a stage buffer.
 template <int ROWS>
 __device__ inline bf16x8 frag_kc(const char* lds, int r) {
@@ -475,13 +499,16 @@ __device__ inline void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int
 // One output tile over k-slices [s0, s1) of 32. With park == nullptr the fused
 // epilogue is applied; otherwise the raw fp32 sums go to park (BM_ x BN_, row-major).
 // Ends with a barrier, so the LDS may be reused by the caller.
-template <int BM_, int BN_, int WM_, int WN_, int STAGES, bool AK, bool BK_, int EPI>
+// KS: k per slice, 32, or 64 when both operands are k-contiguous (s0, s1 count
+// slices of KS).
+template <int BM_, int BN_, int WM_, int WN_, int STAGES, bool AK, bool BK_, int EPI, int KS = 32>
 __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, int tn, int s0, int s1,
                                          float* park) {
+  static_assert(KS == 32 || (KS == 64 && AK && BK_), "64-wide slices need k-contiguous operands");
   constexpr int NW = WM_ * WN_;
   constexpr int TM = BM_ / WM_, TN = BN_ / WN_;
   constexpr int FM = TM / 16, FN = TN / 16;
-  constexpr int AB = BM_ * 32 * 2, BB = BN_ * 32 * 2, SB = AB + BB;
+  constexpr int AB = BM_ * KS * 2, BB = BN_ * KS * 2, SB = AB + BB;
   constexpr int LPS = (AB + BB) / 1024 / NW;     // load instructions per stage per wave
   const int m0 = tm * BM_, n0 = tn * BN_;
   const bf16* A = (const bf16*)p.A;
@@ -498,7 +525,12 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, 
   const int nk = s1 - s0;
   auto issue = [&](int t) {
     char* st = smem + (t % STAGES) * SB;
-    const int k0 = (s0 + t) * 32;
+    const int k0 = (s0 + t) * KS;
+    if constexpr (KS == 64) {
+      dma_kc64<BM_, NW>(A, p.lda, m0, p.M, k0, st, wave, lane);
+      dma_kc64<BN_, NW>(B, p.ldb, n0, p.N, k0, st + AB, wave, lane);
+      return;
+    }
     if constexpr (AK) dma_kc<BM_, NW>(A, p.lda, m0, p.M, k0, st, wave, lane);
     else dma_mc<BM_, NW>(A, p.lda, m0, p.M, k0, st, wave, lane);
     if constexpr (BK_) dma_kc<BN_, NW>(B, p.ldb, n0, p.N, k0, st + AB, wave, lane);
@@ -521,23 +553,28 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, 
     if (t + STAGES - 1 < nk) issue(t + STAGES - 1);
     const char* As = smem + (t % STAGES) * SB;
     const char* Bs = As + AB;
-    bf16x8 af[FM], bfr[FN];
 #pragma unroll
-    for (int i = 0; i < FM; i++) {
-      const int r = wm * TM + i * 16;
-      if constexpr (AK) af[i] = frag_kc<BM_>(As, r + (lane & 15));
-      else af[i] = frag_mc<BM_>(As, r);
+    for (int h = 0; h < KS / 32; h++) {
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; i++) {
+        const int r = wm * TM + i * 16;
+        if constexpr (KS == 64) af[i] = frag_kc64(As, r + (lane & 15), h);
+        else if constexpr (AK) af[i] = frag_kc<BM_>(As, r + (lane & 15));
+        else af[i] = frag_mc<BM_>(As, r);
+      }
+#pragma unroll
+      for (int j = 0; j < FN; j++) {
+        const int r = wn * TN + j * 16;
+        if constexpr (KS == 64) bfr[j] = frag_kc64(Bs, r + (lane & 15), h);
+        else if constexpr (BK_) bfr[j] = frag_kc<BN_>(Bs, r + (lane & 15));
+        else bfr[j] = frag_mc<BN_>(Bs, r);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++) acc[i][j] = Mfma<bf16>::mma(af[i], bfr[j], acc[i][j]);
     }
-#pragma unroll
-    for (int j = 0; j < FN; j++) {
-      const int r = wn * TN + j * 16;
-      if constexpr (BK_) bfr[j] = frag_kc<BN_>(Bs, r + (lane & 15));
-      else bfr[j] = frag_mc<BN_>(Bs, r);
-    }
-#pragma unroll
-    for (int i = 0; i < FM; i++)
-#pragma unroll
-      for (int j = 0; j < FN; j++) acc[i][j] = Mfma<bf16>::mma(af[i], bfr[j], acc[i][j]);
   }
 
   // Epilogue through LDS: each wave parks one 16-row block of its TM x TN
@@ -617,9 +654,9 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, 
   __syncthreads();
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int STAGES, bool AK, bool BK_, int EPI>
+template <int BM_, int BN_, int WM_, int WN_, int STAGES, bool AK, bool BK_, int EPI, int KS = 32>
 __global__ __launch_bounds__(64 * WM_ * WN_) void gemm_dma_kernel(GemmArgs p) {
-  constexpr int SB = (BM_ + BN_) * 32 * 2;
+  constexpr int SB = (BM_ + BN_) * KS * 2;
   static_assert(STAGES * SB >= (WM_ * WN_ * 16 * (BN_ / WN_ + 4) + WM_ * BN_) * 4, "epilogue scratch fits the stages");
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * SB];
   const int tiles_m = (p.M + BM_ - 1) / BM_, tiles_n = (p.N + BN_ - 1) / BN_;
@@ -630,9 +667,9 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void gemm_dma_kernel(GemmArgs p) {
   if (total % 8 == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
   int tm, tn;
   tile_coords(bid, tiles_m, tiles_n, tm, tn);
-  const int s0 = blockIdx.z * (p.kchunk / 32);
-  const int s1 = min(p.K, (int)(blockIdx.z + 1) * p.kchunk) / 32;
-  dma_tile<BM_, BN_, WM_, WN_, STAGES, AK, BK_, EPI>(p, smem, tm, tn, s0, s1, nullptr);
+  const int s0 = blockIdx.z * (p.kchunk / KS);
+  const int s1 = min(p.K, (int)(blockIdx.z + 1) * p.kchunk) / KS;
+  dma_tile<BM_, BN_, WM_, WN_, STAGES, AK, BK_, EPI, KS>(p, smem, tm, tn, s0, s1, nullptr);
 }
 
 // Stream-K: gridDim.x workgroups share the tiles x (K/32) slice-units evenly, each a
@@ -699,15 +736,15 @@ __global__ __launch_bounds__(256) void sk_fixup_kernel(GemmArgs p, const float* 
 }
 
 
-template <int BM_, int BN_, int WM_, int WN_, int STAGES, bool AK, bool BK_>
+template <int BM_, int BN_, int WM_, int WN_, int STAGES, bool AK, bool BK_, int KS = 32>
 static hipError_t dma_epi(const GemmArgs& a, int epi, int splits, hipStream_t s) {
   const int total = ((a.M + BM_ - 1) / BM_) * ((a.N + BN_ - 1) / BN_);
   dim3 grid(total, 1, splits);
   switch (epi) {
-#define GPT_DMA_CASE(E)                                                                                          \
-  case E:                                                                                                        \
-    hipLaunchKernelGGL((gemm_dma_kernel<BM_, BN_, WM_, WN_, STAGES, AK, BK_, E>), grid, dim3(64 * WM_ * WN_), 0, \
-                       s, a);                                                                                    \
+#define GPT_DMA_CASE(E)                                                                                              \
+  case E:                                                                                                            \
+    hipLaunchKernelGGL((gemm_dma_kernel<BM_, BN_, WM_, WN_, STAGES, AK, BK_, E, KS>), grid, dim3(64 * WM_ * WN_), 0, \
+                       s, a);                                                                                        \
     break;
     GPT_DMA_CASE(EPI_STORE)
     GPT_DMA_CASE(EPI_BIAS)
@@ -1002,7 +1039,14 @@ hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
   // (weight gradients, K = B*T; the lm_head input gradient, K = vocab): every CU
   // gets the same number of k-slices. Measured on gfx950 it loses to one tile per
   // workgroup when K <= 3072, where parking partial tiles costs more than it saves.
-  if (use_k192(d, bf16_operands)) return dma_epi<192, 192, 2, 2, 3, true, true>(a, d.epi, 1, s);
+  if (use_k192(d, bf16_operands)) {
+    // one tile per CU or fewer: 64-wide k-slices (half the memory requests per byte;
+    // two stages fill 96 KB of LDS, so one workgroup per CU). Otherwise 32-wide slices
+    // in three stages, which leave room for two workgroups per CU.
+    const int t192 = ((d.M + 191) / 192) * ((d.N + 191) / 192);
+    if (t192 <= num_cus() && d.K % 64 == 0) return dma_epi<192, 192, 2, 2, 2, true, true, 64>(a, d.epi, 1, s);
+    return dma_epi<192, 192, 2, 2, 3, true, true>(a, d.epi, 1, s);
+  }
   a.colsum = nullptr;
   if (pipelined && tiles < 2 * num_cus() && d.K >= 8192 && d.split_ws) {
     const long long KI = d.K / 32;
