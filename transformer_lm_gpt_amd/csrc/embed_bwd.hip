@@ -24,7 +24,7 @@ static int ceil_log2(int x) {
   return s;
 }
 
-int embed_bwd_sort_size(int M) { return 1 << ceil_log2(M < 2 ? 2 : M); }
+int embed_bwd_sort_size(int M) { return 1 << ceil_log2(M < 16 ? 16 : M); }
 
 __global__ void wpe_grad_kernel(const float* __restrict__ dx0, float* __restrict__ dwpe, float beta, int B, int T,
                                 int d) {
@@ -35,28 +35,60 @@ __global__ void wpe_grad_kernel(const float* __restrict__ dx0, float* __restrict
   dwpe[i] = (beta != 0.f ? beta * dwpe[i] : 0.f) + s;
 }
 
-// Bitonic sort of n (a power of two) keys (id << shift) | position in LDS.
+// Bitonic sort of n (a power of two, at least 16) keys (id << shift) | position in
+// LDS. Distances j >= 16 run as LDS passes over the n/2 compare-exchange pairs;
+// the four distances below 16 of every stage run in registers, each thread holding
+// 16 consecutive keys, so only about half the passes need a barrier.
+__device__ inline void cas(uint32_t& a, uint32_t& b, bool up) {
+  if ((a > b) == up) {
+    const uint32_t t = a;
+    a = b;
+    b = t;
+  }
+}
+
 __global__ __launch_bounds__(1024) void sort_keys_kernel(const int32_t* __restrict__ tok, int M, int shift, int n,
                                                          uint32_t* __restrict__ out) {
-  extern __shared__ uint32_t sk[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t sk[];
   for (int i = threadIdx.x; i < n; i += 1024)
     sk[i] = i < M ? (((uint32_t)tok[i]) << shift) | (uint32_t)i : 0xFFFFFFFFu;
   __syncthreads();
   for (int k = 2; k <= n; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n; i += 1024) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const uint32_t a = sk[i], b = sk[ixj];
-          const bool up = (i & k) == 0;
-          if ((a > b) == up) {
-            sk[i] = b;
-            sk[ixj] = a;
-          }
-        }
+    for (int j = k >> 1; j >= 16; j >>= 1) {
+      int lj = 0;
+      while ((1 << lj) < j) lj++;
+      for (int q = threadIdx.x; q < (n >> 1); q += 1024) {
+        const int i = ((q >> lj) << (lj + 1)) | (q & (j - 1));   // i has bit lj clear; partner i + j
+        uint32_t a = sk[i], b = sk[i + j];
+        cas(a, b, (i & k) == 0);
+        sk[i] = a;
+        sk[i + j] = b;
       }
       __syncthreads();
     }
+    // distances 8, 4, 2, 1 (those below k) inside each thread's 16 consecutive keys
+    for (int base = threadIdx.x * 16; base < n; base += 1024 * 16) {
+      uint32_t v[16];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const uint4 w = *(const uint4*)(sk + base + 4 * q);
+        v[4 * q] = w.x;
+        v[4 * q + 1] = w.y;
+        v[4 * q + 2] = w.z;
+        v[4 * q + 3] = w.w;
+      }
+      const bool up = (base & k) == 0;                          // the same for all 16 when k >= 16
+#pragma unroll
+      for (int j = 8; j >= 1; j >>= 1) {
+        if (j >= k) continue;
+#pragma unroll
+        for (int e = 0; e < 16; e++)
+          if ((e & j) == 0) cas(v[e], v[e + j], k >= 16 ? up : (((base + e) & k) == 0));
+      }
+#pragma unroll
+      for (int q = 0; q < 4; q++) *(uint4*)(sk + base + 4 * q) = make_uint4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    }
+    __syncthreads();
   }
   for (int i = threadIdx.x; i < M; i += 1024) out[i] = sk[i];
 }
@@ -110,7 +142,7 @@ hipError_t launch_embed_bwd(const float* dx0, const int32_t* tok, float* dwte, f
                             int T, int d, int Vp, EmbedBwdScratch scr, hipStream_t s) {
   const int M = B * T;
   const int shift = ceil_log2(M < 2 ? 2 : M);
-  const int n = 1 << shift;
+  const int n = 1 << ceil_log2(M < 16 ? 16 : M);   // sort size: at least one thread's 16 keys
   if (n > SORT_MAX || ((uint64_t)Vp << shift) > 0xFFFFFFFFull) return hipErrorInvalidValue;
   hipLaunchKernelGGL(wpe_grad_kernel, dim3((T * d + 255) / 256), dim3(256), 0, s, dx0, dwpe, beta_wpe, B, T, d);
   const size_t lds = (size_t)n * sizeof(uint32_t);
