@@ -160,22 +160,41 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
     pg[j] = pb[j] = pr[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
   const int row0 = blockIdx.x * LN_BWD_ROWS;
+  // the next row's x, dy and dres are requested before this row's reductions run
+  f32x4 xn[NCH], dyn[NCH], rn[NCH];
+  auto fetch = [&](int row) {
+    const int64_t o4 = (int64_t)row * d4;
+#pragma unroll
+    for (int j = 0; j < NCH; j++) {
+      const int c4 = j * 64 + lane;
+      const bool in = c4 < d4;
+      xn[j] = in ? ((const f32x4*)x)[o4 + c4] : (f32x4){0.f, 0.f, 0.f, 0.f};
+      dyn[j] = in ? ((const f32x4*)dy)[o4 + c4] : (f32x4){0.f, 0.f, 0.f, 0.f};
+      rn[j] = in && dres ? ((const f32x4*)dres)[o4 + c4] : (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  if (row0 + w < M) fetch(row0 + w);
   for (int r = w; r < LN_BWD_ROWS; r += 4) {
     const int row = row0 + r;
     if (row >= M) break;
     const int64_t o4 = (int64_t)row * d4;
     const float mu = mean[row], rs = rstd[row];
-    f32x4 xh[NCH], dyv[NCH];
+    f32x4 xh[NCH], dyv[NCH], rv[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; j++) {
+      xh[j] = xn[j];
+      dyv[j] = dyn[j];
+      rv[j] = rn[j];
+    }
+    if (r + 4 < LN_BWD_ROWS && row + 4 < M) fetch(row + 4);
     float sa = 0.f, sbb = 0.f;
 #pragma unroll
     for (int j = 0; j < NCH; j++) {
       const int c4 = j * 64 + lane;
       if (c4 < d4) {
-        const f32x4 xv = ((const f32x4*)x)[o4 + c4];
-        dyv[j] = ((const f32x4*)dy)[o4 + c4];
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-          xh[j][e] = (xv[e] - mu) * rs;
+          xh[j][e] = (xh[j][e] - mu) * rs;
           const float gh = dyv[j][e] * gg[j][e];
           sa += gh;
           sbb += gh * xh[j][e];
@@ -190,12 +209,11 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
     for (int j = 0; j < NCH; j++) {
       const int c4 = j * 64 + lane;
       if (c4 < d4) {
-        f32x4 rv = dres ? ((const f32x4*)dres)[o4 + c4] : (f32x4){0.f, 0.f, 0.f, 0.f};
         f32x4 v;
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-          v[e] = rs * (dyv[j][e] * gg[j][e] - a - xh[j][e] * bb) + rv[e];
-          pr[j][e] += rv[e];
+          v[e] = rs * (dyv[j][e] * gg[j][e] - a - xh[j][e] * bb) + rv[j][e];
+          pr[j][e] += rv[j][e];
         }
         ((f32x4*)dx)[o4 + c4] = v;
         if (dx_op) {
