@@ -140,6 +140,7 @@ def test_step_parity_bpe_12l_bf16():
     ("tiny", "fp32", 3, 11, 2),        # ragged: T below block_size, two micro-batches
     ("char_small", "bf16", 5, 37, 3),
     ("char_small", "fp32", 1, 1, 1),   # a single position
+    ("char_6l", "bf16", 2, 150, 2),    # head_dim 64, three 64-row tiles, the last one ragged
 ])
 def test_step_parity_ragged(name, prec, B, T, A):
     run_steps(name, prec, steps=2, B=B, T=T, A=A)
