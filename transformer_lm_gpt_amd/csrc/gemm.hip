@@ -215,13 +215,36 @@ __device__ inline void epi_store(const GemmArgs& p, int row, int col, float v, f
   }
 }
 
+// Global inputs of the vector epilogue (residual or GELU input) for sixteen columns,
+// loaded ahead of the tile's parked accumulators so the loads of the next 16-row
+// block are in flight while the current one is stored.
+template <int EPI>
+struct EpiPre {
+  static constexpr bool ON = EPI == EPI_BIAS_RESID || EPI == EPI_GELU_BWD;
+  f32x4 r[EPI == EPI_BIAS_RESID ? 4 : 1];
+  bf16x8 u[EPI == EPI_GELU_BWD ? 2 : 1];
+  __device__ inline void load(const GemmArgs& p, int row, int col0) {
+    if constexpr (EPI == EPI_BIAS_RESID) {
+      const float* src = p.resid + (int64_t)row * p.ldr + col0;
+#pragma unroll
+      for (int q = 0; q < 4; q++) r[q] = *(const f32x4*)(src + 4 * q);
+    } else if constexpr (EPI == EPI_GELU_BWD) {
+      const bf16* src = (const bf16*)p.aux + (int64_t)row * p.ldaux + col0;
+#pragma unroll
+      for (int q = 0; q < 2; q++) u[q] = *(const bf16x8*)(src + 8 * q);
+    }
+  }
+};
+
 // Sixteen consecutive output columns col0.. of one row: vector loads and stores
-// when the run is inside the matrix and aligned, element-wise otherwise.
+// when the run is inside the matrix and aligned, element-wise otherwise. pre, if
+// given, holds this run's residual or GELU input, loaded by EpiPre::load.
 // With EPI_GELU_BWD the final fp32 values are also added into sum16 (the bias
 // gradient's column sums); other epilogues leave it alone.
 template <int EPI>
 __device__ inline void epi_store16(const GemmArgs& p, int row, int col0, const float (&v)[16], bool vec,
-                                   float (&sum16)[16]) {
+                                   float (&sum16)[16], const EpiPre<EPI>* pre = nullptr,
+                                   const f32x4* bias16 = nullptr) {
   if (!vec) {
 #pragma unroll
     for (int c = 0; c < 16; c++)
@@ -239,7 +262,7 @@ __device__ inline void epi_store16(const GemmArgs& p, int row, int col0, const f
   if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU) {
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-      const f32x4 b = *(const f32x4*)(p.bias + col0 + 4 * q);
+      const f32x4 b = bias16 ? bias16[q] : *(const f32x4*)(p.bias + col0 + 4 * q);
 #pragma unroll
       for (int e = 0; e < 4; e++) x[4 * q + e] += b[e];
     }
@@ -256,7 +279,7 @@ __device__ inline void epi_store16(const GemmArgs& p, int row, int col0, const f
     const float* r = p.resid + (int64_t)row * p.ldr + col0;
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-      const f32x4 rv = *(const f32x4*)(r + 4 * q);
+      const f32x4 rv = pre ? pre->r[q] : *(const f32x4*)(r + 4 * q);
       f32x4 o;
 #pragma unroll
       for (int e = 0; e < 4; e++) o[e] = rv[e] + x[4 * q + e];
@@ -282,7 +305,7 @@ __device__ inline void epi_store16(const GemmArgs& p, int row, int col0, const f
     const bf16* u = (const bf16*)p.aux + (int64_t)row * p.ldaux + col0;
 #pragma unroll
     for (int q = 0; q < 2; q++) {
-      const bf16x8 uv = *(const bf16x8*)(u + 8 * q);
+      const bf16x8 uv = pre ? pre->u[q] : *(const bf16x8*)(u + 8 * q);
       bf16x8 o;
 #pragma unroll
       for (int e = 0; e < 8; e++) {
@@ -581,9 +604,42 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, 
   // quadrant, then a lane handles 16 contiguous columns of one row (TN/16 such
   // groups per row, so 64 lanes cover the block in one or more passes), so bias,
   // residual and GELU inputs are read and outputs written as vectors.
-  __syncthreads();   // every wave is done with the stage buffers
   constexpr int ELD = TN + 4;
   constexpr int CG = TN / 16, ITEMS = 16 * CG, PASSES = (ITEMS + 63) / 64;
+  // epilogue inputs of 16-row block i (item it = lane + 64*ps: row er, columns ec..)
+  // (the fp32 residual of two blocks does not fit beside the accumulators of two
+  // workgroups per CU: the 32-wide-slice residual kernel loads it in place)
+  constexpr bool PF = EpiPre<EPI>::ON && !(EPI == EPI_BIAS_RESID && KS == 32);
+  EpiPre<EPI> pre[PF ? 2 : 1][PASSES];
+  auto prefetch = [&](int i, EpiPre<EPI> (&dst)[PASSES]) {
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ps++) {
+      const int it = lane + 64 * ps;
+      if (ITEMS % 64 != 0 && it >= ITEMS) break;
+      const int row = m0 + wm * TM + i * 16 + it / CG, col0 = n0 + wn * TN + (it % CG) * 16;
+      if (row < p.M && col0 + 16 <= p.N && p.c_vec) dst[ps].load(p, row, col0);
+    }
+  };
+  if constexpr (PF)
+    if (!park) prefetch(0, pre[0]);
+  // the bias of an item's 16 columns is the same in every row block
+  constexpr bool PB = EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU;
+  f32x4 bias16[PB ? PASSES : 1][4];
+  if constexpr (PB) {
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ps++) {
+      const int it = lane + 64 * ps;
+      if (ITEMS % 64 != 0 && it >= ITEMS) break;
+      const int col0 = n0 + wn * TN + (it % CG) * 16;
+      if (!park && col0 + 16 <= p.N && p.c_vec)
+#pragma unroll
+        for (int q = 0; q < 4; q++) bias16[ps][q] = *(const f32x4*)(p.bias + col0 + 4 * q);
+    }
+  }
+  // Every wave is done with the stage buffers: their LDS reads have returned, and
+  // the last k-slices waited for all global->LDS loads. A plain s_barrier, so the
+  // epilogue loads just issued stay in flight.
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   float* scr = (float*)smem + wave * 16 * ELD;
   // fused bias gradient (GELU backward): this lane's column sums of its items
   constexpr bool CS = EPI == EPI_GELU_BWD;
@@ -595,6 +651,8 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, 
     for (int e = 0; e < 16; e++) cs[ps][e] = 0.f;
 #pragma unroll
   for (int i = 0; i < FM; i++) {
+    if constexpr (PF)
+      if (!park && i + 1 < FM) prefetch(i + 1, pre[(i + 1) & 1]);
 #pragma unroll
     for (int j = 0; j < FN; j++)
 #pragma unroll
@@ -619,7 +677,8 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, 
       } else {
         const int row = m0 + rt, col0 = n0 + wn * TN + ec;
         if (row < p.M && col0 < p.N)
-          epi_store16<EPI>(p, row, col0, v, (col0 + 16 <= p.N) && p.c_vec, cs[ps]);
+          epi_store16<EPI>(p, row, col0, v, (col0 + 16 <= p.N) && p.c_vec, cs[ps], PF ? &pre[i & 1][ps] : nullptr,
+                           PB ? bias16[ps] : nullptr);
       }
     }
   }
@@ -655,7 +714,7 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, 
 }
 
 template <int BM_, int BN_, int WM_, int WN_, int STAGES, bool AK, bool BK_, int EPI, int KS = 32>
-__global__ __launch_bounds__(64 * WM_ * WN_) void gemm_dma_kernel(GemmArgs p) {
+__global__ __launch_bounds__(64 * WM_ * WN_) __attribute__((amdgpu_waves_per_eu(KS == 32 && BM_ == 192 ? 2 : 1))) void gemm_dma_kernel(GemmArgs p) {
   constexpr int SB = (BM_ + BN_) * KS * 2;
   static_assert(STAGES * SB >= (WM_ * WN_ * 16 * (BN_ / WN_ + 4) + WM_ * BN_) * 4, "epilogue scratch fits the stages");
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * SB];
