@@ -93,6 +93,99 @@ __global__ __launch_bounds__(1024) void sort_keys_kernel(const int32_t* __restri
   for (int i = threadIdx.x; i < M; i += 1024) out[i] = sk[i];
 }
 
+// Stable LSD radix sort of the same keys by id, 4 bits per pass, for M <= RADIX_MAX
+// (two key buffers and the per-thread digit counters fit in LDS). The keys start
+// in position order and positions are unique, so the result equals the bitonic
+// sort's. Thread t owns the KPT consecutive keys from t*KPT. Each pass: every
+// thread counts its digits in its own LDS row of sixteen 16-bit counters; the
+// rows, read as eight 32-bit words holding two counters each, are scanned over
+// the wavefront (the counters never exceed M < 2^16, so the pairs add without
+// carries) and then over the wavefronts; each thread turns its row into the
+// destination of its first key of each digit and scatters its keys in order.
+constexpr int RADIX_MAX = 15360;
+constexpr int RADIX_THREADS = 1024;
+constexpr int RADIX_KPT = RADIX_MAX / RADIX_THREADS;
+
+__device__ inline uint32_t wave_incl_scan(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(RADIX_THREADS) void radix_sort_keys_kernel(const int32_t* __restrict__ tok, int M,
+                                                                        int shift, int passes,
+                                                                        uint32_t* __restrict__ out) {
+  __shared__ uint32_t buf[2][RADIX_MAX];
+  __shared__ uint32_t cnt[RADIX_THREADS][8];      // digit 2q in the low half of word q, 2q+1 in the high half
+  __shared__ uint32_t wtot[RADIX_THREADS / 64][8];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int kpt = (M + RADIX_THREADS - 1) / RADIX_THREADS;
+  const int k0 = t * kpt, k1 = min(M, k0 + kpt);
+  for (int i = t; i < M; i += RADIX_THREADS) buf[0][i] = (((uint32_t)tok[i]) << shift) | (uint32_t)i;
+  __syncthreads();
+  for (int p = 0; p < passes; p++) {
+    const uint32_t* src = buf[p & 1];
+    uint32_t* dst = buf[(p & 1) ^ 1];
+    const int dsh = shift + 4 * p;
+#pragma unroll
+    for (int q = 0; q < 8; q++) cnt[t][q] = 0u;
+    for (int j = k0; j < k1; j++) {
+      const uint32_t dg = (src[j] >> dsh) & 15u;
+      cnt[t][dg >> 1] += 1u << ((dg & 1u) << 4);
+    }
+    // exclusive prefix of the counters over the threads before t
+    uint32_t c[8], inc[8];
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+      c[q] = cnt[t][q];
+      inc[q] = wave_incl_scan(c[q]);
+    }
+    if (lane == 63)
+#pragma unroll
+      for (int q = 0; q < 8; q++) wtot[w][q] = inc[q];
+    __syncthreads();
+    uint32_t before[8], total[8];
+#pragma unroll
+    for (int q = 0; q < 8; q++) before[q] = total[q] = 0u;
+    for (int v = 0; v < RADIX_THREADS / 64; v++)
+#pragma unroll
+      for (int q = 0; q < 8; q++) {
+        const uint32_t x = wtot[v][q];
+        total[q] += x;
+        if (v < w) before[q] += x;
+      }
+    // destination of this thread's first key of each digit: the digit's base (an
+    // exclusive scan of the sixteen totals, in digit order) plus the keys of that
+    // digit in earlier threads
+    uint32_t base = 0u, first[8];
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+      const uint32_t mine = before[q] + inc[q] - c[q];
+      const uint32_t lo = base + (mine & 0xFFFFu);
+      base += total[q] & 0xFFFFu;
+      const uint32_t hi = base + (mine >> 16);
+      base += total[q] >> 16;
+      first[q] = lo | (hi << 16);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; q++) cnt[t][q] = first[q];
+    for (int j = k0; j < k1; j++) {
+      const uint32_t k = src[j];
+      const uint32_t dg = (k >> dsh) & 15u, sh = (dg & 1u) << 4;
+      const uint32_t word = cnt[t][dg >> 1];
+      dst[(word >> sh) & 0xFFFFu] = k;
+      cnt[t][dg >> 1] = word + (1u << sh);
+    }
+    __syncthreads();
+  }
+  const uint32_t* res = buf[passes & 1];
+  for (int i = t; i < M; i += RADIX_THREADS) out[i] = res[i];
+}
+
 // One workgroup per chunk of PIECE sorted positions: walks them in order and
 // writes the sum of every same-id run to piece_sums[first position of the run].
 __global__ __launch_bounds__(256) void piece_sum_kernel(const uint32_t* __restrict__ keys, const float* __restrict__ dx0,
@@ -145,6 +238,15 @@ hipError_t launch_embed_bwd(const float* dx0, const int32_t* tok, float* dwte, f
   const int n = 1 << ceil_log2(M < 16 ? 16 : M);   // sort size: at least one thread's 16 keys
   if (n > SORT_MAX || ((uint64_t)Vp << shift) > 0xFFFFFFFFull) return hipErrorInvalidValue;
   hipLaunchKernelGGL(wpe_grad_kernel, dim3((T * d + 255) / 256), dim3(256), 0, s, dx0, dwpe, beta_wpe, B, T, d);
+  if (M <= RADIX_MAX) {
+    const int passes = (ceil_log2(Vp < 2 ? 2 : Vp) + 3) / 4;
+    hipLaunchKernelGGL(radix_sort_keys_kernel, dim3(1), dim3(RADIX_THREADS), 0, s, tok, M, shift, passes, scr.keys);
+    hipLaunchKernelGGL(piece_sum_kernel, dim3((M + PIECE - 1) / PIECE), dim3(256), 0, s, (const uint32_t*)scr.keys,
+                       dx0, scr.piece_sums, M, shift, d);
+    hipLaunchKernelGGL(segment_add_kernel, dim3(M), dim3(256), 0, s, (const uint32_t*)scr.keys,
+                       (const float*)scr.piece_sums, dwte, M, shift, d, Vp);
+    return hipGetLastError();
+  }
   const size_t lds = (size_t)n * sizeof(uint32_t);
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)sort_keys_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,

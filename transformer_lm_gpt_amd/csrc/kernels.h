@@ -90,8 +90,8 @@ hipError_t launch_colsum_partial(const void* X, bool bf16_in, int64_t ldx, int M
                                  hipStream_t s);
 // Deferred column-sum reductions: job j adds the sum of its partial rows,
 // part[r, n] for r < nblk (fixed order), into dst: dst[n] = beta * dst[n] + sum.
-// All jobs of one backward run in a single launch of total_blk workgroups (16
-// columns each); first_blk numbers them, ascending.
+// All jobs of one backward run in a single launch of total_blk workgroups
+// (RED_COLS columns each); first_blk numbers them, ascending.
 struct RedJob {
   int64_t part;       // float offset of the [nblk, n] partials in the partial area
   int64_t dst;        // float offset of the destination in the gradient array
@@ -101,6 +101,7 @@ struct RedJob {
   int32_t pad;
 };
 constexpr int RED_KINDS = 3;
+constexpr int RED_COLS = 64;   // columns of one reduction job per workgroup
 struct RedRows {
   int32_t nblk[RED_KINDS];   // partial rows written by each kind of producer in this backward
 };

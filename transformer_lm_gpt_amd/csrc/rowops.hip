@@ -296,13 +296,13 @@ hipError_t launch_colsum_partial(const void* X, bool bf16_in, int64_t ldx, int M
   return hipGetLastError();
 }
 
-// 16 columns per workgroup, 16 row groups: each thread sums every 16th partial row
-// in order, then the 16 group sums are added in a fixed order. A workgroup finds
-// its job by binary search over first_blk.
+// RED_COLS (64) columns per workgroup, 16 row groups: each thread sums every 16th
+// partial row of its four columns in order, then the 16 group sums are added in a
+// fixed order. A workgroup finds its job by binary search over first_blk.
 __global__ __launch_bounds__(256) void reduce_jobs_kernel(const RedJob* __restrict__ jobs, int njobs,
                                                           const float* __restrict__ part, float* __restrict__ grads,
                                                           RedRows rows, float beta) {
-  __shared__ float red[16][17];
+  __shared__ f32x4 red[16][17];
   __shared__ int job;
   if (threadIdx.x == 0) {
     int lo = 0, hi = njobs - 1;
@@ -318,18 +318,39 @@ __global__ __launch_bounds__(256) void reduce_jobs_kernel(const RedJob* __restri
   const int nblk = rows.nblk[J.rows_kind];
   const float* pp = part + J.part;
   const int cl = threadIdx.x & 15, grp = threadIdx.x >> 4;
-  const int col = ((int)blockIdx.x - J.first_blk) * 16 + cl;
-  float s = 0.f;
-  if (col < J.n)
-    for (int r = grp; r < nblk; r += 16) s += pp[(int64_t)r * J.n + col];
+  const int col = ((int)blockIdx.x - J.first_blk) * RED_COLS + 4 * cl;
+  const int64_t n = J.n;
+  f32x4 s = (f32x4){0.f, 0.f, 0.f, 0.f};
+  if ((n & 3) == 0 && (J.part & 3) == 0) {
+    if (col < n) {
+      const float* q = pp + col;
+      int r = grp;
+      for (; r + 48 < nblk; r += 64) {   // four rows in flight, added in row order
+        const f32x4 a = *(const f32x4*)(q + r * n), b = *(const f32x4*)(q + (r + 16) * n);
+        const f32x4 c = *(const f32x4*)(q + (r + 32) * n), d = *(const f32x4*)(q + (r + 48) * n);
+        s += a;
+        s += b;
+        s += c;
+        s += d;
+      }
+      for (; r < nblk; r += 16) s += *(const f32x4*)(q + r * n);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; e++)
+      if (col + e < n)
+        for (int r = grp; r < nblk; r += 16) s[e] += pp[r * n + col + e];
+  }
   red[grp][cl] = s;
   __syncthreads();
-  if (grp == 0 && col < J.n) {
-    float t = red[0][cl];
+  if (grp == 0) {
+    f32x4 t = red[0][cl];
 #pragma unroll
     for (int q = 1; q < 16; q++) t += red[q][cl];
     float* dst = grads + J.dst;
-    dst[col] = (beta != 0.f ? beta * dst[col] : 0.f) + t;
+#pragma unroll
+    for (int e = 0; e < 4; e++)
+      if (col + e < n) dst[col + e] = (beta != 0.f ? beta * dst[col + e] : 0.f) + t[e];
   }
 }
 
@@ -490,18 +511,29 @@ hipError_t launch_xent(void* z, bool bf16_z, int64_t ldz, const int32_t* y, floa
   return hipGetLastError();
 }
 
-__global__ __launch_bounds__(256) void mean_kernel(const float* __restrict__ x, int M, float* out) {
-  __shared__ float red[4];
+__global__ __launch_bounds__(1024) void mean_kernel(const float* __restrict__ x, int M, float* out) {
+  __shared__ float red[16];
   float s = 0.f;
-  for (int i = threadIdx.x; i < M; i += 256) s += x[i];
+  if ((M & 3) == 0 && ((uintptr_t)x & 15) == 0) {
+    for (int i = threadIdx.x; i < (M >> 2); i += 1024) {
+      const f32x4 v = ((const f32x4*)x)[i];
+      s += (v[0] + v[1]) + (v[2] + v[3]);
+    }
+  } else {
+    for (int i = threadIdx.x; i < M; i += 1024) s += x[i];
+  }
   s = wave_sum(s);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
   __syncthreads();
-  if (threadIdx.x == 0) *out = (((red[0] + red[1]) + red[2]) + red[3]) / (float)M;
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+    for (int i = 0; i < 16; i++) t += red[i];
+    *out = t / (float)M;
+  }
 }
 
 hipError_t launch_mean(const float* row_loss, int M, float* out, hipStream_t s) {
-  hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(256), 0, s, row_loss, M, out);
+  hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(1024), 0, s, row_loss, M, out);
   return hipGetLastError();
 }
 

@@ -306,7 +306,7 @@ void plan(gpt_model* h) {
                         : kind == RED_QKV ? std::max(cs_blk, (size_t)h->Bmax * ((h->Tmax + 63) / 64))
                                           : cs_blk;
     red_floats += rows * t->numel();
-    h->rblocks += (int)((t->numel() + 15) / 16);
+    h->rblocks += (int)((t->numel() + RED_COLS - 1) / RED_COLS);
   };
   // kinds: RED_LN LayerNorm backward partials, RED_QKV and RED_FC the qkv and fc
   // bias column sums (from the GEMM epilogue or a column-sum pass)
