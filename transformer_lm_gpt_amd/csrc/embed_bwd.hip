@@ -26,13 +26,17 @@ static int ceil_log2(int x) {
 
 int embed_bwd_sort_size(int M) { return 1 << ceil_log2(M < 16 ? 16 : M); }
 
+// four elements of dwpe per thread (T*d is a multiple of 4: d is)
 __global__ void wpe_grad_kernel(const float* __restrict__ dx0, float* __restrict__ dwpe, float beta, int B, int T,
                                 int d) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;   // over T*d
+  const int i = 4 * (blockIdx.x * blockDim.x + threadIdx.x);   // over T*d
   if (i >= T * d) return;
-  float s = 0.f;
-  for (int b = 0; b < B; b++) s += dx0[(int64_t)b * T * d + i];
-  dwpe[i] = (beta != 0.f ? beta * dwpe[i] : 0.f) + s;
+  const int64_t td = (int64_t)T * d;
+  f32x4 s = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int b = 0; b < B; b++) s += *(const f32x4*)(dx0 + b * td + i);
+  f32x4* dst = (f32x4*)(dwpe + i);
+  *dst = beta != 0.f ? beta * *dst + s : s;
 }
 
 // Bitonic sort of n (a power of two, at least 16) keys (id << shift) | position in
@@ -188,46 +192,96 @@ __global__ __launch_bounds__(RADIX_THREADS) void radix_sort_keys_kernel(const in
 
 // One workgroup per chunk of PIECE sorted positions: walks them in order and
 // writes the sum of every same-id run to piece_sums[first position of the run].
+// The chunk's rows are all fetched before the in-order walk (four columns per
+// thread), so the walk waits on one round of loads, not on PIECE.
 __global__ __launch_bounds__(256) void piece_sum_kernel(const uint32_t* __restrict__ keys, const float* __restrict__ dx0,
                                                         float* __restrict__ piece_sums, int M, int shift, int d) {
+  __shared__ uint32_t ks[PIECE];
   const int i0 = blockIdx.x * PIECE;
-  const int i1 = min(M, i0 + PIECE);
+  const int n = min(M - i0, PIECE);
+  if ((int)threadIdx.x < n) ks[threadIdx.x] = keys[i0 + threadIdx.x];
+  __syncthreads();
   const uint32_t mask = (1u << shift) - 1u;
-  for (int c = threadIdx.x; c < d; c += 256) {
-    int start = i0;
-    uint32_t cur = keys[i0] >> shift;
-    float s = 0.f;
-    for (int i = i0; i < i1; i++) {
-      const uint32_t k = keys[i];
-      const uint32_t id = k >> shift;
-      if (id != cur) {
-        piece_sums[(int64_t)start * d + c] = s;
-        s = 0.f;
-        start = i;
-        cur = id;
+  for (int c = 4 * threadIdx.x; c < d; c += 4 * 256) {
+    f32x4 x[PIECE];
+#pragma unroll
+    for (int i = 0; i < PIECE; i++)
+      if (i < n) x[i] = *(const f32x4*)(dx0 + (int64_t)(ks[i] & mask) * d + c);
+    int start = 0;
+    uint32_t cur = ks[0] >> shift;
+    f32x4 sum = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < PIECE; i++) {
+      if (i < n) {
+        const uint32_t id = ks[i] >> shift;
+        if (id != cur) {
+          *(f32x4*)(piece_sums + (int64_t)(i0 + start) * d + c) = sum;
+          sum = (f32x4){0.f, 0.f, 0.f, 0.f};
+          start = i;
+          cur = id;
+        }
+        sum += x[i];
       }
-      s += dx0[(int64_t)(k & mask) * d + c];
     }
-    piece_sums[(int64_t)start * d + c] = s;
+    *(f32x4*)(piece_sums + (int64_t)(i0 + start) * d + c) = sum;
   }
 }
 
-// One workgroup per sorted position; those that start an id's run add the run's
-// chunk sums, in order, into dwte[id].
+// Every run of one id adds its chunk sums (at the run's first position and at each
+// chunk boundary inside the run), in order, into dwte[id]. A workgroup covers
+// SEG_POS sorted positions and takes the run starts among them one after another,
+// four columns per thread; the chunk sums of a long run (the most frequent ids)
+// are fetched four at a time.
+constexpr int SEG_POS = 16;
 __global__ __launch_bounds__(256) void segment_add_kernel(const uint32_t* __restrict__ keys,
                                                           const float* __restrict__ piece_sums,
                                                           float* __restrict__ dwte, int M, int shift, int d,
                                                           int Vp) {
-  const int i = blockIdx.x;
-  const uint32_t id = keys[i] >> shift;
-  if (i > 0 && (keys[i - 1] >> shift) == id) return;
-  if (id >= (uint32_t)Vp) return;   // ids outside the table are dropped, never written
-  // pieces of this run start at i and at every chunk boundary inside the run
-  for (int c = threadIdx.x; c < d; c += 256) {
-    float s = piece_sums[(int64_t)i * d + c];
-    for (int j = (i / PIECE + 1) * PIECE; j < M && (keys[j] >> shift) == id; j += PIECE)
-      s += piece_sums[(int64_t)j * d + c];
-    dwte[(int64_t)id * d + c] += s;
+  __shared__ uint32_t ids[SEG_POS + 1];   // ids[0]: the id before the first position (none: ~0)
+  __shared__ int lasts[SEG_POS];          // a run's last chunk boundary (its first position if none)
+  const int i0 = blockIdx.x * SEG_POS;
+  const int n = min(M - i0, SEG_POS);
+  if ((int)threadIdx.x <= n)
+    ids[threadIdx.x] = threadIdx.x == 0 ? (i0 > 0 ? keys[i0 - 1] >> shift : ~0u) : keys[i0 + threadIdx.x - 1] >> shift;
+  __syncthreads();
+  if ((int)threadIdx.x < n) {
+    const uint32_t id = ids[threadIdx.x + 1];
+    const int first = i0 + threadIdx.x;
+    int last = first;
+    if (id != ids[threadIdx.x]) {
+      // the run ends before the first sorted position e with another id (binary search)
+      int lo = first + 1, hi = M;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((keys[mid] >> shift) == id) lo = mid + 1;
+        else hi = mid;
+      }
+      last = max(first, (lo - 1) / PIECE * PIECE);
+    }
+    lasts[threadIdx.x] = last;
+  }
+  __syncthreads();
+  for (int i = 0; i < n; i++) {
+    const uint32_t id = ids[i + 1];
+    if (id == ids[i] || id >= (uint32_t)Vp) continue;   // not a run start, or outside the table (dropped)
+    const int first = i0 + i, last = lasts[i];
+    for (int c = 4 * threadIdx.x; c < d; c += 4 * 256) {
+      const float* ps = piece_sums + c;
+      f32x4 sum = *(const f32x4*)(ps + (int64_t)first * d);
+      int j = (first / PIECE + 1) * PIECE;
+      for (; j + 3 * PIECE <= last; j += 4 * PIECE) {
+        const f32x4 a = *(const f32x4*)(ps + (int64_t)j * d), b = *(const f32x4*)(ps + (int64_t)(j + PIECE) * d);
+        const f32x4 e = *(const f32x4*)(ps + (int64_t)(j + 2 * PIECE) * d);
+        const f32x4 f = *(const f32x4*)(ps + (int64_t)(j + 3 * PIECE) * d);
+        sum += a;
+        sum += b;
+        sum += e;
+        sum += f;
+      }
+      for (; j <= last; j += PIECE) sum += *(const f32x4*)(ps + (int64_t)j * d);
+      f32x4* dst = (f32x4*)(dwte + (int64_t)id * d + c);
+      *dst = *dst + sum;
+    }
   }
 }
 
@@ -237,13 +291,17 @@ hipError_t launch_embed_bwd(const float* dx0, const int32_t* tok, float* dwte, f
   const int shift = ceil_log2(M < 2 ? 2 : M);
   const int n = 1 << ceil_log2(M < 16 ? 16 : M);   // sort size: at least one thread's 16 keys
   if (n > SORT_MAX || ((uint64_t)Vp << shift) > 0xFFFFFFFFull) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(wpe_grad_kernel, dim3((T * d + 255) / 256), dim3(256), 0, s, dx0, dwpe, beta_wpe, B, T, d);
+  // four columns per access
+  if (d % 4 != 0 || (uintptr_t)dx0 % 16 != 0 || (uintptr_t)dwte % 16 != 0 || (uintptr_t)scr.piece_sums % 16 != 0)
+    return hipErrorInvalidValue;
+  if ((uintptr_t)dwpe % 16 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(wpe_grad_kernel, dim3((T * d / 4 + 255) / 256), dim3(256), 0, s, dx0, dwpe, beta_wpe, B, T, d);
   if (M <= RADIX_MAX) {
     const int passes = (ceil_log2(Vp < 2 ? 2 : Vp) + 3) / 4;
     hipLaunchKernelGGL(radix_sort_keys_kernel, dim3(1), dim3(RADIX_THREADS), 0, s, tok, M, shift, passes, scr.keys);
     hipLaunchKernelGGL(piece_sum_kernel, dim3((M + PIECE - 1) / PIECE), dim3(256), 0, s, (const uint32_t*)scr.keys,
                        dx0, scr.piece_sums, M, shift, d);
-    hipLaunchKernelGGL(segment_add_kernel, dim3(M), dim3(256), 0, s, (const uint32_t*)scr.keys,
+    hipLaunchKernelGGL(segment_add_kernel, dim3((M + SEG_POS - 1) / SEG_POS), dim3(256), 0, s, (const uint32_t*)scr.keys,
                        (const float*)scr.piece_sums, dwte, M, shift, d, Vp);
     return hipGetLastError();
   }
@@ -256,7 +314,7 @@ hipError_t launch_embed_bwd(const float* dx0, const int32_t* tok, float* dwte, f
   hipLaunchKernelGGL(sort_keys_kernel, dim3(1), dim3(1024), lds, s, tok, M, shift, n, scr.keys);
   hipLaunchKernelGGL(piece_sum_kernel, dim3((M + PIECE - 1) / PIECE), dim3(256), 0, s, (const uint32_t*)scr.keys,
                      dx0, scr.piece_sums, M, shift, d);
-  hipLaunchKernelGGL(segment_add_kernel, dim3(M), dim3(256), 0, s, (const uint32_t*)scr.keys,
+  hipLaunchKernelGGL(segment_add_kernel, dim3((M + SEG_POS - 1) / SEG_POS), dim3(256), 0, s, (const uint32_t*)scr.keys,
                      (const float*)scr.piece_sums, dwte, M, shift, d, Vp);
   return hipGetLastError();
 }
