@@ -581,6 +581,32 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16* __restr
   const int64_t r0 = (local / tiles_c) * 64, c0 = (local % tiles_c) * 64;
   const bf16* s0 = src + e.offset;
   bf16* d0 = dst + e.offset;
+  if (r0 + 64 <= e.rows && c0 + 64 <= e.cols && e.rows % 8 == 0 && e.cols % 8 == 0 &&
+      ((uintptr_t)s0 | (uintptr_t)d0) % 16 == 0) {
+    // whole tile, 16-byte rows: each thread moves two runs of 8 elements each way
+    __shared__ uint16_t u[64][66];
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+      const int i = threadIdx.x + 256 * k, rr = i >> 3, cu = (i & 7) * 8;
+      const uint4 v = *(const uint4*)(s0 + (r0 + rr) * e.cols + c0 + cu);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        u[rr][cu + 2 * q] = (uint16_t)(w[q] & 0xFFFFu);
+        u[rr][cu + 2 * q + 1] = (uint16_t)(w[q] >> 16);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+      const int i = threadIdx.x + 256 * k, cc = i >> 3, ru = (i & 7) * 8;
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; q++) w[q] = (uint32_t)u[ru + 2 * q][cc] | ((uint32_t)u[ru + 2 * q + 1][cc] << 16);
+      *(uint4*)(d0 + (c0 + cc) * e.rows + r0 + ru) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    return;
+  }
   for (int i = threadIdx.x; i < 64 * 64; i += 256) {
     const int rr = i >> 6, cc = i & 63;
     if (r0 + rr < e.rows && c0 + cc < e.cols) t[rr][cc] = s0[(r0 + rr) * e.cols + c0 + cc];
