@@ -758,10 +758,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_v2(const bf16* __restrict__
                                                         float* __restrict__ bias_part) {
   typedef ATile<HDP> AT;
   constexpr int KK = HDP / 32, CB = HDP / 16;
-  __shared__ __attribute__((aligned(16))) bf16 Qs[64 * HDP];
-  __shared__ __attribute__((aligned(16))) bf16 dOs[64 * HDP];
-  __shared__ __attribute__((aligned(16))) float ls[64];
-  __shared__ __attribute__((aligned(16))) float Ds[64];
+  __shared__ __attribute__((aligned(16))) bf16 Qs2[2][64 * HDP];   // double-buffered Q and dO tiles
+  __shared__ __attribute__((aligned(16))) bf16 dOs2[2][64 * HDP];
+  __shared__ __attribute__((aligned(16))) float ls2[2][64];
+  __shared__ __attribute__((aligned(16))) float Ds2[2][64];
   const int nb_t = (Tn + 63) / 64;
   const int kb = blockIdx.y;                          // key blocks near 0 see the most queries: first
   const int bh = blockIdx.x, b = bh / H, h = bh % H;
@@ -797,23 +797,39 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_v2(const bf16* __restrict__
   if (threadIdx.x < 64) stats(kb * 64 + threadIdx.x, lnext, dnext);
   const auto qsrc = range_rsrc(base, (int64_t)Tn * ld * 2);
   const auto dosrc = range_rsrc(dob, (int64_t)Tn * d * 2);
+  // query tile qt goes to buffer (qt - kb) & 1 during step qt - 1 (one barrier per step)
   TileRegs<HDP> qr, dr;
+  auto put = [&](int buf) {
+    qr.store(Qs2[buf]);
+    dr.store(dOs2[buf]);
+    if (threadIdx.x < 64) {
+      ls2[buf][threadIdx.x] = lnext;
+      Ds2[buf][threadIdx.x] = dnext;
+    }
+  };
   qr.load(qsrc, (int)ld, kb * 64, h * HDP);
   dr.load(dosrc, d, kb * 64, h * HDP);
+  put(0);
+  if (kb + 1 < nb_t) {
+    qr.load(qsrc, (int)ld, kb * 64 + 64, h * HDP);
+    dr.load(dosrc, d, kb * 64 + 64, h * HDP);
+    if (threadIdx.x < 64) stats(kb * 64 + 64 + threadIdx.x, lnext, dnext);
+  }
+  __syncthreads();
   for (int qt = kb; qt < nb_t; qt++) {
-    const int q0 = qt * 64;
-    __syncthreads();
-    qr.store(Qs);
-    dr.store(dOs);
-    if (threadIdx.x < 64) {
-      ls[threadIdx.x] = lnext;
-      Ds[threadIdx.x] = dnext;
-    }
-    __syncthreads();
+    const int q0 = qt * 64, cur = (qt - kb) & 1;
+    const bf16* Qs = Qs2[cur];
+    const bf16* dOs = dOs2[cur];
+    const float* ls = ls2[cur];
+    const float* Ds = Ds2[cur];
     if (qt + 1 < nb_t) {
-      qr.load(qsrc, (int)ld, q0 + 64, h * HDP);
-      dr.load(dosrc, d, q0 + 64, h * HDP);
-      if (threadIdx.x < 64) stats(q0 + 64 + threadIdx.x, lnext, dnext);
+      // buffer cur ^ 1 was last read in step qt - 1, which ended with a barrier
+      put(cur ^ 1);
+      if (qt + 2 < nb_t) {
+        qr.load(qsrc, (int)ld, q0 + 128, h * HDP);
+        dr.load(dosrc, d, q0 + 128, h * HDP);
+        if (threadIdx.x < 64) stats(q0 + 128 + threadIdx.x, lnext, dnext);
+      }
     }
     f32x4 p[4], ds[4];
 #pragma unroll
@@ -854,6 +870,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_v2(const bf16* __restrict__
         dkt[cb] = Mfma<bf16>::mma(qf, df, dkt[cb]);
       }
     }
+    __syncthreads();   // tile qt + 1 is visible; buffer cur is free
   }
   if (key < Tn) {
     bf16* row = dqkv + ((int64_t)b * Tn + key) * ld + h * HDP;
@@ -872,10 +889,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_v2(const bf16* __restrict__
   // keys past Tn see no query with P != 0, so their dk and dv are 0
   if (bias_part) {
     float* dst = bias_part + ((int64_t)b * nb_t + kb) * ld + h * HDP;
+    block_colsum<HDP>(dkt, scale, (float*)Qs2[0], dst + d);
     __syncthreads();
-    block_colsum<HDP>(dkt, scale, (float*)Qs, dst + d);
-    __syncthreads();
-    block_colsum<HDP>(dvt, 1.f, (float*)Qs, dst + 2 * d);
+    block_colsum<HDP>(dvt, 1.f, (float*)Qs2[0], dst + 2 * d);
   }
 }
 
