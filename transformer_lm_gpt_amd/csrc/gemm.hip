@@ -713,8 +713,12 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, 
   __syncthreads();
 }
 
+// The 192-wide, 32-wide-slice kernels run two workgroups per CU (their LDS ring allows
+// it); the register budget is held to that occupancy so the epilogue's prefetched
+// inputs cannot push them to one.
 template <int BM_, int BN_, int WM_, int WN_, int STAGES, bool AK, bool BK_, int EPI, int KS = 32>
-__global__ __launch_bounds__(64 * WM_ * WN_) __attribute__((amdgpu_waves_per_eu(KS == 32 && BM_ == 192 ? 2 : 1))) void gemm_dma_kernel(GemmArgs p) {
+__global__ __launch_bounds__(64 * WM_ * WN_) __attribute__((amdgpu_waves_per_eu(KS == 32 && BM_ == 192 ? 2 : 1)))
+void gemm_dma_kernel(GemmArgs p) {
   constexpr int SB = (BM_ + BN_) * KS * 2;
   static_assert(STAGES * SB >= (WM_ * WN_ * 16 * (BN_ / WN_ + 4) + WM_ * BN_) * 4, "epilogue scratch fits the stages");
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * SB];
