@@ -59,17 +59,17 @@ def cpu_baseline(cfg, params, batches, n_seq: int):
                       f"({dt:.1f} s); AdamW excluded"}
 
 
-def traffic_of(kernel: str):
+def traffic_of(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
-    (profiles/traffic.json), or None when its source has changed since the counters
-    were taken (the summary records a hash of the kernel's source file)."""
+    (profiles/traffic.json), or None when the counters were taken on another workload
+    or its source has changed since (the summary records a hash of the source file)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f).get(kernel)
-    if not rec:
+    if not rec or rec.get("workload") != workload:
         return None
     with open(os.path.join(ROOT, rec["source"]), "rb") as f:
         if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
@@ -175,14 +175,22 @@ def main(argv=None):
                     "avg_launch_ms": round(avg_ms, 4), "launches": kern_n,
                     "work_per_launch": f"2*M*Vp*d = {work:.4g} FLOP, M = {B * T}"}
         elif a.kernel == "gemm_wgrad" and a.precision == "bf16":
-            # one launch per micro-batch: every weight gradient, K = B*T tokens each
-            work = 2.0 * B * T * (Vp * d + L * 12 * d * d)               # FLOPs per launch
-            roof = {"kernel": "grouped weight-gradient GEMM (gemm_group_kernel 256x256 + group_fixup_kernel, "
-                              "bf16 operands, fp32 accumulate)", "bound": "mfma",
-                    "achieved": round(work / (avg_ms / 1e3) / 1e12, 2), "peak": peak / 1e12, "unit": "TFLOP/s",
-                    "frac": round(work / (avg_ms / 1e3) / peak, 4), "traffic": traffic_of("gemm_group_kernel"),
+            # every weight gradient of a micro-batch, K = B*T tokens each: one grouped
+            # launch per micro-batch where every tensor's shape allows it, else one per tensor
+            mbs = a.steps * A
+            work = 2.0 * B * T * (Vp * d + L * 12 * d * d)               # FLOPs per micro-batch
+            per_mb = kern_ms / mbs
+            grouped = kern_n == mbs
+            roof = {"kernel": ("grouped weight-gradient GEMM (gemm_group_kernel 256x256 + group_fixup_kernel, "
+                               "bf16 operands, fp32 accumulate)") if grouped else
+                              f"weight-gradient GEMMs, {kern_n / mbs:g} launches per micro-batch",
+                    "bound": "mfma",
+                    "achieved": round(work / (per_mb / 1e3) / 1e12, 2), "peak": peak / 1e12, "unit": "TFLOP/s",
+                    "frac": round(work / (per_mb / 1e3) / peak, 4),
+                    "traffic": traffic_of("gemm_group_kernel", cfg.name) if grouped else None,
                     "avg_launch_ms": round(avg_ms, 4), "launches": kern_n,
-                    "work_per_launch": f"2*M*(Vp*d + 12*L*d^2) = {work:.4g} FLOP, M = {B * T}"}
+                    ("work_per_launch" if grouped else "work_per_micro_batch"):
+                        f"2*M*(Vp*d + 12*L*d^2) = {work:.4g} FLOP, M = {B * T}"}
         else:
             roof = {"kernel": a.kernel, "avg_launch_ms": round(avg_ms, 4), "launches": kern_n}
 
@@ -190,8 +198,14 @@ def main(argv=None):
     if a.cpu_seqs > 0:
         cpu = cpu_baseline(cfg, params, host_batches[0], a.cpu_seqs)
 
+    metric = ("training tokens/sec and MFU, GPT-2 124M fwd+bwd+AdamW, T=1024, 1 MI355X" if cfg.name == "gpt2_124m"
+              else f"training tokens/sec and MFU, {cfg.name} fwd+bwd+AdamW, T={T}, 1 MI355X")
+    ids = {"zipf_batch": f"Zipf({cfg.zipf_s}) ids over {cfg.vocab_size}",
+           "zipf_stream": f"windows of a Zipf({cfg.zipf_s}) id stream over {cfg.vocab_size}",
+           "markov_stream": f"windows of an order-1 Markov id stream over {cfg.vocab_size}",
+           "uniform": f"uniform ids over {cfg.vocab_size}"}[cfg.data]
     out = {
-        "metric": "training tokens/sec and MFU, GPT-2 124M fwd+bwd+AdamW, T=1024, 1 MI355X",
+        "metric": metric,
         "value": round(tps, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -202,7 +216,7 @@ def main(argv=None):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": a.precision,
-        "data": "synthetic (seeded Zipf(1.07) ids over 50257, random-init weights N(0,0.02))",
+        "data": f"synthetic (seeded {ids}, random-init weights N(0,{cfg.init_std}))",
         "config": {"workload": f"{cfg.name}: L{cfg.n_layer} H{cfg.n_head} d{cfg.n_embd} V{cfg.vocab_size}"
                                f"(pad {cfg.padded_vocab}) B{B} T{T} accum{A}",
                    "global_batch": B * A, "seq_len": T, "tokens_per_step": tokens_per_step},

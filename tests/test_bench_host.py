@@ -1,0 +1,29 @@
+"""Host-side pieces of bench.py (no GPU): the FLOP count behind MFU and the guard on the
+recorded HBM traffic."""
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from transformer_lm_gpt_amd import workloads as W  # noqa: E402
+
+
+def test_flops_per_token_gpt2_124m():
+    # 6N + 12 L d T with N = parameters without wpe: 123,689,472 at Vp 50304, d 768, L 12
+    cfg = W.CONFIGS["gpt2_124m"]
+    d, L, T = cfg.n_embd, cfg.n_layer, cfg.block_size
+    assert bench.flops_per_token(cfg) == 6.0 * 123_689_472 + 12.0 * L * d * T
+    assert abs(bench.flops_per_token(cfg) / 1e6 - 855.4) < 0.05
+
+
+def test_traffic_only_for_its_workload_and_source():
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+        rec = json.load(f)["gemm_group_kernel"]
+    got = bench.traffic_of("gemm_group_kernel", rec["workload"])
+    assert got in (None, rec["bytes_per_launch"])       # None once the source changed
+    assert bench.traffic_of("gemm_group_kernel", "char_6l") is None
+    assert bench.traffic_of("no_such_kernel", rec["workload"]) is None
