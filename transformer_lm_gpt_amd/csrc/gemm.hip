@@ -552,12 +552,12 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, 
     if constexpr (KS == 64) {
       dma_kc64<BM_, NW>(A, p.lda, m0, p.M, k0, st, wave, lane);
       dma_kc64<BN_, NW>(B, p.ldb, n0, p.N, k0, st + AB, wave, lane);
-      return;
+    } else {
+      if constexpr (AK) dma_kc<BM_, NW>(A, p.lda, m0, p.M, k0, st, wave, lane);
+      else dma_mc<BM_, NW>(A, p.lda, m0, p.M, k0, st, wave, lane);
+      if constexpr (BK_) dma_kc<BN_, NW>(B, p.ldb, n0, p.N, k0, st + AB, wave, lane);
+      else dma_mc<BN_, NW>(B, p.ldb, n0, p.N, k0, st + AB, wave, lane);
     }
-    if constexpr (AK) dma_kc<BM_, NW>(A, p.lda, m0, p.M, k0, st, wave, lane);
-    else dma_mc<BM_, NW>(A, p.lda, m0, p.M, k0, st, wave, lane);
-    if constexpr (BK_) dma_kc<BN_, NW>(B, p.ldb, n0, p.N, k0, st + AB, wave, lane);
-    else dma_mc<BN_, NW>(B, p.ldb, n0, p.N, k0, st + AB, wave, lane);
   };
 
 #pragma unroll
@@ -1104,10 +1104,12 @@ hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
   // workgroup when K <= 3072, where parking partial tiles costs more than it saves.
   if (use_k192(d, bf16_operands)) {
     // one tile per CU or fewer: 64-wide k-slices (half the memory requests per byte;
-    // two stages fill 96 KB of LDS, so one workgroup per CU). Otherwise 32-wide slices
-    // in three stages, which leave room for two workgroups per CU.
+    // two stages fill 96 KB of LDS, so one workgroup per CU) and 8 wavefronts of 96 x 48,
+    // which hide more latency than 4 of 96 x 96 when the CU holds no second workgroup
+    // (2-7 % on the step's N = 768 shapes). Otherwise 32-wide slices in three stages,
+    // which leave room for two workgroups per CU.
     const int t192 = ((d.M + 191) / 192) * ((d.N + 191) / 192);
-    if (t192 <= num_cus() && d.K % 64 == 0) return dma_epi<192, 192, 2, 2, 2, true, true, 64>(a, d.epi, 1, s);
+    if (t192 <= num_cus() && d.K % 64 == 0) return dma_epi<192, 192, 2, 4, 2, true, true, 64>(a, d.epi, 1, s);
     return dma_epi<192, 192, 2, 2, 3, true, true>(a, d.epi, 1, s);
   }
   a.colsum = nullptr;
