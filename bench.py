@@ -181,7 +181,7 @@ def main(argv=None):
             work = 2.0 * B * T * (Vp * d + L * 12 * d * d)               # FLOPs per micro-batch
             per_mb = kern_ms / mbs
             grouped = kern_n == mbs
-            roof = {"kernel": ("grouped weight-gradient GEMM (gemm_group_kernel 256x256 + group_fixup_kernel, "
+            roof = {"kernel": ("grouped weight-gradient GEMM (gemm_group_kernel 256x256, 16 wavefronts, + group_fixup_kernel, "
                                "bf16 operands, fp32 accumulate)") if grouped else
                               f"weight-gradient GEMMs, {kern_n / mbs:g} launches per micro-batch",
                     "bound": "mfma",
