@@ -130,7 +130,9 @@ hipError_t launch_attn_bwd(const void* qkv, const void* o, const void* dout, con
 int attn_bwd_colsum_rows(bool bf16_ops, int B, int T, int hd);
 
 // Embedding backward: dwpe[t] = beta * dwpe[t] + sum_b dx0[b, t]; dwte[tok] += rows of dx0,
-// summed deterministically (stable sort by id, fixed-order segment sums).
+// summed deterministically (stable sort by id, fixed-order segment sums). Works on four
+// columns at a time: d must be a multiple of 4 and dx0, dwte, dwpe and piece_sums
+// 16-byte aligned, else hipErrorInvalidValue before any launch.
 struct EmbedBwdScratch {
   uint32_t* keys;       // [sort_n]
   float* piece_sums;    // [M, d]
