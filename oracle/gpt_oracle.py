@@ -26,6 +26,14 @@ What it computes, and the passage each part follows (the nanoGPT pages):
     2-D tensors (run log, section 2.1: wd 0.1, betas 0.9/0.95; microGPT page:
     betas 0.85/0.99, eps 1e-8).
 
+  * dropout (the nanoGPT run log, section 2.2; the microGPT page's parameter
+    list): inverted dropout on the embedding output, on the attention
+    probabilities and on the output of each residual branch before its add, the
+    kept values scaled by 1 / (1 - p). The masks come from the counter-based
+    generator Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random
+    numbers: as easy as 1, 2, 3", SC 2011), keyed by a 64-bit seed; see
+    ``dropout_keep`` for which counter names which element.
+
 Readings where the pages are silent: LayerNorm eps 1e-5 with the biased
 variance; attention scale 1/sqrt(head_dim); the softmax runs over all padded
 vocabulary columns; the clip coefficient is min(1, clip / (norm + 1e-6)) and
@@ -87,6 +95,95 @@ def decays(name: str, shape) -> bool:
     return len(shape) == 2
 
 
+# --------------------------------------------------------------------------- dropout masks
+
+_PHILOX_M = (0xD2511F53, 0xCD9E8D57)    # round multipliers of Philox4x32
+_PHILOX_W = (0x9E3779B9, 0xBB67AE85)    # key increments (golden ratio, sqrt(3) - 1)
+_U32 = np.uint64(0xFFFFFFFF)
+
+
+def philox4x32(counter, key, rounds: int = 10):
+    """Philox4x32-R of Salmon et al. (SC 2011): four 32-bit counter words and a
+    two-word key to four 32-bit outputs.
+
+    counter: uint array [..., 4]; key: two ints. Each round takes the 32x32->64
+    products of counter words 0 and 2 with the two multipliers, and forms the new
+    counter (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)); the
+    key advances by the two Weyl increments between rounds. Returns uint64 [..., 4]
+    holding 32-bit values.
+    """
+    c = np.asarray(counter, dtype=np.uint64)
+    c0, c1, c2, c3 = (c[..., i] for i in range(4))
+    k0, k1 = np.uint64(int(key[0]) & 0xFFFFFFFF), np.uint64(int(key[1]) & 0xFFFFFFFF)
+    for r in range(rounds):
+        if r:
+            k0 = (k0 + np.uint64(_PHILOX_W[0])) & _U32
+            k1 = (k1 + np.uint64(_PHILOX_W[1])) & _U32
+        p0 = np.uint64(_PHILOX_M[0]) * c0       # < 2^64: exact in uint64
+        p1 = np.uint64(_PHILOX_M[1]) * c2
+        c0, c1, c2, c3 = (p1 >> np.uint64(32)) ^ c1 ^ k0, p1 & _U32, (p0 >> np.uint64(32)) ^ c3 ^ k1, p0 & _U32
+    return np.stack([c0, c1, c2, c3], axis=-1)
+
+
+class Dropout:
+    """Dropout rate p, the generator's 64-bit seed and the forward counter.
+
+    An element is dropped when its 32-bit Philox word is below
+    thr = floor(p * 2^32), so it is kept with probability 1 - thr / 2^32, and
+    kept values are multiplied by scale = 1 / (1 - p) rounded to float32.
+    ``call`` numbers the forward passes: each micro-batch forward uses the
+    current value and then advances it (``next_call``).
+    """
+
+    def __init__(self, p: float, seed: int, call: int = 0):
+        if not 0.0 <= p < 1.0:
+            raise ValueError("dropout must be in [0, 1)")
+        self.p = float(np.float32(p))
+        self.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+        self.call = int(call) & 0xFFFFFFFF
+        self.thr = int(math.floor(self.p * 4294967296.0))
+        self.scale = float(np.float32(1.0 / (1.0 - self.p)))
+
+    def next_call(self) -> int:
+        c = self.call
+        self.call = (self.call + 1) & 0xFFFFFFFF
+        return c
+
+
+# Sites: 0 is the embedding output; layer l owns 3l+1 (attention probabilities),
+# 3l+2 (attention branch output) and 3l+3 (MLP branch output).
+def site_embed() -> int: return 0
+def site_attn_prob(l: int) -> int: return 3 * l + 1
+def site_attn_out(l: int) -> int: return 3 * l + 2
+def site_mlp_out(l: int) -> int: return 3 * l + 3
+
+
+def dropout_keep(drop: Dropout, call: int, site: int, rows, ncols: int) -> np.ndarray:
+    """Keep mask [len(rows), ncols] of one site for one forward.
+
+    Element (row, col) takes word col mod 4 of Philox4x32-10 at counter
+    (col div 4, row, site, call) under the key (seed low word, seed high word).
+    Rows and columns are those of the site's tensor: token rows b*T + t and
+    channel columns for the embedding and branch outputs, and rows
+    (b*H + h)*T + i by key columns j for the attention probabilities, with T the
+    micro-batch's sequence length.
+    """
+    rows = np.asarray(rows, dtype=np.uint64)
+    groups = np.arange((ncols + 3) // 4, dtype=np.uint64)
+    ctr = np.empty((len(rows), len(groups), 4), dtype=np.uint64)
+    ctr[..., 0] = groups[None, :]
+    ctr[..., 1] = rows[:, None]
+    ctr[..., 2] = site
+    ctr[..., 3] = call
+    words = philox4x32(ctr, (drop.seed & 0xFFFFFFFF, drop.seed >> 32)).reshape(len(rows), -1)[:, :ncols]
+    return words >= np.uint64(drop.thr)
+
+
+def _zmask(drop, call, site, rows, ncols, dtype):
+    """Keep mask times the scale, as a multiplier in ``dtype``."""
+    return dropout_keep(drop, call, site, rows, ncols).astype(dtype) * dtype(drop.scale)
+
+
 # --------------------------------------------------------------------------- pieces
 
 def layernorm_fwd(x, g, b):
@@ -126,21 +223,28 @@ def softmax_rows(s):
     return e / e.sum(axis=-1, keepdims=True)
 
 
-def attention_fwd(q, k, v):
-    """Causal attention for one sequence. q, k, v: [H, T, hd] -> O [H, T, hd], P."""
+def attention_fwd(q, k, v, z=None):
+    """Causal attention for one sequence. q, k, v: [H, T, hd] -> O [H, T, hd], P.
+
+    z, if given, is the dropout multiplier [H, T, T] applied to the
+    probabilities after the softmax: O = (P * z) V. P is returned undropped.
+    """
     T, hd = q.shape[1], q.shape[2]
     s = np.matmul(q, np.swapaxes(k, 1, 2)) / math.sqrt(hd)
     future = np.triu(np.ones((T, T), dtype=bool), 1)     # key j > query i
     s = np.where(future[None], -np.inf, s)
     p = softmax_rows(s)
-    return np.matmul(p, v), p
+    return np.matmul(p if z is None else p * z, v), p
 
 
-def attention_bwd(dout, q, k, v, p):
+def attention_bwd(dout, q, k, v, p, z=None):
     hd = q.shape[2]
     sc = 1.0 / math.sqrt(hd)
-    dv = np.matmul(np.swapaxes(p, 1, 2), dout)
-    dp = np.matmul(dout, np.swapaxes(v, 1, 2))
+    pd = p if z is None else p * z
+    dv = np.matmul(np.swapaxes(pd, 1, 2), dout)
+    dp = np.matmul(dout, np.swapaxes(v, 1, 2))          # gradient of P * z
+    if z is not None:
+        dp = dp * z                                      # gradient of P
     ds = p * (dp - (p * dp).sum(axis=-1, keepdims=True))
     dq = np.matmul(ds, k) * sc
     dk = np.matmul(np.swapaxes(ds, 1, 2), q) * sc
@@ -163,35 +267,56 @@ def _as(params: Dict[str, np.ndarray], dtype) -> Dict[str, np.ndarray]:
     return {k: np.asarray(v, dtype=dtype) for k, v in params.items()}
 
 
-def forward_sequence(P, tok, cfg):
-    """Forward pass of one sequence (tok: int [T]). Returns logits [T, Vp] and a cache."""
+def forward_sequence(P, tok, cfg, drop=None, b=0):
+    """Forward pass of one sequence (tok: int [T]). Returns logits [T, Vp] and a cache.
+
+    drop: None, or (Dropout, call) to apply dropout as sequence b of its
+    micro-batch (which fixes the mask rows).
+    """
     T = len(tok)
     d, H, L = cfg.n_embd, cfg.n_head, cfg.n_layer
     hd = d // H
+    dt = P["wte"].dtype.type
+    if drop is not None:
+        dr, call = drop
+        tok_rows = b * T + np.arange(T)
+        zm = lambda site: _zmask(dr, call, site, tok_rows, d, dt)
+        head_rows = lambda: ((b * H + np.arange(H))[:, None] * T + np.arange(T)[None, :]).reshape(-1)
     x = P["wte"][tok] + P["wpe"][:T]
+    ze = None
+    if drop is not None:
+        ze = zm(site_embed())
+        x = x * ze
     layers = []
     for l in range(L):
         p = f"h{l}."
         a, c1 = layernorm_fwd(x, P[p + "ln1.g"], P[p + "ln1.b"])
         qkv = a @ P[p + "attn.w"].T + P[p + "attn.b"]
         q, k, v = (qkv[:, i * d:(i + 1) * d].reshape(T, H, hd).transpose(1, 0, 2) for i in range(3))
-        o, pr = attention_fwd(q, k, v)
+        zp = za = zo = None
+        if drop is not None:
+            zp = _zmask(dr, call, site_attn_prob(l), head_rows(), T, dt).reshape(H, T, T)
+            za = zm(site_attn_out(l))
+            zo = zm(site_mlp_out(l))
+        o, pr = attention_fwd(q, k, v, zp)
         o2 = o.transpose(1, 0, 2).reshape(T, d)
-        x1 = x + o2 @ P[p + "proj.w"].T + P[p + "proj.b"]
+        y1 = o2 @ P[p + "proj.w"].T + P[p + "proj.b"]
+        x1 = x + (y1 if za is None else y1 * za)
         b2, c2 = layernorm_fwd(x1, P[p + "ln2.g"], P[p + "ln2.b"])
         u = b2 @ P[p + "fc.w"].T + P[p + "fc.b"]
         h = gelu(u)
-        x2 = x1 + h @ P[p + "fcproj.w"].T + P[p + "fcproj.b"]
-        layers.append((a, c1, q, k, v, pr, o2, b2, c2, u, h))
+        y2 = h @ P[p + "fcproj.w"].T + P[p + "fcproj.b"]
+        x2 = x1 + (y2 if zo is None else y2 * zo)
+        layers.append((a, c1, q, k, v, pr, o2, b2, c2, u, h, zp, za, zo))
         x = x2
     xf, cf = layernorm_fwd(x, P["lnf.g"], P["lnf.b"])
     z = xf @ P["wte"].T
-    return z, (tok, layers, xf, cf)
+    return z, (tok, layers, xf, cf, ze)
 
 
 def backward_sequence(P, cache, dz, cfg, G):
     """Adds the gradients of one sequence (given dL/dlogits) into G."""
-    tok, layers, xf, cf = cache
+    tok, layers, xf, cf, ze = cache
     T = len(tok)
     d, H, L = cfg.n_embd, cfg.n_head, cfg.n_layer
     hd = d // H
@@ -202,11 +327,12 @@ def backward_sequence(P, cache, dz, cfg, G):
     G["lnf.b"] += db
     for l in reversed(range(L)):
         p = f"h{l}."
-        a, c1, q, k, v, pr, o2, b2, c2, u, h = layers[l]
-        # MLP: x2 = x1 + gelu(LN2(x1) Wfc^T + bfc) Wp^T + bp
-        G[p + "fcproj.w"] += dx.T @ h
-        G[p + "fcproj.b"] += dx.sum(axis=0)
-        du = (dx @ P[p + "fcproj.w"]) * gelu_grad(u)
+        a, c1, q, k, v, pr, o2, b2, c2, u, h, zp, za, zo = layers[l]
+        # MLP: x2 = x1 + drop(gelu(LN2(x1) Wfc^T + bfc) Wp^T + bp)
+        dy2 = dx if zo is None else dx * zo
+        G[p + "fcproj.w"] += dy2.T @ h
+        G[p + "fcproj.b"] += dy2.sum(axis=0)
+        du = (dy2 @ P[p + "fcproj.w"]) * gelu_grad(u)
         G[p + "fc.w"] += du.T @ b2
         G[p + "fc.b"] += du.sum(axis=0)
         db2 = du @ P[p + "fc.w"]
@@ -214,12 +340,13 @@ def backward_sequence(P, cache, dz, cfg, G):
         G[p + "ln2.g"] += dg
         G[p + "ln2.b"] += dbb
         dx1 = dx + dln
-        # attention: x1 = x + attn(LN1(x)) Wo^T + bo
-        G[p + "proj.w"] += dx1.T @ o2
-        G[p + "proj.b"] += dx1.sum(axis=0)
-        do2 = dx1 @ P[p + "proj.w"]
+        # attention: x1 = x + drop(attn(LN1(x)) Wo^T + bo)
+        dy1 = dx1 if za is None else dx1 * za
+        G[p + "proj.w"] += dy1.T @ o2
+        G[p + "proj.b"] += dy1.sum(axis=0)
+        do2 = dy1 @ P[p + "proj.w"]
         do = do2.reshape(T, H, hd).transpose(1, 0, 2)
-        dq, dk, dv = attention_bwd(do, q, k, v, pr)
+        dq, dk, dv = attention_bwd(do, q, k, v, pr, zp)
         dqkv = np.concatenate([t.transpose(1, 0, 2).reshape(T, d) for t in (dq, dk, dv)], axis=1)
         G[p + "attn.w"] += dqkv.T @ a
         G[p + "attn.b"] += dqkv.sum(axis=0)
@@ -228,7 +355,9 @@ def backward_sequence(P, cache, dz, cfg, G):
         G[p + "ln1.g"] += dg
         G[p + "ln1.b"] += dbb
         dx = dx1 + dln
-    # x0 = wte[tok] + wpe[:T]; repeated ids add up.
+    # x0 = drop(wte[tok] + wpe[:T]); repeated ids add up.
+    if ze is not None:
+        dx = dx * ze
     np.add.at(G["wte"], tok, dx)
     G["wpe"][:T] += dx
 
@@ -239,7 +368,7 @@ def logits(params, tokens, cfg, dtype=np.float64):
 
 
 def microbatch(params, tokens, targets, cfg, grad_scale=None, dtype=np.float64,
-               grads=None, rows=None):
+               grads=None, rows=None, dropout=None, call=None):
     """Loss of one micro-batch and (optionally) its gradient.
 
     tokens, targets: int [B, T]. The loss is the mean over all B*T positions.
@@ -248,6 +377,8 @@ def microbatch(params, tokens, targets, cfg, grad_scale=None, dtype=np.float64,
     grad_scale = 1 / (B * T * A) for A accumulated micro-batches.
     ``rows`` optionally limits the work to a subset of sequences (their
     per-position losses are still returned in place, others are NaN).
+    ``dropout`` (a Dropout) applies dropout with forward counter ``call``
+    (default: the next value of the Dropout's counter).
     """
     P = _as(params, dtype)
     tokens = np.asarray(tokens)
@@ -256,8 +387,13 @@ def microbatch(params, tokens, targets, cfg, grad_scale=None, dtype=np.float64,
     if grad_scale is not None and grads is None:
         grads = {k: np.zeros_like(v) for k, v in P.items()}
     row_loss = np.full((B, T), np.nan, dtype=dtype)
+    drop = None
+    if dropout is not None:
+        c = dropout.next_call() if call is None else call    # advances for p = 0 too
+        if dropout.p > 0.0:
+            drop = (dropout, c)
     for b in (range(B) if rows is None else rows):
-        z, cache = forward_sequence(P, tokens[b], cfg)
+        z, cache = forward_sequence(P, tokens[b], cfg, drop, b)
         ell, sm = xent_rows(z, targets[b])
         row_loss[b] = ell
         if grad_scale is not None:
@@ -268,15 +404,18 @@ def microbatch(params, tokens, targets, cfg, grad_scale=None, dtype=np.float64,
     return row_loss, grads
 
 
-def accumulate_grads(params, batches, cfg, dtype=np.float64):
-    """Mean loss over A micro-batches and the gradient of that mean."""
+def accumulate_grads(params, batches, cfg, dtype=np.float64, dropout=None):
+    """Mean loss over A micro-batches and the gradient of that mean.
+
+    With a Dropout, micro-batch i takes the Dropout's next forward counter.
+    """
     A = len(batches)
     grads = None
     losses = []
     for tok, tgt in batches:
         B, T = tok.shape
         rl, grads = microbatch(params, tok, tgt, cfg, grad_scale=1.0 / (B * T * A),
-                               dtype=dtype, grads=grads)
+                               dtype=dtype, grads=grads, dropout=dropout)
         losses.append(float(rl.mean()))
     return losses, grads
 
@@ -313,8 +452,9 @@ def adamw_update(params, grads, m, v, t, lr, beta1, beta2, eps, wd, coef, decay_
 class Trainer:
     """Full optimizer steps on the oracle: accumulate, clip, AdamW."""
 
-    def __init__(self, params, cfg, dtype=np.float64):
+    def __init__(self, params, cfg, dtype=np.float64, dropout=None):
         self.cfg = cfg
+        self.dropout = dropout
         self.dtype = dtype
         self.p = _as(params, dtype)
         self.m = {k: np.zeros_like(v) for k, v in self.p.items()}
@@ -330,7 +470,7 @@ class Trainer:
         eps = c.eps if eps is None else eps
         wd = c.weight_decay if wd is None else wd
         clip = c.grad_clip if clip is None else clip
-        losses, grads = accumulate_grads(self.p, batches, c, self.dtype)
+        losses, grads = accumulate_grads(self.p, batches, c, self.dtype, self.dropout)
         norm = grad_norm(grads)
         coef = clip_coef(norm, clip)
         self.t += 1

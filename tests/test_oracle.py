@@ -240,13 +240,14 @@ def test_layernorm_invariants():
     np.testing.assert_allclose(db, dy.sum(0), rtol=1e-14)
 
 
-def _fd_check(c, params, tok, tgt, n_random=20, seed=5):
+def _fd_check(c, params, tok, tgt, n_random=20, seed=5, dropout=None):
     P = {k: v.astype(np.float64) for k, v in params.items()}
     B, T = tok.shape
-    _, G = O.microbatch(P, tok, tgt, c, grad_scale=1.0 / (B * T))
+    call = 7            # one fixed forward counter: every evaluation sees the same masks
+    _, G = O.microbatch(P, tok, tgt, c, grad_scale=1.0 / (B * T), dropout=dropout, call=call)
 
     def loss(Pp):
-        return O.microbatch(Pp, tok, tgt, c)[0].mean()
+        return O.microbatch(Pp, tok, tgt, c, dropout=dropout, call=call)[0].mean()
 
     rng = np.random.default_rng(seed)
     h = 1e-5
@@ -286,6 +287,105 @@ def test_finite_difference_shrunk_char():
     params = W.init_params(c, wrng, perturb=True)
     tok, tgt = W.make_batch(c, drng)
     assert _fd_check(c, params, tok, tgt, n_random=8) > 500
+
+
+# --------------------------------------------------------------------------- dropout
+
+def test_philox_known_answers():
+    """Philox4x32-10 against the generator's published known-answer vectors."""
+    for v in _gold("philox4x32_10_kat.json")["vectors"]:
+        ctr = np.array([int(x, 16) for x in v["counter"]], dtype=np.uint64)
+        key = [int(x, 16) for x in v["key"]]
+        out = O.philox4x32(ctr, key)
+        assert [int(x) for x in out] == [int(x, 16) for x in v["out"]]
+
+
+def test_dropout_threshold_and_scale():
+    d = O.Dropout(0.25, 1)
+    assert d.thr == 1 << 30
+    assert d.scale == float(np.float32(4.0 / 3.0))
+    z = O.Dropout(0.0, 1)
+    assert z.thr == 0 and z.scale == 1.0
+    with pytest.raises(ValueError):
+        O.Dropout(1.0, 1)
+
+
+def test_dropout_keep_rate_unbiased_and_independent():
+    """Kept fraction 1 - p, E[keep * scale] = 1 (inverted dropout), and masks of
+    different sites, calls and seeds are independent (joint keep rate (1-p)^2)."""
+    p = 0.3
+    d = O.Dropout(p, 0x0123456789ABCDEF)
+    rows = np.arange(1024)
+    a = O.dropout_keep(d, 5, 2, rows, 1024)
+    n = a.size
+    sd = math.sqrt(p * (1 - p) / n)
+    assert abs(a.mean() - (1 - p)) < 5 * sd
+    z = a * d.scale
+    assert abs(z.mean() - 1.0) < 5 * d.scale * sd
+    for other in (O.dropout_keep(d, 5, 3, rows, 1024),                 # another site
+                  O.dropout_keep(d, 6, 2, rows, 1024),                 # another forward
+                  O.dropout_keep(O.Dropout(p, 0x0123456789ABCDEE), 5, 2, rows, 1024),   # another seed
+                  O.dropout_keep(d, 5, 2, rows + 1024, 1024)):         # other rows
+        both = (a & other).mean()
+        assert abs(both - (1 - p) ** 2) < 5 * math.sqrt((1 - p) ** 2 * (1 - (1 - p) ** 2) / n)
+
+
+def test_dropout_counter_layout_brute_force():
+    """Element (row, col) takes word col % 4 of the block at counter (col // 4, row, site, call)."""
+    d = O.Dropout(0.5, (7 << 32) | 9)
+    rows = [0, 3, 70000]
+    m = O.dropout_keep(d, 11, 4, rows, 10)
+    for i, r in enumerate(rows):
+        for c in range(10):
+            w = O.philox4x32(np.array([c // 4, r, 4, 11], dtype=np.uint64), (9, 7))[c % 4]
+            assert m[i, c] == (int(w) >= d.thr)
+
+
+def test_dropout_zero_rate_is_bitwise_identity():
+    c, params, tok, tgt = _setup("tiny", perturb=True)
+    B, T = tok.shape
+    l0, g0 = O.microbatch(params, tok, tgt, c, grad_scale=1.0 / (B * T))
+    l1, g1 = O.microbatch(params, tok, tgt, c, grad_scale=1.0 / (B * T), dropout=O.Dropout(0.0, 3))
+    assert np.array_equal(l0, l1)
+    for k in g0:
+        assert np.array_equal(g0[k], g1[k])
+
+
+def test_attention_dropout_uniform_queries():
+    """q = 0 makes every row of P uniform over the visible keys, so the dropped
+    output is O_i = sum_{j<=i} z_ij v_j / (i + 1) with z = keep * scale."""
+    H, T, hd = 2, 6, 4
+    rng = np.random.default_rng(3)
+    k = rng.normal(size=(H, T, hd))
+    v = rng.normal(size=(H, T, hd))
+    d = O.Dropout(0.4, 99)
+    keep = O.dropout_keep(d, 0, 1, np.arange(H * T), T).reshape(H, T, T)
+    z = keep * d.scale
+    out, p = O.attention_fwd(np.zeros((H, T, hd)), k, v, z)
+    for h in range(H):
+        for i in range(T):
+            expect = sum(z[h, i, j] * v[h, j] for j in range(i + 1)) / (i + 1)
+            np.testing.assert_allclose(out[h, i], expect, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(p.sum(-1), 1.0, rtol=1e-14)     # P itself is returned undropped
+
+
+def test_finite_difference_tiny_with_dropout():
+    """With the masks fixed (one forward counter), dropout is linear in each
+    masked value, so central differences pin every mask in the backward."""
+    c, params, tok, tgt = _setup("tiny", perturb=True)
+    assert _fd_check(c, params, tok, tgt, dropout=O.Dropout(0.3, 0xDEADBEEF12345)) > 200
+
+
+def test_dropout_changes_loss_and_advances_counter():
+    c, params, tok, tgt = _setup("tiny", perturb=True)
+    d = O.Dropout(0.2, 5, call=3)
+    l1, _ = O.microbatch(params, tok, tgt, c, dropout=d)
+    assert d.call == 4
+    l2, _ = O.microbatch(params, tok, tgt, c, dropout=d)
+    l0, _ = O.microbatch(params, tok, tgt, c)
+    assert not np.array_equal(l1, l2) and not np.array_equal(l1, l0)
+    l1b, _ = O.microbatch(params, tok, tgt, c, dropout=d, call=3)
+    assert np.array_equal(l1, l1b)
 
 
 def test_grad_accumulation_equals_big_batch():
