@@ -41,7 +41,7 @@ def flops_per_token(cfg) -> float:
     return 6.0 * N + 12.0 * L * d * T
 
 
-def cpu_baseline(cfg, params, batches, n_seq: int):
+def cpu_baseline(cfg, params, batches, n_seq: int, dropout: float = 0.0):
     """The oracle, as it stands, on n_seq sequences of the same workload (float64)."""
     from oracle import gpt_oracle as O
     try:
@@ -52,7 +52,8 @@ def cpu_baseline(cfg, params, batches, n_seq: int):
     tok, tgt = batches[0]
     tok, tgt = tok[:n_seq], tgt[:n_seq]
     t0 = time.perf_counter()
-    O.microbatch(params, tok, tgt, cfg, grad_scale=1.0 / tok.size)
+    O.microbatch(params, tok, tgt, cfg, grad_scale=1.0 / tok.size,
+                 dropout=O.Dropout(dropout, 1337) if dropout > 0 else None)
     dt = time.perf_counter() - t0
     return {"value": round(tok.size / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{n_seq} sequence(s) x {tok.shape[1]} tokens, forward + backward in float64 "
@@ -88,6 +89,8 @@ def main(argv=None):
                     help="kernel family whose launches are timed for the roofline line "
                          "(gemm_wgrad: the grouped weight-gradient GEMM, the step's largest kernel; lm_head_fwd)")
     ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the oracle's timed sample (0: skip)")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="dropout rate of the timed model (the GPT-2 124M workload uses 0)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run 3 plain device copies of this many bytes (calibrates the HBM byte counters)")
     a = ap.parse_args(argv)
@@ -118,8 +121,10 @@ def main(argv=None):
     host_batches = [W.make_step_batches(cfg, drng) for _ in range(min(n_steps, 4))]
     dev_batches = [[(torch.from_numpy(t).cuda(), torch.from_numpy(y).cuda()) for t, y in s] for s in host_batches]
 
-    gpu = GPT(cfg, a.precision, device="cuda:0")
+    gpu = GPT(cfg, a.precision, device="cuda:0", dropout=a.dropout)
     gpu.load_params(params)
+    if a.dropout > 0:
+        gpu.set_dropout_seed(1337, 0)
     loss = torch.zeros(A, dtype=torch.float32, device="cuda:0")
     norm = torch.zeros(1, dtype=torch.float32, device="cuda:0")
 
@@ -196,10 +201,12 @@ def main(argv=None):
 
     cpu = None
     if a.cpu_seqs > 0:
-        cpu = cpu_baseline(cfg, params, host_batches[0], a.cpu_seqs)
+        cpu = cpu_baseline(cfg, params, host_batches[0], a.cpu_seqs, a.dropout)
 
-    metric = ("training tokens/sec and MFU, GPT-2 124M fwd+bwd+AdamW, T=1024, 1 MI355X" if cfg.name == "gpt2_124m"
-              else f"training tokens/sec and MFU, {cfg.name} fwd+bwd+AdamW, T={T}, 1 MI355X")
+    metric = ("training tokens/sec and MFU, GPT-2 124M fwd+bwd+AdamW, T=1024, 1 MI355X"
+              if cfg.name == "gpt2_124m" and a.dropout == 0
+              else f"training tokens/sec and MFU, {cfg.name} fwd+bwd+AdamW, T={T}, 1 MI355X"
+                   + (f", dropout {a.dropout}" if a.dropout else ""))
     ids = {"zipf_batch": f"Zipf({cfg.zipf_s}) ids over {cfg.vocab_size}",
            "zipf_stream": f"windows of a Zipf({cfg.zipf_s}) id stream over {cfg.vocab_size}",
            "markov_stream": f"windows of an order-1 Markov id stream over {cfg.vocab_size}",
@@ -219,7 +226,8 @@ def main(argv=None):
         "data": f"synthetic (seeded {ids}, random-init weights N(0,{cfg.init_std}))",
         "config": {"workload": f"{cfg.name}: L{cfg.n_layer} H{cfg.n_head} d{cfg.n_embd} V{cfg.vocab_size}"
                                f"(pad {cfg.padded_vocab}) B{B} T{T} accum{A}",
-                   "global_batch": B * A, "seq_len": T, "tokens_per_step": tokens_per_step},
+                   "global_batch": B * A, "seq_len": T, "tokens_per_step": tokens_per_step,
+                   "dropout": a.dropout},
         "mfu": round(mfu, 4),
         "mfu_causal_exact": round(tps * causal_ftok / peak, 4),
         "achieved_tflops": round(tps * ftok / 1e12, 1),

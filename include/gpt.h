@@ -18,6 +18,9 @@
  *     betas 0.9/0.95; section 3.1: gradient accumulation adds micro-batch
  *     gradients before one update (effective batch = batch x steps).
  *   - nanoGPT README translation (oa0.com): the GPT-2 124M model at block 1024.
+ *   - Dropout: the nanoGPT run log, sections 2.1 and 2.2 (rate 0.1, or 0.0 on
+ *     large data) and the microGPT page's parameter list (0.2 for the
+ *     Shakespeare character model).
  *
  * Conventions
  *   - All device pointers are plain HIP device addresses. The library never
@@ -70,7 +73,7 @@ typedef struct gpt_config {
   int32_t batch;         /* maximum micro-batch B per gpt_forward_loss call         */
   int32_t grad_accum;    /* A: backward scales the micro-batch mean loss by 1/A     */
   int32_t precision;     /* GPT_PREC_FP32 or GPT_PREC_BF16                          */
-  float   dropout;       /* must be 0                                               */
+  float   dropout;       /* p in [0, 1): see gpt_set_dropout_seed                   */
   uint32_t flags;        /* reserved, must be 0                                     */
 } gpt_config;
 
@@ -135,6 +138,23 @@ int gpt_init_state(gpt_model* h);
  * and kept for gpt_backward. */
 int gpt_forward_loss(gpt_model* h, const int32_t* d_tokens, const int32_t* d_targets,
                      int32_t B, int32_t T, float* d_loss);
+
+/* Dropout (config.dropout = p > 0) in gpt_forward_loss and the backward that
+ * follows it; gpt_forward_logits never drops. Inverted dropout at four kinds of
+ * site: the embedding output (site 0) and, in layer l, the attention
+ * probabilities (3l+1), the attention branch output before its residual add
+ * (3l+2) and the MLP branch output before its add (3l+3). Element (row, col)
+ * of a site's tensor takes word col % 4 of Philox4x32-10 (Salmon, Moraes, Dror
+ * and Shaw, SC 2011) at counter (col / 4, row, site, n) under the key
+ * (seed low 32 bits, seed high 32 bits); it is dropped when that word is below
+ * floor(p * 2^32) and otherwise multiplied by 1 / (1 - p) rounded to float.
+ * Rows and columns: token row b*T + t by channel for the embedding and the
+ * branch outputs, row (b*n_head + h)*T + i by key j for the probabilities of
+ * query i, with T the call's sequence length. n is the forward counter: each
+ * gpt_forward_loss uses the current value and then adds one (with or without
+ * dropout). This call sets the seed and the next forward's counter; both start
+ * at 0. Host-only, no GPU work; returns GPT_E_INVAL for a NULL handle. */
+int gpt_set_dropout_seed(gpt_model* h, uint64_t seed, uint32_t counter);
 
 /* Forward only, up to the logits, copied as fp32 [B, T, padded_vocab] into
  * d_logits. Does not disturb a pending backward's saved state only if no

@@ -61,23 +61,29 @@ def check_tensors(gpu: dict, ref: dict, prec, what="", tol=None, d=None, key_bia
     return worst
 
 
-def new_model(cfg, prec, batch=None, grad_accum=None):
+def new_model(cfg, prec, batch=None, grad_accum=None, dropout=0.0):
     from transformer_lm_gpt_amd.binding import GPT
-    return GPT(cfg, prec, batch=batch, grad_accum=grad_accum)
+    return GPT(cfg, prec, batch=batch, grad_accum=grad_accum, dropout=dropout)
 
 
-def run_steps(name, prec, steps=None, B=None, T=None, A=None, perturb=True, check_every=True, cfg=None):
+def run_steps(name, prec, steps=None, B=None, T=None, A=None, perturb=True, check_every=True, cfg=None,
+              dropout=0.0, seed=0, counter=0):
     """Runs `steps` optimizer steps on both sides and checks losses, gradients,
-    and parameters/moments after every step."""
+    and parameters/moments after every step. With dropout > 0 both sides draw
+    their masks from the same seed and forward counter."""
     cfg = W.CONFIGS[name] if cfg is None else cfg
     steps = cfg.parity_steps if steps is None else steps
     A = cfg.grad_accum if A is None else A
     drng, wrng = W.rngs()
     params = W.init_params(cfg, wrng, perturb=perturb)
-    say(f"[parity] {name} {prec} steps={steps} B={B or cfg.batch} T={T or cfg.block_size} A={A}")
-    gpu = new_model(cfg, prec, grad_accum=A)
+    say(f"[parity] {name} {prec} steps={steps} B={B or cfg.batch} T={T or cfg.block_size} A={A} dropout={dropout}")
+    gpu = new_model(cfg, prec, grad_accum=A, dropout=dropout)
     gpu.load_params(params)
-    tr = O.Trainer(params, cfg)
+    drop = None
+    if dropout > 0.0:
+        gpu.set_dropout_seed(seed, counter)
+        drop = O.Dropout(dropout, seed, counter)
+    tr = O.Trainer(params, cfg, dropout=drop)
     report = []
     for s in range(steps):
         batches = W.make_step_batches(cfg, drng, A=A, B=B, T=T)

@@ -79,7 +79,9 @@ def _raw(**kw):
     (dict(padded_vocab=10), -1),           # below vocab_size
     (dict(precision=7), -1),
     (dict(flags=1), -1),
-    (dict(dropout=0.1), -4),
+    (dict(dropout=1.0), -1),               # dropout must be in [0, 1)
+    (dict(dropout=-0.1), -1),
+    (dict(dropout=float("nan")), -1),
     (dict(n_embd=512, n_head=4), -4),      # head_dim 128
     (dict(batch=4096, block_size=16), -4),  # M above the single-workgroup sort
 ])
@@ -117,3 +119,22 @@ def test_bind_rejects_misaligned_and_null():
         assert lib.gpt_bind(lay.h, C.byref(b), None) == -1
     finally:
         lay.close()
+
+
+def test_dropout_config_and_seed_are_host_only():
+    """A dropout rate in [0, 1) is accepted; the seed call touches no GPU. In fp32
+    mode the workspace grows by one fp32 [M, d] array (the masked operand copy)."""
+    lib = Bd.load_library()
+    c = W.CONFIGS["char_small"]
+    plain = Bd.Layout(c, "fp32")
+    lay = Bd.Layout(c, "fp32", dropout=0.1)
+    try:
+        assert lib.gpt_set_dropout_seed(lay.h, 0xFFFFFFFFFFFFFFFF, 7) == 0
+        assert lib.gpt_set_dropout_seed(None, 1, 0) == -1
+        M = c.batch * c.block_size
+        grow = lay.sizes.workspace_bytes - plain.sizes.workspace_bytes
+        assert M * c.n_embd * 4 <= grow <= M * c.n_embd * 4 + 256
+        assert lay.sizes.activation_bytes == plain.sizes.activation_bytes
+    finally:
+        lay.close()
+        plain.close()

@@ -25,7 +25,7 @@ PREC = {"fp32": 0, "bf16": 1}
 # Every symbol include/gpt.h declares.
 EXPORTS = ["gpt_create", "gpt_destroy", "gpt_last_error", "gpt_get_sizes", "gpt_num_tensors",
            "gpt_tensor_info_at", "gpt_bind", "gpt_init_state", "gpt_forward_loss", "gpt_forward_logits",
-           "gpt_backward", "gpt_zero_grad", "gpt_adamw_step", "gpt_sync", "gpt_get_step",
+           "gpt_backward", "gpt_zero_grad", "gpt_set_dropout_seed", "gpt_adamw_step", "gpt_sync", "gpt_get_step",
            "gpt_debug_copy", "gpt_timer_enable", "gpt_timer_disable", "gpt_timer_read"]
 
 
@@ -80,6 +80,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         "gpt_forward_logits": (C.c_int, [vp, vp, i32, i32, vp]),
         "gpt_backward": (C.c_int, [vp]),
         "gpt_zero_grad": (C.c_int, [vp]),
+        "gpt_set_dropout_seed": (C.c_int, [vp, C.c_uint64, C.c_uint32]),
         "gpt_adamw_step": (C.c_int, [vp, f32, f32, f32, f32, f32, f32, vp]),
         "gpt_sync": (C.c_int, [vp]),
         "gpt_get_step": (C.c_int, [vp, C.POINTER(C.c_int64)]),
@@ -96,21 +97,22 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     return lib
 
 
-def make_config(cfg, precision: str, batch: Optional[int] = None, grad_accum: Optional[int] = None) -> gpt_config:
+def make_config(cfg, precision: str, batch: Optional[int] = None, grad_accum: Optional[int] = None,
+                dropout: float = 0.0) -> gpt_config:
     return gpt_config(cfg.vocab_size, cfg.padded_vocab, cfg.n_layer, cfg.n_head, cfg.n_embd, cfg.block_size,
                       cfg.batch if batch is None else batch,
-                      cfg.grad_accum if grad_accum is None else grad_accum, PREC[precision], 0.0, 0)
+                      cfg.grad_accum if grad_accum is None else grad_accum, PREC[precision], float(dropout), 0)
 
 
 class Layout:
     """Host-side view of a configuration: sizes and the flat tensor table. Needs no GPU."""
 
     def __init__(self, cfg, precision: str = "bf16", batch: Optional[int] = None,
-                 grad_accum: Optional[int] = None, raw: Optional[gpt_config] = None):
+                 grad_accum: Optional[int] = None, raw: Optional[gpt_config] = None, dropout: float = 0.0):
         self.lib = load_library()
         self.cfg = cfg
         self.precision = precision
-        self.raw = raw if raw is not None else make_config(cfg, precision, batch, grad_accum)
+        self.raw = raw if raw is not None else make_config(cfg, precision, batch, grad_accum, dropout)
         h = C.c_void_p()
         rc = self.lib.gpt_create(C.byref(self.raw), C.byref(h))
         if rc != GPT_OK:
@@ -159,9 +161,9 @@ class GPT(Layout):
     """One model bound to device buffers on the current torch device and stream."""
 
     def __init__(self, cfg, precision: str = "bf16", batch: Optional[int] = None,
-                 grad_accum: Optional[int] = None, device: str = "cuda"):
+                 grad_accum: Optional[int] = None, device: str = "cuda", dropout: float = 0.0):
         import torch
-        super().__init__(cfg, precision, batch, grad_accum)
+        super().__init__(cfg, precision, batch, grad_accum, dropout=dropout)
         self.torch = torch
         self.device = torch.device(device)
         s = self.sizes
@@ -232,6 +234,9 @@ class GPT(Layout):
 
     def backward(self):
         self._check(self.lib.gpt_backward(self.h))
+
+    def set_dropout_seed(self, seed: int, counter: int = 0):
+        self._check(self.lib.gpt_set_dropout_seed(self.h, int(seed) & 0xFFFFFFFFFFFFFFFF, int(counter) & 0xFFFFFFFF))
 
     def zero_grad(self):
         self._check(self.lib.gpt_zero_grad(self.h))

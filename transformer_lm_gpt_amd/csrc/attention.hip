@@ -18,6 +18,12 @@
 // accumulated per 64-key tile over the query tiles at or after it; dQ is
 // accumulated per 64-query tile over the key tiles at or before it. Both run
 // without atomics, so the result is deterministic.
+//
+// Dropout on the probabilities (nanoGPT run log, sections 2.1 and 2.2), in the
+// DROP instantiations: with Z the mask times 1/(1-p), O = (P o Z) V, and the
+// backward takes dV = (P o Z)^T dO, dS = P o (Z o dP - D); D = rowsum(dO o O) still
+// equals sum_j P_ij Z_ij dP_ij. The softmax statistics (m, l, lse) are those of
+// the undropped P. Z is recomputed from the counter-based generator, never stored.
 #include "common.h"
 #include "kernels.h"
 
@@ -65,10 +71,10 @@ __device__ inline void load_row_frags(typename Mfma<T>::frag (&f)[HDP / Mfma<T>:
 }
 
 // ----------------------------------------------------------------------------- forward
-template <typename T, int HDP>
+template <typename T, int HDP, bool DROP>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o,
                                                        float* __restrict__ lse, int Tn, int H, int hd,
-                                                       float scale) {
+                                                       float scale, DropArgs da, uint32_t site) {
   constexpr int KPI = Mfma<T>::KPI;
   constexpr int PB = AttnPad<T>::big;
   typedef Tile<T, 64, PB> KT;     // contraction c, rows = keys
@@ -139,8 +145,9 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv
       float rs = 0.f;
 #pragma unroll
       for (int nb = 0; nb < 4; nb++) {
-        const float p = (s[nb][e] == -INFINITY) ? 0.f : __expf(s[nb][e] - mnew);
+        float p = (s[nb][e] == -INFINITY) ? 0.f : __expf(s[nb][e] - mnew);
         rs += p;
+        if constexpr (DROP) p *= drop_mult1(da, site, (uint32_t)(bh * Tn + qi), k0 + nb * 16 + (lane & 15));
         Ps[w][PT::idx(nb * 16 + (lane & 15), (lane >> 4) * 4 + e)] = from_f32<T>(p);
       }
       rs = row16_sum(rs);
@@ -199,11 +206,12 @@ __global__ void attn_bwd_D_kernel(const T* __restrict__ o, const T* __restrict__
   D[((int64_t)b * H + h) * Tn + t] = s;
 }
 
-template <typename T, int HDP>
+template <typename T, int HDP, bool DROP>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const T* __restrict__ qkv, const T* __restrict__ dout,
                                                             const float* __restrict__ lse,
                                                             const float* __restrict__ Dv, T* __restrict__ dqkv,
-                                                            int Tn, int H, int hd, float scale) {
+                                                            int Tn, int H, int hd, float scale, DropArgs da,
+                                                            uint32_t site) {
   constexpr int KPI = Mfma<T>::KPI;
   constexpr int PB = AttnPad<T>::big;
   typedef Tile<T, 64, PB> NT;     // contraction c, rows = queries
@@ -273,8 +281,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const T* __restrict_
       for (int e = 0; e < 4; e++) {
         const int key = k0 + w * 16 + (lane >> 4) * 4 + e;
         const float p = (key <= q && q < Tn) ? __expf(st[e] * scale - ls[ql]) : 0.f;
-        const float ds = p * (dpt[e] - Ds[ql]);
-        PTs[w][WT::idx(ql, (lane >> 4) * 4 + e)] = from_f32<T>(p);
+        const float mk = DROP ? drop_mult1(da, site, (uint32_t)(bh * Tn + q), key) : 1.f;
+        const float ds = p * (dpt[e] * mk - Ds[ql]);
+        PTs[w][WT::idx(ql, (lane >> 4) * 4 + e)] = from_f32<T>(DROP ? p * mk : p);
         dSTs[w][WT::idx(ql, (lane >> 4) * 4 + e)] = from_f32<T>(ds);
       }
     }
@@ -306,11 +315,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const T* __restrict_
   }
 }
 
-template <typename T, int HDP>
+template <typename T, int HDP, bool DROP>
 __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const T* __restrict__ qkv, const T* __restrict__ dout,
                                                           const float* __restrict__ lse,
                                                           const float* __restrict__ Dv, T* __restrict__ dqkv,
-                                                          int Tn, int H, int hd, float scale) {
+                                                          int Tn, int H, int hd, float scale, DropArgs da,
+                                                          uint32_t site) {
   constexpr int KPI = Mfma<T>::KPI;
   constexpr int PB = AttnPad<T>::big;
   typedef Tile<T, 64, PB> NT;     // contraction c, rows = keys
@@ -375,7 +385,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const T* __restrict__ 
       for (int e = 0; e < 4; e++) {
         const int qi = q0 + w * 16 + (lane >> 4) * 4 + e;
         const float p = (key <= qi && key < Tn && qi < Tn) ? __expf(s[e] * scale - lsr[e]) : 0.f;
-        dSs[w][WT::idx(kl, (lane >> 4) * 4 + e)] = from_f32<T>(p * (dp[e] - Dr[e]));
+        const float mk = DROP ? drop_mult1(da, site, (uint32_t)(bh * Tn + qi), key) : 1.f;
+        dSs[w][WT::idx(kl, (lane >> 4) * 4 + e)] = from_f32<T>(p * (dp[e] * mk - Dr[e]));
       }
     }
     __syncthreads();
@@ -533,9 +544,10 @@ __device__ inline void block_colsum(const f32x4 (&acc)[HDP / 16], float mul, flo
 // The exponentials run in base 2 with the 1/sqrt(hd) scale folded in: with
 // c = log2(e)/sqrt(hd), exp(S*scale - x) = exp2(S*c - x*log2(e)), one FMA and one
 // v_exp per score. Only the diagonal tile of a causal block needs the mask.
-template <int HDP>
+template <int HDP, bool DROP>
 __global__ __launch_bounds__(256) void attn_fwd_v2(const bf16* __restrict__ qkv, bf16* __restrict__ o,
-                                                   float* __restrict__ lse, int Tn, int H, float scale) {
+                                                   float* __restrict__ lse, int Tn, int H, float scale, DropArgs da,
+                                                   uint32_t site) {
   typedef ATile<HDP> AT;
   constexpr int KK = HDP / 32, CB = HDP / 16;
   __shared__ __attribute__((aligned(16))) bf16 Ks[64 * HDP];
@@ -614,6 +626,10 @@ __global__ __launch_bounds__(256) void attn_fwd_v2(const bf16* __restrict__ qkv,
         st[nb][i] = p;
         l += p;
       }
+    if constexpr (DROP) {                             // this lane's four keys of a block share one Philox block
+#pragma unroll
+      for (int nb = 0; nb < 4; nb++) st[nb] *= drop_mult4(da, site, (uint32_t)(bh * Tn + q), kt * 16 + nb * 4 + g);
+    }
 #pragma unroll
     for (int kp = 0; kp < 2; kp++) {
       const bf16x8 pf = pack_p(st[2 * kp], st[2 * kp + 1]);
@@ -641,11 +657,12 @@ __global__ __launch_bounds__(256) void attn_fwd_v2(const bf16* __restrict__ qkv,
 
 // dQ for a 64-query block; also writes D = rowsum(dO * O) for these queries,
 // which the dK/dV kernel (launched after) reads.
-template <int HDP>
+template <int HDP, bool DROP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_bwd_dq_v2(const bf16* __restrict__ qkv, const bf16* __restrict__ o,
                                                       const bf16* __restrict__ dout, const float* __restrict__ lse,
                                                       float* __restrict__ Dv, bf16* __restrict__ dqkv, int Tn, int H,
-                                                      float scale, float* __restrict__ bias_part) {
+                                                      float scale, float* __restrict__ bias_part, DropArgs da,
+                                                      uint32_t site) {
   typedef ATile<HDP> AT;
   constexpr int KK = HDP / 32, CB = HDP / 16;
   __shared__ __attribute__((aligned(16))) bf16 Ks[64 * HDP];
@@ -706,6 +723,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
         st[nb] = Mfma<bf16>::mma(AT::row_frag(Ks, nb * 16 + (lane & 15), kk * 4 + g), qf[kk], st[nb]);
         dpt = Mfma<bf16>::mma(AT::row_frag(Vs, nb * 16 + (lane & 15), kk * 4 + g), dof[kk], dpt);
       }
+      if constexpr (DROP) dpt *= drop_mult4(da, site, (uint32_t)(bh * Tn + q), kt * 16 + nb * 4 + g);
       ds[nb] = dpt - Dq;
     }
     if (kt == qb) {                                   // diagonal tile: local keys <= q - k0 are visible
@@ -750,12 +768,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   }
 }
 
+// A quad of lanes (j = lane & 3) each holding one Philox block b_j: lane j gets
+// the words b_0[j], b_1[j], b_2[j], b_3[j]. In round r, lane i offers its word
+// (i + r) & 3 and lane j reads lane (j - r) & 3 (a fixed quad permutation), which
+// offers exactly word j.
+__device__ inline uint32_t sel4(const u32x4& v, int k) {
+  return k == 0 ? v[0] : (k == 1 ? v[1] : (k == 2 ? v[2] : v[3]));
+}
+__device__ inline u32x4 quad_transpose(const u32x4& b) {
+  const int j = threadIdx.x & 3;
+  u32x4 out;
+  out[0] = out[1] = out[2] = out[3] = 0u;
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    const uint32_t send = sel4(b, (j + r) & 3);
+    // quad_perm selectors [(0-r)&3, (1-r)&3, (2-r)&3, (3-r)&3]: lane j reads lane (j - r) & 3
+    uint32_t got = send;
+    if (r == 1) got = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x93, 0xf, 0xf, false);
+    if (r == 2) got = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4E, 0xf, 0xf, false);
+    if (r == 3) got = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x39, 0xf, 0xf, false);
+    const int i = (j - r) & 3;
+#pragma unroll
+    for (int k = 0; k < 4; k++) out[k] = i == k ? got : out[k];
+  }
+  return out;
+}
+
 // dK and dV for a 64-key block over the query tiles at or after it.
-template <int HDP>
+template <int HDP, bool DROP>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_v2(const bf16* __restrict__ qkv, const bf16* __restrict__ dout,
                                                         const float* __restrict__ lse, const float* __restrict__ Dv,
                                                         bf16* __restrict__ dqkv, int Tn, int H, float scale,
-                                                        float* __restrict__ bias_part) {
+                                                        float* __restrict__ bias_part, DropArgs da, uint32_t site) {
   typedef ATile<HDP> AT;
   constexpr int KK = HDP / 32, CB = HDP / 16;
   __shared__ __attribute__((aligned(16))) bf16 Qs2[2][64 * HDP];   // double-buffered Q and dO tiles
@@ -831,7 +875,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_v2(const bf16* __restrict__
         if (threadIdx.x < 64) stats(q0 + 128 + threadIdx.x, lnext, dnext);
       }
     }
-    f32x4 p[4], ds[4];
+    f32x4 p[4], ds[4], mk[DROP ? 4 : 1];
 #pragma unroll
     for (int nb = 0; nb < 4; nb++) {
       f32x4 dp = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -842,6 +886,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_v2(const bf16* __restrict__
         dp = Mfma<bf16>::mma(AT::row_frag(dOs, nb * 16 + (lane & 15), kk * 4 + g), vf[kk], dp);
       }
       p[nb] = __builtin_elementwise_fma(p[nb], (f32x4){c, c, c, c}, -*(const f32x4*)(ls + nb * 16 + 4 * g));
+      if constexpr (DROP) {
+        // this lane holds queries q0 + nb*16 + 4g + i of one key: lane j of the quad
+        // makes the block of query i = j (the quad's four keys are one counter's
+        // words), then the quad trades words
+        const uint32_t qrow = (uint32_t)(bh * Tn + q0 + nb * 16 + 4 * g + (lane & 3));
+        const u32x4 wv = quad_transpose(philox4x32_10((uint32_t)key >> 2, qrow, site, da.call, da.k0, da.k1));
+#pragma unroll
+        for (int i = 0; i < 4; i++) mk[nb][i] = wv[i] >= da.thr ? da.scale : 0.f;
+        dp *= mk[nb];
+      }
       ds[nb] = dp - *(const f32x4*)(Ds + nb * 16 + 4 * g);
     }
     if (qt == kb) {                                   // diagonal tile: local queries >= key - q0 see the key
@@ -858,6 +912,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_v2(const bf16* __restrict__
     }
 #pragma unroll
     for (int nb = 0; nb < 4; nb++) ds[nb] *= p[nb];
+    if constexpr (DROP) {
+#pragma unroll
+      for (int nb = 0; nb < 4; nb++) p[nb] *= mk[nb];
+    }
 #pragma unroll
     for (int qp = 0; qp < 2; qp++) {
       const bf16x8 pf = pack_p(p[2 * qp], p[2 * qp + 1]);
@@ -896,43 +954,57 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_v2(const bf16* __restrict__
 }
 
 // ----------------------------------------------------------------------------- launchers
-template <typename T, int HDP>
-static hipError_t fwd_t(const void* qkv, void* o, float* lse, int B, int Tn, int H, int hd, hipStream_t s) {
+template <typename T, int HDP, bool DROP>
+static hipError_t fwd_t(const void* qkv, void* o, float* lse, int B, int Tn, int H, int hd, const DropArgs& da,
+                        uint32_t site, hipStream_t s) {
   dim3 grid((Tn + 63) / 64, B * H);
   const float scale = 1.0f / sqrtf((float)hd);
-  hipLaunchKernelGGL((attn_fwd_kernel<T, HDP>), grid, dim3(256), 0, s, (const T*)qkv, (T*)o, lse, Tn, H, hd, scale);
+  hipLaunchKernelGGL((attn_fwd_kernel<T, HDP, DROP>), grid, dim3(256), 0, s, (const T*)qkv, (T*)o, lse, Tn, H, hd,
+                     scale, da, site);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_fwd(const void* qkv, void* o, float* lse, bool bf16_ops, int B, int T, int H, int hd,
-                           hipStream_t s) {
-  if (hd <= 0 || hd > 64) return hipErrorInvalidValue;
+template <bool DROP>
+static hipError_t fwd_any(const void* qkv, void* o, float* lse, bool bf16_ops, int B, int T, int H, int hd,
+                          const DropArgs& da, uint32_t site, hipStream_t s) {
   if (bf16_ops && (hd == 32 || hd == 64)) {
     if ((int64_t)T * 3 * H * hd * 2 > INT32_MAX) return hipErrorInvalidValue;   // 32-bit buffer offsets per sequence
     dim3 grid(B * H, (T + 63) / 64);
     const float scale = 1.0f / sqrtf((float)hd);
     if (hd == 64)
-      hipLaunchKernelGGL(attn_fwd_v2<64>, grid, dim3(256), 0, s, (const bf16*)qkv, (bf16*)o, lse, T, H, scale);
+      hipLaunchKernelGGL((attn_fwd_v2<64, DROP>), grid, dim3(256), 0, s, (const bf16*)qkv, (bf16*)o, lse, T, H,
+                         scale, da, site);
     else
-      hipLaunchKernelGGL(attn_fwd_v2<32>, grid, dim3(256), 0, s, (const bf16*)qkv, (bf16*)o, lse, T, H, scale);
+      hipLaunchKernelGGL((attn_fwd_v2<32, DROP>), grid, dim3(256), 0, s, (const bf16*)qkv, (bf16*)o, lse, T, H,
+                         scale, da, site);
     return hipGetLastError();
   }
-  if (bf16_ops) return hd <= 32 ? fwd_t<bf16, 32>(qkv, o, lse, B, T, H, hd, s) : fwd_t<bf16, 64>(qkv, o, lse, B, T, H, hd, s);
-  return hd <= 32 ? fwd_t<float, 32>(qkv, o, lse, B, T, H, hd, s) : fwd_t<float, 64>(qkv, o, lse, B, T, H, hd, s);
+  if (bf16_ops)
+    return hd <= 32 ? fwd_t<bf16, 32, DROP>(qkv, o, lse, B, T, H, hd, da, site, s)
+                    : fwd_t<bf16, 64, DROP>(qkv, o, lse, B, T, H, hd, da, site, s);
+  return hd <= 32 ? fwd_t<float, 32, DROP>(qkv, o, lse, B, T, H, hd, da, site, s)
+                  : fwd_t<float, 64, DROP>(qkv, o, lse, B, T, H, hd, da, site, s);
 }
 
-template <typename T, int HDP>
+hipError_t launch_attn_fwd(const void* qkv, void* o, float* lse, bool bf16_ops, int B, int T, int H, int hd,
+                           const DropArgs& da, uint32_t site, hipStream_t s) {
+  if (hd <= 0 || hd > 64) return hipErrorInvalidValue;
+  return da.on ? fwd_any<true>(qkv, o, lse, bf16_ops, B, T, H, hd, da, site, s)
+               : fwd_any<false>(qkv, o, lse, bf16_ops, B, T, H, hd, da, site, s);
+}
+
+template <typename T, int HDP, bool DROP>
 static hipError_t bwd_t(const void* qkv, const void* o, const void* dout, const float* lse, float* D, void* dqkv,
-                        int B, int Tn, int H, int hd, hipStream_t s) {
+                        int B, int Tn, int H, int hd, const DropArgs& da, uint32_t site, hipStream_t s) {
   const float scale = 1.0f / sqrtf((float)hd);
   const int n = B * H * Tn;
   hipLaunchKernelGGL(attn_bwd_D_kernel<T>, dim3((n + 255) / 256), dim3(256), 0, s, (const T*)o, (const T*)dout, D,
                      B, Tn, H, hd);
   dim3 grid((Tn + 63) / 64, B * H);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HDP>), grid, dim3(256), 0, s, (const T*)qkv, (const T*)dout, lse,
-                     (const float*)D, (T*)dqkv, Tn, H, hd, scale);
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HDP>), grid, dim3(256), 0, s, (const T*)qkv, (const T*)dout, lse,
-                     (const float*)D, (T*)dqkv, Tn, H, hd, scale);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HDP, DROP>), grid, dim3(256), 0, s, (const T*)qkv, (const T*)dout,
+                     lse, (const float*)D, (T*)dqkv, Tn, H, hd, scale, da, site);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HDP, DROP>), grid, dim3(256), 0, s, (const T*)qkv, (const T*)dout, lse,
+                     (const float*)D, (T*)dqkv, Tn, H, hd, scale, da, site);
   return hipGetLastError();
 }
 
@@ -940,32 +1012,41 @@ int attn_bwd_colsum_rows(bool bf16_ops, int B, int T, int hd) {
   return bf16_ops && (hd == 32 || hd == 64) ? B * ((T + 63) / 64) : 0;
 }
 
-hipError_t launch_attn_bwd(const void* qkv, const void* o, const void* dout, const float* lse, float* D,
-                           void* dqkv, bool bf16_ops, int B, int T, int H, int hd, float* bias_part, hipStream_t s) {
-  if (hd <= 0 || hd > 64) return hipErrorInvalidValue;
-  if (bias_part && attn_bwd_colsum_rows(bf16_ops, B, T, hd) == 0) return hipErrorInvalidValue;
+template <bool DROP>
+static hipError_t bwd_any(const void* qkv, const void* o, const void* dout, const float* lse, float* D, void* dqkv,
+                          bool bf16_ops, int B, int T, int H, int hd, float* bias_part, const DropArgs& da,
+                          uint32_t site, hipStream_t s) {
   if (bf16_ops && (hd == 32 || hd == 64)) {
     if ((int64_t)T * 3 * H * hd * 2 > INT32_MAX) return hipErrorInvalidValue;   // 32-bit buffer offsets per sequence
     dim3 grid(B * H, (T + 63) / 64);
     const float scale = 1.0f / sqrtf((float)hd);
     if (hd == 64) {
-      hipLaunchKernelGGL(attn_bwd_dq_v2<64>, grid, dim3(256), 0, s, (const bf16*)qkv, (const bf16*)o,
-                         (const bf16*)dout, lse, D, (bf16*)dqkv, T, H, scale, bias_part);
-      hipLaunchKernelGGL(attn_bwd_dkdv_v2<64>, grid, dim3(256), 0, s, (const bf16*)qkv, (const bf16*)dout, lse,
-                         (const float*)D, (bf16*)dqkv, T, H, scale, bias_part);
+      hipLaunchKernelGGL((attn_bwd_dq_v2<64, DROP>), grid, dim3(256), 0, s, (const bf16*)qkv, (const bf16*)o,
+                         (const bf16*)dout, lse, D, (bf16*)dqkv, T, H, scale, bias_part, da, site);
+      hipLaunchKernelGGL((attn_bwd_dkdv_v2<64, DROP>), grid, dim3(256), 0, s, (const bf16*)qkv, (const bf16*)dout,
+                         lse, (const float*)D, (bf16*)dqkv, T, H, scale, bias_part, da, site);
     } else {
-      hipLaunchKernelGGL(attn_bwd_dq_v2<32>, grid, dim3(256), 0, s, (const bf16*)qkv, (const bf16*)o,
-                         (const bf16*)dout, lse, D, (bf16*)dqkv, T, H, scale, bias_part);
-      hipLaunchKernelGGL(attn_bwd_dkdv_v2<32>, grid, dim3(256), 0, s, (const bf16*)qkv, (const bf16*)dout, lse,
-                         (const float*)D, (bf16*)dqkv, T, H, scale, bias_part);
+      hipLaunchKernelGGL((attn_bwd_dq_v2<32, DROP>), grid, dim3(256), 0, s, (const bf16*)qkv, (const bf16*)o,
+                         (const bf16*)dout, lse, D, (bf16*)dqkv, T, H, scale, bias_part, da, site);
+      hipLaunchKernelGGL((attn_bwd_dkdv_v2<32, DROP>), grid, dim3(256), 0, s, (const bf16*)qkv, (const bf16*)dout,
+                         lse, (const float*)D, (bf16*)dqkv, T, H, scale, bias_part, da, site);
     }
     return hipGetLastError();
   }
   if (bf16_ops)
-    return hd <= 32 ? bwd_t<bf16, 32>(qkv, o, dout, lse, D, dqkv, B, T, H, hd, s)
-                    : bwd_t<bf16, 64>(qkv, o, dout, lse, D, dqkv, B, T, H, hd, s);
-  return hd <= 32 ? bwd_t<float, 32>(qkv, o, dout, lse, D, dqkv, B, T, H, hd, s)
-                  : bwd_t<float, 64>(qkv, o, dout, lse, D, dqkv, B, T, H, hd, s);
+    return hd <= 32 ? bwd_t<bf16, 32, DROP>(qkv, o, dout, lse, D, dqkv, B, T, H, hd, da, site, s)
+                    : bwd_t<bf16, 64, DROP>(qkv, o, dout, lse, D, dqkv, B, T, H, hd, da, site, s);
+  return hd <= 32 ? bwd_t<float, 32, DROP>(qkv, o, dout, lse, D, dqkv, B, T, H, hd, da, site, s)
+                  : bwd_t<float, 64, DROP>(qkv, o, dout, lse, D, dqkv, B, T, H, hd, da, site, s);
+}
+
+hipError_t launch_attn_bwd(const void* qkv, const void* o, const void* dout, const float* lse, float* D,
+                           void* dqkv, bool bf16_ops, int B, int T, int H, int hd, float* bias_part,
+                           const DropArgs& da, uint32_t site, hipStream_t s) {
+  if (hd <= 0 || hd > 64) return hipErrorInvalidValue;
+  if (bias_part && attn_bwd_colsum_rows(bf16_ops, B, T, hd) == 0) return hipErrorInvalidValue;
+  return da.on ? bwd_any<true>(qkv, o, dout, lse, D, dqkv, bf16_ops, B, T, H, hd, bias_part, da, site, s)
+               : bwd_any<false>(qkv, o, dout, lse, D, dqkv, bf16_ops, B, T, H, hd, bias_part, da, site, s);
 }
 
 }  // namespace gpt

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 namespace gpt {
 
 typedef __bf16 bf16;
@@ -96,6 +98,45 @@ __device__ inline float gelu_grad_f(float u) {
   float c, d;
   normal_cdf_pdf(u, c, d);
   return c + u * d;
+}
+
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, SC 2011): ten rounds, each taking
+// the 32x32 -> 64-bit products of counter words 0 and 2 with the two round
+// multipliers and forming (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1,
+// lo(M0 c0)); the key advances by the two Weyl increments between rounds.
+__device__ inline u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                      uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; r++) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    c0 = hi1 ^ c1 ^ k0;
+    c2 = hi0 ^ c3 ^ k1;
+    c1 = lo1;
+    c3 = lo0;
+  }
+  return (u32x4){c0, c1, c2, c3};
+}
+
+// Dropout multipliers (scale when kept, 0 when dropped) of columns 4*grp .. 4*grp+3
+// of `row` at `site`.
+__device__ inline f32x4 drop_mult4(const DropArgs& a, uint32_t site, uint32_t row, uint32_t grp) {
+  const u32x4 w = philox4x32_10(grp, row, site, a.call, a.k0, a.k1);
+  f32x4 m;
+#pragma unroll
+  for (int i = 0; i < 4; i++) m[i] = w[i] >= a.thr ? a.scale : 0.f;
+  return m;
+}
+// The multiplier of one element (row, col).
+__device__ inline float drop_mult1(const DropArgs& a, uint32_t site, uint32_t row, uint32_t col) {
+  const u32x4 w = philox4x32_10(col >> 2, row, site, a.call, a.k0, a.k1);
+  const uint32_t j = col & 3;
+  const uint32_t x = j == 0 ? w[0] : (j == 1 ? w[1] : (j == 2 ? w[2] : w[3]));
+  return x >= a.thr ? a.scale : 0.f;
 }
 
 }  // namespace gpt

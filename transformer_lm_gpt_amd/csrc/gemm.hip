@@ -179,11 +179,17 @@ struct GemmArgs {
   int kchunk;          // contraction length per split (gridDim.z splits)
   float* part;         // split partials [gridDim.z, M, N] (EPI_ACC with gridDim.z > 1)
   float* colsum;       // EPI_GELU_BWD: per-tile-row column sums [tiles_m, N], or NULL
+  DropArgs drop;       // EPI_BIAS_RESID_DROP: the branch output's dropout mask
+  uint32_t drop_site;
 };
+
+// Epilogues that add a residual (with or without dropout on the branch) and those with a bias.
+template <int EPI> constexpr bool epi_resid() { return EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_RESID_DROP; }
+template <int EPI> constexpr bool epi_has_bias() { return EPI == EPI_BIAS || epi_resid<EPI>() || EPI == EPI_BIAS_GELU; }
 
 template <int EPI>
 __device__ inline float epi_bias(const GemmArgs& p, int col) {
-  if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU) return p.bias[col];
+  if constexpr (epi_has_bias<EPI>()) return p.bias[col];
   return 0.f;
 }
 
@@ -197,6 +203,8 @@ __device__ inline void epi_store(const GemmArgs& p, int row, int col, float v, f
     ((T*)p.C)[ci] = from_f32<T>(v + bias);
   } else if constexpr (EPI == EPI_BIAS_RESID) {
     ((float*)p.C)[ci] = p.resid[(int64_t)row * p.ldr + col] + (v + bias);
+  } else if constexpr (EPI == EPI_BIAS_RESID_DROP) {
+    ((float*)p.C)[ci] = p.resid[(int64_t)row * p.ldr + col] + (v + bias) * drop_mult1(p.drop, p.drop_site, row, col);
   } else if constexpr (EPI == EPI_BIAS_GELU) {
     const float u = v + bias;
     ((T*)p.aux)[(int64_t)row * p.ldaux + col] = from_f32<T>(u);
@@ -220,11 +228,11 @@ __device__ inline void epi_store(const GemmArgs& p, int row, int col, float v, f
 // block are in flight while the current one is stored.
 template <int EPI>
 struct EpiPre {
-  static constexpr bool ON = EPI == EPI_BIAS_RESID || EPI == EPI_GELU_BWD;
-  f32x4 r[EPI == EPI_BIAS_RESID ? 4 : 1];
+  static constexpr bool ON = epi_resid<EPI>() || EPI == EPI_GELU_BWD;
+  f32x4 r[epi_resid<EPI>() ? 4 : 1];
   bf16x8 u[EPI == EPI_GELU_BWD ? 2 : 1];
   __device__ inline void load(const GemmArgs& p, int row, int col0) {
-    if constexpr (EPI == EPI_BIAS_RESID) {
+    if constexpr (epi_resid<EPI>()) {
       const float* src = p.resid + (int64_t)row * p.ldr + col0;
 #pragma unroll
       for (int q = 0; q < 4; q++) r[q] = *(const f32x4*)(src + 4 * q);
@@ -259,7 +267,7 @@ __device__ inline void epi_store16(const GemmArgs& p, int row, int col0, const f
   float x[16];
 #pragma unroll
   for (int c = 0; c < 16; c++) x[c] = v[c];
-  if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU) {
+  if constexpr (epi_has_bias<EPI>()) {
 #pragma unroll
     for (int q = 0; q < 4; q++) {
       const f32x4 b = bias16 ? bias16[q] : *(const f32x4*)(p.bias + col0 + 4 * q);
@@ -275,14 +283,20 @@ __device__ inline void epi_store16(const GemmArgs& p, int row, int col0, const f
       for (int e = 0; e < 8; e++) o[e] = (bf16)x[8 * q + e];
       *(bf16x8*)((bf16*)p.C + ci + 8 * q) = o;
     }
-  } else if constexpr (EPI == EPI_BIAS_RESID) {
+  } else if constexpr (epi_resid<EPI>()) {
     const float* r = p.resid + (int64_t)row * p.ldr + col0;
 #pragma unroll
     for (int q = 0; q < 4; q++) {
       const f32x4 rv = pre ? pre->r[q] : *(const f32x4*)(r + 4 * q);
       f32x4 o;
+      if constexpr (EPI == EPI_BIAS_RESID_DROP) {
+        const f32x4 mk = drop_mult4(p.drop, p.drop_site, row, (col0 >> 2) + q);
 #pragma unroll
-      for (int e = 0; e < 4; e++) o[e] = rv[e] + x[4 * q + e];
+        for (int e = 0; e < 4; e++) o[e] = rv[e] + x[4 * q + e] * mk[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; e++) o[e] = rv[e] + x[4 * q + e];
+      }
       *(f32x4*)((float*)p.C + ci + 4 * q) = o;
     }
   } else if constexpr (EPI == EPI_BIAS_GELU) {
@@ -609,7 +623,7 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, 
   // epilogue inputs of 16-row block i (item it = lane + 64*ps: row er, columns ec..)
   // (the fp32 residual of two blocks does not fit beside the accumulators of two
   // workgroups per CU: the 32-wide-slice residual kernel loads it in place)
-  constexpr bool PF = EpiPre<EPI>::ON && !(EPI == EPI_BIAS_RESID && KS == 32);
+  constexpr bool PF = EpiPre<EPI>::ON && !(epi_resid<EPI>() && KS == 32);
   EpiPre<EPI> pre[PF ? 2 : 1][PASSES];
   auto prefetch = [&](int i, EpiPre<EPI> (&dst)[PASSES]) {
 #pragma unroll
@@ -623,7 +637,7 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, 
   if constexpr (PF)
     if (!park) prefetch(0, pre[0]);
   // the bias of an item's 16 columns is the same in every row block
-  constexpr bool PB = EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU;
+  constexpr bool PB = epi_has_bias<EPI>();
   f32x4 bias16[PB ? PASSES : 1][4];
   if constexpr (PB) {
 #pragma unroll
@@ -816,6 +830,7 @@ static hipError_t dma_epi(const GemmArgs& a, int epi, int splits, hipStream_t s)
     GPT_DMA_CASE(EPI_F32)
     GPT_DMA_CASE(EPI_GELU_BWD)
     GPT_DMA_CASE(EPI_ACC)
+    GPT_DMA_CASE(EPI_BIAS_RESID_DROP)
 #undef GPT_DMA_CASE
     default: return hipErrorInvalidValue;
   }
@@ -840,6 +855,7 @@ static hipError_t sk_epi(const GemmArgs& a, int epi, int W, float* ws, int maxse
     GPT_SK_CASE(EPI_F32)
     GPT_SK_CASE(EPI_GELU_BWD)
     GPT_SK_CASE(EPI_ACC)
+    GPT_SK_CASE(EPI_BIAS_RESID_DROP)
 #undef GPT_SK_CASE
     default: return hipErrorInvalidValue;
   }
@@ -887,6 +903,7 @@ static hipError_t dispatch_epi(const GemmArgs& a, int epi, dim3 grid, hipStream_
     GPT_EPI_CASE(EPI_F32)
     GPT_EPI_CASE(EPI_GELU_BWD)
     GPT_EPI_CASE(EPI_ACC)
+    GPT_EPI_CASE(EPI_BIAS_RESID_DROP)
 #undef GPT_EPI_CASE
     default: return hipErrorInvalidValue;
   }
@@ -1064,6 +1081,7 @@ hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
   a.A = d.A; a.lda = d.lda; a.B = d.B; a.ldb = d.ldb; a.C = d.C; a.ldc = d.ldc;
   a.M = d.M; a.N = d.N; a.K = d.K; a.bias = d.bias; a.resid = d.resid; a.ldr = d.ldr;
   a.aux = d.aux; a.ldaux = d.ldaux; a.beta = d.beta;
+  a.drop = d.drop; a.drop_site = d.drop_site;
   const int vw = bf16_operands ? 8 : 4;               // elements per 16-byte vector
   auto vec_ok = [&](const void* ptr, int64_t ld) { return (ld % vw == 0) && ((uintptr_t)ptr % 16 == 0); };
   a.a_vec = vec_ok(d.A, d.lda);

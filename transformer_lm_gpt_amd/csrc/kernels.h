@@ -6,6 +6,29 @@
 
 namespace gpt {
 
+// Dropout masks from the counter-based generator Philox4x32-10 (Salmon, Moraes,
+// Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011), as the
+// nanoGPT run log (sections 2.1 and 2.2) uses dropout: on the embedding output,
+// the attention probabilities and each residual branch before its add. Element
+// (row, col) of a site's tensor takes word col % 4 of the block at counter
+// (col / 4, row, site, call) under the key (k0, k1); it is kept when that word is
+// >= thr, and a kept value is multiplied by `scale`, a dropped one by 0.
+// Rows and columns: token row b*T + t by channel for the embedding and branch
+// outputs; row (b*H + h)*T + i by key j for the attention probabilities.
+struct DropArgs {
+  uint32_t k0, k1;   // key: the seed's low and high words
+  uint32_t call;     // forward counter
+  uint32_t thr;      // floor(p * 2^32)
+  float scale;       // 1 / (1 - p), rounded to fp32
+  int32_t on;        // 0: no dropout (no mask is evaluated)
+};
+// Site numbers: the embedding output, then per layer l the attention
+// probabilities, the attention branch output and the MLP branch output.
+inline uint32_t site_embed() { return 0; }
+inline uint32_t site_attn_prob(int l) { return 3u * l + 1; }
+inline uint32_t site_attn_out(int l) { return 3u * l + 2; }
+inline uint32_t site_mlp_out(int l) { return 3u * l + 3; }
+
 enum Epilogue {
   EPI_STORE = 0,       // C(T)   = acc
   EPI_BIAS = 1,        // C(T)   = acc + bias[n]
@@ -14,6 +37,7 @@ enum Epilogue {
   EPI_F32 = 4,         // C(f32) = acc
   EPI_GELU_BWD = 5,    // C(T)   = acc * gelu'(aux[m, n])   (aux in operand type T)
   EPI_ACC = 6,         // C(f32) = beta * C + acc   (beta is 0 or 1; C is not read when 0)
+  EPI_BIAS_RESID_DROP = 7,  // C(f32) = resid[m, n] + mask(drop_site, m, n) * (acc + bias[n])
 };
 
 // C[m, n] = sum_k A(m, k) B(n, k) followed by the epilogue, where
@@ -34,6 +58,9 @@ struct GemmDesc {
   // optional, EPI_GELU_BWD only: per-tile-row column sums of C (fp32, before
   // rounding) into colsum[r * N + n], r < gemm_colsum_rows(...)
   float* colsum;
+  // EPI_BIAS_RESID_DROP only: the branch output's mask (rows m and columns n of C)
+  DropArgs drop;
+  uint32_t drop_site;
 };
 
 hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s);
@@ -66,10 +93,15 @@ size_t wgrad_group_ws_floats();
 hipError_t launch_wgrad_group(const WgradProblem* probs, int nprob, int total_tiles, int K, float beta, float* ws,
                               size_t ws_floats, hipStream_t s);
 
-// x0[m, :] = wte[tok[m], :] + wpe[m % T, :]   (fp32)
-// Ids outside [0, Vp) produce NaN rows instead of out-of-bounds reads.
+// x0[m, :] = wte[tok[m], :] + wpe[m % T, :]   (fp32), times the embedding
+// site's dropout mask when da.on. Ids outside [0, Vp) produce NaN rows instead of
+// out-of-bounds reads.
 hipError_t launch_embed_fwd(const float* wte, const float* wpe, const int32_t* tok, float* x0,
-                            int M, int T, int d, int Vp, hipStream_t s);
+                            int M, int T, int d, int Vp, const DropArgs& da, hipStream_t s);
+// dst[m, :] = src[m, :] * mask(site, m, :) for an fp32 [M, d] array (dst may be
+// src). d must be a multiple of 4 and both pointers 16-byte aligned.
+hipError_t launch_dropout_rows(const float* src, float* dst, int M, int d, const DropArgs& da, uint32_t site,
+                               hipStream_t s);
 
 // y = LN(x) with gain g, shift b; writes y as operand type, mean and rstd (fp32 [M]).
 hipError_t launch_layernorm_fwd(const float* x, const float* g, const float* b, void* y, bool bf16_out,
@@ -79,10 +111,13 @@ hipError_t launch_layernorm_fwd(const float* x, const float* g, const float* b, 
 // dx_op; per-block partial column sums of dy * xhat, dy and dres (dres may be NULL,
 // then part_r is unused) into part_g / part_b / part_r ([nblk, d] each,
 // nblk = ceil(M / LN_BWD_ROWS)). dx may alias dres. d must be a multiple of 4.
+// With da.on, the dres column sums take dres * mask(site_in) when site_in >= 0,
+// and dx_op holds dx * mask(site_out) when site_out >= 0 (dx itself is unmasked).
 constexpr int LN_BWD_ROWS = 16;
 hipError_t launch_layernorm_bwd(const float* dy, const float* x, const float* mean, const float* rstd,
                                 const float* g, const float* dres, float* dx, void* dx_op, bool bf16_out,
-                                float* part_g, float* part_b, float* part_r, int M, int d, hipStream_t s);
+                                float* part_g, float* part_b, float* part_r, int M, int d, const DropArgs& da,
+                                int site_in, int site_out, hipStream_t s);
 
 // Column sums of an [M, N] matrix (fp32 or bf16) into per-block partials [nblk, N].
 constexpr int COLSUM_ROWS = 64;
@@ -118,15 +153,18 @@ hipError_t launch_mean(const float* row_loss, int M, float* out, hipStream_t s);
 
 // Causal attention forward. qkv: [B*T, 3*d] (q | k | v, head h at columns h*hd);
 // o: [B*T, d]; lse: fp32 [B*H, T].
+// With da.on, O = (P * mask(site)) V; lse stays that of the undropped P.
 hipError_t launch_attn_fwd(const void* qkv, void* o, float* lse, bool bf16_ops, int B, int T, int H,
-                           int hd, hipStream_t s);
+                           int hd, const DropArgs& da, uint32_t site, hipStream_t s);
 // Attention backward: D = rowsum(dO * O), then dK/dV and dQ into dqkv [B*T, 3*d].
 // bias_part (optional): the qkv bias gradient's partial column sums of dqkv (fp32,
 // before rounding), one row per (sequence, 64-row block): [attn_bwd_colsum_rows(), 3 H hd].
 // Must be NULL when attn_bwd_colsum_rows() is 0 for the same arguments.
+// With da.on (the forward's mask): dV = (P * Z)^T dO and dS = P * (Z * dP - D), Z the
+// mask; D = rowsum(dO * O) is unchanged.
 hipError_t launch_attn_bwd(const void* qkv, const void* o, const void* dout, const float* lse,
                            float* Dbuf, void* dqkv, bool bf16_ops, int B, int T, int H, int hd,
-                           float* bias_part, hipStream_t s);
+                           float* bias_part, const DropArgs& da, uint32_t site, hipStream_t s);
 int attn_bwd_colsum_rows(bool bf16_ops, int B, int T, int hd);
 
 // Embedding backward: dwpe[t] = beta * dwpe[t] + sum_b dx0[b, t]; dwte[tok] += rows of dx0,

@@ -8,23 +8,26 @@ namespace gpt {
 
 // ----------------------------------------------------------------------------- embedding
 // Token embedding plus learned position embedding ("Building microGPT from
-// scratch", model-core section: token/pos embedding, no rotary).
+// scratch", model-core section: token/pos embedding, no rotary), then the
+// embedding dropout when da.on (nanoGPT run log, sections 2.1 and 2.2).
 __global__ void embed_fwd_kernel(const float* __restrict__ wte, const float* __restrict__ wpe,
                                  const int32_t* __restrict__ tok, float* __restrict__ x0, int M, int T, int d,
-                                 int Vp) {
+                                 int Vp, DropArgs da) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int64_t total = (int64_t)M * d;
   if (i >= total) return;
   int m = (int)(i / d), c = (int)(i % d);
   const int id = tok[m];
   // an id outside the table poisons the row instead of reading out of bounds
-  x0[i] = (id >= 0 && id < Vp) ? wte[(int64_t)id * d + c] + wpe[(int64_t)(m % T) * d + c] : __builtin_nanf("");
+  float v = (id >= 0 && id < Vp) ? wte[(int64_t)id * d + c] + wpe[(int64_t)(m % T) * d + c] : __builtin_nanf("");
+  if (da.on) v *= drop_mult1(da, 0, m, c);
+  x0[i] = v;
 }
 
 // The same, four columns per thread (d a multiple of 4, 16-byte aligned tables).
 __global__ void embed_fwd4_kernel(const float* __restrict__ wte, const float* __restrict__ wpe,
                                   const int32_t* __restrict__ tok, float* __restrict__ x0, int M, int T, int d,
-                                  int Vp) {
+                                  int Vp, DropArgs da) {
   const int d4 = d >> 2;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (int64_t)M * d4) return;
@@ -37,20 +40,38 @@ __global__ void embed_fwd4_kernel(const float* __restrict__ wte, const float* __
     const float nan = __builtin_nanf("");
     v = (f32x4){nan, nan, nan, nan};
   }
+  if (da.on) v *= drop_mult4(da, 0, m, c >> 2);
   *(f32x4*)(x0 + (int64_t)m * d + c) = v;
 }
 
 hipError_t launch_embed_fwd(const float* wte, const float* wpe, const int32_t* tok, float* x0, int M, int T,
-                            int d, int Vp, hipStream_t s) {
+                            int d, int Vp, const DropArgs& da, hipStream_t s) {
   if (d % 4 == 0 && (uintptr_t)wte % 16 == 0 && (uintptr_t)wpe % 16 == 0 && (uintptr_t)x0 % 16 == 0) {
     const int64_t n4 = (int64_t)M * (d / 4);
     hipLaunchKernelGGL(embed_fwd4_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, wte, wpe, tok, x0, M,
-                       T, d, Vp);
+                       T, d, Vp, da);
     return hipGetLastError();
   }
   int64_t total = (int64_t)M * d;
   hipLaunchKernelGGL(embed_fwd_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, wte, wpe, tok,
-                     x0, M, T, d, Vp);
+                     x0, M, T, d, Vp, da);
+  return hipGetLastError();
+}
+
+// dst = src * mask(site) over an fp32 [M, d] array, four columns per thread.
+__global__ void dropout_rows_kernel(const float* src, float* dst, int M, int d4, DropArgs da, uint32_t site) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)M * d4) return;
+  const int m = (int)(i / d4), g = (int)(i % d4);
+  ((f32x4*)dst)[i] = ((const f32x4*)src)[i] * drop_mult4(da, site, m, g);
+}
+
+hipError_t launch_dropout_rows(const float* src, float* dst, int M, int d, const DropArgs& da, uint32_t site,
+                               hipStream_t s) {
+  if (d % 4 != 0 || (uintptr_t)src % 16 != 0 || (uintptr_t)dst % 16 != 0) return hipErrorInvalidValue;
+  const int64_t n4 = (int64_t)M * (d / 4);
+  hipLaunchKernelGGL(dropout_rows_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, src, dst, M, d / 4,
+                     da, site);
   return hipGetLastError();
 }
 
@@ -166,14 +187,19 @@ hipError_t launch_layernorm_fwd(const float* x, const float* g, const float* b, 
 // written as one partial row per workgroup (reduced later by colsum_final).
 // The dres column sum is the bias gradient of the projection whose output
 // feeds this residual, so it comes for free here.
+// With DROP, the dres column sums take dres times the mask of site_in (the
+// gradient of the dropped branch output whose add fed this residual) and dx_op
+// holds dx times the mask of site_out (the operand of the branch below); a
+// negative site leaves that side unmasked.
 constexpr int LN_MAX_D = 1024;
-template <typename T, int NCH>
+template <typename T, int NCH, bool DROP>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ dy, const float* __restrict__ x,
                                                      const float* __restrict__ mean,
                                                      const float* __restrict__ rstd, const float* __restrict__ g,
                                                      const float* dres, float* dx, T* dx_op,
                                                      float* __restrict__ part_g, float* __restrict__ part_b,
-                                                     float* __restrict__ part_r, int M, int d) {
+                                                     float* __restrict__ part_r, int M, int d, DropArgs da,
+                                                     int site_in, int site_out) {
   __shared__ f32x4 red[4][LN_MAX_D / 4];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int d4 = d >> 2;
@@ -238,9 +264,11 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           v[e] = rs * (dyv[j][e] * gg[j][e] - a - xh[j][e] * bb) + rv[j][e];
-          pr[j][e] += rv[j][e];
+          if constexpr (!DROP) pr[j][e] += rv[j][e];
         }
+        if constexpr (DROP) pr[j] += site_in >= 0 ? rv[j] * drop_mult4(da, site_in, row, c4) : rv[j];
         ((f32x4*)dx)[o4 + c4] = v;
+        if (DROP && site_out >= 0) v *= drop_mult4(da, site_out, row, c4);
         if (dx_op) {
           if constexpr (sizeof(T) == 2) {
             bf16x4 vb;
@@ -275,15 +303,15 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
   }
 }
 
-template <typename T>
+template <typename T, bool DROP>
 static hipError_t ln_bwd_t(const float* dy, const float* x, const float* mean, const float* rstd, const float* g,
                            const float* dres, float* dx, void* dx_op, float* pg, float* pb, float* pr, int M, int d,
-                           hipStream_t s) {
+                           const DropArgs& da, int si, int so, hipStream_t s) {
   dim3 grid((M + LN_BWD_ROWS - 1) / LN_BWD_ROWS);
   const int nch = (d / 4 + 63) / 64;
   switch (nch) {
 #define LNB(N) \
-  case N: hipLaunchKernelGGL((ln_bwd_kernel<T, N>), grid, dim3(256), 0, s, dy, x, mean, rstd, g, dres, dx, (T*)dx_op, pg, pb, pr, M, d); break;
+  case N: hipLaunchKernelGGL((ln_bwd_kernel<T, N, DROP>), grid, dim3(256), 0, s, dy, x, mean, rstd, g, dres, dx, (T*)dx_op, pg, pb, pr, M, d, da, si, so); break;
     LNB(1) LNB(2) LNB(3) LNB(4)
 #undef LNB
     default: return hipErrorInvalidValue;
@@ -293,10 +321,19 @@ static hipError_t ln_bwd_t(const float* dy, const float* x, const float* mean, c
 
 hipError_t launch_layernorm_bwd(const float* dy, const float* x, const float* mean, const float* rstd,
                                 const float* g, const float* dres, float* dx, void* dx_op, bool bf16_out,
-                                float* part_g, float* part_b, float* part_r, int M, int d, hipStream_t s) {
+                                float* part_g, float* part_b, float* part_r, int M, int d, const DropArgs& da,
+                                int site_in, int site_out, hipStream_t s) {
   if (d > LN_MAX_D || d % 4 != 0) return hipErrorInvalidValue;
-  if (bf16_out) return ln_bwd_t<bf16>(dy, x, mean, rstd, g, dres, dx, dx_op, part_g, part_b, part_r, M, d, s);
-  return ln_bwd_t<float>(dy, x, mean, rstd, g, dres, dx, dx_op, part_g, part_b, part_r, M, d, s);
+  const bool drop = da.on && (site_in >= 0 || site_out >= 0);
+  if (bf16_out)
+    return drop ? ln_bwd_t<bf16, true>(dy, x, mean, rstd, g, dres, dx, dx_op, part_g, part_b, part_r, M, d, da,
+                                       site_in, site_out, s)
+                : ln_bwd_t<bf16, false>(dy, x, mean, rstd, g, dres, dx, dx_op, part_g, part_b, part_r, M, d, da,
+                                        site_in, site_out, s);
+  return drop ? ln_bwd_t<float, true>(dy, x, mean, rstd, g, dres, dx, dx_op, part_g, part_b, part_r, M, d, da,
+                                      site_in, site_out, s)
+              : ln_bwd_t<float, false>(dy, x, mean, rstd, g, dres, dx, dx_op, part_g, part_b, part_r, M, d, da,
+                                       site_in, site_out, s);
 }
 
 // ----------------------------------------------------------------------------- column sums

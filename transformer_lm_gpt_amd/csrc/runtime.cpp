@@ -81,6 +81,9 @@ struct gpt_model {
   // d xmid_l, and per-layer du and dqkv, kept for the weight gradients that run
   // together at the end of the backward
   Slice rx, rm, wtable;
+  // fp32 mode with dropout: the masked copy of a residual-stream gradient that the
+  // branch below reads as its GEMM operand
+  Slice dxm;
   size_t layer_stride_du = 0, layer_stride_dqkv = 0, resid_stride = 0;   // bytes
   std::vector<WgradProblem> wprobs;   // host copy of the grouped weight-gradient table
   int wtiles = 0;
@@ -99,6 +102,11 @@ struct gpt_model {
   gpt_buffers buf{};
   bool bound = false;
   hipStream_t stream = nullptr;
+  // dropout: key, threshold and scale (drop.call unused), the next forward's
+  // counter, and the masks of the forward that the pending backward belongs to
+  DropArgs drop{};
+  uint32_t drop_call = 0;
+  DropArgs drop_fwd{};
   // state
   bool grads_fresh = true;
   bool fwd_pending = false;
@@ -293,6 +301,7 @@ void plan(gpt_model* h) {
   h->rm = w.take(h->bf16 ? L * M * d * ob : 0);
   h->dO = w.take(M * d * ob);
   h->dqkv = w.take(per_layer * M * 3 * d * ob);
+  h->dxm = w.take(!h->bf16 && h->cfg.dropout > 0.f ? M * d * fb : 0);
   h->attnD = w.take(bht * fb);
   const size_t ln_blk = (M + LN_BWD_ROWS - 1) / LN_BWD_ROWS;
   const size_t cs_blk = (M + COLSUM_ROWS - 1) / COLSUM_ROWS;
@@ -364,13 +373,17 @@ int colsum(gpt_model* h, const void* X, bool bf16_in, int64_t ldx, int M, int N,
 // LayerNorm backward into dres (in place when dres is given); writes the partial
 // column sums of the gain and shift gradients and, when `resid_bias` names a
 // tensor, of the incoming residual gradient (the bias gradient of that projection).
+// With dropout, site_in names the mask of the branch whose output was added into
+// this residual (its bias gradient sums the masked dres) and site_out the mask that
+// the operand copy dx_op carries (-1: none).
 int ln_bwd(gpt_model* h, const float* dy, const float* x, const float* mean, const float* rstd,
            const std::string& gname, const std::string& bname, const float* dres, const char* resid_bias, void* dx_op,
-           int M) {
+           int M, int site_in = -1, int site_out = -1) {
   float* pr = resid_bias ? red_part(h, resid_bias) : nullptr;
   RUN("layernorm", "layernorm_bwd",
       launch_layernorm_bwd(dy, x, mean, rstd, P(h, gname), dres, ws<float>(h, h->dres), dx_op, h->bf16,
-                           red_part(h, gname), red_part(h, bname), pr, M, h->d, h->stream));
+                           red_part(h, gname), red_part(h, bname), pr, M, h->d, h->drop_fwd, site_in, site_out,
+                           h->stream));
   return GPT_OK;
 }
 
@@ -425,13 +438,16 @@ int upload_tables(gpt_model* h) {
   return GPT_OK;
 }
 
-// Forward up to the logits for B x T tokens already copied into the arena.
-int forward_to_logits(gpt_model* h, int B, int T) {
+// Forward up to the logits for B x T tokens already copied into the arena, with
+// the dropout masks of `da` (da.on = 0: none).
+int forward_to_logits(gpt_model* h, int B, int T, const DropArgs& da) {
   const int d = h->d, M = B * T;
   const bool bf = h->bf16;
   hipStream_t s = h->stream;
   const int32_t* tok = act<int32_t>(h, h->tokens);
-  RUN("embed", "embed_fwd", launch_embed_fwd(P(h, "wte"), P(h, "wpe"), tok, act<float>(h, h->layers[0].x), M, T, d, h->Vp, s));
+  const int resid_epi = da.on ? EPI_BIAS_RESID_DROP : EPI_BIAS_RESID;
+  RUN("embed", "embed_fwd",
+      launch_embed_fwd(P(h, "wte"), P(h, "wpe"), tok, act<float>(h, h->layers[0].x), M, T, d, h->Vp, da, s));
   for (int l = 0; l < h->L; l++) {
     const LayerAct& la = h->layers[l];
     const std::string p = "h" + std::to_string(l) + ".";
@@ -447,13 +463,16 @@ int forward_to_logits(gpt_model* h, int B, int T) {
       g.bias = P(h, p + "attn.b");
       RUN("gemm_fwd", "qkv_fwd", gemm(h, g, bf));
     }
-    RUN("attn_fwd", "attn_fwd", launch_attn_fwd(act(h, la.qkv), act(h, la.att), act<float>(h, la.lse), bf, B, T, h->H, h->hd, s));
+    RUN("attn_fwd", "attn_fwd",
+        launch_attn_fwd(act(h, la.qkv), act(h, la.att), act<float>(h, la.lse), bf, B, T, h->H, h->hd, da,
+                        site_attn_prob(l), s));
     {
-      GemmDesc g = gemm_desc(act(h, la.att), d, true, Wop(h, p + "proj.w"), d, true, xmid, d, M, d, d,
-                             EPI_BIAS_RESID);
+      GemmDesc g = gemm_desc(act(h, la.att), d, true, Wop(h, p + "proj.w"), d, true, xmid, d, M, d, d, resid_epi);
       g.bias = P(h, p + "proj.b");
       g.resid = x;
       g.ldr = d;
+      g.drop = da;
+      g.drop_site = site_attn_out(l);
       RUN("gemm_fwd", "proj_fwd", gemm(h, g, bf));
     }
     RUN("layernorm", "ln2_fwd",
@@ -469,10 +488,12 @@ int forward_to_logits(gpt_model* h, int B, int T) {
     }
     {
       GemmDesc g = gemm_desc(act(h, la.h), 4 * d, true, Wop(h, p + "fcproj.w"), 4 * d, true, xnext, d, M, d,
-                             4 * d, EPI_BIAS_RESID);
+                             4 * d, resid_epi);
       g.bias = P(h, p + "fcproj.b");
       g.resid = xmid;
       g.ldr = d;
+      g.drop = da;
+      g.drop_site = site_mlp_out(l);
       RUN("gemm_fwd", "fcproj_fwd", gemm(h, g, bf));
     }
   }
@@ -524,7 +545,7 @@ int gpt_create(const gpt_config* cfg, gpt_model** out) {
   if (c.n_embd > 1024) return fail(nullptr, GPT_E_UNSUPPORTED, "n_embd above 1024 is not implemented");
   if (c.n_embd % 4 != 0) return fail(nullptr, GPT_E_UNSUPPORTED, "n_embd must be a multiple of 4");
   if (c.precision != GPT_PREC_FP32 && c.precision != GPT_PREC_BF16) return fail(nullptr, GPT_E_INVAL, "unknown precision");
-  if (c.dropout != 0.0f) return fail(nullptr, GPT_E_UNSUPPORTED, "dropout must be 0");
+  if (!(c.dropout >= 0.0f && c.dropout < 1.0f)) return fail(nullptr, GPT_E_INVAL, "dropout must be in [0, 1)");
   if (c.flags != 0) return fail(nullptr, GPT_E_INVAL, "flags must be 0");
   const int64_t M = (int64_t)c.batch * c.block_size;
   if (M > 32768) return fail(nullptr, GPT_E_UNSUPPORTED, "batch * block_size above 32768 is not implemented");
@@ -547,6 +568,10 @@ int gpt_create(const gpt_config* cfg, gpt_model** out) {
   h->Bmax = c.batch;
   h->A = c.grad_accum;
   h->op_size = h->bf16 ? 2 : 4;
+  // keep an element when its Philox word >= floor(p 2^32); scale kept ones by 1/(1-p)
+  h->drop.on = c.dropout > 0.0f ? 1 : 0;
+  h->drop.thr = (uint32_t)std::floor((double)c.dropout * 4294967296.0);
+  h->drop.scale = (float)(1.0 / (1.0 - (double)c.dropout));
   plan(h);
   *out = h;
   return GPT_OK;
@@ -633,7 +658,10 @@ int gpt_forward_loss(gpt_model* h, const int32_t* d_tokens, const int32_t* d_tar
   if ((rc = copy_ids(h, d_tokens, h->tokens, M))) return rc;
   if ((rc = copy_ids(h, d_targets, h->targets, M))) return rc;
   h->fwd_pending = false;
-  if ((rc = forward_to_logits(h, B, T))) return rc;
+  DropArgs da = h->drop;
+  da.call = h->drop_call++;                        // advances with or without dropout
+  h->drop_fwd = da;
+  if ((rc = forward_to_logits(h, B, T, da))) return rc;
   const float scale = (float)(1.0 / ((double)M * (double)h->A));
   RUN("xent", "xent", launch_xent(act(h, h->logits), h->bf16, h->ldz, act<int32_t>(h, h->targets),
                                    act<float>(h, h->row_loss), M, h->Vp, scale, h->stream));
@@ -652,7 +680,8 @@ int gpt_forward_logits(gpt_model* h, const int32_t* d_tokens, int32_t B, int32_t
   const int M = B * T;
   h->fwd_pending = false;
   if ((rc = copy_ids(h, d_tokens, h->tokens, M))) return rc;
-  if ((rc = forward_to_logits(h, B, T))) return rc;
+  const DropArgs none{};                           // inference: no dropout
+  if ((rc = forward_to_logits(h, B, T, none))) return rc;
   RUN("copy", "logits_to_f32",
       launch_rows_to_f32(act(h, h->logits), h->bf16, h->ldz, M, h->Vp, d_logits, h->stream));
   return GPT_OK;
@@ -674,6 +703,9 @@ int gpt_backward(gpt_model* h) {
   float* dres = ws<float>(h, h->dres);
   float* dln = ws<float>(h, h->dln);
   void* dO = ws(h, h->dO);
+  const DropArgs& da = h->drop_fwd;
+  const bool drop = da.on != 0;
+  float* dxm = drop && !bf ? ws<float>(h, h->dxm) : nullptr;   // fp32: masked operand copies
   // In bf16 mode the weight gradients wait for the end of the backward (their
   // operands stay in per-layer slots); in fp32 mode each runs as soon as its
   // operands exist, before the residual gradient is overwritten.
@@ -694,7 +726,8 @@ int gpt_backward(gpt_model* h) {
     RUN("gemm_dgrad", "lm_head_dgrad", gemm(h, g2, bf));
   }
   if ((rc = ln_bwd(h, dln, act<float>(h, h->x_final), act<float>(h, h->lnf_mean), act<float>(h, h->lnf_rstd),
-                   "lnf.g", "lnf.b", nullptr, nullptr, bf ? rx_slot(h, L) : nullptr, M)))
+                   "lnf.g", "lnf.b", nullptr, nullptr, bf ? rx_slot(h, L) : (void*)dxm, M, -1,
+                   (int)site_mlp_out(L - 1))))
     return rc;
 
   for (int l = L - 1; l >= 0; l--) {
@@ -702,9 +735,10 @@ int gpt_backward(gpt_model* h) {
     const std::string p = "h" + std::to_string(l) + ".";
     void* du = bf ? du_slot(h, l) : ws(h, h->du);
     void* dqkv = bf ? dqkv_slot(h, l) : ws(h, h->dqkv);
-    // ---- MLP: x_{l+1} = xmid + gelu(LN2(xmid) Wfc^T + bfc) Wp^T + bp ; dres holds d x_{l+1}
+    // ---- MLP: x_{l+1} = xmid + drop(gelu(LN2(xmid) Wfc^T + bfc) Wp^T + bp) ; dres holds d x_{l+1}
     {
-      const void* dx = bf ? rx_slot(h, l + 1) : (const void*)dres;   // GEMM operand view of d x_{l+1}
+      // GEMM operand view of d x_{l+1} (times the MLP output mask with dropout)
+      const void* dx = bf ? rx_slot(h, l + 1) : (dxm ? (const void*)dxm : (const void*)dres);
       GemmDesc g = bf ? gemm_desc(dx, d, true, WopT(h, p + "fcproj.w"), d, true, du, 4 * d, M, 4 * d, d, EPI_GELU_BWD)
                       : gemm_desc(dx, d, true, Wop(h, p + "fcproj.w"), 4 * d, false, du, 4 * d, M, 4 * d, d,
                                   EPI_GELU_BWD);
@@ -722,12 +756,14 @@ int gpt_backward(gpt_model* h) {
       if (!fc_rows && (rc = colsum(h, du, bf, 4 * d, M, 4 * d, p + "fc.b"))) return rc;
       const std::string fcproj_b = p + "fcproj.b";
       if ((rc = ln_bwd(h, dln, act<float>(h, la.xmid), act<float>(h, la.ln2_mean), act<float>(h, la.ln2_rstd),
-                       p + "ln2.g", p + "ln2.b", dres, fcproj_b.c_str(), bf ? rm_slot(h, l) : nullptr, M)))
+                       p + "ln2.g", p + "ln2.b", dres, fcproj_b.c_str(), bf ? rm_slot(h, l) : (void*)dxm, M,
+                       (int)site_mlp_out(l), (int)site_attn_out(l))))
         return rc;
     }
-    // ---- attention: xmid = x + attn(LN1(x)) Wo^T + bo ; dres now holds d xmid
+    // ---- attention: xmid = x + drop(attn(LN1(x)) Wo^T + bo) ; dres now holds d xmid
     {
-      const void* dx = bf ? rm_slot(h, l) : (const void*)dres;       // GEMM operand view of d xmid
+      // GEMM operand view of d xmid (times the attention output mask with dropout)
+      const void* dx = bf ? rm_slot(h, l) : (dxm ? (const void*)dxm : (const void*)dres);
       GemmDesc g = bf ? gemm_desc(dx, d, true, WopT(h, p + "proj.w"), d, true, dO, d, M, d, d, EPI_STORE)
                       : gemm_desc(dx, d, true, Wop(h, p + "proj.w"), d, false, dO, d, M, d, d, EPI_STORE);
       RUN("gemm_dgrad", "proj_dgrad", gemm(h, g, bf));
@@ -736,7 +772,8 @@ int gpt_backward(gpt_model* h) {
       rows.nblk[RED_QKV] = qkv_rows ? qkv_rows : (M + COLSUM_ROWS - 1) / COLSUM_ROWS;
       RUN("attn_bwd", "attn_bwd",
           launch_attn_bwd(act(h, la.qkv), act(h, la.att), dO, act<float>(h, la.lse), ws<float>(h, h->attnD), dqkv, bf,
-                          B, T, h->H, h->hd, qkv_rows ? red_part(h, p + "attn.b") : nullptr, s));
+                          B, T, h->H, h->hd, qkv_rows ? red_part(h, p + "attn.b") : nullptr, da,
+                          site_attn_prob(l), s));
       GemmDesc g2 = bf ? gemm_desc(dqkv, 3 * d, true, WopT(h, p + "attn.w"), 3 * d, true, dln, d, M, d, 3 * d, EPI_F32)
                        : gemm_desc(dqkv, 3 * d, true, Wop(h, p + "attn.w"), d, false, dln, d, M, d, 3 * d, EPI_F32);
       RUN("gemm_dgrad", "qkv_dgrad", gemm(h, g2, bf));
@@ -744,8 +781,10 @@ int gpt_backward(gpt_model* h) {
       if (!qkv_rows && (rc = colsum(h, dqkv, bf, 3 * d, M, 3 * d, p + "attn.b"))) return rc;
       const std::string proj_b = p + "proj.b";
       // d x_0 feeds only the embedding backward, which reads the fp32 copy
+      void* xop = l == 0 ? nullptr : (bf ? rx_slot(h, l) : (void*)dxm);
       if ((rc = ln_bwd(h, dln, act<float>(h, la.x), act<float>(h, la.ln1_mean), act<float>(h, la.ln1_rstd),
-                       p + "ln1.g", p + "ln1.b", dres, proj_b.c_str(), bf && l > 0 ? rx_slot(h, l) : nullptr, M)))
+                       p + "ln1.g", p + "ln1.b", dres, proj_b.c_str(), xop, M, (int)site_attn_out(l),
+                       l > 0 ? (int)site_mlp_out(l - 1) : -1)))
         return rc;
     }
   }
@@ -772,11 +811,21 @@ int gpt_backward(gpt_model* h) {
     float* wpe_tail = G(h, "wpe") + (size_t)T * d;
     RUN("embed", "zero wpe tail", launch_zero(wpe_tail, (size_t)(h->Tmax - T) * d, s));
   }
+  if (drop)   // x0 = drop(wte[tok] + wpe): the tables see d x0 times the embedding mask
+    RUN("embed", "embed_dropout", launch_dropout_rows(dres, dres, M, d, da, site_embed(), s));
   EmbedBwdScratch scr{ws<uint32_t>(h, h->emb_keys), ws<float>(h, h->emb_piece)};
   RUN("embed", "embed_bwd",
       launch_embed_bwd(dres, act<int32_t>(h, h->tokens), G(h, "wte"), G(h, "wpe"), beta, B, T, d, h->Vp, scr, s));
   h->grads_fresh = false;
   h->fwd_pending = false;
+  return GPT_OK;
+}
+
+int gpt_set_dropout_seed(gpt_model* h, uint64_t seed, uint32_t counter) {
+  if (!h) return GPT_E_INVAL;
+  h->drop.k0 = (uint32_t)(seed & 0xFFFFFFFFu);
+  h->drop.k1 = (uint32_t)(seed >> 32);
+  h->drop_call = counter;
   return GPT_OK;
 }
 
