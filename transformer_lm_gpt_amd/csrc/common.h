@@ -112,12 +112,12 @@ __device__ inline u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uin
       k0 += 0x9E3779B9u;
       k1 += 0xBB67AE85u;
     }
-    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
-    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
-    c0 = hi1 ^ c1 ^ k0;
-    c2 = hi0 ^ c3 ^ k1;
-    c1 = lo1;
-    c3 = lo0;
+    // one v_mad_u64_u32 per product instead of a mul_lo / mul_hi pair
+    const uint64_t p0 = (uint64_t)c0 * 0xD2511F53ull, p1 = (uint64_t)c2 * 0xCD9E8D57ull;
+    c0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    c2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
   }
   return (u32x4){c0, c1, c2, c3};
 }
