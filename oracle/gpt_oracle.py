@@ -34,6 +34,12 @@ What it computes, and the passage each part follows (the nanoGPT pages):
     numbers: as easy as 1, 2, 3", SC 2011), keyed by a 64-bit seed; see
     ``dropout_keep`` for which counter names which element.
 
+  * generation (nanoGPT practical guide on adg.csdn.net, section 4; the microGPT
+    page's single-GPU inference section): logits divided by a temperature, an
+    optional top-k cut, a draw from the softmax, one token appended at a time.
+    ``generate`` recomputes the whole forward for every new token: that is the
+    definition a decoder with a key/value cache has to reproduce.
+
 Readings where the pages are silent: LayerNorm eps 1e-5 with the biased
 variance; attention scale 1/sqrt(head_dim); the softmax runs over all padded
 vocabulary columns; the clip coefficient is min(1, clip / (norm + 1e-6)) and
@@ -478,3 +484,49 @@ class Trainer:
                      coef, self.decay)
         return {"losses": losses, "loss": float(np.mean(losses)), "grads": grads,
                 "norm": norm, "coef": coef}
+
+
+# --------------------------------------------------------------------------- generation
+
+def sample_token(z, temperature: float, top_k: int, u: float) -> int:
+    """One next token from a row of logits z [V] and a uniform u in [0, 1).
+
+    temperature <= 0: the argmax, lowest index on ties. Otherwise the candidates
+    are the logits >= the k-th largest value (all V when top_k <= 0 or >= V; ties
+    at the cut stay in, as nanoGPT's sampler keeps them), weighted by
+    exp((z_i - max z) / temperature); the token is the smallest index whose
+    cumulative weight, summed in index order, exceeds u times the total.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    if temperature <= 0.0:
+        return int(np.argmax(z))
+    V = z.shape[0]
+    cand = np.ones(V, dtype=bool)
+    if 0 < top_k < V:
+        kth = np.sort(z)[V - top_k]
+        cand = z >= kth
+    w = np.where(cand, np.exp((z - z.max()) / temperature), 0.0)
+    c = np.cumsum(w)
+    return int(np.searchsorted(c, u * c[-1], side="right"))
+
+
+def generate(params, prompt, cfg, n_new: int, temperature: float, top_k: int, uniforms,
+             dtype=np.float64):
+    """Autoregressive generation by full recomputation, no cache.
+
+    prompt: int [B, T0]; uniforms: [n_new, B] in [0, 1). Returns the tokens
+    [B, T0 + n_new] and the logits of every generated position [n_new, B, Vp]
+    (the last row of the forward over the sequence so far).
+    """
+    P = _as(params, dtype)
+    seqs = [list(map(int, r)) for r in np.asarray(prompt)]
+    zs = []
+    for s in range(n_new):
+        row = []
+        for b, seq in enumerate(seqs):
+            z, _ = forward_sequence(P, np.asarray(seq), cfg)
+            row.append(z[-1])
+            seq.append(sample_token(z[-1], temperature, top_k, float(uniforms[s][b])))
+        zs.append(np.stack(row))
+    return np.asarray(seqs), np.stack(zs)
+

@@ -388,6 +388,61 @@ def test_dropout_changes_loss_and_advances_counter():
     assert np.array_equal(l1, l1b)
 
 
+# --------------------------------------------------------------------------- sampling
+
+def test_sample_two_logit_closed_form():
+    """z = (0, ln 3): softmax (1/4, 3/4) at temperature 1 and (1/10, 9/10) at 1/2."""
+    z = np.array([0.0, math.log(3.0)])
+    assert O.sample_token(z, 1.0, 0, 0.2) == 0 and O.sample_token(z, 1.0, 0, 0.3) == 1
+    assert O.sample_token(z, 0.5, 0, 0.05) == 0 and O.sample_token(z, 0.5, 0, 0.15) == 1
+    assert O.sample_token(z, 1.0, 0, 0.0) == 0 and O.sample_token(z, 1.0, 0, 0.999999) == 1
+
+
+def test_sample_greedy_and_top1_are_argmax():
+    rng = np.random.default_rng(8)
+    for _ in range(50):
+        z = rng.normal(size=97) * 3
+        a = int(np.argmax(z))
+        assert O.sample_token(z, 0.0, 0, 0.7) == a
+        assert O.sample_token(z, 1.3, 1, float(rng.random())) == a
+    assert O.sample_token(np.array([1.0, 5.0, 5.0, 2.0]), 0.0, 0, 0.5) == 1     # lowest index on ties
+
+
+def test_sample_stratified_frequencies_match_softmax():
+    """With stratified uniforms the token frequencies equal the probabilities of
+    softmax(z / T) restricted to the top-k logits, up to the 1/N stratum width."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(9)
+    z = rng.normal(size=40) * 2
+    N = 20000
+    for temp, k in ((1.0, 0), (0.7, 10), (2.0, 3)):
+        cnt = np.zeros(40)
+        for i in range(N):
+            cnt[O.sample_token(z, temp, k, (i + 0.5) / N)] += 1
+        keep = np.argsort(-z)[:k] if k else np.arange(40)
+        p = np.zeros(40)
+        p[keep] = softmax(z[keep] / temp)
+        assert np.abs(cnt / N - p).max() <= 1.0 / N + 1e-12
+        assert np.all(cnt[np.setdiff1d(np.arange(40), keep)] == 0)
+
+
+def test_sample_top_k_keeps_ties_at_the_cut():
+    z = np.array([1.0, 2.0, 2.0, 0.0])
+    picked = {O.sample_token(z, 1.0, 1, u) for u in (0.1, 0.9)}
+    assert picked == {1, 2}
+
+
+def test_generate_greedy_is_argmax_of_full_forward():
+    c, params, tok, _ = _setup("tiny", perturb=True)
+    prompt = tok[:2, :5]
+    seqs, zs = O.generate(params, prompt, c, 4, 0.0, 0, np.zeros((4, 2)))
+    assert seqs.shape == (2, 9) and np.array_equal(seqs[:, :5], prompt)
+    for s in range(4):
+        z_full = O.logits(params, seqs[:, :5 + s], c)[:, -1]
+        np.testing.assert_allclose(zs[s], z_full, rtol=1e-12, atol=1e-12)
+        assert np.array_equal(seqs[:, 5 + s], np.argmax(z_full, axis=-1))
+
+
 def test_grad_accumulation_equals_big_batch():
     c, params, tok, tgt = _setup("char_small", perturb=True, B=4, T=16)
     _, g_big = O.accumulate_grads(params, [(tok, tgt)], c)
