@@ -59,6 +59,8 @@ extern "C" {
 #define GPT_E_NONFINITE    -6  /* non-finite loss or gradient norm: update skipped   */
 
 #define GPT_PREC_FP32 0        /* every GEMM operand fp32                            */
+#define GPT_F_KV_CACHE 1u      /* gpt_config.flags: reserve the key/value cache of
+                                  gpt_prefill / gpt_decode in the workspace           */
 #define GPT_PREC_BF16 1        /* GEMM/attention operands bf16, everything else fp32 */
 
 typedef struct gpt_model gpt_model;
@@ -74,7 +76,7 @@ typedef struct gpt_config {
   int32_t grad_accum;    /* A: backward scales the micro-batch mean loss by 1/A     */
   int32_t precision;     /* GPT_PREC_FP32 or GPT_PREC_BF16                          */
   float   dropout;       /* p in [0, 1): see gpt_set_dropout_seed                   */
-  uint32_t flags;        /* reserved, must be 0                                     */
+  uint32_t flags;        /* 0 or GPT_F_KV_CACHE                                     */
 } gpt_config;
 
 typedef struct gpt_sizes {
@@ -161,6 +163,33 @@ int gpt_set_dropout_seed(gpt_model* h, uint64_t seed, uint32_t counter);
  * forward_loss is pending; it invalidates it otherwise. */
 int gpt_forward_logits(gpt_model* h, const int32_t* d_tokens, int32_t B, int32_t T,
                        float* d_logits);
+
+/* Generation with a key/value cache ("GPT training and inference from scratch
+ * with nanoGPT" (adg.csdn.net), section 4: sampling with temperature and top_k;
+ * "Building microGPT from scratch", single-GPU inference section: the cache
+ * grows by one position per generated token). Needs GPT_F_KV_CACHE at create;
+ * the cache holds every layer's keys and values for batch x block_size
+ * positions in the workspace. No dropout. A pending backward is invalidated.
+ *
+ * gpt_prefill: forward over prompts d_tokens int32 [B, T] (device); keeps the
+ * keys and values of positions 0..T-1 and writes the fp32 logits of position
+ * T-1 of every sequence to d_logits [B, padded_vocab]. Resets the cache.
+ * gpt_decode: one token per sequence, d_tokens int32 [B] with the B of the
+ * last prefill, at the next position; appends its keys and values and writes
+ * fp32 logits [B, padded_vocab]. The logits equal the last row of a full
+ * forward over the sequence so far (up to rounding). GPT_E_STATE without a
+ * prefill, GPT_E_SEQ_TOO_LONG once block_size positions are cached.
+ * gpt_sample: one token per row of fp32 logits [B, padded_vocab] into
+ * d_tokens_out int32 [B]. temperature <= 0: the argmax, lowest index on ties
+ * (d_uniform may be NULL). Otherwise the candidates are the logits >= the
+ * top_k-th largest (every column when top_k <= 0 or >= padded_vocab; ties at
+ * the cut stay in), weighted by exp((z - max z) / temperature), and the token
+ * is the first index whose running weight, summed in index order, exceeds
+ * d_uniform[b] (in [0, 1)) times the total. */
+int gpt_prefill(gpt_model* h, const int32_t* d_tokens, int32_t B, int32_t T, float* d_logits);
+int gpt_decode(gpt_model* h, const int32_t* d_tokens, float* d_logits);
+int gpt_sample(gpt_model* h, const float* d_logits, int32_t B, float temperature, int32_t top_k,
+               const float* d_uniform, int32_t* d_tokens_out);
 
 /* Backward of the last gpt_forward_loss. Adds d(loss / grad_accum) into the
  * gradients; the first backward after gpt_init_state, gpt_zero_grad or

@@ -78,7 +78,7 @@ def _raw(**kw):
     (dict(n_head=0), -1),
     (dict(padded_vocab=10), -1),           # below vocab_size
     (dict(precision=7), -1),
-    (dict(flags=1), -1),
+    (dict(flags=2), -1),                   # unknown flag
     (dict(dropout=1.0), -1),               # dropout must be in [0, 1)
     (dict(dropout=-0.1), -1),
     (dict(dropout=float("nan")), -1),
@@ -138,3 +138,20 @@ def test_dropout_config_and_seed_are_host_only():
     finally:
         lay.close()
         plain.close()
+
+
+def test_kv_cache_flag_reserves_the_cache():
+    """GPT_F_KV_CACHE adds n_layer arrays of [batch * block_size, 2 n_embd] operand
+    elements to the workspace, and nothing else."""
+    c = W.CONFIGS["char_small"]
+    for prec, ob in (("fp32", 4), ("bf16", 2)):
+        plain = Bd.Layout(c, prec)
+        kv = Bd.Layout(c, prec, kv_cache=True)
+        try:
+            grow = kv.sizes.workspace_bytes - plain.sizes.workspace_bytes
+            want = c.n_layer * c.batch * c.block_size * 2 * c.n_embd * ob
+            assert want <= grow <= want + 256
+            assert kv.sizes.activation_bytes == plain.sizes.activation_bytes
+        finally:
+            kv.close()
+            plain.close()

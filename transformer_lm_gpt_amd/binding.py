@@ -26,6 +26,7 @@ PREC = {"fp32": 0, "bf16": 1}
 EXPORTS = ["gpt_create", "gpt_destroy", "gpt_last_error", "gpt_get_sizes", "gpt_num_tensors",
            "gpt_tensor_info_at", "gpt_bind", "gpt_init_state", "gpt_forward_loss", "gpt_forward_logits",
            "gpt_backward", "gpt_zero_grad", "gpt_set_dropout_seed", "gpt_adamw_step", "gpt_sync", "gpt_get_step",
+           "gpt_prefill", "gpt_decode", "gpt_sample",
            "gpt_debug_copy", "gpt_timer_enable", "gpt_timer_disable", "gpt_timer_read"]
 
 
@@ -81,6 +82,9 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         "gpt_backward": (C.c_int, [vp]),
         "gpt_zero_grad": (C.c_int, [vp]),
         "gpt_set_dropout_seed": (C.c_int, [vp, C.c_uint64, C.c_uint32]),
+        "gpt_prefill": (C.c_int, [vp, vp, i32, i32, vp]),
+        "gpt_decode": (C.c_int, [vp, vp, vp]),
+        "gpt_sample": (C.c_int, [vp, vp, i32, f32, i32, vp, vp]),
         "gpt_adamw_step": (C.c_int, [vp, f32, f32, f32, f32, f32, f32, vp]),
         "gpt_sync": (C.c_int, [vp]),
         "gpt_get_step": (C.c_int, [vp, C.POINTER(C.c_int64)]),
@@ -97,22 +101,27 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     return lib
 
 
+F_KV_CACHE = 1
+
+
 def make_config(cfg, precision: str, batch: Optional[int] = None, grad_accum: Optional[int] = None,
-                dropout: float = 0.0) -> gpt_config:
+                dropout: float = 0.0, kv_cache: bool = False) -> gpt_config:
     return gpt_config(cfg.vocab_size, cfg.padded_vocab, cfg.n_layer, cfg.n_head, cfg.n_embd, cfg.block_size,
                       cfg.batch if batch is None else batch,
-                      cfg.grad_accum if grad_accum is None else grad_accum, PREC[precision], float(dropout), 0)
+                      cfg.grad_accum if grad_accum is None else grad_accum, PREC[precision], float(dropout),
+                      F_KV_CACHE if kv_cache else 0)
 
 
 class Layout:
     """Host-side view of a configuration: sizes and the flat tensor table. Needs no GPU."""
 
     def __init__(self, cfg, precision: str = "bf16", batch: Optional[int] = None,
-                 grad_accum: Optional[int] = None, raw: Optional[gpt_config] = None, dropout: float = 0.0):
+                 grad_accum: Optional[int] = None, raw: Optional[gpt_config] = None, dropout: float = 0.0,
+                 kv_cache: bool = False):
         self.lib = load_library()
         self.cfg = cfg
         self.precision = precision
-        self.raw = raw if raw is not None else make_config(cfg, precision, batch, grad_accum, dropout)
+        self.raw = raw if raw is not None else make_config(cfg, precision, batch, grad_accum, dropout, kv_cache)
         h = C.c_void_p()
         rc = self.lib.gpt_create(C.byref(self.raw), C.byref(h))
         if rc != GPT_OK:
@@ -161,9 +170,10 @@ class GPT(Layout):
     """One model bound to device buffers on the current torch device and stream."""
 
     def __init__(self, cfg, precision: str = "bf16", batch: Optional[int] = None,
-                 grad_accum: Optional[int] = None, device: str = "cuda", dropout: float = 0.0):
+                 grad_accum: Optional[int] = None, device: str = "cuda", dropout: float = 0.0,
+                 kv_cache: bool = False):
         import torch
-        super().__init__(cfg, precision, batch, grad_accum, dropout=dropout)
+        super().__init__(cfg, precision, batch, grad_accum, dropout=dropout, kv_cache=kv_cache)
         self.torch = torch
         self.device = torch.device(device)
         s = self.sizes
@@ -234,6 +244,36 @@ class GPT(Layout):
 
     def backward(self):
         self._check(self.lib.gpt_backward(self.h))
+
+    # ---- generation with the key/value cache
+    def prefill(self, tokens):
+        tok = self._ids(tokens)
+        B, T = tok.shape
+        out = self.torch.empty((B, self.cfg.padded_vocab), dtype=self.torch.float32, device=self.device)
+        self._keep_dec = tok
+        self._check(self.lib.gpt_prefill(self.h, C.c_void_p(tok.data_ptr()), B, T, C.c_void_p(out.data_ptr())))
+        return out
+
+    def decode(self, tokens):
+        tok = self._ids(tokens).reshape(-1)
+        out = self.torch.empty((tok.numel(), self.cfg.padded_vocab), dtype=self.torch.float32, device=self.device)
+        self._keep_dec = tok
+        self._check(self.lib.gpt_decode(self.h, C.c_void_p(tok.data_ptr()), C.c_void_p(out.data_ptr())))
+        return out
+
+    def sample(self, logits, temperature: float, top_k: int = 0, uniforms=None):
+        t = self.torch
+        z = logits.to(self.device, t.float32).contiguous()
+        B = z.shape[0]
+        u = None
+        if uniforms is not None:
+            u = t.as_tensor(np.asarray(uniforms, dtype=np.float32)).to(self.device).contiguous()
+        out = t.empty(B, dtype=t.int32, device=self.device)
+        self._keep_dec = (z, u)
+        self._check(self.lib.gpt_sample(self.h, C.c_void_p(z.data_ptr()), B, float(temperature), int(top_k),
+                                        C.c_void_p(u.data_ptr()) if u is not None else None,
+                                        C.c_void_p(out.data_ptr())))
+        return out
 
     def set_dropout_seed(self, seed: int, counter: int = 0):
         self._check(self.lib.gpt_set_dropout_seed(self.h, int(seed) & 0xFFFFFFFFFFFFFFFF, int(counter) & 0xFFFFFFFF))

@@ -1,0 +1,287 @@
+// Inference with a key/value cache: one new token per sequence against the keys
+// and values of every earlier position ("GPT training and inference from scratch
+// with nanoGPT", section 4; the microGPT page's single-GPU inference section: the
+// cache grows by one position per generated token), and the token draw
+// (temperature, top-k cut, softmax, one uniform per row).
+//
+// Cache layout: per layer [B_max * T_max, 2 * d] in operand type, row b * T_max + t,
+// keys in columns [0, d) and values in [d, 2d), head h at columns h * hd of each.
+#include "common.h"
+#include "kernels.h"
+
+namespace gpt {
+
+// x[b, :] = wte[tok[b], :] + wpe[pos, :] (NaN for an id outside the table).
+__global__ void embed_pos_kernel(const float* __restrict__ wte, const float* __restrict__ wpe,
+                                 const int32_t* __restrict__ tok, float* __restrict__ x, int B, int d, int Vp,
+                                 int pos) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B * d) return;
+  const int b = i / d, c = i % d;
+  const int id = tok[b];
+  x[i] = (id >= 0 && id < Vp) ? wte[(int64_t)id * d + c] + wpe[(int64_t)pos * d + c] : __builtin_nanf("");
+}
+
+hipError_t launch_embed_pos(const float* wte, const float* wpe, const int32_t* tok, float* x, int B, int d, int Vp,
+                            int pos, hipStream_t s) {
+  const int n = B * d;
+  hipLaunchKernelGGL(embed_pos_kernel, dim3((n + 255) / 256), dim3(256), 0, s, wte, wpe, tok, x, B, d, Vp, pos);
+  return hipGetLastError();
+}
+
+// cache[b * Tmax + pos0 + t, c] = qkv[b * T + t, d + c] for c < 2d: the keys and values
+// of T new positions of every sequence.
+template <typename T>
+__global__ void kv_append_kernel(const T* __restrict__ qkv, T* __restrict__ cache, int B, int Tn, int Tmax,
+                                 int pos0, int d) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_row = 2 * (int64_t)d;
+  if (i >= (int64_t)B * Tn * per_row) return;
+  const int64_t r = i / per_row;
+  const int c = (int)(i % per_row);
+  const int b = (int)(r / Tn), t = (int)(r % Tn);
+  cache[((int64_t)b * Tmax + pos0 + t) * per_row + c] = qkv[r * 3 * d + d + c];
+}
+
+hipError_t launch_kv_append(const void* qkv, bool bf16_ops, void* cache, int B, int T, int Tmax, int pos0, int d,
+                            hipStream_t s) {
+  if (pos0 < 0 || pos0 + T > Tmax) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)B * T * 2 * d;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (bf16_ops)
+    hipLaunchKernelGGL(kv_append_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)qkv, (bf16*)cache, B, T, Tmax,
+                       pos0, d);
+  else
+    hipLaunchKernelGGL(kv_append_kernel<float>, grid, dim3(256), 0, s, (const float*)qkv, (float*)cache, B, T,
+                       Tmax, pos0, d);
+  return hipGetLastError();
+}
+
+// One query per (sequence, head) against keys 0 .. len-1 of the cache:
+// s_j = q . k_j / sqrt(hd), p = softmax(s), o = sum_j p_j v_j. One workgroup of 256
+// per (b, h); the scores of all keys sit in LDS (len <= DEC_MAX_T). The value sum
+// gives each wavefront every fourth key, a lane per head column, and the four
+// partial vectors are added in a fixed order.
+constexpr int DEC_MAX_T = 8192;
+template <typename T>
+__global__ __launch_bounds__(256) void attn_decode_kernel(const T* __restrict__ qkv, const T* __restrict__ cache,
+                                                          T* __restrict__ out, int H, int hd, int Tmax, int len,
+                                                          float scale) {
+  __shared__ float sc[DEC_MAX_T];
+  __shared__ float qs[64];
+  __shared__ float red[4][64];
+  const int b = blockIdx.x / H, h = blockIdx.x % H;
+  const int d = H * hd;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid < hd) qs[tid] = to_f32(qkv[(int64_t)b * 3 * d + h * hd + tid]);
+  __syncthreads();
+  const T* kb = cache + (int64_t)b * Tmax * 2 * d + h * hd;
+  float mx = -INFINITY;
+  for (int j = tid; j < len; j += 256) {
+    const T* kr = kb + (int64_t)j * 2 * d;
+    float s = 0.f;
+    for (int c = 0; c < hd; c++) s += qs[c] * to_f32(kr[c]);
+    s *= scale;
+    sc[j] = s;
+    mx = fmaxf(mx, s);
+  }
+  mx = wave_max(mx);
+  if (lane == 0) red[0][w] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+  __syncthreads();
+  float sum = 0.f;
+  for (int j = tid; j < len; j += 256) {
+    const float p = __expf(sc[j] - mx);
+    sc[j] = p;
+    sum += p;
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) red[0][w] = sum;
+  __syncthreads();
+  sum = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+  __syncthreads();
+  float o = 0.f;
+  if (lane < hd) {
+    const T* vb = kb + d + lane;
+    for (int j = w; j < len; j += 4) o += sc[j] * to_f32(vb[(int64_t)j * 2 * d]);
+  }
+  red[w][lane] = o;
+  __syncthreads();
+  if (tid < hd) {
+    const float t = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+    out[(int64_t)b * d + h * hd + tid] = from_f32<T>(t / sum);
+  }
+}
+
+hipError_t launch_attn_decode(const void* qkv, const void* cache, void* out, bool bf16_ops, int B, int H, int hd,
+                              int Tmax, int len, hipStream_t s) {
+  if (hd <= 0 || hd > 64 || len < 1 || len > Tmax || len > DEC_MAX_T) return hipErrorInvalidValue;
+  const float scale = 1.0f / sqrtf((float)hd);
+  if (bf16_ops)
+    hipLaunchKernelGGL(attn_decode_kernel<bf16>, dim3(B * H), dim3(256), 0, s, (const bf16*)qkv, (const bf16*)cache,
+                       (bf16*)out, H, hd, Tmax, len, scale);
+  else
+    hipLaunchKernelGGL(attn_decode_kernel<float>, dim3(B * H), dim3(256), 0, s, (const float*)qkv,
+                       (const float*)cache, (float*)out, H, hd, Tmax, len, scale);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- sampling
+// One workgroup of 1024 per row. temperature <= 0: the argmax, lowest index on ties.
+// Otherwise: the candidates are the logits >= the k-th largest (found exactly by a
+// four-pass radix select on order-preserving integer keys; all V when top_k <= 0 or
+// >= V), weighted by exp((z - max) / temperature); each thread owns a contiguous run
+// of indices, the runs' sums are scanned in thread order, and the token is the first
+// index whose running sum exceeds u times the total.
+constexpr int SAMPLE_THREADS = 1024;
+
+__device__ inline uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);   // ascending floats -> ascending keys
+}
+
+__global__ __launch_bounds__(SAMPLE_THREADS) void sample_kernel(const float* __restrict__ logits, int64_t ld, int V,
+                                                                float temperature, int top_k,
+                                                                const float* __restrict__ uniform,
+                                                                int32_t* __restrict__ out) {
+  __shared__ uint32_t hist[256];
+  __shared__ float fred[SAMPLE_THREADS / 64];
+  __shared__ int ired[SAMPLE_THREADS / 64];
+  __shared__ uint32_t sel[2];   // prefix of the k-th key, count still needed
+  __shared__ int answer;   // the thread whose run holds the draw
+  const float* z = logits + (int64_t)blockIdx.x * ld;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int NW = SAMPLE_THREADS / 64;
+
+  // maximum, with its lowest index
+  float mx = -INFINITY;
+  int mi = 0x7fffffff;
+  for (int i = tid; i < V; i += SAMPLE_THREADS) {
+    const float v = z[i];
+    if (v > mx) {
+      mx = v;
+      mi = i;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float v2 = __shfl_xor(mx, o, 64);
+    const int i2 = __shfl_xor(mi, o, 64);
+    if (v2 > mx || (v2 == mx && i2 < mi)) {
+      mx = v2;
+      mi = i2;
+    }
+  }
+  if (lane == 0) {
+    fred[w] = mx;
+    ired[w] = mi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float m = fred[0];
+    int k = ired[0];
+    for (int q = 1; q < NW; q++)
+      if (fred[q] > m || (fred[q] == m && ired[q] < k)) {
+        m = fred[q];
+        k = ired[q];
+      }
+    fred[0] = m;
+    ired[0] = k;
+  }
+  __syncthreads();
+  mx = fred[0];
+  if (temperature <= 0.f) {
+    if (tid == 0) out[blockIdx.x] = ired[0];
+    return;
+  }
+
+  // k-th largest key (radix select, most significant byte first)
+  uint32_t kth = 0;                                   // keys >= kth are candidates
+  if (top_k > 0 && top_k < V) {
+    if (tid == 0) {
+      sel[0] = 0;
+      sel[1] = (uint32_t)top_k;
+    }
+    for (int pass = 0; pass < 4; pass++) {
+      const int shift = 24 - 8 * pass;
+      if (tid < 256) hist[tid] = 0;
+      __syncthreads();
+      const uint32_t prefix = sel[0];
+      const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+      for (int i = tid; i < V; i += SAMPLE_THREADS) {
+        const uint32_t key = order_key(z[i]);
+        if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t need = sel[1];
+        int bin = 255;
+        for (; bin > 0; bin--) {                      // from the largest bin down
+          if (hist[bin] >= need) break;
+          need -= hist[bin];
+        }
+        sel[0] = prefix | ((uint32_t)bin << shift);
+        sel[1] = need;
+      }
+      __syncthreads();
+    }
+    kth = sel[0];
+  }
+
+  // weights, per-thread runs and their scan in thread order
+  const float inv_t = 1.0f / temperature;
+  const int per = (V + SAMPLE_THREADS - 1) / SAMPLE_THREADS;
+  const int i0 = tid * per, i1 = min(V, i0 + per);
+  float run = 0.f;
+  for (int i = i0; i < i1; i++) {
+    const float v = z[i];
+    if (order_key(v) >= kth) run += __expf((v - mx) * inv_t);
+  }
+  if (tid == 0) answer = -1;
+  __syncthreads();
+  // inclusive scan over the 1024 run sums: each wave scans 64, then the wave totals
+  float incl = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) fred[w] = incl;
+  __syncthreads();
+  float before = 0.f;
+  for (int q = 0; q < w; q++) before += fred[q];
+  float total = 0.f;
+  for (int q = 0; q < NW; q++) total += fred[q];
+  const float start = before + incl - run;           // sum of every earlier run
+  const float target = uniform[blockIdx.x] * total;
+  // the run holding the target is the last non-empty one that starts at or before it
+  if (run > 0.f && start <= target) atomicMax(&answer, tid);
+  __syncthreads();
+  if (tid == answer) {
+    float acc = start;
+    int pick = -1, last = -1;
+    for (int i = i0; i < i1; i++) {
+      const float v = z[i];
+      if (order_key(v) >= kth) {
+        last = i;
+        acc += __expf((v - mx) * inv_t);
+        if (acc > target) {
+          pick = i;
+          break;
+        }
+      }
+    }
+    out[blockIdx.x] = pick >= 0 ? pick : last;        // rounding can leave the target past the run's sum
+  }
+}
+
+hipError_t launch_sample(const float* logits, int64_t ld, int B, int V, float temperature, int top_k,
+                         const float* uniform, int32_t* out, hipStream_t s) {
+  if (B < 1 || V < 1 || ld < V) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sample_kernel, dim3(B), dim3(SAMPLE_THREADS), 0, s, logits, ld, V, temperature, top_k, uniform,
+                     out);
+  return hipGetLastError();
+}
+
+}  // namespace gpt

@@ -179,6 +179,25 @@ int embed_bwd_sort_size(int M);   // power of two >= M
 hipError_t launch_embed_bwd(const float* dx0, const int32_t* tok, float* dwte, float* dwpe, float beta_wpe,
                             int B, int T, int d, int Vp, EmbedBwdScratch scr, hipStream_t s);
 
+// ---- inference with a key/value cache (decode.hip)
+// x[b, :] = wte[tok[b], :] + wpe[pos, :] for B single-token rows.
+hipError_t launch_embed_pos(const float* wte, const float* wpe, const int32_t* tok, float* x, int B, int d, int Vp,
+                            int pos, hipStream_t s);
+// Copies the keys and values (columns d .. 3d) of qkv [B*T, 3d] into cache rows
+// b * Tmax + pos0 + t ([B_max * Tmax, 2d], operand type). pos0 + T <= Tmax.
+hipError_t launch_kv_append(const void* qkv, bool bf16_ops, void* cache, int B, int T, int Tmax, int pos0, int d,
+                            hipStream_t s);
+// Causal attention of one new query per sequence (q in qkv [B, 3d]) against cache
+// positions 0 .. len-1: out [B, d]. len <= 8192.
+hipError_t launch_attn_decode(const void* qkv, const void* cache, void* out, bool bf16_ops, int B, int H, int hd,
+                              int Tmax, int len, hipStream_t s);
+// One token per row of fp32 logits [B, ld] over V columns: the argmax (lowest index
+// on ties) when temperature <= 0, else a draw with uniform[b] from the softmax of
+// logits / temperature over the logits >= the top_k-th largest (all when top_k <= 0
+// or >= V), by inverse CDF in index order.
+hipError_t launch_sample(const float* logits, int64_t ld, int B, int V, float temperature, int top_k,
+                         const float* uniform, int32_t* out, hipStream_t s);
+
 // Sum of squares of n floats into per-block partials [NORM_BLOCKS].
 constexpr int NORM_BLOCKS = 1024;
 hipError_t launch_sumsq_partial(const float* g, size_t n, float* part, hipStream_t s);

@@ -84,6 +84,9 @@ struct gpt_model {
   // fp32 mode with dropout: the masked copy of a residual-stream gradient that the
   // branch below reads as its GEMM operand
   Slice dxm;
+  // GPT_F_KV_CACHE: keys and values of every layer, [B_max * T_max, 2d] operand type each
+  Slice kv;
+  size_t kv_stride = 0;   // bytes per layer
   size_t layer_stride_du = 0, layer_stride_dqkv = 0, resid_stride = 0;   // bytes
   std::vector<WgradProblem> wprobs;   // host copy of the grouped weight-gradient table
   int wtiles = 0;
@@ -107,6 +110,7 @@ struct gpt_model {
   DropArgs drop{};
   uint32_t drop_call = 0;
   DropArgs drop_fwd{};
+  int kv_len = 0, kv_B = 0;   // cached positions per sequence and sequences, after gpt_prefill
   // state
   bool grads_fresh = true;
   bool fwd_pending = false;
@@ -302,6 +306,8 @@ void plan(gpt_model* h) {
   h->dO = w.take(M * d * ob);
   h->dqkv = w.take(per_layer * M * 3 * d * ob);
   h->dxm = w.take(!h->bf16 && h->cfg.dropout > 0.f ? M * d * fb : 0);
+  h->kv_stride = (h->cfg.flags & GPT_F_KV_CACHE) ? M * 2 * d * ob : 0;
+  h->kv = w.take((size_t)L * h->kv_stride);
   h->attnD = w.take(bht * fb);
   const size_t ln_blk = (M + LN_BWD_ROWS - 1) / LN_BWD_ROWS;
   const size_t cs_blk = (M + COLSUM_ROWS - 1) / COLSUM_ROWS;
@@ -392,6 +398,7 @@ void* rx_slot(gpt_model* h, int l) { return (char*)ws(h, h->rx) + (size_t)l * h-
 void* rm_slot(gpt_model* h, int l) { return (char*)ws(h, h->rm) + (size_t)l * h->resid_stride; }
 void* du_slot(gpt_model* h, int l) { return (char*)ws(h, h->du) + (size_t)l * h->layer_stride_du; }
 void* dqkv_slot(gpt_model* h, int l) { return (char*)ws(h, h->dqkv) + (size_t)l * h->layer_stride_dqkv; }
+void* kv_slot(gpt_model* h, int l) { return (char*)ws(h, h->kv) + (size_t)l * h->kv_stride; }
 
 // The grouped weight-gradient problems with this binding's addresses.
 void build_wgrad_table(gpt_model* h) {
@@ -546,7 +553,7 @@ int gpt_create(const gpt_config* cfg, gpt_model** out) {
   if (c.n_embd % 4 != 0) return fail(nullptr, GPT_E_UNSUPPORTED, "n_embd must be a multiple of 4");
   if (c.precision != GPT_PREC_FP32 && c.precision != GPT_PREC_BF16) return fail(nullptr, GPT_E_INVAL, "unknown precision");
   if (!(c.dropout >= 0.0f && c.dropout < 1.0f)) return fail(nullptr, GPT_E_INVAL, "dropout must be in [0, 1)");
-  if (c.flags != 0) return fail(nullptr, GPT_E_INVAL, "flags must be 0");
+  if (c.flags & ~(uint32_t)GPT_F_KV_CACHE) return fail(nullptr, GPT_E_INVAL, "unknown flags");
   const int64_t M = (int64_t)c.batch * c.block_size;
   if (M > 32768) return fail(nullptr, GPT_E_UNSUPPORTED, "batch * block_size above 32768 is not implemented");
   {
@@ -669,6 +676,111 @@ int gpt_forward_loss(gpt_model* h, const int32_t* d_tokens, const int32_t* d_tar
   h->fwd_pending = true;
   h->cur_B = B;
   h->cur_T = T;
+  return GPT_OK;
+}
+
+int gpt_prefill(gpt_model* h, const int32_t* d_tokens, int32_t B, int32_t T, float* d_logits) {
+  int rc = check_usable(h);
+  if (rc) return rc;
+  if (!(h->cfg.flags & GPT_F_KV_CACHE)) return fail(h, GPT_E_UNSUPPORTED, "create the model with GPT_F_KV_CACHE to decode");
+  if (!d_tokens || !d_logits) return fail(h, GPT_E_INVAL, "NULL pointer");
+  if ((rc = check_shape(h, B, T))) return rc;
+  h->fwd_pending = false;
+  h->kv_len = 0;
+  if ((rc = copy_ids(h, d_tokens, h->tokens, B * T))) return rc;
+  const DropArgs none{};
+  if ((rc = forward_to_logits(h, B, T, none))) return rc;
+  // the last position of every sequence: rows b*T + T-1 of the logits
+  const char* last = (const char*)act(h, h->logits) + (size_t)(T - 1) * h->ldz * h->op_size;
+  RUN("copy", "logits_to_f32", launch_rows_to_f32(last, h->bf16, (int64_t)T * h->ldz, B, h->Vp, d_logits, h->stream));
+  for (int l = 0; l < h->L; l++)
+    RUN("decode", "kv_append",
+        launch_kv_append(act(h, h->layers[l].qkv), h->bf16, kv_slot(h, l), B, T, h->Tmax, 0, h->d, h->stream));
+  h->kv_len = T;
+  h->kv_B = B;
+  return GPT_OK;
+}
+
+int gpt_decode(gpt_model* h, const int32_t* d_tokens, float* d_logits) {
+  int rc = check_usable(h);
+  if (rc) return rc;
+  if (!(h->cfg.flags & GPT_F_KV_CACHE)) return fail(h, GPT_E_UNSUPPORTED, "create the model with GPT_F_KV_CACHE to decode");
+  if (!d_tokens || !d_logits) return fail(h, GPT_E_INVAL, "NULL pointer");
+  if (h->kv_len < 1) return fail(h, GPT_E_STATE, "gpt_decode needs a preceding gpt_prefill");
+  if (h->kv_len >= h->Tmax) return fail(h, GPT_E_SEQ_TOO_LONG, "the cache holds block_size positions already");
+  const int B = h->kv_B, d = h->d, pos = h->kv_len;
+  const bool bf = h->bf16;
+  hipStream_t s = h->stream;
+  h->fwd_pending = false;
+  if ((rc = copy_ids(h, d_tokens, h->tokens, B))) return rc;
+  // B single-token rows through the layer-0 activation slots
+  const LayerAct& a = h->layers[0];
+  float* x = act<float>(h, a.x);
+  float* xmid = act<float>(h, a.xmid);
+  RUN("decode", "embed", launch_embed_pos(P(h, "wte"), P(h, "wpe"), act<int32_t>(h, h->tokens), x, B, d, h->Vp, pos, s));
+  for (int l = 0; l < h->L; l++) {
+    const std::string p = "h" + std::to_string(l) + ".";
+    RUN("layernorm", "ln1_fwd",
+        launch_layernorm_fwd(x, P(h, p + "ln1.g"), P(h, p + "ln1.b"), act(h, a.ln1), bf, act<float>(h, a.ln1_mean),
+                             act<float>(h, a.ln1_rstd), B, d, s));
+    {
+      GemmDesc g = gemm_desc(act(h, a.ln1), d, true, Wop(h, p + "attn.w"), d, true, act(h, a.qkv), 3 * d, B, 3 * d, d,
+                             EPI_BIAS);
+      g.bias = P(h, p + "attn.b");
+      RUN("decode", "qkv", gemm(h, g, bf));
+    }
+    RUN("decode", "kv_append", launch_kv_append(act(h, a.qkv), bf, kv_slot(h, l), B, 1, h->Tmax, pos, d, s));
+    RUN("decode", "attn",
+        launch_attn_decode(act(h, a.qkv), kv_slot(h, l), act(h, a.att), bf, B, h->H, h->hd, h->Tmax, pos + 1, s));
+    {
+      GemmDesc g = gemm_desc(act(h, a.att), d, true, Wop(h, p + "proj.w"), d, true, xmid, d, B, d, d, EPI_BIAS_RESID);
+      g.bias = P(h, p + "proj.b");
+      g.resid = x;
+      g.ldr = d;
+      RUN("decode", "proj", gemm(h, g, bf));
+    }
+    RUN("layernorm", "ln2_fwd",
+        launch_layernorm_fwd(xmid, P(h, p + "ln2.g"), P(h, p + "ln2.b"), act(h, a.ln2), bf,
+                             act<float>(h, a.ln2_mean), act<float>(h, a.ln2_rstd), B, d, s));
+    {
+      GemmDesc g = gemm_desc(act(h, a.ln2), d, true, Wop(h, p + "fc.w"), d, true, act(h, a.h), 4 * d, B, 4 * d, d,
+                             EPI_BIAS_GELU);
+      g.bias = P(h, p + "fc.b");
+      g.aux = act(h, a.u);
+      g.ldaux = 4 * d;
+      RUN("decode", "fc", gemm(h, g, bf));
+    }
+    {
+      GemmDesc g = gemm_desc(act(h, a.h), 4 * d, true, Wop(h, p + "fcproj.w"), 4 * d, true, x, d, B, d, 4 * d,
+                             EPI_BIAS_RESID);
+      g.bias = P(h, p + "fcproj.b");
+      g.resid = xmid;
+      g.ldr = d;
+      RUN("decode", "fcproj", gemm(h, g, bf));
+    }
+  }
+  RUN("layernorm", "lnf_fwd",
+      launch_layernorm_fwd(x, P(h, "lnf.g"), P(h, "lnf.b"), act(h, h->lnf), bf, act<float>(h, h->lnf_mean),
+                           act<float>(h, h->lnf_rstd), B, d, s));
+  {
+    GemmDesc g = gemm_desc(act(h, h->lnf), d, true, Wop(h, "wte"), d, true, act(h, h->logits), h->ldz, B, h->Vp, d,
+                           EPI_STORE);
+    RUN("decode", "lm_head", gemm(h, g, bf));
+  }
+  RUN("copy", "logits_to_f32", launch_rows_to_f32(act(h, h->logits), bf, h->ldz, B, h->Vp, d_logits, s));
+  h->kv_len = pos + 1;
+  return GPT_OK;
+}
+
+int gpt_sample(gpt_model* h, const float* d_logits, int32_t B, float temperature, int32_t top_k,
+               const float* d_uniform, int32_t* d_tokens_out) {
+  int rc = check_usable(h);
+  if (rc) return rc;
+  if (!d_logits || !d_tokens_out || (temperature > 0.f && !d_uniform)) return fail(h, GPT_E_INVAL, "NULL pointer");
+  if (B < 1) return fail(h, GPT_E_INVAL, "B must be >= 1");
+  if (!(temperature == temperature)) return fail(h, GPT_E_INVAL, "temperature is NaN");
+  RUN("decode", "sample",
+      launch_sample(d_logits, h->Vp, B, h->Vp, temperature, top_k, d_uniform, d_tokens_out, h->stream));
   return GPT_OK;
 }
 
