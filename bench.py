@@ -13,6 +13,13 @@ library's kernels. Prints one JSON line.
 
 MFU uses the conventional count of 6N + 12 L d T FLOPs per token (N = parameters
 without the position embedding) against 2.5 PFLOP/s dense bf16.
+
+    python bench.py --decode [--prompt 128] [--new 256] [--temperature 0.8] [--top-k 40]
+
+measures generation instead: a prefill of B prompts, then --new decode steps, each
+one token per sequence through the key/value cache and one sampling launch, the
+sampled tokens fed straight back on the device. Prints one JSON line with decode
+tokens/s and the HBM roofline of a decode step.
 """
 from __future__ import annotations
 
@@ -60,6 +67,99 @@ def cpu_baseline(cfg, params, batches, n_seq: int, dropout: float = 0.0):
                       f"({dt:.1f} s); AdamW excluded"}
 
 
+def decode_bytes(cfg, B: int, length: int, op_bytes: int) -> float:
+    """Algorithmic HBM bytes of one decode step at cache length `length` (the new
+    position included): every weight read once in operand type (the tied wte for the
+    lm_head, 12 d^2 per layer), biases and LayerNorm parameters in fp32, the keys and
+    values of `length` positions read and one position written per layer and
+    sequence, the embedding rows, the fp32 logits written."""
+    d, L, V = cfg.n_embd, cfg.n_layer, cfg.padded_vocab
+    weights = (V * d + L * 12 * d * d) * op_bytes + (L * 13 * d + 2 * d) * 4
+    kv = L * B * (length + 1) * 2 * d * op_bytes
+    rows = B * 2 * d * 4 + B * V * 4
+    return float(weights + kv + rows)
+
+
+def bench_decode(a, cfg) -> int:
+    import torch
+    from transformer_lm_gpt_amd import workloads as W
+    from transformer_lm_gpt_amd.binding import GPT
+    B, T0, n = cfg.batch, a.prompt, a.new
+    if T0 < 1 or T0 + n > cfg.block_size:
+        print(f"--prompt {T0} + --new {n} exceeds block_size {cfg.block_size}", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    drng, wrng = W.rngs()
+    params = W.init_params(cfg, wrng)
+    prompt, _ = W.make_batch(cfg, drng, B=B, T=T0)
+    urng = np.random.default_rng(7)
+    uni = torch.from_numpy(urng.random((n, B)).astype(np.float32)).cuda()
+    tok = torch.from_numpy(prompt).cuda()
+    gpu = GPT(cfg, a.precision, device="cuda:0", kv_cache=True)
+    gpu.load_params(params)
+    stream = torch.cuda.current_stream()
+
+    def generate():
+        z = gpu.prefill(tok)
+        t = gpu.sample(z, a.temperature, a.top_k, None if a.temperature <= 0 else uni[0])
+        e0 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(1, n + 1):
+            z = gpu.decode(t)
+            t = gpu.sample(z, a.temperature, a.top_k, None if a.temperature <= 0 else uni[s % n])
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record(stream)
+        return e0, e1, t
+
+    generate()                                        # warm-up
+    gpu.sync()
+    torch.cuda.synchronize()
+    ep = torch.cuda.Event(enable_timing=True)
+    ep.record(stream)
+    e0, e1, t = generate()
+    torch.cuda.synchronize()
+    gpu.sync()
+    dec_ms = e0.elapsed_time(e1)
+    pre_ms = ep.elapsed_time(e0)
+    step_ms = dec_ms / n
+    op = 2 if a.precision == "bf16" else 4
+    bytes_avg = sum(decode_bytes(cfg, B, T0 + s, op) for s in range(n)) / n
+    achieved = bytes_avg / (step_ms / 1e3)
+    cpu = None
+    if a.cpu_seqs > 0:
+        from oracle import gpt_oracle as O
+        t0 = time.perf_counter()
+        O.generate(params, prompt[:1], cfg, 2, a.temperature, a.top_k, np.full((2, 1), 0.5))
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(2 / dt, 3), "unit": "tokens/s", "cores": os.cpu_count(), "kind": "oracle",
+               "sample": f"1 sequence, prompt {T0}, 2 new tokens by full float64 recomputation ({dt:.1f} s)"}
+    out = {
+        "metric": f"decode tokens/sec with a key/value cache, {cfg.name}, 1 MI355X",
+        "value": round(B * n / (dec_ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": n,
+        "warmup": 1,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": a.precision,
+        "data": f"synthetic prompts (seeded, {cfg.data}), random-init weights N(0,{cfg.init_std})",
+        "config": {"workload": f"{cfg.name}: L{cfg.n_layer} H{cfg.n_head} d{cfg.n_embd} V{cfg.padded_vocab} "
+                               f"B{B} prompt {T0} + {n} new, temperature {a.temperature}, top-k {a.top_k}"},
+        "prefill_ms": round(pre_ms, 3),
+        "roofline": {"kernel": "one decode step (all layers, lm_head, sampling)", "bound": "hbm",
+                     "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM, 4), "traffic": None,
+                     "bytes_per_step": round(bytes_avg)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    gpu.close()
+    return 0
+
+
 def traffic_of(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
     (profiles/traffic.json), or None when the counters were taken on another workload
@@ -91,6 +191,11 @@ def main(argv=None):
     ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the oracle's timed sample (0: skip)")
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="dropout rate of the timed model (the GPT-2 124M workload uses 0)")
+    ap.add_argument("--decode", action="store_true", help="measure generation with the key/value cache")
+    ap.add_argument("--prompt", type=int, default=128, help="--decode: prompt length")
+    ap.add_argument("--new", type=int, default=256, help="--decode: generated tokens per sequence")
+    ap.add_argument("--temperature", type=float, default=0.8, help="--decode: sampling temperature")
+    ap.add_argument("--top-k", type=int, default=40, help="--decode: top-k cut (0: none)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run 3 plain device copies of this many bytes (calibrates the HBM byte counters)")
     a = ap.parse_args(argv)
@@ -113,6 +218,8 @@ def main(argv=None):
         return 0
 
     cfg = W.CONFIGS[a.workload]
+    if a.decode:
+        return bench_decode(a, cfg)
     B, T, A = cfg.batch, cfg.block_size, cfg.grad_accum
     torch.cuda.set_device(0)
     drng, wrng = W.rngs()

@@ -266,7 +266,9 @@ class GPT(Layout):
         z = logits.to(self.device, t.float32).contiguous()
         B = z.shape[0]
         u = None
-        if uniforms is not None:
+        if isinstance(uniforms, t.Tensor):
+            u = uniforms.to(self.device, t.float32).contiguous()
+        elif uniforms is not None:
             u = t.as_tensor(np.asarray(uniforms, dtype=np.float32)).to(self.device).contiguous()
         out = t.empty(B, dtype=t.int32, device=self.device)
         self._keep_dec = (z, u)

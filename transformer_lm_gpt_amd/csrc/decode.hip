@@ -59,9 +59,10 @@ hipError_t launch_kv_append(const void* qkv, bool bf16_ops, void* cache, int B, 
 
 // One query per (sequence, head) against keys 0 .. len-1 of the cache:
 // s_j = q . k_j / sqrt(hd), p = softmax(s), o = sum_j p_j v_j. One workgroup of 256
-// per (b, h); the scores of all keys sit in LDS (len <= DEC_MAX_T). The value sum
-// gives each wavefront every fourth key, a lane per head column, and the four
-// partial vectors are added in a fixed order.
+// per (b, h); the scores of all keys sit in LDS (len <= DEC_MAX_T). For the value sum
+// with 16-byte rows, thread t takes 8 columns (t mod hd/8) of every (256 / (hd/8))-th
+// key, and the per-slot partial vectors are added in slot order; otherwise each
+// wavefront takes every fourth key with a lane per column.
 constexpr int DEC_MAX_T = 8192;
 template <typename T>
 __global__ __launch_bounds__(256) void attn_decode_kernel(const T* __restrict__ qkv, const T* __restrict__ cache,
@@ -70,6 +71,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const T* __restrict__ 
   __shared__ float sc[DEC_MAX_T];
   __shared__ float qs[64];
   __shared__ float red[4][64];
+  __shared__ float vred[256 * 8];
   const int b = blockIdx.x / H, h = blockIdx.x % H;
   const int d = H * hd;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -77,10 +79,19 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const T* __restrict__ 
   __syncthreads();
   const T* kb = cache + (int64_t)b * Tmax * 2 * d + h * hd;
   float mx = -INFINITY;
+  const bool vec = sizeof(T) == 2 && hd % 8 == 0;   // 16-byte key reads (rows 16-byte aligned)
   for (int j = tid; j < len; j += 256) {
     const T* kr = kb + (int64_t)j * 2 * d;
     float s = 0.f;
-    for (int c = 0; c < hd; c++) s += qs[c] * to_f32(kr[c]);
+    if (vec) {
+      for (int c8 = 0; c8 < hd; c8 += 8) {
+        const bf16x8 kv = *(const bf16x8*)(kr + c8);
+#pragma unroll
+        for (int e = 0; e < 8; e++) s += qs[c8 + e] * (float)kv[e];
+      }
+    } else {
+      for (int c = 0; c < hd; c++) s += qs[c] * to_f32(kr[c]);
+    }
     s *= scale;
     sc[j] = s;
     mx = fmaxf(mx, s);
@@ -101,6 +112,32 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const T* __restrict__ 
   __syncthreads();
   sum = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
   __syncthreads();
+  if (vec) {
+    const int nch = hd / 8, slots = 256 / nch;       // 8-column chunks, keys per round
+    const int ch = tid % nch, slot = tid / nch;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) acc[e] = 0.f;
+    if (slot < slots) {
+      const T* vb = kb + d + ch * 8;
+#pragma unroll 4
+      for (int j = slot; j < len; j += slots) {
+        const bf16x8 v = *(const bf16x8*)(vb + (int64_t)j * 2 * d);
+        const float pj = sc[j];
+#pragma unroll
+        for (int e = 0; e < 8; e++) acc[e] += pj * (float)v[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; e++) vred[slot * hd + ch * 8 + e] = acc[e];
+    }
+    __syncthreads();
+    if (tid < hd) {
+      float t = 0.f;
+      for (int q = 0; q < slots; q++) t += vred[q * hd + tid];
+      out[(int64_t)b * d + h * hd + tid] = from_f32<T>(t / sum);
+    }
+    return;
+  }
   float o = 0.f;
   if (lane < hd) {
     const T* vb = kb + d + lane;
@@ -131,8 +168,8 @@ hipError_t launch_attn_decode(const void* qkv, const void* cache, void* out, boo
 // One workgroup of 1024 per row. temperature <= 0: the argmax, lowest index on ties.
 // Otherwise: the candidates are the logits >= the k-th largest (found exactly by a
 // four-pass radix select on order-preserving integer keys; all V when top_k <= 0 or
-// >= V), weighted by exp((z - max) / temperature); each thread owns a contiguous run
-// of indices, the runs' sums are scanned in thread order, and the token is the first
+// >= V), weighted by exp((z - max) / temperature); each wavefront owns a contiguous
+// segment of indices, the segment sums are added in order, and the token is the first
 // index whose running sum exceeds u times the total.
 constexpr int SAMPLE_THREADS = 1024;
 
@@ -145,24 +182,30 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_kernel(const float* __r
                                                                 float temperature, int top_k,
                                                                 const float* __restrict__ uniform,
                                                                 int32_t* __restrict__ out) {
-  __shared__ uint32_t hist[256];
-  __shared__ float fred[SAMPLE_THREADS / 64];
-  __shared__ int ired[SAMPLE_THREADS / 64];
-  __shared__ uint32_t sel[2];   // prefix of the k-th key, count still needed
-  __shared__ int answer;   // the thread whose run holds the draw
+  constexpr int NW = SAMPLE_THREADS / 64;
+  constexpr int UNR = 8;                              // loads in flight per thread in the strided passes
+  __shared__ uint32_t hist[NW][256];                  // one histogram per wavefront
+  __shared__ float fred[NW];
+  __shared__ int ired[NW];
+  __shared__ uint32_t sel[2];                         // prefix of the k-th key, count still needed
+  __shared__ float csum[NW][64];                      // weight sum of each lane's run
+  __shared__ int answer;                              // the wavefront whose segment holds the draw
   const float* z = logits + (int64_t)blockIdx.x * ld;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  constexpr int NW = SAMPLE_THREADS / 64;
 
   // maximum, with its lowest index
   float mx = -INFINITY;
   int mi = 0x7fffffff;
-  for (int i = tid; i < V; i += SAMPLE_THREADS) {
-    const float v = z[i];
-    if (v > mx) {
-      mx = v;
-      mi = i;
-    }
+  for (int i0 = tid; i0 < V; i0 += UNR * SAMPLE_THREADS) {
+    float v[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; u++) v[u] = i0 + u * SAMPLE_THREADS < V ? z[i0 + u * SAMPLE_THREADS] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < UNR; u++)
+      if (v[u] > mx) {                                // indices rise with u: the first maximum stays
+        mx = v[u];
+        mi = i0 + u * SAMPLE_THREADS;
+      }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -191,6 +234,7 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_kernel(const float* __r
   }
   __syncthreads();
   mx = fred[0];
+  __syncthreads();                                    // fred is written again below
   if (temperature <= 0.f) {
     if (tid == 0) out[blockIdx.x] = ired[0];
     return;
@@ -205,75 +249,108 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_kernel(const float* __r
     }
     for (int pass = 0; pass < 4; pass++) {
       const int shift = 24 - 8 * pass;
-      if (tid < 256) hist[tid] = 0;
+      for (int i = tid; i < NW * 256; i += SAMPLE_THREADS) hist[i / 256][i % 256] = 0;
       __syncthreads();
       const uint32_t prefix = sel[0];
       const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-      for (int i = tid; i < V; i += SAMPLE_THREADS) {
-        const uint32_t key = order_key(z[i]);
-        if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      for (int i0 = tid; i0 < V; i0 += UNR * SAMPLE_THREADS) {
+        uint32_t key[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; u++) {
+          const int i = i0 + u * SAMPLE_THREADS;
+          key[u] = i < V ? order_key(z[i]) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; u++)
+          if (i0 + u * SAMPLE_THREADS < V && (key[u] & hi_mask) == prefix)
+            atomicAdd(&hist[w][(key[u] >> shift) & 255u], 1u);
       }
       __syncthreads();
-      if (tid == 0) {
-        uint32_t need = sel[1];
-        int bin = 255;
-        for (; bin > 0; bin--) {                      // from the largest bin down
-          if (hist[bin] >= need) break;
-          need -= hist[bin];
+      if (tid < 256) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int q = 0; q < NW; q++) c += hist[q][tid];
+        hist[0][tid] = c;
+      }
+      __syncthreads();
+      // the bin holding the need-th largest key: the one whose suffix count (bins at or
+      // above it) reaches `need` while the suffix above it does not; every bin in parallel
+      const uint32_t need = sel[1];
+      __syncthreads();
+      if (tid < 256) {
+        uint32_t above = 0;
+        for (int j = 255; j > tid; j--) above += hist[0][j];
+        if (above < need && above + hist[0][tid] >= need) {
+          sel[0] = prefix | ((uint32_t)tid << shift);
+          sel[1] = need - above;
         }
-        sel[0] = prefix | ((uint32_t)bin << shift);
-        sel[1] = need;
       }
       __syncthreads();
     }
     kth = sel[0];
   }
 
-  // weights, per-thread runs and their scan in thread order
+  // weights exp((z - max) / temperature) of the candidates, summed in index order:
+  // wavefront w owns the segment [w S, (w + 1) S) and its lane l the run
+  // [w S + l CH, w S + (l + 1) CH) (S = 64 CH, CH a multiple of 4), summed in order by
+  // that lane; runs add up across lanes, segments across wavefronts
   const float inv_t = 1.0f / temperature;
-  const int per = (V + SAMPLE_THREADS - 1) / SAMPLE_THREADS;
-  const int i0 = tid * per, i1 = min(V, i0 + per);
-  float run = 0.f;
-  for (int i = i0; i < i1; i++) {
-    const float v = z[i];
-    if (order_key(v) >= kth) run += __expf((v - mx) * inv_t);
+  const int CH = ((V + NW - 1) / NW + 255) / 256 * 4;
+  const int s0 = min(V, w * 64 * CH), s1 = min(V, s0 + 64 * CH);
+  const int a0 = min(s1, s0 + lane * CH), a1 = min(s1, a0 + CH);
+  auto weight = [&](float v) -> float { return order_key(v) >= kth ? __expf((v - mx) * inv_t) : 0.f; };
+  float cs = 0.f;
+  if (a1 - a0 == CH && ((uintptr_t)z & 15) == 0) {   // whole run of an aligned row: 16-byte loads
+    for (int i = a0; i < a1; i += 4 * UNR) {
+      f32x4 v[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; u++) v[u] = i + 4 * u < a1 ? *(const f32x4*)(z + i + 4 * u) : (f32x4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+      for (int u = 0; u < UNR; u++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) cs += i + 4 * u < a1 ? weight(v[u][e]) : 0.f;
+    }
+  } else {
+    for (int i = a0; i < a1; i++) cs += weight(z[i]);
   }
+  csum[w][lane] = cs;
+  const float wtot = wave_sum(cs);
+  if (lane == 0) fred[w] = wtot;
   if (tid == 0) answer = -1;
   __syncthreads();
-  // inclusive scan over the 1024 run sums: each wave scans 64, then the wave totals
-  float incl = run;
+  float start = 0.f, total = 0.f;
+  for (int q = 0; q < NW; q++) {
+    if (q < w) start += fred[q];
+    total += fred[q];
+  }
+  const float target = uniform[blockIdx.x] * total;
+  // the segment holding the target is the last non-empty one that starts at or before it
+  if (lane == 0 && wtot > 0.f && start <= target) atomicMax(&answer, w);
+  __syncthreads();
+  if (w != answer) return;
+  float incl = cs;                                    // runs before this lane's, in lane order
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const float t = __shfl_up(incl, o, 64);
     if (lane >= o) incl += t;
   }
-  if (lane == 63) fred[w] = incl;
-  __syncthreads();
-  float before = 0.f;
-  for (int q = 0; q < w; q++) before += fred[q];
-  float total = 0.f;
-  for (int q = 0; q < NW; q++) total += fred[q];
-  const float start = before + incl - run;           // sum of every earlier run
-  const float target = uniform[blockIdx.x] * total;
-  // the run holding the target is the last non-empty one that starts at or before it
-  if (run > 0.f && start <= target) atomicMax(&answer, tid);
-  __syncthreads();
-  if (tid == answer) {
-    float acc = start;
-    int pick = -1, last = -1;
-    for (int i = i0; i < i1; i++) {
-      const float v = z[i];
-      if (order_key(v) >= kth) {
-        last = i;
-        acc += __expf((v - mx) * inv_t);
-        if (acc > target) {
-          pick = i;
-          break;
-        }
+  const float lstart = start + incl - cs;
+  const uint64_t claim = __ballot(cs > 0.f && lstart <= target);
+  if (lane != 63 - __builtin_clzll(claim)) return;    // the last non-empty run starting at or before it
+  float acc = lstart;
+  int pick = -1, last = -1;
+  for (int i = a0; i < a1; i++) {
+    const float wi = weight(z[i]);
+    if (wi > 0.f) {
+      last = i;
+      acc += wi;
+      if (acc > target) {
+        pick = i;
+        break;
       }
     }
-    out[blockIdx.x] = pick >= 0 ? pick : last;        // rounding can leave the target past the run's sum
   }
+  out[blockIdx.x] = pick >= 0 ? pick : last;          // rounding can leave the target past the run's sum
 }
 
 hipError_t launch_sample(const float* logits, int64_t ld, int B, int V, float temperature, int top_k,

@@ -1029,6 +1029,61 @@ __global__ __launch_bounds__(256) void group_fixup_kernel(const WgradProblem* __
 
 static int num_cus();
 
+// ----------------------------------------------------------------------------- few output rows
+// M <= 16 (one token per sequence while decoding): the weight operand streams from
+// HBM once and nothing is worth staging. One workgroup of 16 wavefronts per 16 output
+// columns; wavefront w multiplies every 16th 32-wide k-slice with fragments read
+// straight from global memory (A: the M rows, zero past M; B: 16 weight rows), and the
+// 16 partial tiles are added in LDS in a fixed order before the element epilogue.
+template <int EPI>
+__global__ __launch_bounds__(1024) void gemm_skinny_kernel(GemmArgs p) {
+  __shared__ f32x4 part[16][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  const bool arow = r < p.M, brow = n0 + r < p.N;
+  const bf16* ap = (const bf16*)p.A + (int64_t)(arow ? r : 0) * p.lda + g * 8;
+  const bf16* bp = (const bf16*)p.B + (int64_t)(brow ? n0 + r : 0) * p.ldb + g * 8;
+  f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const int nk = p.K / 32;
+#pragma unroll 4
+  for (int kt = w; kt < nk; kt += 16) {
+    const bf16x8 af = arow ? *(const bf16x8*)(ap + kt * 32) : (bf16x8){};
+    const bf16x8 bfr = brow ? *(const bf16x8*)(bp + kt * 32) : (bf16x8){};
+    acc = Mfma<bf16>::mma(af, bfr, acc);
+  }
+  part[w][lane] = acc;
+  __syncthreads();
+  if (w == 0) {
+    f32x4 t = part[0][lane];
+#pragma unroll
+    for (int q = 1; q < 16; q++) t += part[q][lane];
+    const int col = n0 + r;                           // lane holds rows 4g + i of column r
+    if (col < p.N) {
+      const float bias = epi_bias<EPI>(p, col);
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        if (4 * g + i < p.M) epi_store<bf16, EPI>(p, 4 * g + i, col, t[i], bias);
+    }
+  }
+}
+
+static hipError_t skinny_epi(const GemmArgs& a, int epi, hipStream_t s) {
+  const dim3 grid((a.N + 15) / 16);
+  switch (epi) {
+#define GPT_SKINNY_CASE(E) \
+  case E: hipLaunchKernelGGL((gemm_skinny_kernel<E>), grid, dim3(1024), 0, s, a); break;
+    GPT_SKINNY_CASE(EPI_STORE)
+    GPT_SKINNY_CASE(EPI_BIAS)
+    GPT_SKINNY_CASE(EPI_BIAS_RESID)
+    GPT_SKINNY_CASE(EPI_BIAS_GELU)
+    GPT_SKINNY_CASE(EPI_F32)
+#undef GPT_SKINNY_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 bool wgrad_group_ok(int M, int N, int64_t lda, int64_t ldb, int64_t ldc) {
   return M >= 8 && N >= 8 && M % 8 == 0 && N % 8 == 0 && lda % 8 == 0 && ldb % 8 == 0 && ldc >= N;
 }
@@ -1095,6 +1150,11 @@ hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
     if (d.epi == EPI_ACC && d.split_ws) cv = cv && (d.N % 4 == 0) && ((uintptr_t)d.split_ws % 16 == 0);
     a.c_vec = cv;
   }
+  // few rows, both operands k-contiguous, aligned 16-byte fragments
+  if (bf16_operands && d.M <= 16 && d.a_kc && d.b_kc && d.K % 32 == 0 && a.a_vec && a.b_vec &&
+      (d.epi == EPI_STORE || d.epi == EPI_BIAS || d.epi == EPI_BIAS_RESID || d.epi == EPI_BIAS_GELU ||
+       d.epi == EPI_F32))
+    return skinny_epi(a, d.epi, s);
   const bool pipelined = pipelined_ok(d, bf16_operands);
   const int TBM = pipelined ? 256 : BM, TBN = pipelined ? 256 : BN;
   const int tiles = ((d.M + TBM - 1) / TBM) * ((d.N + TBN - 1) / TBN);
