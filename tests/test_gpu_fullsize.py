@@ -95,3 +95,37 @@ def test_gpt2_full_step_identical_copies():
     wv = check_tensors(v_gpu, tr.v, "bf16", "v", tol=6e-2, d=d, key_bias_bound=1e-6 * gmax * gmax)
     say(f"  loss {np.mean(gl):.5f} vs {ref['loss']:.5f}; worst grad {wg}; param {wp[0]:.2e} m {wm[0]:.2e} v {wv[0]:.2e}")
     gpu.close()
+
+
+@pytest.mark.timeout(900)
+def test_gpt2_forward_with_dropout_sampled_sequences():
+    """Dropout 0.1 at the full size and launch configuration: the input of the final
+    LayerNorm after all 12 dropped blocks, for two sampled sequences of a B 12 x T 1024
+    micro-batch, against the oracle's forward of those sequences with the same masks
+    (logits and per-position losses formed on the host from the GPU's activations)."""
+    import torch
+    cfg = W.CONFIGS[NAME]
+    drng, wrng = W.rngs()
+    params = W.init_params(cfg, wrng, perturb=True)
+    tok, tgt = W.make_batch(cfg, drng)
+    seed, call = 0x0DD5EED, 3
+    say(f"[fullsize] forward with dropout 0.1, B={tok.shape[0]} T={tok.shape[1]} bf16")
+    gpu = new_model(cfg, "bf16", dropout=0.1)
+    gpu.load_params(params)
+    gpu.set_dropout_seed(seed, call)
+    gpu.forward_loss(tok, tgt)
+    B, T, d = tok.shape[0], tok.shape[1], cfg.n_embd
+    xL = gpu.debug("x", cfg.n_layer, (B, T, d), torch.float32).cpu().numpy()
+    gpu.close()
+    P = {k: v.astype(np.float64) for k, v in params.items()}
+    drop = (O.Dropout(0.1, seed, call), call)
+    for b in (0, B - 1):
+        zr, _ = O.forward_sequence(P, tok[b], cfg, drop, b)
+        xf, _ = O.layernorm_fwd(xL[b].astype(np.float64), P["lnf.g"], P["lnf.b"])
+        zg = xf @ P["wte"].T
+        r = rel(zg, zr)
+        say(f"  sequence {b}: logits rel err {r:.2e}")
+        assert r < 2e-2
+        lg = _lse_loss(zg, tgt[b]).mean()
+        lo = _lse_loss(zr, tgt[b]).mean()
+        assert abs(lg - lo) / lo < 2e-2, (b, lg, lo)

@@ -193,6 +193,13 @@ __device__ inline float epi_bias(const GemmArgs& p, int col) {
   return 0.f;
 }
 
+// The branch mask of one output element, kept out of line: the element epilogues
+// below are unrolled over whole tiles, and inlined generator rounds for every element
+// would be scheduled together and spill.
+__device__ __noinline__ float drop_mult_elem(const DropArgs& a, uint32_t site, uint32_t row, uint32_t col) {
+  return drop_mult1(a, site, row, col);
+}
+
 // One output element: the fused epilogue of every GEMM of the step.
 template <typename T, int EPI>
 __device__ inline void epi_store(const GemmArgs& p, int row, int col, float v, float bias) {
@@ -204,7 +211,7 @@ __device__ inline void epi_store(const GemmArgs& p, int row, int col, float v, f
   } else if constexpr (EPI == EPI_BIAS_RESID) {
     ((float*)p.C)[ci] = p.resid[(int64_t)row * p.ldr + col] + (v + bias);
   } else if constexpr (EPI == EPI_BIAS_RESID_DROP) {
-    ((float*)p.C)[ci] = p.resid[(int64_t)row * p.ldr + col] + (v + bias) * drop_mult1(p.drop, p.drop_site, row, col);
+    ((float*)p.C)[ci] = p.resid[(int64_t)row * p.ldr + col] + (v + bias) * drop_mult_elem(p.drop, p.drop_site, row, col);
   } else if constexpr (EPI == EPI_BIAS_GELU) {
     const float u = v + bias;
     ((T*)p.aux)[(int64_t)row * p.ldaux + col] = from_f32<T>(u);
@@ -290,7 +297,11 @@ __device__ inline void epi_store16(const GemmArgs& p, int row, int col0, const f
       const f32x4 rv = pre ? pre->r[q] : *(const f32x4*)(r + 4 * q);
       f32x4 o;
       if constexpr (EPI == EPI_BIAS_RESID_DROP) {
-        const f32x4 mk = drop_mult4(p.drop, p.drop_site, row, (col0 >> 2) + q);
+        // the opaque copy of the row keeps each mask block after the stores before it:
+        // hoisted together, the blocks of every pass spill the parked accumulators
+        uint32_t mrow = (uint32_t)row;
+        asm volatile("" : "+v"(mrow)::"memory");
+        const f32x4 mk = drop_mult4(p.drop, p.drop_site, mrow, (col0 >> 2) + q);
 #pragma unroll
         for (int e = 0; e < 4; e++) o[e] = rv[e] + x[4 * q + e] * mk[e];
       } else {
