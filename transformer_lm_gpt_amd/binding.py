@@ -252,10 +252,14 @@ class GPT(Layout):
         out = self.torch.empty((B, self.cfg.padded_vocab), dtype=self.torch.float32, device=self.device)
         self._keep_dec = tok
         self._check(self.lib.gpt_prefill(self.h, C.c_void_p(tok.data_ptr()), B, T, C.c_void_p(out.data_ptr())))
+        self._kv_B = B
         return out
 
     def decode(self, tokens):
         tok = self._ids(tokens).reshape(-1)
+        if tok.numel() != getattr(self, "_kv_B", tok.numel()):
+            raise ValueError(f"decode takes one token per sequence of the last prefill ({self._kv_B}), "
+                             f"got {tok.numel()}")
         out = self.torch.empty((tok.numel(), self.cfg.padded_vocab), dtype=self.torch.float32, device=self.device)
         self._keep_dec = tok
         self._check(self.lib.gpt_decode(self.h, C.c_void_p(tok.data_ptr()), C.c_void_p(out.data_ptr())))
