@@ -40,6 +40,11 @@ What it computes, and the passage each part follows (the nanoGPT pages):
     ``generate`` recomputes the whole forward for every new token: that is the
     definition a decoder with a key/value cache has to reproduce.
 
+  * the microGPT variant (configuration variant "microgpt"; same page, model-core
+    section): weightless RMSNorm, ReLU instead of GELU, no biases, an lm_head of
+    its own. Its norms sit where the GPT-2 block has them (before attention,
+    before the MLP and before the head), with eps 1e-5.
+
 Readings where the pages are silent: LayerNorm eps 1e-5 with the biased
 variance; attention scale 1/sqrt(head_dim); the softmax runs over all padded
 vocabulary columns; the clip coefficient is min(1, clip / (norm + 1e-6)) and
@@ -61,14 +66,21 @@ CLIP_EPS = 1e-6
 
 # --------------------------------------------------------------------------- layout
 
-def param_shapes(cfg, variant: str = "gpt2") -> List[Tuple[str, Tuple[int, ...]]]:
+def variant_of(cfg) -> str:
+    return getattr(cfg, "variant", "gpt2")
+
+
+def param_shapes(cfg, variant: str | None = None) -> List[Tuple[str, Tuple[int, ...]]]:
     """Trainable tensors. Linear weights are [out, in] and act as y = x W^T + b.
 
     variant "gpt2": LayerNorm gain/shift, biased linears, tied head.
-    variant "microgpt": the microGPT block (weightless RMSNorm, no biases,
-    separate q/k/v/o matrices, untied lm_head) used only to check the page's
-    printed parameter count.
+    variant "microgpt": the microGPT block ("Building microGPT from scratch",
+    model-core section: weightless RMSNorm, ReLU, no biases, an lm_head of its
+    own). Its q, k and v matrices are the three row blocks of attn.w, its output
+    matrix is proj.w and its two MLP matrices fc.w and fcproj.w.
+    (Default: the configuration's own variant.)
     """
+    variant = variant_of(cfg) if variant is None else variant
     V, d, T, L = cfg.padded_vocab, cfg.n_embd, cfg.block_size, cfg.n_layer
     out: List[Tuple[str, Tuple[int, ...]]] = [("wte", (V, d)), ("wpe", (T, d))]
     for l in range(L):
@@ -81,8 +93,8 @@ def param_shapes(cfg, variant: str = "gpt2") -> List[Tuple[str, Tuple[int, ...]]
                     (p + "fc.w", (4 * d, d)), (p + "fc.b", (4 * d,)),
                     (p + "fcproj.w", (d, 4 * d)), (p + "fcproj.b", (d,))]
         elif variant == "microgpt":
-            out += [(p + "wq", (d, d)), (p + "wk", (d, d)), (p + "wv", (d, d)),
-                    (p + "wo", (d, d)), (p + "fc1", (4 * d, d)), (p + "fc2", (d, 4 * d))]
+            out += [(p + "attn.w", (3 * d, d)), (p + "proj.w", (d, d)),
+                    (p + "fc.w", (4 * d, d)), (p + "fcproj.w", (d, 4 * d))]
         else:
             raise ValueError(variant)
     if variant == "gpt2":
@@ -92,7 +104,7 @@ def param_shapes(cfg, variant: str = "gpt2") -> List[Tuple[str, Tuple[int, ...]]
     return out
 
 
-def n_params(cfg, variant: str = "gpt2") -> int:
+def n_params(cfg, variant: str | None = None) -> int:
     return int(sum(int(np.prod(s)) for _, s in param_shapes(cfg, variant)))
 
 
@@ -211,6 +223,26 @@ def layernorm_bwd(dy, cache, g):
     return dx, dg, db
 
 
+def rmsnorm_fwd(x):
+    """Weightless RMSNorm: x / sqrt(mean(x^2) + eps) (the microGPT block's norm)."""
+    rstd = 1.0 / np.sqrt((x * x).mean(axis=-1, keepdims=True) + LN_EPS)
+    xhat = x * rstd
+    return xhat, (xhat, rstd)
+
+
+def rmsnorm_bwd(dy, cache):
+    xhat, rstd = cache
+    return rstd * (dy - xhat * (dy * xhat).mean(axis=-1, keepdims=True))
+
+
+def relu(u):
+    return np.maximum(u, 0.0)
+
+
+def relu_grad(u):
+    return (u > 0.0).astype(u.dtype)
+
+
 def gelu(u):
     """Exact GELU: u * Phi(u) with the standard normal CDF Phi."""
     return 0.5 * u * (1.0 + erf(u / math.sqrt(2.0)))
@@ -283,6 +315,11 @@ def forward_sequence(P, tok, cfg, drop=None, b=0):
     d, H, L = cfg.n_embd, cfg.n_head, cfg.n_layer
     hd = d // H
     dt = P["wte"].dtype.type
+    micro = variant_of(cfg) == "microgpt"
+    # microGPT: weightless RMSNorm, ReLU, no biases, its own lm_head
+    norm = (lambda x, name: rmsnorm_fwd(x)) if micro else (lambda x, name: layernorm_fwd(x, P[name + ".g"], P[name + ".b"]))
+    act = relu if micro else gelu
+    bias = (lambda name: 0.0) if micro else (lambda name: P[name])
     if drop is not None:
         dr, call = drop
         tok_rows = b * T + np.arange(T)
@@ -296,8 +333,8 @@ def forward_sequence(P, tok, cfg, drop=None, b=0):
     layers = []
     for l in range(L):
         p = f"h{l}."
-        a, c1 = layernorm_fwd(x, P[p + "ln1.g"], P[p + "ln1.b"])
-        qkv = a @ P[p + "attn.w"].T + P[p + "attn.b"]
+        a, c1 = norm(x, p + "ln1")
+        qkv = a @ P[p + "attn.w"].T + bias(p + "attn.b")
         q, k, v = (qkv[:, i * d:(i + 1) * d].reshape(T, H, hd).transpose(1, 0, 2) for i in range(3))
         zp = za = zo = None
         if drop is not None:
@@ -306,17 +343,17 @@ def forward_sequence(P, tok, cfg, drop=None, b=0):
             zo = zm(site_mlp_out(l))
         o, pr = attention_fwd(q, k, v, zp)
         o2 = o.transpose(1, 0, 2).reshape(T, d)
-        y1 = o2 @ P[p + "proj.w"].T + P[p + "proj.b"]
+        y1 = o2 @ P[p + "proj.w"].T + bias(p + "proj.b")
         x1 = x + (y1 if za is None else y1 * za)
-        b2, c2 = layernorm_fwd(x1, P[p + "ln2.g"], P[p + "ln2.b"])
-        u = b2 @ P[p + "fc.w"].T + P[p + "fc.b"]
-        h = gelu(u)
-        y2 = h @ P[p + "fcproj.w"].T + P[p + "fcproj.b"]
+        b2, c2 = norm(x1, p + "ln2")
+        u = b2 @ P[p + "fc.w"].T + bias(p + "fc.b")
+        h = act(u)
+        y2 = h @ P[p + "fcproj.w"].T + bias(p + "fcproj.b")
         x2 = x1 + (y2 if zo is None else y2 * zo)
         layers.append((a, c1, q, k, v, pr, o2, b2, c2, u, h, zp, za, zo))
         x = x2
-    xf, cf = layernorm_fwd(x, P["lnf.g"], P["lnf.b"])
-    z = xf @ P["wte"].T
+    xf, cf = norm(x, "lnf")
+    z = xf @ P["lm_head" if micro else "wte"].T
     return z, (tok, layers, xf, cf, ze)
 
 
@@ -326,41 +363,49 @@ def backward_sequence(P, cache, dz, cfg, G):
     T = len(tok)
     d, H, L = cfg.n_embd, cfg.n_head, cfg.n_layer
     hd = d // H
-    G["wte"] += dz.T @ xf
-    dxf = dz @ P["wte"]
-    dx, dg, db = layernorm_bwd(dxf, cf, P["lnf.g"])
-    G["lnf.g"] += dg
-    G["lnf.b"] += db
+    micro = variant_of(cfg) == "microgpt"
+    head = "lm_head" if micro else "wte"
+
+    def norm_bwd(dy, c, name):
+        if micro:
+            return rmsnorm_bwd(dy, c)
+        dxn, dgn, dbn = layernorm_bwd(dy, c, P[name + ".g"])
+        G[name + ".g"] += dgn
+        G[name + ".b"] += dbn
+        return dxn
+
+    def add_bias(name, g):
+        if not micro:
+            G[name] += g.sum(axis=0)
+
+    act_grad = relu_grad if micro else gelu_grad
+    G[head] += dz.T @ xf
+    dxf = dz @ P[head]
+    dx = norm_bwd(dxf, cf, "lnf")
     for l in reversed(range(L)):
         p = f"h{l}."
         a, c1, q, k, v, pr, o2, b2, c2, u, h, zp, za, zo = layers[l]
         # MLP: x2 = x1 + drop(gelu(LN2(x1) Wfc^T + bfc) Wp^T + bp)
         dy2 = dx if zo is None else dx * zo
         G[p + "fcproj.w"] += dy2.T @ h
-        G[p + "fcproj.b"] += dy2.sum(axis=0)
-        du = (dy2 @ P[p + "fcproj.w"]) * gelu_grad(u)
+        add_bias(p + "fcproj.b", dy2)
+        du = (dy2 @ P[p + "fcproj.w"]) * act_grad(u)
         G[p + "fc.w"] += du.T @ b2
-        G[p + "fc.b"] += du.sum(axis=0)
+        add_bias(p + "fc.b", du)
         db2 = du @ P[p + "fc.w"]
-        dln, dg, dbb = layernorm_bwd(db2, c2, P[p + "ln2.g"])
-        G[p + "ln2.g"] += dg
-        G[p + "ln2.b"] += dbb
-        dx1 = dx + dln
+        dx1 = dx + norm_bwd(db2, c2, p + "ln2")
         # attention: x1 = x + drop(attn(LN1(x)) Wo^T + bo)
         dy1 = dx1 if za is None else dx1 * za
         G[p + "proj.w"] += dy1.T @ o2
-        G[p + "proj.b"] += dy1.sum(axis=0)
+        add_bias(p + "proj.b", dy1)
         do2 = dy1 @ P[p + "proj.w"]
         do = do2.reshape(T, H, hd).transpose(1, 0, 2)
         dq, dk, dv = attention_bwd(do, q, k, v, pr, zp)
         dqkv = np.concatenate([t.transpose(1, 0, 2).reshape(T, d) for t in (dq, dk, dv)], axis=1)
         G[p + "attn.w"] += dqkv.T @ a
-        G[p + "attn.b"] += dqkv.sum(axis=0)
+        add_bias(p + "attn.b", dqkv)
         da = dqkv @ P[p + "attn.w"]
-        dln, dg, dbb = layernorm_bwd(da, c1, P[p + "ln1.g"])
-        G[p + "ln1.g"] += dg
-        G[p + "ln1.b"] += dbb
-        dx = dx1 + dln
+        dx = dx1 + norm_bwd(da, c1, p + "ln1")
     # x0 = drop(wte[tok] + wpe[:T]); repeated ids add up.
     if ze is not None:
         dx = dx * ze

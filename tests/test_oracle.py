@@ -481,3 +481,58 @@ def test_init_std_and_residual_scale():
     assert abs(p["h0.fcproj.w"].std() - 0.02 / math.sqrt(24)) < 2e-4
     assert abs(p["h0.proj.w"].std() - 0.02 / math.sqrt(24)) < 3e-4
     assert np.all(p["h0.ln1.g"] == 1) and np.all(p["h0.attn.b"] == 0)
+
+
+# --------------------------------------------------------------------------- the microGPT variant
+
+def test_micro_param_count_is_the_page_value():
+    g = _gold("page_values.json")["microgpt_param_count"]
+    c = W.CONFIGS["micro"]
+    assert O.n_params(c) == g["value"] == 4192
+    assert W.tensor_table(c) == O.param_shapes(c)
+    assert all(len(sh) == 2 for _, sh in O.param_shapes(c))          # every tensor decays
+
+
+def test_rmsnorm_closed_form_and_invariants():
+    """x = (1, -1, 1, -1): mean square 1, so y = x / sqrt(1 + 1e-5); x = (3, 4):
+    mean square 12.5. The input gradient is orthogonal to xhat up to the eps term:
+    sum(dx xhat) = rstd sum(dy xhat) eps / (ms + eps)."""
+    y, _ = O.rmsnorm_fwd(np.array([[1.0, -1.0, 1.0, -1.0]]))
+    np.testing.assert_allclose(y, [[x / math.sqrt(1 + 1e-5) for x in (1, -1, 1, -1)]], rtol=1e-15)
+    y, _ = O.rmsnorm_fwd(np.array([[3.0, 4.0]]))
+    np.testing.assert_allclose(y, [[3 / math.sqrt(12.5 + 1e-5), 4 / math.sqrt(12.5 + 1e-5)]], rtol=1e-15)
+    rng = np.random.default_rng(11)
+    x = rng.normal(size=(6, 24)) * 2 + 0.5
+    dy = rng.normal(size=(6, 24))
+    xh, cache = O.rmsnorm_fwd(x)
+    dx = O.rmsnorm_bwd(dy, cache)
+    ms = (x * x).mean(-1, keepdims=True)
+    rstd = cache[1]
+    expect = (rstd * (dy * xh).sum(-1, keepdims=True) * 1e-5 / (ms + 1e-5))[:, 0]
+    np.testing.assert_allclose((dx * xh).sum(-1), expect, rtol=1e-6, atol=1e-15)
+
+
+def test_micro_zero_head_gives_log_vocab():
+    c = W.CONFIGS["micro"]
+    drng, wrng = W.rngs()
+    params = W.init_params(c, wrng)
+    params["lm_head"][:] = 0.0
+    tok, tgt = W.make_batch(c, drng)
+    rl, _ = O.microbatch(params, tok, tgt, c)
+    np.testing.assert_allclose(rl, math.log(c.padded_vocab), rtol=0, atol=1e-12)
+
+
+def test_finite_difference_micro():
+    c = W.CONFIGS["micro"]
+    drng, wrng = W.rngs()
+    params = W.init_params(c, wrng)
+    tok, tgt = W.make_batch(c, drng)
+    assert _fd_check(c, params, tok, tgt) > 100
+
+
+def test_finite_difference_micro_with_dropout():
+    c = W.CONFIGS["micro"]
+    drng, wrng = W.rngs()
+    params = W.init_params(c, wrng)
+    tok, tgt = W.make_batch(c, drng)
+    assert _fd_check(c, params, tok, tgt, dropout=O.Dropout(0.25, 77)) > 100

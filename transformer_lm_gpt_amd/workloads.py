@@ -60,6 +60,7 @@ class GPTConfig:
     grad_clip: float = 1.0
     parity_steps: int = 1
     precisions: Tuple[str, ...] = ("bf16",)
+    variant: str = "gpt2"    # "gpt2" | "microgpt" (weightless RMSNorm, ReLU, no biases, untied head)
 
     @property
     def head_dim(self) -> int:
@@ -96,6 +97,12 @@ CONFIGS: Dict[str, GPTConfig] = {
 
 ORDER = ["tiny", "char_small", "char_6l", "bpe_12l_512", "gpt2_124m"]
 
+# The microGPT block ("Building microGPT from scratch", model-core section) at the
+# page's own size (4,192 parameters) and at the char_small shape.
+CONFIGS["micro"] = CONFIGS["tiny"].with_(name="micro", variant="microgpt")
+CONFIGS["char_small_micro"] = CONFIGS["char_small"].with_(name="char_small_micro", variant="microgpt")
+VARIANT_CONFIGS = ["micro", "char_small_micro"]
+
 
 def rngs(seed: int = SEED) -> Tuple[np.random.Generator, np.random.Generator]:
     """(data stream, weight stream): two independent PCG64 generators."""
@@ -109,6 +116,12 @@ def tensor_table(cfg: GPTConfig) -> List[Tuple[str, Tuple[int, ...]]]:
     """Names and shapes of the trainable tensors, linear weights as [out, in]."""
     V, d, T, L = cfg.padded_vocab, cfg.n_embd, cfg.block_size, cfg.n_layer
     out = [("wte", (V, d)), ("wpe", (T, d))]
+    if cfg.variant == "microgpt":
+        for l in range(L):
+            p = f"h{l}."
+            out += [(p + "attn.w", (3 * d, d)), (p + "proj.w", (d, d)),
+                    (p + "fc.w", (4 * d, d)), (p + "fcproj.w", (d, 4 * d))]
+        return out + [("lm_head", (V, d))]
     for l in range(L):
         p = f"h{l}."
         out += [(p + "ln1.g", (d,)), (p + "ln1.b", (d,)),
