@@ -61,6 +61,14 @@ extern "C" {
 #define GPT_PREC_FP32 0        /* every GEMM operand fp32                            */
 #define GPT_F_KV_CACHE 1u      /* gpt_config.flags: reserve the key/value cache of
                                   gpt_prefill / gpt_decode in the workspace           */
+#define GPT_F_MICROGPT 2u      /* gpt_config.flags: the microGPT block ("Building
+                                  microGPT from scratch", model-core section):
+                                  weightless RMSNorm y = x / sqrt(mean(x^2) + 1e-5)
+                                  where the LayerNorms are, ReLU instead of GELU, no
+                                  biases and an lm_head [padded_vocab, n_embd] of its
+                                  own (tensors wte, wpe, h<l>.attn.w (q|k|v rows),
+                                  h<l>.proj.w, h<l>.fc.w, h<l>.fcproj.w, lm_head; all
+                                  decayed)                                           */
 #define GPT_PREC_BF16 1        /* GEMM/attention operands bf16, everything else fp32 */
 
 typedef struct gpt_model gpt_model;
@@ -76,7 +84,7 @@ typedef struct gpt_config {
   int32_t grad_accum;    /* A: backward scales the micro-batch mean loss by 1/A     */
   int32_t precision;     /* GPT_PREC_FP32 or GPT_PREC_BF16                          */
   float   dropout;       /* p in [0, 1): see gpt_set_dropout_seed                   */
-  uint32_t flags;        /* 0 or GPT_F_KV_CACHE                                     */
+  uint32_t flags;        /* GPT_F_KV_CACHE | GPT_F_MICROGPT, or 0                   */
 } gpt_config;
 
 typedef struct gpt_sizes {

@@ -37,7 +37,7 @@ def test_library_is_gfx950_only():
         assert other not in blob
 
 
-@pytest.mark.parametrize("name", W.ORDER)
+@pytest.mark.parametrize("name", W.ORDER + W.VARIANT_CONFIGS)
 @pytest.mark.parametrize("prec", ["fp32", "bf16"])
 def test_layout_matches_oracle(name, prec):
     cfg = W.CONFIGS[name]
@@ -78,7 +78,7 @@ def _raw(**kw):
     (dict(n_head=0), -1),
     (dict(padded_vocab=10), -1),           # below vocab_size
     (dict(precision=7), -1),
-    (dict(flags=2), -1),                   # unknown flag
+    (dict(flags=4), -1),                   # unknown flag
     (dict(dropout=1.0), -1),               # dropout must be in [0, 1)
     (dict(dropout=-0.1), -1),
     (dict(dropout=float("nan")), -1),

@@ -1,0 +1,66 @@
+"""The microGPT block variant (weightless RMSNorm, ReLU, no biases, an lm_head of
+its own) on the HIP path against the oracle: full optimizer steps, with dropout,
+and generation with the key/value cache."""
+import numpy as np
+import pytest
+
+from oracle import gpt_oracle as O
+from transformer_lm_gpt_amd import workloads as W
+
+from gpu_helpers import rel, run_steps, say
+
+pytestmark = pytest.mark.gpu
+
+
+# bf16 bound for this variant: ReLU's derivative jumps at 0, and the pre-activation
+# formed from bf16 operands carries about 2^-9 relative rounding, which flips the
+# gate of the few elements that lie that close to 0; each flip changes its element
+# of the MLP input gradient by its whole value. Measured against the fp32 GPU path
+# (which matches the oracle to 4e-7): 1.2-3.3e-2 per tensor at the char_small shape,
+# the largest in layer 0 and the embeddings, which collect every layer's flips. The
+# smooth-GELU block of the same shape stays within 5.5e-3. The variant's bf16 steps
+# are therefore held to 5e-2 for one optimizer step (fp32 keeps the strict bound over
+# ten). Over several bf16 steps the two trajectories part by design: the gates that
+# flipped feed Adam's nearly sign-like first updates, and the flips compound.
+MICRO_BF16_TOL = 5e-2
+
+
+@pytest.mark.parametrize("name,prec,steps,B,T,A", [
+    ("micro", "fp32", 10, None, None, None),      # the page's 4,192-parameter model
+    ("micro", "fp32", 2, 3, 11, 2),               # ragged, two micro-batches
+    ("char_small_micro", "fp32", 3, None, None, None),
+    ("char_small_micro", "bf16", 1, None, None, None),
+])
+def test_micro_step_parity(name, prec, steps, B, T, A):
+    run_steps(name, prec, steps=steps, B=B, T=T, A=A, perturb=False,
+              rel_tol=MICRO_BF16_TOL if prec == "bf16" else None)
+
+
+def test_micro_step_parity_with_dropout():
+    # one step: a second fp32 step already parts by 1.8e-3 (the first Adam update turns
+    # the 4e-7 gradient differences of near-zero gradients into lr-sized weight
+    # differences, and the ReLU gates amplify them); the first matches to 4.4e-7
+    run_steps("char_small_micro", "fp32", steps=1, dropout=0.2, seed=0xABCDEF, counter=1, perturb=False)
+    run_steps("char_small_micro", "bf16", steps=1, dropout=0.2, seed=0xABCDEF, counter=1, perturb=False,
+              rel_tol=MICRO_BF16_TOL)
+
+
+@pytest.mark.parametrize("name,prec", [("micro", "fp32"), ("char_small_micro", "bf16")])
+def test_micro_decode_matches_full_forward(name, prec):
+    from transformer_lm_gpt_amd.binding import GPT
+    cfg = W.CONFIGS[name]
+    drng, wrng = W.rngs()
+    params = W.init_params(cfg, wrng)
+    B, T0, steps = 3, 6, 5
+    tok, _ = W.make_batch(cfg, drng, B=B, T=T0 + steps)
+    say(f"[micro decode] {name} {prec}")
+    gpu = GPT(cfg, prec, kv_cache=True)
+    gpu.load_params(params)
+    tol = 1e-5 if prec == "fp32" else 2e-2
+    z = gpu.prefill(tok[:, :T0]).cpu().numpy()
+    assert rel(z, O.logits(params, tok[:, :T0], cfg)[:, -1]) < tol
+    for s in range(steps):
+        z = gpu.decode(tok[:, T0 + s]).cpu().numpy()
+        zr = O.logits(params, tok[:, :T0 + s + 1], cfg)[:, -1]
+        assert rel(z, zr) < tol, (s, rel(z, zr))
+    gpu.close()

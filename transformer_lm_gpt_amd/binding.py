@@ -102,6 +102,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
 
 
 F_KV_CACHE = 1
+F_MICROGPT = 2
 
 
 def make_config(cfg, precision: str, batch: Optional[int] = None, grad_accum: Optional[int] = None,
@@ -109,7 +110,7 @@ def make_config(cfg, precision: str, batch: Optional[int] = None, grad_accum: Op
     return gpt_config(cfg.vocab_size, cfg.padded_vocab, cfg.n_layer, cfg.n_head, cfg.n_embd, cfg.block_size,
                       cfg.batch if batch is None else batch,
                       cfg.grad_accum if grad_accum is None else grad_accum, PREC[precision], float(dropout),
-                      F_KV_CACHE if kv_cache else 0)
+                      (F_KV_CACHE if kv_cache else 0) | (F_MICROGPT if getattr(cfg, "variant", "gpt2") == "microgpt" else 0))
 
 
 class Layout:

@@ -185,7 +185,11 @@ struct GemmArgs {
 
 // Epilogues that add a residual (with or without dropout on the branch) and those with a bias.
 template <int EPI> constexpr bool epi_resid() { return EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_RESID_DROP; }
-template <int EPI> constexpr bool epi_has_bias() { return EPI == EPI_BIAS || epi_resid<EPI>() || EPI == EPI_BIAS_GELU; }
+template <int EPI> constexpr bool epi_has_bias() {
+  return EPI == EPI_BIAS || epi_resid<EPI>() || EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_RELU;
+}
+// Epilogues that scale by the activation's derivative at the saved input (and can sum columns).
+template <int EPI> constexpr bool epi_act_bwd() { return EPI == EPI_GELU_BWD || EPI == EPI_RELU_BWD; }
 
 template <int EPI>
 __device__ inline float epi_bias(const GemmArgs& p, int col) {
@@ -218,8 +222,14 @@ __device__ inline void epi_store(const GemmArgs& p, int row, int col, float v, f
     ((T*)p.C)[ci] = from_f32<T>(gelu_f(u));
   } else if constexpr (EPI == EPI_F32) {
     ((float*)p.C)[ci] = v;
+  } else if constexpr (EPI == EPI_BIAS_RELU) {
+    const float u = v + bias;
+    ((T*)p.aux)[(int64_t)row * p.ldaux + col] = from_f32<T>(u);
+    ((T*)p.C)[ci] = from_f32<T>(fmaxf(u, 0.f));
   } else if constexpr (EPI == EPI_GELU_BWD) {
     ((T*)p.C)[ci] = from_f32<T>(v * gelu_grad_f(to_f32(((const T*)p.aux)[(int64_t)row * p.ldaux + col])));
+  } else if constexpr (EPI == EPI_RELU_BWD) {
+    ((T*)p.C)[ci] = from_f32<T>(to_f32(((const T*)p.aux)[(int64_t)row * p.ldaux + col]) > 0.f ? v : 0.f);
   } else {  // EPI_ACC
     if (gridDim.z > 1) {
       p.part[((int64_t)blockIdx.z * p.M + row) * p.N + col] = v;
@@ -235,15 +245,15 @@ __device__ inline void epi_store(const GemmArgs& p, int row, int col, float v, f
 // block are in flight while the current one is stored.
 template <int EPI>
 struct EpiPre {
-  static constexpr bool ON = epi_resid<EPI>() || EPI == EPI_GELU_BWD;
+  static constexpr bool ON = epi_resid<EPI>() || epi_act_bwd<EPI>();
   f32x4 r[epi_resid<EPI>() ? 4 : 1];
-  bf16x8 u[EPI == EPI_GELU_BWD ? 2 : 1];
+  bf16x8 u[epi_act_bwd<EPI>() ? 2 : 1];
   __device__ inline void load(const GemmArgs& p, int row, int col0) {
     if constexpr (epi_resid<EPI>()) {
       const float* src = p.resid + (int64_t)row * p.ldr + col0;
 #pragma unroll
       for (int q = 0; q < 4; q++) r[q] = *(const f32x4*)(src + 4 * q);
-    } else if constexpr (EPI == EPI_GELU_BWD) {
+    } else if constexpr (epi_act_bwd<EPI>()) {
       const bf16* src = (const bf16*)p.aux + (int64_t)row * p.ldaux + col0;
 #pragma unroll
       for (int q = 0; q < 2; q++) u[q] = *(const bf16x8*)(src + 8 * q);
@@ -267,6 +277,8 @@ __device__ inline void epi_store16(const GemmArgs& p, int row, int col0, const f
         epi_store<bf16, EPI>(p, row, col0 + c, v[c], epi_bias<EPI>(p, col0 + c));
         if constexpr (EPI == EPI_GELU_BWD)
           sum16[c] += v[c] * gelu_grad_f((float)((const bf16*)p.aux)[(int64_t)row * p.ldaux + col0 + c]);
+        if constexpr (EPI == EPI_RELU_BWD)
+          sum16[c] += (float)((const bf16*)p.aux)[(int64_t)row * p.ldaux + col0 + c] > 0.f ? v[c] : 0.f;
       }
     return;
   }
@@ -321,6 +333,33 @@ __device__ inline void epi_store16(const GemmArgs& p, int row, int col0, const f
         o[e] = (bf16)gelu_f(x[8 * q + e]);
       }
       *(bf16x8*)(u + 8 * q) = uo;
+      *(bf16x8*)((bf16*)p.C + ci + 8 * q) = o;
+    }
+  } else if constexpr (EPI == EPI_BIAS_RELU) {
+    bf16* u = (bf16*)p.aux + (int64_t)row * p.ldaux + col0;
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      bf16x8 uo, o;
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        uo[e] = (bf16)x[8 * q + e];
+        o[e] = (bf16)fmaxf(x[8 * q + e], 0.f);
+      }
+      *(bf16x8*)(u + 8 * q) = uo;
+      *(bf16x8*)((bf16*)p.C + ci + 8 * q) = o;
+    }
+  } else if constexpr (EPI == EPI_RELU_BWD) {
+    const bf16* u = (const bf16*)p.aux + (int64_t)row * p.ldaux + col0;
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      const bf16x8 uv = pre ? pre->u[q] : *(const bf16x8*)(u + 8 * q);
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const float y = (float)uv[e] > 0.f ? x[8 * q + e] : 0.f;
+        o[e] = (bf16)y;
+        sum16[8 * q + e] += y;
+      }
       *(bf16x8*)((bf16*)p.C + ci + 8 * q) = o;
     }
   } else if constexpr (EPI == EPI_F32) {
@@ -667,7 +706,7 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, 
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   float* scr = (float*)smem + wave * 16 * ELD;
   // fused bias gradient (GELU backward): this lane's column sums of its items
-  constexpr bool CS = EPI == EPI_GELU_BWD;
+  constexpr bool CS = epi_act_bwd<EPI>();
   const bool colsum = CS && p.colsum && !park;
   float cs[PASSES][16];
 #pragma unroll
@@ -842,6 +881,8 @@ static hipError_t dma_epi(const GemmArgs& a, int epi, int splits, hipStream_t s)
     GPT_DMA_CASE(EPI_GELU_BWD)
     GPT_DMA_CASE(EPI_ACC)
     GPT_DMA_CASE(EPI_BIAS_RESID_DROP)
+    GPT_DMA_CASE(EPI_BIAS_RELU)
+    GPT_DMA_CASE(EPI_RELU_BWD)
 #undef GPT_DMA_CASE
     default: return hipErrorInvalidValue;
   }
@@ -867,6 +908,8 @@ static hipError_t sk_epi(const GemmArgs& a, int epi, int W, float* ws, int maxse
     GPT_SK_CASE(EPI_GELU_BWD)
     GPT_SK_CASE(EPI_ACC)
     GPT_SK_CASE(EPI_BIAS_RESID_DROP)
+    GPT_SK_CASE(EPI_BIAS_RELU)
+    GPT_SK_CASE(EPI_RELU_BWD)
 #undef GPT_SK_CASE
     default: return hipErrorInvalidValue;
   }
@@ -915,6 +958,8 @@ static hipError_t dispatch_epi(const GemmArgs& a, int epi, dim3 grid, hipStream_
     GPT_EPI_CASE(EPI_GELU_BWD)
     GPT_EPI_CASE(EPI_ACC)
     GPT_EPI_CASE(EPI_BIAS_RESID_DROP)
+    GPT_EPI_CASE(EPI_BIAS_RELU)
+    GPT_EPI_CASE(EPI_RELU_BWD)
 #undef GPT_EPI_CASE
     default: return hipErrorInvalidValue;
   }
@@ -1088,6 +1133,7 @@ static hipError_t skinny_epi(const GemmArgs& a, int epi, hipStream_t s) {
     GPT_SKINNY_CASE(EPI_BIAS)
     GPT_SKINNY_CASE(EPI_BIAS_RESID)
     GPT_SKINNY_CASE(EPI_BIAS_GELU)
+    GPT_SKINNY_CASE(EPI_BIAS_RELU)
     GPT_SKINNY_CASE(EPI_F32)
 #undef GPT_SKINNY_CASE
     default: return hipErrorInvalidValue;
@@ -1135,7 +1181,7 @@ static bool use_k192(const GemmDesc& d, bool bf16_operands) {
 }
 
 int gemm_colsum_rows(const GemmDesc& d, bool bf16_operands) {
-  if (d.epi != EPI_GELU_BWD || !use_k192(d, bf16_operands)) return 0;
+  if ((d.epi != EPI_GELU_BWD && d.epi != EPI_RELU_BWD) || !use_k192(d, bf16_operands)) return 0;
   return (d.M + 191) / 192;
 }
 
@@ -1163,7 +1209,7 @@ hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
   }
   // few rows, both operands k-contiguous, aligned 16-byte fragments
   if (bf16_operands && d.M <= 16 && d.a_kc && d.b_kc && d.K % 32 == 0 && a.a_vec && a.b_vec &&
-      (d.epi == EPI_STORE || d.epi == EPI_BIAS || d.epi == EPI_BIAS_RESID || d.epi == EPI_BIAS_GELU ||
+      (d.epi == EPI_STORE || d.epi == EPI_BIAS || d.epi == EPI_BIAS_RESID || d.epi == EPI_BIAS_GELU || d.epi == EPI_BIAS_RELU ||
        d.epi == EPI_F32))
     return skinny_epi(a, d.epi, s);
   const bool pipelined = pipelined_ok(d, bf16_operands);

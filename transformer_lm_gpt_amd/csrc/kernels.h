@@ -38,6 +38,8 @@ enum Epilogue {
   EPI_GELU_BWD = 5,    // C(T)   = acc * gelu'(aux[m, n])   (aux in operand type T)
   EPI_ACC = 6,         // C(f32) = beta * C + acc   (beta is 0 or 1; C is not read when 0)
   EPI_BIAS_RESID_DROP = 7,  // C(f32) = resid[m, n] + mask(drop_site, m, n) * (acc + bias[n])
+  EPI_BIAS_RELU = 8,   // aux(T) = u = acc + bias[n];  C(T) = max(u, 0)
+  EPI_RELU_BWD = 9,    // C(T)   = acc * (aux[m, n] > 0)   (aux in operand type T)
 };
 
 // C[m, n] = sum_k A(m, k) B(n, k) followed by the epilogue, where
@@ -107,12 +109,18 @@ hipError_t launch_dropout_rows(const float* src, float* dst, int M, int d, const
 hipError_t launch_layernorm_fwd(const float* x, const float* g, const float* b, void* y, bool bf16_out,
                                 float* mean, float* rstd, int M, int d, hipStream_t s);
 
+// Weightless RMSNorm y = x / sqrt(mean(x^2) + 1e-5) (operand type); writes mean = 0 and
+// rstd, so launch_layernorm_bwd with g = NULL is its backward. d a multiple of 4.
+hipError_t launch_rmsnorm_fwd(const float* x, void* y, bool bf16_out, float* mean, float* rstd, int M, int d,
+                              hipStream_t s);
+
 // dx = dres + LN backward of dy; writes dx (fp32) and optionally its operand-type copy
 // dx_op; per-block partial column sums of dy * xhat, dy and dres (dres may be NULL,
 // then part_r is unused) into part_g / part_b / part_r ([nblk, d] each,
 // nblk = ceil(M / LN_BWD_ROWS)). dx may alias dres. d must be a multiple of 4.
 // With da.on, the dres column sums take dres * mask(site_in) when site_in >= 0,
 // and dx_op holds dx * mask(site_out) when site_out >= 0 (dx itself is unmasked).
+// g = NULL: the backward of the weightless RMSNorm (part_g and part_b unused).
 constexpr int LN_BWD_ROWS = 16;
 hipError_t launch_layernorm_bwd(const float* dy, const float* x, const float* mean, const float* rstd,
                                 const float* g, const float* dres, float* dx, void* dx_op, bool bf16_out,

@@ -179,6 +179,51 @@ hipError_t launch_layernorm_fwd(const float* x, const float* g, const float* b, 
   return ln_fwd_t<float>(x, g, b, (float*)y, mean, rstd, M, d, s);
 }
 
+// Weightless RMSNorm (the microGPT block): y = x / sqrt(mean(x^2) + 1e-5). One
+// wavefront per row, d a multiple of 4; writes mean = 0 and rstd so that the
+// LayerNorm backward's xhat = (x - mean) rstd is this norm's output.
+template <typename T>
+__global__ __launch_bounds__(256) void rms_fwd_kernel(const float* __restrict__ x, T* __restrict__ y,
+                                                      float* __restrict__ mean, float* __restrict__ rstd, int M, int d) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int d4 = d >> 2;
+  const f32x4* xr = (const f32x4*)(x + (int64_t)row * d);
+  float s = 0.f;
+  for (int c4 = lane; c4 < d4; c4 += 64) {
+    const f32x4 v = xr[c4];
+    s += (v[0] * v[0] + v[1] * v[1]) + (v[2] * v[2] + v[3] * v[3]);
+  }
+  const float rs = 1.0f / sqrtf(wave_sum(s) / d + 1e-5f);
+  for (int c4 = lane; c4 < d4; c4 += 64) {
+    const f32x4 v = xr[c4];
+    if constexpr (sizeof(T) == 2) {
+      bf16x4 ob;
+#pragma unroll
+      for (int e = 0; e < 4; e++) ob[e] = (bf16)(v[e] * rs);
+      ((bf16x4*)(y + (int64_t)row * d))[c4] = ob;
+    } else {
+      ((f32x4*)(y + (int64_t)row * d))[c4] = v * rs;
+    }
+  }
+  if (lane == 0) {
+    mean[row] = 0.f;
+    rstd[row] = rs;
+  }
+}
+
+hipError_t launch_rmsnorm_fwd(const float* x, void* y, bool bf16_out, float* mean, float* rstd, int M, int d,
+                              hipStream_t s) {
+  if (d % 4 != 0 || (uintptr_t)x % 16 != 0 || (uintptr_t)y % (bf16_out ? 8 : 16) != 0) return hipErrorInvalidValue;
+  dim3 grid((M + 3) / 4);
+  if (bf16_out)
+    hipLaunchKernelGGL(rms_fwd_kernel<bf16>, grid, dim3(256), 0, s, x, (bf16*)y, mean, rstd, M, d);
+  else
+    hipLaunchKernelGGL(rms_fwd_kernel<float>, grid, dim3(256), 0, s, x, (float*)y, mean, rstd, M, d);
+  return hipGetLastError();
+}
+
 // Backward: with xhat = (x - mu) rstd and gh = dy * g,
 //   dx = rstd (gh - mean(gh) - xhat mean(gh xhat)) + dres.
 // One wavefront per row, LN_BWD_ROWS rows per workgroup. Each lane owns
@@ -191,8 +236,10 @@ hipError_t launch_layernorm_fwd(const float* x, const float* g, const float* b, 
 // gradient of the dropped branch output whose add fed this residual) and dx_op
 // holds dx times the mask of site_out (the operand of the branch below); a
 // negative site leaves that side unmasked.
+// With RMS (the weightless RMSNorm, mean = 0 saved): gh = dy, no mean(gh) term,
+// and no gain or shift partials.
 constexpr int LN_MAX_D = 1024;
-template <typename T, int NCH, bool DROP>
+template <typename T, int NCH, bool DROP, bool RMS = false>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ dy, const float* __restrict__ x,
                                                      const float* __restrict__ mean,
                                                      const float* __restrict__ rstd, const float* __restrict__ g,
@@ -207,7 +254,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
 #pragma unroll
   for (int j = 0; j < NCH; j++) {
     const int c4 = j * 64 + lane;
-    gg[j] = c4 < d4 ? ((const f32x4*)g)[c4] : (f32x4){0.f, 0.f, 0.f, 0.f};
+    gg[j] = RMS ? (f32x4){1.f, 1.f, 1.f, 1.f} : (c4 < d4 ? ((const f32x4*)g)[c4] : (f32x4){0.f, 0.f, 0.f, 0.f});
     pg[j] = pb[j] = pr[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
   const int row0 = blockIdx.x * LN_BWD_ROWS;
@@ -254,7 +301,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
         }
       }
     }
-    const float a = wave_sum(sa) / d;
+    const float a = RMS ? 0.f : wave_sum(sa) / d;
     const float bb = wave_sum(sbb) / d;
 #pragma unroll
     for (int j = 0; j < NCH; j++) {
@@ -285,7 +332,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
   // fixed-order combine of the four waves, one quantity at a time
   float* const outs[3] = {part_g, part_b, part_r};
 #pragma unroll
-  for (int q = 0; q < 3; q++) {
+  for (int q = RMS ? 2 : 0; q < 3; q++) {
     if (q == 2 && !part_r) break;
 #pragma unroll
     for (int j = 0; j < NCH; j++) {
@@ -303,7 +350,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
   }
 }
 
-template <typename T, bool DROP>
+template <typename T, bool DROP, bool RMS = false>
 static hipError_t ln_bwd_t(const float* dy, const float* x, const float* mean, const float* rstd, const float* g,
                            const float* dres, float* dx, void* dx_op, float* pg, float* pb, float* pr, int M, int d,
                            const DropArgs& da, int si, int so, hipStream_t s) {
@@ -311,7 +358,7 @@ static hipError_t ln_bwd_t(const float* dy, const float* x, const float* mean, c
   const int nch = (d / 4 + 63) / 64;
   switch (nch) {
 #define LNB(N) \
-  case N: hipLaunchKernelGGL((ln_bwd_kernel<T, N, DROP>), grid, dim3(256), 0, s, dy, x, mean, rstd, g, dres, dx, (T*)dx_op, pg, pb, pr, M, d, da, si, so); break;
+  case N: hipLaunchKernelGGL((ln_bwd_kernel<T, N, DROP, RMS>), grid, dim3(256), 0, s, dy, x, mean, rstd, g, dres, dx, (T*)dx_op, pg, pb, pr, M, d, da, si, so); break;
     LNB(1) LNB(2) LNB(3) LNB(4)
 #undef LNB
     default: return hipErrorInvalidValue;
@@ -325,6 +372,17 @@ hipError_t launch_layernorm_bwd(const float* dy, const float* x, const float* me
                                 int site_in, int site_out, hipStream_t s) {
   if (d > LN_MAX_D || d % 4 != 0) return hipErrorInvalidValue;
   const bool drop = da.on && (site_in >= 0 || site_out >= 0);
+  if (!g) {   // weightless RMSNorm
+    if (bf16_out)
+      return drop ? ln_bwd_t<bf16, true, true>(dy, x, mean, rstd, g, dres, dx, dx_op, part_g, part_b, part_r, M, d,
+                                               da, site_in, site_out, s)
+                  : ln_bwd_t<bf16, false, true>(dy, x, mean, rstd, g, dres, dx, dx_op, part_g, part_b, part_r, M, d,
+                                                da, site_in, site_out, s);
+    return drop ? ln_bwd_t<float, true, true>(dy, x, mean, rstd, g, dres, dx, dx_op, part_g, part_b, part_r, M, d,
+                                              da, site_in, site_out, s)
+                : ln_bwd_t<float, false, true>(dy, x, mean, rstd, g, dres, dx, dx_op, part_g, part_b, part_r, M, d,
+                                               da, site_in, site_out, s);
+  }
   if (bf16_out)
     return drop ? ln_bwd_t<bf16, true>(dy, x, mean, rstd, g, dres, dx, dx_op, part_g, part_b, part_r, M, d, da,
                                        site_in, site_out, s)

@@ -111,6 +111,10 @@ struct gpt_model {
   uint32_t drop_call = 0;
   DropArgs drop_fwd{};
   int kv_len = 0, kv_B = 0;   // cached positions per sequence and sequences, after gpt_prefill
+  // GPT_F_MICROGPT: weightless RMSNorm, ReLU, no biases, an lm_head of its own
+  bool micro = false;
+  std::string head = "wte";   // the tensor the logits are taken against
+  Slice zbias;                // zeros standing in for the absent biases (4d floats)
   // state
   bool grads_fresh = true;
   bool fwd_pending = false;
@@ -242,8 +246,9 @@ void plan(gpt_model* h) {
     add(p + "fc.w", 4 * d, d, 2, 1);
     add(p + "fcproj.w", d, 4 * d, 2, 1);
   }
+  if (h->micro) add("lm_head", Vp, d, 2, 1);
   h->n_decay = off;
-  for (int l = 0; l < L; l++) {
+  for (int l = 0; l < L && !h->micro; l++) {
     const std::string p = "h" + std::to_string(l) + ".";
     add(p + "ln1.g", d, 1, 1, 0);
     add(p + "ln1.b", d, 1, 1, 0);
@@ -254,8 +259,10 @@ void plan(gpt_model* h) {
     add(p + "fc.b", 4 * d, 1, 1, 0);
     add(p + "fcproj.b", d, 1, 1, 0);
   }
-  add("lnf.g", d, 1, 1, 0);
-  add("lnf.b", d, 1, 1, 0);
+  if (!h->micro) {
+    add("lnf.g", d, 1, 1, 0);
+    add("lnf.b", d, 1, 1, 0);
+  }
   h->n_flat = round_up(off, 256);
 
   // ---- activations for the largest micro-batch
@@ -325,13 +332,15 @@ void plan(gpt_model* h) {
   };
   // kinds: RED_LN LayerNorm backward partials, RED_QKV and RED_FC the qkv and fc
   // bias column sums (from the GEMM epilogue or a column-sum pass)
-  red_job("lnf.g", RED_LN);
-  red_job("lnf.b", RED_LN);
-  for (int l = 0; l < h->L; l++) {
-    const std::string p = "h" + std::to_string(l) + ".";
-    for (const char* n : {"ln1.g", "ln1.b", "proj.b", "ln2.g", "ln2.b", "fcproj.b"}) red_job(p + n, RED_LN);
-    red_job(p + "fc.b", RED_FC);
-    red_job(p + "attn.b", RED_QKV);
+  if (!h->micro) {   // the microGPT block has no bias or norm parameter
+    red_job("lnf.g", RED_LN);
+    red_job("lnf.b", RED_LN);
+    for (int l = 0; l < h->L; l++) {
+      const std::string p = "h" + std::to_string(l) + ".";
+      for (const char* n : {"ln1.g", "ln1.b", "proj.b", "ln2.g", "ln2.b", "fcproj.b"}) red_job(p + n, RED_LN);
+      red_job(p + "fc.b", RED_FC);
+      red_job(p + "attn.b", RED_QKV);
+    }
   }
   h->red = w.take(red_floats * fb);
   h->rtable = w.take(h->rjobs.size() * sizeof(RedJob));
@@ -352,6 +361,7 @@ void plan(gpt_model* h) {
   }
   h->ttable = w.take(h->tentries.size() * sizeof(TransposeEntry));
   h->opt = w.take(sizeof(OptState));
+  h->zbias = w.take(4 * (size_t)d * fb);
   // the weight gradients as one grouped launch: wte (tied lm_head), then per layer
   // fcproj.w, fc.w, proj.w, attn.w; operands are [tokens, features] (m-contiguous)
   if (h->bf16) {
@@ -385,13 +395,29 @@ int colsum(gpt_model* h, const void* X, bool bf16_in, int64_t ldx, int M, int N,
 int ln_bwd(gpt_model* h, const float* dy, const float* x, const float* mean, const float* rstd,
            const std::string& gname, const std::string& bname, const float* dres, const char* resid_bias, void* dx_op,
            int M, int site_in = -1, int site_out = -1) {
-  float* pr = resid_bias ? red_part(h, resid_bias) : nullptr;
+  // the microGPT block: weightless RMSNorm (g = NULL), and no bias to take column sums for
+  float* pr = resid_bias && !h->micro ? red_part(h, resid_bias) : nullptr;
+  const float* g = h->micro ? nullptr : P(h, gname);
+  float* pg = h->micro ? nullptr : red_part(h, gname);
+  float* pb = h->micro ? nullptr : red_part(h, bname);
   RUN("layernorm", "layernorm_bwd",
-      launch_layernorm_bwd(dy, x, mean, rstd, P(h, gname), dres, ws<float>(h, h->dres), dx_op, h->bf16,
-                           red_part(h, gname), red_part(h, bname), pr, M, h->d, h->drop_fwd, site_in, site_out,
-                           h->stream));
+      launch_layernorm_bwd(dy, x, mean, rstd, g, dres, ws<float>(h, h->dres), dx_op, h->bf16, pg, pb, pr, M, h->d,
+                           h->drop_fwd, site_in, site_out, h->stream));
   return GPT_OK;
 }
+
+// The block's norm in front of a GEMM: LayerNorm with gain and shift `name`.g / .b,
+// or the microGPT block's weightless RMSNorm.
+int norm_fwd(gpt_model* h, const float* x, const std::string& name, void* y, float* mean, float* rstd, int M) {
+  if (h->micro)
+    RUN("layernorm", "rms_fwd", launch_rmsnorm_fwd(x, y, h->bf16, mean, rstd, M, h->d, h->stream));
+  else
+    RUN("layernorm", "ln_fwd",
+        launch_layernorm_fwd(x, P(h, name + ".g"), P(h, name + ".b"), y, h->bf16, mean, rstd, M, h->d, h->stream));
+  return GPT_OK;
+}
+// A linear layer's bias, or zeros for the microGPT block.
+const float* bias_of(gpt_model* h, const std::string& name) { return h->micro ? ws<float>(h, h->zbias) : P(h, name); }
 
 // bf16 operand slots of the backward (see gpt_model)
 void* rx_slot(gpt_model* h, int l) { return (char*)ws(h, h->rx) + (size_t)l * h->resid_stride; }
@@ -415,7 +441,7 @@ void build_wgrad_table(gpt_model* h) {
     h->wtiles += wgrad_group_tiles(Mo, No);
     h->wprobs.push_back(q);
   };
-  add(act(h, h->logits), h->ldz, act(h, h->lnf), d, "wte", h->Vp, d);
+  add(act(h, h->logits), h->ldz, act(h, h->lnf), d, h->head, h->Vp, d);
   for (int l = h->L - 1; l >= 0; l--) {
     const LayerAct& la = h->layers[l];
     const std::string p = "h" + std::to_string(l) + ".";
@@ -461,13 +487,13 @@ int forward_to_logits(gpt_model* h, int B, int T, const DropArgs& da) {
     float* x = act<float>(h, la.x);
     float* xmid = act<float>(h, la.xmid);
     float* xnext = (l + 1 < h->L) ? act<float>(h, h->layers[l + 1].x) : act<float>(h, h->x_final);
-    RUN("layernorm", "ln1_fwd",
-        launch_layernorm_fwd(x, P(h, p + "ln1.g"), P(h, p + "ln1.b"), act(h, la.ln1), bf, act<float>(h, la.ln1_mean),
-                             act<float>(h, la.ln1_rstd), M, d, s));
+    int rc;
+    if ((rc = norm_fwd(h, x, p + "ln1", act(h, la.ln1), act<float>(h, la.ln1_mean), act<float>(h, la.ln1_rstd), M)))
+      return rc;
     {
       GemmDesc g = gemm_desc(act(h, la.ln1), d, true, Wop(h, p + "attn.w"), d, true, act(h, la.qkv), 3 * d, M,
                              3 * d, d, EPI_BIAS);
-      g.bias = P(h, p + "attn.b");
+      g.bias = bias_of(h, p + "attn.b");
       RUN("gemm_fwd", "qkv_fwd", gemm(h, g, bf));
     }
     RUN("attn_fwd", "attn_fwd",
@@ -475,20 +501,20 @@ int forward_to_logits(gpt_model* h, int B, int T, const DropArgs& da) {
                         site_attn_prob(l), s));
     {
       GemmDesc g = gemm_desc(act(h, la.att), d, true, Wop(h, p + "proj.w"), d, true, xmid, d, M, d, d, resid_epi);
-      g.bias = P(h, p + "proj.b");
+      g.bias = bias_of(h, p + "proj.b");
       g.resid = x;
       g.ldr = d;
       g.drop = da;
       g.drop_site = site_attn_out(l);
       RUN("gemm_fwd", "proj_fwd", gemm(h, g, bf));
     }
-    RUN("layernorm", "ln2_fwd",
-        launch_layernorm_fwd(xmid, P(h, p + "ln2.g"), P(h, p + "ln2.b"), act(h, la.ln2), bf,
-                             act<float>(h, la.ln2_mean), act<float>(h, la.ln2_rstd), M, d, s));
+    if ((rc = norm_fwd(h, xmid, p + "ln2", act(h, la.ln2), act<float>(h, la.ln2_mean), act<float>(h, la.ln2_rstd),
+                       M)))
+      return rc;
     {
       GemmDesc g = gemm_desc(act(h, la.ln2), d, true, Wop(h, p + "fc.w"), d, true, act(h, la.h), 4 * d, M, 4 * d,
-                             d, EPI_BIAS_GELU);
-      g.bias = P(h, p + "fc.b");
+                             d, h->micro ? EPI_BIAS_RELU : EPI_BIAS_GELU);
+      g.bias = bias_of(h, p + "fc.b");
       g.aux = act(h, la.u);
       g.ldaux = 4 * d;
       RUN("gemm_fwd", "fc_fwd", gemm(h, g, bf));
@@ -496,7 +522,7 @@ int forward_to_logits(gpt_model* h, int B, int T, const DropArgs& da) {
     {
       GemmDesc g = gemm_desc(act(h, la.h), 4 * d, true, Wop(h, p + "fcproj.w"), 4 * d, true, xnext, d, M, d,
                              4 * d, resid_epi);
-      g.bias = P(h, p + "fcproj.b");
+      g.bias = bias_of(h, p + "fcproj.b");
       g.resid = xmid;
       g.ldr = d;
       g.drop = da;
@@ -504,11 +530,13 @@ int forward_to_logits(gpt_model* h, int B, int T, const DropArgs& da) {
       RUN("gemm_fwd", "fcproj_fwd", gemm(h, g, bf));
     }
   }
-  RUN("layernorm", "lnf_fwd",
-      launch_layernorm_fwd(act<float>(h, h->x_final), P(h, "lnf.g"), P(h, "lnf.b"), act(h, h->lnf), bf,
-                           act<float>(h, h->lnf_mean), act<float>(h, h->lnf_rstd), M, d, s));
   {
-    GemmDesc g = gemm_desc(act(h, h->lnf), d, true, Wop(h, "wte"), d, true, act(h, h->logits), h->ldz, M, h->Vp, d,
+    int rc = norm_fwd(h, act<float>(h, h->x_final), "lnf", act(h, h->lnf), act<float>(h, h->lnf_mean),
+                      act<float>(h, h->lnf_rstd), M);
+    if (rc) return rc;
+  }
+  {
+    GemmDesc g = gemm_desc(act(h, h->lnf), d, true, Wop(h, h->head), d, true, act(h, h->logits), h->ldz, M, h->Vp, d,
                            EPI_STORE);
     RUN("lm_head_fwd", "lm_head_fwd", gemm(h, g, bf));
   }
@@ -553,7 +581,7 @@ int gpt_create(const gpt_config* cfg, gpt_model** out) {
   if (c.n_embd % 4 != 0) return fail(nullptr, GPT_E_UNSUPPORTED, "n_embd must be a multiple of 4");
   if (c.precision != GPT_PREC_FP32 && c.precision != GPT_PREC_BF16) return fail(nullptr, GPT_E_INVAL, "unknown precision");
   if (!(c.dropout >= 0.0f && c.dropout < 1.0f)) return fail(nullptr, GPT_E_INVAL, "dropout must be in [0, 1)");
-  if (c.flags & ~(uint32_t)GPT_F_KV_CACHE) return fail(nullptr, GPT_E_INVAL, "unknown flags");
+  if (c.flags & ~(uint32_t)(GPT_F_KV_CACHE | GPT_F_MICROGPT)) return fail(nullptr, GPT_E_INVAL, "unknown flags");
   const int64_t M = (int64_t)c.batch * c.block_size;
   if (M > 32768) return fail(nullptr, GPT_E_UNSUPPORTED, "batch * block_size above 32768 is not implemented");
   {
@@ -574,6 +602,8 @@ int gpt_create(const gpt_config* cfg, gpt_model** out) {
   h->Tmax = c.block_size;
   h->Bmax = c.batch;
   h->A = c.grad_accum;
+  h->micro = (c.flags & GPT_F_MICROGPT) != 0;
+  h->head = h->micro ? "lm_head" : "wte";
   h->op_size = h->bf16 ? 2 : 4;
   // keep an element when its Philox word >= floor(p 2^32); scale kept ones by 1/(1-p)
   h->drop.on = c.dropout > 0.0f ? 1 : 0;
@@ -645,6 +675,7 @@ int gpt_init_state(gpt_model* h) {
   RUN("init", "zero m", launch_zero(h->buf.m, h->n_flat, s));
   RUN("init", "zero v", launch_zero(h->buf.v, h->n_flat, s));
   RUN("init", "zero optimizer state", launch_zero(ws(h, h->opt), sizeof(OptState) / 4, s));
+  RUN("init", "zero stand-in biases", launch_zero(ws(h, h->zbias), 4 * (size_t)h->d, s));
   if (h->bf16) {
     RUN("init", "bf16 shadow", launch_cast_bf16((const float*)h->buf.params, h->buf.shadow, h->n_flat, s));
     if ((rc = upload_tables(h))) return rc;
@@ -720,13 +751,12 @@ int gpt_decode(gpt_model* h, const int32_t* d_tokens, float* d_logits) {
   RUN("decode", "embed", launch_embed_pos(P(h, "wte"), P(h, "wpe"), act<int32_t>(h, h->tokens), x, B, d, h->Vp, pos, s));
   for (int l = 0; l < h->L; l++) {
     const std::string p = "h" + std::to_string(l) + ".";
-    RUN("layernorm", "ln1_fwd",
-        launch_layernorm_fwd(x, P(h, p + "ln1.g"), P(h, p + "ln1.b"), act(h, a.ln1), bf, act<float>(h, a.ln1_mean),
-                             act<float>(h, a.ln1_rstd), B, d, s));
+    if ((rc = norm_fwd(h, x, p + "ln1", act(h, a.ln1), act<float>(h, a.ln1_mean), act<float>(h, a.ln1_rstd), B)))
+      return rc;
     {
       GemmDesc g = gemm_desc(act(h, a.ln1), d, true, Wop(h, p + "attn.w"), d, true, act(h, a.qkv), 3 * d, B, 3 * d, d,
                              EPI_BIAS);
-      g.bias = P(h, p + "attn.b");
+      g.bias = bias_of(h, p + "attn.b");
       RUN("decode", "qkv", gemm(h, g, bf));
     }
     RUN("decode", "kv_append", launch_kv_append(act(h, a.qkv), bf, kv_slot(h, l), B, 1, h->Tmax, pos, d, s));
@@ -734,18 +764,17 @@ int gpt_decode(gpt_model* h, const int32_t* d_tokens, float* d_logits) {
         launch_attn_decode(act(h, a.qkv), kv_slot(h, l), act(h, a.att), bf, B, h->H, h->hd, h->Tmax, pos + 1, s));
     {
       GemmDesc g = gemm_desc(act(h, a.att), d, true, Wop(h, p + "proj.w"), d, true, xmid, d, B, d, d, EPI_BIAS_RESID);
-      g.bias = P(h, p + "proj.b");
+      g.bias = bias_of(h, p + "proj.b");
       g.resid = x;
       g.ldr = d;
       RUN("decode", "proj", gemm(h, g, bf));
     }
-    RUN("layernorm", "ln2_fwd",
-        launch_layernorm_fwd(xmid, P(h, p + "ln2.g"), P(h, p + "ln2.b"), act(h, a.ln2), bf,
-                             act<float>(h, a.ln2_mean), act<float>(h, a.ln2_rstd), B, d, s));
+    if ((rc = norm_fwd(h, xmid, p + "ln2", act(h, a.ln2), act<float>(h, a.ln2_mean), act<float>(h, a.ln2_rstd), B)))
+      return rc;
     {
       GemmDesc g = gemm_desc(act(h, a.ln2), d, true, Wop(h, p + "fc.w"), d, true, act(h, a.h), 4 * d, B, 4 * d, d,
-                             EPI_BIAS_GELU);
-      g.bias = P(h, p + "fc.b");
+                             h->micro ? EPI_BIAS_RELU : EPI_BIAS_GELU);
+      g.bias = bias_of(h, p + "fc.b");
       g.aux = act(h, a.u);
       g.ldaux = 4 * d;
       RUN("decode", "fc", gemm(h, g, bf));
@@ -753,17 +782,16 @@ int gpt_decode(gpt_model* h, const int32_t* d_tokens, float* d_logits) {
     {
       GemmDesc g = gemm_desc(act(h, a.h), 4 * d, true, Wop(h, p + "fcproj.w"), 4 * d, true, x, d, B, d, 4 * d,
                              EPI_BIAS_RESID);
-      g.bias = P(h, p + "fcproj.b");
+      g.bias = bias_of(h, p + "fcproj.b");
       g.resid = xmid;
       g.ldr = d;
       RUN("decode", "fcproj", gemm(h, g, bf));
     }
   }
-  RUN("layernorm", "lnf_fwd",
-      launch_layernorm_fwd(x, P(h, "lnf.g"), P(h, "lnf.b"), act(h, h->lnf), bf, act<float>(h, h->lnf_mean),
-                           act<float>(h, h->lnf_rstd), B, d, s));
+  if ((rc = norm_fwd(h, x, "lnf", act(h, h->lnf), act<float>(h, h->lnf_mean), act<float>(h, h->lnf_rstd), B)))
+    return rc;
   {
-    GemmDesc g = gemm_desc(act(h, h->lnf), d, true, Wop(h, "wte"), d, true, act(h, h->logits), h->ldz, B, h->Vp, d,
+    GemmDesc g = gemm_desc(act(h, h->lnf), d, true, Wop(h, h->head), d, true, act(h, h->logits), h->ldz, B, h->Vp, d,
                            EPI_STORE);
     RUN("decode", "lm_head", gemm(h, g, bf));
   }
@@ -831,10 +859,10 @@ int gpt_backward(gpt_model* h) {
 
   // lm_head (tied): dwte = dlogits^T lnf; dlnf = dlogits wte
   {
-    if (!bf && (rc = wgrad_now(act(h, h->logits), h->ldz, act(h, h->lnf), d, "wte", h->Vp, d, "lm_head_wgrad")))
+    if (!bf && (rc = wgrad_now(act(h, h->logits), h->ldz, act(h, h->lnf), d, h->head, h->Vp, d, "lm_head_wgrad")))
       return rc;
-    GemmDesc g2 = bf ? gemm_desc(act(h, h->logits), h->ldz, true, WopT(h, "wte"), h->Vp, true, dln, d, M, d, h->Vp, EPI_F32)
-                     : gemm_desc(act(h, h->logits), h->ldz, true, Wop(h, "wte"), d, false, dln, d, M, d, h->Vp, EPI_F32);
+    GemmDesc g2 = bf ? gemm_desc(act(h, h->logits), h->ldz, true, WopT(h, h->head), h->Vp, true, dln, d, M, d, h->Vp, EPI_F32)
+                     : gemm_desc(act(h, h->logits), h->ldz, true, Wop(h, h->head), d, false, dln, d, M, d, h->Vp, EPI_F32);
     RUN("gemm_dgrad", "lm_head_dgrad", gemm(h, g2, bf));
   }
   if ((rc = ln_bwd(h, dln, act<float>(h, h->x_final), act<float>(h, h->lnf_mean), act<float>(h, h->lnf_rstd),
@@ -851,12 +879,12 @@ int gpt_backward(gpt_model* h) {
     {
       // GEMM operand view of d x_{l+1} (times the MLP output mask with dropout)
       const void* dx = bf ? rx_slot(h, l + 1) : (dxm ? (const void*)dxm : (const void*)dres);
-      GemmDesc g = bf ? gemm_desc(dx, d, true, WopT(h, p + "fcproj.w"), d, true, du, 4 * d, M, 4 * d, d, EPI_GELU_BWD)
-                      : gemm_desc(dx, d, true, Wop(h, p + "fcproj.w"), 4 * d, false, du, 4 * d, M, 4 * d, d,
-                                  EPI_GELU_BWD);
+      const int act_bwd = h->micro ? EPI_RELU_BWD : EPI_GELU_BWD;
+      GemmDesc g = bf ? gemm_desc(dx, d, true, WopT(h, p + "fcproj.w"), d, true, du, 4 * d, M, 4 * d, d, act_bwd)
+                      : gemm_desc(dx, d, true, Wop(h, p + "fcproj.w"), 4 * d, false, du, 4 * d, M, 4 * d, d, act_bwd);
       g.aux = act(h, la.u);
       g.ldaux = 4 * d;
-      const int fc_rows = gemm_colsum_rows(g, bf);   // fc.b gradient fused into this GEMM when possible
+      const int fc_rows = h->micro ? 0 : gemm_colsum_rows(g, bf);   // fc.b gradient fused into this GEMM when possible
       if (fc_rows) g.colsum = red_part(h, p + "fc.b");
       rows.nblk[RED_FC] = fc_rows ? fc_rows : (M + COLSUM_ROWS - 1) / COLSUM_ROWS;
       RUN("gemm_dgrad", "fcproj_dgrad", gemm(h, g, bf));
@@ -865,7 +893,7 @@ int gpt_backward(gpt_model* h) {
                        : gemm_desc(du, 4 * d, true, Wop(h, p + "fc.w"), d, false, dln, d, M, d, 4 * d, EPI_F32);
       RUN("gemm_dgrad", "fc_dgrad", gemm(h, g2, bf));
       if (!bf && (rc = wgrad_now(du, 4 * d, act(h, la.ln2), d, p + "fc.w", 4 * d, d, "fc_wgrad"))) return rc;
-      if (!fc_rows && (rc = colsum(h, du, bf, 4 * d, M, 4 * d, p + "fc.b"))) return rc;
+      if (!h->micro && !fc_rows && (rc = colsum(h, du, bf, 4 * d, M, 4 * d, p + "fc.b"))) return rc;
       const std::string fcproj_b = p + "fcproj.b";
       if ((rc = ln_bwd(h, dln, act<float>(h, la.xmid), act<float>(h, la.ln2_mean), act<float>(h, la.ln2_rstd),
                        p + "ln2.g", p + "ln2.b", dres, fcproj_b.c_str(), bf ? rm_slot(h, l) : (void*)dxm, M,
@@ -880,7 +908,7 @@ int gpt_backward(gpt_model* h) {
                       : gemm_desc(dx, d, true, Wop(h, p + "proj.w"), d, false, dO, d, M, d, d, EPI_STORE);
       RUN("gemm_dgrad", "proj_dgrad", gemm(h, g, bf));
       if (!bf && (rc = wgrad_now(dx, d, act(h, la.att), d, p + "proj.w", d, d, "proj_wgrad"))) return rc;
-      const int qkv_rows = attn_bwd_colsum_rows(bf, B, T, h->hd);   // attn.b gradient fused into the kernels
+      const int qkv_rows = h->micro ? 0 : attn_bwd_colsum_rows(bf, B, T, h->hd);   // attn.b gradient fused into the kernels
       rows.nblk[RED_QKV] = qkv_rows ? qkv_rows : (M + COLSUM_ROWS - 1) / COLSUM_ROWS;
       RUN("attn_bwd", "attn_bwd",
           launch_attn_bwd(act(h, la.qkv), act(h, la.att), dO, act<float>(h, la.lse), ws<float>(h, h->attnD), dqkv, bf,
@@ -890,7 +918,7 @@ int gpt_backward(gpt_model* h) {
                        : gemm_desc(dqkv, 3 * d, true, Wop(h, p + "attn.w"), d, false, dln, d, M, d, 3 * d, EPI_F32);
       RUN("gemm_dgrad", "qkv_dgrad", gemm(h, g2, bf));
       if (!bf && (rc = wgrad_now(dqkv, 3 * d, act(h, la.ln1), d, p + "attn.w", 3 * d, d, "qkv_wgrad"))) return rc;
-      if (!qkv_rows && (rc = colsum(h, dqkv, bf, 3 * d, M, 3 * d, p + "attn.b"))) return rc;
+      if (!h->micro && !qkv_rows && (rc = colsum(h, dqkv, bf, 3 * d, M, 3 * d, p + "attn.b"))) return rc;
       const std::string proj_b = p + "proj.b";
       // d x_0 feeds only the embedding backward, which reads the fp32 copy
       void* xop = l == 0 ? nullptr : (bf ? rx_slot(h, l) : (void*)dxm);
@@ -915,10 +943,14 @@ int gpt_backward(gpt_model* h) {
       }
     }
   }
-  RUN("colsum", "bias_and_ln_grads",
-      launch_reduce_jobs(ws<RedJob>(h, h->rtable), (int)h->rjobs.size(), h->rblocks, ws<float>(h, h->red),
-                         (float*)h->buf.grads, rows, beta, s));
-  // ---- embeddings: dres holds d x0 (after the lm_head weight gradient: both write wte's gradient)
+  if (!h->rjobs.empty())
+    RUN("colsum", "bias_and_ln_grads",
+        launch_reduce_jobs(ws<RedJob>(h, h->rtable), (int)h->rjobs.size(), h->rblocks, ws<float>(h, h->red),
+                           (float*)h->buf.grads, rows, beta, s));
+  // ---- embeddings: dres holds d x0 (after the lm_head weight gradient: both write wte's gradient;
+  // with an lm_head of its own, the embedding scatter is wte's only gradient and starts from zero)
+  if (h->grads_fresh && h->micro)
+    RUN("embed", "zero wte grad", launch_zero(G(h, "wte"), (size_t)h->Vp * d, s));
   if (h->grads_fresh && T < h->Tmax) {
     float* wpe_tail = G(h, "wpe") + (size_t)T * d;
     RUN("embed", "zero wpe tail", launch_zero(wpe_tail, (size_t)(h->Tmax - T) * d, s));
