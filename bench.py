@@ -42,9 +42,15 @@ PEAK_HBM = 8.0e12         # bytes/s
 
 
 def flops_per_token(cfg) -> float:
+    """6N + 12 L d T with N the parameters that multiply activations: all but the
+    position table (GPT-2: the tied wte counts once, as the lm_head); for the
+    microGPT block, its matrices and its own lm_head (the wte gather is no product)."""
     d, L, T, V = cfg.n_embd, cfg.n_layer, cfg.block_size, cfg.padded_vocab
-    n_params = V * d + T * d + L * (12 * d * d + 13 * d) + 2 * d
-    N = n_params - T * d
+    if getattr(cfg, "variant", "gpt2") == "microgpt":
+        N = V * d + L * 12 * d * d
+    else:
+        n_params = V * d + T * d + L * (12 * d * d + 13 * d) + 2 * d
+        N = n_params - T * d
     return 6.0 * N + 12.0 * L * d * T
 
 

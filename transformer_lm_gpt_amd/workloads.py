@@ -101,7 +101,9 @@ ORDER = ["tiny", "char_small", "char_6l", "bpe_12l_512", "gpt2_124m"]
 # page's own size (4,192 parameters) and at the char_small shape.
 CONFIGS["micro"] = CONFIGS["tiny"].with_(name="micro", variant="microgpt")
 CONFIGS["char_small_micro"] = CONFIGS["char_small"].with_(name="char_small_micro", variant="microgpt")
-VARIANT_CONFIGS = ["micro", "char_small_micro"]
+# the block at the GPT-2 124M shape, for throughput
+CONFIGS["gpt2_124m_micro"] = CONFIGS["gpt2_124m"].with_(name="gpt2_124m_micro", variant="microgpt")
+VARIANT_CONFIGS = ["micro", "char_small_micro", "gpt2_124m_micro"]
 
 
 def rngs(seed: int = SEED) -> Tuple[np.random.Generator, np.random.Generator]:
