@@ -84,10 +84,11 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p, const
   const float inv_bc2 = 1.f / st->bc2;
   const float decay = 1.f - lr * wd;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
-    f32x4 pv = ((f32x4*)p)[i];
-    const f32x4 gv = ((const f32x4*)g)[i];
-    f32x4 mv = ((f32x4*)m)[i];
-    f32x4 vv = ((f32x4*)v)[i];
+    // every byte is touched once: streaming loads and stores keep the caches out of it
+    f32x4 pv = __builtin_nontemporal_load((f32x4*)p + i);
+    const f32x4 gv = __builtin_nontemporal_load((const f32x4*)g + i);
+    f32x4 mv = __builtin_nontemporal_load((f32x4*)m + i);
+    f32x4 vv = __builtin_nontemporal_load((f32x4*)v + i);
     const bool dec = i * 4 < n_decay;   // n_decay is a multiple of 64
 #pragma unroll
     for (int e = 0; e < 4; e++) {
@@ -99,14 +100,14 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p, const
       float pe = dec ? pv[e] * decay : pv[e];
       pv[e] = pe - lr * mhat / (sqrtf(vhat) + eps);
     }
-    ((f32x4*)p)[i] = pv;
-    ((f32x4*)m)[i] = mv;
-    ((f32x4*)v)[i] = vv;
+    __builtin_nontemporal_store(pv, (f32x4*)p + i);
+    __builtin_nontemporal_store(mv, (f32x4*)m + i);
+    __builtin_nontemporal_store(vv, (f32x4*)v + i);
     if (shadow) {
       bf16x4 sv;
 #pragma unroll
       for (int e = 0; e < 4; e++) sv[e] = (bf16)pv[e];
-      ((bf16x4*)shadow)[i] = sv;
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x2, sv), (u32x2*)shadow + i);
     }
   }
 }
@@ -115,7 +116,7 @@ hipError_t launch_adamw(float* p, const float* g, float* m, float* v, void* shad
                         const OptState* st, float lr, float beta1, float beta2, float eps, float wd,
                         hipStream_t s) {
   const size_t n4 = n / 4;
-  unsigned blocks = (unsigned)std::min<size_t>((n4 + 255) / 256, 8192);
+  unsigned blocks = (unsigned)std::min<size_t>((n4 + 255) / 256, 65536);
   hipLaunchKernelGGL(adamw_kernel, dim3(blocks), dim3(256), 0, s, p, g, m, v, (bf16*)shadow_bf16, n4, n_decay, st,
                      lr, beta1, beta2, eps, wd);
   return hipGetLastError();

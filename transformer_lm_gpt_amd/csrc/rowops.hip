@@ -558,7 +558,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
   for (int j = 0; j < NV; j++) {
     const int i = tid + 1024 * j;
     if (i < nv) {
-      v[j] = *(const bf16x8*)(zr + 8 * i);
+      // the row is read once and overwritten once: streaming accesses
+      v[j] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)(zr + 8 * i)));
 #pragma unroll
       for (int e = 0; e < 8; e++) m = fmaxf(m, (float)v[j][e]);
     }
@@ -605,7 +606,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
         if (8 * i + e == tgt) g -= grad_scale;
         o[e] = (bf16)g;
       }
-      *(bf16x8*)(zr + 8 * i) = o;
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, o), (u32x4*)(zr + 8 * i));
     }
   }
 }
