@@ -45,6 +45,13 @@ What it computes, and the passage each part follows (the nanoGPT pages):
     its own. Its norms sit where the GPT-2 block has them (before attention,
     before the MLP and before the head), with eps 1e-5.
 
+  * LoRA (configuration fields lora_rank r > 0 and lora_alpha; the fine-tuning
+    article on blog.hotdry.top, LoRA section): the q and v projections of every
+    block gain a low-rank branch, q = a W0_q^T + b_q + s (a A_q^T) B_q^T with
+    A [r, n_embd], B [n_embd, r] and s = lora_alpha / r; only the A and B
+    tensors are trained, every other tensor stays frozen; the merged weight
+    W0 + s B A gives the same forward.
+
 Readings where the pages are silent: LayerNorm eps 1e-5 with the biased
 variance; attention scale 1/sqrt(head_dim); the softmax runs over all padded
 vocabulary columns; the clip coefficient is min(1, clip / (norm + 1e-6)) and
@@ -101,7 +108,27 @@ def param_shapes(cfg, variant: str | None = None) -> List[Tuple[str, Tuple[int, 
         out += [("lnf.g", (d,)), ("lnf.b", (d,))]
     else:
         out += [("lm_head", (V, d))]
+    r, _ = lora_of(cfg)
+    for l in range(L):
+        for t in ("q", "v"):
+            out += [(f"h{l}.lora_{t}.A", (r, d)), (f"h{l}.lora_{t}.B", (d, r))] if r else []
     return out
+
+
+def lora_of(cfg) -> Tuple[int, float]:
+    """(rank r, branch scale lora_alpha / r), or (0, 0.0) without adapters.
+
+    The fine-tuning article (LoRA section) names lora_alpha as the scaling factor;
+    the scale applied to B A is alpha / r, as in the LoRA paper (Hu et al., 2021).
+    """
+    r = int(getattr(cfg, "lora_rank", 0) or 0)
+    return (r, float(cfg.lora_alpha) / r) if r > 0 else (0, 0.0)
+
+
+def trainable(cfg, name: str) -> bool:
+    """With adapters only their A and B tensors train (the article freezes W0 and
+    updates the low-rank matrices alone); otherwise every tensor does."""
+    return ".lora_" in name if lora_of(cfg)[0] else True
 
 
 def n_params(cfg, variant: str | None = None) -> int:
@@ -316,6 +343,7 @@ def forward_sequence(P, tok, cfg, drop=None, b=0):
     hd = d // H
     dt = P["wte"].dtype.type
     micro = variant_of(cfg) == "microgpt"
+    r_lora, s_lora = lora_of(cfg)
     # microGPT: weightless RMSNorm, ReLU, no biases, its own lm_head
     norm = (lambda x, name: rmsnorm_fwd(x)) if micro else (lambda x, name: layernorm_fwd(x, P[name + ".g"], P[name + ".b"]))
     act = relu if micro else gelu
@@ -335,6 +363,14 @@ def forward_sequence(P, tok, cfg, drop=None, b=0):
         p = f"h{l}."
         a, c1 = norm(x, p + "ln1")
         qkv = a @ P[p + "attn.w"].T + bias(p + "attn.b")
+        lo = None
+        if r_lora:
+            # low-rank branches on the q and v columns: s (a A^T) B^T
+            uq = a @ P[p + "lora_q.A"].T
+            uv = a @ P[p + "lora_v.A"].T
+            qkv[:, :d] += s_lora * (uq @ P[p + "lora_q.B"].T)
+            qkv[:, 2 * d:] += s_lora * (uv @ P[p + "lora_v.B"].T)
+            lo = (uq, uv)
         q, k, v = (qkv[:, i * d:(i + 1) * d].reshape(T, H, hd).transpose(1, 0, 2) for i in range(3))
         zp = za = zo = None
         if drop is not None:
@@ -350,7 +386,7 @@ def forward_sequence(P, tok, cfg, drop=None, b=0):
         h = act(u)
         y2 = h @ P[p + "fcproj.w"].T + bias(p + "fcproj.b")
         x2 = x1 + (y2 if zo is None else y2 * zo)
-        layers.append((a, c1, q, k, v, pr, o2, b2, c2, u, h, zp, za, zo))
+        layers.append((a, c1, q, k, v, pr, o2, b2, c2, u, h, zp, za, zo, lo))
         x = x2
     xf, cf = norm(x, "lnf")
     z = xf @ P["lm_head" if micro else "wte"].T
@@ -365,6 +401,7 @@ def backward_sequence(P, cache, dz, cfg, G):
     hd = d // H
     micro = variant_of(cfg) == "microgpt"
     head = "lm_head" if micro else "wte"
+    s_lora = lora_of(cfg)[1]
 
     def norm_bwd(dy, c, name):
         if micro:
@@ -384,7 +421,7 @@ def backward_sequence(P, cache, dz, cfg, G):
     dx = norm_bwd(dxf, cf, "lnf")
     for l in reversed(range(L)):
         p = f"h{l}."
-        a, c1, q, k, v, pr, o2, b2, c2, u, h, zp, za, zo = layers[l]
+        a, c1, q, k, v, pr, o2, b2, c2, u, h, zp, za, zo, lo = layers[l]
         # MLP: x2 = x1 + drop(gelu(LN2(x1) Wfc^T + bfc) Wp^T + bp)
         dy2 = dx if zo is None else dx * zo
         G[p + "fcproj.w"] += dy2.T @ h
@@ -405,6 +442,13 @@ def backward_sequence(P, cache, dz, cfg, G):
         G[p + "attn.w"] += dqkv.T @ a
         add_bias(p + "attn.b", dqkv)
         da = dqkv @ P[p + "attn.w"]
+        if lo is not None:
+            # q (or v) = ... + s u B^T with u = a A^T
+            for t, uu, dt_ in (("q", lo[0], dqkv[:, :d]), ("v", lo[1], dqkv[:, 2 * d:])):
+                G[p + f"lora_{t}.B"] += s_lora * (dt_.T @ uu)
+                du_ = s_lora * (dt_ @ P[p + f"lora_{t}.B"])
+                G[p + f"lora_{t}.A"] += du_.T @ a
+                da = da + du_ @ P[p + f"lora_{t}.A"]
         dx = dx1 + norm_bwd(da, c1, p + "ln1")
     # x0 = drop(wte[tok] + wpe[:T]); repeated ids add up.
     if ze is not None:
@@ -481,15 +525,16 @@ def clip_coef(norm: float, clip: float) -> float:
     return min(1.0, clip / (norm + CLIP_EPS))
 
 
-def adamw_update(params, grads, m, v, t, lr, beta1, beta2, eps, wd, coef, decay_mask):
-    """One AdamW update in place. t is the step number after increment (>= 1).
+def adamw_update(params, grads, m, v, t, lr, beta1, beta2, eps, wd, coef, decay_mask, keys=None):
+    """One AdamW update in place of the tensors ``keys`` (default: all of
+    ``params``). t is the step number after increment (>= 1).
 
     Decoupled decay first: p <- p (1 - lr wd) for decayed tensors, then
     p <- p - lr * mhat / (sqrt(vhat) + eps) with bias-corrected moments.
     """
     bc1 = 1.0 - beta1 ** t
     bc2 = 1.0 - beta2 ** t
-    for k in params:
+    for k in (params if keys is None else keys):
         g = grads[k] * coef
         m[k] = beta1 * m[k] + (1.0 - beta1) * g
         v[k] = beta2 * v[k] + (1.0 - beta2) * g * g
@@ -512,6 +557,7 @@ class Trainer:
         self.v = {k: np.zeros_like(v) for k, v in self.p.items()}
         self.t = 0
         self.decay = {k: decays(k, v.shape) for k, v in self.p.items()}
+        self.train = [k for k in self.p if trainable(cfg, k)]
 
     def step(self, batches, lr=None, beta1=None, beta2=None, eps=None, wd=None, clip=None):
         c = self.cfg
@@ -522,11 +568,12 @@ class Trainer:
         wd = c.weight_decay if wd is None else wd
         clip = c.grad_clip if clip is None else clip
         losses, grads = accumulate_grads(self.p, batches, c, self.dtype, self.dropout)
+        grads = {k: grads[k] for k in self.train}     # frozen tensors take no part
         norm = grad_norm(grads)
         coef = clip_coef(norm, clip)
         self.t += 1
         adamw_update(self.p, grads, self.m, self.v, self.t, lr, beta1, beta2, eps, wd,
-                     coef, self.decay)
+                     coef, self.decay, keys=self.train)
         return {"losses": losses, "loss": float(np.mean(losses)), "grads": grads,
                 "norm": norm, "coef": coef}
 

@@ -536,3 +536,85 @@ def test_finite_difference_micro_with_dropout():
     params = W.init_params(c, wrng)
     tok, tgt = W.make_batch(c, drng)
     assert _fd_check(c, params, tok, tgt, dropout=O.Dropout(0.25, 77)) > 100
+
+
+# --------------------------------------------------------------------------- LoRA adapters
+# The fine-tuning article (blog.hotdry.top), LoRA section: W0 frozen, low-rank A and B
+# on the q and v projections, h = W0 x + B A x scaled by lora_alpha / r, only A and B
+# trained, and B A can be merged into W0.
+
+@pytest.mark.parametrize("name", W.LORA_CONFIGS)
+def test_lora_layout_and_count(name):
+    c = W.CONFIGS[name]
+    assert W.tensor_table(c) == O.param_shapes(c)
+    base = O.n_params(c.with_(lora_rank=0))
+    L, d, r = c.n_layer, c.n_embd, c.lora_rank
+    assert O.n_params(c) - base == 4 * L * d * r          # A [r, d] and B [d, r], for q and v
+    trained = [n for n, _ in O.param_shapes(c) if O.trainable(c, n)]
+    assert len(trained) == 4 * L and all(".lora_" in n for n in trained)
+    assert O.lora_of(c) == (r, c.lora_alpha / r)
+
+
+def test_lora_zero_B_is_the_base_model_bitwise():
+    c, params, tok, tgt = _setup("tiny_lora")               # B = 0, A random
+    assert all(not np.any(params[f"h{l}.lora_{t}.B"]) for l in range(c.n_layer) for t in "qv")
+    base = {k: v for k, v in params.items() if ".lora_" not in k}
+    z = O.logits(params, tok, c)
+    zb = O.logits(base, tok, c.with_(lora_rank=0))
+    assert np.array_equal(z, zb)
+    # with B = 0 the A gradient vanishes exactly (its only path runs through B)
+    _, G = O.microbatch(params, tok, tgt, c, grad_scale=1.0 / tok.size)
+    for l in range(c.n_layer):
+        for t in "qv":
+            assert not np.any(G[f"h{l}.lora_{t}.A"])
+            assert np.any(G[f"h{l}.lora_{t}.B"])
+
+
+@pytest.mark.parametrize("name,B", [("tiny_lora", None), ("char_small_lora", 2)])
+def test_lora_equals_merged_weight(name, B):
+    # the article's merge: W0 + s B A in the q and v row blocks gives the same model
+    c, params, tok, tgt = _setup(name, perturb=True, B=B)
+    r, s = O.lora_of(c)
+    d = c.n_embd
+    merged = {k: v.astype(np.float64).copy() for k, v in params.items() if ".lora_" not in k}
+    for l in range(c.n_layer):
+        w = merged[f"h{l}.attn.w"]
+        for t, rows in (("q", slice(0, d)), ("v", slice(2 * d, 3 * d))):
+            Bm = params[f"h{l}.lora_{t}.B"].astype(np.float64)
+            Am = params[f"h{l}.lora_{t}.A"].astype(np.float64)
+            w[rows] += s * (Bm @ Am)
+    z = O.logits(params, tok, c)
+    zm = O.logits(merged, tok, c.with_(lora_rank=0))
+    assert np.max(np.abs(z - zm)) <= 1e-12 * np.max(np.abs(zm))
+    assert np.max(np.abs(z - O.logits({k: v for k, v in params.items() if ".lora_" not in k}, tok,
+                                      c.with_(lora_rank=0)))) > 1e-3   # the adapters do change the model
+
+
+def test_finite_difference_tiny_lora():
+    c, params, tok, tgt = _setup("tiny_lora", perturb=True)
+    assert _fd_check(c, params, tok, tgt) > 250
+
+
+def test_lora_first_step_closed_form_and_frozen_base():
+    # B0 = 0: dA = 0, so A only decays, A1 = A0 (1 - lr wd); B1 = -lr c g / (c |g| + eps)
+    # elementwise (the Adam step-1 closed form with clip coefficient c); nothing else moves.
+    c = W.CONFIGS["tiny_lora"].with_(weight_decay=0.1, grad_clip=0.05)
+    drng, wrng = W.rngs()
+    params = W.init_params(c, wrng)
+    batches = W.make_step_batches(c, drng)
+    tr = O.Trainer(params, c)
+    out = tr.step(batches)
+    assert set(out["grads"]) == {n for n in params if ".lora_" in n}
+    norm = math.sqrt(sum(float(np.sum(g.astype(np.float64) ** 2)) for g in out["grads"].values()))
+    assert out["norm"] == pytest.approx(norm, rel=1e-12)
+    coef = O.clip_coef(norm, c.grad_clip)
+    assert coef < 1.0
+    for k, p0 in params.items():
+        p1 = tr.p[k]
+        if ".lora_" not in k:
+            assert np.array_equal(p1, p0.astype(np.float64)), k
+        elif k.endswith(".A"):
+            np.testing.assert_allclose(p1, p0.astype(np.float64) * (1.0 - c.lr * c.weight_decay), rtol=1e-15, atol=0)
+        else:
+            g = out["grads"][k]
+            np.testing.assert_allclose(p1, -c.lr * coef * g / (coef * np.abs(g) + c.eps), rtol=1e-12, atol=1e-15)

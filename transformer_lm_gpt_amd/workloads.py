@@ -61,6 +61,8 @@ class GPTConfig:
     parity_steps: int = 1
     precisions: Tuple[str, ...] = ("bf16",)
     variant: str = "gpt2"    # "gpt2" | "microgpt" (weightless RMSNorm, ReLU, no biases, untied head)
+    lora_rank: int = 0       # r > 0: low-rank adapters on the q and v projections, only they train
+    lora_alpha: float = 16.0 # the adapters' branch is scaled by lora_alpha / r
 
     @property
     def head_dim(self) -> int:
@@ -104,6 +106,13 @@ CONFIGS["char_small_micro"] = CONFIGS["char_small"].with_(name="char_small_micro
 # the block at the GPT-2 124M shape, for throughput
 CONFIGS["gpt2_124m_micro"] = CONFIGS["gpt2_124m"].with_(name="gpt2_124m_micro", variant="microgpt")
 VARIANT_CONFIGS = ["micro", "char_small_micro", "gpt2_124m_micro"]
+# LoRA fine-tuning (the fine-tuning article on blog.hotdry.top, LoRA section:
+# adapters on the q and v projections, lora_alpha 16, r from 16 down) on the
+# toy, the char_small shape and GPT-2 124M.
+CONFIGS["tiny_lora"] = CONFIGS["tiny"].with_(name="tiny_lora", lora_rank=4, lora_alpha=16.0)
+CONFIGS["char_small_lora"] = CONFIGS["char_small"].with_(name="char_small_lora", lora_rank=8, lora_alpha=16.0)
+CONFIGS["gpt2_124m_lora"] = CONFIGS["gpt2_124m"].with_(name="gpt2_124m_lora", lora_rank=16, lora_alpha=16.0)
+LORA_CONFIGS = ["tiny_lora", "char_small_lora", "gpt2_124m_lora"]
 
 
 def rngs(seed: int = SEED) -> Tuple[np.random.Generator, np.random.Generator]:
@@ -123,7 +132,7 @@ def tensor_table(cfg: GPTConfig) -> List[Tuple[str, Tuple[int, ...]]]:
             p = f"h{l}."
             out += [(p + "attn.w", (3 * d, d)), (p + "proj.w", (d, d)),
                     (p + "fc.w", (4 * d, d)), (p + "fcproj.w", (d, 4 * d))]
-        return out + [("lm_head", (V, d))]
+        return out + [("lm_head", (V, d))] + _lora_table(cfg)
     for l in range(L):
         p = f"h{l}."
         out += [(p + "ln1.g", (d,)), (p + "ln1.b", (d,)),
@@ -133,6 +142,16 @@ def tensor_table(cfg: GPTConfig) -> List[Tuple[str, Tuple[int, ...]]]:
                 (p + "fc.w", (4 * d, d)), (p + "fc.b", (4 * d,)),
                 (p + "fcproj.w", (d, 4 * d)), (p + "fcproj.b", (d,))]
     out += [("lnf.g", (d,)), ("lnf.b", (d,))]
+    return out + _lora_table(cfg)
+
+
+def _lora_table(cfg: GPTConfig) -> List[Tuple[str, Tuple[int, ...]]]:
+    """The adapters, after every base tensor: per block A [r, d] and B [d, r] for q, then v."""
+    r, d = cfg.lora_rank, cfg.n_embd
+    out: List[Tuple[str, Tuple[int, ...]]] = []
+    for l in range(cfg.n_layer if r > 0 else 0):
+        for t in ("q", "v"):
+            out += [(f"h{l}.lora_{t}.A", (r, d)), (f"h{l}.lora_{t}.B", (d, r))]
     return out
 
 
@@ -143,13 +162,17 @@ def init_params(cfg: GPTConfig, rng: np.random.Generator | None = None,
 
     With ``perturb`` the biases, gains and shifts get small random values too, so
     that parity checks exercise every term (an all-zero bias hides a dropped add).
+    Adapters: A is N(0, std) and B is 0 (so training starts from the base model),
+    B N(0, std) too with ``perturb``.
     """
     if rng is None:
         rng = rngs()[1]
     params: Dict[str, np.ndarray] = {}
     for name, shape in tensor_table(cfg):
         leaf = name.split(".")[-1]
-        if len(shape) == 2:
+        if ".lora_" in name and leaf == "B" and not perturb:
+            a = np.zeros(shape)
+        elif len(shape) == 2:
             std = cfg.init_std
             if cfg.resid_scaled and (name.endswith("proj.w")):
                 std = std / np.sqrt(2.0 * cfg.n_layer)
