@@ -51,6 +51,11 @@ def flops_per_token(cfg) -> float:
     else:
         n_params = V * d + T * d + L * (12 * d * d + 13 * d) + 2 * d
         N = n_params - T * d
+    if getattr(cfg, "lora_rank", 0) > 0:
+        # LoRA fine-tuning: forward 2N + 4 L d T, input gradients 2N + 8 L d T, and of
+        # the weight gradients only the q and v blocks, 4 L d^2 (the adapters' own
+        # products run once per step, not per token)
+        return 4.0 * N + 12.0 * L * d * T + 4.0 * L * d * d
     return 6.0 * N + 12.0 * L * d * T
 
 
@@ -296,7 +301,8 @@ def main(argv=None):
             # every weight gradient of a micro-batch, K = B*T tokens each: one grouped
             # launch per micro-batch where every tensor's shape allows it, else one per tensor
             mbs = a.steps * A
-            work = 2.0 * B * T * (Vp * d + L * 12 * d * d)               # FLOPs per micro-batch
+            lora = cfg.lora_rank > 0                                     # q and v blocks only
+            work = 2.0 * B * T * (2 * L * d * d if lora else Vp * d + L * 12 * d * d)   # FLOPs per micro-batch
             per_mb = kern_ms / mbs
             grouped = kern_n == mbs
             roof = {"kernel": ("grouped weight-gradient GEMM (gemm_group_kernel 256x256, 16 wavefronts, + group_fixup_kernel, "
@@ -308,7 +314,8 @@ def main(argv=None):
                     "traffic": traffic_of("gemm_group_kernel", cfg.name) if grouped else None,
                     "avg_launch_ms": round(avg_ms, 4), "launches": kern_n,
                     ("work_per_launch" if grouped else "work_per_micro_batch"):
-                        f"2*M*(Vp*d + 12*L*d^2) = {work:.4g} FLOP, M = {B * T}"}
+                        (f"2*M*(2*L*d^2) = {work:.4g} FLOP" if lora else f"2*M*(Vp*d + 12*L*d^2) = {work:.4g} FLOP")
+                        + f", M = {B * T}"}
         else:
             roof = {"kernel": a.kernel, "avg_launch_ms": round(avg_ms, 4), "launches": kern_n}
 
@@ -340,7 +347,9 @@ def main(argv=None):
         "config": {"workload": f"{cfg.name}: L{cfg.n_layer} H{cfg.n_head} d{cfg.n_embd} V{cfg.vocab_size}"
                                f"(pad {cfg.padded_vocab}) B{B} T{T} accum{A}",
                    "global_batch": B * A, "seq_len": T, "tokens_per_step": tokens_per_step,
-                   "dropout": a.dropout},
+                   "dropout": a.dropout,
+                   **({"lora_rank": cfg.lora_rank, "lora_alpha": cfg.lora_alpha, "lora_on": "q, v"}
+                      if cfg.lora_rank else {})},
         "mfu": round(mfu, 4),
         "mfu_causal_exact": round(tps * causal_ftok / peak, 4),
         "achieved_tflops": round(tps * ftok / 1e12, 1),

@@ -21,6 +21,9 @@
  *   - Dropout: the nanoGPT run log, sections 2.1 and 2.2 (rate 0.1, or 0.0 on
  *     large data) and the microGPT page's parameter list (0.2 for the
  *     Shakespeare character model).
+ *   - LoRA: the fine-tuning article (blog.hotdry.top), LoRA section: W0
+ *     frozen, low-rank A and B on the q and v projections, the branch B A x
+ *     scaled by lora_alpha / r, only A and B trained, B A mergeable into W0.
  *
  * Conventions
  *   - All device pointers are plain HIP device addresses. The library never
@@ -36,8 +39,9 @@
  *   - Layout: parameters, gradients and both Adam moments are flat fp32 arrays
  *     with identical offsets (gpt_tensor_info_at). Every linear weight is
  *     stored [out, in] row-major and acts as y = x W^T + b. All 2-D tensors
- *     (the decayed ones) come first, then all 1-D tensors; every tensor starts
- *     at a multiple of 64 elements and the gaps are zero.
+ *     (the decayed ones) come first, then all 1-D tensors, then the LoRA
+ *     adapters when lora_rank > 0; every tensor starts at a multiple of 64
+ *     elements and the gaps are zero.
  */
 #ifndef GPT_MI355X_H
 #define GPT_MI355X_H
@@ -85,10 +89,24 @@ typedef struct gpt_config {
   int32_t precision;     /* GPT_PREC_FP32 or GPT_PREC_BF16                          */
   float   dropout;       /* p in [0, 1): see gpt_set_dropout_seed                   */
   uint32_t flags;        /* GPT_F_KV_CACHE | GPT_F_MICROGPT, or 0                   */
+  int32_t lora_rank;     /* r in [0, 64]; r > 0 adds low-rank adapters (fine-tuning
+                            article, LoRA section) to the q and v projections of
+                            every block: tensors h<l>.lora_q.A [r, n_embd],
+                            h<l>.lora_q.B [n_embd, r] and the same for v, after all
+                            base tensors; q = a W0_q^T + b_q + (alpha / r) (a A^T) B^T.
+                            Then only the adapters train: gpt_backward forms their
+                            gradients alone (the gradients of every other tensor are
+                            left undefined: that part of the array is scratch), and
+                            gpt_adamw_step's norm, clip and update cover them alone.
+                            The base weights stay as loaded; the GEMMs read the
+                            merged W0 + (alpha / r) B A, rebuilt by gpt_init_state
+                            and after every update. 0: no adapters.               */
+  float   lora_alpha;    /* the branch scale is lora_alpha / lora_rank (finite,
+                            nonzero when lora_rank > 0; ignored otherwise)         */
 } gpt_config;
 
 typedef struct gpt_sizes {
-  size_t n_params;         /* trainable scalars (no alignment gaps)                 */
+  size_t n_params;         /* scalars of every tensor, adapters included (no gaps)  */
   size_t n_flat;           /* elements of the flat param/grad/m/v arrays            */
   size_t param_bytes;      /* fp32 master weights                                    */
   size_t grad_bytes;       /* fp32 gradients                                         */
@@ -135,7 +153,8 @@ int gpt_tensor_info_at(const gpt_model* h, int i, gpt_tensor_info* out);
  * until gpt_destroy or the next gpt_bind. */
 int gpt_bind(gpt_model* h, const gpt_buffers* bufs, void* hip_stream);
 
-/* Call after writing weights into `params`: refreshes the bf16 shadow, zeroes
+/* Call after writing weights into `params`: refreshes the bf16 shadow (and,
+ * with LoRA adapters, the merged qkv weights W0 + (alpha / r) B A), zeroes
  * gradients, both moments and the step counter. */
 int gpt_init_state(gpt_model* h);
 
@@ -211,7 +230,9 @@ int gpt_zero_grad(gpt_model* h);
  * clip > 0 else 1; t += 1; for every element: g' = coef g,
  * m = beta1 m + (1 - beta1) g', v = beta2 v + (1 - beta2) g'^2,
  * p = p (1 - lr wd) [decayed tensors only] - lr (m / (1 - beta1^t)) /
- * (sqrt(v / (1 - beta2^t)) + eps); then refreshes both bf16 shadows.
+ * (sqrt(v / (1 - beta2^t)) + eps); then refreshes both bf16 shadows. With
+ * LoRA adapters (config.lora_rank > 0) "all" is the adapters alone, and the
+ * merged qkv weights are rebuilt from the updated A and B.
  * d_grad_norm (nullable) receives n (before clipping). If n is not finite the
  * update is skipped on the device, t is not advanced, and the next gpt_sync
  * returns GPT_E_NONFINITE. */

@@ -37,7 +37,7 @@ def test_library_is_gfx950_only():
         assert other not in blob
 
 
-@pytest.mark.parametrize("name", W.ORDER + W.VARIANT_CONFIGS)
+@pytest.mark.parametrize("name", W.ORDER + W.VARIANT_CONFIGS + W.LORA_CONFIGS)
 @pytest.mark.parametrize("prec", ["fp32", "bf16"])
 def test_layout_matches_oracle(name, prec):
     cfg = W.CONFIGS[name]
@@ -47,13 +47,17 @@ def test_layout_matches_oracle(name, prec):
         table = {n: (shape, dec) for n, _, shape, dec in lay.tensors}
         oracle = {n: (s, O.decays(n, s)) for n, s in O.param_shapes(cfg)}
         assert table == oracle
-        # offsets: 64-aligned, disjoint, decayed tensors first
-        spans = sorted((off, off + int(np.prod(shape)), dec) for _, off, shape, dec in lay.tensors)
-        for (a0, a1, _), (b0, _, _) in zip(spans, spans[1:]):
+        # offsets: 64-aligned, disjoint, decayed tensors first, then the 1-D tensors,
+        # then the adapters (all after every base tensor)
+        spans = sorted((off, off + int(np.prod(shape)), dec, ".lora_" in n) for n, off, shape, dec in lay.tensors)
+        for (a0, a1, _, _), (b0, _, _, _) in zip(spans, spans[1:]):
             assert a1 <= b0
         assert all(off % 64 == 0 for _, off, _, _ in lay.tensors)
-        decs = [dec for _, _, dec in spans]
+        kinds = [ad for _, _, _, ad in spans]
+        assert kinds == sorted(kinds)
+        decs = [dec for _, _, dec, ad in spans if not ad]
         assert decs == sorted(decs, reverse=True)
+        assert all(dec for _, _, dec, ad in spans if ad)
         assert spans[-1][1] <= lay.sizes.n_flat and lay.sizes.n_flat % 256 == 0
         assert lay.sizes.shadow_bytes == (lay.sizes.n_flat * 4 if prec == "bf16" else 0)   # weights + transposed weights
         # round trip through the flat layout
@@ -84,6 +88,10 @@ def _raw(**kw):
     (dict(dropout=float("nan")), -1),
     (dict(n_embd=512, n_head=4), -4),      # head_dim 128
     (dict(batch=4096, block_size=16), -4),  # M above the single-workgroup sort
+    (dict(lora_rank=-1), -1),
+    (dict(lora_rank=65), -1),              # above the adapter kernels' rank
+    (dict(lora_rank=4, lora_alpha=0.0), -1),
+    (dict(lora_rank=4, lora_alpha=float("inf")), -1),
 ])
 def test_create_rejects(kw, code):
     lib = Bd.load_library()

@@ -27,3 +27,11 @@ def test_traffic_only_for_its_workload_and_source():
     assert got in (None, rec["bytes_per_launch"])       # None once the source changed
     assert bench.traffic_of("gemm_group_kernel", "char_6l") is None
     assert bench.traffic_of("no_such_kernel", rec["workload"]) is None
+
+
+def test_flops_per_token_gpt2_124m_lora():
+    # LoRA on q and v: 4N + 12 L d T + 4 L d^2 (no weight gradients but the q and v blocks)
+    cfg = W.CONFIGS["gpt2_124m_lora"]
+    d, L, T = cfg.n_embd, cfg.n_layer, cfg.block_size
+    assert bench.flops_per_token(cfg) == 4.0 * 123_689_472 + 12.0 * L * d * T + 4.0 * L * d * d
+    assert abs(bench.flops_per_token(cfg) / 1e6 - 636.3) < 0.05

@@ -40,7 +40,8 @@ class gpt_config(C.Structure):
     _fields_ = [("vocab_size", C.c_int32), ("padded_vocab", C.c_int32), ("n_layer", C.c_int32),
                 ("n_head", C.c_int32), ("n_embd", C.c_int32), ("block_size", C.c_int32),
                 ("batch", C.c_int32), ("grad_accum", C.c_int32), ("precision", C.c_int32),
-                ("dropout", C.c_float), ("flags", C.c_uint32)]
+                ("dropout", C.c_float), ("flags", C.c_uint32), ("lora_rank", C.c_int32),
+                ("lora_alpha", C.c_float)]
 
 
 class gpt_sizes(C.Structure):
@@ -110,7 +111,8 @@ def make_config(cfg, precision: str, batch: Optional[int] = None, grad_accum: Op
     return gpt_config(cfg.vocab_size, cfg.padded_vocab, cfg.n_layer, cfg.n_head, cfg.n_embd, cfg.block_size,
                       cfg.batch if batch is None else batch,
                       cfg.grad_accum if grad_accum is None else grad_accum, PREC[precision], float(dropout),
-                      (F_KV_CACHE if kv_cache else 0) | (F_MICROGPT if getattr(cfg, "variant", "gpt2") == "microgpt" else 0))
+                      (F_KV_CACHE if kv_cache else 0) | (F_MICROGPT if getattr(cfg, "variant", "gpt2") == "microgpt" else 0),
+                      int(getattr(cfg, "lora_rank", 0)), float(getattr(cfg, "lora_alpha", 0.0)))
 
 
 class Layout:

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgpt.so")
 
-SOURCES = ["gemm.hip", "attention.hip", "rowops.hip", "embed_bwd.hip", "optim.hip", "decode.hip", "runtime.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "rowops.hip", "embed_bwd.hip", "optim.hip", "decode.hip", "lora.hip", "runtime.cpp"]
 ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # per-source device flags: attention keeps its MFMA accumulators in ordinary VGPRs,

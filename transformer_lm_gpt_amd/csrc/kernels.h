@@ -235,6 +235,24 @@ hipError_t launch_transpose_bf16(const void* src, void* dst, const TransposeEntr
                                  int64_t total_tiles, hipStream_t s);
 // bf16 copy of n fp32 values.
 hipError_t launch_cast_bf16(const float* src, void* dst, size_t n, hipStream_t s);
+
+// Low-rank adapters: one job per adapted d x d block (the q or v rows of one
+// layer's qkv weight). A [r, d], B [d, r], W0 and dW [d, d] row-major fp32.
+struct LoraJob {
+  const float* A;
+  const float* B;
+  const float* W0;      // frozen base block
+  const float* dW;      // the block's weight gradient dq^T a (input of the adapter gradients)
+  float* dA;
+  float* dB;
+  float* weff;          // fp32 merged block, or NULL
+  void* weff_bf16;      // bf16 merged block, or NULL
+};
+// weff = W0 + s B A for every job; 1 <= r <= 64.
+hipError_t launch_lora_merge(const LoraJob* jobs, int njobs, int d, int r, float s, hipStream_t st);
+// dB = beta dB + s dW A^T and dA = beta dA + s B^T dW for every job (beta 0 or 1;
+// the outputs are not read when it is 0); 1 <= r <= 64.
+hipError_t launch_lora_grad(const LoraJob* jobs, int njobs, int d, int r, float s, float beta, hipStream_t st);
 // Zero n 32-bit words with a fill kernel (safe inside captured graphs).
 hipError_t launch_zero(void* p, size_t n_words, hipStream_t s);
 // dst[m * N + n] = float(src[m * ld + n]) for an [M, N] block of operand type.

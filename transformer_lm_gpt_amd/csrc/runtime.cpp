@@ -115,6 +115,14 @@ struct gpt_model {
   bool micro = false;
   std::string head = "wte";   // the tensor the logits are taken against
   Slice zbias;                // zeros standing in for the absent biases (4d floats)
+  // LoRA adapters on the q and v rows of every qkv weight: rank, branch scale
+  // alpha / r, first flat element of the adapters (they end the flat arrays), one
+  // job per adapted block, and in fp32 mode the merged qkv weights [L][3d][d]
+  int lora_r = 0;
+  float lora_s = 0.f;
+  size_t lora_off = 0;
+  std::vector<LoraJob> ljobs;
+  Slice ltable, weff;
   // state
   bool grads_fresh = true;
   bool fwd_pending = false;
@@ -150,9 +158,16 @@ const Tensor* find(const gpt_model* h, const std::string& name) {
 float* P(gpt_model* h, const std::string& name) { return (float*)h->buf.params + find(h, name)->offset; }
 float* G(gpt_model* h, const std::string& name) { return (float*)h->buf.grads + find(h, name)->offset; }
 // Weight as a GEMM operand: the bf16 shadow in bf16 mode, the fp32 master otherwise.
+// With adapters, the qkv weights are the merged W0 + s B A: written into the shadow
+// in bf16 mode, kept in the workspace in fp32 mode.
 const void* Wop(gpt_model* h, const std::string& name) {
   const Tensor* t = find(h, name);
   if (h->bf16) return (const uint16_t*)h->buf.shadow + t->offset;
+  const size_t n = name.size();
+  if (h->lora_r && n > 7 && name.compare(n - 7, 7, ".attn.w") == 0) {
+    const int l = std::atoi(name.c_str() + 1);   // "h<l>.attn.w"
+    return (const float*)((char*)h->buf.workspace + h->weff.off) + (size_t)l * 3 * h->d * h->d;
+  }
   return (const float*)h->buf.params + t->offset;
 }
 
@@ -263,6 +278,15 @@ void plan(gpt_model* h) {
     add("lnf.g", d, 1, 1, 0);
     add("lnf.b", d, 1, 1, 0);
   }
+  // the adapters end the flat arrays, so the optimizer's range is one contiguous run
+  h->lora_off = off;
+  for (int l = 0; l < L && h->lora_r; l++) {
+    const std::string p = "h" + std::to_string(l) + ".";
+    for (const char* t : {"q", "v"}) {
+      add(p + "lora_" + t + ".A", h->lora_r, d, 2, 1);
+      add(p + "lora_" + t + ".B", d, h->lora_r, 2, 1);
+    }
+  }
   h->n_flat = round_up(off, 256);
 
   // ---- activations for the largest micro-batch
@@ -354,7 +378,7 @@ void plan(gpt_model* h) {
   if (h->bf16) h->split_floats = std::max(h->split_floats, wgrad_group_ws_floats());
   h->split = w.take(h->split_floats * fb);
   for (const Tensor& t : h->tensors) {
-    if (t.ndim != 2 || t.name == "wpe") continue;
+    if (t.ndim != 2 || t.name == "wpe" || t.name.find(".lora_") != std::string::npos) continue;
     TransposeEntry e{(int64_t)t.offset, t.rows, t.cols, h->ttiles};
     h->tentries.push_back(e);
     h->ttiles += ((t.rows + 63) / 64) * ((t.cols + 63) / 64);
@@ -362,6 +386,8 @@ void plan(gpt_model* h) {
   h->ttable = w.take(h->tentries.size() * sizeof(TransposeEntry));
   h->opt = w.take(sizeof(OptState));
   h->zbias = w.take(4 * (size_t)d * fb);
+  h->weff = w.take(h->lora_r && !h->bf16 ? (size_t)L * 3 * d * d * fb : 0);
+  h->ltable = w.take(h->lora_r ? 2 * (size_t)L * sizeof(LoraJob) : 0);
   // the weight gradients as one grouped launch: wte (tied lm_head), then per layer
   // fcproj.w, fc.w, proj.w, attn.w; operands are [tokens, features] (m-contiguous)
   if (h->bf16) {
@@ -369,6 +395,9 @@ void plan(gpt_model* h) {
     bool ok = wgrad_group_ok(h->Vp, d, h->ldz, D, D) && h->split_floats >= wgrad_group_ws_floats();
     ok = ok && wgrad_group_ok(d, 4 * d, D, 4 * D, 4 * D) && wgrad_group_ok(4 * d, d, 4 * D, D, D);
     ok = ok && wgrad_group_ok(d, d, D, D, D) && wgrad_group_ok(3 * d, d, 3 * D, D, D);
+    // with adapters: the q and v row blocks of each qkv weight gradient only
+    if (h->lora_r)
+      ok = wgrad_group_ok(d, d, 3 * D, D, D) && d % 8 == 0 && h->split_floats >= wgrad_group_ws_floats();
     h->wgroup = ok;
     (void)Vp;
     h->wtable = w.take((4 * (size_t)L + 1) * sizeof(WgradProblem));
@@ -431,9 +460,9 @@ void build_wgrad_table(gpt_model* h) {
   h->wprobs.clear();
   h->wtiles = 0;
   const int d = h->d;
-  auto add = [&](const void* A, int64_t lda, const void* B, int64_t ldb, const std::string& w, int Mo, int No) {
+  auto add = [&](const void* A, int64_t lda, const void* B, int64_t ldb, float* C, int Mo, int No) {
     WgradProblem q;
-    q.A = A; q.lda = lda; q.B = B; q.ldb = ldb; q.C = G(h, w); q.ldc = No;
+    q.A = A; q.lda = lda; q.B = B; q.ldb = ldb; q.C = C; q.ldc = No;
     q.M = Mo; q.N = No;
     q.tiles_m = (Mo + 255) / 256; q.tiles_n = (No + 255) / 256;
     q.first_tile = h->wtiles;
@@ -441,14 +470,49 @@ void build_wgrad_table(gpt_model* h) {
     h->wtiles += wgrad_group_tiles(Mo, No);
     h->wprobs.push_back(q);
   };
-  add(act(h, h->logits), h->ldz, act(h, h->lnf), d, h->head, h->Vp, d);
+  if (h->lora_r) {
+    // adapters: dW of the q and v row blocks, the input of the adapter gradients
+    for (int l = h->L - 1; l >= 0; l--) {
+      const LayerAct& la = h->layers[l];
+      const std::string w = "h" + std::to_string(l) + ".attn.w";
+      add(dqkv_slot(h, l), 3 * d, act(h, la.ln1), d, G(h, w), d, d);
+      add((char*)dqkv_slot(h, l) + 2 * (size_t)d * h->op_size, 3 * d, act(h, la.ln1), d, G(h, w) + 2 * (size_t)d * d,
+          d, d);
+    }
+    return;
+  }
+  add(act(h, h->logits), h->ldz, act(h, h->lnf), d, G(h, h->head), h->Vp, d);
   for (int l = h->L - 1; l >= 0; l--) {
     const LayerAct& la = h->layers[l];
     const std::string p = "h" + std::to_string(l) + ".";
-    add(rx_slot(h, l + 1), d, act(h, la.h), 4 * d, p + "fcproj.w", d, 4 * d);
-    add(du_slot(h, l), 4 * d, act(h, la.ln2), d, p + "fc.w", 4 * d, d);
-    add(rm_slot(h, l), d, act(h, la.att), d, p + "proj.w", d, d);
-    add(dqkv_slot(h, l), 3 * d, act(h, la.ln1), d, p + "attn.w", 3 * d, d);
+    add(rx_slot(h, l + 1), d, act(h, la.h), 4 * d, G(h, p + "fcproj.w"), d, 4 * d);
+    add(du_slot(h, l), 4 * d, act(h, la.ln2), d, G(h, p + "fc.w"), 4 * d, d);
+    add(rm_slot(h, l), d, act(h, la.att), d, G(h, p + "proj.w"), d, d);
+    add(dqkv_slot(h, l), 3 * d, act(h, la.ln1), d, G(h, p + "attn.w"), 3 * d, d);
+  }
+}
+
+// The adapter jobs with this binding's addresses: layer l's q block, then its v block.
+void build_lora_jobs(gpt_model* h) {
+  h->ljobs.clear();
+  const size_t d = h->d;
+  for (int l = 0; l < h->L; l++) {
+    const std::string p = "h" + std::to_string(l) + ".";
+    const size_t attn = find(h, p + "attn.w")->offset;
+    for (int t = 0; t < 2; t++) {
+      const std::string a = p + (t ? "lora_v" : "lora_q");
+      const size_t row0 = t ? 2 * d : 0;   // first row of the block in the [3d, d] weight
+      LoraJob j;
+      j.A = P(h, a + ".A");
+      j.B = P(h, a + ".B");
+      j.W0 = (const float*)h->buf.params + attn + row0 * d;
+      j.dW = (const float*)h->buf.grads + attn + row0 * d;
+      j.dA = G(h, a + ".A");
+      j.dB = G(h, a + ".B");
+      j.weff = h->bf16 ? nullptr : (float*)((char*)h->buf.workspace + h->weff.off) + ((size_t)l * 3 * d + row0) * d;
+      j.weff_bf16 = h->bf16 ? (void*)((uint16_t*)h->buf.shadow + attn + row0 * d) : nullptr;
+      h->ljobs.push_back(j);
+    }
   }
 }
 
@@ -465,9 +529,21 @@ int upload_tables(gpt_model* h) {
     e = hipMemcpyAsync(ws(h, h->wtable), h->wprobs.data(), h->wprobs.size() * sizeof(WgradProblem),
                        hipMemcpyHostToDevice, h->stream);
   }
+  if (e == hipSuccess && h->lora_r) {
+    build_lora_jobs(h);
+    e = hipMemcpyAsync(ws(h, h->ltable), h->ljobs.data(), h->ljobs.size() * sizeof(LoraJob), hipMemcpyHostToDevice,
+                       h->stream);
+  }
   if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
   if (e != hipSuccess) return hip_check(h, e, "upload tables");
   h->tables_ready = true;
+  return GPT_OK;
+}
+
+// The merged qkv weights W0 + s B A (fp32 workspace copy or bf16 shadow rows).
+int lora_merge(gpt_model* h) {
+  RUN("lora", "lora_merge",
+      launch_lora_merge(ws<LoraJob>(h, h->ltable), 2 * h->L, h->d, h->lora_r, h->lora_s, h->stream));
   return GPT_OK;
 }
 
@@ -582,6 +658,9 @@ int gpt_create(const gpt_config* cfg, gpt_model** out) {
   if (c.precision != GPT_PREC_FP32 && c.precision != GPT_PREC_BF16) return fail(nullptr, GPT_E_INVAL, "unknown precision");
   if (!(c.dropout >= 0.0f && c.dropout < 1.0f)) return fail(nullptr, GPT_E_INVAL, "dropout must be in [0, 1)");
   if (c.flags & ~(uint32_t)(GPT_F_KV_CACHE | GPT_F_MICROGPT)) return fail(nullptr, GPT_E_INVAL, "unknown flags");
+  if (c.lora_rank < 0 || c.lora_rank > 64) return fail(nullptr, GPT_E_INVAL, "lora_rank must be in [0, 64]");
+  if (c.lora_rank > 0 && !(std::isfinite(c.lora_alpha) && c.lora_alpha != 0.0f))
+    return fail(nullptr, GPT_E_INVAL, "lora_alpha must be finite and nonzero");
   const int64_t M = (int64_t)c.batch * c.block_size;
   if (M > 32768) return fail(nullptr, GPT_E_UNSUPPORTED, "batch * block_size above 32768 is not implemented");
   {
@@ -605,6 +684,8 @@ int gpt_create(const gpt_config* cfg, gpt_model** out) {
   h->micro = (c.flags & GPT_F_MICROGPT) != 0;
   h->head = h->micro ? "lm_head" : "wte";
   h->op_size = h->bf16 ? 2 : 4;
+  h->lora_r = c.lora_rank;
+  h->lora_s = c.lora_rank > 0 ? c.lora_alpha / (float)c.lora_rank : 0.f;
   // keep an element when its Philox word >= floor(p 2^32); scale kept ones by 1/(1-p)
   h->drop.on = c.dropout > 0.0f ? 1 : 0;
   h->drop.thr = (uint32_t)std::floor((double)c.dropout * 4294967296.0);
@@ -679,7 +760,16 @@ int gpt_init_state(gpt_model* h) {
   if (h->bf16) {
     RUN("init", "bf16 shadow", launch_cast_bf16((const float*)h->buf.params, h->buf.shadow, h->n_flat, s));
     if ((rc = upload_tables(h))) return rc;
+    if (h->lora_r && (rc = lora_merge(h))) return rc;
     RUN("init", "transposed shadow", transpose_shadow(h));
+  } else if (h->lora_r) {
+    if ((rc = upload_tables(h))) return rc;
+    const size_t dd = (size_t)h->d * h->d;
+    for (int l = 0; l < h->L; l++)   // the k rows stay W0; the merge rewrites q and v
+      RUN("init", "qkv weight copy",
+          hipMemcpyAsync(ws<float>(h, h->weff) + (size_t)l * 3 * dd, P(h, "h" + std::to_string(l) + ".attn.w"),
+                         3 * dd * 4, hipMemcpyDeviceToDevice, s));
+    if ((rc = lora_merge(h))) return rc;
   }
   h->grads_fresh = true;
   h->fwd_pending = false;
@@ -849,10 +939,15 @@ int gpt_backward(gpt_model* h) {
   // In bf16 mode the weight gradients wait for the end of the backward (their
   // operands stay in per-layer slots); in fp32 mode each runs as soon as its
   // operands exist, before the residual gradient is overwritten.
+  // With adapters only the qkv weight gradient is formed, as this micro-batch's
+  // input to the adapter gradients (beta 0); the frozen tensors get none.
+  const bool lora = h->lora_r > 0;
   auto wgrad_now = [&](const void* A, int64_t lda, const void* Bm, int64_t ldb, const std::string& w, int Mo,
                        int No, const char* what) {
+    const size_t n = w.size();
+    if (lora && !(n > 7 && w.compare(n - 7, 7, ".attn.w") == 0)) return GPT_OK;
     GemmDesc g = gemm_desc(A, lda, false, Bm, ldb, false, G(h, w), No, Mo, No, M, EPI_ACC);
-    g.beta = beta;
+    g.beta = lora ? 0.f : beta;
     RUN("gemm_wgrad", what, gemm(h, g, bf));
     return GPT_OK;
   };
@@ -893,7 +988,7 @@ int gpt_backward(gpt_model* h) {
                        : gemm_desc(du, 4 * d, true, Wop(h, p + "fc.w"), d, false, dln, d, M, d, 4 * d, EPI_F32);
       RUN("gemm_dgrad", "fc_dgrad", gemm(h, g2, bf));
       if (!bf && (rc = wgrad_now(du, 4 * d, act(h, la.ln2), d, p + "fc.w", 4 * d, d, "fc_wgrad"))) return rc;
-      if (!h->micro && !fc_rows && (rc = colsum(h, du, bf, 4 * d, M, 4 * d, p + "fc.b"))) return rc;
+      if (!h->micro && !lora && !fc_rows && (rc = colsum(h, du, bf, 4 * d, M, 4 * d, p + "fc.b"))) return rc;
       const std::string fcproj_b = p + "fcproj.b";
       if ((rc = ln_bwd(h, dln, act<float>(h, la.xmid), act<float>(h, la.ln2_mean), act<float>(h, la.ln2_rstd),
                        p + "ln2.g", p + "ln2.b", dres, fcproj_b.c_str(), bf ? rm_slot(h, l) : (void*)dxm, M,
@@ -918,7 +1013,7 @@ int gpt_backward(gpt_model* h) {
                        : gemm_desc(dqkv, 3 * d, true, Wop(h, p + "attn.w"), d, false, dln, d, M, d, 3 * d, EPI_F32);
       RUN("gemm_dgrad", "qkv_dgrad", gemm(h, g2, bf));
       if (!bf && (rc = wgrad_now(dqkv, 3 * d, act(h, la.ln1), d, p + "attn.w", 3 * d, d, "qkv_wgrad"))) return rc;
-      if (!h->micro && !qkv_rows && (rc = colsum(h, dqkv, bf, 3 * d, M, 3 * d, p + "attn.b"))) return rc;
+      if (!h->micro && !lora && !qkv_rows && (rc = colsum(h, dqkv, bf, 3 * d, M, 3 * d, p + "attn.b"))) return rc;
       const std::string proj_b = p + "proj.b";
       // d x_0 feeds only the embedding backward, which reads the fp32 copy
       void* xop = l == 0 ? nullptr : (bf ? rx_slot(h, l) : (void*)dxm);
@@ -933,15 +1028,24 @@ int gpt_backward(gpt_model* h) {
     // allow it (K = B*T a multiple of 32), else one GEMM each
     if (h->wgroup && M % 32 == 0) {
       RUN("gemm_wgrad", "grouped_wgrad",
-          launch_wgrad_group(ws<WgradProblem>(h, h->wtable), (int)h->wprobs.size(), h->wtiles, M, beta,
+          launch_wgrad_group(ws<WgradProblem>(h, h->wtable), (int)h->wprobs.size(), h->wtiles, M, lora ? 0.f : beta,
                              (float*)((char*)h->buf.workspace + h->split.off), h->split_floats, s));
     } else {
       for (const WgradProblem& q : h->wprobs) {
         GemmDesc g = gemm_desc(q.A, q.lda, false, q.B, q.ldb, false, q.C, q.ldc, q.M, q.N, M, EPI_ACC);
-        g.beta = beta;
+        g.beta = lora ? 0.f : beta;
         RUN("gemm_wgrad", "wgrad", gemm(h, g, bf));
       }
     }
+  }
+  if (lora) {
+    // the adapters' gradients from this micro-batch's q and v weight gradients; the
+    // frozen biases, norms and embeddings take none
+    RUN("lora", "lora_grad",
+        launch_lora_grad(ws<LoraJob>(h, h->ltable), 2 * L, d, h->lora_r, h->lora_s, beta, s));
+    h->grads_fresh = false;
+    h->fwd_pending = false;
+    return GPT_OK;
   }
   if (!h->rjobs.empty())
     RUN("colsum", "bias_and_ln_grads",
@@ -990,12 +1094,19 @@ int gpt_adamw_step(gpt_model* h, float lr, float beta1, float beta2, float eps, 
   hipStream_t s = h->stream;
   float* part = ws<float>(h, h->norm_part);
   OptState* st = ws<OptState>(h, h->opt);
-  RUN("adamw", "grad_sumsq", launch_sumsq_partial((const float*)h->buf.grads, h->n_flat, part, s));
+  // With adapters the norm, the clip and the update cover the adapters alone (the
+  // last, contiguous run of the flat arrays, all 2-D and decayed); the merged qkv
+  // weights are rebuilt after the update.
+  const size_t o = h->lora_r ? h->lora_off : 0;
+  const size_t n = h->n_flat - o;
+  const size_t n_decay = h->lora_r ? n : h->n_decay;
+  RUN("adamw", "grad_sumsq", launch_sumsq_partial((const float*)h->buf.grads + o, n, part, s));
   RUN("adamw", "opt_prepare", launch_opt_prepare(part, st, clip, beta1, beta2, d_grad_norm, s));
   RUN("adamw", "adamw",
-      launch_adamw((float*)h->buf.params, (const float*)h->buf.grads, (float*)h->buf.m, (float*)h->buf.v,
-                   h->bf16 ? h->buf.shadow : nullptr, h->n_flat, h->n_decay, st, lr, beta1, beta2, eps, weight_decay,
-                   s));
+      launch_adamw((float*)h->buf.params + o, (const float*)h->buf.grads + o, (float*)h->buf.m + o,
+                   (float*)h->buf.v + o, h->bf16 && !h->lora_r ? h->buf.shadow : nullptr, n, n_decay, st, lr, beta1,
+                   beta2, eps, weight_decay, s));
+  if (h->lora_r && (rc = lora_merge(h))) return rc;
   if (h->bf16) RUN("adamw", "transposed shadow", transpose_shadow(h));
   h->grads_fresh = true;
   return GPT_OK;
