@@ -129,3 +129,22 @@ def test_gpt2_lora_full_step_identical_copies():
     wv = check_tensors(v_gpu, tr.v, "bf16", "v", tol=6e-2)
     say(f"  loss {np.mean(gl):.5f} vs {ref['loss']:.5f}; worst grad {wg}; param {wp[0]:.2e} m {wm[0]:.2e} v {wv[0]:.2e}")
     gpu.close()
+
+
+@pytest.mark.parametrize("rank,prec,steps", [
+    (12, "fp32", 2),     # a full rank chunk of 8 and a partial one
+    (5, "bf16", 1),      # one partial chunk
+    (64, "fp32", 1),     # the largest rank the adapter kernels take
+    (64, "bf16", 1),
+])
+def test_lora_rank_edges(rank, prec, steps):
+    cfg = W.CONFIGS["char_small_lora"].with_(lora_rank=rank)
+    run_steps("char_small_lora", prec, steps=steps, cfg=cfg)
+
+
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+def test_lora_widest_rows(prec):
+    # n_embd 1024: four float4 per lane in the merge and dB kernels, and B's rank
+    # chunk for all 1024 rows filling the dA kernel's LDS stage
+    cfg = W.CONFIGS["char_small_lora"].with_(n_layer=1, n_head=16, n_embd=1024, block_size=16, batch=2)
+    run_steps("char_small_lora", prec, steps=1, cfg=cfg)
