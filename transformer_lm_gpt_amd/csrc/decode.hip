@@ -172,6 +172,7 @@ hipError_t launch_attn_decode(const void* qkv, const void* cache, void* out, boo
 // segment of indices, the segment sums are added in order, and the token is the first
 // index whose running sum exceeds u times the total.
 constexpr int SAMPLE_THREADS = 1024;
+constexpr int SAMPLE_REG = 50;                        // logits per thread kept in registers (V <= 51,200)
 
 __device__ inline uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -190,23 +191,35 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_kernel(const float* __r
   __shared__ uint32_t sel[2];                         // prefix of the k-th key, count still needed
   __shared__ float csum[NW][64];                      // weight sum of each lane's run
   __shared__ int answer;                              // the wavefront whose segment holds the draw
+  __shared__ uint32_t wsuf[4];                        // bins counted by each quarter of the histogram
   const float* z = logits + (int64_t)blockIdx.x * ld;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
-  // maximum, with its lowest index
+  // Thread tid takes the logits tid + j * SAMPLE_THREADS: the first SAMPLE_REG of them
+  // stay in registers for the maximum and the radix passes (every vocabulary up to
+  // SAMPLE_REG * SAMPLE_THREADS), the rest are read again from memory in each pass.
+  float zr[SAMPLE_REG];
+#pragma unroll
+  for (int j = 0; j < SAMPLE_REG; j++) {
+    const int i = tid + j * SAMPLE_THREADS;
+    zr[j] = i < V ? z[i] : -INFINITY;
+  }
+  auto each = [&](auto&& f) {                         // f(value, index), indices ascending
+#pragma unroll
+    for (int j = 0; j < SAMPLE_REG; j++)
+      if (tid + j * SAMPLE_THREADS < V) f(zr[j], tid + j * SAMPLE_THREADS);
+    for (int i = tid + SAMPLE_REG * SAMPLE_THREADS; i < V; i += SAMPLE_THREADS) f(z[i], i);
+  };
+
+  // maximum, with its lowest index (indices rise within a thread: the first maximum stays)
   float mx = -INFINITY;
   int mi = 0x7fffffff;
-  for (int i0 = tid; i0 < V; i0 += UNR * SAMPLE_THREADS) {
-    float v[UNR];
-#pragma unroll
-    for (int u = 0; u < UNR; u++) v[u] = i0 + u * SAMPLE_THREADS < V ? z[i0 + u * SAMPLE_THREADS] : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < UNR; u++)
-      if (v[u] > mx) {                                // indices rise with u: the first maximum stays
-        mx = v[u];
-        mi = i0 + u * SAMPLE_THREADS;
-      }
-  }
+  each([&](float v, int i) {
+    if (v > mx) {
+      mx = v;
+      mi = i;
+    }
+  });
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float v2 = __shfl_xor(mx, o, 64);
@@ -253,18 +266,10 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_kernel(const float* __r
       __syncthreads();
       const uint32_t prefix = sel[0];
       const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-      for (int i0 = tid; i0 < V; i0 += UNR * SAMPLE_THREADS) {
-        uint32_t key[UNR];
-#pragma unroll
-        for (int u = 0; u < UNR; u++) {
-          const int i = i0 + u * SAMPLE_THREADS;
-          key[u] = i < V ? order_key(z[i]) : 0u;
-        }
-#pragma unroll
-        for (int u = 0; u < UNR; u++)
-          if (i0 + u * SAMPLE_THREADS < V && (key[u] & hi_mask) == prefix)
-            atomicAdd(&hist[w][(key[u] >> shift) & 255u], 1u);
-      }
+      each([&](float v, int) {
+        const uint32_t key = order_key(v);
+        if ((key & hi_mask) == prefix) atomicAdd(&hist[w][(key >> shift) & 255u], 1u);
+      });
       __syncthreads();
       if (tid < 256) {
         uint32_t c = 0;
@@ -276,11 +281,24 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_kernel(const float* __r
       // the bin holding the need-th largest key: the one whose suffix count (bins at or
       // above it) reaches `need` while the suffix above it does not; every bin in parallel
       const uint32_t need = sel[1];
+      // suffix counts (bins at or above each bin) by a scan over the four wavefronts
+      // that hold the 256 bins, then their totals
+      uint32_t c = 0, suf = 0;
+      if (tid < 256) {
+        c = suf = hist[0][tid];
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t t = __shfl_down(suf, o, 64);
+          if (lane + o < 64) suf += t;
+        }
+        if (lane == 0) wsuf[w] = suf;
+      }
       __syncthreads();
       if (tid < 256) {
-        uint32_t above = 0;
-        for (int j = 255; j > tid; j--) above += hist[0][j];
-        if (above < need && above + hist[0][tid] >= need) {
+        uint32_t incl = suf;
+        for (int q = w + 1; q < 4; q++) incl += wsuf[q];
+        const uint32_t above = incl - c;
+        if (above < need && incl >= need) {
           sel[0] = prefix | ((uint32_t)tid << shift);
           sel[1] = need - above;
         }
@@ -337,16 +355,20 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_kernel(const float* __r
   const float lstart = start + incl - cs;
   const uint64_t claim = __ballot(cs > 0.f && lstart <= target);
   if (lane != 63 - __builtin_clzll(claim)) return;    // the last non-empty run starting at or before it
+  // the run's weights added in index order, sixteen logits fetched at a time
   float acc = lstart;
   int pick = -1, last = -1;
-  for (int i = a0; i < a1; i++) {
-    const float wi = weight(z[i]);
-    if (wi > 0.f) {
-      last = i;
-      acc += wi;
-      if (acc > target) {
-        pick = i;
-        break;
+  for (int i = a0; i < a1 && pick < 0; i += 16) {
+    float v[16];
+#pragma unroll
+    for (int e = 0; e < 16; e++) v[e] = i + e < a1 ? z[i + e] : -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; e++) {
+      const float wi = i + e < a1 ? weight(v[e]) : 0.f;
+      if (pick < 0 && wi > 0.f) {
+        last = i + e;
+        acc += wi;
+        if (acc > target) pick = i + e;
       }
     }
   }
