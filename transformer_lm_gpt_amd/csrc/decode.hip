@@ -57,15 +57,18 @@ hipError_t launch_kv_append(const void* qkv, bool bf16_ops, void* cache, int B, 
   return hipGetLastError();
 }
 
-// One query per (sequence, head) against keys 0 .. len-1 of the cache:
+// One query per (sequence, head) against keys 0 .. len-1:
 // s_j = q . k_j / sqrt(hd), p = softmax(s), o = sum_j p_j v_j. One workgroup of 256
-// per (b, h); the scores of all keys sit in LDS (len <= DEC_MAX_T). For the value sum
+// per (b, h); the scores of all keys sit in LDS (len <= DEC_MAX_T). Keys and values
+// 0 .. len-2 come from the cache; those of the new position len-1 are read from this
+// step's qkv row, and the workgroup also stores them (its head's columns) into the
+// cache row len-1 for later steps, which no workgroup of this launch reads. For the value sum
 // with 16-byte rows, thread t takes 8 columns (t mod hd/8) of every (256 / (hd/8))-th
 // key, and the per-slot partial vectors are added in slot order; otherwise each
 // wavefront takes every fourth key with a lane per column.
 constexpr int DEC_MAX_T = 8192;
 template <typename T>
-__global__ __launch_bounds__(256) void attn_decode_kernel(const T* __restrict__ qkv, const T* __restrict__ cache,
+__global__ __launch_bounds__(256) void attn_decode_kernel(const T* __restrict__ qkv, T* __restrict__ cache,
                                                           T* __restrict__ out, int H, int hd, int Tmax, int len,
                                                           float scale) {
   __shared__ float sc[DEC_MAX_T];
@@ -75,13 +78,18 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const T* __restrict__ 
   const int b = blockIdx.x / H, h = blockIdx.x % H;
   const int d = H * hd;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if (tid < hd) qs[tid] = to_f32(qkv[(int64_t)b * 3 * d + h * hd + tid]);
+  const T* qrow = qkv + (int64_t)b * 3 * d + h * hd;   // this head's q; its k at + d, v at + 2d
+  T* kb = cache + (int64_t)b * Tmax * 2 * d + h * hd;
+  if (tid < hd) {
+    qs[tid] = to_f32(qrow[tid]);
+    kb[(int64_t)(len - 1) * 2 * d + tid] = qrow[d + tid];
+    kb[(int64_t)(len - 1) * 2 * d + d + tid] = qrow[2 * d + tid];
+  }
   __syncthreads();
-  const T* kb = cache + (int64_t)b * Tmax * 2 * d + h * hd;
   float mx = -INFINITY;
   const bool vec = sizeof(T) == 2 && hd % 8 == 0;   // 16-byte key reads (rows 16-byte aligned)
   for (int j = tid; j < len; j += 256) {
-    const T* kr = kb + (int64_t)j * 2 * d;
+    const T* kr = j == len - 1 ? qrow + d : kb + (int64_t)j * 2 * d;
     float s = 0.f;
     if (vec) {
       for (int c8 = 0; c8 < hd; c8 += 8) {
@@ -122,7 +130,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const T* __restrict__ 
       const T* vb = kb + d + ch * 8;
 #pragma unroll 4
       for (int j = slot; j < len; j += slots) {
-        const bf16x8 v = *(const bf16x8*)(vb + (int64_t)j * 2 * d);
+        const bf16x8 v = *(const bf16x8*)(j == len - 1 ? qrow + 2 * d + ch * 8 : vb + (int64_t)j * 2 * d);
         const float pj = sc[j];
 #pragma unroll
         for (int e = 0; e < 8; e++) acc[e] += pj * (float)v[e];
@@ -141,7 +149,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const T* __restrict__ 
   float o = 0.f;
   if (lane < hd) {
     const T* vb = kb + d + lane;
-    for (int j = w; j < len; j += 4) o += sc[j] * to_f32(vb[(int64_t)j * 2 * d]);
+    for (int j = w; j < len; j += 4) o += sc[j] * to_f32(j == len - 1 ? qrow[2 * d + lane] : vb[(int64_t)j * 2 * d]);
   }
   red[w][lane] = o;
   __syncthreads();
@@ -151,16 +159,16 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const T* __restrict__ 
   }
 }
 
-hipError_t launch_attn_decode(const void* qkv, const void* cache, void* out, bool bf16_ops, int B, int H, int hd,
+hipError_t launch_attn_decode(const void* qkv, void* cache, void* out, bool bf16_ops, int B, int H, int hd,
                               int Tmax, int len, hipStream_t s) {
   if (hd <= 0 || hd > 64 || len < 1 || len > Tmax || len > DEC_MAX_T) return hipErrorInvalidValue;
   const float scale = 1.0f / sqrtf((float)hd);
   if (bf16_ops)
-    hipLaunchKernelGGL(attn_decode_kernel<bf16>, dim3(B * H), dim3(256), 0, s, (const bf16*)qkv, (const bf16*)cache,
+    hipLaunchKernelGGL(attn_decode_kernel<bf16>, dim3(B * H), dim3(256), 0, s, (const bf16*)qkv, (bf16*)cache,
                        (bf16*)out, H, hd, Tmax, len, scale);
   else
     hipLaunchKernelGGL(attn_decode_kernel<float>, dim3(B * H), dim3(256), 0, s, (const float*)qkv,
-                       (const float*)cache, (float*)out, H, hd, Tmax, len, scale);
+                       (float*)cache, (float*)out, H, hd, Tmax, len, scale);
   return hipGetLastError();
 }
 

@@ -195,9 +195,10 @@ hipError_t launch_embed_pos(const float* wte, const float* wpe, const int32_t* t
 // b * Tmax + pos0 + t ([B_max * Tmax, 2d], operand type). pos0 + T <= Tmax.
 hipError_t launch_kv_append(const void* qkv, bool bf16_ops, void* cache, int B, int T, int Tmax, int pos0, int d,
                             hipStream_t s);
-// Causal attention of one new query per sequence (q in qkv [B, 3d]) against cache
-// positions 0 .. len-1: out [B, d]. len <= 8192.
-hipError_t launch_attn_decode(const void* qkv, const void* cache, void* out, bool bf16_ops, int B, int H, int hd,
+// Causal attention of one new query per sequence (q, k, v in qkv [B, 3d]) against
+// positions 0 .. len-1: 0 .. len-2 from the cache, len-1 from qkv, whose k and v the
+// call also stores into cache position len-1. out [B, d]. len <= 8192.
+hipError_t launch_attn_decode(const void* qkv, void* cache, void* out, bool bf16_ops, int B, int H, int hd,
                               int Tmax, int len, hipStream_t s);
 // One token per row of fp32 logits [B, ld] over V columns: the argmax (lowest index
 // on ties) when temperature <= 0, else a draw with uniform[b] from the softmax of

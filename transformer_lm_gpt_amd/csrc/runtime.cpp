@@ -849,7 +849,7 @@ int gpt_decode(gpt_model* h, const int32_t* d_tokens, float* d_logits) {
       g.bias = bias_of(h, p + "attn.b");
       RUN("decode", "qkv", gemm(h, g, bf));
     }
-    RUN("decode", "kv_append", launch_kv_append(act(h, a.qkv), bf, kv_slot(h, l), B, 1, h->Tmax, pos, d, s));
+    // the attention stores this position's keys and values into the cache itself
     RUN("decode", "attn",
         launch_attn_decode(act(h, a.qkv), kv_slot(h, l), act(h, a.att), bf, B, h->H, h->hd, h->Tmax, pos + 1, s));
     {
