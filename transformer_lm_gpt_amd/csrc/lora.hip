@@ -56,38 +56,52 @@ __global__ __launch_bounds__(256) void lora_merge_kernel(const LoraJob* __restri
   }
 }
 
-// dB[n, j] = beta * dB[n, j] + s * sum_k dW[n, k] A[j, k]: one wavefront per row n of
-// one job; the row of dW stays in registers, and per j the 64 lanes reduce in a
-// fixed order (lane j keeps the sum, lanes < r store).
+// dB[n, j] = beta * dB[n, j] + s * sum_k dW[n, k] A[j, k]: one wavefront per four rows
+// n of one job (each row of A is read once for the four); the rows of dW stay in
+// registers, and per j and row the 64 lanes reduce in a fixed order (lane j keeps
+// the sum, lanes < r store).
+constexpr int LORA_B_ROWS = 4;
 __global__ __launch_bounds__(256) void lora_grad_b_kernel(const LoraJob* __restrict__ jobs, int d, int r, float s,
                                                           float beta) {
   const LoraJob jb = jobs[blockIdx.y];
-  const int n = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (n >= d) return;
-  f32x4 w[LORA_MAX_NI];
+  const int n0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * LORA_B_ROWS, lane = threadIdx.x & 63;
+  if (n0 >= d) return;
+  f32x4 w[LORA_B_ROWS][LORA_MAX_NI];
 #pragma unroll
-  for (int i = 0; i < LORA_MAX_NI; i++) {
-    const int k = 4 * lane + 256 * i;
-    w[i] = k < d ? ld4(jb.dW + (size_t)n * d + k) : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  float mine = 0.f;
-  for (int j = 0; j < r; j++) {
-    const float* Arow = jb.A + (size_t)j * d;
-    float p = 0.f;
+  for (int q = 0; q < LORA_B_ROWS; q++)
 #pragma unroll
     for (int i = 0; i < LORA_MAX_NI; i++) {
       const int k = 4 * lane + 256 * i;
-      if (k < d) {
-        const f32x4 a = ld4(Arow + k);
-        p += (w[i][0] * a[0] + w[i][1] * a[1]) + (w[i][2] * a[2] + w[i][3] * a[3]);
-      }
+      w[q][i] = k < d && n0 + q < d ? ld4(jb.dW + (size_t)(n0 + q) * d + k) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    p = wave_sum(p);
-    if (lane == j) mine = p;
+  float mine[LORA_B_ROWS];
+#pragma unroll
+  for (int q = 0; q < LORA_B_ROWS; q++) mine[q] = 0.f;
+  for (int j = 0; j < r; j++) {
+    const float* Arow = jb.A + (size_t)j * d;
+    f32x4 a[LORA_MAX_NI];
+#pragma unroll
+    for (int i = 0; i < LORA_MAX_NI; i++) {
+      const int k = 4 * lane + 256 * i;
+      a[i] = k < d ? ld4(Arow + k) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int q = 0; q < LORA_B_ROWS; q++) {
+      float p = 0.f;
+#pragma unroll
+      for (int i = 0; i < LORA_MAX_NI; i++)
+        if (4 * lane + 256 * i < d)
+          p += (w[q][i][0] * a[i][0] + w[q][i][1] * a[i][1]) + (w[q][i][2] * a[i][2] + w[q][i][3] * a[i][3]);
+      p = wave_sum(p);
+      if (lane == j) mine[q] = p;
+    }
   }
-  if (lane < r) {
-    float* o = jb.dB + (size_t)n * r + lane;
-    *o = (beta != 0.f ? beta * *o : 0.f) + s * mine;
+#pragma unroll
+  for (int q = 0; q < LORA_B_ROWS; q++) {
+    if (lane < r && n0 + q < d) {
+      float* o = jb.dB + (size_t)(n0 + q) * r + lane;
+      *o = (beta != 0.f ? beta * *o : 0.f) + s * mine[q];
+    }
   }
 }
 
@@ -161,7 +175,8 @@ hipError_t launch_lora_merge(const LoraJob* jobs, int njobs, int d, int r, float
 hipError_t launch_lora_grad(const LoraJob* jobs, int njobs, int d, int r, float s, float beta, hipStream_t st) {
   if (njobs <= 0) return hipSuccess;
   if (r < 1 || r > LORA_MAX_RANK || d < 1 || d % 4 != 0 || d > 256 * LORA_MAX_NI) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(lora_grad_b_kernel, dim3((d + 3) / 4, njobs), dim3(256), 0, st, jobs, d, r, s, beta);
+  hipLaunchKernelGGL(lora_grad_b_kernel, dim3((d + 4 * LORA_B_ROWS - 1) / (4 * LORA_B_ROWS), njobs), dim3(256), 0, st,
+                     jobs, d, r, s, beta);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(lora_grad_a_kernel, dim3((d + 255) / 256, njobs), dim3(256), 0, st, jobs, d, r, s, beta);
