@@ -106,8 +106,8 @@ __global__ __launch_bounds__(256) void lora_grad_b_kernel(const LoraJob* __restr
 }
 
 // dA[j, k] = beta * dA[j, k] + s * sum_n B[n, j] dW[n, k]: a workgroup takes 256
-// columns of one job, its four wavefronts a quarter of the rows each (in order,
-// loads fetched eight rows ahead), eight ranks at a time with those ranks' column
+// columns of one job and eight ranks (blockIdx.z), its four wavefronts a quarter of
+// the rows each (in order, loads fetched eight rows ahead), with those ranks' column
 // of B staged in LDS (zero past r); the quarters are added in wavefront order.
 constexpr int LORA_JC = 8;
 typedef const f32x4 __attribute__((address_space(1)))* gf32x4p;   // global memory
@@ -121,8 +121,8 @@ __global__ __launch_bounds__(256) void lora_grad_a_kernel(const LoraJob* __restr
   const int k = blockIdx.x * 256 + 4 * lane;
   const bool live = k < d;
   const int rows = (d + 3) / 4, n0 = wv * rows, n1 = min(d, n0 + rows);
-  for (int j0 = 0; j0 < r; j0 += LORA_JC) {
-    __syncthreads();   // the previous chunk's readers of bsh are done
+  {
+    const int j0 = blockIdx.z * LORA_JC;
     float* bs = (float*)bsh;
     for (int e = threadIdx.x; e < d * LORA_JC; e += 256) {
       const int n = e / LORA_JC, j = j0 + e % LORA_JC;
@@ -179,7 +179,8 @@ hipError_t launch_lora_grad(const LoraJob* jobs, int njobs, int d, int r, float 
                      jobs, d, r, s, beta);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lora_grad_a_kernel, dim3((d + 255) / 256, njobs), dim3(256), 0, st, jobs, d, r, s, beta);
+  hipLaunchKernelGGL(lora_grad_a_kernel, dim3((d + 255) / 256, njobs, (r + LORA_JC - 1) / LORA_JC), dim3(256), 0, st,
+                     jobs, d, r, s, beta);
   return hipGetLastError();
 }
 
