@@ -1015,7 +1015,9 @@ int gpt_backward(gpt_model* h) {
       if (!bf && (rc = wgrad_now(dqkv, 3 * d, act(h, la.ln1), d, p + "attn.w", 3 * d, d, "qkv_wgrad"))) return rc;
       if (!h->micro && !lora && !qkv_rows && (rc = colsum(h, dqkv, bf, 3 * d, M, 3 * d, p + "attn.b"))) return rc;
       const std::string proj_b = p + "proj.b";
-      // d x_0 feeds only the embedding backward, which reads the fp32 copy
+      // d x_0 feeds only the embedding backward, which reads the fp32 copy; with
+      // adapters the embeddings are frozen and nothing reads it
+      if (lora && l == 0) continue;
       void* xop = l == 0 ? nullptr : (bf ? rx_slot(h, l) : (void*)dxm);
       if ((rc = ln_bwd(h, dln, act<float>(h, la.x), act<float>(h, la.ln1_mean), act<float>(h, la.ln1_rstd),
                        p + "ln1.g", p + "ln1.b", dres, proj_b.c_str(), xop, M, (int)site_attn_out(l),
