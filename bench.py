@@ -59,23 +59,43 @@ def flops_per_token(cfg) -> float:
     return 6.0 * N + 12.0 * L * d * T
 
 
-def cpu_baseline(cfg, params, batches, n_seq: int, dropout: float = 0.0):
-    """The oracle, as it stands, on n_seq sequences of the same workload (float64)."""
-    from oracle import gpt_oracle as O
+def blas_info():
+    """(library, threads) of the BLAS NumPy calls, as threadpoolctl reports it."""
     try:
         from threadpoolctl import threadpool_info
-        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return f"{i.get('internal_api')} {i.get('version') or ''}".strip(), int(i.get("num_threads", 1))
     except Exception:
-        threads = os.cpu_count() or 1
+        pass
+    return "unknown", 0
+
+
+def cpu_baseline(cfg, params, batches, n_seq: int, dropout: float = 0.0):
+    """The oracle as it stands, in float32, on the first micro-batch of the workload
+    (its first n_seq sequences: the whole micro-batch by default) and one AdamW
+    update of every parameter. The step rate is extrapolated to the workload's A
+    micro-batches per update: tokens of A micro-batches over A times the measured
+    forward + backward plus the measured clip + AdamW."""
+    from oracle import gpt_oracle as O
     tok, tgt = batches[0]
     tok, tgt = tok[:n_seq], tgt[:n_seq]
+    A = len(batches)
+    lib, threads = blas_info()
+    tr = O.Trainer(params, cfg, dtype=np.float32, dropout=O.Dropout(dropout, 1337) if dropout > 0 else None)
+    marks = []
     t0 = time.perf_counter()
-    O.microbatch(params, tok, tgt, cfg, grad_scale=1.0 / tok.size,
-                 dropout=O.Dropout(dropout, 1337) if dropout > 0 else None)
-    dt = time.perf_counter() - t0
-    return {"value": round(tok.size / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_seq} sequence(s) x {tok.shape[1]} tokens, forward + backward in float64 "
-                      f"({dt:.1f} s); AdamW excluded"}
+    tr.step([(tok, tgt)], progress=lambda i, l: marks.append(time.perf_counter()))
+    t2 = time.perf_counter()
+    t_mb, t_opt = marks[0] - t0, t2 - marks[0]
+    step_s = A * t_mb + t_opt
+    return {"value": round(A * tok.size / step_s, 3), "unit": "tokens/s", "cores": os.cpu_count(),
+            "kind": "oracle",
+            "sample": f"float32 oracle: 1 micro-batch of {tok.shape[0]} x {tok.shape[1]} tokens forward + backward "
+                      f"({t_mb:.1f} s) and one clip + AdamW over all {O.n_params(cfg)} parameters ({t_opt:.1f} s); "
+                      f"rate for a step of {A} micro-batches = {A} x {t_mb:.1f} + {t_opt:.1f} s",
+            "blas": lib, "blas_threads": threads,
+            "note": "per-sequence loops in NumPy: only the BLAS matrix products use several threads"}
 
 
 def decode_bytes(cfg, B: int, length: int, op_bytes: int) -> float:
@@ -199,7 +219,8 @@ def main(argv=None):
     ap.add_argument("--kernel", default="gemm_wgrad",
                     help="kernel family whose launches are timed for the roofline line "
                          "(gemm_wgrad: the grouped weight-gradient GEMM, the step's largest kernel; lm_head_fwd)")
-    ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the oracle's timed sample (0: skip)")
+    ap.add_argument("--cpu-seqs", type=int, default=12,
+                    help="sequences of the first micro-batch in the oracle's timed sample (0: skip)")
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="dropout rate of the timed model (the GPT-2 124M workload uses 0)")
     ap.add_argument("--decode", action="store_true", help="measure generation with the key/value cache")

@@ -73,6 +73,23 @@ extern "C" {
                                   own (tensors wte, wpe, h<l>.attn.w (q|k|v rows),
                                   h<l>.proj.w, h<l>.fc.w, h<l>.fcproj.w, lm_head; all
                                   decayed)                                           */
+#define GPT_F_DEBUG_CHECKS 4u  /* gpt_config.flags: check every token id (gpt_forward_loss,
+                                  gpt_forward_logits, gpt_prefill, gpt_decode) and target
+                                  id (gpt_forward_loss) against [0, vocab_size) on the
+                                  device before the embedding gather reads them (the
+                                  fine-tuning article, data paragraph, and the nanoGPT
+                                  README translation's OpenWebText preparation: the
+                                  ids are GPT-2 BPE ids stored as uint16, of a
+                                  50,257-token vocabulary). An id outside
+                                  that range sets a sticky device flag: the next
+                                  gpt_adamw_step is skipped (parameters, moments and the
+                                  step counter untouched) and the next gpt_sync returns
+                                  GPT_E_INVAL. Nothing reads outside the tables either
+                                  way: without the flag an id in [vocab_size,
+                                  padded_vocab) is an ordinary padded row and an id
+                                  outside [0, padded_vocab) yields NaN rows and a NaN
+                                  loss (GPT_E_NONFINITE at the step). One extra launch
+                                  of M threads per call.                               */
 #define GPT_PREC_BF16 1        /* GEMM/attention operands bf16, everything else fp32 */
 
 typedef struct gpt_model gpt_model;
@@ -88,7 +105,7 @@ typedef struct gpt_config {
   int32_t grad_accum;    /* A: backward scales the micro-batch mean loss by 1/A     */
   int32_t precision;     /* GPT_PREC_FP32 or GPT_PREC_BF16                          */
   float   dropout;       /* p in [0, 1): see gpt_set_dropout_seed                   */
-  uint32_t flags;        /* GPT_F_KV_CACHE | GPT_F_MICROGPT, or 0                   */
+  uint32_t flags;        /* GPT_F_KV_CACHE | GPT_F_MICROGPT | GPT_F_DEBUG_CHECKS    */
   int32_t lora_rank;     /* r in [0, 64]; r > 0 adds low-rank adapters (fine-tuning
                             article, LoRA section) to the q and v projections of
                             every block: tensors h<l>.lora_q.A [r, n_embd],
@@ -158,9 +175,20 @@ int gpt_bind(gpt_model* h, const gpt_buffers* bufs, void* hip_stream);
  * gradients, both moments and the step counter. */
 int gpt_init_state(gpt_model* h);
 
+/* Call after writing new weights into `params` mid-training (a host load of a
+ * checkpoint's weights, a manual edit): rebuilds what is derived from them, the
+ * bf16 shadow and its transposed half and, with LoRA adapters, the merged qkv
+ * weights W0 + (alpha / r) B A, and nothing else. Gradients, both Adam moments
+ * and the step counter are left as they are (gpt_init_state resets them). A
+ * pending forward is invalidated: its saved activations belong to the old
+ * weights, so gpt_backward returns GPT_E_STATE until the next gpt_forward_loss.
+ * GPT_E_STATE if no buffers are bound. */
+int gpt_params_loaded(gpt_model* h);
+
 /* Forward of one micro-batch and the loss.
  * d_tokens, d_targets: int32 [B, T] row-major on the device, ids in
- * [0, vocab_size); 1 <= B <= batch, 1 <= T <= block_size. The tokens are
+ * [0, vocab_size) (checked on the device only with GPT_F_DEBUG_CHECKS);
+ * 1 <= B <= batch, 1 <= T <= block_size. The tokens are
  * copied, so the caller may reuse them after the call returns.
  * d_loss (nullable): receives the fp32 mean over the B*T positions of
  * -log softmax(logits)[target]. The loss gradient is formed in the same pass
@@ -240,6 +268,7 @@ int gpt_adamw_step(gpt_model* h, float lr, float beta1, float beta2, float eps,
                    float weight_decay, float clip, float* d_grad_norm);
 
 /* Waits for the stream, then reports a pending sticky error, a device-side
+ * out-of-range id flag (GPT_E_INVAL, GPT_F_DEBUG_CHECKS only), a device-side
  * non-finite flag (GPT_E_NONFINITE) or GPT_OK, and clears them. */
 int gpt_sync(gpt_model* h);
 

@@ -499,20 +499,81 @@ def microbatch(params, tokens, targets, cfg, grad_scale=None, dtype=np.float64,
     return row_loss, grads
 
 
-def accumulate_grads(params, batches, cfg, dtype=np.float64, dropout=None):
+def accumulate_grads(params, batches, cfg, dtype=np.float64, dropout=None, progress=None):
     """Mean loss over A micro-batches and the gradient of that mean.
 
     With a Dropout, micro-batch i takes the Dropout's next forward counter.
+    progress (optional) is called with (i, loss_i) after each micro-batch; it
+    only reports, it takes no part in the arithmetic.
     """
     A = len(batches)
     grads = None
     losses = []
-    for tok, tgt in batches:
+    for i, (tok, tgt) in enumerate(batches):
         B, T = tok.shape
         rl, grads = microbatch(params, tok, tgt, cfg, grad_scale=1.0 / (B * T * A),
                                dtype=dtype, grads=grads, dropout=dropout)
         losses.append(float(rl.mean()))
+        if progress is not None:
+            progress(i, losses[-1])
     return losses, grads
+
+
+def relu_gate_band(params, batches, cfg, rel_round: float = 2.0 ** -7, dtype=np.float64,
+                   dropout=None, call0: int = 0):
+    """How far the gradient of one step can move when the ReLU gates that lie within
+    operand rounding of zero change side (the microGPT block: ReLU in the MLP,
+    "Building microGPT from scratch", model-core section).
+
+    A gate is ambiguous when |u| <= rel_round * sum_k |b_k| |W_jk|, with u = b W^T the
+    pre-activation of MLP column j and b the normed input: rel_round = 2^-7 is the
+    relative rounding of a product of two operands each rounded to bf16 (8
+    significant bits, half an ulp each), so such a u may take either sign once its
+    operands are rounded. Every ambiguous gate is flipped in the backward (the
+    forward output ReLU(u) moves by at most |u|, within rounding, and is left alone)
+    and the step's gradients are formed again. Returns ({tensor: ||G_flip - G|| /
+    ||G||}, with "__all__" for the whole gradient vector, and the fraction of
+    gates that are ambiguous). A rounded computation flips some subset of these
+    gates; their effects add with random signs, so flipping all of them gives the
+    scale of the deviation such flips cause. Uses the oracle's own values only.
+
+    dropout / call0: a Dropout, and the forward counter of the first micro-batch
+    (micro-batch i uses call0 + i), as accumulate_grads would draw them.
+    """
+    if variant_of(cfg) != "microgpt":
+        raise ValueError("only the ReLU block has gates")
+    P = _as(params, dtype)
+    A = len(batches)
+    G0 = {k: np.zeros_like(v) for k, v in P.items()}
+    G1 = {k: np.zeros_like(v) for k, v in P.items()}
+    amb_n = tot_n = 0
+    for i, (tok, tgt) in enumerate(batches):
+        tok, tgt = np.asarray(tok), np.asarray(tgt)
+        B, T = tok.shape
+        drop = (dropout, (call0 + i) & 0xFFFFFFFF) if dropout is not None and dropout.p > 0.0 else None
+        for b in range(B):
+            z, cache = forward_sequence(P, tok[b], cfg, drop, b)
+            _, sm = xent_rows(z, tgt[b])
+            dz = sm
+            dz[np.arange(T), tgt[b]] -= 1.0
+            dz *= 1.0 / (B * T * A)
+            backward_sequence(P, cache, dz, cfg, G0)
+            layers = []
+            for l, lay in enumerate(cache[1]):
+                b2, u = lay[7], lay[9]
+                scale = np.abs(b2) @ np.abs(P[f"h{l}.fc.w"]).T
+                amb = np.abs(u) <= rel_round * scale
+                amb_n += int(amb.sum())
+                tot_n += amb.size
+                # the backward reads u only through the gate (u > 0): give every
+                # ambiguous element the other side
+                uf = np.where(amb, np.where(u > 0.0, -1.0, 1.0), u)
+                layers.append(lay[:9] + (uf,) + lay[10:])
+            backward_sequence(P, (cache[0], layers) + tuple(cache[2:]), dz, cfg, G1)
+    band = {k: float(np.linalg.norm(G1[k] - G0[k]) / max(np.linalg.norm(G0[k]), 1e-300)) for k in P}
+    num = math.sqrt(sum(float(np.sum(np.square(G1[k] - G0[k]))) for k in P))
+    band["__all__"] = num / max(grad_norm(G0), 1e-300)
+    return band, amb_n / max(tot_n, 1)
 
 
 def grad_norm(grads) -> float:
@@ -559,7 +620,7 @@ class Trainer:
         self.decay = {k: decays(k, v.shape) for k, v in self.p.items()}
         self.train = [k for k in self.p if trainable(cfg, k)]
 
-    def step(self, batches, lr=None, beta1=None, beta2=None, eps=None, wd=None, clip=None):
+    def step(self, batches, lr=None, beta1=None, beta2=None, eps=None, wd=None, clip=None, progress=None):
         c = self.cfg
         lr = c.lr if lr is None else lr
         beta1 = c.beta1 if beta1 is None else beta1
@@ -567,7 +628,7 @@ class Trainer:
         eps = c.eps if eps is None else eps
         wd = c.weight_decay if wd is None else wd
         clip = c.grad_clip if clip is None else clip
-        losses, grads = accumulate_grads(self.p, batches, c, self.dtype, self.dropout)
+        losses, grads = accumulate_grads(self.p, batches, c, self.dtype, self.dropout, progress)
         grads = {k: grads[k] for k in self.train}     # frozen tensors take no part
         norm = grad_norm(grads)
         coef = clip_coef(norm, clip)

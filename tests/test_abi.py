@@ -82,7 +82,7 @@ def _raw(**kw):
     (dict(n_head=0), -1),
     (dict(padded_vocab=10), -1),           # below vocab_size
     (dict(precision=7), -1),
-    (dict(flags=4), -1),                   # unknown flag
+    (dict(flags=8), -1),                   # unknown flag
     (dict(dropout=1.0), -1),               # dropout must be in [0, 1)
     (dict(dropout=-0.1), -1),
     (dict(dropout=float("nan")), -1),
@@ -111,6 +111,29 @@ def test_calls_before_bind_are_state_errors():
         assert b"bind" in lib.gpt_last_error(lay.h)
     finally:
         lay.close()
+    lay = Bd.Layout(W.CONFIGS["tiny"], "bf16")
+    try:
+        assert lib.gpt_params_loaded(lay.h) == -3
+        assert lib.gpt_params_loaded(None) == -1
+    finally:
+        lay.close()
+
+
+@pytest.mark.parametrize("name", ["tiny", "char_small", "gpt2_124m"])
+def test_debug_checks_flag_is_accepted_and_changes_no_layout(name):
+    """GPT_F_DEBUG_CHECKS (4) is a valid flag: the id check reuses the optimizer's
+    device state, so sizes and the tensor table are those of the plain model."""
+    c = W.CONFIGS[name]
+    plain = Bd.Layout(c, "bf16")
+    chk = Bd.Layout(c, "bf16", debug_checks=True)
+    try:
+        assert chk.raw.flags & Bd.F_DEBUG_CHECKS
+        for f in ("n_params", "n_flat", "shadow_bytes", "activation_bytes", "workspace_bytes"):
+            assert getattr(chk.sizes, f) == getattr(plain.sizes, f), f
+        assert chk.tensors == plain.tensors
+    finally:
+        chk.close()
+        plain.close()
 
 
 def test_bind_rejects_misaligned_and_null():

@@ -35,3 +35,19 @@ def test_flops_per_token_gpt2_124m_lora():
     d, L, T = cfg.n_embd, cfg.n_layer, cfg.block_size
     assert bench.flops_per_token(cfg) == 4.0 * 123_689_472 + 12.0 * L * d * T + 4.0 * L * d * d
     assert abs(bench.flops_per_token(cfg) / 1e6 - 636.3) < 0.05
+
+
+def test_cpu_baseline_reports_cores_blas_and_a_whole_step():
+    """The oracle's timed sample: float32, a micro-batch plus one AdamW update, the
+    rate extrapolated to the workload's A micro-batches; os.cpu_count(), the BLAS
+    library and its thread count reported apart (a toy size keeps this quick)."""
+    import numpy as np
+    cfg = W.CONFIGS["char_small"].with_(grad_accum=3)
+    drng, wrng = W.rngs()
+    params = W.init_params(cfg, wrng)
+    batches = W.make_step_batches(cfg, drng)
+    out = bench.cpu_baseline(cfg, params, batches, n_seq=cfg.batch)
+    assert out["kind"] == "oracle" and out["unit"] == "tokens/s" and out["value"] > 0
+    assert out["cores"] == os.cpu_count()
+    assert isinstance(out["blas"], str) and out["blas_threads"] >= 0
+    assert "float32" in out["sample"] and "3 micro-batches" in out["sample"]

@@ -150,10 +150,11 @@ def test_lora_widest_rows(prec):
     run_steps("char_small_lora", prec, steps=1, cfg=cfg)
 
 
-def test_lora_on_the_microgpt_block():
+@pytest.mark.parametrize("prec,steps", [("fp32", 3), ("bf16", 1)])
+def test_lora_on_the_microgpt_block(prec, steps):
     # Adapters on the microGPT block's bias-free q and v rows (untied head, RMSNorm,
-    # ReLU), in fp32. In bf16 this combination is not held to a bound: the ReLU gates
-    # that bf16 rounding flips (the variant's own tests bound their effect at 5e-2)
-    # reach 5.3e-2 on the layer-0 adapter gradients, which collect every layer's flips.
+    # ReLU). In bf16 the ReLU gates within rounding of 0 may flip (the layer-0 adapter
+    # gradients collect every layer's flips): run_steps adds the oracle's gate band
+    # (O.relu_gate_band) to each tensor's bound, as for the block without adapters.
     cfg = W.CONFIGS["char_small_micro"].with_(lora_rank=8, lora_alpha=16.0)
-    run_steps("char_small_micro", "fp32", steps=3, cfg=cfg)
+    run_steps("char_small_micro", prec, steps=steps, cfg=cfg)

@@ -618,3 +618,68 @@ def test_lora_first_step_closed_form_and_frozen_base():
         else:
             g = out["grads"][k]
             np.testing.assert_allclose(p1, -c.lr * coef * g / (coef * np.abs(g) + c.eps), rtol=1e-12, atol=1e-15)
+
+
+# --------------------------------------------------------------------------- the ReLU gate band
+
+def _micro_case(B=2):
+    cfg = W.CONFIGS["micro"]
+    drng, wrng = W.rngs()
+    params = W.init_params(cfg, wrng)
+    return cfg, params, [W.make_batch(cfg, drng, B=B)]
+
+
+def test_gate_band_zero_rounding_flips_nothing():
+    cfg, params, batches = _micro_case()
+    band, frac = O.relu_gate_band(params, batches, cfg, rel_round=0.0)
+    assert frac == 0.0 and all(v == 0.0 for v in band.values())
+
+
+def test_gate_band_counts_the_gates_a_loop_finds():
+    """The ambiguous fraction against a plain loop over every pre-activation of the
+    one-layer toy: |u_mj| <= 2^-7 sum_k |b_mk W_jk|."""
+    cfg, params, batches = _micro_case()
+    _, frac = O.relu_gate_band(params, batches, cfg)
+    P = {k: v.astype(np.float64) for k, v in params.items()}
+    W_ = P["h0.fc.w"]
+    amb = tot = 0
+    for tok in batches[0][0]:
+        _, cache = O.forward_sequence(P, tok, cfg)
+        b2, u = cache[1][0][7], cache[1][0][9]
+        for m in range(b2.shape[0]):
+            for j in range(W_.shape[0]):
+                s = sum(abs(b2[m, k] * W_[j, k]) for k in range(b2.shape[1]))
+                amb += abs(u[m, j]) <= 2.0 ** -7 * s
+                tot += 1
+    assert amb > 0 and frac == amb / tot
+
+
+def test_gate_band_all_flipped_is_the_complementary_gate():
+    """With every gate ambiguous the band is the gradient formed with the other side
+    of every gate, which the oracle's backward gives when fed -u."""
+    cfg, params, batches = _micro_case()
+    band, frac = O.relu_gate_band(params, batches, cfg, rel_round=1e30)
+    assert frac == 1.0
+    P = {k: v.astype(np.float64) for k, v in params.items()}
+    tok, tgt = batches[0]
+    B, T = tok.shape
+    G0 = {k: np.zeros_like(v) for k, v in P.items()}
+    G1 = {k: np.zeros_like(v) for k, v in P.items()}
+    for b in range(B):
+        z, cache = O.forward_sequence(P, tok[b], cfg)
+        _, dz = O.xent_rows(z, tgt[b])
+        dz[np.arange(T), tgt[b]] -= 1.0
+        dz /= B * T
+        O.backward_sequence(P, cache, dz, cfg, G0)
+        neg = [lay[:9] + (-lay[9],) + lay[10:] for lay in cache[1]]
+        O.backward_sequence(P, (cache[0], neg) + tuple(cache[2:]), dz, cfg, G1)
+    for k in P:
+        want = np.linalg.norm(G1[k] - G0[k]) / np.linalg.norm(G0[k])
+        assert abs(band[k] - want) <= 1e-12 * max(1.0, want), k
+    assert band["h0.fc.w"] > 0.1     # the flip is visible, not rounding noise
+
+
+def test_gate_band_needs_the_relu_block():
+    cfg = W.CONFIGS["tiny"]
+    with pytest.raises(ValueError):
+        O.relu_gate_band({}, [], cfg)

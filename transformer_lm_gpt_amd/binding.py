@@ -24,7 +24,8 @@ PREC = {"fp32": 0, "bf16": 1}
 
 # Every symbol include/gpt.h declares.
 EXPORTS = ["gpt_create", "gpt_destroy", "gpt_last_error", "gpt_get_sizes", "gpt_num_tensors",
-           "gpt_tensor_info_at", "gpt_bind", "gpt_init_state", "gpt_forward_loss", "gpt_forward_logits",
+           "gpt_tensor_info_at", "gpt_bind", "gpt_init_state", "gpt_params_loaded", "gpt_forward_loss",
+           "gpt_forward_logits",
            "gpt_backward", "gpt_zero_grad", "gpt_set_dropout_seed", "gpt_adamw_step", "gpt_sync", "gpt_get_step",
            "gpt_prefill", "gpt_decode", "gpt_sample",
            "gpt_debug_copy", "gpt_timer_enable", "gpt_timer_disable", "gpt_timer_read"]
@@ -78,6 +79,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         "gpt_tensor_info_at": (C.c_int, [vp, C.c_int, C.POINTER(gpt_tensor_info)]),
         "gpt_bind": (C.c_int, [vp, C.POINTER(gpt_buffers), vp]),
         "gpt_init_state": (C.c_int, [vp]),
+        "gpt_params_loaded": (C.c_int, [vp]),
         "gpt_forward_loss": (C.c_int, [vp, vp, vp, i32, i32, vp]),
         "gpt_forward_logits": (C.c_int, [vp, vp, i32, i32, vp]),
         "gpt_backward": (C.c_int, [vp]),
@@ -104,14 +106,16 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
 
 F_KV_CACHE = 1
 F_MICROGPT = 2
+F_DEBUG_CHECKS = 4
 
 
 def make_config(cfg, precision: str, batch: Optional[int] = None, grad_accum: Optional[int] = None,
-                dropout: float = 0.0, kv_cache: bool = False) -> gpt_config:
+                dropout: float = 0.0, kv_cache: bool = False, debug_checks: bool = False) -> gpt_config:
     return gpt_config(cfg.vocab_size, cfg.padded_vocab, cfg.n_layer, cfg.n_head, cfg.n_embd, cfg.block_size,
                       cfg.batch if batch is None else batch,
                       cfg.grad_accum if grad_accum is None else grad_accum, PREC[precision], float(dropout),
-                      (F_KV_CACHE if kv_cache else 0) | (F_MICROGPT if getattr(cfg, "variant", "gpt2") == "microgpt" else 0),
+                      (F_KV_CACHE if kv_cache else 0) | (F_MICROGPT if getattr(cfg, "variant", "gpt2") == "microgpt" else 0)
+                      | (F_DEBUG_CHECKS if debug_checks else 0),
                       int(getattr(cfg, "lora_rank", 0)), float(getattr(cfg, "lora_alpha", 0.0)))
 
 
@@ -120,11 +124,12 @@ class Layout:
 
     def __init__(self, cfg, precision: str = "bf16", batch: Optional[int] = None,
                  grad_accum: Optional[int] = None, raw: Optional[gpt_config] = None, dropout: float = 0.0,
-                 kv_cache: bool = False):
+                 kv_cache: bool = False, debug_checks: bool = False):
         self.lib = load_library()
         self.cfg = cfg
         self.precision = precision
-        self.raw = raw if raw is not None else make_config(cfg, precision, batch, grad_accum, dropout, kv_cache)
+        self.raw = raw if raw is not None else make_config(cfg, precision, batch, grad_accum, dropout, kv_cache,
+                                                           debug_checks)
         h = C.c_void_p()
         rc = self.lib.gpt_create(C.byref(self.raw), C.byref(h))
         if rc != GPT_OK:
@@ -174,9 +179,10 @@ class GPT(Layout):
 
     def __init__(self, cfg, precision: str = "bf16", batch: Optional[int] = None,
                  grad_accum: Optional[int] = None, device: str = "cuda", dropout: float = 0.0,
-                 kv_cache: bool = False):
+                 kv_cache: bool = False, debug_checks: bool = False):
         import torch
-        super().__init__(cfg, precision, batch, grad_accum, dropout=dropout, kv_cache=kv_cache)
+        super().__init__(cfg, precision, batch, grad_accum, dropout=dropout, kv_cache=kv_cache,
+                         debug_checks=debug_checks)
         self.torch = torch
         self.device = torch.device(device)
         s = self.sizes
@@ -196,10 +202,12 @@ class GPT(Layout):
         self.norm_buf = torch.zeros(1, dtype=torch.float32, device=self.device)
 
     # ---- weights and state
-    def load_params(self, params: Dict[str, np.ndarray]):
+    def load_params(self, params: Dict[str, np.ndarray], reset_state: bool = True):
+        """Copies the weights in; reset_state=False keeps gradients, moments and the
+        step counter (gpt_params_loaded), True starts training afresh (gpt_init_state)."""
         flat = self.torch.from_numpy(self.flatten(params))
         self.buf["params"].view(self.torch.float32)[: flat.numel()].copy_(flat)
-        self._check(self.lib.gpt_init_state(self.h))
+        self._check(self.lib.gpt_init_state(self.h) if reset_state else self.lib.gpt_params_loaded(self.h))
 
     def _flat(self, key: str) -> np.ndarray:
         self.sync()

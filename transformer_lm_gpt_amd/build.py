@@ -1,10 +1,20 @@
 """Builds libgpt.so (the gfx950 kernels and the C ABI) in-tree with hipcc.
 
     python -m transformer_lm_gpt_amd.build [--jobs N]
+    python -m transformer_lm_gpt_amd.build --asan
 
 Every HIP source is compiled for gfx950 only. Packed fp32 instructions are
 disabled for device code (-packed-fp32-ops); hipcc's host pass warns that it
 does not know that feature, which is harmless.
+
+--asan builds a second library, _build/asan/libgpt.so, whose host runtime
+(runtime.cpp: configuration checks, layout planning, the launch sequences and
+the error paths) is compiled with AddressSanitizer for the host only; the
+kernels are the same gfx950 objects. Load it into a process with the sanitizer
+runtime preloaded (asan_env() gives the environment), e.g. for the ABI tests,
+which need no GPU:
+
+    env $(python -m transformer_lm_gpt_amd.build --asan --print-env) python -m pytest tests/test_abi.py
 """
 from __future__ import annotations
 
@@ -49,6 +59,52 @@ def _compile(src: str) -> str:
     return obj
 
 
+ASAN_DIR = os.path.join(BUILD, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libgpt.so")
+# host-only sanitizer flags: each -fsanitize= right after -Xarch_host
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-fno-omit-frame-pointer", "-g"]
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang++")
+    if not os.path.exists(clang):
+        clang = shutil.which("clang++") or clang
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.exists(path):
+        raise RuntimeError("AddressSanitizer runtime not found")
+    return path
+
+
+def asan_env() -> dict:
+    """Environment that loads the sanitized library into an unsanitized Python:
+    the runtime preloaded, leak checks off (the interpreter's own allocations are
+    not ours), the binding pointed at the sanitized build."""
+    return {"LD_PRELOAD": asan_runtime(), "ASAN_OPTIONS": "detect_leaks=0:abort_on_error=1",
+            "GPT_MI355X_LIB": ASAN_LIB}
+
+
+def build_asan(jobs: int = 8, verbose: bool = False) -> str:
+    """The kernels as usual, runtime.cpp with host AddressSanitizer, linked into ASAN_LIB."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(_compile, [x for x in SOURCES if x != "runtime.cpp"]))
+    obj = os.path.join(ASAN_DIR, "runtime.o")
+    cmd = [hipcc(), *COMMON, *ASAN_FLAGS, "-c", os.path.join(CSRC, "runtime.cpp"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-shared-libasan", "-o", ASAN_LIB, *objs, obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {ASAN_LIB}")
+    return ASAN_LIB
+
+
 def build(jobs: int = 8, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
@@ -67,8 +123,16 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=min(8, os.cpu_count() or 1))
+    ap.add_argument("--asan", action="store_true", help="build the host-sanitized runtime into _build/asan")
+    ap.add_argument("--print-env", action="store_true", help="with --asan: only print the environment to load it")
     a = ap.parse_args(argv)
-    build(a.jobs, verbose=True)
+    if a.asan and a.print_env:
+        print(" ".join(f"{k}={v}" for k, v in asan_env().items()))
+        return 0
+    if a.asan:
+        build_asan(a.jobs, verbose=True)
+    else:
+        build(a.jobs, verbose=True)
 
 
 if __name__ == "__main__":

@@ -217,9 +217,14 @@ struct OptState {
   float norm;           // last gradient norm (pre-clip)
   float coef;           // clip coefficient applied
   float bc1, bc2;       // 1 - beta^t for the pending step
-  int32_t skip;         // 1 if the pending step is skipped (non-finite norm)
+  int32_t skip;         // 1 if the pending step is skipped (non-finite norm or bad ids)
   int32_t nonfinite;    // sticky flag read by the host at sync
+  int32_t bad_ids;      // sticky: a checked token or target id was outside [0, vocab_size)
+  int32_t pad;
 };
+// Sets st->bad_ids when any of the n ids lies outside [0, V) (a checking pass in
+// front of the embedding gather; ids are only read).
+hipError_t launch_check_ids(const int32_t* ids, int n, int V, OptState* st, hipStream_t s);
 // Reduces the partials to the norm, decides skip/coef, advances t, sets bias corrections.
 hipError_t launch_opt_prepare(const float* part, OptState* st, float clip, float beta1, float beta2,
                               float* norm_out, hipStream_t s);

@@ -49,6 +49,11 @@ __global__ __launch_bounds__(256) void opt_prepare_kernel(const float* __restric
     const float nf = (float)norm;
     st->norm = nf;
     if (norm_out) *norm_out = nf;
+    if (st->bad_ids) {   // gradients of out-of-range ids: no update (reported at sync)
+      st->skip = 1;
+      st->coef = 0.f;
+      return;
+    }
     if (!isfinite(norm)) {
       st->skip = 1;
       st->nonfinite = 1;
@@ -69,6 +74,19 @@ __global__ __launch_bounds__(256) void opt_prepare_kernel(const float* __restric
 hipError_t launch_opt_prepare(const float* part, OptState* st, float clip, float beta1, float beta2,
                               float* norm_out, hipStream_t s) {
   hipLaunchKernelGGL(opt_prepare_kernel, dim3(1), dim3(256), 0, s, part, st, clip, beta1, beta2, norm_out);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void check_ids_kernel(const int32_t* __restrict__ ids, int n, int V, OptState* st) {
+  bool bad = false;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) bad |= (uint32_t)ids[i] >= (uint32_t)V;
+  if (bad) st->bad_ids = 1;   // the same value from every offending lane
+}
+
+hipError_t launch_check_ids(const int32_t* ids, int n, int V, OptState* st, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int blocks = std::min((n + 255) / 256, 256);
+  hipLaunchKernelGGL(check_ids_kernel, dim3(blocks), dim3(256), 0, s, ids, n, V, st);
   return hipGetLastError();
 }
 

@@ -624,6 +624,13 @@ int copy_ids(gpt_model* h, const int32_t* src, const Slice& dst, int M) {
                    "copy token ids");
 }
 
+// GPT_F_DEBUG_CHECKS: ids of the arena copy checked against [0, vocab_size) before use.
+int check_ids(gpt_model* h, const Slice& ids, int n) {
+  if (!(h->cfg.flags & GPT_F_DEBUG_CHECKS)) return GPT_OK;
+  RUN("check", "check_ids", launch_check_ids(act<int32_t>(h, ids), n, h->V, ws<OptState>(h, h->opt), h->stream));
+  return GPT_OK;
+}
+
 int check_shape(gpt_model* h, int B, int T) {
   if (B < 1 || T < 1) return fail(h, GPT_E_INVAL, "B and T must be >= 1");
   if (B > h->Bmax || T > h->Tmax)
@@ -657,7 +664,8 @@ int gpt_create(const gpt_config* cfg, gpt_model** out) {
   if (c.n_embd % 4 != 0) return fail(nullptr, GPT_E_UNSUPPORTED, "n_embd must be a multiple of 4");
   if (c.precision != GPT_PREC_FP32 && c.precision != GPT_PREC_BF16) return fail(nullptr, GPT_E_INVAL, "unknown precision");
   if (!(c.dropout >= 0.0f && c.dropout < 1.0f)) return fail(nullptr, GPT_E_INVAL, "dropout must be in [0, 1)");
-  if (c.flags & ~(uint32_t)(GPT_F_KV_CACHE | GPT_F_MICROGPT)) return fail(nullptr, GPT_E_INVAL, "unknown flags");
+  if (c.flags & ~(uint32_t)(GPT_F_KV_CACHE | GPT_F_MICROGPT | GPT_F_DEBUG_CHECKS))
+    return fail(nullptr, GPT_E_INVAL, "unknown flags");
   if (c.lora_rank < 0 || c.lora_rank > 64) return fail(nullptr, GPT_E_INVAL, "lora_rank must be in [0, 64]");
   if (c.lora_rank > 0 && !(std::isfinite(c.lora_alpha) && c.lora_alpha != 0.0f))
     return fail(nullptr, GPT_E_INVAL, "lora_alpha must be finite and nonzero");
@@ -748,15 +756,11 @@ int gpt_bind(gpt_model* h, const gpt_buffers* bufs, void* hip_stream) {
   return GPT_OK;
 }
 
-int gpt_init_state(gpt_model* h) {
-  int rc = check_usable(h);
-  if (rc) return rc;
+// Everything derived from the fp32 weights: the bf16 shadow and its transposed half,
+// and with adapters the merged qkv weights.
+static int refresh_derived(gpt_model* h) {
+  int rc;
   hipStream_t s = h->stream;
-  RUN("init", "zero grads", launch_zero(h->buf.grads, h->n_flat, s));
-  RUN("init", "zero m", launch_zero(h->buf.m, h->n_flat, s));
-  RUN("init", "zero v", launch_zero(h->buf.v, h->n_flat, s));
-  RUN("init", "zero optimizer state", launch_zero(ws(h, h->opt), sizeof(OptState) / 4, s));
-  RUN("init", "zero stand-in biases", launch_zero(ws(h, h->zbias), 4 * (size_t)h->d, s));
   if (h->bf16) {
     RUN("init", "bf16 shadow", launch_cast_bf16((const float*)h->buf.params, h->buf.shadow, h->n_flat, s));
     if ((rc = upload_tables(h))) return rc;
@@ -771,7 +775,28 @@ int gpt_init_state(gpt_model* h) {
                          3 * dd * 4, hipMemcpyDeviceToDevice, s));
     if ((rc = lora_merge(h))) return rc;
   }
+  return GPT_OK;
+}
+
+int gpt_init_state(gpt_model* h) {
+  int rc = check_usable(h);
+  if (rc) return rc;
+  hipStream_t s = h->stream;
+  RUN("init", "zero grads", launch_zero(h->buf.grads, h->n_flat, s));
+  RUN("init", "zero m", launch_zero(h->buf.m, h->n_flat, s));
+  RUN("init", "zero v", launch_zero(h->buf.v, h->n_flat, s));
+  RUN("init", "zero optimizer state", launch_zero(ws(h, h->opt), sizeof(OptState) / 4, s));
+  RUN("init", "zero stand-in biases", launch_zero(ws(h, h->zbias), 4 * (size_t)h->d, s));
+  if ((rc = refresh_derived(h))) return rc;
   h->grads_fresh = true;
+  h->fwd_pending = false;
+  return GPT_OK;
+}
+
+int gpt_params_loaded(gpt_model* h) {
+  int rc = check_usable(h);
+  if (rc) return rc;
+  if ((rc = refresh_derived(h))) return rc;
   h->fwd_pending = false;
   return GPT_OK;
 }
@@ -785,6 +810,7 @@ int gpt_forward_loss(gpt_model* h, const int32_t* d_tokens, const int32_t* d_tar
   const int M = B * T;
   if ((rc = copy_ids(h, d_tokens, h->tokens, M))) return rc;
   if ((rc = copy_ids(h, d_targets, h->targets, M))) return rc;
+  if ((rc = check_ids(h, h->tokens, M)) || (rc = check_ids(h, h->targets, M))) return rc;
   h->fwd_pending = false;
   DropArgs da = h->drop;
   da.call = h->drop_call++;                        // advances with or without dropout
@@ -809,6 +835,7 @@ int gpt_prefill(gpt_model* h, const int32_t* d_tokens, int32_t B, int32_t T, flo
   h->fwd_pending = false;
   h->kv_len = 0;
   if ((rc = copy_ids(h, d_tokens, h->tokens, B * T))) return rc;
+  if ((rc = check_ids(h, h->tokens, B * T))) return rc;
   const DropArgs none{};
   if ((rc = forward_to_logits(h, B, T, none))) return rc;
   // the last position of every sequence: rows b*T + T-1 of the logits
@@ -834,6 +861,7 @@ int gpt_decode(gpt_model* h, const int32_t* d_tokens, float* d_logits) {
   hipStream_t s = h->stream;
   h->fwd_pending = false;
   if ((rc = copy_ids(h, d_tokens, h->tokens, B))) return rc;
+  if ((rc = check_ids(h, h->tokens, B))) return rc;
   // B single-token rows through the layer-0 activation slots
   const LayerAct& a = h->layers[0];
   float* x = act<float>(h, a.x);
@@ -910,6 +938,7 @@ int gpt_forward_logits(gpt_model* h, const int32_t* d_tokens, int32_t B, int32_t
   const int M = B * T;
   h->fwd_pending = false;
   if ((rc = copy_ids(h, d_tokens, h->tokens, M))) return rc;
+  if ((rc = check_ids(h, h->tokens, M))) return rc;
   const DropArgs none{};                           // inference: no dropout
   if ((rc = forward_to_logits(h, B, T, none))) return rc;
   RUN("copy", "logits_to_f32",
@@ -1009,15 +1038,16 @@ int gpt_backward(gpt_model* h) {
           launch_attn_bwd(act(h, la.qkv), act(h, la.att), dO, act<float>(h, la.lse), ws<float>(h, h->attnD), dqkv, bf,
                           B, T, h->H, h->hd, qkv_rows ? red_part(h, p + "attn.b") : nullptr, da,
                           site_attn_prob(l), s));
+      if (!bf && (rc = wgrad_now(dqkv, 3 * d, act(h, la.ln1), d, p + "attn.w", 3 * d, d, "qkv_wgrad"))) return rc;
+      if (!h->micro && !lora && !qkv_rows && (rc = colsum(h, dqkv, bf, 3 * d, M, 3 * d, p + "attn.b"))) return rc;
+      // d x_0 feeds only the embedding backward, which reads the fp32 copy; with
+      // adapters the embeddings are frozen, so layer 0's input gradient (this GEMM
+      // and the LayerNorm backward) has no reader
+      if (lora && l == 0) continue;
       GemmDesc g2 = bf ? gemm_desc(dqkv, 3 * d, true, WopT(h, p + "attn.w"), 3 * d, true, dln, d, M, d, 3 * d, EPI_F32)
                        : gemm_desc(dqkv, 3 * d, true, Wop(h, p + "attn.w"), d, false, dln, d, M, d, 3 * d, EPI_F32);
       RUN("gemm_dgrad", "qkv_dgrad", gemm(h, g2, bf));
-      if (!bf && (rc = wgrad_now(dqkv, 3 * d, act(h, la.ln1), d, p + "attn.w", 3 * d, d, "qkv_wgrad"))) return rc;
-      if (!h->micro && !lora && !qkv_rows && (rc = colsum(h, dqkv, bf, 3 * d, M, 3 * d, p + "attn.b"))) return rc;
       const std::string proj_b = p + "proj.b";
-      // d x_0 feeds only the embedding backward, which reads the fp32 copy; with
-      // adapters the embeddings are frozen and nothing reads it
-      if (lora && l == 0) continue;
       void* xop = l == 0 ? nullptr : (bf ? rx_slot(h, l) : (void*)dxm);
       if ((rc = ln_bwd(h, dln, act<float>(h, la.x), act<float>(h, la.ln1_mean), act<float>(h, la.ln1_rstd),
                        p + "ln1.g", p + "ln1.b", dres, proj_b.c_str(), xop, M, (int)site_attn_out(l),
@@ -1085,16 +1115,12 @@ int gpt_zero_grad(gpt_model* h) {
   return GPT_OK;
 }
 
-int gpt_adamw_step(gpt_model* h, float lr, float beta1, float beta2, float eps, float weight_decay, float clip,
-                   float* d_grad_norm) {
-  int rc = check_usable(h);
-  if (rc) return rc;
-  if (!(beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f && eps >= 0.f && std::isfinite(lr) &&
-        std::isfinite(weight_decay) && std::isfinite(clip)))
-    return fail(h, GPT_E_INVAL, "invalid AdamW hyper-parameters");
-  if (h->grads_fresh) return fail(h, GPT_E_STATE, "gpt_adamw_step needs at least one gpt_backward since the last step");
+// The update of gpt_adamw_step with the gradient norm's partial sums in `part`
+// (NORM_BLOCKS floats of the bound workspace).
+static int adamw_step(gpt_model* h, float lr, float beta1, float beta2, float eps, float weight_decay, float clip,
+                      float* d_grad_norm, float* part) {
   hipStream_t s = h->stream;
-  float* part = ws<float>(h, h->norm_part);
+  int rc;
   OptState* st = ws<OptState>(h, h->opt);
   // With adapters the norm, the clip and the update cover the adapters alone (the
   // last, contiguous run of the flat arrays, all 2-D and decayed); the merged qkv
@@ -1114,6 +1140,24 @@ int gpt_adamw_step(gpt_model* h, float lr, float beta1, float beta2, float eps, 
   return GPT_OK;
 }
 
+static int adamw_check(gpt_model* h, float lr, float beta1, float beta2, float eps, float weight_decay, float clip) {
+  int rc = check_usable(h);
+  if (rc) return rc;
+  if (!(beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f && eps >= 0.f && std::isfinite(lr) &&
+        std::isfinite(weight_decay) && std::isfinite(clip)))
+    return fail(h, GPT_E_INVAL, "invalid AdamW hyper-parameters");
+  if (h->grads_fresh) return fail(h, GPT_E_STATE, "gpt_adamw_step needs at least one gpt_backward since the last step");
+  return GPT_OK;
+}
+
+int gpt_adamw_step(gpt_model* h, float lr, float beta1, float beta2, float eps, float weight_decay, float clip,
+                   float* d_grad_norm) {
+  int rc = adamw_check(h, lr, beta1, beta2, eps, weight_decay, clip);
+  if (rc) return rc;
+  return adamw_step(h, lr, beta1, beta2, eps, weight_decay, clip, d_grad_norm, ws<float>(h, h->norm_part));
+}
+
+
 int gpt_sync(gpt_model* h) {
   if (!h) return GPT_E_INVAL;
   hipError_t e = hipStreamSynchronize(h->stream);
@@ -1125,6 +1169,14 @@ int gpt_sync(gpt_model* h) {
     OptState st;
     e = hipMemcpy(&st, ws(h, h->opt), sizeof(st), hipMemcpyDeviceToHost);
     if (e != hipSuccess) return fail(h, GPT_E_HIP, std::string("read optimizer state: ") + hipGetErrorString(e));
+    if (st.bad_ids) {
+      const int32_t zero2[2] = {0, 0};   // bad_ids and nonfinite: the ids explain a NaN loss
+      static_assert(offsetof(OptState, bad_ids) == offsetof(OptState, nonfinite) + 4, "flag order");
+      e = hipMemcpy((char*)ws(h, h->opt) + offsetof(OptState, nonfinite), zero2, 8, hipMemcpyHostToDevice);
+      if (e != hipSuccess) return fail(h, GPT_E_HIP, std::string("clear id flag: ") + hipGetErrorString(e));
+      h->err = "a token or target id lies outside [0, vocab_size): the AdamW update was skipped";
+      return GPT_E_INVAL;
+    }
     if (st.nonfinite) {
       int32_t zero = 0;
       e = hipMemcpy((char*)ws(h, h->opt) + offsetof(OptState, nonfinite), &zero, 4, hipMemcpyHostToDevice);
