@@ -267,6 +267,21 @@ int gpt_zero_grad(gpt_model* h);
 int gpt_adamw_step(gpt_model* h, float lr, float beta1, float beta2, float eps,
                    float weight_decay, float clip, float* d_grad_norm);
 
+/* gpt_adamw_step for callers that cannot allocate device memory or hand over
+ * scratch (code under HIP graph capture, tight serving or training loops,
+ * harnesses that forbid hipMalloc): the same update, the same kernels and a
+ * bitwise identical result, but the gradient norm's per-block partial sums live
+ * in a file-scope device array of the library (4 KB per GPU, kept until the
+ * process ends) instead of the bound workspace. The partials do not grow with
+ * the model: every size gpt_create accepts fits; a build whose partial count
+ * exceeded the array would return GPT_E_UNSUPPORTED. The array is looked up once
+ * per device on the first call there. Calls nothing that allocates. Every call on
+ * one GPU shares that GPU's array, which keeps the last call's partials (each
+ * call overwrites all of them before reading): calls that overlap on one GPU
+ * (several streams or threads) race and must be serialized by the caller. */
+int gpt_adamw_step_noalloc(gpt_model* h, float lr, float beta1, float beta2, float eps,
+                           float weight_decay, float clip, float* d_grad_norm);
+
 /* Waits for the stream, then reports a pending sticky error, a device-side
  * out-of-range id flag (GPT_E_INVAL, GPT_F_DEBUG_CHECKS only), a device-side
  * non-finite flag (GPT_E_NONFINITE) or GPT_OK, and clears them. */

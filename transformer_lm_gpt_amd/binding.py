@@ -27,7 +27,7 @@ EXPORTS = ["gpt_create", "gpt_destroy", "gpt_last_error", "gpt_get_sizes", "gpt_
            "gpt_tensor_info_at", "gpt_bind", "gpt_init_state", "gpt_params_loaded", "gpt_forward_loss",
            "gpt_forward_logits",
            "gpt_backward", "gpt_zero_grad", "gpt_set_dropout_seed", "gpt_adamw_step", "gpt_sync", "gpt_get_step",
-           "gpt_prefill", "gpt_decode", "gpt_sample",
+           "gpt_prefill", "gpt_decode", "gpt_sample", "gpt_adamw_step_noalloc",
            "gpt_debug_copy", "gpt_timer_enable", "gpt_timer_disable", "gpt_timer_read"]
 
 
@@ -89,6 +89,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         "gpt_decode": (C.c_int, [vp, vp, vp]),
         "gpt_sample": (C.c_int, [vp, vp, i32, f32, i32, vp, vp]),
         "gpt_adamw_step": (C.c_int, [vp, f32, f32, f32, f32, f32, f32, vp]),
+        "gpt_adamw_step_noalloc": (C.c_int, [vp, f32, f32, f32, f32, f32, f32, vp]),
         "gpt_sync": (C.c_int, [vp]),
         "gpt_get_step": (C.c_int, [vp, C.POINTER(C.c_int64)]),
         "gpt_debug_copy": (C.c_int, [vp, C.c_char_p, i32, vp, C.c_size_t]),
@@ -298,10 +299,12 @@ class GPT(Layout):
     def zero_grad(self):
         self._check(self.lib.gpt_zero_grad(self.h))
 
-    def adamw_step(self, lr, beta1, beta2, eps, weight_decay, clip, norm_out=None):
+    def adamw_step(self, lr, beta1, beta2, eps, weight_decay, clip, norm_out=None, noalloc=False):
+        """noalloc=True: gpt_adamw_step_noalloc (the norm's partials in the library's
+        static device array instead of the workspace)."""
         out = self.norm_buf if norm_out is None else norm_out
-        self._check(self.lib.gpt_adamw_step(self.h, lr, beta1, beta2, eps, weight_decay, clip,
-                                            C.c_void_p(out.data_ptr())))
+        f = self.lib.gpt_adamw_step_noalloc if noalloc else self.lib.gpt_adamw_step
+        self._check(f(self.h, lr, beta1, beta2, eps, weight_decay, clip, C.c_void_p(out.data_ptr())))
         return out
 
     def sync(self):

@@ -210,6 +210,11 @@ hipError_t launch_sample(const float* logits, int64_t ld, int B, int V, float te
 // Sum of squares of n floats into per-block partials [NORM_BLOCKS].
 constexpr int NORM_BLOCKS = 1024;
 hipError_t launch_sumsq_partial(const float* g, size_t n, float* part, hipStream_t s);
+// Floats of the static device array behind gpt_adamw_step_noalloc (4 KB per GPU).
+constexpr size_t NOALLOC_SCRATCH_FLOATS = 1024;
+// Device address of that array on `device` (looked up once per device, with the
+// device made current for the lookup).
+hipError_t noalloc_norm_scratch(int device, float** out);
 
 // Device state used by the optimizer (lives in the workspace).
 struct OptState {

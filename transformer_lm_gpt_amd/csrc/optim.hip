@@ -7,10 +7,42 @@
 // double precision), so it is bitwise reproducible. The step counter, the clip
 // coefficient and the bias corrections stay on the device; a non-finite norm
 // skips the update without a host round trip.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace gpt {
+
+// The gradient norm's per-block partial sums for gpt_adamw_step_noalloc, which takes
+// no workspace for them: one file-scope array per GPU, alive until the process ends.
+// Host code never passes `scratch` itself (in host code the name is a stand-in, not
+// the device address): noalloc_norm_scratch() looks up each device's address once,
+// with that device current, and hands that out.
+static __device__ __align__(256) float scratch[NOALLOC_SCRATCH_FLOATS];
+
+hipError_t noalloc_norm_scratch(int device, float** out) {
+  constexpr int MAX_DEVICES = 64;
+  static std::mutex mu;
+  static float* ptr[MAX_DEVICES] = {};
+  if (device < 0 || device >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[device]) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t e2 = cur != device ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (e2 != hipSuccess) return e2;
+    if (!p) return hipErrorInvalidSymbol;
+    ptr[device] = (float*)p;
+  }
+  *out = ptr[device];
+  return hipSuccess;
+}
 
 __global__ __launch_bounds__(256) void sumsq_partial_kernel(const float* __restrict__ g, size_t n4,
                                                             float* __restrict__ part) {

@@ -1116,7 +1116,8 @@ int gpt_zero_grad(gpt_model* h) {
 }
 
 // The update of gpt_adamw_step with the gradient norm's partial sums in `part`
-// (NORM_BLOCKS floats of the bound workspace).
+// (NORM_BLOCKS floats): the bound workspace, or the static array of the
+// no-allocation variant.
 static int adamw_step(gpt_model* h, float lr, float beta1, float beta2, float eps, float weight_decay, float clip,
                       float* d_grad_norm, float* part) {
   hipStream_t s = h->stream;
@@ -1157,6 +1158,23 @@ int gpt_adamw_step(gpt_model* h, float lr, float beta1, float beta2, float eps, 
   return adamw_step(h, lr, beta1, beta2, eps, weight_decay, clip, d_grad_norm, ws<float>(h, h->norm_part));
 }
 
+int gpt_adamw_step_noalloc(gpt_model* h, float lr, float beta1, float beta2, float eps, float weight_decay,
+                           float clip, float* d_grad_norm) {
+  int rc = adamw_check(h, lr, beta1, beta2, eps, weight_decay, clip);
+  if (rc) return rc;
+  static_assert(NORM_BLOCKS <= NOALLOC_SCRATCH_FLOATS, "the norm's partials fit the static scratch");
+  const size_t need = NORM_BLOCKS;   // partial sums of the norm, whatever the model's size
+  if (need > NOALLOC_SCRATCH_FLOATS)
+    return fail(h, GPT_E_UNSUPPORTED, "gradient-norm partials (" + std::to_string(need) +
+                                          " floats) exceed the static scratch (" +
+                                          std::to_string(NOALLOC_SCRATCH_FLOATS) + " floats)");
+  hipDevice_t dev = 0;
+  hipError_t e = hipStreamGetDevice(h->stream, &dev);
+  if (e != hipSuccess) return hip_check(h, e, "hipStreamGetDevice");
+  float* part = nullptr;
+  if ((e = noalloc_norm_scratch((int)dev, &part)) != hipSuccess) return hip_check(h, e, "static scratch address");
+  return adamw_step(h, lr, beta1, beta2, eps, weight_decay, clip, d_grad_norm, part);
+}
 
 int gpt_sync(gpt_model* h) {
   if (!h) return GPT_E_INVAL;
