@@ -12,6 +12,9 @@
 // LDS tiles are stored as [BK/KG][rows + pad][KG], so that one MFMA operand
 // fragment (KG contraction-consecutive values of one row) is one LDS read.
 // Operands that arrive m-contiguous are transposed in registers on the way in.
+#include <cstdlib>
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -490,9 +493,22 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ inline int mc_swz(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
 
+// The loaders below fill LDS with buffer loads (MUBUF LDS DMA) over a resource whose
+// base is the tile's first row (k-contiguous) or column (m-contiguous), so every
+// per-lane byte offset fits 32 bits. The buffer form matters to the compiler: with a
+// FLAT-encoded LDS DMA (global_load_lds) in a loop, its wait-count pass must assume
+// LDS accesses complete out of order and waits for every LDS read in flight before
+// each use, where the buffer form keeps the counts exact and lets fragment reads
+// overlap the MFMAs.
+__device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const bf16* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+
+// rmax: rows of the operand from the tile's first row on (>= 1); rows past it are
+// clamped to the last one (their products are masked at the store).
 template <int ROWS, int NW>
-__device__ inline void dma_kc(const bf16* __restrict__ src, int64_t ld, int row0, int nrows, int k0, char* lds,
-                              int wave, int lane) {
+__device__ inline void dma_kc(__amdgpu_buffer_rsrc_t src, int64_t ld, int rmax, int k0, char* lds, int wave,
+                              int lane) {
   constexpr int CHUNKS = ROWS * 32 * 2 / 1024;   // 1 KB per wavefront instruction
   static_assert(ROWS % 16 == 0 && CHUNKS % NW == 0, "k-contiguous tile shape");
 #pragma unroll
@@ -500,15 +516,17 @@ __device__ inline void dma_kc(const bf16* __restrict__ src, int64_t ld, int row0
     const int ch = wave + NW * i;
     const int r = ch * 16 + (lane >> 2);
     const int u = (lane & 3) ^ ((r >> 1) & 3);
-    const int gr = min(row0 + r, nrows - 1);
-    const bf16* g = src + (int64_t)gr * ld + k0 + 8 * u;
-    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(lds + ch * 1024), 16, 0, 0);
+    const int gr = min(r, rmax - 1);
+    const uint32_t off = (uint32_t)(((int64_t)gr * ld + k0 + 8 * u) * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)(lds + ch * 1024), 16, off, 0, 0, 0);
   }
 }
 
+// m-contiguous: the resource starts at the tile's first column; mmax = columns from
+// it on (a multiple of 8, >= 8), the last 8-column unit standing in for those past it.
 template <int ROWS, int NW>
-__device__ inline void dma_mc(const bf16* __restrict__ src, int64_t ld, int row0, int nrows, int k0, char* lds,
-                              int wave, int lane) {
+__device__ inline void dma_mc(__amdgpu_buffer_rsrc_t src, int64_t ld, int mmax, int k0, char* lds, int wave,
+                              int lane) {
   constexpr int UPR = ROWS / 8;                  // 16-byte units per k-row
   constexpr int RPC = 64 / UPR;                  // k-rows per 1 KB chunk
   constexpr int CHUNKS = 32 / RPC;
@@ -518,9 +536,9 @@ __device__ inline void dma_mc(const bf16* __restrict__ src, int64_t ld, int row0
     const int ch = wave + NW * i;
     const int k = ch * RPC + lane / UPR;
     const int mu = (lane % UPR) ^ mc_swz(k);
-    const int gm = min(row0 + 8 * mu, nrows - 8);
-    const bf16* g = src + (int64_t)(k0 + k) * ld + gm;
-    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(lds + ch * 1024), 16, 0, 0);
+    const int gm = min(8 * mu, mmax - 8);
+    const uint32_t off = (uint32_t)(((int64_t)(k0 + k) * ld + gm) * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)(lds + ch * 1024), 16, off, 0, 0, 0);
   }
 }
 
@@ -528,8 +546,8 @@ __device__ inline void dma_mc(const bf16* __restrict__ src, int64_t ld, int row0
 // row r at r*8 + (u ^ ((r >> 1) & 7)); a 1 KB wavefront instruction covers 8 rows, one
 // whole 128-byte line per row (half the requests per byte of the 32-wide slices).
 template <int ROWS, int NW>
-__device__ inline void dma_kc64(const bf16* __restrict__ src, int64_t ld, int row0, int nrows, int k0, char* lds,
-                                int wave, int lane) {
+__device__ inline void dma_kc64(__amdgpu_buffer_rsrc_t src, int64_t ld, int rmax, int k0, char* lds, int wave,
+                                int lane) {
   constexpr int CHUNKS = ROWS * 64 * 2 / 1024;
   static_assert(ROWS % 16 == 0 && CHUNKS % NW == 0, "k-contiguous tile shape");
 #pragma unroll
@@ -537,9 +555,9 @@ __device__ inline void dma_kc64(const bf16* __restrict__ src, int64_t ld, int ro
     const int ch = wave + NW * i;
     const int r = ch * 8 + (lane >> 3);
     const int u = (lane & 7) ^ ((r >> 1) & 7);
-    const int gr = min(row0 + r, nrows - 1);
-    const bf16* g = src + (int64_t)gr * ld + k0 + 8 * u;
-    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(lds + ch * 1024), 16, 0, 0);
+    const int gr = min(r, rmax - 1);
+    const uint32_t off = (uint32_t)(((int64_t)gr * ld + k0 + 8 * u) * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)(lds + ch * 1024), 16, off, 0, 0, 0);
   }
 }
 // fragment of the h-th 32-wide half of a 64-wide slice
@@ -583,87 +601,18 @@ __device__ inline void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int
   tn = (t % group) / gsz;
 }
 
-// One output tile over k-slices [s0, s1) of 32. With park == nullptr the fused
-// epilogue is applied; otherwise the raw fp32 sums go to park (BM_ x BN_, row-major).
-// Ends with a barrier, so the LDS may be reused by the caller.
-// KS: k per slice, 32, or 64 when both operands are k-contiguous (s0, s1 count
-// slices of KS).
-template <int BM_, int BN_, int WM_, int WN_, int STAGES, bool AK, bool BK_, int EPI, int KS = 32>
-__device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, int tn, int s0, int s1,
-                                         float* park) {
-  static_assert(KS == 32 || (KS == 64 && AK && BK_), "64-wide slices need k-contiguous operands");
+// Epilogue of one BM_ x BN_ tile whose wavefronts (WM_ x WN_ of them, TM x TN each)
+// hold their sums in acc: the fused epilogue, or the raw fp32 sums parked in `park`
+// (BM_ x BN_, row-major) when it is given. Ends with a barrier, so the LDS may be
+// reused by the caller. PF_OK: the epilogue's global inputs may be loaded one
+// 16-row block ahead (registers allow it).
+template <int BN_, int WM_, int WN_, int TM, int TN, int EPI, bool PF_OK>
+__device__ __forceinline__ void tile_epilogue(const GemmArgs& p, char* smem, int tm, int m0, int n0,
+                                              f32x4 (&acc)[TM / 16][TN / 16], float* park) {
   constexpr int NW = WM_ * WN_;
-  constexpr int TM = BM_ / WM_, TN = BN_ / WN_;
   constexpr int FM = TM / 16, FN = TN / 16;
-  constexpr int AB = BM_ * KS * 2, BB = BN_ * KS * 2, SB = AB + BB;
-  constexpr int LPS = (AB + BB) / 1024 / NW;     // load instructions per stage per wave
-  const int m0 = tm * BM_, n0 = tn * BN_;
-  const bf16* A = (const bf16*)p.A;
-  const bf16* B = (const bf16*)p.B;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN_, wn = wave % WN_;
-
-  f32x4 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; i++)
-#pragma unroll
-    for (int j = 0; j < FN; j++) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-  const int nk = s1 - s0;
-  auto issue = [&](int t) {
-    char* st = smem + (t % STAGES) * SB;
-    const int k0 = (s0 + t) * KS;
-    if constexpr (KS == 64) {
-      dma_kc64<BM_, NW>(A, p.lda, m0, p.M, k0, st, wave, lane);
-      dma_kc64<BN_, NW>(B, p.ldb, n0, p.N, k0, st + AB, wave, lane);
-    } else {
-      if constexpr (AK) dma_kc<BM_, NW>(A, p.lda, m0, p.M, k0, st, wave, lane);
-      else dma_mc<BM_, NW>(A, p.lda, m0, p.M, k0, st, wave, lane);
-      if constexpr (BK_) dma_kc<BN_, NW>(B, p.ldb, n0, p.N, k0, st + AB, wave, lane);
-      else dma_mc<BN_, NW>(B, p.ldb, n0, p.N, k0, st + AB, wave, lane);
-    }
-  };
-
-#pragma unroll
-  for (int t = 0; t < STAGES - 1; t++)
-    if (t < nk) issue(t);
-
-  for (int t = 0; t < nk; t++) {
-    // A plain s_barrier: __syncthreads() would also wait for every global->LDS
-    // load still in flight, which would serialise the pipeline. LDS reads of the
-    // previous slice are complete (their MFMAs consumed them) before the barrier.
-    if (t + STAGES - 2 < nk) {
-      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((STAGES - 2) * LPS) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    }
-    if (t + STAGES - 1 < nk) issue(t + STAGES - 1);
-    const char* As = smem + (t % STAGES) * SB;
-    const char* Bs = As + AB;
-#pragma unroll
-    for (int h = 0; h < KS / 32; h++) {
-      bf16x8 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; i++) {
-        const int r = wm * TM + i * 16;
-        if constexpr (KS == 64) af[i] = frag_kc64(As, r + (lane & 15), h);
-        else if constexpr (AK) af[i] = frag_kc<BM_>(As, r + (lane & 15));
-        else af[i] = frag_mc<BM_>(As, r);
-      }
-#pragma unroll
-      for (int j = 0; j < FN; j++) {
-        const int r = wn * TN + j * 16;
-        if constexpr (KS == 64) bfr[j] = frag_kc64(Bs, r + (lane & 15), h);
-        else if constexpr (BK_) bfr[j] = frag_kc<BN_>(Bs, r + (lane & 15));
-        else bfr[j] = frag_mc<BN_>(Bs, r);
-      }
-#pragma unroll
-      for (int i = 0; i < FM; i++)
-#pragma unroll
-        for (int j = 0; j < FN; j++) acc[i][j] = Mfma<bf16>::mma(af[i], bfr[j], acc[i][j]);
-    }
-  }
-
   // Epilogue through LDS: each wave parks one 16-row block of its TM x TN
   // quadrant, then a lane handles 16 contiguous columns of one row (TN/16 such
   // groups per row, so 64 lanes cover the block in one or more passes), so bias,
@@ -673,7 +622,7 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, 
   // epilogue inputs of 16-row block i (item it = lane + 64*ps: row er, columns ec..)
   // (the fp32 residual of two blocks does not fit beside the accumulators of two
   // workgroups per CU: the 32-wide-slice residual kernel loads it in place)
-  constexpr bool PF = EpiPre<EPI>::ON && !(epi_resid<EPI>() && KS == 32);
+  constexpr bool PF = EpiPre<EPI>::ON && PF_OK;
   EpiPre<EPI> pre[PF ? 2 : 1][PASSES];
   auto prefetch = [&](int i, EpiPre<EPI> (&dst)[PASSES]) {
 #pragma unroll
@@ -776,6 +725,95 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, 
   }
   __syncthreads();
 }
+
+// One output tile over k-slices [s0, s1) of 32. With park == nullptr the fused
+// epilogue is applied; otherwise the raw fp32 sums go to park (BM_ x BN_, row-major).
+// Ends with a barrier, so the LDS may be reused by the caller.
+// KS: k per slice, 32, or 64 when both operands are k-contiguous (s0, s1 count
+// slices of KS).
+template <int BM_, int BN_, int WM_, int WN_, int STAGES, bool AK, bool BK_, int EPI, int KS = 32>
+__device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, int tn, int s0, int s1,
+                                         float* park) {
+  static_assert(KS == 32 || (KS == 64 && AK && BK_), "64-wide slices need k-contiguous operands");
+  constexpr int NW = WM_ * WN_;
+  constexpr int TM = BM_ / WM_, TN = BN_ / WN_;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr int AB = BM_ * KS * 2, BB = BN_ * KS * 2, SB = AB + BB;
+  constexpr int LPS = (AB + BB) / 1024 / NW;     // load instructions per stage per wave
+  const int m0 = tm * BM_, n0 = tn * BN_;
+  const bf16* A = (const bf16*)p.A;
+  const bf16* B = (const bf16*)p.B;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN_, wn = wave % WN_;
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; i++)
+#pragma unroll
+    for (int j = 0; j < FN; j++) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int nk = s1 - s0;
+  // resources from the tile's first row (k-contiguous) or column (m-contiguous)
+  const __amdgpu_buffer_rsrc_t ra = tile_rsrc(AK ? A + (int64_t)m0 * p.lda : A + m0);
+  const __amdgpu_buffer_rsrc_t rb = tile_rsrc(BK_ ? B + (int64_t)n0 * p.ldb : B + n0);
+  const int am = p.M - m0, bn = p.N - n0;
+  auto issue = [&](int t) {
+    char* st = smem + (t % STAGES) * SB;
+    const int k0 = (s0 + t) * KS;
+    if constexpr (KS == 64) {
+      dma_kc64<BM_, NW>(ra, p.lda, am, k0, st, wave, lane);
+      dma_kc64<BN_, NW>(rb, p.ldb, bn, k0, st + AB, wave, lane);
+    } else {
+      if constexpr (AK) dma_kc<BM_, NW>(ra, p.lda, am, k0, st, wave, lane);
+      else dma_mc<BM_, NW>(ra, p.lda, am, k0, st, wave, lane);
+      if constexpr (BK_) dma_kc<BN_, NW>(rb, p.ldb, bn, k0, st + AB, wave, lane);
+      else dma_mc<BN_, NW>(rb, p.ldb, bn, k0, st + AB, wave, lane);
+    }
+  };
+
+#pragma unroll
+  for (int t = 0; t < STAGES - 1; t++)
+    if (t < nk) issue(t);
+
+  for (int t = 0; t < nk; t++) {
+    // A plain s_barrier: __syncthreads() would also wait for every global->LDS
+    // load still in flight, which would serialise the pipeline. LDS reads of the
+    // previous slice are complete (their MFMAs consumed them) before the barrier.
+    if (t + STAGES - 2 < nk) {
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((STAGES - 2) * LPS) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    if (t + STAGES - 1 < nk) issue(t + STAGES - 1);
+    const char* As = smem + (t % STAGES) * SB;
+    const char* Bs = As + AB;
+#pragma unroll
+    for (int h = 0; h < KS / 32; h++) {
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; i++) {
+        const int r = wm * TM + i * 16;
+        if constexpr (KS == 64) af[i] = frag_kc64(As, r + (lane & 15), h);
+        else if constexpr (AK) af[i] = frag_kc<BM_>(As, r + (lane & 15));
+        else af[i] = frag_mc<BM_>(As, r);
+      }
+#pragma unroll
+      for (int j = 0; j < FN; j++) {
+        const int r = wn * TN + j * 16;
+        if constexpr (KS == 64) bfr[j] = frag_kc64(Bs, r + (lane & 15), h);
+        else if constexpr (BK_) bfr[j] = frag_kc<BN_>(Bs, r + (lane & 15));
+        else bfr[j] = frag_mc<BN_>(Bs, r);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++) acc[i][j] = Mfma<bf16>::mma(af[i], bfr[j], acc[i][j]);
+    }
+  }
+
+  tile_epilogue<BN_, WM_, WN_, TM, TN, EPI, !(epi_resid<EPI>() && KS == 32)>(p, smem, tm, m0, n0, acc, park);
+}
+
 
 // The 192-wide, 32-wide-slice kernels run two workgroups per CU (their LDS ring allows
 // it); the register budget is held to that occupancy so the epilogue's prefetched
@@ -1083,6 +1121,170 @@ __global__ __launch_bounds__(256) void group_fixup_kernel(const WgradProblem* __
   epi_store16<EPI_ACC>(p, row, col0, v, p.c_vec && col0 + 16 <= p.N, unused);
 }
 
+// ----------------------------------------------------------------------------- wide tiles
+// 256 x 256 tile on four wavefronts of 128 x 128 (64 accumulators of 16 x 16 each,
+// held in the accumulation registers: one wavefront per SIMD). Per 32-wide k-slice a
+// wavefront reads 16 KB of fragments for 64 MFMAs, half the LDS traffic per MFMA of
+// 64 x 64 wavefront tiles. With a single wavefront per SIMD the LDS latency is
+// hidden inside the wavefront, with few registers: a slice runs row block by row
+// block (8 MFMAs on one A fragment each); the A fragment of row block i+2 is read
+// during row block i into a ring of four (crossing into the next slice at the end),
+// and the next slice's B fragments are read into a second set, one per row block.
+// One barrier per slice publishes the next slice's stage and frees the stage the
+// next load overwrites; loads run STAGES - 2 slices ahead of the slice being read.
+// One 16 x 16 x 32 bf16 MFMA accumulating into acc, which the constraint keeps in
+// the accumulation registers for the whole k-loop (the compiler otherwise moves
+// 256 accumulators between register files around the loop's blocks). Volatile: the
+// MFMAs keep the order written; LDS reads are still scheduled between them.
+__device__ __forceinline__ void mfma_agpr(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// After the last mfma_agpr of a tile and before its accumulators are read: the
+// compiler cannot see the MFMA inside the asm, so the wait states between an MFMA
+// writing a register and a plain read of it are spent here (24 > the 18 an 8-pass
+// MFMA needs), and each accumulator is passed through an empty asm after them, so
+// no read of it can be scheduled before the wait.
+__device__ __forceinline__ void mfma_agpr_drain(f32x4 (&acc)[8][8]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 8; i++)
+#pragma unroll
+    for (int j = 0; j < 8; j++) asm volatile("" : "+a"(acc[i][j]));
+}
+
+template <bool AK, bool BK_, int STAGES>
+__device__ __forceinline__ void wide_mainloop(const GemmArgs& p, char* smem, int m0, int n0, int s0, int s1,
+                                              f32x4 (&acc)[8][8]) {
+  constexpr int BM_ = 256, BN_ = 256, NW = 4, KS = 32;
+  constexpr int AB = BM_ * KS * 2, SB = 2 * AB;
+  constexpr int LPS = SB / 1024 / NW;              // load instructions per stage per wavefront
+  static_assert(STAGES >= 3, "a stage is read while one is loaded and one is being freed");
+  const bf16* A = (const bf16*)p.A;
+  const bf16* B = (const bf16*)p.B;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const __amdgpu_buffer_rsrc_t ra = tile_rsrc(AK ? A + (int64_t)m0 * p.lda : A + m0);
+  const __amdgpu_buffer_rsrc_t rb = tile_rsrc(BK_ ? B + (int64_t)n0 * p.ldb : B + n0);
+  const int am = p.M - m0, bn = p.N - n0;
+  auto issue_to = [&](char* st, int t) {
+    const int k0 = (s0 + t) * KS;
+    if constexpr (AK) dma_kc<BM_, NW>(ra, p.lda, am, k0, st, wave, lane);
+    else dma_mc<BM_, NW>(ra, p.lda, am, k0, st, wave, lane);
+    if constexpr (BK_) dma_kc<BN_, NW>(rb, p.ldb, bn, k0, st + AB, wave, lane);
+    else dma_mc<BN_, NW>(rb, p.ldb, bn, k0, st + AB, wave, lane);
+  };
+  auto issue = [&](int t) { issue_to(smem + (t % STAGES) * SB, t); };
+  auto afrag = [&](const char* st, int i) {
+    if constexpr (AK) return frag_kc<BM_>(st, wm * 128 + i * 16 + (lane & 15));
+    else return frag_mc<BM_>(st, wm * 128 + i * 16);
+  };
+  auto bfrag = [&](const char* st, int j) {
+    if constexpr (BK_) return frag_kc<BN_>(st + AB, wn * 128 + j * 16 + (lane & 15));
+    else return frag_mc<BN_>(st + AB, wn * 128 + j * 16);
+  };
+  const int nk = s1 - s0;
+#pragma unroll
+  for (int t = 0; t < STAGES - 1; t++)
+    if (t < nk) issue(t);
+  // stage 0 is in LDS for every wavefront
+  if (nk >= STAGES - 1) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((STAGES - 2) * LPS) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  bf16x8 fa[4], fb0[8], fb1[8];
+  fa[0] = afrag(smem, 0);
+  fa[1] = afrag(smem, 1);
+#pragma unroll
+  for (int j = 0; j < 8; j++) fb0[j] = bfrag(smem, j);
+  // slice t: its B fragments are in fb_c, rows 0 and 1 of A in fa[0], fa[1]. The
+  // steady state (MORE: a later slice exists and the slice STAGES - 1 ahead is to be
+  // loaded) has no branches, so the accumulators stay in their registers through it.
+  // The three stages a slice touches (the one loaded, the two read) are distinct, and
+  // are passed as restrict pointers: the compiler can then tell that the fragment
+  // reads do not touch the stage being loaded (otherwise it waits for every load in
+  // flight before each transposing read).
+  auto slice_in = [&](auto more_c, int t, bf16x8 (&fb_c)[8], bf16x8 (&fb_n)[8], char* __restrict__ dst,
+                      const char* __restrict__ cur, const char* __restrict__ nxt) {
+    constexpr bool STEADY = decltype(more_c)::value;
+    const bool more = STEADY || t + 1 < nk;
+    if (STEADY) {
+      // this wavefront's loads of slice t+1 have landed; after the barrier every
+      // wavefront's have, and every wavefront has consumed its reads of slice t-1,
+      // whose stage the next load overwrites
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((STAGES - 3) * LPS) : "memory");
+      issue_to(dst, t + STAGES - 1);
+    } else if (more) {
+      if (t + STAGES - 2 < nk) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((STAGES - 3) * LPS) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      if (t + STAGES - 1 < nk) issue_to(dst, t + STAGES - 1);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 2 < 8) fa[(i + 2) & 3] = afrag(cur, i + 2);
+      else if (more) fa[(i + 2) & 3] = afrag(nxt, i - 6);
+      if (more) fb_n[i] = bfrag(nxt, i);
+#pragma unroll
+      for (int j = 0; j < 8; j++) mfma_agpr(acc[i][j], fa[i & 3], fb_c[j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto slice = [&](auto more_c, int t, bf16x8 (&fb_c)[8], bf16x8 (&fb_n)[8]) {
+    slice_in(more_c, t, fb_c, fb_n, smem + ((t + STAGES - 1) % STAGES) * SB, smem + (t % STAGES) * SB,
+             smem + ((t + 1) % STAGES) * SB);
+  };
+  using steady = std::integral_constant<bool, true>;
+  using edge = std::integral_constant<bool, false>;
+  int t = 0;
+  for (; t + STAGES < nk; t += 2) {   // both slices steady: t + 1 + STAGES - 1 < nk
+    slice(steady{}, t, fb0, fb1);
+    slice(steady{}, t + 1, fb1, fb0);
+  }
+  for (; t + 1 < nk; t += 2) {
+    slice(edge{}, t, fb0, fb1);
+    slice(edge{}, t + 1, fb1, fb0);
+  }
+  if (t < nk) slice(edge{}, t, fb0, fb1);
+  mfma_agpr_drain(acc);
+}
+
+// All weight gradients of a micro-batch on wide tiles: the grouped launch of
+// gemm_group_kernel with 256 x 256 tiles on four wavefronts of 128 x 128.
+template <int STAGES>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_group_wide_kernel(const WgradProblem* __restrict__ probs, int nprob, int total, int dp_tiles, int K,
+                            float beta, float* __restrict__ ws) {
+  constexpr int SB = 2 * 256 * 32 * 2;
+  static_assert(STAGES * SB >= 4 * 16 * (128 + 4) * 4, "epilogue scratch fits the stages");
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * SB];
+  const int W = gridDim.x, w = blockIdx.x, KI = K / 32;
+  auto run = [&](int t, int s0, int s1, float* park) {
+    const WgradProblem pr = probs[find_problem(probs, nprob, t)];
+    const GemmArgs p = problem_args(pr, K, beta);
+    int tm, tn;
+    tile_coords(t - pr.first_tile, pr.tiles_m, pr.tiles_n, tm, tn);
+    f32x4 acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+#pragma unroll
+      for (int j = 0; j < 8; j++) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    wide_mainloop<false, false, STAGES>(p, smem, tm * 256, tn * 256, s0, s1, acc);
+    tile_epilogue<256, 2, 2, 128, 128, EPI_ACC, true>(p, smem, tm, tm * 256, tn * 256, acc, park);
+  };
+  const int lw = W % 8 == 0 ? (w & 7) * (W >> 3) + (w >> 3) : w;
+  for (int t = lw; t < dp_tiles; t += W) run(t, 0, KI, nullptr);
+  const int rem = total - dp_tiles;
+  if (rem == 0) return;
+  const long long U = (long long)rem * KI;
+  const long long beg = (long long)w * U / W, end = (long long)(w + 1) * U / W;
+  for (long long x = beg; x < end;) {
+    const int r = (int)(x / KI);
+    const int s0 = (int)(x - (long long)r * KI);
+    const int s1 = (int)min((long long)KI, end - (long long)r * KI);
+    const bool split = sk_owner((long long)r * KI, W, U) != sk_owner((long long)r * KI + KI - 1, W, U);
+    run(dp_tiles + r, s0, s1, split ? ws + (int64_t)group_slot(w, r, W, U, KI) * (256 * 256) : nullptr);
+    x = (long long)r * KI + s1;
+  }
+}
+
 static int num_cus();
 
 // ----------------------------------------------------------------------------- few output rows
@@ -1148,6 +1350,16 @@ int wgrad_group_tiles(int M, int N) { return ((M + 255) / 256) * ((N + 255) / 25
 // two parked 256 x 256 partial tiles per workgroup, for up to 256 workgroups
 size_t wgrad_group_ws_floats() { return (size_t)2 * 256 * 256 * 256; }
 
+// GPT_GEMM_WIDE=0 selects the 16-wavefront grouped kernel (for comparisons).
+static bool wgrad_wide() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = std::getenv("GPT_GEMM_WIDE");
+    on = (e && e[0] == '0') ? 0 : 1;
+  }
+  return on == 1;
+}
+
 hipError_t launch_wgrad_group(const WgradProblem* probs, int nprob, int total_tiles, int K, float beta, float* ws,
                               size_t ws_floats, hipStream_t s) {
   if (nprob <= 0 || total_tiles <= 0 || K <= 0) return hipSuccess;
@@ -1156,8 +1368,12 @@ hipError_t launch_wgrad_group(const WgradProblem* probs, int nprob, int total_ti
   const int dp = total_tiles / W * W, rem = total_tiles - dp;
   // 16 wavefronts of 64 x 64 per 256 x 256 tile: four per SIMD hide the transposing LDS
   // reads and the global->LDS waits better than eight of 128 x 64 (-6 % per launch)
-  hipLaunchKernelGGL((gemm_group_kernel<256, 256, 4, 4, 4>), dim3(W), dim3(1024), 0, s, probs, nprob, total_tiles, dp,
-                     K, beta, ws);
+  if (wgrad_wide())
+    hipLaunchKernelGGL((gemm_group_wide_kernel<4>), dim3(W), dim3(256), 0, s, probs, nprob, total_tiles, dp, K, beta,
+                       ws);
+  else
+    hipLaunchKernelGGL((gemm_group_kernel<256, 256, 4, 4, 4>), dim3(W), dim3(1024), 0, s, probs, nprob, total_tiles,
+                       dp, K, beta, ws);
   if (rem > 0)
     hipLaunchKernelGGL((group_fixup_kernel<256, 256>), dim3(rem, 16), dim3(256), 0, s, probs, nprob, total_tiles, dp,
                        K, beta, (const float*)ws, W);
