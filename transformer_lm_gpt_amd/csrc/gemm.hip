@@ -1122,19 +1122,24 @@ __global__ __launch_bounds__(256) void group_fixup_kernel(const WgradProblem* __
 }
 
 // ----------------------------------------------------------------------------- wide tiles
-// 256 x 256 tile on four wavefronts of 128 x 128 (64 accumulators of 16 x 16 each,
-// held in the accumulation registers: one wavefront per SIMD). Per 32-wide k-slice a
-// wavefront reads 16 KB of fragments for 64 MFMAs, half the LDS traffic per MFMA of
-// 64 x 64 wavefront tiles. With a single wavefront per SIMD the LDS latency is
-// hidden inside the wavefront, with few registers: a slice runs row block by row
-// block (8 MFMAs on one A fragment each); the A fragment of row block i+2 is read
-// during row block i into a ring of four (crossing into the next slice at the end),
-// and the next slice's B fragments are read into a second set, one per row block.
-// One barrier per slice publishes the next slice's stage and frees the stage the
-// next load overwrites; loads run STAGES - 2 slices ahead of the slice being read.
+// A (2 TM) x (2 TN) tile on four wavefronts of TM x TN (the grouped weight gradients
+// use 256 x 256 tiles of 128 x 128), one workgroup per CU, with the accumulators held
+// in the accumulation registers for the whole k-loop. 128 x 128 wavefront tiles read
+// 16 KB of fragments per 32-wide slice for 64 MFMAs, half the LDS traffic per MFMA
+// of 64 x 64 ones. (On k-contiguous operands this schedule measured slower than the
+// 192 x 192 kernels with two workgroups per CU: with one, each tile's pipeline fill
+// and output stores stand between k-loops.)
+// The LDS latency is hidden inside each wavefront, with few registers: a slice runs
+// row block by row block (FN MFMAs on one A fragment each); the A fragment of row
+// block i+2 is read during row block i into a small ring (crossing into the next
+// slice at the end), and the next slice's B fragments are read into a second set, a
+// share of them per row block. One barrier per slice publishes the next slice's
+// stage and frees the stage the next load overwrites; loads run STAGES - 2 slices
+// ahead of the slice being read.
+
 // One 16 x 16 x 32 bf16 MFMA accumulating into acc, which the constraint keeps in
-// the accumulation registers for the whole k-loop (the compiler otherwise moves
-// 256 accumulators between register files around the loop's blocks). Volatile: the
+// the accumulation registers for the whole k-loop (the compiler otherwise moves the
+// accumulators between register files around the loop's blocks). Volatile: the
 // MFMAs keep the order written; LDS reads are still scheduled between them.
 __device__ __forceinline__ void mfma_agpr(f32x4& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
@@ -1144,21 +1149,29 @@ __device__ __forceinline__ void mfma_agpr(f32x4& acc, const bf16x8& a, const bf1
 // writing a register and a plain read of it are spent here (24 > the 18 an 8-pass
 // MFMA needs), and each accumulator is passed through an empty asm after them, so
 // no read of it can be scheduled before the wait.
-__device__ __forceinline__ void mfma_agpr_drain(f32x4 (&acc)[8][8]) {
+template <int FM, int FN>
+__device__ __forceinline__ void mfma_agpr_drain(f32x4 (&acc)[FM][FN]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-  for (int i = 0; i < 8; i++)
+  for (int i = 0; i < FM; i++)
 #pragma unroll
-    for (int j = 0; j < 8; j++) asm volatile("" : "+a"(acc[i][j]));
+    for (int j = 0; j < FN; j++) asm volatile("" : "+a"(acc[i][j]));
 }
 
-template <bool AK, bool BK_, int STAGES>
+template <int TM, int TN, bool AK, bool BK_, int STAGES, int AHEAD = 3>
 __device__ __forceinline__ void wide_mainloop(const GemmArgs& p, char* smem, int m0, int n0, int s0, int s1,
-                                              f32x4 (&acc)[8][8]) {
-  constexpr int BM_ = 256, BN_ = 256, NW = 4, KS = 32;
-  constexpr int AB = BM_ * KS * 2, SB = 2 * AB;
+                                              f32x4 (&acc)[TM / 16][TN / 16]) {
+  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr int BM_ = 2 * TM, BN_ = 2 * TN, NW = 4, KS = 32;
+  constexpr int AB = BM_ * KS * 2, SB = AB + BN_ * KS * 2;
   constexpr int LPS = SB / 1024 / NW;              // load instructions per stage per wavefront
+  // A fragments are read AHEAD row blocks early into a ring of RING (a multiple of
+  // FM's divisor so the ring wraps into the next slice in phase); the next slice's B
+  // fragments are read during the first half of the slice, BPR per row block.
+  constexpr int RING = FM % (AHEAD + 1) == 0 ? AHEAD + 1 : FM;
+  constexpr int BPR = (2 * FN + FM - 1) / FM;
   static_assert(STAGES >= 3, "a stage is read while one is loaded and one is being freed");
+  static_assert(FM % RING == 0 && RING > AHEAD && FM >= AHEAD, "the A ring wraps into the next slice in phase");
   const bf16* A = (const bf16*)p.A;
   const bf16* B = (const bf16*)p.B;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1173,37 +1186,36 @@ __device__ __forceinline__ void wide_mainloop(const GemmArgs& p, char* smem, int
     if constexpr (BK_) dma_kc<BN_, NW>(rb, p.ldb, bn, k0, st + AB, wave, lane);
     else dma_mc<BN_, NW>(rb, p.ldb, bn, k0, st + AB, wave, lane);
   };
-  auto issue = [&](int t) { issue_to(smem + (t % STAGES) * SB, t); };
   auto afrag = [&](const char* st, int i) {
-    if constexpr (AK) return frag_kc<BM_>(st, wm * 128 + i * 16 + (lane & 15));
-    else return frag_mc<BM_>(st, wm * 128 + i * 16);
+    if constexpr (AK) return frag_kc<BM_>(st, wm * TM + i * 16 + (lane & 15));
+    else return frag_mc<BM_>(st, wm * TM + i * 16);
   };
   auto bfrag = [&](const char* st, int j) {
-    if constexpr (BK_) return frag_kc<BN_>(st + AB, wn * 128 + j * 16 + (lane & 15));
-    else return frag_mc<BN_>(st + AB, wn * 128 + j * 16);
+    if constexpr (BK_) return frag_kc<BN_>(st + AB, wn * TN + j * 16 + (lane & 15));
+    else return frag_mc<BN_>(st + AB, wn * TN + j * 16);
   };
   const int nk = s1 - s0;
 #pragma unroll
   for (int t = 0; t < STAGES - 1; t++)
-    if (t < nk) issue(t);
+    if (t < nk) issue_to(smem + t * SB, t);
   // stage 0 is in LDS for every wavefront
   if (nk >= STAGES - 1) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((STAGES - 2) * LPS) : "memory");
   else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  bf16x8 fa[4], fb0[8], fb1[8];
-  fa[0] = afrag(smem, 0);
-  fa[1] = afrag(smem, 1);
+  bf16x8 fa[RING], fb0[FN], fb1[FN];
 #pragma unroll
-  for (int j = 0; j < 8; j++) fb0[j] = bfrag(smem, j);
-  // slice t: its B fragments are in fb_c, rows 0 and 1 of A in fa[0], fa[1]. The
-  // steady state (MORE: a later slice exists and the slice STAGES - 1 ahead is to be
+  for (int i = 0; i < AHEAD; i++) fa[i] = afrag(smem, i);
+#pragma unroll
+  for (int j = 0; j < FN; j++) fb0[j] = bfrag(smem, j);
+  // Slice t: its B fragments are in fb_c, rows 0 .. AHEAD-1 of A in the ring. The
+  // steady state (a later slice exists and the slice STAGES - 1 ahead is to be
   // loaded) has no branches, so the accumulators stay in their registers through it.
-  // The three stages a slice touches (the one loaded, the two read) are distinct, and
-  // are passed as restrict pointers: the compiler can then tell that the fragment
-  // reads do not touch the stage being loaded (otherwise it waits for every load in
-  // flight before each transposing read).
-  auto slice_in = [&](auto more_c, int t, bf16x8 (&fb_c)[8], bf16x8 (&fb_n)[8], char* __restrict__ dst,
+  // The three stages a slice touches (the one loaded, the two read) are distinct and
+  // passed as restrict pointers: the compiler can then tell that the fragment reads
+  // do not touch the stage being loaded (otherwise it waits for every load in flight
+  // before each transposing read).
+  auto slice_in = [&](auto steady_c, int t, bf16x8 (&fb_c)[FN], bf16x8 (&fb_n)[FN], char* __restrict__ dst,
                       const char* __restrict__ cur, const char* __restrict__ nxt) {
-    constexpr bool STEADY = decltype(more_c)::value;
+    constexpr bool STEADY = decltype(steady_c)::value;
     const bool more = STEADY || t + 1 < nk;
     if (STEADY) {
       // this wavefront's loads of slice t+1 have landed; after the barrier every
@@ -1217,18 +1229,20 @@ __device__ __forceinline__ void wide_mainloop(const GemmArgs& p, char* smem, int
       if (t + STAGES - 1 < nk) issue_to(dst, t + STAGES - 1);
     }
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
+    for (int i = 0; i < FM; i++) {
       __builtin_amdgcn_sched_barrier(0);
-      if (i + 2 < 8) fa[(i + 2) & 3] = afrag(cur, i + 2);
-      else if (more) fa[(i + 2) & 3] = afrag(nxt, i - 6);
-      if (more) fb_n[i] = bfrag(nxt, i);
+      if (i + AHEAD < FM) fa[(i + AHEAD) % RING] = afrag(cur, i + AHEAD);
+      else if (more) fa[(i + AHEAD) % RING] = afrag(nxt, i + AHEAD - FM);
+      if (more)
 #pragma unroll
-      for (int j = 0; j < 8; j++) mfma_agpr(acc[i][j], fa[i & 3], fb_c[j]);
+        for (int j = i * BPR; j < (i + 1) * BPR && j < FN; j++) fb_n[j] = bfrag(nxt, j);
+#pragma unroll
+      for (int j = 0; j < FN; j++) mfma_agpr(acc[i][j], fa[i % RING], fb_c[j]);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto slice = [&](auto more_c, int t, bf16x8 (&fb_c)[8], bf16x8 (&fb_n)[8]) {
-    slice_in(more_c, t, fb_c, fb_n, smem + ((t + STAGES - 1) % STAGES) * SB, smem + (t % STAGES) * SB,
+  auto slice = [&](auto steady_c, int t, bf16x8 (&fb_c)[FN], bf16x8 (&fb_n)[FN]) {
+    slice_in(steady_c, t, fb_c, fb_n, smem + ((t + STAGES - 1) % STAGES) * SB, smem + (t % STAGES) * SB,
              smem + ((t + 1) % STAGES) * SB);
   };
   using steady = std::integral_constant<bool, true>;
@@ -1243,9 +1257,12 @@ __device__ __forceinline__ void wide_mainloop(const GemmArgs& p, char* smem, int
     slice(edge{}, t + 1, fb1, fb0);
   }
   if (t < nk) slice(edge{}, t, fb0, fb1);
-  mfma_agpr_drain(acc);
+  mfma_agpr_drain<FM, FN>(acc);
 }
 
+// One (2 TM) x (2 TN) output tile per workgroup, both operands k-contiguous (the
+// forward GEMMs and the input gradients). WPE: workgroups per CU the registers are
+// held to (1: 512 registers per wavefront).
 // All weight gradients of a micro-batch on wide tiles: the grouped launch of
 // gemm_group_kernel with 256 x 256 tiles on four wavefronts of 128 x 128.
 template <int STAGES>
@@ -1266,7 +1283,7 @@ void gemm_group_wide_kernel(const WgradProblem* __restrict__ probs, int nprob, i
     for (int i = 0; i < 8; i++)
 #pragma unroll
       for (int j = 0; j < 8; j++) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    wide_mainloop<false, false, STAGES>(p, smem, tm * 256, tn * 256, s0, s1, acc);
+    wide_mainloop<128, 128, false, false, STAGES>(p, smem, tm * 256, tn * 256, s0, s1, acc);
     tile_epilogue<256, 2, 2, 128, 128, EPI_ACC, true>(p, smem, tm, tm * 256, tn * 256, acc, park);
   };
   const int lw = W % 8 == 0 ? (w & 7) * (W >> 3) + (w >> 3) : w;
