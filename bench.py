@@ -326,13 +326,13 @@ def main(argv=None):
             work = 2.0 * B * T * (2 * L * d * d if lora else Vp * d + L * 12 * d * d)   # FLOPs per micro-batch
             per_mb = kern_ms / mbs
             grouped = kern_n == mbs
-            roof = {"kernel": ("grouped weight-gradient GEMM (gemm_group_kernel 256x256, 16 wavefronts, + group_fixup_kernel, "
-                               "bf16 operands, fp32 accumulate)") if grouped else
+            roof = {"kernel": ("grouped weight-gradient GEMM (gemm_group_wide_kernel: 256x256 tiles on 4 wavefronts of "
+                               "128x128, + group_fixup_kernel; bf16 operands, fp32 accumulate)") if grouped else
                               f"weight-gradient GEMMs, {kern_n / mbs:g} launches per micro-batch",
                     "bound": "mfma",
                     "achieved": round(work / (per_mb / 1e3) / 1e12, 2), "peak": peak / 1e12, "unit": "TFLOP/s",
                     "frac": round(work / (per_mb / 1e3) / peak, 4),
-                    "traffic": traffic_of("gemm_group_kernel", cfg.name) if grouped else None,
+                    "traffic": traffic_of("gemm_group_wide_kernel", cfg.name) if grouped else None,
                     "avg_launch_ms": round(avg_ms, 4), "launches": kern_n,
                     ("work_per_launch" if grouped else "work_per_micro_batch"):
                         (f"2*M*(2*L*d^2) = {work:.4g} FLOP" if lora else f"2*M*(Vp*d + 12*L*d^2) = {work:.4g} FLOP")

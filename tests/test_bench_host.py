@@ -22,10 +22,10 @@ def test_flops_per_token_gpt2_124m():
 
 def test_traffic_only_for_its_workload_and_source():
     with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
-        rec = json.load(f)["gemm_group_kernel"]
-    got = bench.traffic_of("gemm_group_kernel", rec["workload"])
+        rec = json.load(f)["gemm_group_wide_kernel"]
+    got = bench.traffic_of("gemm_group_wide_kernel", rec["workload"])
     assert got in (None, rec["bytes_per_launch"])       # None once the source changed
-    assert bench.traffic_of("gemm_group_kernel", "char_6l") is None
+    assert bench.traffic_of("gemm_group_wide_kernel", "char_6l") is None
     assert bench.traffic_of("no_such_kernel", rec["workload"]) is None
 
 
