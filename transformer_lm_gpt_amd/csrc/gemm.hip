@@ -184,6 +184,10 @@ struct GemmArgs {
   float* colsum;       // EPI_GELU_BWD: per-tile-row column sums [tiles_m, N], or NULL
   DropArgs drop;       // EPI_BIAS_RESID_DROP: the branch output's dropout mask
   uint32_t drop_site;
+  // workgroups [stagger_lo, stagger_hi) sleep stagger_iters x 2048 cycles before
+  // their first load (the second workgroup of each CU in the first round, so the
+  // two tiles of a CU reach their epilogues apart)
+  int stagger_lo = 0, stagger_hi = 0, stagger_iters = 0;
 };
 
 // Epilogues that add a residual (with or without dropout on the branch) and those with a bias.
@@ -824,6 +828,8 @@ void gemm_dma_kernel(GemmArgs p) {
   constexpr int SB = (BM_ + BN_) * KS * 2;
   static_assert(STAGES * SB >= (WM_ * WN_ * 16 * (BN_ / WN_ + 4) + WM_ * BN_) * 4, "epilogue scratch fits the stages");
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * SB];
+  if ((int)blockIdx.x >= p.stagger_lo && (int)blockIdx.x < p.stagger_hi)
+    for (int i = 0; i < p.stagger_iters; i++) __builtin_amdgcn_s_sleep(32);
   const int tiles_m = (p.M + BM_ - 1) / BM_, tiles_n = (p.N + BN_ - 1) / BN_;
   const int total = tiles_m * tiles_n;
   // the hardware deals workgroups round-robin to the 8 XCDs; give each XCD a
@@ -1418,6 +1424,23 @@ int gemm_colsum_rows(const GemmDesc& d, bool bf16_operands) {
   return (d.M + 191) / 192;
 }
 
+// The start delay (n x 2048 cycles) of the second workgroup per CU in the
+// two-workgroup kernels. The first round's two workgroups of a CU otherwise finish
+// their k-loops together and run their epilogues side by side; offset, one's
+// epilogue overlaps the other's MFMAs. Measured on the GPT-2 step (whole-step
+// A/B in one session): n = 4..10 took 0.3 ms off 72.3 ms, n >= 12 less. The
+// workgroups dealt to the second slot are [num_cus, 2 num_cus): probed on gfx950,
+// every CU of a 512-workgroup grid of two workgroups per CU held one from each
+// half. GPT_GEMM_STAGGER=n overrides (for comparisons).
+static int gemm_stagger() {
+  static int n = -1;
+  if (n < 0) {
+    const char* e = std::getenv("GPT_GEMM_STAGGER");
+    n = e ? std::max(0, std::min(64, std::atoi(e))) : 6;
+  }
+  return n;
+}
+
 hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
   if (d.M <= 0 || d.N <= 0) return hipSuccess;
   if (d.colsum && gemm_colsum_rows(d, bf16_operands) == 0) return hipErrorInvalidValue;
@@ -1480,6 +1503,9 @@ hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
     // which leave room for two workgroups per CU.
     const int t192 = ((d.M + 191) / 192) * ((d.N + 191) / 192);
     if (t192 <= num_cus() && d.K % 64 == 0) return dma_epi<192, 192, 2, 4, 2, true, true, 64>(a, d.epi, 1, s);
+    a.stagger_lo = num_cus();
+    a.stagger_hi = 2 * num_cus();
+    a.stagger_iters = gemm_stagger();
     return dma_epi<192, 192, 2, 2, 3, true, true>(a, d.epi, 1, s);
   }
   a.colsum = nullptr;

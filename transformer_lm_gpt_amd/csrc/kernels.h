@@ -115,14 +115,14 @@ hipError_t launch_rmsnorm_fwd(const float* x, void* y, bool bf16_out, float* mea
                               hipStream_t s);
 
 // dx = dres + LN backward of dy; writes dx (fp32) and optionally its operand-type copy
-// dx_op; per-block partial column sums of dy * xhat, dy and dres (dres may be NULL,
+// dx_op. dy is in the operand type (bf16 when bf16_out, else fp32); per-block partial column sums of dy * xhat, dy and dres (dres may be NULL,
 // then part_r is unused) into part_g / part_b / part_r ([nblk, d] each,
 // nblk = ceil(M / LN_BWD_ROWS)). dx may alias dres. d must be a multiple of 4.
 // With da.on, the dres column sums take dres * mask(site_in) when site_in >= 0,
 // and dx_op holds dx * mask(site_out) when site_out >= 0 (dx itself is unmasked).
 // g = NULL: the backward of the weightless RMSNorm (part_g and part_b unused).
 constexpr int LN_BWD_ROWS = 16;
-hipError_t launch_layernorm_bwd(const float* dy, const float* x, const float* mean, const float* rstd,
+hipError_t launch_layernorm_bwd(const void* dy, const float* x, const float* mean, const float* rstd,
                                 const float* g, const float* dres, float* dx, void* dx_op, bool bf16_out,
                                 float* part_g, float* part_b, float* part_r, int M, int d, const DropArgs& da,
                                 int site_in, int site_out, hipStream_t s);

@@ -226,6 +226,8 @@ hipError_t launch_rmsnorm_fwd(const float* x, void* y, bool bf16_out, float* mea
 
 // Backward: with xhat = (x - mu) rstd and gh = dy * g,
 //   dx = rstd (gh - mean(gh) - xhat mean(gh xhat)) + dres.
+// dy arrives in the operand type T (bf16 from the input-gradient GEMMs in bf16
+// mode, fp32 otherwise); everything else is fp32.
 // One wavefront per row, LN_BWD_ROWS rows per workgroup. Each lane owns
 // NCH float4 column groups and keeps its column partials of dy*xhat, dy and
 // dres in registers; the four waves are combined in LDS in a fixed order and
@@ -240,7 +242,7 @@ hipError_t launch_rmsnorm_fwd(const float* x, void* y, bool bf16_out, float* mea
 // and no gain or shift partials.
 constexpr int LN_MAX_D = 1024;
 template <typename T, int NCH, bool DROP, bool RMS = false>
-__global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ dy, const float* __restrict__ x,
+__global__ __launch_bounds__(256) void ln_bwd_kernel(const T* __restrict__ dy, const float* __restrict__ x,
                                                      const float* __restrict__ mean,
                                                      const float* __restrict__ rstd, const float* __restrict__ g,
                                                      const float* dres, float* dx, T* dx_op,
@@ -267,7 +269,16 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
       const int c4 = j * 64 + lane;
       const bool in = c4 < d4;
       xn[j] = in ? ((const f32x4*)x)[o4 + c4] : (f32x4){0.f, 0.f, 0.f, 0.f};
-      dyn[j] = in ? ((const f32x4*)dy)[o4 + c4] : (f32x4){0.f, 0.f, 0.f, 0.f};
+      if constexpr (sizeof(T) == 2) {
+        if (in) {
+          const bf16x4 t = ((const bf16x4*)dy)[o4 + c4];
+          dyn[j] = (f32x4){(float)t[0], (float)t[1], (float)t[2], (float)t[3]};
+        } else {
+          dyn[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+      } else {
+        dyn[j] = in ? ((const f32x4*)dy)[o4 + c4] : (f32x4){0.f, 0.f, 0.f, 0.f};
+      }
       rn[j] = in && dres ? ((const f32x4*)dres)[o4 + c4] : (f32x4){0.f, 0.f, 0.f, 0.f};
     }
   };
@@ -351,14 +362,14 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
 }
 
 template <typename T, bool DROP, bool RMS = false>
-static hipError_t ln_bwd_t(const float* dy, const float* x, const float* mean, const float* rstd, const float* g,
+static hipError_t ln_bwd_t(const void* dy, const float* x, const float* mean, const float* rstd, const float* g,
                            const float* dres, float* dx, void* dx_op, float* pg, float* pb, float* pr, int M, int d,
                            const DropArgs& da, int si, int so, hipStream_t s) {
   dim3 grid((M + LN_BWD_ROWS - 1) / LN_BWD_ROWS);
   const int nch = (d / 4 + 63) / 64;
   switch (nch) {
 #define LNB(N) \
-  case N: hipLaunchKernelGGL((ln_bwd_kernel<T, N, DROP, RMS>), grid, dim3(256), 0, s, dy, x, mean, rstd, g, dres, dx, (T*)dx_op, pg, pb, pr, M, d, da, si, so); break;
+  case N: hipLaunchKernelGGL((ln_bwd_kernel<T, N, DROP, RMS>), grid, dim3(256), 0, s, (const T*)dy, x, mean, rstd, g, dres, dx, (T*)dx_op, pg, pb, pr, M, d, da, si, so); break;
     LNB(1) LNB(2) LNB(3) LNB(4)
 #undef LNB
     default: return hipErrorInvalidValue;
@@ -366,7 +377,7 @@ static hipError_t ln_bwd_t(const float* dy, const float* x, const float* mean, c
   return hipGetLastError();
 }
 
-hipError_t launch_layernorm_bwd(const float* dy, const float* x, const float* mean, const float* rstd,
+hipError_t launch_layernorm_bwd(const void* dy, const float* x, const float* mean, const float* rstd,
                                 const float* g, const float* dres, float* dx, void* dx_op, bool bf16_out,
                                 float* part_g, float* part_b, float* part_r, int M, int d, const DropArgs& da,
                                 int site_in, int site_out, hipStream_t s) {

@@ -326,7 +326,7 @@ void plan(gpt_model* h) {
   Planner w;
   h->dres = w.take(M * d * fb);
 
-  h->dln = w.take(M * d * fb);
+  h->dln = w.take(M * d * ob);   // the LayerNorm backward's dy, in the operand type
   const size_t per_layer = h->bf16 ? (size_t)L : 1;
   h->layer_stride_du = h->bf16 ? M * 4 * d * ob : 0;
   h->layer_stride_dqkv = h->bf16 ? M * 3 * d * ob : 0;
@@ -421,7 +421,7 @@ int colsum(gpt_model* h, const void* X, bool bf16_in, int64_t ldx, int M, int N,
 // With dropout, site_in names the mask of the branch whose output was added into
 // this residual (its bias gradient sums the masked dres) and site_out the mask that
 // the operand copy dx_op carries (-1: none).
-int ln_bwd(gpt_model* h, const float* dy, const float* x, const float* mean, const float* rstd,
+int ln_bwd(gpt_model* h, const void* dy, const float* x, const float* mean, const float* rstd,
            const std::string& gname, const std::string& bname, const float* dres, const char* resid_bias, void* dx_op,
            int M, int site_in = -1, int site_out = -1) {
   // the microGPT block: weightless RMSNorm (g = NULL), and no bias to take column sums for
@@ -960,7 +960,7 @@ int gpt_backward(gpt_model* h) {
   hipStream_t s = h->stream;
   const float beta = h->grads_fresh ? 0.f : 1.f;
   float* dres = ws<float>(h, h->dres);
-  float* dln = ws<float>(h, h->dln);
+  void* dln = ws(h, h->dln);   // input gradients into a LayerNorm backward (operand type)
   void* dO = ws(h, h->dO);
   const DropArgs& da = h->drop_fwd;
   const bool drop = da.on != 0;
@@ -985,7 +985,7 @@ int gpt_backward(gpt_model* h) {
   {
     if (!bf && (rc = wgrad_now(act(h, h->logits), h->ldz, act(h, h->lnf), d, h->head, h->Vp, d, "lm_head_wgrad")))
       return rc;
-    GemmDesc g2 = bf ? gemm_desc(act(h, h->logits), h->ldz, true, WopT(h, h->head), h->Vp, true, dln, d, M, d, h->Vp, EPI_F32)
+    GemmDesc g2 = bf ? gemm_desc(act(h, h->logits), h->ldz, true, WopT(h, h->head), h->Vp, true, dln, d, M, d, h->Vp, EPI_STORE)
                      : gemm_desc(act(h, h->logits), h->ldz, true, Wop(h, h->head), d, false, dln, d, M, d, h->Vp, EPI_F32);
     RUN("gemm_dgrad", "lm_head_dgrad", gemm(h, g2, bf));
   }
@@ -1013,7 +1013,7 @@ int gpt_backward(gpt_model* h) {
       rows.nblk[RED_FC] = fc_rows ? fc_rows : (M + COLSUM_ROWS - 1) / COLSUM_ROWS;
       RUN("gemm_dgrad", "fcproj_dgrad", gemm(h, g, bf));
       if (!bf && (rc = wgrad_now(dx, d, act(h, la.h), 4 * d, p + "fcproj.w", d, 4 * d, "fcproj_wgrad"))) return rc;
-      GemmDesc g2 = bf ? gemm_desc(du, 4 * d, true, WopT(h, p + "fc.w"), 4 * d, true, dln, d, M, d, 4 * d, EPI_F32)
+      GemmDesc g2 = bf ? gemm_desc(du, 4 * d, true, WopT(h, p + "fc.w"), 4 * d, true, dln, d, M, d, 4 * d, EPI_STORE)
                        : gemm_desc(du, 4 * d, true, Wop(h, p + "fc.w"), d, false, dln, d, M, d, 4 * d, EPI_F32);
       RUN("gemm_dgrad", "fc_dgrad", gemm(h, g2, bf));
       if (!bf && (rc = wgrad_now(du, 4 * d, act(h, la.ln2), d, p + "fc.w", 4 * d, d, "fc_wgrad"))) return rc;
@@ -1044,7 +1044,7 @@ int gpt_backward(gpt_model* h) {
       // adapters the embeddings are frozen, so layer 0's input gradient (this GEMM
       // and the LayerNorm backward) has no reader
       if (lora && l == 0) continue;
-      GemmDesc g2 = bf ? gemm_desc(dqkv, 3 * d, true, WopT(h, p + "attn.w"), 3 * d, true, dln, d, M, d, 3 * d, EPI_F32)
+      GemmDesc g2 = bf ? gemm_desc(dqkv, 3 * d, true, WopT(h, p + "attn.w"), 3 * d, true, dln, d, M, d, 3 * d, EPI_STORE)
                        : gemm_desc(dqkv, 3 * d, true, Wop(h, p + "attn.w"), d, false, dln, d, M, d, 3 * d, EPI_F32);
       RUN("gemm_dgrad", "qkv_dgrad", gemm(h, g2, bf));
       const std::string proj_b = p + "proj.b";
