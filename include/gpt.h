@@ -293,8 +293,10 @@ int gpt_get_step(gpt_model* h, int64_t* t);
 /* Synchronous copy of a saved activation into caller memory on the device.
  * what: "x" (fp32 [M, d] residual input of block `layer`, layer == n_layer
  * is the input of the final LayerNorm), "qkv" ([M, 3d], operand type),
- * "attn" ([M, d], operand type), "lse" (fp32 [B, H, T]), "u" (GELU input,
- * [M, 4d], operand type), "h" (GELU output, [M, 4d], operand type). bytes
+ * "attn" ([M, d], operand type), "lse" (fp32 [B, H, T]), "u" (what the MLP
+ * backward reads: GELU'(u) of the GELU block's pre-activation u, or u itself for
+ * the ReLU block; [M, 4d], operand type), "h" (the activation's output, [M, 4d],
+ * operand type). bytes
  * must equal the size of the request. */
 int gpt_debug_copy(gpt_model* h, const char* what, int32_t layer, void* d_dst, size_t bytes);
 

@@ -99,6 +99,14 @@ __device__ inline float gelu_grad_f(float u) {
   normal_cdf_pdf(u, c, d);
   return c + u * d;
 }
+// Both from one evaluation of Phi and phi: the forward epilogue saves GELU'(u) for
+// the backward, which then only multiplies by it.
+__device__ inline void gelu_and_grad(float u, float& g, float& dg) {
+  float c, d;
+  normal_cdf_pdf(u, c, d);
+  g = u * c;
+  dg = c + u * d;
+}
 
 // Philox4x32-10 (Salmon, Moraes, Dror and Shaw, SC 2011): ten rounds, each taking
 // the 32x32 -> 64-bit products of counter words 0 and 2 with the two round

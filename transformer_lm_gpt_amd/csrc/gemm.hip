@@ -224,9 +224,10 @@ __device__ inline void epi_store(const GemmArgs& p, int row, int col, float v, f
   } else if constexpr (EPI == EPI_BIAS_RESID_DROP) {
     ((float*)p.C)[ci] = p.resid[(int64_t)row * p.ldr + col] + (v + bias) * drop_mult_elem(p.drop, p.drop_site, row, col);
   } else if constexpr (EPI == EPI_BIAS_GELU) {
-    const float u = v + bias;
-    ((T*)p.aux)[(int64_t)row * p.ldaux + col] = from_f32<T>(u);
-    ((T*)p.C)[ci] = from_f32<T>(gelu_f(u));
+    float g, dg;
+    gelu_and_grad(v + bias, g, dg);
+    ((T*)p.aux)[(int64_t)row * p.ldaux + col] = from_f32<T>(dg);
+    ((T*)p.C)[ci] = from_f32<T>(g);
   } else if constexpr (EPI == EPI_F32) {
     ((float*)p.C)[ci] = v;
   } else if constexpr (EPI == EPI_BIAS_RELU) {
@@ -234,7 +235,7 @@ __device__ inline void epi_store(const GemmArgs& p, int row, int col, float v, f
     ((T*)p.aux)[(int64_t)row * p.ldaux + col] = from_f32<T>(u);
     ((T*)p.C)[ci] = from_f32<T>(fmaxf(u, 0.f));
   } else if constexpr (EPI == EPI_GELU_BWD) {
-    ((T*)p.C)[ci] = from_f32<T>(v * gelu_grad_f(to_f32(((const T*)p.aux)[(int64_t)row * p.ldaux + col])));
+    ((T*)p.C)[ci] = from_f32<T>(v * to_f32(((const T*)p.aux)[(int64_t)row * p.ldaux + col]));
   } else if constexpr (EPI == EPI_RELU_BWD) {
     ((T*)p.C)[ci] = from_f32<T>(to_f32(((const T*)p.aux)[(int64_t)row * p.ldaux + col]) > 0.f ? v : 0.f);
   } else {  // EPI_ACC
@@ -247,8 +248,8 @@ __device__ inline void epi_store(const GemmArgs& p, int row, int col, float v, f
   }
 }
 
-// Global inputs of the vector epilogue (residual or GELU input) for sixteen columns,
-// loaded ahead of the tile's parked accumulators so the loads of the next 16-row
+// Global inputs of the vector epilogue (the residual, or the saved GELU'(u) / ReLU
+// input) for sixteen columns, loaded ahead of the tile's parked accumulators so the loads of the next 16-row
 // block are in flight while the current one is stored.
 template <int EPI>
 struct EpiPre {
@@ -270,7 +271,7 @@ struct EpiPre {
 
 // Sixteen consecutive output columns col0.. of one row: vector loads and stores
 // when the run is inside the matrix and aligned, element-wise otherwise. pre, if
-// given, holds this run's residual or GELU input, loaded by EpiPre::load.
+// given, holds this run's residual or saved GELU'(u) / ReLU input, loaded by EpiPre::load.
 // With EPI_GELU_BWD the final fp32 values are also added into sum16 (the bias
 // gradient's column sums); other epilogues leave it alone.
 template <int EPI>
@@ -283,7 +284,7 @@ __device__ inline void epi_store16(const GemmArgs& p, int row, int col0, const f
       if (col0 + c < p.N) {
         epi_store<bf16, EPI>(p, row, col0 + c, v[c], epi_bias<EPI>(p, col0 + c));
         if constexpr (EPI == EPI_GELU_BWD)
-          sum16[c] += v[c] * gelu_grad_f((float)((const bf16*)p.aux)[(int64_t)row * p.ldaux + col0 + c]);
+          sum16[c] += v[c] * (float)((const bf16*)p.aux)[(int64_t)row * p.ldaux + col0 + c];
         if constexpr (EPI == EPI_RELU_BWD)
           sum16[c] += (float)((const bf16*)p.aux)[(int64_t)row * p.ldaux + col0 + c] > 0.f ? v[c] : 0.f;
       }
@@ -330,16 +331,18 @@ __device__ inline void epi_store16(const GemmArgs& p, int row, int col0, const f
       *(f32x4*)((float*)p.C + ci + 4 * q) = o;
     }
   } else if constexpr (EPI == EPI_BIAS_GELU) {
-    bf16* u = (bf16*)p.aux + (int64_t)row * p.ldaux + col0;
+    bf16* dgp = (bf16*)p.aux + (int64_t)row * p.ldaux + col0;
 #pragma unroll
     for (int q = 0; q < 2; q++) {
-      bf16x8 uo, o;
+      bf16x8 dgo, o;
 #pragma unroll
       for (int e = 0; e < 8; e++) {
-        uo[e] = (bf16)x[8 * q + e];
-        o[e] = (bf16)gelu_f(x[8 * q + e]);
+        float g, dg;
+        gelu_and_grad(x[8 * q + e], g, dg);
+        dgo[e] = (bf16)dg;
+        o[e] = (bf16)g;
       }
-      *(bf16x8*)(u + 8 * q) = uo;
+      *(bf16x8*)(dgp + 8 * q) = dgo;
       *(bf16x8*)((bf16*)p.C + ci + 8 * q) = o;
     }
   } else if constexpr (EPI == EPI_BIAS_RELU) {
@@ -380,7 +383,7 @@ __device__ inline void epi_store16(const GemmArgs& p, int row, int col0, const f
       bf16x8 o;
 #pragma unroll
       for (int e = 0; e < 8; e++) {
-        const float y = x[8 * q + e] * gelu_grad_f((float)uv[e]);
+        const float y = x[8 * q + e] * (float)uv[e];
         o[e] = (bf16)y;
         sum16[8 * q + e] += y;
       }
@@ -620,7 +623,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, char* smem, int
   // Epilogue through LDS: each wave parks one 16-row block of its TM x TN
   // quadrant, then a lane handles 16 contiguous columns of one row (TN/16 such
   // groups per row, so 64 lanes cover the block in one or more passes), so bias,
-  // residual and GELU inputs are read and outputs written as vectors.
+  // residual and saved derivative inputs are read and outputs written as vectors.
   constexpr int ELD = TN + 4;
   constexpr int CG = TN / 16, ITEMS = 16 * CG, PASSES = (ITEMS + 63) / 64;
   // epilogue inputs of 16-row block i (item it = lane + 64*ps: row er, columns ec..)

@@ -33,9 +33,9 @@ enum Epilogue {
   EPI_STORE = 0,       // C(T)   = acc
   EPI_BIAS = 1,        // C(T)   = acc + bias[n]
   EPI_BIAS_RESID = 2,  // C(f32) = resid[m, n] + acc + bias[n]
-  EPI_BIAS_GELU = 3,   // aux(T) = u = acc + bias[n];  C(T) = gelu(u)
+  EPI_BIAS_GELU = 3,   // u = acc + bias[n]: aux(T) = gelu'(u) (saved for EPI_GELU_BWD);  C(T) = gelu(u)
   EPI_F32 = 4,         // C(f32) = acc
-  EPI_GELU_BWD = 5,    // C(T)   = acc * gelu'(aux[m, n])   (aux in operand type T)
+  EPI_GELU_BWD = 5,    // C(T)   = acc * aux[m, n], aux = gelu'(u) from EPI_BIAS_GELU (operand type T)
   EPI_ACC = 6,         // C(f32) = beta * C + acc   (beta is 0 or 1; C is not read when 0)
   EPI_BIAS_RESID_DROP = 7,  // C(f32) = resid[m, n] + mask(drop_site, m, n) * (acc + bias[n])
   EPI_BIAS_RELU = 8,   // aux(T) = u = acc + bias[n];  C(T) = max(u, 0)

@@ -308,7 +308,7 @@ void plan(gpt_model* h) {
     la.ln2 = a.take(M * d * ob);
     la.ln2_mean = a.take(M * fb);
     la.ln2_rstd = a.take(M * fb);
-    la.u = a.take(M * 4 * d * ob);
+    la.u = a.take(M * 4 * d * ob);   // GELU'(u) (GELU block) or u (ReLU block), for the MLP backward
     la.h = a.take(M * 4 * d * ob);
   }
   h->x_final = a.take(M * d * fb);
