@@ -613,20 +613,25 @@ __device__ inline void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int
 // (BM_ x BN_, row-major) when it is given. Ends with a barrier, so the LDS may be
 // reused by the caller. PF_OK: the epilogue's global inputs may be loaded one
 // 16-row block ahead (registers allow it).
-template <int BN_, int WM_, int WN_, int TM, int TN, int EPI, bool PF_OK>
+// RB: 16-row blocks per round. A round parks RB blocks of the wave's quadrant and
+// its lanes take 16-column items of them, so RB is chosen to make the items a
+// multiple of 64 (with 96-wide wave tiles one block gives 96 items: a second pass
+// with half the lanes idle; two give 192, three full passes).
+template <int BN_, int WM_, int WN_, int TM, int TN, int EPI, bool PF_OK, int RB = 1>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, char* smem, int tm, int m0, int n0,
                                               f32x4 (&acc)[TM / 16][TN / 16], float* park) {
   constexpr int NW = WM_ * WN_;
   constexpr int FM = TM / 16, FN = TN / 16;
+  static_assert(FM % RB == 0, "whole rounds of row blocks");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN_, wn = wave % WN_;
-  // Epilogue through LDS: each wave parks one 16-row block of its TM x TN
-  // quadrant, then a lane handles 16 contiguous columns of one row (TN/16 such
-  // groups per row, so 64 lanes cover the block in one or more passes), so bias,
-  // residual and saved derivative inputs are read and outputs written as vectors.
+  // Epilogue through LDS: each wave parks RB 16-row blocks of its TM x TN quadrant,
+  // then a lane handles 16 contiguous columns of one row (TN/16 such groups per
+  // row, so 64 lanes cover the round in one or more passes), so bias, residual and
+  // saved derivative inputs are read and outputs written as vectors.
   constexpr int ELD = TN + 4;
-  constexpr int CG = TN / 16, ITEMS = 16 * CG, PASSES = (ITEMS + 63) / 64;
-  // epilogue inputs of 16-row block i (item it = lane + 64*ps: row er, columns ec..)
+  constexpr int CG = TN / 16, ROWS = 16 * RB, ITEMS = ROWS * CG, PASSES = (ITEMS + 63) / 64;
+  // epilogue inputs of round i (item it = lane + 64*ps: row er, columns ec..)
   // (the fp32 residual of two blocks does not fit beside the accumulators of two
   // workgroups per CU: the 32-wide-slice residual kernel loads it in place)
   constexpr bool PF = EpiPre<EPI>::ON && PF_OK;
@@ -636,13 +641,13 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, char* smem, int
     for (int ps = 0; ps < PASSES; ps++) {
       const int it = lane + 64 * ps;
       if (ITEMS % 64 != 0 && it >= ITEMS) break;
-      const int row = m0 + wm * TM + i * 16 + it / CG, col0 = n0 + wn * TN + (it % CG) * 16;
+      const int row = m0 + wm * TM + i * ROWS + it / CG, col0 = n0 + wn * TN + (it % CG) * 16;
       if (row < p.M && col0 + 16 <= p.N && p.c_vec) dst[ps].load(p, row, col0);
     }
   };
   if constexpr (PF)
     if (!park) prefetch(0, pre[0]);
-  // the bias of an item's 16 columns is the same in every row block
+  // the bias of an item's 16 columns is the same in every round
   constexpr bool PB = epi_has_bias<EPI>();
   f32x4 bias16[PB ? PASSES : 1][4];
   if constexpr (PB) {
@@ -660,7 +665,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, char* smem, int
   // the last k-slices waited for all global->LDS loads. A plain s_barrier, so the
   // epilogue loads just issued stay in flight.
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  float* scr = (float*)smem + wave * 16 * ELD;
+  float* scr = (float*)smem + wave * ROWS * ELD;
   // fused bias gradient (GELU backward): this lane's column sums of its items
   constexpr bool CS = epi_act_bwd<EPI>();
   const bool colsum = CS && p.colsum && !park;
@@ -670,13 +675,16 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, char* smem, int
 #pragma unroll
     for (int e = 0; e < 16; e++) cs[ps][e] = 0.f;
 #pragma unroll
-  for (int i = 0; i < FM; i++) {
+  for (int i = 0; i < FM / RB; i++) {
     if constexpr (PF)
-      if (!park && i + 1 < FM) prefetch(i + 1, pre[(i + 1) & 1]);
+      if (!park && i + 1 < FM / RB) prefetch(i + 1, pre[(i + 1) & 1]);
 #pragma unroll
-    for (int j = 0; j < FN; j++)
+    for (int r = 0; r < RB; r++)
 #pragma unroll
-      for (int e = 0; e < 4; e++) scr[(4 * (lane >> 4) + e) * ELD + j * 16 + (lane & 15)] = acc[i][j][e];
+      for (int j = 0; j < FN; j++)
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+          scr[(16 * r + 4 * (lane >> 4) + e) * ELD + j * 16 + (lane & 15)] = acc[i * RB + r][j][e];
 #pragma unroll
     for (int ps = 0; ps < PASSES; ps++) {
       const int it = lane + 64 * ps;
@@ -689,7 +697,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, char* smem, int
 #pragma unroll
         for (int e = 0; e < 4; e++) v[4 * q + e] = t[e];
       }
-      const int rt = wm * TM + i * 16 + er;      // row within the tile
+      const int rt = wm * TM + i * ROWS + er;    // row within the tile
       if (park) {
         float* d = park + (int64_t)rt * BN_ + wn * TN + ec;
 #pragma unroll
@@ -706,7 +714,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, char* smem, int
     if (colsum) {
       // rows of each wave's items through its own scratch, then the WM waves that
       // share a column range in a fixed order, into one partial row per tile row
-      float* red = (float*)smem + NW * 16 * ELD;   // [WM_][BN_]
+      float* red = (float*)smem + NW * ROWS * ELD;   // [WM_][BN_]
 #pragma unroll
       for (int ps = 0; ps < PASSES; ps++) {
         const int it = lane + 64 * ps;
@@ -718,7 +726,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, char* smem, int
       for (int c = lane; c < TN; c += 64) {
         float t = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; r++) t += scr[r * ELD + c];
+        for (int r = 0; r < ROWS; r++) t += scr[r * ELD + c];
         red[wm * BN_ + wn * TN + c] = t;
       }
       __syncthreads();
@@ -818,7 +826,12 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, 
     }
   }
 
-  tile_epilogue<BN_, WM_, WN_, TM, TN, EPI, !(epi_resid<EPI>() && KS == 32)>(p, smem, tm, m0, n0, acc, park);
+  // two row blocks per epilogue round when one leaves lanes idle and the scratch fits the stages
+  constexpr int CGE = TN / 16;
+  constexpr bool RB2 = CGE % 4 != 0 && (2 * CGE) % 4 == 0 && FM % 2 == 0 &&
+                       (NW * 32 * (TN + 4) + WM_ * BN_) * 4 <= STAGES * SB;
+  tile_epilogue<BN_, WM_, WN_, TM, TN, EPI, !(epi_resid<EPI>() && KS == 32), RB2 ? 2 : 1>(p, smem, tm, m0, n0, acc,
+                                                                                          park);
 }
 
 
