@@ -37,6 +37,24 @@ def test_library_is_gfx950_only():
         assert other not in blob
 
 
+def test_every_launch_stub_has_its_device_kernel():
+    # each host launch stub (gpt::__device_stub__<kernel>) must find a kernel
+    # descriptor of the same mangled name in the gfx950 code object; a library whose
+    # host and device passes saw different versions of a kernel's signature builds
+    # and loads, and fails only at the first launch of that kernel
+    blob = open(Bd.LIB_PATH, "rb").read()
+    stubs = set(re.findall(rb"_ZN3gpt(\d+)__device_stub__([A-Za-z0-9_]+)", blob))
+    assert len(stubs) > 100
+    missing = []
+    for n, tail in stubs:
+        name_len = int(n) - len("__device_stub__")
+        name, rest = tail[:name_len], tail[name_len:]
+        kernel = b"_ZN3gpt" + str(name_len).encode() + name + rest
+        if kernel + b".kd" not in blob:
+            missing.append(kernel.decode())
+    assert not missing, missing
+
+
 @pytest.mark.parametrize("name", W.ORDER + W.VARIANT_CONFIGS + W.LORA_CONFIGS)
 @pytest.mark.parametrize("prec", ["fp32", "bf16"])
 def test_layout_matches_oracle(name, prec):

@@ -54,15 +54,28 @@ def test_gpt2_forward_all_sequences():
         pr = np.linalg.norm(zs - zr, axis=1) / np.linalg.norm(zr, axis=1)
         lg, lo = _lse_loss(zs, tgt[b]), _lse_loss(zr, tgt[b])
         host.append(lg.mean())
+        # The argmax is an integer that floating point decides. It is unique at this
+        # precision where the oracle's top two logits are further apart than the GPU's
+        # errors can move their gap: each of the two logits may move by half a bf16 ulp
+        # (its storage) plus six times the sequence's RMS logit error (its computation),
+        # and in opposite directions, so the band is twice (ulp + 6 RMS). There the argmax
+        # must agree; elsewhere several indices are correct, and the GPU's pick must lie
+        # within the band below the oracle's maximum.
         top = np.sort(zr, -1)[..., -2:]
-        clear = (top[..., 1] - top[..., 0]) > 0.05 * zr.std(-1)
-        agree = np.array_equal(np.argmax(zs, -1)[clear], np.argmax(zr, -1)[clear])
+        ulp = 2.0 ** (np.floor(np.log2(np.abs(top[..., 1]) + 1e-30)) - 7)
+        sigma = np.sqrt(np.mean((zs - zr) ** 2, axis=-1))
+        band = 2.0 * (ulp + 6.0 * sigma)
+        clear = (top[..., 1] - top[..., 0]) > band
+        ag, ar = np.argmax(zs, -1), np.argmax(zr, -1)
+        in_band = zr[np.arange(zr.shape[0]), ag] >= top[..., 1] - band
         say(f"  sequence {b}: logits rel {r:.2e}, worst position {pr.max():.2e}, "
-            f"loss {lg.mean():.5f} vs {lo.mean():.5f}, argmax agrees on {int(clear.sum())} clear positions")
+            f"loss {lg.mean():.5f} vs {lo.mean():.5f}, argmax agrees on {int(clear.sum())} clear positions, "
+            f"{int((ag != ar).sum())} differ, all within the band: {bool(in_band.all())}")
         assert r < 2e-2 and pr.max() < 2e-2, (b, r, float(pr.max()))
         assert abs(lg.mean() - lo.mean()) / lo.mean() < 2e-2, (b, lg.mean(), lo.mean())
         assert np.max(np.abs(lg - lo)) < 2e-2 * lo.mean(), b
-        assert agree, b
+        assert np.array_equal(ag[clear], ar[clear]), (b, np.nonzero(ag[clear] != ar[clear]))
+        assert in_band.all(), (b, np.nonzero(~in_band))
     # the fused cross-entropy agrees with the loss recomputed from the GPU's own logits
     assert abs(loss - float(np.mean(host))) < 1e-3 * loss, (loss, float(np.mean(host)))
     gpu.close()

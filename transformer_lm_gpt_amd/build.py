@@ -38,7 +38,7 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # per-source device flags: attention keeps its MFMA accumulators in ordinary VGPRs,
 # so the softmax arithmetic on them needs no copies out of the accumulation registers
 SOURCE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
-COMMON = ["-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
+COMMON_FLAGS = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function"]
 
 
 def hipcc() -> str:
@@ -48,9 +48,27 @@ def hipcc() -> str:
     return p
 
 
+SNAP = os.path.join(BUILD, "src")
+SNAP_CSRC = os.path.join(SNAP, os.path.relpath(CSRC, ROOT))
+SNAP_INC = ["-I", os.path.join(SNAP, "include"), "-I", SNAP_CSRC]
+
+
+def _snapshot() -> None:
+    """Copies csrc/ and include/ into _build/src, in the repository's layout (the
+    sources include the public header by a relative path). hipcc reads a source once for the
+    device pass and again for the host pass; compiling from a frozen copy keeps an
+    edit made during a build from giving host stubs and device code of different
+    versions (a launch of such a kernel fails with a missing-symbol error)."""
+    for d in (CSRC, INCLUDE):
+        dst = os.path.join(SNAP, os.path.relpath(d, ROOT))
+        if os.path.isdir(dst):
+            shutil.rmtree(dst)
+        shutil.copytree(d, dst, ignore=shutil.ignore_patterns("*.o", "__pycache__"))
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *SNAP_INC, "-c", os.path.join(SNAP_CSRC, src), "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = [f"--offload-arch={ARCH}", *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, [])]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -88,10 +106,11 @@ def asan_env() -> dict:
 def build_asan(jobs: int = 8, verbose: bool = False) -> str:
     """The kernels as usual, runtime.cpp with host AddressSanitizer, linked into ASAN_LIB."""
     os.makedirs(ASAN_DIR, exist_ok=True)
+    _snapshot()
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(_compile, [x for x in SOURCES if x != "runtime.cpp"]))
     obj = os.path.join(ASAN_DIR, "runtime.o")
-    cmd = [hipcc(), *COMMON, *ASAN_FLAGS, "-c", os.path.join(CSRC, "runtime.cpp"), "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *SNAP_INC, *ASAN_FLAGS, "-c", os.path.join(SNAP_CSRC, "runtime.cpp"), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -107,6 +126,7 @@ def build_asan(jobs: int = 8, verbose: bool = False) -> str:
 
 def build(jobs: int = 8, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    _snapshot()
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"

@@ -188,6 +188,7 @@ struct GemmArgs {
   // their first load (the second workgroup of each CU in the first round, so the
   // two tiles of a CU reach their epilogues apart)
   int stagger_lo = 0, stagger_hi = 0, stagger_iters = 0;
+  int krot = 0;        // rotate each tile's k-slice order by its position in the launch
 };
 
 // Epilogues that add a residual (with or without dropout on the branch) and those with a bias.
@@ -748,7 +749,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, char* smem, int
 // slices of KS).
 template <int BM_, int BN_, int WM_, int WN_, int STAGES, bool AK, bool BK_, int EPI, int KS = 32>
 __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, int tn, int s0, int s1,
-                                         float* park) {
+                                         float* park, int rot = 0) {
   static_assert(KS == 32 || (KS == 64 && AK && BK_), "64-wide slices need k-contiguous operands");
   constexpr int NW = WM_ * WN_;
   constexpr int TM = BM_ / WM_, TN = BN_ / WN_;
@@ -774,7 +775,10 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, 
   const int am = p.M - m0, bn = p.N - n0;
   auto issue = [&](int t) {
     char* st = smem + (t % STAGES) * SB;
-    const int k0 = (s0 + t) * KS;
+    // rot: this tile's first k-slice (the tiles of a launch then walk the shared operand
+    // rows at different k instead of all at once)
+    const int tr = t + rot < nk ? t + rot : t + rot - nk;
+    const int k0 = (s0 + tr) * KS;
     if constexpr (KS == 64) {
       dma_kc64<BM_, NW>(ra, p.lda, am, k0, st, wave, lane);
       dma_kc64<BN_, NW>(rb, p.ldb, bn, k0, st + AB, wave, lane);
@@ -856,7 +860,8 @@ void gemm_dma_kernel(GemmArgs p) {
   tile_coords(bid, tiles_m, tiles_n, tm, tn);
   const int s0 = blockIdx.z * (p.kchunk / KS);
   const int s1 = min(p.K, (int)(blockIdx.z + 1) * p.kchunk) / KS;
-  dma_tile<BM_, BN_, WM_, WN_, STAGES, AK, BK_, EPI, KS>(p, smem, tm, tn, s0, s1, nullptr);
+  const int rot = p.krot && gridDim.z == 1 ? (int)((int64_t)bid * (s1 - s0) / total) : 0;
+  dma_tile<BM_, BN_, WM_, WN_, STAGES, AK, BK_, EPI, KS>(p, smem, tm, tn, s0, s1, nullptr, rot);
 }
 
 // Stream-K: gridDim.x workgroups share the tiles x (K/32) slice-units evenly, each a
@@ -1282,9 +1287,6 @@ __device__ __forceinline__ void wide_mainloop(const GemmArgs& p, char* smem, int
   mfma_agpr_drain<FM, FN>(acc);
 }
 
-// One (2 TM) x (2 TN) output tile per workgroup, both operands k-contiguous (the
-// forward GEMMs and the input gradients). WPE: workgroups per CU the registers are
-// held to (1: 512 registers per wavefront).
 // All weight gradients of a micro-batch on wide tiles: the grouped launch of
 // gemm_group_kernel with 256 x 256 tiles on four wavefronts of 128 x 128.
 template <int STAGES>
@@ -1457,6 +1459,24 @@ static int gemm_stagger() {
   return n;
 }
 
+// Each tile of a 192-wide launch walks its k-slices starting at its own position in
+// the launch (tile i of T starts at slice i * nk / T and wraps around), so the tiles
+// that share an operand panel do not all request the same rows at the same moment.
+// Measured on the GPT-2 step (whole-step A/B, each pair in one session): 68.8 -> 67.1
+// and 69.5 -> 68.2 ms, most of it in the lm_head forward and the 768-column residual
+// GEMMs. The same rotation of the grouped weight-gradient tiles measured slower (68.6-68.9
+// against 68.2 ms), so that launch keeps the plain order. The fp32 sums of a
+// tile are taken in the rotated order (fixed per tile, so the result is deterministic).
+// GPT_GEMM_KROT=0 restores the plain order (for comparisons).
+static int gemm_krot() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = std::getenv("GPT_GEMM_KROT");
+    on = (e && e[0] == '0') ? 0 : 1;
+  }
+  return on;
+}
+
 hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
   if (d.M <= 0 || d.N <= 0) return hipSuccess;
   if (d.colsum && gemm_colsum_rows(d, bf16_operands) == 0) return hipErrorInvalidValue;
@@ -1518,6 +1538,7 @@ hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
     // (2-7 % on the step's N = 768 shapes). Otherwise 32-wide slices in three stages,
     // which leave room for two workgroups per CU.
     const int t192 = ((d.M + 191) / 192) * ((d.N + 191) / 192);
+    a.krot = gemm_krot();
     if (t192 <= num_cus() && d.K % 64 == 0) return dma_epi<192, 192, 2, 4, 2, true, true, 64>(a, d.epi, 1, s);
     a.stagger_lo = num_cus();
     a.stagger_hi = 2 * num_cus();
