@@ -132,12 +132,12 @@ def bench_decode(a, cfg) -> int:
 
     def generate():
         z = gpu.prefill(tok)
-        t = gpu.sample(z, a.temperature, a.top_k, None if a.temperature <= 0 else uni[0])
+        t = gpu.sample(z, a.temperature, a.top_k, None if a.temperature <= 0 else uni[0], out=gpu.decode_tokens())
         e0 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for s in range(1, n + 1):
             z = gpu.decode(t)
-            t = gpu.sample(z, a.temperature, a.top_k, None if a.temperature <= 0 else uni[s % n])
+            t = gpu.sample(z, a.temperature, a.top_k, None if a.temperature <= 0 else uni[s % n], out=t)
         e1 = torch.cuda.Event(enable_timing=True)
         e1.record(stream)
         return e0, e1, t

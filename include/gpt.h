@@ -233,7 +233,13 @@ int gpt_forward_logits(gpt_model* h, const int32_t* d_tokens, int32_t B, int32_t
  * last prefill, at the next position; appends its keys and values and writes
  * fp32 logits [B, padded_vocab]. The logits equal the last row of a full
  * forward over the sequence so far (up to rounding). GPT_E_STATE without a
- * prefill, GPT_E_SEQ_TOO_LONG once block_size positions are cached.
+ * prefill, GPT_E_SEQ_TOO_LONG once block_size positions are cached. The ids are
+ * read and the logits written by the step's kernels, in stream order (d_tokens
+ * may be rewritten once the call's work has run). A call whose d_tokens,
+ * d_logits and batch repeat the previous call's replays a graph of the step,
+ * recorded by the library at the first repeat (the position is kept on the
+ * device); any other call launches the kernels one by one. The results are the
+ * same either way. The graph holds the bound buffers' addresses: gpt_bind drops it.
  * gpt_sample: one token per row of fp32 logits [B, padded_vocab] into
  * d_tokens_out int32 [B]. temperature <= 0: the argmax, lowest index on ties
  * (d_uniform may be NULL). Otherwise the candidates are the logits >= the

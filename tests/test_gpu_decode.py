@@ -62,6 +62,50 @@ def test_decode_gpt2_124m_bf16():
     gpu.close()
 
 
+@pytest.mark.parametrize("name,prec", [("char_6l", "bf16"), ("tiny", "fp32")])
+def test_decode_graph_replays_equal_direct_launches(name, prec):
+    """A decode call that repeats the previous call's token and logits pointers replays
+    the recorded step; one whose pointers differ launches the kernels one by one. Both
+    give the same logits, bit for bit, at every step. Each replay is followed by eager
+    work (the sampler) and a host synchronization. A second prefill of another length
+    moves the device position that the same recording then reads."""
+    import ctypes as C
+    import torch
+    cfg = W.CONFIGS[name]
+    drng, wrng = W.rngs()
+    params = W.init_params(cfg, wrng, perturb=True)
+    B, steps, lens = 3, 4, (min(21, cfg.block_size // 3), min(34, cfg.block_size // 2))
+    tok, _ = W.make_batch(cfg, drng, B=B, T=max(lens) + steps)
+    say(f"[decode graph] {name} {prec} B={B} prompts {lens}")
+    gpu = _model(cfg, prec)
+    gpu.load_params(params)
+    recorded = {}
+    for T0 in lens:                                   # the binding's fixed buffers: replays
+        gpu.prefill(tok[:, :T0])
+        zs = []
+        for s in range(steps):
+            z = gpu.decode(tok[:, T0 + s])
+            gpu.sample(z, 0.0)
+            gpu.sync()
+            zs.append(z.cpu().numpy().copy())
+        recorded[T0] = zs
+    tb = gpu.decode_tokens()
+    outs = [torch.empty_like(gpu._dec_out), torch.empty_like(gpu._dec_out)]
+    tol = 1e-5 if prec == "fp32" else 2e-2
+    for T0 in lens:                                   # alternating logits buffers: direct launches
+        gpu.prefill(tok[:, :T0])
+        for s in range(steps):
+            tb.copy_(torch.from_numpy(np.ascontiguousarray(tok[:, T0 + s], dtype=np.int32)).to(tb.device))
+            o = outs[s % 2]
+            gpu._check(gpu.lib.gpt_decode(gpu.h, C.c_void_p(tb.data_ptr()), C.c_void_p(o.data_ptr())))
+            zd = o.cpu().numpy()
+            assert np.array_equal(zd, recorded[T0][s]), (T0, s, float(np.max(np.abs(zd - recorded[T0][s]))))
+        zr = O.logits(params, tok[:, :T0 + steps], cfg)[:, -1]
+        say(f"  prompt {T0}: {steps} steps equal; last step rel {rel(recorded[T0][-1], zr):.2e}")
+        assert rel(recorded[T0][-1], zr) < tol
+    gpu.close()
+
+
 def test_greedy_generation_matches_oracle():
     """fp32, spread logits: the greedy tokens equal the oracle's wherever its top-1
     and top-2 logits are more than 1e-3 apart (after the first unclear step the

@@ -201,6 +201,7 @@ class GPT(Layout):
         self._check(self.lib.gpt_bind(self.h, C.byref(b), C.c_void_p(self.stream.cuda_stream)))
         self.loss_buf = torch.zeros(1, dtype=torch.float32, device=self.device)
         self.norm_buf = torch.zeros(1, dtype=torch.float32, device=self.device)
+        self._dec_tok = self._dec_out = None   # decode's token and logits buffers
 
     # ---- weights and state
     def load_params(self, params: Dict[str, np.ndarray], reset_state: bool = True):
@@ -267,17 +268,34 @@ class GPT(Layout):
         self._kv_B = B
         return out
 
+    def decode_tokens(self, B: Optional[int] = None):
+        """The token buffer decode() reads, one id per sequence of the last prefill (or
+        B): sample(..., out=gpu.decode_tokens()) draws straight into it, with no copy."""
+        B = getattr(self, "_kv_B", None) if B is None else B
+        if B is None:
+            raise RuntimeError("decode_tokens() needs a preceding prefill or B")
+        if self._dec_tok is None or self._dec_tok.numel() != B:
+            t = self.torch
+            self._dec_tok = t.zeros(B, dtype=t.int32, device=self.device)
+            self._dec_out = t.empty((B, self.cfg.padded_vocab), dtype=t.float32, device=self.device)
+        return self._dec_tok
+
     def decode(self, tokens):
+        """One decode step. The ids go through one token buffer and the fp32 logits come
+        back in one logits buffer, both kept by this object, so that every call passes the
+        library the same pointers and it replays its recorded step. The returned logits
+        are overwritten by the next decode: clone them to keep them."""
         tok = self._ids(tokens).reshape(-1)
         if tok.numel() != getattr(self, "_kv_B", tok.numel()):
             raise ValueError(f"decode takes one token per sequence of the last prefill ({self._kv_B}), "
                              f"got {tok.numel()}")
-        out = self.torch.empty((tok.numel(), self.cfg.padded_vocab), dtype=self.torch.float32, device=self.device)
-        self._keep_dec = tok
-        self._check(self.lib.gpt_decode(self.h, C.c_void_p(tok.data_ptr()), C.c_void_p(out.data_ptr())))
-        return out
+        buf = self.decode_tokens(tok.numel())   # without a prefill the library reports the state error
+        if tok.data_ptr() != buf.data_ptr():
+            buf.copy_(tok)
+        self._check(self.lib.gpt_decode(self.h, C.c_void_p(buf.data_ptr()), C.c_void_p(self._dec_out.data_ptr())))
+        return self._dec_out
 
-    def sample(self, logits, temperature: float, top_k: int = 0, uniforms=None):
+    def sample(self, logits, temperature: float, top_k: int = 0, uniforms=None, out=None):
         t = self.torch
         z = logits.to(self.device, t.float32).contiguous()
         B = z.shape[0]
@@ -286,7 +304,10 @@ class GPT(Layout):
             u = uniforms.to(self.device, t.float32).contiguous()
         elif uniforms is not None:
             u = t.as_tensor(np.asarray(uniforms, dtype=np.float32)).to(self.device).contiguous()
-        out = t.empty(B, dtype=t.int32, device=self.device)
+        if out is None:
+            out = t.empty(B, dtype=t.int32, device=self.device)
+        elif out.dtype != t.int32 or out.numel() != B or not out.is_contiguous() or out.device != z.device:
+            raise ValueError("out must be a contiguous int32 device tensor of one token per row")
         self._keep_dec = (z, u)
         self._check(self.lib.gpt_sample(self.h, C.c_void_p(z.data_ptr()), B, float(temperature), int(top_k),
                                         C.c_void_p(u.data_ptr()) if u is not None else None,

@@ -6,26 +6,40 @@
 //
 // Cache layout: per layer [B_max * T_max, 2 * d] in operand type, row b * T_max + t,
 // keys in columns [0, d) and values in [d, 2d), head h at columns h * hd of each.
+#include <cstdlib>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace gpt {
 
-// x[b, :] = wte[tok[b], :] + wpe[pos, :] (NaN for an id outside the table).
+// x[b, :] = wte[tok[b], :] + wpe[pos, :] (NaN for an id outside the table), pos read
+// from device memory and clamped to the table's Tmax rows.
 __global__ void embed_pos_kernel(const float* __restrict__ wte, const float* __restrict__ wpe,
                                  const int32_t* __restrict__ tok, float* __restrict__ x, int B, int d, int Vp,
-                                 int pos) {
+                                 const int* __restrict__ pos_p, int Tmax) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= B * d) return;
   const int b = i / d, c = i % d;
   const int id = tok[b];
+  const int pos = min(max(*pos_p, 0), Tmax - 1);
   x[i] = (id >= 0 && id < Vp) ? wte[(int64_t)id * d + c] + wpe[(int64_t)pos * d + c] : __builtin_nanf("");
 }
 
 hipError_t launch_embed_pos(const float* wte, const float* wpe, const int32_t* tok, float* x, int B, int d, int Vp,
-                            int pos, hipStream_t s) {
+                            const int* pos, int Tmax, hipStream_t s) {
+  if (!pos || Tmax < 1) return hipErrorInvalidValue;
   const int n = B * d;
-  hipLaunchKernelGGL(embed_pos_kernel, dim3((n + 255) / 256), dim3(256), 0, s, wte, wpe, tok, x, B, d, Vp, pos);
+  hipLaunchKernelGGL(embed_pos_kernel, dim3((n + 255) / 256), dim3(256), 0, s, wte, wpe, tok, x, B, d, Vp, pos, Tmax);
+  return hipGetLastError();
+}
+
+__global__ void set_i32_kernel(int* p, int v) {
+  if (threadIdx.x == 0) *p = v;
+}
+
+hipError_t launch_set_i32(int* p, int v, hipStream_t s) {
+  hipLaunchKernelGGL(set_i32_kernel, dim3(1), dim3(64), 0, s, p, v);
   return hipGetLastError();
 }
 
@@ -57,7 +71,8 @@ hipError_t launch_kv_append(const void* qkv, bool bf16_ops, void* cache, int B, 
   return hipGetLastError();
 }
 
-// One query per (sequence, head) against keys 0 .. len-1:
+// One query per (sequence, head) against keys 0 .. len-1, len = *pos + 1 read from
+// device memory (clamped to [1, Tmax]):
 // s_j = q . k_j / sqrt(hd), p = softmax(s), o = sum_j p_j v_j. One workgroup of 256
 // per (b, h); the scores of all keys sit in LDS (len <= DEC_MAX_T). Keys and values
 // 0 .. len-2 come from the cache; those of the new position len-1 are read from this
@@ -67,10 +82,21 @@ hipError_t launch_kv_append(const void* qkv, bool bf16_ops, void* cache, int B, 
 // key, and the per-slot partial vectors are added in slot order; otherwise each
 // wavefront takes every fourth key with a lane per column.
 constexpr int DEC_MAX_T = 8192;
+
+// GPT_DECODE_ATTN_VEC=0: the bf16 decode attention on attn_decode_kernel (for comparisons).
+static bool decode_attn_vec() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = std::getenv("GPT_DECODE_ATTN_VEC");
+    on = (e && e[0] == '0') ? 0 : 1;
+  }
+  return on == 1;
+}
 template <typename T>
 __global__ __launch_bounds__(256) void attn_decode_kernel(const T* __restrict__ qkv, T* __restrict__ cache,
-                                                          T* __restrict__ out, int H, int hd, int Tmax, int len,
-                                                          float scale) {
+                                                          T* __restrict__ out, int H, int hd, int Tmax,
+                                                          const int* __restrict__ pos, float scale) {
+  const int len = min(max(*pos + 1, 1), Tmax);
   __shared__ float sc[DEC_MAX_T];
   __shared__ float qs[64];
   __shared__ float red[4][64];
@@ -159,16 +185,138 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const T* __restrict__ 
   }
 }
 
+// The bf16 kernel for head_dim HD (32 or 64), with every global load of a workgroup
+// issued before the first reduction: each thread's value chunks of up to NVP keys of
+// its slot, and the key rows of two scores per thread. The arithmetic and its order
+// are those of attn_decode_kernel (dot products over 8-column chunks in column order;
+// value sums per slot in key order, then over the slots in order), so the output is
+// the same.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_decode_vec_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ cache,
+                                                              bf16* __restrict__ out, int H, int Tmax,
+                                                              const int* __restrict__ pos, float scale) {
+  constexpr int NCH = HD / 8, SLOTS = 256 / NCH, NVP = 512 / SLOTS;
+  __shared__ float sc[DEC_MAX_T];
+  __shared__ float red[4];
+  __shared__ float vred[SLOTS * HD];
+  const int len = min(max(*pos + 1, 1), Tmax);
+  const int b = blockIdx.x / H, h = blockIdx.x % H;
+  const int d = H * HD;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int ch = tid % NCH, slot = tid / NCH;
+  const bf16* qrow = qkv + (int64_t)b * 3 * d + h * HD;
+  bf16* kb = cache + (int64_t)b * Tmax * 2 * d + h * HD;
+  auto krow = [&](int j) { return j == len - 1 ? qrow + d : kb + (int64_t)j * 2 * d; };
+  auto vrow = [&](int j) { return j == len - 1 ? qrow + 2 * d : kb + d + (int64_t)j * 2 * d; };
+  bf16x8 vp[NVP];
+#pragma unroll
+  for (int i = 0; i < NVP; i++) {
+    const int j = slot + SLOTS * i;
+    vp[i] = j < len ? *(const bf16x8*)(vrow(j) + ch * 8) : (bf16x8){};
+  }
+  bf16x8 qv[NCH], k0[NCH], k1[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; c++) qv[c] = *(const bf16x8*)(qrow + c * 8);
+  const int j0 = tid, j1 = tid + 256;
+#pragma unroll
+  for (int c = 0; c < NCH; c++) {
+    k0[c] = j0 < len ? *(const bf16x8*)(krow(j0) + c * 8) : (bf16x8){};
+    k1[c] = j1 < len ? *(const bf16x8*)(krow(j1) + c * 8) : (bf16x8){};
+  }
+  if (tid < HD) {                                    // this position's key and value into the cache
+    kb[(int64_t)(len - 1) * 2 * d + tid] = qrow[d + tid];
+    kb[(int64_t)(len - 1) * 2 * d + d + tid] = qrow[2 * d + tid];
+  }
+  auto dot = [&](const bf16x8 (&k)[NCH]) {
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; c++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) s += (float)qv[c][e] * (float)k[c][e];
+    return s * scale;
+  };
+  float mx = -INFINITY;
+  if (j0 < len) {
+    const float s = dot(k0);
+    sc[j0] = s;
+    mx = s;
+  }
+  if (j1 < len) {
+    const float s = dot(k1);
+    sc[j1] = s;
+    mx = fmaxf(mx, s);
+  }
+  for (int j = tid + 512; j < len; j += 256) {        // beyond 512 keys: loaded as they come
+    bf16x8 kr[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; c++) kr[c] = *(const bf16x8*)(krow(j) + c * 8);
+    const float s = dot(kr);
+    sc[j] = s;
+    mx = fmaxf(mx, s);
+  }
+  mx = wave_max(mx);
+  if (lane == 0) red[w] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float sum = 0.f;
+  for (int j = tid; j < len; j += 256) {
+    const float p = __expf(sc[j] - mx);
+    sc[j] = p;
+    sum += p;
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) red[w] = sum;
+  __syncthreads();
+  sum = (red[0] + red[1]) + (red[2] + red[3]);
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) acc[e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < NVP; i++) {
+    const int j = slot + SLOTS * i;
+    if (j < len) {
+      const float pj = sc[j];
+#pragma unroll
+      for (int e = 0; e < 8; e++) acc[e] += pj * (float)vp[i][e];
+    }
+  }
+  for (int j = slot + SLOTS * NVP; j < len; j += SLOTS) {
+    const bf16x8 v = *(const bf16x8*)(vrow(j) + ch * 8);
+    const float pj = sc[j];
+#pragma unroll
+    for (int e = 0; e < 8; e++) acc[e] += pj * (float)v[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; e++) vred[slot * HD + ch * 8 + e] = acc[e];
+  __syncthreads();
+  if (tid < HD) {
+    float t = 0.f;
+    for (int q = 0; q < SLOTS; q++) t += vred[q * HD + tid];
+    out[(int64_t)b * d + h * HD + tid] = from_f32<bf16>(t / sum);
+  }
+}
+
 hipError_t launch_attn_decode(const void* qkv, void* cache, void* out, bool bf16_ops, int B, int H, int hd,
-                              int Tmax, int len, hipStream_t s) {
-  if (hd <= 0 || hd > 64 || len < 1 || len > Tmax || len > DEC_MAX_T) return hipErrorInvalidValue;
+                              int Tmax, const int* pos, hipStream_t s) {
+  if (hd <= 0 || hd > 64 || !pos || Tmax < 1 || Tmax > DEC_MAX_T) return hipErrorInvalidValue;
   const float scale = 1.0f / sqrtf((float)hd);
+  const bool aligned = ((uintptr_t)qkv | (uintptr_t)cache) % 16 == 0;
+  if (bf16_ops && aligned && (hd == 64 || hd == 32) && decode_attn_vec()) {
+    if (hd == 64)
+      hipLaunchKernelGGL(attn_decode_vec_kernel<64>, dim3(B * H), dim3(256), 0, s, (const bf16*)qkv, (bf16*)cache,
+                         (bf16*)out, H, Tmax, pos, scale);
+    else
+      hipLaunchKernelGGL(attn_decode_vec_kernel<32>, dim3(B * H), dim3(256), 0, s, (const bf16*)qkv, (bf16*)cache,
+                         (bf16*)out, H, Tmax, pos, scale);
+    return hipGetLastError();
+  }
   if (bf16_ops)
     hipLaunchKernelGGL(attn_decode_kernel<bf16>, dim3(B * H), dim3(256), 0, s, (const bf16*)qkv, (bf16*)cache,
-                       (bf16*)out, H, hd, Tmax, len, scale);
+                       (bf16*)out, H, hd, Tmax, pos, scale);
   else
     hipLaunchKernelGGL(attn_decode_kernel<float>, dim3(B * H), dim3(256), 0, s, (const float*)qkv,
-                       (float*)cache, (float*)out, H, hd, Tmax, len, scale);
+                       (float*)cache, (float*)out, H, hd, Tmax, pos, scale);
   return hipGetLastError();
 }
 

@@ -189,6 +189,12 @@ struct GemmArgs {
   // two tiles of a CU reach their epilogues apart)
   int stagger_lo = 0, stagger_hi = 0, stagger_iters = 0;
   int krot = 0;        // rotate each tile's k-slice order by its position in the launch
+  int* bump = nullptr; // few-rows kernel: block 0 adds one to *bump (no block reads it)
+  // few-rows kernel with the normalization fused in front: A = norm(nx) (rows of K
+  // fp32, gain ng and shift nb for the LayerNorm), computed into LDS
+  const float* nx = nullptr;
+  const float* ng = nullptr;
+  const float* nb = nullptr;
 };
 
 // Epilogues that add a residual (with or without dropout on the branch) and those with a bias.
@@ -1330,23 +1336,28 @@ static int num_cus();
 
 // ----------------------------------------------------------------------------- few output rows
 // M <= 16 (one token per sequence while decoding): the weight operand streams from
-// HBM once and nothing is worth staging. One workgroup of 16 wavefronts per 16 output
-// columns; wavefront w multiplies every 16th 32-wide k-slice with fragments read
-// straight from global memory (A: the M rows, zero past M; B: 16 weight rows), and the
-// 16 partial tiles are added in LDS in a fixed order before the element epilogue.
-template <int EPI>
-__global__ __launch_bounds__(1024) void gemm_skinny_kernel(GemmArgs p) {
-  __shared__ f32x4 part[16][64];
+// HBM once and nothing is worth staging. One workgroup of NW wavefronts per 16 output
+// columns; wavefront w multiplies every NW-th 32-wide k-slice with fragments read
+// straight from global memory (A: the M rows, zero past M; B: 16 weight rows), and
+// the NW partial tiles are added in LDS in a fixed order before the element epilogue
+// (bias, residual, GELU, store). NW = 16 for outputs of up to 4 column groups per CU;
+// wider outputs (the lm_head) take NW = 4, so that more workgroups are resident per CU
+// (21.4 against 23.2 us for the GPT-2 lm_head at 12 rows). Measured and dropped: every
+// k-slice of a wavefront loaded before its first MFMA (+15 us per decode step).
+template <int EPI, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(GemmArgs p) {
+  __shared__ f32x4 part[NW][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.x * 16;
+  if (p.bump && blockIdx.x == 0 && threadIdx.x == 0) *p.bump += 1;
   const bool arow = r < p.M, brow = n0 + r < p.N;
   const bf16* ap = (const bf16*)p.A + (int64_t)(arow ? r : 0) * p.lda + g * 8;
   const bf16* bp = (const bf16*)p.B + (int64_t)(brow ? n0 + r : 0) * p.ldb + g * 8;
   f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
   const int nk = p.K / 32;
 #pragma unroll 4
-  for (int kt = w; kt < nk; kt += 16) {
+  for (int kt = w; kt < nk; kt += NW) {
     const bf16x8 af = arow ? *(const bf16x8*)(ap + kt * 32) : (bf16x8){};
     const bf16x8 bfr = brow ? *(const bf16x8*)(bp + kt * 32) : (bf16x8){};
     acc = Mfma<bf16>::mma(af, bfr, acc);
@@ -1356,7 +1367,7 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(GemmArgs p) {
   if (w == 0) {
     f32x4 t = part[0][lane];
 #pragma unroll
-    for (int q = 1; q < 16; q++) t += part[q][lane];
+    for (int q = 1; q < NW; q++) t += part[q][lane];
     const int col = n0 + r;                           // lane holds rows 4g + i of column r
     if (col < p.N) {
       const float bias = epi_bias<EPI>(p, col);
@@ -1367,11 +1378,142 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(GemmArgs p) {
   }
 }
 
-static hipError_t skinny_epi(const GemmArgs& a, int epi, hipStream_t s) {
+// The same product with A = norm(x) computed by every workgroup from the M rows of x
+// (fp32, K columns): NORM 1 is the LayerNorm (x - mean) / sqrt(var + 1e-5) * g + b,
+// NORM 2 the weightless RMSNorm x / sqrt(mean(x^2) + 1e-5), each as the row kernels
+// compute it, rounded to bf16. A wavefront's weight fragments are loaded before the
+// normalization, so the weight stream is in flight while the rows are normalized into
+// LDS (wavefront w takes row w); the k-loop then reads A from LDS. K <= 16 * 32 * SKN_S.
+constexpr int SKN_S = 2;
+constexpr int SKN_MAXK = 16 * 32 * SKN_S;
+template <int EPI, int NORM>
+__global__ __launch_bounds__(1024) void gemm_skinny_norm_kernel(GemmArgs p) {
+  __shared__ f32x4 part[16][64];
+  __shared__ __attribute__((aligned(16))) bf16 an[16 * (SKN_MAXK + 8)];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  const int K = p.K, ka = K + 8;                     // LDS row stride: 16 bytes of padding
+  if (p.bump && blockIdx.x == 0 && threadIdx.x == 0) *p.bump += 1;
+  const bool brow = n0 + r < p.N;
+  const bf16* bp = (const bf16*)p.B + (int64_t)(brow ? n0 + r : 0) * p.ldb + g * 8;
+  const int nk = K / 32;
+  bf16x8 bfr[SKN_S];
+#pragma unroll
+  for (int i = 0; i < SKN_S; i++) {
+    const int kt = w + 16 * i;
+    bfr[i] = brow && kt < nk ? *(const bf16x8*)(bp + kt * 32) : (bf16x8){};
+  }
+  {
+    bf16* arow = an + w * ka;
+    const int K4 = K >> 2;
+    if (w < p.M) {
+      const f32x4* xr = (const f32x4*)(p.nx + (int64_t)w * K);
+      f32x4 xv[SKN_MAXK / 256];
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < SKN_MAXK / 256; j++) {
+        const int c4 = j * 64 + lane;
+        xv[j] = c4 < K4 ? xr[c4] : (f32x4){0.f, 0.f, 0.f, 0.f};
+        if constexpr (NORM == 1) s += (xv[j][0] + xv[j][1]) + (xv[j][2] + xv[j][3]);
+        else s += (xv[j][0] * xv[j][0] + xv[j][1] * xv[j][1]) + (xv[j][2] * xv[j][2] + xv[j][3] * xv[j][3]);
+      }
+      float mu = 0.f, rs;
+      if constexpr (NORM == 1) {
+        mu = wave_sum(s) / K;
+        float v = 0.f;
+#pragma unroll
+        for (int j = 0; j < SKN_MAXK / 256; j++)
+          if (j * 64 + lane < K4)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+              const float t = xv[j][e] - mu;
+              v += t * t;
+            }
+        rs = 1.0f / sqrtf(wave_sum(v) / K + 1e-5f);
+      } else {
+        rs = 1.0f / sqrtf(wave_sum(s) / K + 1e-5f);
+      }
+#pragma unroll
+      for (int j = 0; j < SKN_MAXK / 256; j++) {
+        const int c4 = j * 64 + lane;
+        if (c4 >= K4) continue;
+        bf16x4 ob;
+        if constexpr (NORM == 1) {
+          const f32x4 gv = ((const f32x4*)p.ng)[c4], bv = ((const f32x4*)p.nb)[c4];
+#pragma unroll
+          for (int e = 0; e < 4; e++) ob[e] = (bf16)((xv[j][e] - mu) * rs * gv[e] + bv[e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; e++) ob[e] = (bf16)(xv[j][e] * rs);
+        }
+        *(bf16x4*)(arow + 4 * c4) = ob;
+      }
+    } else {                                          // rows past M: zeros
+      for (int c4 = lane; c4 < K4; c4 += 64) *(bf16x4*)(arow + 4 * c4) = (bf16x4){};
+    }
+  }
+  __syncthreads();
+  f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < SKN_S; i++) {
+    const int kt = w + 16 * i;
+    if (kt < nk) acc = Mfma<bf16>::mma(*(const bf16x8*)(an + r * ka + kt * 32 + g * 8), bfr[i], acc);
+  }
+  part[w][lane] = acc;
+  __syncthreads();
+  if (w == 0) {
+    f32x4 t = part[0][lane];
+#pragma unroll
+    for (int q = 1; q < 16; q++) t += part[q][lane];
+    const int col = n0 + r;
+    if (col < p.N) {
+      const float bias = epi_bias<EPI>(p, col);
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        if (4 * g + i < p.M) epi_store<bf16, EPI>(p, 4 * g + i, col, t[i], bias);
+    }
+  }
+}
+
+__global__ void bump_kernel(int* c) {
+  if (threadIdx.x == 0) *c += 1;
+}
+
+template <int NORM>
+static hipError_t skinny_norm_epi(const GemmArgs& a, int epi, hipStream_t s) {
   const dim3 grid((a.N + 15) / 16);
   switch (epi) {
 #define GPT_SKINNY_CASE(E) \
-  case E: hipLaunchKernelGGL((gemm_skinny_kernel<E>), grid, dim3(1024), 0, s, a); break;
+  case E: hipLaunchKernelGGL((gemm_skinny_norm_kernel<E, NORM>), grid, dim3(1024), 0, s, a); break;
+    GPT_SKINNY_CASE(EPI_BIAS)
+    GPT_SKINNY_CASE(EPI_BIAS_GELU)
+    GPT_SKINNY_CASE(EPI_BIAS_RELU)
+#undef GPT_SKINNY_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// GPT_SKINNY_NW4=0: every few-rows product on 16-wavefront workgroups (for comparisons).
+static bool skinny_nw4() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = std::getenv("GPT_SKINNY_NW4");
+    on = (e && e[0] == '0') ? 0 : 1;
+  }
+  return on == 1;
+}
+
+static hipError_t skinny_epi(const GemmArgs& a, int epi, hipStream_t s) {
+  const dim3 grid((a.N + 15) / 16);
+  const bool nw4 = skinny_nw4() && (int)grid.x > 4 * num_cus();
+  switch (epi) {
+#define GPT_SKINNY_CASE(E)                                                                  \
+  case E:                                                                                   \
+    if (nw4) hipLaunchKernelGGL((gemm_skinny_kernel<E, 4>), grid, dim3(256), 0, s, a);     \
+    else hipLaunchKernelGGL((gemm_skinny_kernel<E, 16>), grid, dim3(1024), 0, s, a);       \
+    break;
     GPT_SKINNY_CASE(EPI_STORE)
     GPT_SKINNY_CASE(EPI_BIAS)
     GPT_SKINNY_CASE(EPI_BIAS_RESID)
@@ -1477,8 +1619,28 @@ static int gemm_krot() {
   return on;
 }
 
+// few rows, both operands k-contiguous, aligned 16-byte fragments
+static bool skinny_ok(const GemmDesc& d, bool bf16_operands) {
+  const int vw = bf16_operands ? 8 : 4;
+  auto vec_ok = [&](const void* ptr, int64_t ld) { return (ld % vw == 0) && ((uintptr_t)ptr % 16 == 0); };
+  return bf16_operands && d.M >= 1 && d.M <= 16 && d.a_kc && d.b_kc && d.K % 32 == 0 && d.K > 0 &&
+         (d.norm || vec_ok(d.A, d.lda)) && vec_ok(d.B, d.ldb) &&
+         (d.epi == EPI_STORE || d.epi == EPI_BIAS || d.epi == EPI_BIAS_RESID || d.epi == EPI_BIAS_GELU ||
+          d.epi == EPI_BIAS_RELU || d.epi == EPI_F32);
+}
+
+bool gemm_norm_fusable(const GemmDesc& d, bool bf16_operands) {
+  return (d.norm == 1 || d.norm == 2) && skinny_ok(d, bf16_operands) && d.K <= SKN_MAXK && d.K % 4 == 0 &&
+         (d.epi == EPI_BIAS || d.epi == EPI_BIAS_GELU || d.epi == EPI_BIAS_RELU) && d.norm_x &&
+         (uintptr_t)d.norm_x % 16 == 0 &&
+         (d.norm == 2 || (d.norm_g && d.norm_b && ((uintptr_t)d.norm_g | (uintptr_t)d.norm_b) % 16 == 0));
+}
+
 hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
-  if (d.M <= 0 || d.N <= 0) return hipSuccess;
+  if (d.M <= 0 || d.N <= 0) {
+    if (d.bump) hipLaunchKernelGGL(bump_kernel, dim3(1), dim3(64), 0, s, d.bump);
+    return hipGetLastError();
+  }
   if (d.colsum && gemm_colsum_rows(d, bf16_operands) == 0) return hipErrorInvalidValue;
   GemmArgs a;
   a.colsum = d.colsum;
@@ -1499,11 +1661,25 @@ hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
     if (d.epi == EPI_ACC && d.split_ws) cv = cv && (d.N % 4 == 0) && ((uintptr_t)d.split_ws % 16 == 0);
     a.c_vec = cv;
   }
+  if (d.norm) {
+    if (!gemm_norm_fusable(d, bf16_operands)) return hipErrorInvalidValue;
+    a.bump = d.bump;
+    a.nx = d.norm_x; a.ng = d.norm_g; a.nb = d.norm_b;
+    return d.norm == 1 ? skinny_norm_epi<1>(a, d.epi, s) : skinny_norm_epi<2>(a, d.epi, s);
+  }
   // few rows, both operands k-contiguous, aligned 16-byte fragments
-  if (bf16_operands && d.M <= 16 && d.a_kc && d.b_kc && d.K % 32 == 0 && a.a_vec && a.b_vec &&
-      (d.epi == EPI_STORE || d.epi == EPI_BIAS || d.epi == EPI_BIAS_RESID || d.epi == EPI_BIAS_GELU || d.epi == EPI_BIAS_RELU ||
-       d.epi == EPI_F32))
+  if (skinny_ok(d, bf16_operands)) {
+    a.bump = d.bump;
     return skinny_epi(a, d.epi, s);
+  }
+  if (d.bump) {
+    GemmDesc e = d;
+    e.bump = nullptr;
+    const hipError_t r = launch_gemm(e, bf16_operands, s);
+    if (r != hipSuccess) return r;
+    hipLaunchKernelGGL(bump_kernel, dim3(1), dim3(64), 0, s, d.bump);
+    return hipGetLastError();
+  }
   const bool pipelined = pipelined_ok(d, bf16_operands);
   const int TBM = pipelined ? 256 : BM, TBN = pipelined ? 256 : BN;
   const int tiles = ((d.M + TBM - 1) / TBM) * ((d.N + TBN - 1) / TBN);

@@ -63,9 +63,23 @@ struct GemmDesc {
   // EPI_BIAS_RESID_DROP only: the branch output's mask (rows m and columns n of C)
   DropArgs drop;
   uint32_t drop_site;
+  // optional: a device counter the call adds one to once its product is written
+  // (the decode step's cache position); in the same launch when the product takes
+  // the few-rows kernel, else by a one-thread launch after it
+  int* bump;
+  // optional (norm 1: LayerNorm with gain norm_g and shift norm_b, eps 1e-5; norm 2:
+  // weightless RMSNorm): A is not read; the product takes A = norm(norm_x) over
+  // rows of K fp32, computed inside the launch. Only where gemm_norm_fusable holds.
+  int norm;
+  const float* norm_x;
+  const float* norm_g;
+  const float* norm_b;
 };
 
 hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s);
+// Whether launch_gemm takes `d` with its normalization fused (bf16 operands, M <= 16,
+// K <= 1024, a bias epilogue); otherwise the caller normalizes A itself.
+bool gemm_norm_fusable(const GemmDesc& d, bool bf16_operands);
 // Partial rows the fused column sum of `d` writes, or 0 when the kernel chosen for
 // `d` cannot fuse it (then colsum must be NULL and the caller sums C itself).
 int gemm_colsum_rows(const GemmDesc& d, bool bf16_operands);
@@ -188,18 +202,22 @@ hipError_t launch_embed_bwd(const float* dx0, const int32_t* tok, float* dwte, f
                             int B, int T, int d, int Vp, EmbedBwdScratch scr, hipStream_t s);
 
 // ---- inference with a key/value cache (decode.hip)
-// x[b, :] = wte[tok[b], :] + wpe[pos, :] for B single-token rows.
+// x[b, :] = wte[tok[b], :] + wpe[pos, :] for B single-token rows; pos is read from
+// device memory when the kernel runs (clamped to [0, Tmax)).
 hipError_t launch_embed_pos(const float* wte, const float* wpe, const int32_t* tok, float* x, int B, int d, int Vp,
-                            int pos, hipStream_t s);
+                            const int* pos, int Tmax, hipStream_t s);
+// *p = v, as a kernel (stream-ordered; recordable in a graph, unlike a memset).
+hipError_t launch_set_i32(int* p, int v, hipStream_t s);
 // Copies the keys and values (columns d .. 3d) of qkv [B*T, 3d] into cache rows
 // b * Tmax + pos0 + t ([B_max * Tmax, 2d], operand type). pos0 + T <= Tmax.
 hipError_t launch_kv_append(const void* qkv, bool bf16_ops, void* cache, int B, int T, int Tmax, int pos0, int d,
                             hipStream_t s);
 // Causal attention of one new query per sequence (q, k, v in qkv [B, 3d]) against
-// positions 0 .. len-1: 0 .. len-2 from the cache, len-1 from qkv, whose k and v the
-// call also stores into cache position len-1. out [B, d]. len <= 8192.
+// positions 0 .. len-1, len = *pos + 1 read from device memory when the kernel runs
+// (clamped to [1, Tmax]): 0 .. len-2 from the cache, len-1 from qkv, whose k and v the
+// call also stores into cache position len-1. out [B, d]. Tmax <= 8192.
 hipError_t launch_attn_decode(const void* qkv, void* cache, void* out, bool bf16_ops, int B, int H, int hd,
-                              int Tmax, int len, hipStream_t s);
+                              int Tmax, const int* pos, hipStream_t s);
 // One token per row of fp32 logits [B, ld] over V columns: the argmax (lowest index
 // on ties) when temperature <= 0, else a draw with uniform[b] from the softmax of
 // logits / temperature over the logits >= the top_k-th largest (all when top_k <= 0

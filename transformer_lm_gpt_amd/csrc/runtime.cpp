@@ -87,6 +87,7 @@ struct gpt_model {
   // GPT_F_KV_CACHE: keys and values of every layer, [B_max * T_max, 2d] operand type each
   Slice kv;
   size_t kv_stride = 0;   // bytes per layer
+  Slice kvpos;            // the next decode position (int32), on the device: the decode kernels read it
   size_t layer_stride_du = 0, layer_stride_dqkv = 0, resid_stride = 0;   // bytes
   std::vector<WgradProblem> wprobs;   // host copy of the grouped weight-gradient table
   int wtiles = 0;
@@ -111,6 +112,15 @@ struct gpt_model {
   uint32_t drop_call = 0;
   DropArgs drop_fwd{};
   int kv_len = 0, kv_B = 0;   // cached positions per sequence and sequences, after gpt_prefill
+  // the decode step recorded as a graph, with the pointers and batch it was recorded for
+  struct {
+    hipStream_t cap = nullptr;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    const int32_t* tok = nullptr;
+    const float* out = nullptr;
+    int B = 0;
+  } dg;
   // GPT_F_MICROGPT: weightless RMSNorm, ReLU, no biases, an lm_head of its own
   bool micro = false;
   std::string head = "wte";   // the tensor the logits are taken against
@@ -339,6 +349,7 @@ void plan(gpt_model* h) {
   h->dxm = w.take(!h->bf16 && h->cfg.dropout > 0.f ? M * d * fb : 0);
   h->kv_stride = (h->cfg.flags & GPT_F_KV_CACHE) ? M * 2 * d * ob : 0;
   h->kv = w.take((size_t)L * h->kv_stride);
+  h->kvpos = w.take((h->cfg.flags & GPT_F_KV_CACHE) ? 4 : 0);
   h->attnD = w.take(bht * fb);
   const size_t ln_blk = (M + LN_BWD_ROWS - 1) / LN_BWD_ROWS;
   const size_t cs_blk = (M + COLSUM_ROWS - 1) / COLSUM_ROWS;
@@ -709,6 +720,9 @@ void gpt_destroy(gpt_model* h) {
     hipEventDestroy(e.first);
     hipEventDestroy(e.second);
   }
+  if (h->dg.exec) (void)hipGraphExecDestroy(h->dg.exec);
+  if (h->dg.graph) (void)hipGraphDestroy(h->dg.graph);
+  if (h->dg.cap) (void)hipStreamDestroy(h->dg.cap);
   delete h;
 }
 
@@ -750,6 +764,13 @@ int gpt_bind(gpt_model* h, const gpt_buffers* bufs, void* hip_stream) {
   h->buf = *bufs;
   h->stream = (hipStream_t)hip_stream;
   h->bound = true;
+  // a recorded decode step holds the old buffers' addresses
+  if (h->dg.exec) (void)hipGraphExecDestroy(h->dg.exec);
+  if (h->dg.graph) (void)hipGraphDestroy(h->dg.graph);
+  h->dg.exec = nullptr;
+  h->dg.graph = nullptr;
+  h->dg.tok = nullptr;
+  h->dg.out = nullptr;
   h->tables_ready = false;
   h->fwd_pending = false;
   h->grads_fresh = true;
@@ -844,42 +865,72 @@ int gpt_prefill(gpt_model* h, const int32_t* d_tokens, int32_t B, int32_t T, flo
   for (int l = 0; l < h->L; l++)
     RUN("decode", "kv_append",
         launch_kv_append(act(h, h->layers[l].qkv), h->bf16, kv_slot(h, l), B, T, h->Tmax, 0, h->d, h->stream));
+  RUN("decode", "kv_position", launch_set_i32(ws<int>(h, h->kvpos), T, h->stream));
   h->kv_len = T;
   h->kv_B = B;
   return GPT_OK;
 }
 
-int gpt_decode(gpt_model* h, const int32_t* d_tokens, float* d_logits) {
-  int rc = check_usable(h);
-  if (rc) return rc;
-  if (!(h->cfg.flags & GPT_F_KV_CACHE)) return fail(h, GPT_E_UNSUPPORTED, "create the model with GPT_F_KV_CACHE to decode");
-  if (!d_tokens || !d_logits) return fail(h, GPT_E_INVAL, "NULL pointer");
-  if (h->kv_len < 1) return fail(h, GPT_E_STATE, "gpt_decode needs a preceding gpt_prefill");
-  if (h->kv_len >= h->Tmax) return fail(h, GPT_E_SEQ_TOO_LONG, "the cache holds block_size positions already");
-  const int B = h->kv_B, d = h->d, pos = h->kv_len;
+}  // extern "C"
+
+namespace {
+
+// The launches of one decode step on h->stream: token ids read from d_tokens, fp32
+// logits written to d_logits [B, Vp], the position taken from (and, by the lm_head
+// launch, advanced in) the device counter kvpos. Nothing here depends on the host's
+// copy of the position, so a recording of these launches serves every step.
+// GPT_DECODE_FUSE_NORM=0: the decode step's normalizations as launches of their own
+// (for comparisons).
+bool decode_fuse_norm() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = std::getenv("GPT_DECODE_FUSE_NORM");
+    on = (e && e[0] == '0') ? 0 : 1;
+  }
+  return on == 1;
+}
+
+int decode_launches(gpt_model* h, const int32_t* d_tokens, float* d_logits) {
+  const int B = h->kv_B, d = h->d;
   const bool bf = h->bf16;
   hipStream_t s = h->stream;
-  h->fwd_pending = false;
-  if ((rc = copy_ids(h, d_tokens, h->tokens, B))) return rc;
-  if ((rc = check_ids(h, h->tokens, B))) return rc;
+  int* pos = ws<int>(h, h->kvpos);
+  int rc;
+  if (h->cfg.flags & GPT_F_DEBUG_CHECKS)
+    RUN("check", "check_ids", launch_check_ids(d_tokens, B, h->V, ws<OptState>(h, h->opt), s));
   // B single-token rows through the layer-0 activation slots
   const LayerAct& a = h->layers[0];
   float* x = act<float>(h, a.x);
   float* xmid = act<float>(h, a.xmid);
-  RUN("decode", "embed", launch_embed_pos(P(h, "wte"), P(h, "wpe"), act<int32_t>(h, h->tokens), x, B, d, h->Vp, pos, s));
+  RUN("decode", "embed", launch_embed_pos(P(h, "wte"), P(h, "wpe"), d_tokens, x, B, d, h->Vp, pos, h->Tmax, s));
+  // The normalization in front of the qkv and MLP-up products runs inside their
+  // launch where the few-rows kernel allows it (its output is not kept: nothing
+  // reads it after a decode step), else as a launch of its own.
+  auto normed_gemm = [&](const float* xin, const std::string& ln, const Slice& y, const Slice& mean,
+                         const Slice& rstd, GemmDesc g, const char* what) -> int {
+    g.norm = h->micro ? 2 : 1;
+    g.norm_x = xin;
+    g.norm_g = h->micro ? nullptr : P(h, ln + ".g");
+    g.norm_b = h->micro ? nullptr : P(h, ln + ".b");
+    if (!decode_fuse_norm() || !gemm_norm_fusable(g, bf)) {
+      g.norm = 0;
+      int r;
+      if ((r = norm_fwd(h, xin, ln, act(h, y), act<float>(h, mean), act<float>(h, rstd), B))) return r;
+    }
+    RUN("decode", what, gemm(h, g, bf));
+    return GPT_OK;
+  };
   for (int l = 0; l < h->L; l++) {
     const std::string p = "h" + std::to_string(l) + ".";
-    if ((rc = norm_fwd(h, x, p + "ln1", act(h, a.ln1), act<float>(h, a.ln1_mean), act<float>(h, a.ln1_rstd), B)))
-      return rc;
     {
       GemmDesc g = gemm_desc(act(h, a.ln1), d, true, Wop(h, p + "attn.w"), d, true, act(h, a.qkv), 3 * d, B, 3 * d, d,
                              EPI_BIAS);
       g.bias = bias_of(h, p + "attn.b");
-      RUN("decode", "qkv", gemm(h, g, bf));
+      if ((rc = normed_gemm(x, p + "ln1", a.ln1, a.ln1_mean, a.ln1_rstd, g, "qkv"))) return rc;
     }
     // the attention stores this position's keys and values into the cache itself
     RUN("decode", "attn",
-        launch_attn_decode(act(h, a.qkv), kv_slot(h, l), act(h, a.att), bf, B, h->H, h->hd, h->Tmax, pos + 1, s));
+        launch_attn_decode(act(h, a.qkv), kv_slot(h, l), act(h, a.att), bf, B, h->H, h->hd, h->Tmax, pos, s));
     {
       GemmDesc g = gemm_desc(act(h, a.att), d, true, Wop(h, p + "proj.w"), d, true, xmid, d, B, d, d, EPI_BIAS_RESID);
       g.bias = bias_of(h, p + "proj.b");
@@ -887,15 +938,13 @@ int gpt_decode(gpt_model* h, const int32_t* d_tokens, float* d_logits) {
       g.ldr = d;
       RUN("decode", "proj", gemm(h, g, bf));
     }
-    if ((rc = norm_fwd(h, xmid, p + "ln2", act(h, a.ln2), act<float>(h, a.ln2_mean), act<float>(h, a.ln2_rstd), B)))
-      return rc;
     {
       GemmDesc g = gemm_desc(act(h, a.ln2), d, true, Wop(h, p + "fc.w"), d, true, act(h, a.h), 4 * d, B, 4 * d, d,
                              h->micro ? EPI_BIAS_RELU : EPI_BIAS_GELU);
       g.bias = bias_of(h, p + "fc.b");
       g.aux = act(h, a.u);
       g.ldaux = 4 * d;
-      RUN("decode", "fc", gemm(h, g, bf));
+      if ((rc = normed_gemm(xmid, p + "ln2", a.ln2, a.ln2_mean, a.ln2_rstd, g, "fc"))) return rc;
     }
     {
       GemmDesc g = gemm_desc(act(h, a.h), 4 * d, true, Wop(h, p + "fcproj.w"), 4 * d, true, x, d, B, d, 4 * d,
@@ -909,12 +958,90 @@ int gpt_decode(gpt_model* h, const int32_t* d_tokens, float* d_logits) {
   if ((rc = norm_fwd(h, x, "lnf", act(h, h->lnf), act<float>(h, h->lnf_mean), act<float>(h, h->lnf_rstd), B)))
     return rc;
   {
-    GemmDesc g = gemm_desc(act(h, h->lnf), d, true, Wop(h, h->head), d, true, act(h, h->logits), h->ldz, B, h->Vp, d,
-                           EPI_STORE);
+    // fp32 logits straight into the caller's rows (the fp32 accumulators, not a
+    // rounded operand-type copy); the same launch advances the position
+    GemmDesc g = gemm_desc(act(h, h->lnf), d, true, Wop(h, h->head), d, true, d_logits, h->Vp, B, h->Vp, d,
+                           bf ? EPI_F32 : EPI_STORE);
+    g.bump = pos;
     RUN("decode", "lm_head", gemm(h, g, bf));
   }
-  RUN("copy", "logits_to_f32", launch_rows_to_f32(act(h, h->logits), bf, h->ldz, B, h->Vp, d_logits, s));
-  h->kv_len = pos + 1;
+  return GPT_OK;
+}
+
+// GPT_DECODE_GRAPH=0: every decode step launched one kernel at a time (for comparisons).
+bool decode_graph_on() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = std::getenv("GPT_DECODE_GRAPH");
+    on = (e && e[0] == '0') ? 0 : 1;
+  }
+  return on == 1;
+}
+
+void drop_decode_graph(gpt_model* h) {
+  if (h->dg.exec) (void)hipGraphExecDestroy(h->dg.exec);
+  if (h->dg.graph) (void)hipGraphDestroy(h->dg.graph);
+  h->dg.exec = nullptr;
+  h->dg.graph = nullptr;
+}
+
+// Records decode_launches on the library's own capture stream (the caller's stream
+// may be the null stream, which cannot be captured) and instantiates the graph.
+int record_decode_graph(gpt_model* h, const int32_t* d_tokens, float* d_logits) {
+  int rc;
+  if (!h->dg.cap && (rc = hip_check(h, hipStreamCreateWithFlags(&h->dg.cap, hipStreamNonBlocking),
+                                    "decode graph stream")))
+    return rc;
+  if ((rc = hip_check(h, hipStreamBeginCapture(h->dg.cap, hipStreamCaptureModeThreadLocal), "decode graph capture")))
+    return rc;
+  hipStream_t user = h->stream;
+  h->stream = h->dg.cap;
+  rc = decode_launches(h, d_tokens, d_logits);
+  h->stream = user;
+  hipGraph_t g = nullptr;
+  const hipError_t e = hipStreamEndCapture(h->dg.cap, &g);
+  if (rc != GPT_OK) {
+    if (g) (void)hipGraphDestroy(g);
+    return rc;
+  }
+  if ((rc = hip_check(h, e, "decode graph capture"))) return rc;
+  hipGraphExec_t x = nullptr;
+  if ((rc = hip_check(h, hipGraphInstantiate(&x, g, nullptr, nullptr, 0), "decode graph instantiate"))) {
+    (void)hipGraphDestroy(g);
+    return rc;
+  }
+  h->dg.graph = g;
+  h->dg.exec = x;
+  return GPT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gpt_decode(gpt_model* h, const int32_t* d_tokens, float* d_logits) {
+  int rc = check_usable(h);
+  if (rc) return rc;
+  if (!(h->cfg.flags & GPT_F_KV_CACHE)) return fail(h, GPT_E_UNSUPPORTED, "create the model with GPT_F_KV_CACHE to decode");
+  if (!d_tokens || !d_logits) return fail(h, GPT_E_INVAL, "NULL pointer");
+  if (h->kv_len < 1) return fail(h, GPT_E_STATE, "gpt_decode needs a preceding gpt_prefill");
+  if (h->kv_len >= h->Tmax) return fail(h, GPT_E_SEQ_TOO_LONG, "the cache holds block_size positions already");
+  h->fwd_pending = false;
+  // A call with the previous call's token and logits pointers and batch replays the
+  // recorded step (recorded at the first such repeat); any other call runs the
+  // launches directly and becomes the new reference.
+  const bool repeat = h->dg.tok == d_tokens && h->dg.out == d_logits && h->dg.B == h->kv_B;
+  if (repeat && decode_graph_on() && !h->timer.on) {
+    if (!h->dg.exec && (rc = record_decode_graph(h, d_tokens, d_logits))) return rc;
+    if ((rc = hip_check(h, hipGraphLaunch(h->dg.exec, h->stream), "decode graph launch"))) return rc;
+  } else {
+    drop_decode_graph(h);
+    h->dg.tok = d_tokens;
+    h->dg.out = d_logits;
+    h->dg.B = h->kv_B;
+    if ((rc = decode_launches(h, d_tokens, d_logits))) return rc;
+  }
+  h->kv_len++;
   return GPT_OK;
 }
 
