@@ -1335,6 +1335,34 @@ void gemm_group_wide_kernel(const WgradProblem* __restrict__ probs, int nprob, i
 static int num_cus();
 
 // ----------------------------------------------------------------------------- few output rows
+// The epilogue inputs of a few-rows tile (lane: column n0 + (lane & 15), rows 4g..4g+3),
+// loaded by the wavefront that stores the tile at the start of the kernel, so that
+// their latency overlaps the weight stream instead of following the reduction.
+template <int EPI>
+struct SkinnyEpiIn {
+  float bias = 0.f;
+  f32x4 res = (f32x4){0.f, 0.f, 0.f, 0.f};
+  __device__ inline void load(const GemmArgs& p, int col, int g) {
+    if (col >= p.N) return;
+    bias = epi_bias<EPI>(p, col);
+    if constexpr (EPI == EPI_BIAS_RESID) {
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        if (4 * g + i < p.M) res[i] = p.resid[(int64_t)(4 * g + i) * p.ldr + col];
+    }
+  }
+  __device__ inline void store(const GemmArgs& p, int col, int g, const f32x4& t) const {
+    if (col >= p.N) return;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int row = 4 * g + i;
+      if (row >= p.M) continue;
+      if constexpr (EPI == EPI_BIAS_RESID) ((float*)p.C)[(int64_t)row * p.ldc + col] = res[i] + (t[i] + bias);
+      else epi_store<bf16, EPI>(p, row, col, t[i], bias);
+    }
+  }
+};
+
 // M <= 16 (one token per sequence while decoding): the weight operand streams from
 // HBM once and nothing is worth staging. One workgroup of NW wavefronts per 16 output
 // columns; wavefront w multiplies every NW-th 32-wide k-slice with fragments read
@@ -1354,6 +1382,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(GemmArgs p) {
   const bool arow = r < p.M, brow = n0 + r < p.N;
   const bf16* ap = (const bf16*)p.A + (int64_t)(arow ? r : 0) * p.lda + g * 8;
   const bf16* bp = (const bf16*)p.B + (int64_t)(brow ? n0 + r : 0) * p.ldb + g * 8;
+  SkinnyEpiIn<EPI> ein;
+  if (w == 0) ein.load(p, n0 + r, g);
   f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
   const int nk = p.K / 32;
 #pragma unroll 4
@@ -1368,13 +1398,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(GemmArgs p) {
     f32x4 t = part[0][lane];
 #pragma unroll
     for (int q = 1; q < NW; q++) t += part[q][lane];
-    const int col = n0 + r;                           // lane holds rows 4g + i of column r
-    if (col < p.N) {
-      const float bias = epi_bias<EPI>(p, col);
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-        if (4 * g + i < p.M) epi_store<bf16, EPI>(p, 4 * g + i, col, t[i], bias);
-    }
+    ein.store(p, n0 + r, g, t);                       // lane holds rows 4g + i of column r
   }
 }
 
@@ -1397,6 +1421,8 @@ __global__ __launch_bounds__(1024) void gemm_skinny_norm_kernel(GemmArgs p) {
   if (p.bump && blockIdx.x == 0 && threadIdx.x == 0) *p.bump += 1;
   const bool brow = n0 + r < p.N;
   const bf16* bp = (const bf16*)p.B + (int64_t)(brow ? n0 + r : 0) * p.ldb + g * 8;
+  SkinnyEpiIn<EPI> ein;
+  if (w == 0) ein.load(p, n0 + r, g);
   const int nk = K / 32;
   bf16x8 bfr[SKN_S];
 #pragma unroll
@@ -1466,13 +1492,7 @@ __global__ __launch_bounds__(1024) void gemm_skinny_norm_kernel(GemmArgs p) {
     f32x4 t = part[0][lane];
 #pragma unroll
     for (int q = 1; q < 16; q++) t += part[q][lane];
-    const int col = n0 + r;
-    if (col < p.N) {
-      const float bias = epi_bias<EPI>(p, col);
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-        if (4 * g + i < p.M) epi_store<bf16, EPI>(p, 4 * g + i, col, t[i], bias);
-    }
+    ein.store(p, n0 + r, g, t);
   }
 }
 
