@@ -120,6 +120,7 @@ struct gpt_model {
     const int32_t* tok = nullptr;
     const float* out = nullptr;
     int B = 0;
+    bool off = false;   // the graph API failed once: direct launches from then on
   } dg;
   // GPT_F_MICROGPT: weightless RMSNorm, ReLU, no biases, an lm_head of its own
   bool micro = false;
@@ -986,32 +987,46 @@ void drop_decode_graph(gpt_model* h) {
 }
 
 // Records decode_launches on the library's own capture stream (the caller's stream
-// may be the null stream, which cannot be captured) and instantiates the graph.
-int record_decode_graph(gpt_model* h, const int32_t* d_tokens, float* d_logits) {
-  int rc;
-  if (!h->dg.cap && (rc = hip_check(h, hipStreamCreateWithFlags(&h->dg.cap, hipStreamNonBlocking),
-                                    "decode graph stream")))
-    return rc;
-  if ((rc = hip_check(h, hipStreamBeginCapture(h->dg.cap, hipStreamCaptureModeThreadLocal), "decode graph capture")))
-    return rc;
+// may be the null stream, which cannot be captured) and instantiates the graph. A
+// failure of the graph API itself is not an error of the step: the model then stops
+// recording (dg.off) and the step runs as direct launches. Returns whether a graph
+// is ready, or a GPT_E_* code for an error of the launches themselves.
+int record_decode_graph(gpt_model* h, const int32_t* d_tokens, float* d_logits, bool* ready) {
+  *ready = false;
+  if (!h->dg.cap && hipStreamCreateWithFlags(&h->dg.cap, hipStreamNonBlocking) != hipSuccess) {
+    (void)hipGetLastError();
+    h->dg.cap = nullptr;
+    h->dg.off = true;
+    return GPT_OK;
+  }
+  if (hipStreamBeginCapture(h->dg.cap, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+    (void)hipGetLastError();
+    h->dg.off = true;
+    return GPT_OK;
+  }
   hipStream_t user = h->stream;
   h->stream = h->dg.cap;
-  rc = decode_launches(h, d_tokens, d_logits);
+  const int rc = decode_launches(h, d_tokens, d_logits);
   h->stream = user;
   hipGraph_t g = nullptr;
   const hipError_t e = hipStreamEndCapture(h->dg.cap, &g);
-  if (rc != GPT_OK) {
+  if (rc != GPT_OK || e != hipSuccess) {
     if (g) (void)hipGraphDestroy(g);
-    return rc;
+    (void)hipGetLastError();
+    if (rc != GPT_OK) return rc;
+    h->dg.off = true;
+    return GPT_OK;
   }
-  if ((rc = hip_check(h, e, "decode graph capture"))) return rc;
   hipGraphExec_t x = nullptr;
-  if ((rc = hip_check(h, hipGraphInstantiate(&x, g, nullptr, nullptr, 0), "decode graph instantiate"))) {
+  if (hipGraphInstantiate(&x, g, nullptr, nullptr, 0) != hipSuccess) {
+    (void)hipGetLastError();
     (void)hipGraphDestroy(g);
-    return rc;
+    h->dg.off = true;
+    return GPT_OK;
   }
   h->dg.graph = g;
   h->dg.exec = x;
+  *ready = true;
   return GPT_OK;
 }
 
@@ -1031,9 +1046,14 @@ int gpt_decode(gpt_model* h, const int32_t* d_tokens, float* d_logits) {
   // recorded step (recorded at the first such repeat); any other call runs the
   // launches directly and becomes the new reference.
   const bool repeat = h->dg.tok == d_tokens && h->dg.out == d_logits && h->dg.B == h->kv_B;
-  if (repeat && decode_graph_on() && !h->timer.on) {
-    if (!h->dg.exec && (rc = record_decode_graph(h, d_tokens, d_logits))) return rc;
+  bool ready = h->dg.exec != nullptr;
+  if (repeat && !ready && decode_graph_on() && !h->timer.on && !h->dg.off &&
+      (rc = record_decode_graph(h, d_tokens, d_logits, &ready)))
+    return rc;
+  if (repeat && ready && !h->timer.on) {
     if ((rc = hip_check(h, hipGraphLaunch(h->dg.exec, h->stream), "decode graph launch"))) return rc;
+  } else if (repeat) {
+    if ((rc = decode_launches(h, d_tokens, d_logits))) return rc;
   } else {
     drop_decode_graph(h);
     h->dg.tok = d_tokens;
