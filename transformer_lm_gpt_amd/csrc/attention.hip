@@ -573,7 +573,14 @@ __global__ __launch_bounds__(256) void attn_fwd_v2(const bf16* __restrict__ qkv,
 #pragma unroll
   for (int cb = 0; cb < CB; cb++) ot[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY;   // running max of S*c over the keys seen (same in the four lanes of a query)
-  float l = 0.f;         // this lane's part of the running sum of exp2(S*c - m)
+  // The running sum of exp2(S*c - m) comes from the matrix cores: an A fragment of
+  // ones times a P fragment gives, in each of the four entries, the sum of the
+  // fragment's 32 (bf16-rounded) probabilities of this lane's query. That moves 16
+  // VALU adds per tile (the forward is VALU-bound) to two MFMAs, and normalizes O by
+  // the sum of the very values that weighted V (with dropout: the undropped P).
+  f32x4 lt = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const bf16x8 ones = (bf16x8){(bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f,
+                               (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f};
 
   const auto src = range_rsrc(base, (int64_t)Tn * ld * 2);
   TileRegs<HDP> kr, vr;
@@ -620,7 +627,7 @@ __global__ __launch_bounds__(256) void attn_fwd_v2(const bf16* __restrict__ qkv,
     if (__any(mt > m + RESCALE_LAG)) {
       const float mnew = fmaxf(m, mt);
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-      l *= alpha;
+      lt *= alpha;
 #pragma unroll
       for (int cb = 0; cb < CB; cb++) ot[cb] *= alpha;
       m = mnew;
@@ -631,15 +638,17 @@ __global__ __launch_bounds__(256) void attn_fwd_v2(const bf16* __restrict__ qkv,
       for (int i = 0; i < 4; i++) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[nb][i], c, -m));
         st[nb][i] = p;
-        l += p;
       }
     if constexpr (DROP) {                             // this lane's four keys of a block share one Philox block
+#pragma unroll
+      for (int kp = 0; kp < 2; kp++) lt = Mfma<bf16>::mma(ones, pack_p(st[2 * kp], st[2 * kp + 1]), lt);
 #pragma unroll
       for (int nb = 0; nb < 4; nb++) st[nb] *= drop_mult4(da, site, (uint32_t)(bh * Tn + q), kt * 16 + nb * 4 + g);
     }
 #pragma unroll
     for (int kp = 0; kp < 2; kp++) {
       const bf16x8 pf = pack_p(st[2 * kp], st[2 * kp + 1]);
+      if constexpr (!DROP) lt = Mfma<bf16>::mma(ones, pf, lt);
 #pragma unroll
       for (int cb = 0; cb < CB; cb++) {
         const bf16x8 vf = cat4(AT::tr(Vs, 32 * kp + 4 * g, cb * 16), AT::tr(Vs, 32 * kp + 16 + 4 * g, cb * 16));
@@ -647,7 +656,7 @@ __global__ __launch_bounds__(256) void attn_fwd_v2(const bf16* __restrict__ qkv,
       }
     }
   }
-  l = group_sum(l);
+  const float l = lt[0];
   if (q < Tn) {
     const float inv = 1.f / l;
     bf16* orow = o + ((int64_t)b * Tn + q) * d + h * HDP;
@@ -723,15 +732,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     f32x4 st[4], ds[4];
 #pragma unroll
     for (int nb = 0; nb < 4; nb++) {
-      f32x4 dpt = (f32x4){0.f, 0.f, 0.f, 0.f};
+      // the dP accumulator starts at -D, so the MFMAs leave dP - D
+      f32x4 dpt = (f32x4){-Dq, -Dq, -Dq, -Dq};
       st[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KK; kk++) {
         st[nb] = Mfma<bf16>::mma(AT::row_frag(Ks, nb * 16 + (lane & 15), kk * 4 + g), qf[kk], st[nb]);
         dpt = Mfma<bf16>::mma(AT::row_frag(Vs, nb * 16 + (lane & 15), kk * 4 + g), dof[kk], dpt);
       }
-      if constexpr (DROP) dpt *= drop_mult4(da, site, (uint32_t)(bh * Tn + q), kt * 16 + nb * 4 + g);
-      ds[nb] = dpt - Dq;
+      if constexpr (DROP) {
+        // Z dP - D from t = dP - D: Z t + (Z - 1) D for a kept element (Z = 1/(1-p)),
+        // -D for a dropped one (Z = 0); at Z = 1 this is t itself, bit for bit
+        const f32x4 mk = drop_mult4(da, site, (uint32_t)(bh * Tn + q), kt * 16 + nb * 4 + g);
+        const float kd = (da.scale - 1.f) * Dq;
+#pragma unroll
+        for (int i = 0; i < 4; i++) dpt[i] = __builtin_fmaf(mk[i], dpt[i], mk[i] != 0.f ? kd : -Dq);
+      }
+      ds[nb] = dpt;
     }
     if (kt == qb) {                                   // diagonal tile: local keys <= q - k0 are visible
       const int lim = q - kt * 64;
