@@ -11,9 +11,10 @@
 // Layout: qkv is [B*T, 3*d] with q | k | v and head h at columns h*hd; O and dO
 // are [B*T, d]; lse and D are fp32 [B*H, T].
 //
-// Forward: one workgroup per (64-query tile, batch*head); its four wavefronts
-// own 16 queries each and stream 64-key tiles of K and V through LDS with an
-// online softmax (running max and sum per row, rescaling the O accumulator).
+// Forward: one workgroup per (query tile, batch*head); its four wavefronts own
+// 16 queries each (fp32: 64-query tiles) or 32 each (bf16: 128-query tiles) and
+// stream 64-key tiles of K and V through LDS with an online softmax (running max
+// and sum per row, rescaling the O accumulator).
 // Backward: the score tile is recomputed from Q, K and lse. dK and dV are
 // accumulated per 64-key tile over the query tiles at or after it; dQ is
 // accumulated per 64-query tile over the key tiles at or before it. Both run
@@ -542,132 +543,163 @@ __device__ inline void block_colsum(const f32x4 (&acc)[HDP / 16], float mul, flo
   }
 }
 
+// The forward with 128 queries per workgroup, 32 per wavefront. Each K fragment and
+// each transposed V fragment read from LDS feeds the MFMAs of two 16-query halves
+// (register blocking on the query side), which halves the LDS read bytes per score
+// (with 16 queries per wavefront every 16 queries read the whole 64 x hd K and V
+// tiles). Wavefront w owns queries 128 QB + 32 w + 16 hh + (lane & 15), which lie in
+// the 64-query block sb = 2 QB + w/2: key tiles before sb are fully visible, tile sb
+// is the diagonal one, later tiles are skipped (the wavefront only helps stage them).
+// Per query the arithmetic, and its order, is that of 16 queries per wavefront.
 // The exponentials run in base 2 with the 1/sqrt(hd) scale folded in: with
 // c = log2(e)/sqrt(hd), exp(S*scale - x) = exp2(S*c - x*log2(e)), one FMA and one
 // v_exp per score. Only the diagonal tile of a causal block needs the mask.
 template <int HDP, bool DROP>
-__global__ __launch_bounds__(256) void attn_fwd_v2(const bf16* __restrict__ qkv, bf16* __restrict__ o,
+__global__ __launch_bounds__(256) void attn_fwd_v3(const bf16* __restrict__ qkv, bf16* __restrict__ o,
                                                    float* __restrict__ lse, int Tn, int H, float scale, DropArgs da,
                                                    uint32_t site) {
   typedef ATile<HDP> AT;
   constexpr int KK = HDP / 32, CB = HDP / 16;
   __shared__ __attribute__((aligned(16))) bf16 Ks[64 * HDP];
   __shared__ __attribute__((aligned(16))) bf16 Vs[64 * HDP];
-  const int nqb = (Tn + 63) / 64;
-  // (batch*head) varies fastest, so every block of a query-block index is issued
-  // before any shorter one (longest first keeps the tail short) and one head's
-  // blocks share an XCD's L2 (workgroups go round-robin over the 8 XCDs)
-  const int qb = nqb - 1 - blockIdx.y;
+  const int nkt = (Tn + 63) / 64;
+  const int nQB = (Tn + 127) / 128;
+  const int QB = nQB - 1 - blockIdx.y;                // longest first
   const int bh = blockIdx.x, b = bh / H, h = bh % H;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4;
   const int d = H * HDP;
   const int64_t ld = 3 * (int64_t)d;
   const bf16* base = qkv + (int64_t)b * Tn * ld;
-  const int q = qb * 64 + w * 16 + (lane & 15);      // this lane's query
+  const int sb = 2 * QB + (w >> 1);                   // this wavefront's 64-query block
+  const int q0w = QB * 128 + w * 32;                  // its first query
+  const bool active = q0w < Tn;                       // wave-uniform: some query is in range
+  int q[2];
+  q[0] = q0w + (lane & 15);
+  q[1] = q[0] + 16;
   const float c = scale * LOG2E_F;
-  bf16x8 qf[KK];
+  bf16x8 qf[2][KK];
 #pragma unroll
-  for (int kk = 0; kk < KK; kk++)
-    qf[kk] = q < Tn ? *(const bf16x8*)(base + (int64_t)q * ld + h * HDP + kk * 32 + g * 8) : (bf16x8){};
-  f32x4 ot[CB];
+  for (int hh = 0; hh < 2; hh++)
 #pragma unroll
-  for (int cb = 0; cb < CB; cb++) ot[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY;   // running max of S*c over the keys seen (same in the four lanes of a query)
-  // The running sum of exp2(S*c - m) comes from the matrix cores: an A fragment of
-  // ones times a P fragment gives, in each of the four entries, the sum of the
-  // fragment's 32 (bf16-rounded) probabilities of this lane's query. That moves 16
-  // VALU adds per tile (the forward is VALU-bound) to two MFMAs, and normalizes O by
-  // the sum of the very values that weighted V (with dropout: the undropped P).
-  f32x4 lt = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < KK; kk++)
+      qf[hh][kk] = q[hh] < Tn ? *(const bf16x8*)(base + (int64_t)q[hh] * ld + h * HDP + kk * 32 + g * 8)
+                              : (bf16x8){};
+  f32x4 ot[2][CB];
+  f32x4 lt[2];
+  float m[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; hh++) {
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++) ot[hh][cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    lt[hh] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    m[hh] = -INFINITY;
+  }
   const bf16x8 ones = (bf16x8){(bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f,
                                (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f};
+  const int last = min(2 * QB + 1, nkt - 1);          // the block's last key tile
 
   const auto src = range_rsrc(base, (int64_t)Tn * ld * 2);
   TileRegs<HDP> kr, vr;
   kr.load(src, (int)ld, 0, d + h * HDP);
   vr.load(src, (int)ld, 0, 2 * d + h * HDP);
-  for (int kt = 0; kt <= qb; kt++) {
+  for (int kt = 0; kt <= last; kt++) {
     __syncthreads();
     kr.store(Ks);
     vr.store(Vs);
     __syncthreads();
-    if (kt < qb) {
+    if (kt < last) {
       kr.load(src, (int)ld, (kt + 1) * 64, d + h * HDP);
       vr.load(src, (int)ld, (kt + 1) * 64, 2 * d + h * HDP);
     }
-    f32x4 st[4];
+    if (!active || kt > sb) continue;                 // wave-uniform
+    f32x4 st[2][4];
 #pragma unroll
     for (int nb = 0; nb < 4; nb++) {
-      st[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      st[0][nb] = st[1][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KK; kk++)
-        st[nb] = Mfma<bf16>::mma(AT::row_frag(Ks, nb * 16 + (lane & 15), kk * 4 + g), qf[kk], st[nb]);
+      for (int kk = 0; kk < KK; kk++) {
+        const bf16x8 kf = AT::row_frag(Ks, nb * 16 + (lane & 15), kk * 4 + g);
+        st[0][nb] = Mfma<bf16>::mma(kf, qf[0][kk], st[0][nb]);
+        st[1][nb] = Mfma<bf16>::mma(kf, qf[1][kk], st[1][nb]);
+      }
     }
-    if (kt == qb) {                                   // keys after the query, or past Tn
-      const int lim = q - kt * 64;
+    if (kt == sb) {                                   // keys after the query, or past Tn
+#pragma unroll
+      for (int hh = 0; hh < 2; hh++) {
+        const int lim = q[hh] - kt * 64;
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const int kl = nb * 16 + 4 * g + i;
+            if (kl > lim || kt * 64 + kl >= Tn) st[hh][nb][i] = -INFINITY;
+          }
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; hh++) {
+      float mx = st[hh][0][0];
 #pragma unroll
       for (int nb = 0; nb < 4; nb++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const int kl = nb * 16 + 4 * g + i;
-          if (kl > lim || kt * 64 + kl >= Tn) st[nb][i] = -INFINITY;
-        }
-    }
-    float mx = st[0][0];
+        for (int i = 0; i < 4; i++) mx = fmaxf(mx, st[hh][nb][i]);
+      // the running max moves only when a row's max grows by more than 2^RESCALE_LAG
+      // (and on the first tile): until then P = exp2(S c - m) stays below 2^8, which bf16
+      // and the fp32 sums hold at full relative precision, and the sums and the output
+      // carry the same stale m, so the result is the same; most tiles skip the rescale
+      const float mt = group_max(mx) * c;            // finite: key 0 is always visible
+      if (__any(mt > m[hh] + RESCALE_LAG)) {
+        const float mnew = fmaxf(m[hh], mt);
+        const float alpha = __builtin_amdgcn_exp2f(m[hh] - mnew);
+        lt[hh] *= alpha;
 #pragma unroll
-    for (int nb = 0; nb < 4; nb++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) mx = fmaxf(mx, st[nb][i]);
-    // The running max is moved only when a row's max grows by more than 2^RESCALE_LAG
-    // over it (and on the first tile): until then P = exp2(S c - m) stays below 2^8,
-    // which bf16 and the fp32 sums hold at full relative precision, and l and the
-    // output carry the same stale m, so the result is the same. Most tiles then skip
-    // the rescale of the output accumulators.
-    const float mt = group_max(mx) * c;              // finite: key 0 is always visible
-    if (__any(mt > m + RESCALE_LAG)) {
-      const float mnew = fmaxf(m, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-      lt *= alpha;
-#pragma unroll
-      for (int cb = 0; cb < CB; cb++) ot[cb] *= alpha;
-      m = mnew;
-    }
-#pragma unroll
-    for (int nb = 0; nb < 4; nb++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[nb][i], c, -m));
-        st[nb][i] = p;
+        for (int cb = 0; cb < CB; cb++) ot[hh][cb] *= alpha;
+        m[hh] = mnew;
       }
-    if constexpr (DROP) {                             // this lane's four keys of a block share one Philox block
 #pragma unroll
-      for (int kp = 0; kp < 2; kp++) lt = Mfma<bf16>::mma(ones, pack_p(st[2 * kp], st[2 * kp + 1]), lt);
+      for (int nb = 0; nb < 4; nb++)
 #pragma unroll
-      for (int nb = 0; nb < 4; nb++) st[nb] *= drop_mult4(da, site, (uint32_t)(bh * Tn + q), kt * 16 + nb * 4 + g);
+        for (int i = 0; i < 4; i++) st[hh][nb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[hh][nb][i], c, -m[hh]));
+      if constexpr (DROP) {
+#pragma unroll
+        for (int kp = 0; kp < 2; kp++)
+          lt[hh] = Mfma<bf16>::mma(ones, pack_p(st[hh][2 * kp], st[hh][2 * kp + 1]), lt[hh]);
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++)
+          st[hh][nb] *= drop_mult4(da, site, (uint32_t)(bh * Tn + q[hh]), kt * 16 + nb * 4 + g);
+      }
     }
 #pragma unroll
     for (int kp = 0; kp < 2; kp++) {
-      const bf16x8 pf = pack_p(st[2 * kp], st[2 * kp + 1]);
-      if constexpr (!DROP) lt = Mfma<bf16>::mma(ones, pf, lt);
+      bf16x8 pf[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; hh++) {
+        pf[hh] = pack_p(st[hh][2 * kp], st[hh][2 * kp + 1]);
+        if constexpr (!DROP) lt[hh] = Mfma<bf16>::mma(ones, pf[hh], lt[hh]);
+      }
 #pragma unroll
       for (int cb = 0; cb < CB; cb++) {
         const bf16x8 vf = cat4(AT::tr(Vs, 32 * kp + 4 * g, cb * 16), AT::tr(Vs, 32 * kp + 16 + 4 * g, cb * 16));
-        ot[cb] = Mfma<bf16>::mma(vf, pf, ot[cb]);
+        ot[0][cb] = Mfma<bf16>::mma(vf, pf[0], ot[0][cb]);
+        ot[1][cb] = Mfma<bf16>::mma(vf, pf[1], ot[1][cb]);
       }
     }
   }
-  const float l = lt[0];
-  if (q < Tn) {
-    const float inv = 1.f / l;
-    bf16* orow = o + ((int64_t)b * Tn + q) * d + h * HDP;
 #pragma unroll
-    for (int cb = 0; cb < CB; cb++) {
-      bf16x4 v;
+  for (int hh = 0; hh < 2; hh++) {
+    if (q[hh] < Tn) {
+      const float l = lt[hh][0];
+      const float inv = 1.f / l;
+      bf16* orow = o + ((int64_t)b * Tn + q[hh]) * d + h * HDP;
 #pragma unroll
-      for (int i = 0; i < 4; i++) v[i] = (bf16)(ot[cb][i] * inv);
-      *(bf16x4*)(orow + cb * 16 + 4 * g) = v;
+      for (int cb = 0; cb < CB; cb++) {
+        bf16x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; i++) v[i] = (bf16)(ot[hh][cb][i] * inv);
+        *(bf16x4*)(orow + cb * 16 + 4 * g) = v;
+      }
+      if (g == 0) lse[(int64_t)bh * Tn + q[hh]] = (m[hh] + log2f(l)) * LN2_F;
     }
-    if (g == 0) lse[(int64_t)bh * Tn + q] = (m + log2f(l)) * LN2_F;
   }
 }
 
@@ -993,13 +1025,13 @@ static hipError_t fwd_any(const void* qkv, void* o, float* lse, bool bf16_ops, i
                           const DropArgs& da, uint32_t site, hipStream_t s) {
   if (bf16_ops && (hd == 32 || hd == 64)) {
     if ((int64_t)T * 3 * H * hd * 2 > INT32_MAX) return hipErrorInvalidValue;   // 32-bit buffer offsets per sequence
-    dim3 grid(B * H, (T + 63) / 64);
+    dim3 grid(B * H, (T + 127) / 128);
     const float scale = 1.0f / sqrtf((float)hd);
     if (hd == 64)
-      hipLaunchKernelGGL((attn_fwd_v2<64, DROP>), grid, dim3(256), 0, s, (const bf16*)qkv, (bf16*)o, lse, T, H,
+      hipLaunchKernelGGL((attn_fwd_v3<64, DROP>), grid, dim3(256), 0, s, (const bf16*)qkv, (bf16*)o, lse, T, H,
                          scale, da, site);
     else
-      hipLaunchKernelGGL((attn_fwd_v2<32, DROP>), grid, dim3(256), 0, s, (const bf16*)qkv, (bf16*)o, lse, T, H,
+      hipLaunchKernelGGL((attn_fwd_v3<32, DROP>), grid, dim3(256), 0, s, (const bf16*)qkv, (bf16*)o, lse, T, H,
                          scale, da, site);
     return hipGetLastError();
   }
