@@ -703,6 +703,137 @@ __global__ __launch_bounds__(256) void attn_fwd_v3(const bf16* __restrict__ qkv,
   }
 }
 
+// The dropout forward: 64-query workgroups, 16 queries per wavefront. With the
+// generator's state, 32 queries per wavefront (attn_fwd_v3) would leave two
+// wavefronts per SIMD instead of four. Per query the arithmetic, and its order, is
+// that of attn_fwd_v3, so a rate that keeps every element reproduces the undropped
+// result bit for bit.
+template <int HDP, bool DROP>
+__global__ __launch_bounds__(256) void attn_fwd_v2(const bf16* __restrict__ qkv, bf16* __restrict__ o,
+                                                   float* __restrict__ lse, int Tn, int H, float scale, DropArgs da,
+                                                   uint32_t site) {
+  typedef ATile<HDP> AT;
+  constexpr int KK = HDP / 32, CB = HDP / 16;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[64 * HDP];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[64 * HDP];
+  const int nqb = (Tn + 63) / 64;
+  // (batch*head) varies fastest, so every block of a query-block index is issued
+  // before any shorter one (longest first keeps the tail short) and one head's
+  // blocks share an XCD's L2 (workgroups go round-robin over the 8 XCDs)
+  const int qb = nqb - 1 - blockIdx.y;
+  const int bh = blockIdx.x, b = bh / H, h = bh % H;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4;
+  const int d = H * HDP;
+  const int64_t ld = 3 * (int64_t)d;
+  const bf16* base = qkv + (int64_t)b * Tn * ld;
+  const int q = qb * 64 + w * 16 + (lane & 15);      // this lane's query
+  const float c = scale * LOG2E_F;
+  bf16x8 qf[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; kk++)
+    qf[kk] = q < Tn ? *(const bf16x8*)(base + (int64_t)q * ld + h * HDP + kk * 32 + g * 8) : (bf16x8){};
+  f32x4 ot[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; cb++) ot[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY;   // running max of S*c over the keys seen (same in the four lanes of a query)
+  // The running sum of exp2(S*c - m) comes from the matrix cores: an A fragment of
+  // ones times a P fragment gives, in each of the four entries, the sum of the
+  // fragment's 32 (bf16-rounded) probabilities of this lane's query. That moves 16
+  // VALU adds per tile (the forward is VALU-bound) to two MFMAs, and normalizes O by
+  // the sum of the very values that weighted V (with dropout: the undropped P).
+  f32x4 lt = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const bf16x8 ones = (bf16x8){(bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f,
+                               (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f};
+
+  const auto src = range_rsrc(base, (int64_t)Tn * ld * 2);
+  TileRegs<HDP> kr, vr;
+  kr.load(src, (int)ld, 0, d + h * HDP);
+  vr.load(src, (int)ld, 0, 2 * d + h * HDP);
+  for (int kt = 0; kt <= qb; kt++) {
+    __syncthreads();
+    kr.store(Ks);
+    vr.store(Vs);
+    __syncthreads();
+    if (kt < qb) {
+      kr.load(src, (int)ld, (kt + 1) * 64, d + h * HDP);
+      vr.load(src, (int)ld, (kt + 1) * 64, 2 * d + h * HDP);
+    }
+    f32x4 st[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; nb++) {
+      st[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; kk++)
+        st[nb] = Mfma<bf16>::mma(AT::row_frag(Ks, nb * 16 + (lane & 15), kk * 4 + g), qf[kk], st[nb]);
+    }
+    if (kt == qb) {                                   // keys after the query, or past Tn
+      const int lim = q - kt * 64;
+#pragma unroll
+      for (int nb = 0; nb < 4; nb++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int kl = nb * 16 + 4 * g + i;
+          if (kl > lim || kt * 64 + kl >= Tn) st[nb][i] = -INFINITY;
+        }
+    }
+    float mx = st[0][0];
+#pragma unroll
+    for (int nb = 0; nb < 4; nb++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) mx = fmaxf(mx, st[nb][i]);
+    // The running max is moved only when a row's max grows by more than 2^RESCALE_LAG
+    // over it (and on the first tile): until then P = exp2(S c - m) stays below 2^8,
+    // which bf16 and the fp32 sums hold at full relative precision, and l and the
+    // output carry the same stale m, so the result is the same. Most tiles then skip
+    // the rescale of the output accumulators.
+    const float mt = group_max(mx) * c;              // finite: key 0 is always visible
+    if (__any(mt > m + RESCALE_LAG)) {
+      const float mnew = fmaxf(m, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      lt *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < CB; cb++) ot[cb] *= alpha;
+      m = mnew;
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; nb++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[nb][i], c, -m));
+        st[nb][i] = p;
+      }
+    if constexpr (DROP) {                             // this lane's four keys of a block share one Philox block
+#pragma unroll
+      for (int kp = 0; kp < 2; kp++) lt = Mfma<bf16>::mma(ones, pack_p(st[2 * kp], st[2 * kp + 1]), lt);
+#pragma unroll
+      for (int nb = 0; nb < 4; nb++) st[nb] *= drop_mult4(da, site, (uint32_t)(bh * Tn + q), kt * 16 + nb * 4 + g);
+    }
+#pragma unroll
+    for (int kp = 0; kp < 2; kp++) {
+      const bf16x8 pf = pack_p(st[2 * kp], st[2 * kp + 1]);
+      if constexpr (!DROP) lt = Mfma<bf16>::mma(ones, pf, lt);
+#pragma unroll
+      for (int cb = 0; cb < CB; cb++) {
+        const bf16x8 vf = cat4(AT::tr(Vs, 32 * kp + 4 * g, cb * 16), AT::tr(Vs, 32 * kp + 16 + 4 * g, cb * 16));
+        ot[cb] = Mfma<bf16>::mma(vf, pf, ot[cb]);
+      }
+    }
+  }
+  const float l = lt[0];
+  if (q < Tn) {
+    const float inv = 1.f / l;
+    bf16* orow = o + ((int64_t)b * Tn + q) * d + h * HDP;
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++) {
+      bf16x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; i++) v[i] = (bf16)(ot[cb][i] * inv);
+      *(bf16x4*)(orow + cb * 16 + 4 * g) = v;
+    }
+    if (g == 0) lse[(int64_t)bh * Tn + q] = (m + log2f(l)) * LN2_F;
+  }
+}
+
 // dQ for a 64-query block; also writes D = rowsum(dO * O) for these queries,
 // which the dK/dV kernel (launched after) reads.
 template <int HDP, bool DROP>
@@ -773,12 +904,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
         dpt = Mfma<bf16>::mma(AT::row_frag(Vs, nb * 16 + (lane & 15), kk * 4 + g), dof[kk], dpt);
       }
       if constexpr (DROP) {
-        // Z dP - D from t = dP - D: Z t + (Z - 1) D for a kept element (Z = 1/(1-p)),
-        // -D for a dropped one (Z = 0); at Z = 1 this is t itself, bit for bit
+        // Z dP - D from t = dP - D as Z t + (Z D - D): at Z = 1 the inner term is exactly
+        // 0 and the result is t itself, bit for bit; at Z = 0 it is -D
         const f32x4 mk = drop_mult4(da, site, (uint32_t)(bh * Tn + q), kt * 16 + nb * 4 + g);
-        const float kd = (da.scale - 1.f) * Dq;
 #pragma unroll
-        for (int i = 0; i < 4; i++) dpt[i] = __builtin_fmaf(mk[i], dpt[i], mk[i] != 0.f ? kd : -Dq);
+        for (int i = 0; i < 4; i++) dpt[i] = __builtin_fmaf(mk[i], dpt[i], __builtin_fmaf(mk[i], Dq, -Dq));
       }
       ds[nb] = dpt;
     }
@@ -1025,14 +1155,24 @@ static hipError_t fwd_any(const void* qkv, void* o, float* lse, bool bf16_ops, i
                           const DropArgs& da, uint32_t site, hipStream_t s) {
   if (bf16_ops && (hd == 32 || hd == 64)) {
     if ((int64_t)T * 3 * H * hd * 2 > INT32_MAX) return hipErrorInvalidValue;   // 32-bit buffer offsets per sequence
-    dim3 grid(B * H, (T + 127) / 128);
     const float scale = 1.0f / sqrtf((float)hd);
-    if (hd == 64)
-      hipLaunchKernelGGL((attn_fwd_v3<64, DROP>), grid, dim3(256), 0, s, (const bf16*)qkv, (bf16*)o, lse, T, H,
-                         scale, da, site);
-    else
-      hipLaunchKernelGGL((attn_fwd_v3<32, DROP>), grid, dim3(256), 0, s, (const bf16*)qkv, (bf16*)o, lse, T, H,
-                         scale, da, site);
+    if (DROP) {
+      dim3 grid(B * H, (T + 63) / 64);
+      if (hd == 64)
+        hipLaunchKernelGGL((attn_fwd_v2<64, true>), grid, dim3(256), 0, s, (const bf16*)qkv, (bf16*)o, lse, T, H,
+                           scale, da, site);
+      else
+        hipLaunchKernelGGL((attn_fwd_v2<32, true>), grid, dim3(256), 0, s, (const bf16*)qkv, (bf16*)o, lse, T, H,
+                           scale, da, site);
+    } else {
+      dim3 grid(B * H, (T + 127) / 128);
+      if (hd == 64)
+        hipLaunchKernelGGL((attn_fwd_v3<64, false>), grid, dim3(256), 0, s, (const bf16*)qkv, (bf16*)o, lse, T, H,
+                           scale, da, site);
+      else
+        hipLaunchKernelGGL((attn_fwd_v3<32, false>), grid, dim3(256), 0, s, (const bf16*)qkv, (bf16*)o, lse, T, H,
+                           scale, da, site);
+    }
     return hipGetLastError();
   }
   if (bf16_ops)
