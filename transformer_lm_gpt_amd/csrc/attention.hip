@@ -554,10 +554,13 @@ __device__ inline void block_colsum(const f32x4 (&acc)[HDP / 16], float mul, flo
 // The exponentials run in base 2 with the 1/sqrt(hd) scale folded in: with
 // c = log2(e)/sqrt(hd), exp(S*scale - x) = exp2(S*c - x*log2(e)), one FMA and one
 // v_exp per score. Only the diagonal tile of a causal block needs the mask.
+// Without dropout only (DROP = false; da and site are unused): the dropout forward is
+// attn_fwd_v2 below.
 template <int HDP, bool DROP>
 __global__ __launch_bounds__(256) void attn_fwd_v3(const bf16* __restrict__ qkv, bf16* __restrict__ o,
                                                    float* __restrict__ lse, int Tn, int H, float scale, DropArgs da,
                                                    uint32_t site) {
+  static_assert(!DROP, "the dropout forward is attn_fwd_v2");
   typedef ATile<HDP> AT;
   constexpr int KK = HDP / 32, CB = HDP / 16;
   __shared__ __attribute__((aligned(16))) bf16 Ks[64 * HDP];
@@ -585,6 +588,8 @@ __global__ __launch_bounds__(256) void attn_fwd_v3(const bf16* __restrict__ qkv,
       qf[hh][kk] = q[hh] < Tn ? *(const bf16x8*)(base + (int64_t)q[hh] * ld + h * HDP + kk * 32 + g * 8)
                               : (bf16x8){};
   f32x4 ot[2][CB];
+  // running sums of the bf16-rounded P, from one MFMA of a ones fragment against
+  // each P fragment (every entry of the output block holds its query's sum)
   f32x4 lt[2];
   float m[2];
 #pragma unroll
@@ -660,14 +665,6 @@ __global__ __launch_bounds__(256) void attn_fwd_v3(const bf16* __restrict__ qkv,
       for (int nb = 0; nb < 4; nb++)
 #pragma unroll
         for (int i = 0; i < 4; i++) st[hh][nb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[hh][nb][i], c, -m[hh]));
-      if constexpr (DROP) {
-#pragma unroll
-        for (int kp = 0; kp < 2; kp++)
-          lt[hh] = Mfma<bf16>::mma(ones, pack_p(st[hh][2 * kp], st[hh][2 * kp + 1]), lt[hh]);
-#pragma unroll
-        for (int nb = 0; nb < 4; nb++)
-          st[hh][nb] *= drop_mult4(da, site, (uint32_t)(bh * Tn + q[hh]), kt * 16 + nb * 4 + g);
-      }
     }
 #pragma unroll
     for (int kp = 0; kp < 2; kp++) {
@@ -675,7 +672,7 @@ __global__ __launch_bounds__(256) void attn_fwd_v3(const bf16* __restrict__ qkv,
 #pragma unroll
       for (int hh = 0; hh < 2; hh++) {
         pf[hh] = pack_p(st[hh][2 * kp], st[hh][2 * kp + 1]);
-        if constexpr (!DROP) lt[hh] = Mfma<bf16>::mma(ones, pf[hh], lt[hh]);
+        lt[hh] = Mfma<bf16>::mma(ones, pf[hh], lt[hh]);
       }
 #pragma unroll
       for (int cb = 0; cb < CB; cb++) {
@@ -707,11 +704,12 @@ __global__ __launch_bounds__(256) void attn_fwd_v3(const bf16* __restrict__ qkv,
 // generator's state, 32 queries per wavefront (attn_fwd_v3) would leave two
 // wavefronts per SIMD instead of four. Per query the arithmetic, and its order, is
 // that of attn_fwd_v3, so a rate that keeps every element reproduces the undropped
-// result bit for bit.
+// result bit for bit. DROP = true only.
 template <int HDP, bool DROP>
 __global__ __launch_bounds__(256) void attn_fwd_v2(const bf16* __restrict__ qkv, bf16* __restrict__ o,
                                                    float* __restrict__ lse, int Tn, int H, float scale, DropArgs da,
                                                    uint32_t site) {
+  static_assert(DROP, "the forward without dropout is attn_fwd_v3");
   typedef ATile<HDP> AT;
   constexpr int KK = HDP / 32, CB = HDP / 16;
   __shared__ __attribute__((aligned(16))) bf16 Ks[64 * HDP];
@@ -740,7 +738,8 @@ __global__ __launch_bounds__(256) void attn_fwd_v2(const bf16* __restrict__ qkv,
   // ones times a P fragment gives, in each of the four entries, the sum of the
   // fragment's 32 (bf16-rounded) probabilities of this lane's query. That moves 16
   // VALU adds per tile (the forward is VALU-bound) to two MFMAs, and normalizes O by
-  // the sum of the very values that weighted V (with dropout: the undropped P).
+  // the sum of the probabilities before the mask (the mask multiplies only the P that
+  // weights V).
   f32x4 lt = (f32x4){0.f, 0.f, 0.f, 0.f};
   const bf16x8 ones = (bf16x8){(bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f,
                                (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f};
@@ -802,16 +801,15 @@ __global__ __launch_bounds__(256) void attn_fwd_v2(const bf16* __restrict__ qkv,
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[nb][i], c, -m));
         st[nb][i] = p;
       }
-    if constexpr (DROP) {                             // this lane's four keys of a block share one Philox block
+    // the row sum takes the undropped P; this lane's four keys of a block share one
+    // Philox block
 #pragma unroll
-      for (int kp = 0; kp < 2; kp++) lt = Mfma<bf16>::mma(ones, pack_p(st[2 * kp], st[2 * kp + 1]), lt);
+    for (int kp = 0; kp < 2; kp++) lt = Mfma<bf16>::mma(ones, pack_p(st[2 * kp], st[2 * kp + 1]), lt);
 #pragma unroll
-      for (int nb = 0; nb < 4; nb++) st[nb] *= drop_mult4(da, site, (uint32_t)(bh * Tn + q), kt * 16 + nb * 4 + g);
-    }
+    for (int nb = 0; nb < 4; nb++) st[nb] *= drop_mult4(da, site, (uint32_t)(bh * Tn + q), kt * 16 + nb * 4 + g);
 #pragma unroll
     for (int kp = 0; kp < 2; kp++) {
       const bf16x8 pf = pack_p(st[2 * kp], st[2 * kp + 1]);
-      if constexpr (!DROP) lt = Mfma<bf16>::mma(ones, pf, lt);
 #pragma unroll
       for (int cb = 0; cb < CB; cb++) {
         const bf16x8 vf = cat4(AT::tr(Vs, 32 * kp + 4 * g, cb * 16), AT::tr(Vs, 32 * kp + 16 + 4 * g, cb * 16));
