@@ -845,11 +845,11 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, char* smem, int tm, 
 }
 
 
-// The 192-wide, 32-wide-slice kernels run two workgroups per CU (their LDS ring allows
-// it); the register budget is held to that occupancy so the epilogue's prefetched
-// inputs cannot push them to one.
+// The 192-wide, 32-wide-slice kernels and the 96 x 192 kernel run two workgroups per
+// CU (their LDS rings allow it); the register budget is held to that occupancy so the
+// epilogue's prefetched inputs cannot push them to one.
 template <int BM_, int BN_, int WM_, int WN_, int STAGES, bool AK, bool BK_, int EPI, int KS = 32>
-__global__ __launch_bounds__(64 * WM_ * WN_) __attribute__((amdgpu_waves_per_eu(KS == 32 && BM_ == 192 ? 2 : 1)))
+__global__ __launch_bounds__(64 * WM_ * WN_) __attribute__((amdgpu_waves_per_eu((KS == 32 && BM_ == 192) || BM_ == 96 ? 2 : 1)))
 void gemm_dma_kernel(GemmArgs p) {
   constexpr int SB = (BM_ + BN_) * KS * 2;
   static_assert(STAGES * SB >= (WM_ * WN_ * 16 * (BN_ / WN_ + 4) + WM_ * BN_) * 4, "epilogue scratch fits the stages");
@@ -1599,9 +1599,18 @@ static bool use_k192(const GemmDesc& d, bool bf16_operands) {
   return pipelined_ok(d, bf16_operands) && d.a_kc && d.b_kc && d.epi != EPI_ACC;
 }
 
+// Rows per tile of the launch use_k192 picks: 96 x 192 tiles (two workgroups per CU)
+// when one 192 x 192 tile per CU or fewer would cover the output and K <= 4096, else
+// 192 x 192. The fused column sums write one partial row per tile row.
+static int k192_tile_rows(const GemmDesc& d) {
+  const int t192 = ((d.M + 191) / 192) * ((d.N + 191) / 192);
+  return t192 <= num_cus() && d.K % 64 == 0 && d.K <= 4096 ? 96 : 192;
+}
+
 int gemm_colsum_rows(const GemmDesc& d, bool bf16_operands) {
   if ((d.epi != EPI_GELU_BWD && d.epi != EPI_RELU_BWD) || !use_k192(d, bf16_operands)) return 0;
-  return (d.M + 191) / 192;
+  const int r = k192_tile_rows(d);
+  return (d.M + r - 1) / r;
 }
 
 // The start delay (n x 2048 cycles) of the second workgroup per CU in the
@@ -1728,14 +1737,28 @@ hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
   // gets the same number of k-slices. Measured on gfx950 it loses to one tile per
   // workgroup when K <= 3072, where parking partial tiles costs more than it saves.
   if (use_k192(d, bf16_operands)) {
-    // one tile per CU or fewer: 64-wide k-slices (half the memory requests per byte;
-    // two stages fill 96 KB of LDS, so one workgroup per CU) and 8 wavefronts of 96 x 48,
-    // which hide more latency than 4 of 96 x 96 when the CU holds no second workgroup
-    // (2-7 % on the step's N = 768 shapes). Otherwise 32-wide slices in three stages,
-    // which leave room for two workgroups per CU.
+    // one 192 x 192 tile per CU or fewer, with 64-wide k-slices (half the memory
+    // requests per byte). Up to K = 4096 (the step's N = 768 launches: the out-projection
+    // and MLP down-projection forwards with their residual epilogue, the fc, qkv and
+    // out-projection input gradients) as 96 x 192 tiles, two workgroups of 4 wavefronts
+    // of 48 x 96 per CU (two stages of 36 KB each), the second one's start staggered:
+    // one's epilogue then overlaps the other's k-loop, where a single tile per CU finishes
+    // all its k-slices with the others and its stores stand alone (measured: 66.58 ->
+    // 66.18 ms per step, the residual launches 6.55 -> 6.23 ms). Longer contractions (the
+    // lm_head input gradient) as 192 x 192 tiles on 8 wavefronts of 96 x 48, which hide
+    // more latency than 4 of 96 x 96 when the CU holds no second workgroup. Otherwise
+    // 32-wide slices in three stages, which leave room for two workgroups per CU.
     const int t192 = ((d.M + 191) / 192) * ((d.N + 191) / 192);
     a.krot = gemm_krot();
-    if (t192 <= num_cus() && d.K % 64 == 0) return dma_epi<192, 192, 2, 4, 2, true, true, 64>(a, d.epi, 1, s);
+    if (t192 <= num_cus() && d.K % 64 == 0) {
+      if (k192_tile_rows(d) == 96) {
+        a.stagger_lo = num_cus();
+        a.stagger_hi = 2 * num_cus();
+        a.stagger_iters = gemm_stagger();
+        return dma_epi<96, 192, 2, 2, 2, true, true, 64>(a, d.epi, 1, s);
+      }
+      return dma_epi<192, 192, 2, 4, 2, true, true, 64>(a, d.epi, 1, s);
+    }
     a.stagger_lo = num_cus();
     a.stagger_hi = 2 * num_cus();
     a.stagger_iters = gemm_stagger();
