@@ -1599,12 +1599,24 @@ static bool use_k192(const GemmDesc& d, bool bf16_operands) {
   return pipelined_ok(d, bf16_operands) && d.a_kc && d.b_kc && d.epi != EPI_ACC;
 }
 
-// Rows per tile of the launch use_k192 picks: 96 x 192 tiles (two workgroups per CU)
-// when one 192 x 192 tile per CU or fewer would cover the output and K <= 4096, else
-// 192 x 192. The fused column sums write one partial row per tile row.
+// Rows per tile of the launch use_k192 picks (K <= 4096, K a multiple of 64): 96 x 192
+// tiles, two workgroups per CU, when one 192 x 192 tile per CU or fewer would cover the
+// output, or when the 96-row tiles fill the last round of two workgroups per CU clearly
+// better (the QKV projection: 768 tiles of 192 rows are 1.5 rounds, 1,536 of 96 rows are
+// 3); else 192 x 192. Measured per launch at M 12,288, K 768: QKV (N 2,304) 55.0 -> 52.8 us
+// on 96-row tiles; MLP up (N 3,072, two whole rounds either way) 88 -> 93 us and the
+// lm_head (N 50,304) slower, so they keep 192 rows. The fused column sums write one
+// partial row per tile row.
 static int k192_tile_rows(const GemmDesc& d) {
-  const int t192 = ((d.M + 191) / 192) * ((d.N + 191) / 192);
-  return t192 <= num_cus() && d.K % 64 == 0 && d.K <= 4096 ? 96 : 192;
+  if (d.K % 64 != 0 || d.K > 4096) return 192;
+  const int64_t t192 = (int64_t)((d.M + 191) / 192) * ((d.N + 191) / 192);
+  if (t192 <= num_cus()) return 96;
+  const int64_t t96 = (int64_t)((d.M + 95) / 96) * ((d.N + 191) / 192);
+  const int64_t slots = 2 * (int64_t)num_cus();
+  // last-round fill of each tiling, in 1/100
+  const int64_t f192 = 100 * t192 / (((t192 + slots - 1) / slots) * slots);
+  const int64_t f96 = 100 * t96 / (((t96 + slots - 1) / slots) * slots);
+  return f96 >= f192 + 20 ? 96 : 192;
 }
 
 int gemm_colsum_rows(const GemmDesc& d, bool bf16_operands) {
@@ -1737,28 +1749,27 @@ hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
   // gets the same number of k-slices. Measured on gfx950 it loses to one tile per
   // workgroup when K <= 3072, where parking partial tiles costs more than it saves.
   if (use_k192(d, bf16_operands)) {
-    // one 192 x 192 tile per CU or fewer, with 64-wide k-slices (half the memory
-    // requests per byte). Up to K = 4096 (the step's N = 768 launches: the out-projection
-    // and MLP down-projection forwards with their residual epilogue, the fc, qkv and
-    // out-projection input gradients) as 96 x 192 tiles, two workgroups of 4 wavefronts
-    // of 48 x 96 per CU (two stages of 36 KB each), the second one's start staggered:
-    // one's epilogue then overlaps the other's k-loop, where a single tile per CU finishes
-    // all its k-slices with the others and its stores stand alone (measured: 66.58 ->
-    // 66.18 ms per step, the residual launches 6.55 -> 6.23 ms). Longer contractions (the
-    // lm_head input gradient) as 192 x 192 tiles on 8 wavefronts of 96 x 48, which hide
-    // more latency than 4 of 96 x 96 when the CU holds no second workgroup. Otherwise
-    // 32-wide slices in three stages, which leave room for two workgroups per CU.
+    // 96 x 192 tiles where k192_tile_rows picks them (the step's N = 768 launches: the
+    // out-projection and MLP down-projection forwards with their residual epilogue, the
+    // fc, qkv and out-projection input gradients; and the QKV projection): two workgroups
+    // of 4 wavefronts of 48 x 96 per CU over 64-wide k-slices (half the memory requests
+    // per byte) in two stages of 36 KB, the second one's start staggered. With one
+    // 192 x 192 tile per CU every tile finished its k-loop at once and its stores stood
+    // alone; with two workgroups one's epilogue overlaps the other's k-loop (measured:
+    // 66.58 -> 66.18 ms per step, the residual launches 6.55 -> 6.23 ms). Otherwise one
+    // 192 x 192 tile per CU or fewer (the lm_head input gradient, K = 50,304) runs 8
+    // wavefronts of 96 x 48 over 64-wide slices, which hide more latency than 4 of
+    // 96 x 96 when the CU holds no second workgroup; more tiles run 32-wide slices in
+    // three stages, which leave room for two workgroups per CU.
     const int t192 = ((d.M + 191) / 192) * ((d.N + 191) / 192);
     a.krot = gemm_krot();
-    if (t192 <= num_cus() && d.K % 64 == 0) {
-      if (k192_tile_rows(d) == 96) {
-        a.stagger_lo = num_cus();
-        a.stagger_hi = 2 * num_cus();
-        a.stagger_iters = gemm_stagger();
-        return dma_epi<96, 192, 2, 2, 2, true, true, 64>(a, d.epi, 1, s);
-      }
-      return dma_epi<192, 192, 2, 4, 2, true, true, 64>(a, d.epi, 1, s);
+    if (k192_tile_rows(d) == 96) {
+      a.stagger_lo = num_cus();
+      a.stagger_hi = 2 * num_cus();
+      a.stagger_iters = gemm_stagger();
+      return dma_epi<96, 192, 2, 2, 2, true, true, 64>(a, d.epi, 1, s);
     }
+    if (t192 <= num_cus() && d.K % 64 == 0) return dma_epi<192, 192, 2, 4, 2, true, true, 64>(a, d.epi, 1, s);
     a.stagger_lo = num_cus();
     a.stagger_hi = 2 * num_cus();
     a.stagger_iters = gemm_stagger();
