@@ -1626,7 +1626,8 @@ int gemm_colsum_rows(const GemmDesc& d, bool bf16_operands) {
 }
 
 // The start delay (n x 2048 cycles) of the second workgroup per CU in the
-// two-workgroup kernels. The first round's two workgroups of a CU otherwise finish
+// 192 x 192 two-workgroup kernels (launches of several rounds; the 96 x 192 launches
+// take none). The first round's two workgroups of a CU otherwise finish
 // their k-loops together and run their epilogues side by side; offset, one's
 // epilogue overlaps the other's MFMAs. Measured on the GPT-2 step (whole-step
 // A/B in one session): n = 4..10 took 0.3 ms off 72.3 ms, n >= 12 less. The
@@ -1753,22 +1754,20 @@ hipError_t launch_gemm(const GemmDesc& d, bool bf16_operands, hipStream_t s) {
     // out-projection and MLP down-projection forwards with their residual epilogue, the
     // fc, qkv and out-projection input gradients; and the QKV projection): two workgroups
     // of 4 wavefronts of 48 x 96 per CU over 64-wide k-slices (half the memory requests
-    // per byte) in two stages of 36 KB, the second one's start staggered. With one
-    // 192 x 192 tile per CU every tile finished its k-loop at once and its stores stood
-    // alone; with two workgroups one's epilogue overlaps the other's k-loop (measured:
-    // 66.58 -> 66.18 ms per step, the residual launches 6.55 -> 6.23 ms). Otherwise one
+    // per byte) in two stages of 36 KB. With one 192 x 192 tile per CU every tile
+    // finished its k-loop at once and its stores stood alone; with two workgroups per CU
+    // the two interleave (measured: 66.58 -> 66.18 ms per step, the residual launches
+    // 6.55 -> 6.23 ms). These launches take no staggered start: their tiles are all
+    // resident from the start (or nearly), so a delayed second workgroup only lengthens
+    // the launch (delays of 0, 1, 2, 3, 4 and 6 units: 65.60-65.64, 65.66-65.68,
+    // 65.70-65.75, 65.83-65.89, 65.96-65.99 and 66.32-66.34 ms per step). Otherwise one
     // 192 x 192 tile per CU or fewer (the lm_head input gradient, K = 50,304) runs 8
     // wavefronts of 96 x 48 over 64-wide slices, which hide more latency than 4 of
     // 96 x 96 when the CU holds no second workgroup; more tiles run 32-wide slices in
     // three stages, which leave room for two workgroups per CU.
     const int t192 = ((d.M + 191) / 192) * ((d.N + 191) / 192);
     a.krot = gemm_krot();
-    if (k192_tile_rows(d) == 96) {
-      a.stagger_lo = num_cus();
-      a.stagger_hi = 2 * num_cus();
-      a.stagger_iters = gemm_stagger();
-      return dma_epi<96, 192, 2, 2, 2, true, true, 64>(a, d.epi, 1, s);
-    }
+    if (k192_tile_rows(d) == 96) return dma_epi<96, 192, 2, 2, 2, true, true, 64>(a, d.epi, 1, s);
     if (t192 <= num_cus() && d.K % 64 == 0) return dma_epi<192, 192, 2, 4, 2, true, true, 64>(a, d.epi, 1, s);
     a.stagger_lo = num_cus();
     a.stagger_hi = 2 * num_cus();
